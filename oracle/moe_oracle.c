@@ -1,0 +1,383 @@
+/*
+ * CPU oracle for the sparse Mixture-of-Experts feed-forward layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the plain, slow, obviously correct
+ * reference that the GPU kernels are checked against.  Only the test suite,
+ * the smoke entry point and the benchmark's CPU-baseline leg may load it; the
+ * product path never does.  It shares no code, header or table with the HIP
+ * library.
+ *
+ * Everything is computed in fp64 from the exact input values (fp32 inputs, or
+ * bf16 bit patterns widened exactly), with plain loops in the order the
+ * definitions below state.  No blocking, fusion or reordering beyond an
+ * OpenMP split over independent tokens / slots.
+ *
+ * Sources (web pages; cited by title and section):
+ *  [SMoE]  "Mistral 8x7B SMoE architecture deep dive: sparse activation and
+ *          expert division of labour" (jsqmd.com news 960234), sections 2.2,
+ *          3.1, 3.2.
+ *  [CH10]  "Chapter 10 MoE: holding more knowledge with less compute"
+ *          (LLMs-from-scratch ch.10), sections 10.1-10.5.
+ *  [BENCH] "Trillion-parameter MoE activates only 4.9%: 7 expert configs
+ *          measured" (m.xxqk.cn news 679798), parameter accounting paragraph
+ *          and the numpy forward listing.
+ *  [MIXA]  "Mixtral and MoE architecture" (astro-blog-cod.pages.dev), the
+ *          MixtralMoE / FeedForward listing.
+ *
+ * Layouts (row-major; every weight held as a Linear weight [out][in]):
+ *   x   [T][d]         Wg  [E][d]        bias [E] (fp32, optional)
+ *   W1  [E][d_ff][d]   W3  [E][d_ff][d]  W2   [E][d][d_ff]
+ *   Ws1 [d_ffs][d]     Ws3 [d_ffs][d]    Ws2  [d][d_ffs]   (shared expert)
+ *
+ * Parity status per function (pins live in the CPU test suite):
+ *   orc_logits        pinned (numpy fp64 matmul)
+ *   orc_topk          pinned (brute-force stable sort; constructed ties)
+ *   orc_gate          pinned (closed forms; softmax-all + renormalise form)
+ *   orc_count/permute pinned (bincount; numpy stable argsort)
+ *   orc_swiglu_row    pinned (E=1,k=1 dense FFN via numpy matmul)
+ *   orc_forward       pinned (k=E softmax-weighted sum; invariants)
+ *   orc_param_count   pinned (50,331,648 stated as 50.3M on [BENCH])
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_F32 0
+#define ORC_BF16 1
+
+/* Widen one stored element to double.  bf16 is the upper half of an IEEE
+ * binary32, so the widening is exact. */
+static double elem(const void *p, int dt, size_t i)
+{
+    if (dt == ORC_BF16) {
+        uint32_t u = ((uint32_t)((const uint16_t *)p)[i]) << 16;
+        float f;
+        memcpy(&f, &u, sizeof f);
+        return (double)f;
+    }
+    return (double)((const float *)p)[i];
+}
+
+static void row_to_double(const void *p, int dt, size_t off, int n, double *dst)
+{
+    for (int i = 0; i < n; ++i)
+        dst[i] = elem(p, dt, off + (size_t)i);
+}
+
+static double dot(const double *a, const double *b, int n)
+{
+    double s = 0.0;
+    for (int i = 0; i < n; ++i)
+        s += a[i] * b[i];
+    return s;
+}
+
+/* Router scores [SMoE 3.2; CH10 10.3; BENCH listing; MIXA listing]:
+ * logits[t][e] = sum_i x[t][i] * Wg[e][i]  (+ bias[e] when given). */
+void orc_logits(const void *x, const void *Wg, const float *bias, int dt,
+                long T, int d, int E, double *logits)
+{
+    double *wg = malloc(sizeof(double) * (size_t)E * d);
+    for (int e = 0; e < E; ++e)
+        row_to_double(Wg, dt, (size_t)e * d, d, wg + (size_t)e * d);
+#pragma omp parallel
+    {
+        double *xr = malloc(sizeof(double) * d);
+#pragma omp for schedule(static)
+        for (long t = 0; t < T; ++t) {
+            row_to_double(x, dt, (size_t)t * d, d, xr);
+            for (int e = 0; e < E; ++e) {
+                double l = dot(xr, wg + (size_t)e * d, d);
+                if (bias)
+                    l += (double)bias[e];
+                logits[(size_t)t * E + e] = l;
+            }
+        }
+        free(xr);
+    }
+    free(wg);
+}
+
+/* Top-k selection [SMoE 2.2; CH10 10.3]: k rounds; each round takes the
+ * largest logit not yet chosen, scanning experts in ascending order with a
+ * strict '>' so an exact tie goes to the lower expert index.  idx[t][j] is
+ * therefore ordered by descending logit.  Returns 0, or -1 on bad k. */
+int orc_topk(const double *logits, long T, int E, int k, int32_t *idx)
+{
+    if (k < 1 || k > E)
+        return -1;
+    for (long t = 0; t < T; ++t) {
+        const double *l = logits + (size_t)t * E;
+        char *taken = calloc((size_t)E, 1);
+        for (int j = 0; j < k; ++j) {
+            int best = -1;
+            for (int e = 0; e < E; ++e) {
+                if (taken[e])
+                    continue;
+                if (best < 0 || l[e] > l[best])
+                    best = e;
+            }
+            taken[best] = 1;
+            idx[(size_t)t * k + j] = best;
+        }
+        free(taken);
+    }
+    return 0;
+}
+
+/* Gate weights [SMoE 3.2 step 3; CH10 10.3]: softmax over the k selected
+ * logits only, so each token's gates sum to one.  Max-subtracted form:
+ * gate_j = exp(l_j - l_0) / sum_j' exp(l_j' - l_0), l_0 the largest. */
+void orc_gate(const double *logits, const int32_t *idx, long T, int E, int k,
+              double *gate)
+{
+    for (long t = 0; t < T; ++t) {
+        const double *l = logits + (size_t)t * E;
+        const int32_t *ix = idx + (size_t)t * k;
+        double m = l[ix[0]];
+        double z = 0.0;
+        for (int j = 0; j < k; ++j)
+            z += exp(l[ix[j]] - m);
+        for (int j = 0; j < k; ++j)
+            gate[(size_t)t * k + j] = exp(l[ix[j]] - m) / z;
+    }
+}
+
+/* Tokens per expert [CH10 10.4 grouping by expert; BENCH listing's per-expert
+ * row lists]: counts[e] = number of (token, slot) pairs routed to e;
+ * offsets is the exclusive prefix sum, offsets[E] = T*k. */
+void orc_count(const int32_t *idx, long T, int E, int k, int32_t *counts,
+               int32_t *offsets)
+{
+    for (int e = 0; e < E; ++e)
+        counts[e] = 0;
+    for (long p = 0; p < T * (long)k; ++p)
+        counts[idx[p]] += 1;
+    offsets[0] = 0;
+    for (int e = 0; e < E; ++e)
+        offsets[e + 1] = offsets[e] + counts[e];
+}
+
+/* Grouping of pairs by expert [CH10 10.4 (nonzero / index_select); BENCH
+ * listing (np.where per expert)]: both list an expert's rows in ascending
+ * token order.  Flat pair id p = t*k + j; pairs are placed expert by expert,
+ * ascending p inside each expert (a stable counting sort).
+ * perm[s] = pair at sorted slot s; inv[p] = slot of pair p. */
+void orc_permute(const int32_t *idx, long T, int E, int k,
+                 const int32_t *offsets, int32_t *perm, int32_t *inv)
+{
+    int32_t *cursor = malloc(sizeof(int32_t) * (size_t)E);
+    for (int e = 0; e < E; ++e)
+        cursor[e] = offsets[e];
+    for (long p = 0; p < T * (long)k; ++p) {
+        int32_t s = cursor[idx[p]]++;
+        perm[s] = (int32_t)p;
+        inv[p] = s;
+    }
+    free(cursor);
+}
+
+/* One SwiGLU expert on one token [SMoE 3.1; CH10 10.1; MIXA FeedForward]:
+ * a = W1 x, c = W3 x (length dff), h = SiLU(a) * c with SiLU(a) = a/(1+e^-a),
+ * out = W2 h (length d).  xr is the token row already widened to double;
+ * w1/w3/w2 point at this expert's matrices, element offsets o1/o3/o2. */
+static void swiglu(const double *xr, int d, int dff, const void *W1, size_t o1,
+                   const void *W3, size_t o3, const void *W2, size_t o2, int dt,
+                   double *h, double *wrow, double *out)
+{
+    for (int n = 0; n < dff; ++n) {
+        row_to_double(W1, dt, o1 + (size_t)n * d, d, wrow);
+        double a = dot(xr, wrow, d);
+        row_to_double(W3, dt, o3 + (size_t)n * d, d, wrow);
+        double c = dot(xr, wrow, d);
+        h[n] = a / (1.0 + exp(-a)) * c;
+    }
+    for (int j = 0; j < d; ++j) {
+        row_to_double(W2, dt, o2 + (size_t)j * dff, dff, wrow);
+        out[j] = dot(h, wrow, dff);
+    }
+}
+
+/* Exposed single-row expert evaluation (used by per-token sampled checks):
+ * out[d] = W2_e(SiLU(W1_e x_t) * W3_e x_t). */
+void orc_swiglu_row(const void *x, int dt, long t, int d, const void *W1,
+                    const void *W3, const void *W2, int e, int dff, double *out)
+{
+    int wmax = d > dff ? d : dff;
+    double *xr = malloc(sizeof(double) * d);
+    double *h = malloc(sizeof(double) * dff);
+    double *wrow = malloc(sizeof(double) * wmax);
+    row_to_double(x, dt, (size_t)t * d, d, xr);
+    size_t eo = (size_t)e * dff * d;
+    swiglu(xr, d, dff, W1, eo, W3, eo, W2, eo, dt, h, wrow, out);
+    free(xr);
+    free(h);
+    free(wrow);
+}
+
+/* Whole layer, computed through the permutation (the pages group pairs by
+ * expert before running each expert):
+ *   Yp[s] = FFN_e(x_t) with p = perm[s], t = p / k, e = idx[p];
+ *   y[t]  = sum_{j<k} gate[t][j] * Yp[inv[t*k+j]]   (j ascending)
+ *           + shared FFN(x_t) with weight 1 when Ws1 != NULL [CH10 10.5].
+ * Routing comes from `logits_in` when given (e.g. another implementation's
+ * router scores), else from orc_logits.  Outputs that are non-NULL receive
+ * the intermediates.  y is [T][d] in double.  Returns 0 or -1. */
+int orc_forward(const void *x, const void *Wg, const float *bias,
+                const void *W1, const void *W3, const void *W2,
+                const void *Ws1, const void *Ws3, const void *Ws2, int dffs,
+                long T, int E, int k, int d, int dff, int dt,
+                const double *logits_in, double *logits_out, int32_t *idx_out,
+                double *gate_out, int32_t *counts_out, int32_t *offsets_out,
+                int32_t *perm_out, int32_t *inv_out, double *y)
+{
+    if (T < 0 || E < 1 || k < 1 || k > E || d < 1 || dff < 1)
+        return -1;
+    long P = T * (long)k;
+    double *logits = malloc(sizeof(double) * (size_t)(T > 0 ? T : 1) * E);
+    if (logits_in)
+        memcpy(logits, logits_in, sizeof(double) * (size_t)T * E);
+    else
+        orc_logits(x, Wg, bias, dt, T, d, E, logits);
+    int32_t *idx = malloc(sizeof(int32_t) * (size_t)(P > 0 ? P : 1));
+    double *gate = malloc(sizeof(double) * (size_t)(P > 0 ? P : 1));
+    int32_t *counts = malloc(sizeof(int32_t) * (size_t)E);
+    int32_t *offsets = malloc(sizeof(int32_t) * (size_t)(E + 1));
+    int32_t *perm = malloc(sizeof(int32_t) * (size_t)(P > 0 ? P : 1));
+    int32_t *inv = malloc(sizeof(int32_t) * (size_t)(P > 0 ? P : 1));
+    orc_topk(logits, T, E, k, idx);
+    orc_gate(logits, idx, T, E, k, gate);
+    orc_count(idx, T, E, k, counts, offsets);
+    orc_permute(idx, T, E, k, offsets, perm, inv);
+
+    double *Yp = malloc(sizeof(double) * (size_t)(P > 0 ? P : 1) * d);
+    int wmax = d > dff ? d : dff;
+    if (dffs > wmax)
+        wmax = dffs;
+#pragma omp parallel
+    {
+        double *xr = malloc(sizeof(double) * d);
+        double *h = malloc(sizeof(double) * (dff > dffs ? dff : dffs));
+        double *wrow = malloc(sizeof(double) * wmax);
+#pragma omp for schedule(dynamic, 1)
+        for (long s = 0; s < P; ++s) {
+            long p = perm[s];
+            long t = p / k;
+            int e = idx[p];
+            size_t eo = (size_t)e * dff * d;
+            row_to_double(x, dt, (size_t)t * d, d, xr);
+            swiglu(xr, d, dff, W1, eo, W3, eo, W2, eo, dt, h, wrow,
+                   Yp + (size_t)s * d);
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (long t = 0; t < T; ++t) {
+            double *yt = y + (size_t)t * d;
+            for (int c = 0; c < d; ++c)
+                yt[c] = 0.0;
+            for (int j = 0; j < k; ++j) {
+                double g = gate[(size_t)t * k + j];
+                const double *yp = Yp + (size_t)inv[(size_t)t * k + j] * d;
+                for (int c = 0; c < d; ++c)
+                    yt[c] += g * yp[c];
+            }
+            if (Ws1) {
+                double *ys = malloc(sizeof(double) * d);
+                row_to_double(x, dt, (size_t)t * d, d, xr);
+                swiglu(xr, d, dffs, Ws1, 0, Ws3, 0, Ws2, 0, dt, h, wrow, ys);
+                for (int c = 0; c < d; ++c)
+                    yt[c] += ys[c];
+                free(ys);
+            }
+        }
+        free(xr);
+        free(h);
+        free(wrow);
+    }
+
+    if (logits_out)
+        memcpy(logits_out, logits, sizeof(double) * (size_t)T * E);
+    if (idx_out)
+        memcpy(idx_out, idx, sizeof(int32_t) * (size_t)P);
+    if (gate_out)
+        memcpy(gate_out, gate, sizeof(double) * (size_t)P);
+    if (counts_out)
+        memcpy(counts_out, counts, sizeof(int32_t) * (size_t)E);
+    if (offsets_out)
+        memcpy(offsets_out, offsets, sizeof(int32_t) * (size_t)(E + 1));
+    if (perm_out)
+        memcpy(perm_out, perm, sizeof(int32_t) * (size_t)P);
+    if (inv_out)
+        memcpy(inv_out, inv, sizeof(int32_t) * (size_t)P);
+    free(logits);
+    free(idx);
+    free(gate);
+    free(counts);
+    free(offsets);
+    free(perm);
+    free(inv);
+    free(Yp);
+    return 0;
+}
+
+/* Output rows for a chosen list of tokens, given their routing (idx, gate
+ * rows of those tokens): y[r] = sum_j gate[r][j] * FFN_{idx[r][j]}(x_{tok[r]})
+ * (+ shared FFN).  Each token's output depends only on its own routing, so a
+ * sample of a large workload can be checked row by row. */
+void orc_forward_rows(const void *x, const void *W1, const void *W3,
+                      const void *W2, const void *Ws1, const void *Ws3,
+                      const void *Ws2, int dffs, int k, int d, int dff, int dt,
+                      long nrows, const int64_t *tok, const int32_t *idx,
+                      const double *gate, double *y)
+{
+    int wmax = d > dff ? d : dff;
+    if (dffs > wmax)
+        wmax = dffs;
+#pragma omp parallel
+    {
+        double *xr = malloc(sizeof(double) * d);
+        double *h = malloc(sizeof(double) * (dff > dffs ? dff : dffs));
+        double *wrow = malloc(sizeof(double) * wmax);
+        double *o = malloc(sizeof(double) * d);
+#pragma omp for schedule(dynamic, 1)
+        for (long r = 0; r < nrows; ++r) {
+            double *yr = y + (size_t)r * d;
+            row_to_double(x, dt, (size_t)tok[r] * d, d, xr);
+            for (int c = 0; c < d; ++c)
+                yr[c] = 0.0;
+            for (int j = 0; j < k; ++j) {
+                int e = idx[(size_t)r * k + j];
+                size_t eo = (size_t)e * dff * d;
+                swiglu(xr, d, dff, W1, eo, W3, eo, W2, eo, dt, h, wrow, o);
+                double g = gate[(size_t)r * k + j];
+                for (int c = 0; c < d; ++c)
+                    yr[c] += g * o[c];
+            }
+            if (Ws1) {
+                swiglu(xr, d, dffs, Ws1, 0, Ws3, 0, Ws2, 0, dt, h, wrow, o);
+                for (int c = 0; c < d; ++c)
+                    yr[c] += o[c];
+            }
+        }
+        free(xr);
+        free(h);
+        free(wrow);
+        free(o);
+    }
+}
+
+/* Parameter accounting [BENCH parameter paragraph]: a layer holds
+ * 3 * d * E * d_ff expert weights (gate+up counted as two, down as one);
+ * the router is not included. */
+long long orc_param_count(long long d, long long E, long long dff)
+{
+    return 3LL * d * E * dff;
+}
+
+/* Fraction of expert parameters a token activates: k / E [BENCH parameter
+ * paragraph; CH10 10.6]. */
+double orc_active_fraction(int E, int k)
+{
+    return (double)k / (double)E;
+}

@@ -1,0 +1,278 @@
+"""Pins of the CPU oracle to things other than itself (CPU only).
+
+Each check compares the oracle against an independent route to the same
+answer: torch/numpy fp64 library routines for special cases that reduce to a
+dense computation, brute force on tiny inputs, closed forms, invariants, and
+the numbers the pages print (tests/golden/page_numbers.json).  The
+planted-mistake test at the bottom builds copies of the oracle source with one
+plausible mistake each and shows that every such copy fails at least one pin.
+"""
+import json
+import os
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import oracle as O
+from sparse_mixture_experts_permute_amd.inputs import LayerConfig, bf16_bits_to_f32, make_inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_numbers.json")
+
+
+def f64(a):
+    return (bf16_bits_to_f32(a) if a.dtype == np.uint16 else a).astype(np.float64)
+
+
+def tiny(T, d, E, dff, k, dtype="f32", seed=1, dffs=0, skew=0.0):
+    cfg = LayerConfig("tiny", T, d, E, dff, k, dtype, d_ff_shared=dffs, skew=skew, seed=seed)
+    return make_inputs(cfg)
+
+
+def t64(a):
+    return torch.from_numpy(f64(a))
+
+
+def torch_ffn(x, W1, W3, W2):
+    """Dense SwiGLU FFN from torch's own fp64 Linear and SiLU."""
+    X = t64(x)
+    return F.linear(F.silu(F.linear(X, t64(W1))) * F.linear(X, t64(W3)), t64(W2)).numpy()
+
+
+# ---------------------------------------------------------------- checks ---
+
+def check_logits():
+    for dt in ("f32", "bf16"):
+        inp = tiny(37, 64, 6, 64, 2, dt, seed=3, skew=0.75)
+        got = O.logits(inp["x"], inp["Wg"], inp["bias"])
+        ref = F.linear(t64(inp["x"]), t64(inp["Wg"]),
+                       torch.from_numpy(inp["bias"].astype(np.float64))).numpy()
+        np.testing.assert_allclose(got, ref, rtol=1e-13, atol=1e-15)
+
+
+def _brute_topk(lg, k):
+    E = lg.shape[1]
+    out = np.empty((lg.shape[0], k), np.int32)
+    for t in range(lg.shape[0]):
+        order = np.lexsort((np.arange(E), -lg[t]))  # by (-logit, expert index)
+        out[t] = order[:k]
+    return out
+
+
+def check_topk_bruteforce():
+    rng = np.random.default_rng(5)
+    for E in (1, 2, 7, 16):
+        cont = rng.standard_normal((64, E))
+        ties = rng.integers(0, 3, size=(64, E)).astype(np.float64)  # many exact ties
+        for lg in (cont, ties):
+            for k in range(1, E + 1):
+                np.testing.assert_array_equal(O.topk(lg, k), _brute_topk(lg, k))
+
+
+def check_topk_duplicate_rows():
+    # Wg rows 1 and 4 identical -> identical logits; the lower index must win.
+    inp = tiny(48, 32, 6, 32, 1, "f32", seed=9)
+    Wg = inp["Wg"].copy()
+    Wg[4] = Wg[1]
+    Wg[1] *= np.float32(4.0)  # make expert 1 (and 4) often the top score
+    Wg[4] = Wg[1]
+    lg = O.logits(inp["x"], Wg)
+    assert np.array_equal(lg[:, 1], lg[:, 4])
+    idx = O.topk(lg, 2)
+    both = (idx[:, 0] == 1) | (idx[:, 0] == 4)
+    assert both.any()
+    top1 = idx[both, 0]
+    assert np.all(top1 == 1) and np.all(idx[both, 1] == 4)
+
+
+def check_gates():
+    rng = np.random.default_rng(11)
+    lg = rng.standard_normal((200, 9)) * 2.0
+    for k in range(1, 10):
+        idx = O.topk(lg, k)
+        g = O.gate(lg, idx)
+        np.testing.assert_allclose(g.sum(1), 1.0, rtol=0, atol=4e-16 * k)
+        if k == 1:
+            assert np.all(g == 1.0)
+        # softmax over all experts -> top-k -> renormalise, with torch's routines
+        probs = torch.softmax(torch.from_numpy(lg), dim=-1)
+        pv, pi = torch.topk(probs, k, dim=-1)
+        ren = (pv / pv.sum(-1, keepdim=True)).numpy()
+        np.testing.assert_array_equal(pi.numpy(), idx)
+        np.testing.assert_allclose(g, ren, rtol=1e-13, atol=1e-15)
+    # exact ties between the two selected logits -> 0.5 each
+    lg2 = np.array([[0.3, 1.25, -2.0, 1.25], [7.0, 7.0, 7.0, 7.0]])
+    g2 = O.gate(lg2, O.topk(lg2, 2))
+    assert np.all(g2 == 0.5)
+    assert O.topk(lg2, 2).tolist() == [[1, 3], [0, 1]]
+
+
+def check_counts_and_permutation():
+    rng = np.random.default_rng(13)
+    for (T, E, k) in [(1, 1, 1), (5, 3, 2), (300, 8, 2), (129, 64, 4), (512, 128, 8)]:
+        lg = rng.standard_normal((T, E))
+        idx = O.topk(lg, k)
+        counts, offsets, perm, inv = O.permute(idx, E)
+        flat = idx.reshape(-1)
+        np.testing.assert_array_equal(counts, np.bincount(flat, minlength=E))
+        np.testing.assert_array_equal(offsets, np.concatenate([[0], np.cumsum(counts)]))
+        assert offsets[-1] == T * k
+        np.testing.assert_array_equal(perm, np.argsort(flat, kind="stable"))
+        np.testing.assert_array_equal(inv[perm], np.arange(T * k))
+        for e in range(E):
+            seg = perm[offsets[e]:offsets[e + 1]]
+            assert np.all(flat[seg] == e) and np.all(np.diff(seg) > 0)
+
+
+def check_dense_special_case():
+    # E = 1, k = 1: the layer is the dense SwiGLU FFN of its single expert.
+    for dt in ("f32", "bf16"):
+        inp = tiny(23, 64, 1, 96, 1, dt, seed=17)
+        out = O.forward(inp["x"], inp["Wg"], inp["W1"], inp["W3"], inp["W2"], 1)
+        assert np.all(out["gate"] == 1.0)
+        ref = torch_ffn(inp["x"], inp["W1"][0], inp["W3"][0], inp["W2"][0])
+        np.testing.assert_allclose(out["y"], ref, rtol=1e-11, atol=1e-13)
+
+
+def check_all_experts_special_case():
+    # k = E: every expert runs on every token, weighted by the softmax over all logits.
+    for dt in ("f32", "bf16"):
+        E = 5
+        inp = tiny(19, 32, E, 64, E, dt, seed=19, skew=0.5)
+        out = O.forward(inp["x"], inp["Wg"], inp["W1"], inp["W3"], inp["W2"], E,
+                        bias=inp["bias"])
+        lg = F.linear(t64(inp["x"]), t64(inp["Wg"]), torch.from_numpy(inp["bias"].astype(np.float64)))
+        p = torch.softmax(lg, dim=-1).numpy()
+        ref = sum(p[:, e:e + 1] * torch_ffn(inp["x"], inp["W1"][e], inp["W3"][e], inp["W2"][e])
+                  for e in range(E))
+        np.testing.assert_allclose(out["y"], ref, rtol=1e-11, atol=1e-13)
+
+
+def check_shared_expert():
+    inp = tiny(21, 32, 4, 48, 2, "bf16", seed=23, dffs=40)
+    sh = (inp["Ws1"], inp["Ws3"], inp["Ws2"])
+    a = O.forward(inp["x"], inp["Wg"], inp["W1"], inp["W3"], inp["W2"], 2, shared=sh)
+    b = O.forward(inp["x"], inp["Wg"], inp["W1"], inp["W3"], inp["W2"], 2)
+    ref = torch_ffn(inp["x"], *sh)
+    np.testing.assert_allclose(a["y"] - b["y"], ref, rtol=1e-10, atol=1e-12)
+
+
+def check_invariants():
+    inp = tiny(41, 32, 6, 32, 2, "f32", seed=29, skew=0.3)
+    base = O.forward(inp["x"], inp["Wg"], inp["W1"], inp["W3"], inp["W2"], 2, bias=inp["bias"])
+    # relabel experts: permuting router rows and expert weights together leaves y unchanged
+    r = np.random.default_rng(0).permutation(6)
+    rel = O.forward(inp["x"], inp["Wg"][r], inp["W1"][r], inp["W3"][r], inp["W2"][r], 2,
+                    bias=inp["bias"][r])
+    np.testing.assert_allclose(rel["y"], base["y"], rtol=1e-12, atol=1e-14)
+    np.testing.assert_array_equal(r[rel["idx"]], base["idx"])
+    # permuting tokens permutes the rows of y
+    q = np.random.default_rng(1).permutation(41)
+    tp = O.forward(inp["x"][q], inp["Wg"], inp["W1"], inp["W3"], inp["W2"], 2, bias=inp["bias"])
+    np.testing.assert_allclose(tp["y"], base["y"][q], rtol=1e-12, atol=1e-14)
+
+
+def check_given_logits_and_rows():
+    # routing from given scores == own routing when the given scores are the oracle's own;
+    # the per-token evaluation agrees with the permuted evaluation.
+    inp = tiny(33, 32, 8, 32, 3, "bf16", seed=31, dffs=32)
+    sh = (inp["Ws1"], inp["Ws3"], inp["Ws2"])
+    a = O.forward(inp["x"], inp["Wg"], inp["W1"], inp["W3"], inp["W2"], 3, shared=sh)
+    b = O.forward(inp["x"], inp["Wg"], inp["W1"], inp["W3"], inp["W2"], 3, shared=sh,
+                  logits_in=a["logits"])
+    np.testing.assert_array_equal(a["y"], b["y"])
+    rows = [0, 5, 32]
+    y = O.forward_rows(inp["x"], inp["W1"], inp["W3"], inp["W2"], rows, a["idx"][rows],
+                       a["gate"][rows], shared=sh)
+    np.testing.assert_allclose(y, a["y"][rows], rtol=1e-13, atol=1e-15)
+
+
+def check_page_numbers():
+    g = json.load(open(GOLDEN))
+    sw = g["granularity_sweep"]
+    for row in sw["rows"]:
+        assert row["E"] * row["d_ff"] == sw["E_times_dff"]
+        n = O.param_count(sw["d"], row["E"], row["d_ff"])
+        assert round(n / 1e6, 1) == sw["total_params_printed_millions"]
+        assert n == 50_331_648
+        assert f"{100 * O.active_fraction(row['E'], row['k']):.2f}" == row["active_percent_printed"] \
+            or f"{np.floor(10000 * O.active_fraction(row['E'], row['k'])) / 100:.2f}" == \
+            row["active_percent_printed"]
+    ec = g["expert_calls"]
+    rng = np.random.default_rng(37)
+    idx = O.topk(rng.standard_normal((ec["T"], ec["E"])), ec["k"])
+    counts, _ = O.count(idx, ec["E"])
+    assert int(counts.sum()) == ec["expert_calls_printed"]
+    me = g["memory_estimator"]
+    dense = O.param_count(me["emb"], 1, me["hidden"])
+    assert round(dense / 1e8, 2) == me["dense_params_printed_1e8"]
+    assert round(dense * me["bytes_per_param_assumed"] / 1e9, 2) == me["dense_gb_printed"]
+    router = me["emb"] * me["E"]
+    h = round((dense - router) / O.param_count(me["emb"], me["E"], 1))
+    assert h == me["moe_hidden_printed"]
+    active = router + me["k"] * O.param_count(me["emb"], 1, h)
+    assert round(active / 1e8, 2) == me["active_params_printed_1e8"]
+    assert round(active * me["bytes_per_param_assumed"] / 1e9, 2) == me["active_gb_printed"]
+
+
+CHECKS = [check_logits, check_topk_bruteforce, check_topk_duplicate_rows, check_gates,
+          check_counts_and_permutation, check_dense_special_case,
+          check_all_experts_special_case, check_shared_expert, check_invariants,
+          check_given_logits_and_rows, check_page_numbers]
+
+
+@pytest.mark.parametrize("check", CHECKS, ids=[c.__name__ for c in CHECKS])
+def test_oracle_pin(check):
+    check()
+
+
+# ------------------------------------------------------ planted mistakes ---
+
+MUTANTS = [
+    ("silu_sign", "h[n] = a / (1.0 + exp(-a)) * c;", "h[n] = a / (1.0 + exp(a)) * c;"),
+    ("drop_w3_branch", "h[n] = a / (1.0 + exp(-a)) * c;", "h[n] = a / (1.0 + exp(-a));"),
+    ("w3_for_w1", "row_to_double(W1, dt, o1 + (size_t)n * d, d, wrow);",
+     "row_to_double(W3, dt, o3 + (size_t)n * d, d, wrow);"),
+    ("w2_transposed", "row_to_double(W2, dt, o2 + (size_t)j * dff, dff, wrow);\n        out[j] = dot(h, wrow, dff);",
+     "for (int n2 = 0; n2 < dff; ++n2) wrow[n2] = elem(W2, dt, o2 + (size_t)n2 * d + j % d);\n        out[j] = dot(h, wrow, dff);"),
+    ("tie_to_higher", "if (best < 0 || l[e] > l[best])", "if (best < 0 || l[e] >= l[best])"),
+    ("gate_wrong_index", "gate[(size_t)t * k + j] = exp(l[ix[j]] - m) / z;",
+     "gate[(size_t)t * k + j] = exp(l[ix[k - 1 - j]] - m) / z;"),
+    ("gate_unnormalised", "gate[(size_t)t * k + j] = exp(l[ix[j]] - m) / z;",
+     "gate[(size_t)t * k + j] = exp(l[ix[j]] - m);"),
+    ("bias_dropped", "l += (double)bias[e];", "l += 0.0;"),
+    ("perm_unstable", "for (long p = 0; p < T * (long)k; ++p) {\n        int32_t s",
+     "for (long p = T * (long)k - 1; p >= 0; --p) {\n        int32_t s"),
+    ("combine_wrong_slot", "const double *yp = Yp + (size_t)inv[(size_t)t * k + j] * d;",
+     "const double *yp = Yp + (size_t)inv[(size_t)t * k] * d;"),
+    ("shared_half", "yt[c] += ys[c];", "yt[c] += 0.5 * ys[c];"),
+    ("logit_index", "double l = dot(xr, wg + (size_t)e * d, d);",
+     "double l = dot(xr, wg + (size_t)(E - 1 - e) * d, d);"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(tmp_path, name, old, new):
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    src = open(O._SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not unique"
+    mutated = tmp_path / "mutant.c"
+    mutated.write_text(src.replace(old, new))
+    so = tmp_path / "libmutant.so"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+                           "-ffp-contract=off", "-o", str(so), str(mutated), "-lm"])
+    O.use_library(str(so))
+    failed = []
+    try:
+        for check in CHECKS:
+            try:
+                check()
+            except AssertionError:
+                failed.append(check.__name__)
+    finally:
+        O.use_library(None)
+    assert failed, f"planted mistake {name} passed every pin"
