@@ -1,0 +1,256 @@
+"""Benchmark of the MoE layer on one MI355X.
+
+One step = one full layer forward (router, top-k and gate, permutation,
+grouped SwiGLU GEMM, grouped down GEMM, combine) over one batch of seeded
+synthetic tokens already resident in HBM.  Default workload: the
+Mixtral-8x7B-shaped prefill layer (T=8192, d=4096, E=8, d_ff=14336, top-2,
+bf16).  Prints one JSON line.
+
+Per-stage kernel times come from HIP events that the library records on the
+stream it launches on (moe_forward_timed).  The CPU baseline times the CPU
+oracle on a bounded prefix of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="mixtral_prefill_T8192")
+    ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=0,
+                    help="tokens in the CPU-oracle sample (0: size it to ~15 s)")
+    return ap.parse_args()
+
+
+def algorithmic(cfg, counts):
+    """Algorithmic work of the SwiGLU GEMM (the dominant kernel) and of the layer.
+
+    SwiGLU GEMM per routed pair: 4*d*d_ff FLOP (W1 and W3 rows); bytes: the W1 and
+    W3 matrices of every expert hit once + the pair's x row in + its H row out.
+    Layer: 6*d*d_ff FLOP per pair (+6*d*d_ffs per token for a shared expert);
+    bytes: the weights of the experts hit + x + y + router weights.
+    """
+    es = 2 if cfg.dtype == "bf16" else 4
+    P = cfg.T * cfg.k
+    hit = int((counts > 0).sum())
+    g1_flop = 4.0 * cfg.d * cfg.d_ff * P
+    g1_bytes = (hit * 2.0 * cfg.d * cfg.d_ff * es + P * cfg.d * es + P * cfg.d_ff * es)
+    layer_flop = 6.0 * cfg.d * cfg.d_ff * P + 6.0 * cfg.d * cfg.d_ff_shared * cfg.T
+    layer_bytes = (hit * 3.0 * cfg.d * cfg.d_ff * es + 3.0 * cfg.d * cfg.d_ff_shared * es
+                   + 2.0 * cfg.T * cfg.d * es + cfg.E * cfg.d * es)
+    return dict(g1_flop=g1_flop, g1_bytes=g1_bytes, layer_flop=layer_flop,
+                layer_bytes=layer_bytes, experts_hit=hit)
+
+
+def run_workload(cfg, host, dev, steps, warmup, flush_mb=0):
+    import numpy as np
+    import torch
+
+    from sparse_mixture_experts_permute_amd import moe
+
+    T = cfg.T
+    x = dev["x"][:T].contiguous()
+    bias = None
+    if cfg.skew:
+        b = np.zeros(cfg.E, np.float32)
+        b[0] = cfg.skew
+        bias = torch.from_numpy(b).cuda()
+    shared = (dev["Ws1"], dev["Ws3"], dev["Ws2"]) if cfg.d_ff_shared else None
+    layer = moe.MoELayer(dev["Wg"], dev["W1"], dev["W3"], dev["W2"], cfg.k, bias, shared)
+    y = torch.empty_like(x)
+    layer.workspace(T)
+    flush = torch.empty(flush_mb << 20, dtype=torch.uint8, device="cuda") if flush_mb else None
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(moe.NSTAGE_EVENTS)]
+              for _ in range(steps)]
+    for row in events:
+        for e in row:
+            e.record()
+    for _ in range(warmup):
+        layer(x, y)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    t_start.record()
+    for i in range(steps):
+        if flush is not None:
+            flush.zero_()  # evict the 256 MB MALL between steps
+        layer.timed(x, y, events[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    total_ms = t_start.elapsed_time(t_end)
+    stage = np.zeros(len(moe.STAGES))
+    for row in events:
+        for s in range(len(moe.STAGES)):
+            stage[s] += row[s].elapsed_time(row[s + 1])
+    stage /= steps
+    layer_ms = float(stage.sum())
+    counts = layer.intermediates(T)["counts"].cpu().numpy()
+    return dict(total_ms=total_ms, wall_s=wall, stage_ms=stage, layer_ms=layer_ms,
+                counts=counts, layer=layer)
+
+
+def roofline_for(cfg, res):
+    from sparse_mixture_experts_permute_amd import moe
+    a = algorithmic(cfg, res["counts"])
+    g1_ms = float(res["stage_ms"][moe.STAGES.index("gemm_swiglu")])
+    ai = a["g1_flop"] / a["g1_bytes"]
+    peak_f = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    ridge = peak_f * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if ai >= ridge:
+        ach = a["g1_flop"] / (g1_ms * 1e-3) / 1e12
+        rl = dict(bound="mfma", achieved=round(ach, 2), peak=peak_f, unit="TFLOP/s",
+                  frac=round(ach / peak_f, 4))
+    else:
+        ach = a["g1_bytes"] / (g1_ms * 1e-3) / 1e9
+        rl = dict(bound="hbm", achieved=round(ach, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                  frac=round(ach / PEAK_HBM_GBS, 4))
+    rl.update(traffic=None, kernel="grouped_gemm_swiglu", kernel_ms=round(g1_ms, 4),
+              algorithmic_flop=a["g1_flop"], algorithmic_bytes=a["g1_bytes"])
+    # whole-layer fractions
+    lt = res["layer_ms"] * 1e-3
+    layer = dict(mfma_frac=round(a["layer_flop"] / lt / (peak_f * 1e12), 4),
+                 hbm_frac=round(a["layer_bytes"] / lt / (PEAK_HBM_GBS * 1e9), 4),
+                 experts_hit=a["experts_hit"])
+    return rl, layer
+
+
+def cpu_baseline(cfg, host, n_tokens):
+    import numpy as np
+
+    from oracle import oracle as O
+    if n_tokens <= 0:
+        # size the sample from a short probe run to about 15 s of CPU work
+        probe = 8
+        t0 = time.perf_counter()
+        O.forward(host["x"][:probe], host["Wg"], host["W1"], host["W3"], host["W2"], cfg.k)
+        rate = probe / max(time.perf_counter() - t0, 1e-6)
+        n_tokens = int(min(cfg.T, max(16, rate * 15.0)))
+    x = np.ascontiguousarray(host["x"][:n_tokens])
+    bias = None
+    if cfg.skew:
+        bias = np.zeros(cfg.E, np.float32)
+        bias[0] = cfg.skew
+    shared = (host["Ws1"], host["Ws3"], host["Ws2"]) if cfg.d_ff_shared else None
+    t0 = time.perf_counter()
+    O.forward(x, host["Wg"], host["W1"], host["W3"], host["W2"], cfg.k, bias=bias, shared=shared)
+    el = time.perf_counter() - t0
+    return dict(value=round(n_tokens / el, 3), unit="tokens/s", cores=O.num_threads(),
+                kind="oracle",
+                sample=f"first {n_tokens} of {cfg.T} tokens of {cfg.name}, whole layer "
+                       f"(fp64 router, top-k, permutation, experts, combine) in {el:.1f} s")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer's "
+              "single-GPU path is what this build measures", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from sparse_mixture_experts_permute_amd import moe
+    from sparse_mixture_experts_permute_amd.inputs import CONFIGS, make_inputs
+
+    moe.lib()
+    cfg = CONFIGS[args.workload]
+    fam_T = max(cfg.T, 8192 if cfg.d == 4096 and cfg.E == 8 else cfg.T)
+    log(f"generating inputs for {cfg.name} (x for {fam_T} tokens)")
+    t0 = time.perf_counter()
+    host = make_inputs(cfg.with_(skew=0.0), T=fam_T)
+    dev = {n: moe.tensor_from_numpy(a) for n, a in host.items() if a is not None}
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
+
+    res = run_workload(cfg, host, dev, args.steps, args.warmup)
+    rl, layer_fr = roofline_for(cfg, res)
+    ms = res["total_ms"] / args.steps
+    value = cfg.T / (ms * 1e-3)
+    stage = {s: round(float(v), 4) for s, v in zip(moe.STAGES, res["stage_ms"])}
+    log(f"{cfg.name}: {ms:.3f} ms/step, {value:.0f} tokens/s, stages {stage}")
+    counts = res["counts"]
+
+    extra = []
+    if not args.no_extra and cfg.d == 4096 and cfg.E == 8:
+        for name, steps, flush in [("mixtral_prefill_T2048", 10, 0),
+                                   ("mixtral_prefill_T8192_skew", 5, 0),
+                                   ("mixtral_decode_T1", 20, 512),
+                                   ("mixtral_decode_T128", 20, 512)]:
+            if name == cfg.name:
+                continue
+            c2 = CONFIGS[name]
+            r2 = run_workload(c2, host, dev, steps, 2, flush_mb=flush)
+            rl2, lf2 = roofline_for(c2, r2)
+            ms2 = r2["layer_ms"]
+            e = dict(workload=name, T=c2.T, ms_per_step=round(ms2, 4),
+                     tokens_per_s=round(c2.T / (ms2 * 1e-3), 1),
+                     stage_ms={s: round(float(v), 4) for s, v in zip(moe.STAGES,
+                                                                      r2["stage_ms"])},
+                     roofline=rl2, layer=lf2, mall_flushed=bool(flush))
+            if c2.skew:
+                e["hot_expert_share"] = round(float(r2["counts"][0] / r2["counts"].sum()), 4)
+            log(f"{name}: {ms2:.4f} ms/step (sum of stages), {e['tokens_per_s']} tokens/s")
+            extra.append(e)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(cfg, host, args.cpu_tokens)
+        log(f"cpu baseline: {cpu}")
+
+    out = {
+        "metric": "MoE-layer tokens/s; % bf16 MFMA peak (prefill) and % HBM BW (decode)",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) tokens, N(0,1/fan_in) expert weights, "
+                "router N(0,0.02^2), bf16-rounded)",
+        "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "d_ff": cfg.d_ff,
+                   "k": cfg.k, "d_ff_shared": cfg.d_ff_shared, "skew": cfg.skew,
+                   "global_batch": cfg.T, "parallelism": "single GPU"},
+        "roofline": rl,
+        "layer_roofline": layer_fr,
+        "stage_ms": stage,
+        "expert_counts": {"min": int(counts.min()), "max": int(counts.max()),
+                          "mean": float(counts.mean())},
+        "cpu_baseline": cpu,
+        "extra": extra,
+        "wall_s_timed": round(res["wall_s"], 3),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,136 @@
+/*
+ * moe_mi355x.h -- C ABI of the sparse Mixture-of-Experts feed-forward layer
+ * for AMD MI355X (gfx950).
+ *
+ * The layer (sources cited by page title and section):
+ *   router    logits[t][e] = sum_i x[t][i] * Wg[e][i] (+ bias[e])
+ *             ("Chapter 10 MoE" of LLMs-from-scratch, section 10.3;
+ *              "Mistral 8x7B SMoE architecture deep dive", section 3.2)
+ *   top-k     the k largest logits per token, ordered by descending logit;
+ *             an exact tie goes to the lower expert index
+ *   gate      softmax over the k selected logits only (sums to one)
+ *             (same sections; the chapter stresses selected-only softmax)
+ *   experts   FFN_e(x) = W2_e( SiLU(W1_e x) * (W3_e x) ),  SiLU(a) = a*sigmoid(a)
+ *             ("Mistral 8x7B SMoE ..." section 3.1; "Mixtral and MoE
+ *              architecture", FeedForward listing)
+ *   combine   y[t] = sum_j gate[t][j] * FFN_{idx[t][j]}(x_t)
+ *             (+ an always-on shared expert with weight 1, "Chapter 10 MoE"
+ *              section 10.5)
+ * Pairs are grouped by expert before the expert GEMMs ("Chapter 10 MoE"
+ * section 10.4; the per-expert row lists of the "Trillion-parameter MoE ...
+ * 7 expert configs measured" numpy listing): a stable counting sort of the
+ * flat pair ids p = t*k + j by expert.
+ *
+ * Conventions for every call
+ *  - All tensors are row-major and dense.  Every weight is held as a Linear
+ *    weight [out][in]:  Wg [E][d], W1 and W3 [E][d_ff][d], W2 [E][d][d_ff],
+ *    shared Ws1 and Ws3 [d_ff_shared][d], Ws2 [d][d_ff_shared].
+ *  - Every pointer argument is a DEVICE pointer owned by the caller; the
+ *    library never allocates, frees or retains memory, and never synchronises
+ *    the host with the device.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  All work is
+ *    enqueued on it asynchronously; results are valid once the stream has
+ *    reached that point.
+ *  - dtype MOE_BF16: x, weights and y are bf16 (IEEE binary32 upper halves);
+ *    dtype MOE_F32: all fp32.  Accumulation is always fp32.  Router logits and
+ *    gates are always fp32; indices and counts are int32.
+ *  - Return value: MOE_OK (0) or a negative error code (see moe_strerror).
+ *    Argument errors are detected before anything is enqueued.  A fault
+ *    inside a kernel is reported by the stream, not by these calls.
+ *  - Shape limits: 1 <= k <= E <= 256; T >= 0 (T = 0 enqueues nothing);
+ *    d and d_ff (and d_ff_shared) positive multiples of 64;
+ *    T * k < 2^31 and every tensor under 2^31 elements per expert slice.
+ *  - Inputs must be finite.  Calls that share a workspace on overlapping
+ *    streams race.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+enum {
+    MOE_OK = 0,
+    MOE_EINVAL = -1,     /* bad shape, k, E, or a required NULL pointer */
+    MOE_EDTYPE = -2,     /* dtype not MOE_F32 / MOE_BF16 */
+    MOE_EWORKSPACE = -3, /* workspace too small or misaligned (needs 256 B) */
+    MOE_ELAUNCH = -4,    /* the HIP runtime refused a kernel launch */
+    MOE_EDEVICE = -5     /* current device is not a gfx950 GPU */
+};
+
+/* Router + top-k + gate (the first two steps above).
+ *   x      [T][d]   dtype          Wg [E][d] dtype
+ *   bias   [E] fp32 or NULL (a per-expert logit offset, e.g. to skew routing)
+ *   idx    [T][k] int32  out: selected experts, descending logit, ties -> lower e
+ *   gate   [T][k] fp32   out: softmax over the selected logits
+ *   logits [T][E] fp32   out (may be NULL): the router scores idx/gate came from */
+int moe_route(const void *x, const void *Wg, const float *bias, int T, int d, int E, int k,
+              int dtype, int32_t *idx, float *gate, float *logits, void *stream);
+
+/* Bytes of scratch moe_permute needs for (T, E, k). */
+size_t moe_permute_workspace_bytes(int T, int E, int k);
+
+/* Grouping of the T*k (token, slot) pairs by expert (stable counting sort).
+ *   idx     [T][k] int32 in, values in [0, E)
+ *   counts  [E]    out: pairs routed to each expert
+ *   offsets [E+1]  out: exclusive prefix sum, offsets[E] = T*k
+ *   perm    [T*k]  out: perm[s] = flat pair id t*k+j placed at slot s; slots of
+ *                  expert e are offsets[e]..offsets[e+1]-1 in ascending pair id
+ *   inv     [T*k]  out: inv[perm[s]] = s
+ * Deterministic (no atomic-order dependence).  `workspace` is device scratch of
+ * moe_permute_workspace_bytes(T, E, k) bytes, 256-byte aligned. */
+int moe_permute(const int32_t *idx, int T, int E, int k, int32_t *counts, int32_t *offsets,
+                int32_t *perm, int32_t *inv, void *workspace, size_t workspace_bytes,
+                void *stream);
+
+/* Bytes of scratch moe_forward needs (d_ff_shared = 0: no shared expert). */
+size_t moe_workspace_bytes(int T, int d, int d_ff, int E, int k, int d_ff_shared, int dtype);
+
+/* Byte offsets inside the moe_forward workspace of the intermediates, so that
+ * a caller can read them after the call:
+ *   out[0] logits [T][E] f32    out[1] idx  [T][k] i32   out[2] gate [T][k] f32
+ *   out[3] counts [E] i32       out[4] offsets [E+1] i32 out[5] perm [T*k] i32
+ *   out[6] inv [T*k] i32
+ * Returns MOE_OK or MOE_EINVAL / MOE_EDTYPE. */
+#define MOE_WS_NFIELDS 7
+int moe_workspace_offsets(int T, int d, int d_ff, int E, int k, int d_ff_shared, int dtype,
+                          size_t out[MOE_WS_NFIELDS]);
+
+/* The whole layer: route -> permute -> grouped SwiGLU expert GEMMs -> combine.
+ *   x [T][d]; Wg [E][d]; bias [E] fp32 or NULL; W1, W3 [E][d_ff][d]; W2 [E][d][d_ff]
+ *   Ws1, Ws3 [d_ff_shared][d], Ws2 [d][d_ff_shared]: the shared expert, or all
+ *     NULL with d_ff_shared = 0
+ *   workspace: device scratch of moe_workspace_bytes(...) bytes, 256-byte aligned
+ *   y [T][d] out, dtype.  y may not alias x. */
+int moe_forward(const void *x, const void *Wg, const float *bias, const void *W1,
+                const void *W3, const void *W2, const void *Ws1, const void *Ws3,
+                const void *Ws2, int d_ff_shared, int T, int E, int k, int d, int d_ff,
+                int dtype, void *workspace, size_t workspace_bytes, void *y, void *stream);
+
+/* moe_forward that also records a timing event on `stream` at each stage
+ * boundary, for measurement.  `events` holds MOE_NSTAGE_EVENTS caller-created
+ * hipEvent_t handles: [0] before the router, [1] after the router, [2] after
+ * the permutation, [3] after the row gather, [4] after the SwiGLU GEMM, [5]
+ * after the down GEMM, [6] after the shared expert (if any), [7] after the
+ * combine.  Same results and errors as moe_forward; MOE_EINVAL if `events`
+ * or any of its handles is NULL. */
+#define MOE_NSTAGE_EVENTS 8
+int moe_forward_timed(const void *x, const void *Wg, const float *bias, const void *W1,
+                      const void *W3, const void *W2, const void *Ws1, const void *Ws3,
+                      const void *Ws2, int d_ff_shared, int T, int E, int k, int d, int d_ff,
+                      int dtype, void *workspace, size_t workspace_bytes, void *y, void *stream,
+                      void *const *events);
+
+/* Static text for a status code. */
+const char *moe_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

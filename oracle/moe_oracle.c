@@ -39,6 +39,9 @@
  *   orc_param_count   pinned (50,331,648 stated as 50.3M on [BENCH])
  */
 #include <math.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 #include <stddef.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -380,4 +383,14 @@ long long orc_param_count(long long d, long long E, long long dff)
 double orc_active_fraction(int E, int k)
 {
     return (double)k / (double)E;
+}
+
+/* Threads an OpenMP region of the oracle uses (for reporting CPU timings). */
+int orc_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
 }

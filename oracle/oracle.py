@@ -64,6 +64,7 @@ def _bind(path: str):
     L.orc_param_count.restype = ctypes.c_longlong
     L.orc_active_fraction.argtypes = [ctypes.c_int, ctypes.c_int]
     L.orc_active_fraction.restype = ctypes.c_double
+    L.orc_num_threads.restype = ctypes.c_int
     return L
 
 
@@ -228,3 +229,8 @@ def param_count(d, E, dff) -> int:
 
 def active_fraction(E, k) -> float:
     return float(lib().orc_active_fraction(E, k))
+
+
+def num_threads() -> int:
+    """Threads the oracle's OpenMP regions use."""
+    return int(lib().orc_num_threads())

@@ -1,0 +1,271 @@
+// C ABI of the MoE layer: argument checks, workspace layout and the launch
+// sequence route -> permute -> gather -> grouped SwiGLU GEMM -> grouped down
+// GEMM -> combine, all enqueued on the caller's stream with no host sync.
+#include <string.h>
+
+#include "../../include/moe_mi355x.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+enum Field {
+  F_LOGITS, F_IDX, F_GATE, F_COUNTS, F_OFFSETS, F_PERM, F_INV, F_MT0, F_MT1, F_SHSEG, F_BLK,
+  F_XP, F_H, F_YP, F_HS, F_YS, F_COUNT
+};
+
+struct Layout {
+  size_t off[F_COUNT];
+  size_t total;
+};
+
+bool dims_ok(int T, int d, int d_ff, int E, int k, int dffs) {
+  if (T < 0 || E < 1 || E > 256 || k < 1 || k > E) return false;
+  if (d < 64 || d % 64 || d_ff < 64 || d_ff % 64) return false;
+  if (dffs < 0 || dffs % 64) return false;
+  if ((long long)T * k >= (1LL << 31)) return false;
+  if ((long long)T * k * (long long)(d > d_ff ? d : d_ff) >= (1LL << 40)) return false;
+  return true;
+}
+
+size_t esize(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
+
+Layout layout(int T, int d, int d_ff, int E, int k, int dffs, int dtype) {
+  Layout L;
+  const size_t P = (size_t)T * k, es = esize(dtype);
+  const size_t nb = (size_t)moe::permute_nblocks((int)P);
+  size_t sz[F_COUNT] = {};
+  sz[F_LOGITS] = (size_t)T * E * 4;
+  sz[F_IDX] = P * 4;
+  sz[F_GATE] = P * 4;
+  sz[F_COUNTS] = (size_t)E * 4;
+  sz[F_OFFSETS] = (size_t)(E + 1) * 4;
+  sz[F_PERM] = P * 4;
+  sz[F_INV] = P * 4;
+  sz[F_MT0] = (size_t)(E + 1) * 4;
+  sz[F_MT1] = (size_t)(E + 1) * 4;
+  sz[F_SHSEG] = 8 * 4;
+  sz[F_BLK] = nb * E * 4;
+  sz[F_XP] = P * d * es;
+  sz[F_H] = P * d_ff * es;
+  sz[F_YP] = P * d * 4;
+  sz[F_HS] = (size_t)T * dffs * es;
+  sz[F_YS] = dffs ? (size_t)T * d * 4 : 0;
+  size_t o = 0;
+  for (int f = 0; f < F_COUNT; ++f) {
+    L.off[f] = o;
+    o += align_up(sz[f]);
+  }
+  L.total = o;
+  return L;
+}
+
+// Device check, cached per device id.
+int device_ok() {
+  static int state[64];  // 0 unknown, 1 ok, 2 bad
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MOE_EDEVICE;
+  if (dev < 64 && state[dev]) return state[dev] == 1 ? MOE_OK : MOE_EDEVICE;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOE_EDEVICE;
+  const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < 64) state[dev] = ok ? 1 : 2;
+  return ok ? MOE_OK : MOE_EDEVICE;
+}
+
+int launched(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ELAUNCH; }
+
+template <typename P> P *at(void *ws, size_t off) {
+  return reinterpret_cast<P *>(reinterpret_cast<char *>(ws) + off);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *moe_strerror(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument (shape, k, E or a required NULL pointer)";
+    case MOE_EDTYPE: return "unsupported dtype (MOE_F32 or MOE_BF16)";
+    case MOE_EWORKSPACE: return "workspace too small or not 256-byte aligned";
+    case MOE_ELAUNCH: return "kernel launch failed";
+    case MOE_EDEVICE: return "current device is not a gfx950 GPU";
+    default: return "unknown status";
+  }
+}
+
+int moe_route(const void *x, const void *Wg, const float *bias, int T, int d, int E, int k,
+              int dtype, int32_t *idx, float *gate, float *logits, void *stream) {
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_EDTYPE;
+  if (T < 0 || E < 1 || E > 256 || k < 1 || k > E || d < 64 || d % 64) return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  if (!x || !Wg || !idx || !gate) return MOE_EINVAL;
+  int st = device_ok();
+  if (st != MOE_OK) return st;
+  return launched(moe::launch_router(dtype, x, Wg, bias, T, d, E, k, idx, gate, logits,
+                                     (hipStream_t)stream));
+}
+
+size_t moe_permute_workspace_bytes(int T, int E, int k) {
+  if (T < 0 || E < 1 || k < 1) return 0;
+  const size_t nb = (size_t)moe::permute_nblocks(T * k);
+  return align_up(nb * E * 4) + 3 * align_up((size_t)(E + 1) * 4 + 32);
+}
+
+int moe_permute(const int32_t *idx, int T, int E, int k, int32_t *counts, int32_t *offsets,
+                int32_t *perm, int32_t *inv, void *workspace, size_t workspace_bytes,
+                void *stream) {
+  if (T < 0 || E < 1 || E > 256 || k < 1 || k > E) return MOE_EINVAL;
+  if ((long long)T * k >= (1LL << 31)) return MOE_EINVAL;
+  if (T == 0) {
+    if (!offsets) return MOE_EINVAL;
+    // all counts and offsets are zero: nothing routed
+    hipStream_t s = (hipStream_t)stream;
+    if (counts && hipMemsetAsync(counts, 0, (size_t)E * 4, s) != hipSuccess) return MOE_ELAUNCH;
+    return launched(hipMemsetAsync(offsets, 0, (size_t)(E + 1) * 4, s));
+  }
+  if (!idx || !counts || !offsets || !perm || !inv || !workspace) return MOE_EINVAL;
+  if (workspace_bytes < moe_permute_workspace_bytes(T, E, k) ||
+      ((uintptr_t)workspace % kAlign))
+    return MOE_EWORKSPACE;
+  int st = device_ok();
+  if (st != MOE_OK) return st;
+  const size_t nb = (size_t)moe::permute_nblocks(T * k);
+  char *w = (char *)workspace;
+  int32_t *blk = (int32_t *)w;
+  int32_t *mt0 = (int32_t *)(w + align_up(nb * E * 4));
+  int32_t *mt1 = mt0 + align_up((size_t)(E + 1) * 4 + 32) / 4;
+  int32_t *sh = mt1 + align_up((size_t)(E + 1) * 4 + 32) / 4;
+  const int bm = moe::gemm_bm();
+  return launched(moe::launch_permute(idx, T, E, k, bm, bm, blk, counts, offsets, perm, inv, mt0,
+                                      mt1, sh, (hipStream_t)stream));
+}
+
+size_t moe_workspace_bytes(int T, int d, int d_ff, int E, int k, int d_ff_shared, int dtype) {
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return 0;
+  if (!dims_ok(T, d, d_ff, E, k, d_ff_shared)) return 0;
+  return layout(T, d, d_ff, E, k, d_ff_shared, dtype).total;
+}
+
+int moe_workspace_offsets(int T, int d, int d_ff, int E, int k, int d_ff_shared, int dtype,
+                          size_t out[MOE_WS_NFIELDS]) {
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_EDTYPE;
+  if (!dims_ok(T, d, d_ff, E, k, d_ff_shared) || !out) return MOE_EINVAL;
+  Layout L = layout(T, d, d_ff, E, k, d_ff_shared, dtype);
+  const Field f[MOE_WS_NFIELDS] = {F_LOGITS, F_IDX, F_GATE, F_COUNTS, F_OFFSETS, F_PERM, F_INV};
+  for (int i = 0; i < MOE_WS_NFIELDS; ++i) out[i] = L.off[f[i]];
+  return MOE_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+int forward_impl(const void *x, const void *Wg, const float *bias, const void *W1,
+                 const void *W3, const void *W2, const void *Ws1, const void *Ws3,
+                 const void *Ws2, int d_ff_shared, int T, int E, int k, int d, int d_ff,
+                 int dtype, void *workspace, size_t workspace_bytes, void *y, void *stream,
+                 void *const *events) {
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_EDTYPE;
+  if (!dims_ok(T, d, d_ff, E, k, d_ff_shared)) return MOE_EINVAL;
+  const bool shared = d_ff_shared > 0;
+  if (shared != (Ws1 != nullptr) || shared != (Ws3 != nullptr) || shared != (Ws2 != nullptr))
+    return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  if (!x || !Wg || !W1 || !W3 || !W2 || !y || !workspace || x == y) return MOE_EINVAL;
+  const Layout L = layout(T, d, d_ff, E, k, d_ff_shared, dtype);
+  if (workspace_bytes < L.total || ((uintptr_t)workspace % kAlign)) return MOE_EWORKSPACE;
+  int st = device_ok();
+  if (st != MOE_OK) return st;
+
+  hipStream_t s = (hipStream_t)stream;
+  void *ws = workspace;
+  const int P = T * k;
+  const int bm = moe::gemm_bm();
+  float *logits = at<float>(ws, L.off[F_LOGITS]);
+  int32_t *idx = at<int32_t>(ws, L.off[F_IDX]);
+  float *gate = at<float>(ws, L.off[F_GATE]);
+  int32_t *counts = at<int32_t>(ws, L.off[F_COUNTS]);
+  int32_t *offsets = at<int32_t>(ws, L.off[F_OFFSETS]);
+  int32_t *perm = at<int32_t>(ws, L.off[F_PERM]);
+  int32_t *inv = at<int32_t>(ws, L.off[F_INV]);
+  int32_t *mt0 = at<int32_t>(ws, L.off[F_MT0]);
+  int32_t *mt1 = at<int32_t>(ws, L.off[F_MT1]);
+  int32_t *shseg = at<int32_t>(ws, L.off[F_SHSEG]);
+  int32_t *blk = at<int32_t>(ws, L.off[F_BLK]);
+  void *Xp = at<char>(ws, L.off[F_XP]);
+  void *H = at<char>(ws, L.off[F_H]);
+  float *Yp = at<float>(ws, L.off[F_YP]);
+  void *Hs = at<char>(ws, L.off[F_HS]);
+  float *Ys = at<float>(ws, L.off[F_YS]);
+
+  hipError_t e;
+  // stage boundary i: an optional timing event recorded on the stream
+#define MOE_MARK(i) \
+  if (events && hipEventRecord((hipEvent_t)events[i], s) != hipSuccess) goto fail;
+  MOE_MARK(0);
+  if ((e = moe::launch_router(dtype, x, Wg, bias, T, d, E, k, idx, gate, logits, s))) goto fail;
+  MOE_MARK(1);
+  if ((e = moe::launch_permute(idx, T, E, k, bm, bm, blk, counts, offsets, perm, inv, mt0, mt1,
+                               shseg, s)))
+    goto fail;
+  MOE_MARK(2);
+  if ((e = moe::launch_gather(x, perm, P, k, d, (int)esize(dtype), Xp, s))) goto fail;
+  MOE_MARK(3);
+  {
+    const int maxmt = (P + bm - 1) / bm + E;
+    if ((e = moe::launch_gemm_swiglu(dtype, Xp, W1, W3, H, offsets, mt0, E, d_ff, d, maxmt, s)))
+      goto fail;
+    MOE_MARK(4);
+    if ((e = moe::launch_gemm_down(dtype, H, W2, Yp, offsets, mt1, E, d, d_ff, maxmt, s)))
+      goto fail;
+    MOE_MARK(5);
+  }
+  if (shared) {
+    const int maxmt = (T + bm - 1) / bm;
+    if ((e = moe::launch_gemm_swiglu(dtype, x, Ws1, Ws3, Hs, shseg, shseg + 2, 1, d_ff_shared, d,
+                                     maxmt, s)))
+      goto fail;
+    if ((e = moe::launch_gemm_down(dtype, Hs, Ws2, Ys, shseg, shseg + 4, 1, d, d_ff_shared,
+                                   maxmt, s)))
+      goto fail;
+  }
+  MOE_MARK(6);
+  if ((e = moe::launch_combine(dtype, Yp, shared ? Ys : nullptr, inv, gate, T, k, d, y, s)))
+    goto fail;
+  MOE_MARK(7);
+#undef MOE_MARK
+  return MOE_OK;
+fail:
+  return MOE_ELAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_forward(const void *x, const void *Wg, const float *bias, const void *W1,
+                const void *W3, const void *W2, const void *Ws1, const void *Ws3,
+                const void *Ws2, int d_ff_shared, int T, int E, int k, int d, int d_ff,
+                int dtype, void *workspace, size_t workspace_bytes, void *y, void *stream) {
+  return forward_impl(x, Wg, bias, W1, W3, W2, Ws1, Ws3, Ws2, d_ff_shared, T, E, k, d, d_ff,
+                      dtype, workspace, workspace_bytes, y, stream, nullptr);
+}
+
+int moe_forward_timed(const void *x, const void *Wg, const float *bias, const void *W1,
+                      const void *W3, const void *W2, const void *Ws1, const void *Ws3,
+                      const void *Ws2, int d_ff_shared, int T, int E, int k, int d, int d_ff,
+                      int dtype, void *workspace, size_t workspace_bytes, void *y, void *stream,
+                      void *const *events) {
+  if (!events) return MOE_EINVAL;
+  for (int i = 0; i < MOE_NSTAGE_EVENTS; ++i)
+    if (!events[i]) return MOE_EINVAL;
+  return forward_impl(x, Wg, bias, W1, W3, W2, Ws1, Ws3, Ws2, d_ff_shared, T, E, k, d, d_ff,
+                      dtype, workspace, workspace_bytes, y, stream, events);
+}
+
+}  // extern "C"

@@ -1,0 +1,61 @@
+// Gate-weighted combine back to token order:
+//   y[t][:] = sum_{j<k} gate[t][j] * Yp[inv[t*k+j]][:]  (+ Ys[t][:] for the shared expert)
+// summed in fp32 with j ascending, written once per token with no atomics
+// ("Chapter 10 MoE", sections 10.4 and 10.5; "Mixtral and MoE architecture",
+// weighted accumulation in the MixtralMoE listing).
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+// One block per token; each thread handles 4 consecutive columns per step.
+template <typename T>
+__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ Yp,
+                                                      const float *__restrict__ Ys,
+                                                      const int32_t *__restrict__ inv,
+                                                      const float *__restrict__ gate, int k,
+                                                      int d, T *__restrict__ y) {
+  const int t = blockIdx.x;
+  const int d4 = d / 4;
+  for (int c = threadIdx.x; c < d4; c += 256) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < k; ++j) {
+      const float g = gate[(size_t)t * k + j];
+      const float4 v = reinterpret_cast<const float4 *>(Yp)[(size_t)inv[(size_t)t * k + j] * d4 + c];
+      acc.x = fmaf(g, v.x, acc.x);
+      acc.y = fmaf(g, v.y, acc.y);
+      acc.z = fmaf(g, v.z, acc.z);
+      acc.w = fmaf(g, v.w, acc.w);
+    }
+    if (Ys) {
+      const float4 v = reinterpret_cast<const float4 *>(Ys)[(size_t)t * d4 + c];
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
+    const size_t o = (size_t)t * d + 4 * c;
+    Elem<T>::store(y, o + 0, acc.x);
+    Elem<T>::store(y, o + 1, acc.y);
+    Elem<T>::store(y, o + 2, acc.z);
+    Elem<T>::store(y, o + 3, acc.w);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(int dtype, const float *Yp, const float *Ys, const int32_t *inv,
+                          const float *gate, int T, int k, int d, void *y, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (dtype == 1)
+    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(T), dim3(256), 0, s, Yp, Ys, inv, gate, k, d,
+                       (bf16_t *)y);
+  else
+    hipLaunchKernelGGL(combine_kernel<float>, dim3(T), dim3(256), 0, s, Yp, Ys, inv, gate, k, d,
+                       (float *)y);
+  return hipGetLastError();
+}
+
+}  // namespace moe

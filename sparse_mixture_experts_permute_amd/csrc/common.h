@@ -1,0 +1,56 @@
+// Kernel-side helpers shared by the HIP sources of the MoE layer (gfx950).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef uint16_t bf16_t;  // bf16 held as its bit pattern
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_v;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_v;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_v;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_v;
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t h) {
+  return __uint_as_float(((uint32_t)h) << 16);
+}
+
+// Round to nearest even; inputs are finite.
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  __device__ __forceinline__ static float load(const float *p, size_t i) { return p[i]; }
+  __device__ __forceinline__ static void store(float *p, size_t i, float v) { p[i] = v; }
+};
+template <> struct Elem<bf16_t> {
+  __device__ __forceinline__ static float load(const bf16_t *p, size_t i) {
+    return bf16_to_f32(p[i]);
+  }
+  __device__ __forceinline__ static void store(bf16_t *p, size_t i, float v) {
+    p[i] = f32_to_bf16(v);
+  }
+};
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
+
+__device__ __forceinline__ float silu(float a) { return a / (1.0f + __expf(-a)); }
+
+// First index i in [0, n) with a[i+1] > g, for non-decreasing a[0..n] with a[0] <= g.
+__device__ __forceinline__ int upper_segment(const int32_t *a, int n, int g) {
+  int lo = 0, hi = n;  // invariant: a[lo] <= g, answer in [lo, hi)
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (a[mid] <= g) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+}  // namespace moe

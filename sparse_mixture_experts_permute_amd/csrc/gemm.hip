@@ -1,0 +1,254 @@
+// Grouped expert GEMMs on the gfx950 matrix cores.
+//
+// For each expert segment e (rows offsets[e] .. offsets[e+1]-1 of the permuted
+// activations):
+//   SWIGLU = true : H = SiLU(A W1_e^T) * (A W3_e^T)   (W1, W3 [E][N][K], H [rows][N])
+//   SWIGLU = false: Y = A W2_e^T                       (W2 [E][N][K], Y fp32 [rows][N])
+// ("Mistral 8x7B SMoE architecture deep dive", section 3.1; "Mixtral and MoE
+// architecture", FeedForward listing; the fused gate/up layout of the numpy
+// listing in "Trillion-parameter MoE ... 7 expert configs measured" is what
+// pairing W1 and W3 tiles in one workgroup follows.)
+//
+// Tiling.  A workgroup of 256 threads (4 wavefronts, WM x WN) owns a BM x BNB
+// tile, where BNB counts B rows: for SWIGLU the B tile interleaves 32-row
+// blocks of W1 and W3 for the same output columns, so a wave holds the W1 and
+// W3 accumulators of an output element in the same lane and register and the
+// SiLU * mul epilogue needs no data movement.  K is streamed in BK slices
+// through double-buffered LDS (one barrier per slice; the next slice's global
+// loads are in flight while the current one feeds the MFMAs).  LDS rows are
+// padded by 16 bytes, which keeps the 16-byte fragment reads conflict-free.
+//
+// Operands: both A and B are K-contiguous ([rows][K] and [N][K]), the layout
+// in which every lane of a 32x32 MFMA reads 16 consecutive bytes of K.
+//   bf16: v_mfma_f32_32x32x16_bf16, one per 16-wide K step.
+//   fp32: v_mfma_f32_32x32x2_f32, eight per 16-wide K step; lane group g feeds
+//         K indices g*8 + i to the i-th MFMA (A and B use the same order).
+//
+// Tile map.  blockIdx.x is the N tile; blockIdx.y is a global m-tile index g.
+// mtile_off[e] is the prefix of ceil(count_e / BM), so g belongs to the expert
+// e with mtile_off[e] <= g < mtile_off[e+1]; indices past mtile_off[E] exit.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+template <typename T> struct MfmaTraits;
+template <> struct MfmaTraits<bf16_t> {
+  static constexpr int BK = 64;  // 128 bytes of K per LDS row
+  static constexpr int FRAG_U4 = 1;  // uint4 per lane per 16-wide K step
+  __device__ __forceinline__ static void mma(const uint4 *a, const uint4 *b, f32x16_v &c) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_v, a[0]),
+                                                __builtin_bit_cast(bf16x8_v, b[0]), c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static void store(bf16_t *p, size_t i, float v) {
+    p[i] = f32_to_bf16(v);
+  }
+};
+template <> struct MfmaTraits<float> {
+  static constexpr int BK = 32;
+  static constexpr int FRAG_U4 = 2;
+  __device__ __forceinline__ static void mma(const uint4 *a, const uint4 *b, f32x16_v &c) {
+    const float *af = reinterpret_cast<const float *>(a);
+    const float *bf = reinterpret_cast<const float *>(b);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i], bf[i], c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static void store(float *p, size_t i, float v) { p[i] = v; }
+};
+
+constexpr int GM_THREADS = 256;
+
+template <typename T, int BM, int BNB, int WM, int WN, bool SWIGLU>
+__global__ __launch_bounds__(GM_THREADS) void grouped_gemm_kernel(
+    const T *__restrict__ A, const T *__restrict__ B1, const T *__restrict__ B3,
+    void *__restrict__ C, const int32_t *__restrict__ seg_off,
+    const int32_t *__restrict__ mtile_off, int G, int N, int K) {
+  constexpr int BK = MfmaTraits<T>::BK;
+  constexpr int ES = sizeof(T);
+  constexpr int CPR = BK * ES / 16;            // 16-byte chunks per tile row (8)
+  constexpr int LDW = (BK * ES + 16) / 16;     // LDS row stride in uint4 (9)
+  constexpr int TM = BM / WM / 32;             // 32-row MFMA blocks per wave
+  constexpr int TN = BNB / WN / 32;            // 32-col MFMA blocks per wave
+  constexpr int A_CH = BM * CPR / GM_THREADS;  // A chunks per thread
+  constexpr int B_CH = BNB * CPR / GM_THREADS;
+  constexpr int FU = MfmaTraits<T>::FRAG_U4;
+  static_assert(!SWIGLU || (TN % 2 == 0), "SwiGLU pairs W1/W3 blocks inside a wave");
+  static_assert(A_CH * GM_THREADS == BM * CPR && B_CH * GM_THREADS == BNB * CPR, "tile/threads");
+
+  __shared__ uint4 lds[2][(BM + BNB) * LDW];
+
+  const int g = blockIdx.y;
+  const int total = mtile_off[G];
+  if (g >= total) return;
+  const int e = upper_segment(mtile_off, G, g);
+  const int row0 = seg_off[e] + (g - mtile_off[e]) * BM;
+  const int rows = min(BM, seg_off[e + 1] - row0);
+  const int NOUT = N;  // output columns
+  const int n0 = blockIdx.x * (SWIGLU ? BNB / 2 : BNB);  // first output column
+
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave, lane = lane_id();
+  const int wm = wave / WN, wn = wave % WN;
+
+  // ---- global source pointers for this thread's chunks (fixed over K) ----
+  const uint4 *srcA[A_CH];
+  const uint4 *srcB[B_CH];
+  int dstA[A_CH], dstB[B_CH];
+  const size_t rowq = (size_t)K * ES / 16;
+#pragma unroll
+  for (int i = 0; i < A_CH; ++i) {
+    int c = tid + i * GM_THREADS;
+    int r = c / CPR, q = c % CPR;
+    int rr = min(r, rows - 1);
+    srcA[i] = reinterpret_cast<const uint4 *>(A) + (size_t)(row0 + rr) * rowq + q;
+    dstA[i] = r * LDW + q;
+  }
+  const size_t bexp = (size_t)e * N * rowq;  // expert offset in uint4
+#pragma unroll
+  for (int i = 0; i < B_CH; ++i) {
+    int c = tid + i * GM_THREADS;
+    int r = c / CPR, q = c % CPR;
+    const T *base;
+    int col;
+    if (SWIGLU) {
+      int rb = r / 32, wnb = rb / TN, j = rb % TN;
+      col = n0 + wnb * (TN / 2) * 32 + (j / 2) * 32 + (r % 32);
+      base = (j & 1) ? B3 : B1;
+    } else {
+      col = n0 + r;
+      base = B1;
+    }
+    col = min(col, N - 1);
+    srcB[i] = reinterpret_cast<const uint4 *>(base) + bexp + (size_t)col * rowq + q;
+    dstB[i] = (BM + r) * LDW + q;
+  }
+
+  f32x16_v acc[TM][TN];
+#pragma unroll
+  for (int a = 0; a < TM; ++a)
+#pragma unroll
+    for (int b = 0; b < TN; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
+
+  uint4 ra[A_CH], rb[B_CH];
+  const int nk = K / BK;
+  auto gload = [&](int kt) {
+    const size_t ko = (size_t)kt * CPR;
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) ra[i] = srcA[i][ko];
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i) rb[i] = srcB[i][ko];
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) lds[buf][dstA[i]] = ra[i];
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i) lds[buf][dstB[i]] = rb[i];
+  };
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+
+  // fragment addressing inside a tile (uint4 units)
+  const int frow = lane & 31;
+  const int fk = (lane >> 5) * FU;  // lane group's first uint4 within a 16-wide K step
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) gload(kt + 1);
+    const uint4 *L = lds[buf];
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int ko = ks * 2 * FU + fk;  // 16-wide K step = 2*FU uint4
+      uint4 af[TM][FU], bfr[TN][FU];
+#pragma unroll
+      for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int u = 0; u < FU; ++u) af[a][u] = L[((wm * TM + a) * 32 + frow) * LDW + ko + u];
+#pragma unroll
+      for (int b = 0; b < TN; ++b)
+#pragma unroll
+        for (int u = 0; u < FU; ++u)
+          bfr[b][u] = L[(BM + (wn * TN + b) * 32 + frow) * LDW + ko + u];
+#pragma unroll
+      for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int b = 0; b < TN; ++b) MfmaTraits<T>::mma(af[a], bfr[b], acc[a][b]);
+    }
+    if (kt + 1 < nk) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue ----
+  const int ccol = lane & 31;
+  const int crow4 = (lane >> 5) * 4;
+#pragma unroll
+  for (int a = 0; a < TM; ++a) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = (wm * TM + a) * 32 + (i / 4) * 8 + crow4 + (i % 4);
+      if (r >= rows) continue;
+      const size_t orow = (size_t)(row0 + r) * NOUT;
+      if (SWIGLU) {
+#pragma unroll
+        for (int q = 0; q < TN / 2; ++q) {
+          const int col = n0 + wn * (TN / 2) * 32 + q * 32 + ccol;
+          if (col < N) {
+            const float h = silu(acc[a][2 * q][i]) * acc[a][2 * q + 1][i];
+            MfmaTraits<T>::store(reinterpret_cast<T *>(C), orow + col, h);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int b = 0; b < TN; ++b) {
+          const int col = n0 + (wn * TN + b) * 32 + ccol;
+          if (col < N) reinterpret_cast<float *>(C)[orow + col] = acc[a][b][i];
+        }
+      }
+    }
+  }
+}
+
+template <typename T, int BM, int BNB, int WM, int WN, bool SWIGLU>
+hipError_t launch_one(const void *A, const void *B1, const void *B3, void *C,
+                      const int32_t *seg_off, const int32_t *mtile_off, int G, int N, int K,
+                      int max_mtiles, hipStream_t s) {
+  const int cols = SWIGLU ? BNB / 2 : BNB;
+  dim3 grid((N + cols - 1) / cols, max_mtiles);
+  hipLaunchKernelGGL((grouped_gemm_kernel<T, BM, BNB, WM, WN, SWIGLU>), grid, dim3(GM_THREADS),
+                     0, s, (const T *)A, (const T *)B1, (const T *)B3, C, seg_off, mtile_off, G,
+                     N, K);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int gemm_bm() { return 128; }
+
+hipError_t launch_gemm_swiglu(int dtype, const void *A, const void *W1, const void *W3, void *H,
+                              const int32_t *seg_off, const int32_t *mtile_off, int G, int N,
+                              int K, int max_mtiles, hipStream_t s) {
+  if (max_mtiles <= 0) return hipSuccess;
+  if (dtype == 1)
+    return launch_one<bf16_t, 128, 128, 2, 2, true>(A, W1, W3, H, seg_off, mtile_off, G, N, K,
+                                                    max_mtiles, s);
+  return launch_one<float, 128, 128, 2, 2, true>(A, W1, W3, H, seg_off, mtile_off, G, N, K,
+                                                 max_mtiles, s);
+}
+
+hipError_t launch_gemm_down(int dtype, const void *A, const void *W2, float *Y,
+                            const int32_t *seg_off, const int32_t *mtile_off, int G, int N, int K,
+                            int max_mtiles, hipStream_t s) {
+  if (max_mtiles <= 0) return hipSuccess;
+  if (dtype == 1)
+    return launch_one<bf16_t, 128, 128, 2, 2, false>(A, W2, nullptr, Y, seg_off, mtile_off, G,
+                                                     N, K, max_mtiles, s);
+  return launch_one<float, 128, 128, 2, 2, false>(A, W2, nullptr, Y, seg_off, mtile_off, G, N,
+                                                  K, max_mtiles, s);
+}
+
+}  // namespace moe

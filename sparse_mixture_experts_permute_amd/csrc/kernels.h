@@ -1,0 +1,31 @@
+// Launchers of the HIP kernels (host-side declarations, internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+hipError_t launch_router(int dtype, const void *x, const void *Wg, const float *bias, int T,
+                         int d, int E, int k, int32_t *idx, float *gate, float *logits,
+                         hipStream_t s);
+
+int permute_nblocks(int P);
+hipError_t launch_permute(const int32_t *idx, int T, int E, int k, int bm0, int bm1,
+                          int32_t *blk, int32_t *counts, int32_t *offsets, int32_t *perm,
+                          int32_t *inv, int32_t *mtiles0, int32_t *mtiles1,
+                          int32_t *shared_seg, hipStream_t s);
+hipError_t launch_gather(const void *x, const int32_t *perm, int P, int k, int d, int esize,
+                         void *xp, hipStream_t s);
+
+int gemm_bm();
+hipError_t launch_gemm_swiglu(int dtype, const void *A, const void *W1, const void *W3, void *H,
+                              const int32_t *seg_off, const int32_t *mtile_off, int G, int N,
+                              int K, int max_mtiles, hipStream_t s);
+hipError_t launch_gemm_down(int dtype, const void *A, const void *W2, float *Y,
+                            const int32_t *seg_off, const int32_t *mtile_off, int G, int N, int K,
+                            int max_mtiles, hipStream_t s);
+
+hipError_t launch_combine(int dtype, const float *Yp, const float *Ys, const int32_t *inv,
+                          const float *gate, int T, int k, int d, void *y, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,162 @@
+// Grouping of (token, slot) pairs by expert: histogram -> prefix scan ->
+// stable scatter ("Chapter 10 MoE", section 10.4 groups an expert's tokens in
+// ascending order; the numpy listing of "Trillion-parameter MoE ... 7 expert
+// configs measured" builds the same per-expert row lists).
+//
+// The result is the stable counting sort of the flat pair ids p = t*k + j by
+// expert, independent of scheduling: ranks come from block-local histograms
+// plus block-prefix bases and from in-wave ballots, never from the order in
+// which atomics land.
+//
+//   hist    : block b counts the experts of pairs [256b, 256b+256) -> blk[b][e]
+//   scan    : one block turns blk[][] into per-block bases, counts, offsets and
+//             the m-tile prefix used by the grouped GEMM tile maps
+//   scatter : block b re-reads its pairs; a pair's slot is
+//             base[b][e] + (pairs of e in earlier waves of b) + (rank in wave)
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int PM_CHUNK = 256;  // pairs per block == threads per block
+
+__global__ __launch_bounds__(PM_CHUNK) void permute_hist_kernel(const int32_t *__restrict__ idx,
+                                                                int P, int E,
+                                                                int32_t *__restrict__ blk) {
+  __shared__ int h[256];
+  const int tid = threadIdx.x;
+  if (tid < E) h[tid] = 0;
+  __syncthreads();
+  const int p = blockIdx.x * PM_CHUNK + tid;
+  if (p < P) {
+    const int e = idx[p];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&h[e], 1);  // out-of-range ids are not placed
+  }
+  __syncthreads();
+  if (tid < E) blk[(size_t)blockIdx.x * E + tid] = h[tid];
+}
+
+// One block of 256 threads; thread e owns expert e.
+__global__ __launch_bounds__(256) void permute_scan_kernel(
+    int32_t *__restrict__ blk, int nb, int E, int P, int T, int bm0, int bm1,
+    int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int32_t *__restrict__ mtiles0,
+    int32_t *__restrict__ mtiles1, int32_t *__restrict__ shared_seg) {
+  __shared__ int s0[256], s1[256], s2[256];
+  const int e = threadIdx.x;
+  int total = 0;
+  if (e < E)
+    for (int b = 0; b < nb; ++b) total += blk[(size_t)b * E + e];
+  s0[e] = e < E ? total : 0;
+  s1[e] = e < E ? (total + bm0 - 1) / bm0 : 0;
+  s2[e] = e < E ? (total + bm1 - 1) / bm1 : 0;
+  __syncthreads();
+  // inclusive Hillis-Steele scans over the experts (256 entries)
+  for (int off = 1; off < 256; off <<= 1) {
+    int a0 = e >= off ? s0[e - off] : 0;
+    int a1 = e >= off ? s1[e - off] : 0;
+    int a2 = e >= off ? s2[e - off] : 0;
+    __syncthreads();
+    s0[e] += a0;
+    s1[e] += a1;
+    s2[e] += a2;
+    __syncthreads();
+  }
+  if (e < E) {
+    const int excl = s0[e] - total;
+    counts[e] = total;
+    offsets[e] = excl;
+    mtiles0[e] = s1[e] - (total + bm0 - 1) / bm0;
+    mtiles1[e] = s2[e] - (total + bm1 - 1) / bm1;
+    int run = excl;
+    for (int b = 0; b < nb; ++b) {
+      int c = blk[(size_t)b * E + e];
+      blk[(size_t)b * E + e] = run;
+      run += c;
+    }
+  }
+  if (e == 0) {
+    offsets[E] = s0[255];  // == P when every id is in range
+    mtiles0[E] = s1[255];
+    mtiles1[E] = s2[255];
+    // the shared expert is one segment of all T tokens
+    shared_seg[0] = 0;
+    shared_seg[1] = T;
+    shared_seg[2] = 0;
+    shared_seg[3] = (T + bm0 - 1) / bm0;
+    shared_seg[4] = 0;
+    shared_seg[5] = (T + bm1 - 1) / bm1;
+  }
+}
+
+__global__ __launch_bounds__(PM_CHUNK) void permute_scatter_kernel(
+    const int32_t *__restrict__ idx, int P, int E, const int32_t *__restrict__ base,
+    int32_t *__restrict__ perm, int32_t *__restrict__ inv) {
+  __shared__ int wc[PM_CHUNK / kWave][256];
+  const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
+  for (int i = tid; i < (PM_CHUNK / kWave) * 256; i += PM_CHUNK) (&wc[0][0])[i] = 0;
+  __syncthreads();
+  const int p = blockIdx.x * PM_CHUNK + tid;
+  const int ev = p < P ? idx[p] : -1;
+  const bool valid = (unsigned)ev < (unsigned)E;
+  const int e = valid ? ev : 0;
+  // lanes holding the same expert: intersect ballots over the 8 bits of e
+  uint64_t same = __ballot(valid);
+#pragma unroll
+  for (int bit = 0; bit < 8; ++bit) {
+    uint64_t ones = __ballot(valid && ((e >> bit) & 1));
+    same &= ((e >> bit) & 1) ? ones : ~ones;
+  }
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  const int rank = __popcll(same & below);
+  if (valid && rank == 0) wc[w][e] = __popcll(same);
+  __syncthreads();
+  if (valid) {
+    int pos = base[(size_t)blockIdx.x * E + e] + rank;
+    for (int w2 = 0; w2 < w; ++w2) pos += wc[w2][e];
+    perm[pos] = p;
+    inv[p] = pos;
+  }
+}
+
+// Xp[s][:] = x[perm[s] / k][:]; one block copies 4 rows with 16-byte accesses.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint4 *__restrict__ x,
+                                                          const int32_t *__restrict__ perm,
+                                                          int P, int k, int rowq,
+                                                          uint4 *__restrict__ xp) {
+  const int r0 = blockIdx.x * 4;
+  for (int r = r0; r < r0 + 4 && r < P; ++r) {
+    const size_t src = (size_t)(perm[r] / k) * rowq;
+    const size_t dst = (size_t)r * rowq;
+    for (int q = threadIdx.x; q < rowq; q += 256) xp[dst + q] = x[src + q];
+  }
+}
+
+}  // namespace
+
+int permute_nblocks(int P) { return (P + PM_CHUNK - 1) / PM_CHUNK; }
+
+hipError_t launch_permute(const int32_t *idx, int T, int E, int k, int bm0, int bm1,
+                          int32_t *blk, int32_t *counts, int32_t *offsets, int32_t *perm,
+                          int32_t *inv, int32_t *mtiles0, int32_t *mtiles1,
+                          int32_t *shared_seg, hipStream_t s) {
+  const int P = T * k;
+  const int nb = permute_nblocks(P);
+  hipLaunchKernelGGL(permute_hist_kernel, dim3(nb), dim3(PM_CHUNK), 0, s, idx, P, E, blk);
+  hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(256), 0, s, blk, nb, E, P, T, bm0, bm1,
+                     counts, offsets, mtiles0, mtiles1, shared_seg);
+  hipLaunchKernelGGL(permute_scatter_kernel, dim3(nb), dim3(PM_CHUNK), 0, s, idx, P, E, blk,
+                     perm, inv);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const void *x, const int32_t *perm, int P, int k, int d, int esize,
+                         void *xp, hipStream_t s) {
+  const int rowq = d * esize / 16;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3((P + 3) / 4), dim3(256), 0, s,
+                     (const uint4 *)x, perm, P, k, rowq, (uint4 *)xp);
+  return hipGetLastError();
+}
+
+}  // namespace moe

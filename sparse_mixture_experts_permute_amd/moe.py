@@ -1,0 +1,217 @@
+"""Thin torch-facing binding of the C ABI in ``include/moe_mi355x.h``.
+
+Argument marshalling only: every step of the layer runs in the HIP library
+``libmoe_mi355x.so``.  Tensors must be contiguous and on the current HIP
+device; work is enqueued on torch's current stream.  There is no fallback: if
+the library is missing or the device is not a gfx950 GPU the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
+
+MOE_F32, MOE_BF16 = 0, 1
+NSTAGE_EVENTS = 8
+STAGES = ("router", "permute", "gather", "gemm_swiglu", "gemm_down", "shared_expert", "combine")
+WS_FIELDS = ("logits", "idx", "gate", "counts", "offsets", "perm", "inv")
+
+_lib = None
+
+
+class MoEError(RuntimeError):
+    pass
+
+
+def lib():
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise MoEError(f"HIP library not built: {LIB_PATH} "
+                           "(run python -m sparse_mixture_experts_permute_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        L.moe_route.argtypes = [vp, vp, vp, i, i, i, i, i, vp, vp, vp, vp]
+        L.moe_route.restype = i
+        L.moe_permute_workspace_bytes.argtypes = [i, i, i]
+        L.moe_permute_workspace_bytes.restype = sz
+        L.moe_permute.argtypes = [vp, i, i, i, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_permute.restype = i
+        L.moe_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+        L.moe_workspace_bytes.restype = sz
+        L.moe_workspace_offsets.argtypes = [i, i, i, i, i, i, i, ctypes.POINTER(sz)]
+        L.moe_workspace_offsets.restype = i
+        L.moe_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp,
+                                  sz, vp, vp]
+        L.moe_forward.restype = i
+        L.moe_forward_timed.argtypes = L.moe_forward.argtypes + [vp]
+        L.moe_forward_timed.restype = i
+        L.moe_strerror.argtypes = [i]
+        L.moe_strerror.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise MoEError(f"{what}: {lib().moe_strerror(rc).decode()} (status {rc})")
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    if t.dtype == torch.float32:
+        return MOE_F32
+    raise MoEError(f"unsupported dtype {t.dtype}")
+
+
+def _p(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise MoEError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def tensor_from_numpy(a: np.ndarray, device="cuda") -> torch.Tensor:
+    """numpy -> device tensor; uint16 arrays are taken as bf16 bit patterns."""
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(a).to(device)
+
+
+def tensor_to_numpy(t: torch.Tensor) -> np.ndarray:
+    """device tensor -> numpy; bf16 comes back as uint16 bit patterns."""
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def route(x: torch.Tensor, Wg: torch.Tensor, k: int, bias: torch.Tensor | None = None):
+    """(idx [T][k] int32, gate [T][k] fp32, logits [T][E] fp32)."""
+    T, d = x.shape
+    E = Wg.shape[0]
+    idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    gate = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    _check(lib().moe_route(_p(x), _p(Wg), _p(bias), T, d, E, k, _dt(x), _p(idx), _p(gate),
+                           _p(logits), _stream()), "moe_route")
+    return idx, gate, logits
+
+
+def permute(idx: torch.Tensor, E: int):
+    """(counts [E], offsets [E+1], perm [T*k], inv [T*k]), all int32."""
+    T, k = idx.shape
+    dev = idx.device
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(T * k, dtype=torch.int32, device=dev)
+    inv = torch.empty(T * k, dtype=torch.int32, device=dev)
+    nbytes = lib().moe_permute_workspace_bytes(T, E, k)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    _check(lib().moe_permute(_p(idx), T, E, k, _p(counts), _p(offsets), _p(perm), _p(inv),
+                             _p(ws), nbytes, _stream()), "moe_permute")
+    return counts, offsets, perm, inv
+
+
+def workspace_bytes(T, d, d_ff, E, k, d_ff_shared=0, dtype=MOE_BF16) -> int:
+    n = lib().moe_workspace_bytes(T, d, d_ff, E, k, d_ff_shared, dtype)
+    if n == 0:
+        raise MoEError("invalid layer shape")
+    return n
+
+
+def workspace_offsets(T, d, d_ff, E, k, d_ff_shared=0, dtype=MOE_BF16) -> dict:
+    arr = (ctypes.c_size_t * len(WS_FIELDS))()
+    _check(lib().moe_workspace_offsets(T, d, d_ff, E, k, d_ff_shared, dtype, arr),
+           "moe_workspace_offsets")
+    return dict(zip(WS_FIELDS, list(arr)))
+
+
+class MoELayer:
+    """One layer's weights plus a reusable workspace.
+
+    W1, W3 [E][d_ff][d]; W2 [E][d][d_ff]; Wg [E][d]; optional bias [E] fp32;
+    optional shared (Ws1 [dffs][d], Ws3 [dffs][d], Ws2 [d][dffs]).
+    """
+
+    def __init__(self, Wg, W1, W3, W2, k, bias=None, shared=None):
+        self.Wg, self.W1, self.W3, self.W2, self.k, self.bias = Wg, W1, W3, W2, k, bias
+        self.E, self.d_ff, self.d = W1.shape
+        self.shared = shared
+        self.d_ff_shared = shared[0].shape[0] if shared is not None else 0
+        self.dtype = _dt(W1)
+        self._ws = None
+        self._ws_T = -1
+
+    def workspace(self, T):
+        n = workspace_bytes(T, self.d, self.d_ff, self.E, self.k, self.d_ff_shared, self.dtype)
+        if self._ws is None or self._ws.numel() < n:
+            self._ws = torch.empty(n, dtype=torch.uint8, device=self.W1.device)
+        return self._ws, n
+
+    def __call__(self, x: torch.Tensor, y: torch.Tensor | None = None) -> torch.Tensor:
+        shape = x.shape
+        x2 = x.reshape(-1, self.d)  # batch dims flattened into tokens
+        T = x2.shape[0]
+        if y is None:
+            y = torch.empty_like(x2)
+        ws, n = self.workspace(T)
+        Ws1, Ws3, Ws2 = self.shared if self.shared is not None else (None, None, None)
+        _check(lib().moe_forward(_p(x2), _p(self.Wg), _p(self.bias), _p(self.W1), _p(self.W3),
+                                 _p(self.W2), _p(Ws1), _p(Ws3), _p(Ws2), self.d_ff_shared, T,
+                                 self.E, self.k, self.d, self.d_ff, self.dtype, _p(ws), n, _p(y),
+                                 _stream()), "moe_forward")
+        return y.reshape(shape)
+
+    def timed(self, x: torch.Tensor, y: torch.Tensor, events) -> torch.Tensor:
+        """Same as a call, recording `events` (NSTAGE_EVENTS torch.cuda.Event,
+        already created by a record) at the stage boundaries on the stream."""
+        T = x.shape[0]
+        ws, n = self.workspace(T)
+        Ws1, Ws3, Ws2 = self.shared if self.shared is not None else (None, None, None)
+        handles = (ctypes.c_void_p * NSTAGE_EVENTS)(*[ctypes.c_void_p(e.cuda_event)
+                                                      for e in events])
+        _check(lib().moe_forward_timed(_p(x), _p(self.Wg), _p(self.bias), _p(self.W1),
+                                       _p(self.W3), _p(self.W2), _p(Ws1), _p(Ws3), _p(Ws2),
+                                       self.d_ff_shared, T, self.E, self.k, self.d, self.d_ff,
+                                       self.dtype, _p(ws), n, _p(y), _stream(), handles),
+               "moe_forward_timed")
+        return y
+
+    def intermediates(self, T) -> dict:
+        """Views of the routing intermediates of the last call with T tokens."""
+        off = workspace_offsets(T, self.d, self.d_ff, self.E, self.k, self.d_ff_shared,
+                                self.dtype)
+        ws = self._ws
+        P = T * self.k
+
+        def view(name, n, dtype):
+            o = off[name]
+            return ws[o:o + n * 4].view(dtype)
+
+        return dict(logits=view("logits", T * self.E, torch.float32).view(T, self.E),
+                    idx=view("idx", P, torch.int32).view(T, self.k),
+                    gate=view("gate", P, torch.float32).view(T, self.k),
+                    counts=view("counts", self.E, torch.int32),
+                    offsets=view("offsets", self.E + 1, torch.int32),
+                    perm=view("perm", P, torch.int32), inv=view("inv", P, torch.int32))
+
+
+def forward(x, Wg, W1, W3, W2, k, bias=None, shared=None):
+    """y = MoE(x) for x [..., d] (allocates its workspace)."""
+    return MoELayer(Wg, W1, W3, W2, k, bias, shared)(x)

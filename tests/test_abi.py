@@ -1,0 +1,99 @@
+"""The C-ABI library loads and exports what include/*.h declares; host-side
+argument checks reject bad calls before touching a device (CPU only)."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = glob.glob(os.path.join(ROOT, "include", "*.h"))
+
+
+def declared_functions():
+    names = set()
+    for h in HEADERS:
+        src = open(h).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", "", src)
+        for m in re.finditer(r"\b(moe_[a-z0-9_]+)\s*\(", src):
+            names.add(m.group(1))
+    return sorted(names)
+
+
+@pytest.fixture(scope="module")
+def L():
+    from sparse_mixture_experts_permute_amd import moe
+    if not os.path.exists(moe.LIB_PATH):
+        from sparse_mixture_experts_permute_amd import build
+        build.build(verbose=False)
+    return moe.lib()
+
+
+def test_header_declares_entry_points():
+    names = declared_functions()
+    for n in ("moe_route", "moe_permute", "moe_forward", "moe_workspace_bytes", "moe_strerror"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for n in declared_functions():
+        assert hasattr(L, n), f"{n} declared but not exported"
+
+
+def test_strerror(L):
+    for code in (0, -1, -2, -3, -4, -5):
+        assert L.moe_strerror(code)
+    assert b"unknown" in L.moe_strerror(-99)
+
+
+def test_workspace_sizes(L):
+    from sparse_mixture_experts_permute_amd import moe
+    n = L.moe_workspace_bytes(512, 512, 4096, 8, 2, 0, moe.MOE_F32)
+    P = 1024
+    # at least the permuted activations, hidden and down-projection buffers
+    assert n >= P * 512 * 4 + P * 4096 * 4 + P * 512 * 4
+    assert n % 256 == 0
+    assert L.moe_workspace_bytes(512, 512, 4096, 8, 9, 0, moe.MOE_F32) == 0  # k > E
+    assert L.moe_workspace_bytes(512, 500, 4096, 8, 2, 0, moe.MOE_F32) == 0  # d % 64
+    assert L.moe_workspace_bytes(512, 512, 4096, 8, 2, 0, 7) == 0  # dtype
+    assert L.moe_workspace_bytes(16, 512, 4096, 257, 2, 0, moe.MOE_BF16) == 0  # E > 256
+    off = moe.workspace_offsets(100, 512, 1024, 8, 2, 0, moe.MOE_BF16)
+    assert list(off) == list(moe.WS_FIELDS)
+    assert all(v % 256 == 0 for v in off.values())
+    assert sorted(off.values()) == list(off.values())
+
+
+def test_argument_errors_before_launch(L):
+    vp = ctypes.c_void_p
+    fake = vp(0x1000)
+    # bad dtype
+    assert L.moe_route(fake, fake, None, 4, 64, 8, 2, 9, fake, fake, None, None) == -2
+    # k > E, k < 1, E > 256, d not a multiple of 64
+    assert L.moe_route(fake, fake, None, 4, 64, 8, 9, 1, fake, fake, None, None) == -1
+    assert L.moe_route(fake, fake, None, 4, 64, 8, 0, 1, fake, fake, None, None) == -1
+    assert L.moe_route(fake, fake, None, 4, 64, 300, 2, 1, fake, fake, None, None) == -1
+    assert L.moe_route(fake, fake, None, 4, 65, 8, 2, 1, fake, fake, None, None) == -1
+    # missing required pointers
+    assert L.moe_route(None, fake, None, 4, 64, 8, 2, 1, fake, fake, None, None) == -1
+    # T = 0 is a no-op
+    assert L.moe_route(None, None, None, 0, 64, 8, 2, 1, None, None, None, None) == 0
+    # forward: shared-expert pointers inconsistent with d_ff_shared
+    args = [fake, fake, None, fake, fake, fake, fake, None, None, 64, 4, 8, 2, 64, 64, 1,
+            fake, 1 << 30, vp(0x2000), None]
+    assert L.moe_forward(*args) == -1
+    # forward: workspace too small
+    args = [fake, fake, None, fake, fake, fake, None, None, None, 0, 4, 8, 2, 64, 64, 1,
+            vp(0x100000), 16, vp(0x2000), None]
+    assert L.moe_forward(*args) == -3
+    # forward: misaligned workspace
+    args[16] = vp(0x100010)
+    args[17] = 1 << 40
+    assert L.moe_forward(*args) == -3
+    # forward: y aliasing x
+    args = [fake, fake, None, fake, fake, fake, None, None, None, 0, 4, 8, 2, 64, 64, 1,
+            vp(0x100000), 1 << 40, fake, None]
+    assert L.moe_forward(*args) == -1
+    # permute: too-small workspace
+    assert L.moe_permute(fake, 4, 8, 2, fake, fake, fake, fake, vp(0x100000), 8, None) == -3
