@@ -28,6 +28,8 @@ bool dims_ok(int T, int d, int d_ff, int E, int k, int dffs) {
   if (dffs < 0 || dffs % 64) return false;
   if ((long long)T * k >= (1LL << 31)) return false;
   if ((long long)T * k * (long long)(d > d_ff ? d : d_ff) >= (1LL << 40)) return false;
+  // one expert's weight matrix is addressed with 32-bit byte offsets
+  if ((long long)d * d_ff >= (1LL << 31) || (long long)d * dffs >= (1LL << 31)) return false;
   return true;
 }
 
@@ -140,7 +142,7 @@ int moe_permute(const int32_t *idx, int T, int E, int k, int32_t *counts, int32_
   int32_t *mt0 = (int32_t *)(w + align_up(nb * E * 4));
   int32_t *mt1 = mt0 + align_up((size_t)(E + 1) * 4 + 32) / 4;
   int32_t *sh = mt1 + align_up((size_t)(E + 1) * 4 + 32) / 4;
-  const int bm = moe::gemm_bm();
+  const int bm = moe::gemm_bm(MOE_BF16);
   return launched(moe::launch_permute(idx, T, E, k, bm, bm, blk, counts, offsets, perm, inv, mt0,
                                       mt1, sh, (hipStream_t)stream));
 }
@@ -185,7 +187,7 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
   hipStream_t s = (hipStream_t)stream;
   void *ws = workspace;
   const int P = T * k;
-  const int bm = moe::gemm_bm();
+  const int bm = moe::gemm_bm(dtype);
   float *logits = at<float>(ws, L.off[F_LOGITS]);
   int32_t *idx = at<int32_t>(ws, L.off[F_IDX]);
   float *gate = at<float>(ws, L.off[F_GATE]);

@@ -41,6 +41,15 @@ template <> struct Elem<bf16_t> {
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
 
+// 16 bytes per lane from global memory straight into LDS.  `lds` must be the
+// same for every lane of the wavefront; lane l's bytes land at lds + 16*l.
+__device__ __forceinline__ void global_to_lds16(const void *g, uint4 *lds) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+}
+
+// Wait until this wavefront's outstanding vector-memory operations are done.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x3f70); }
+
 __device__ __forceinline__ float silu(float a) { return a / (1.0f + __expf(-a)); }
 
 // First index i in [0, n) with a[i+1] > g, for non-decreasing a[0..n] with a[0] <= g.

@@ -213,6 +213,183 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 variant with direct global->LDS loads (global_load_lds_dwordx4).
+//
+// Each wavefront instruction moves 64 x 16 bytes into 1 KB of contiguous LDS:
+// 8 tile rows of 128 bytes (64 bf16 of K).  Rows are not padded; instead lane
+// l of an instruction fetches global 16-byte chunk (l % 8) ^ f(row) of its row,
+// with f(row) = (row >> 1) & 7, so LDS chunk c of row r holds global chunk
+// c ^ f(r).  A fragment read (16 lanes, 16 consecutive rows, one global chunk)
+// then touches 16 distinct 16-byte slots modulo 256 bytes: conflict-free on
+// the 64 LDS banks.  Two stages of (BM + BNB) x 128 bytes; the loads of slice
+// kt+1 run while slice kt feeds the MFMAs, with no staging registers.
+// ---------------------------------------------------------------------------
+template <int BM, int BNB, bool SWIGLU>
+__global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
+    const bf16_t *__restrict__ A, const bf16_t *__restrict__ B1, const bf16_t *__restrict__ B3,
+    void *__restrict__ C, const int32_t *__restrict__ seg_off,
+    const int32_t *__restrict__ mtile_off, int G, int N, int K) {
+  constexpr int WM = 2, WN = 2;
+  constexpr int TM = BM / WM / 32, TN = BNB / WN / 32;
+  constexpr int ROWS = BM + BNB;          // tile rows per stage (A then B)
+  constexpr int STAGE_U4 = ROWS * 8;      // uint4 per stage
+  static_assert(!SWIGLU || (TN % 2 == 0), "SwiGLU pairs W1/W3 blocks inside a wave");
+  static_assert(BM % 32 == 0 && BNB % 32 == 0, "rows per stage must split over 4 waves");
+
+  __shared__ uint4 st0[STAGE_U4];
+  __shared__ uint4 st1[STAGE_U4];
+
+  const int g = blockIdx.y;
+  const int total = mtile_off[G];
+  if (g >= total) return;
+  const int e = upper_segment(mtile_off, G, g);
+  const int row0 = seg_off[e] + (g - mtile_off[e]) * BM;
+  const int rows = min(BM, seg_off[e + 1] - row0);
+  const int n0 = blockIdx.x * (SWIGLU ? BNB / 2 : BNB);
+
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave, lane = lane_id();
+  const int wm = wave / WN, wn = wave % WN;
+
+  // Per-instruction global byte offsets (relative to uniform bases).  Wave w
+  // loads A blocks w*IA .. w*IA+IA-1 and B blocks w*IB .. w*IB+IB-1 (8 rows
+  // each), so whether an instruction reads A, W1 or W3 is fixed per j.
+  constexpr int IA = BM / 32, IB = BNB / 32;  // instructions per wave per stage
+  const char *abase = reinterpret_cast<const char *>(A) + (size_t)row0 * K * 2;
+  const size_t eoff = (size_t)e * N * K * 2;
+  const char *b1base = reinterpret_cast<const char *>(B1) + eoff;
+  const char *b3base = SWIGLU ? reinterpret_cast<const char *>(B3) + eoff : b1base;
+  uint32_t aoff[IA], boff[IB];
+  const int lrow = lane >> 3, lchunk = lane & 7;
+#pragma unroll
+  for (int j = 0; j < IA; ++j) {
+    const int r = (wave * IA + j) * 8 + lrow;
+    const int gch = lchunk ^ ((r >> 1) & 7);
+    aoff[j] = (uint32_t)min(r, rows - 1) * K * 2 + gch * 16;
+  }
+#pragma unroll
+  for (int j = 0; j < IB; ++j) {
+    const int br = (wave * IB + j) * 8 + lrow;
+    const int gch = lchunk ^ ((br >> 1) & 7);
+    int col;
+    if (SWIGLU) {
+      // 32-row blocks alternate W1 / W3 for the same 32 output columns
+      const int rb = br / 32, wnb = rb / TN, jj = rb % TN;
+      col = n0 + wnb * (TN / 2) * 32 + (jj / 2) * 32 + (br % 32);
+    } else {
+      col = n0 + br;
+    }
+    boff[j] = (uint32_t)min(col, N - 1) * K * 2 + gch * 16;
+  }
+  // B block parity: block (wave*IB + j)/4 is odd (a W3 block) iff (j/4) is odd,
+  // because IB is a multiple of 8
+  static_assert(!SWIGLU || IB % 8 == 0, "W1/W3 choice must be fixed per instruction");
+  auto issue = [&](uint4 *stage, int kt) {
+    const uint32_t ko = (uint32_t)kt * 128;
+#pragma unroll
+    for (int j = 0; j < IA; ++j)
+      global_to_lds16(abase + aoff[j] + ko, stage + (wave * IA + j) * 64);
+#pragma unroll
+    for (int j = 0; j < IB; ++j) {
+      const char *bb = (SWIGLU && ((j / 4) & 1)) ? b3base : b1base;
+      global_to_lds16(bb + boff[j] + ko, stage + BM * 8 + (wave * IB + j) * 64);
+    }
+  };
+
+  f32x16_v acc[TM][TN];
+#pragma unroll
+  for (int a = 0; a < TM; ++a)
+#pragma unroll
+    for (int b = 0; b < TN; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
+
+  // fragment addressing: row part and the swizzled chunk of each 16-wide K step
+  const int frow = lane & 31;
+  const int xf = (frow >> 1) & 7;
+  int cidx[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) cidx[ks] = (ks * 2 + (lane >> 5)) ^ xf;
+  auto compute = [&](const uint4 *stage) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      uint4 af[TM], bfr[TN];
+#pragma unroll
+      for (int a = 0; a < TM; ++a) af[a] = stage[((wm * TM + a) * 32 + frow) * 8 + cidx[ks]];
+#pragma unroll
+      for (int b = 0; b < TN; ++b)
+        bfr[b] = stage[(BM + (wn * TN + b) * 32 + frow) * 8 + cidx[ks]];
+#pragma unroll
+      for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int b = 0; b < TN; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8_v, af[a]), __builtin_bit_cast(bf16x8_v, bfr[b]),
+              acc[a][b], 0, 0, 0);
+    }
+  };
+
+  // Two-stage pipeline; the loop body has no early exit so the accumulators
+  // stay in place, and an odd final slice is handled after the loop.
+  const int nk = K / 64;
+  issue(st0, 0);
+  wait_vmem();
+  __syncthreads();
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    issue(st1, kt + 1);
+    compute(st0);
+    wait_vmem();
+    __syncthreads();
+    if (kt + 2 < nk) issue(st0, kt + 2);
+    compute(st1);
+    wait_vmem();
+    __syncthreads();
+  }
+  if (kt < nk) compute(st0);
+
+  // ---- epilogue ----
+  const int ccol = lane & 31;
+  const int crow4 = (lane >> 5) * 4;
+#pragma unroll
+  for (int a = 0; a < TM; ++a) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = (wm * TM + a) * 32 + (i / 4) * 8 + crow4 + (i % 4);
+      if (r >= rows) continue;
+      const size_t orow = (size_t)(row0 + r) * N;
+      if (SWIGLU) {
+#pragma unroll
+        for (int q = 0; q < TN / 2; ++q) {
+          const int col = n0 + wn * (TN / 2) * 32 + q * 32 + ccol;
+          if (col < N)
+            reinterpret_cast<bf16_t *>(C)[orow + col] =
+                f32_to_bf16(silu(acc[a][2 * q][i]) * acc[a][2 * q + 1][i]);
+        }
+      } else {
+#pragma unroll
+        for (int b = 0; b < TN; ++b) {
+          const int col = n0 + (wn * TN + b) * 32 + ccol;
+          if (col < N) reinterpret_cast<float *>(C)[orow + col] = acc[a][b][i];
+        }
+      }
+    }
+  }
+}
+
+template <int BM, int BNB, bool SWIGLU>
+hipError_t launch_dl(const void *A, const void *B1, const void *B3, void *C,
+                     const int32_t *seg_off, const int32_t *mtile_off, int G, int N, int K,
+                     int max_mtiles, hipStream_t s) {
+  const int cols = SWIGLU ? BNB / 2 : BNB;
+  dim3 grid((N + cols - 1) / cols, max_mtiles);
+  hipLaunchKernelGGL((grouped_gemm_dl_kernel<BM, BNB, SWIGLU>), grid, dim3(GM_THREADS), 0, s,
+                     (const bf16_t *)A, (const bf16_t *)B1, (const bf16_t *)B3, C, seg_off,
+                     mtile_off, G, N, K);
+  return hipGetLastError();
+}
+
 template <typename T, int BM, int BNB, int WM, int WN, bool SWIGLU>
 hipError_t launch_one(const void *A, const void *B1, const void *B3, void *C,
                       const int32_t *seg_off, const int32_t *mtile_off, int G, int N, int K,
@@ -227,15 +404,14 @@ hipError_t launch_one(const void *A, const void *B1, const void *B3, void *C,
 
 }  // namespace
 
-int gemm_bm() { return 128; }
+int gemm_bm(int dtype) { return dtype == 1 ? 256 : 128; }
 
 hipError_t launch_gemm_swiglu(int dtype, const void *A, const void *W1, const void *W3, void *H,
                               const int32_t *seg_off, const int32_t *mtile_off, int G, int N,
                               int K, int max_mtiles, hipStream_t s) {
   if (max_mtiles <= 0) return hipSuccess;
   if (dtype == 1)
-    return launch_one<bf16_t, 128, 128, 2, 2, true>(A, W1, W3, H, seg_off, mtile_off, G, N, K,
-                                                    max_mtiles, s);
+    return launch_dl<256, 256, true>(A, W1, W3, H, seg_off, mtile_off, G, N, K, max_mtiles, s);
   return launch_one<float, 128, 128, 2, 2, true>(A, W1, W3, H, seg_off, mtile_off, G, N, K,
                                                  max_mtiles, s);
 }
@@ -245,8 +421,8 @@ hipError_t launch_gemm_down(int dtype, const void *A, const void *W2, float *Y,
                             int max_mtiles, hipStream_t s) {
   if (max_mtiles <= 0) return hipSuccess;
   if (dtype == 1)
-    return launch_one<bf16_t, 128, 128, 2, 2, false>(A, W2, nullptr, Y, seg_off, mtile_off, G,
-                                                     N, K, max_mtiles, s);
+    return launch_dl<256, 256, false>(A, W2, nullptr, Y, seg_off, mtile_off, G, N, K,
+                                      max_mtiles, s);
   return launch_one<float, 128, 128, 2, 2, false>(A, W2, nullptr, Y, seg_off, mtile_off, G, N,
                                                   K, max_mtiles, s);
 }

@@ -17,7 +17,7 @@ hipError_t launch_permute(const int32_t *idx, int T, int E, int k, int bm0, int 
 hipError_t launch_gather(const void *x, const int32_t *perm, int P, int k, int d, int esize,
                          void *xp, hipStream_t s);
 
-int gemm_bm();
+int gemm_bm(int dtype);
 hipError_t launch_gemm_swiglu(int dtype, const void *A, const void *W1, const void *W3, void *H,
                               const int32_t *seg_off, const int32_t *mtile_off, int G, int N,
                               int K, int max_mtiles, hipStream_t s);
