@@ -142,9 +142,9 @@ int moe_permute(const int32_t *idx, int T, int E, int k, int32_t *counts, int32_
   int32_t *mt0 = (int32_t *)(w + align_up(nb * E * 4));
   int32_t *mt1 = mt0 + align_up((size_t)(E + 1) * 4 + 32) / 4;
   int32_t *sh = mt1 + align_up((size_t)(E + 1) * 4 + 32) / 4;
-  const int bm = moe::gemm_bm(MOE_BF16);
-  return launched(moe::launch_permute(idx, T, E, k, bm, bm, blk, counts, offsets, perm, inv, mt0,
-                                      mt1, sh, (hipStream_t)stream));
+  // the m-tile prefixes are by-products here; any tile height will do
+  return launched(moe::launch_permute(idx, T, E, k, 256, 256, blk, counts, offsets, perm, inv,
+                                      mt0, mt1, sh, (hipStream_t)stream));
 }
 
 size_t moe_workspace_bytes(int T, int d, int d_ff, int E, int k, int d_ff_shared, int dtype) {
@@ -187,7 +187,7 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
   hipStream_t s = (hipStream_t)stream;
   void *ws = workspace;
   const int P = T * k;
-  const int bm = moe::gemm_bm(dtype);
+  const moe::GemmPlan plan = moe::gemm_plan(dtype, d, d_ff, d_ff_shared);
   float *logits = at<float>(ws, L.off[F_LOGITS]);
   int32_t *idx = at<int32_t>(ws, L.off[F_IDX]);
   float *gate = at<float>(ws, L.off[F_GATE]);
@@ -212,28 +212,26 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
   MOE_MARK(0);
   if ((e = moe::launch_router(dtype, x, Wg, bias, T, d, E, k, idx, gate, logits, s))) goto fail;
   MOE_MARK(1);
-  if ((e = moe::launch_permute(idx, T, E, k, bm, bm, blk, counts, offsets, perm, inv, mt0, mt1,
-                               shseg, s)))
+  if ((e = moe::launch_permute(idx, T, E, k, plan.bm1, plan.bm2, blk, counts, offsets, perm, inv,
+                               mt0, mt1, shseg, s)))
     goto fail;
   MOE_MARK(2);
   if ((e = moe::launch_gather(x, perm, P, k, d, (int)esize(dtype), Xp, s))) goto fail;
   MOE_MARK(3);
-  {
-    const int maxmt = (P + bm - 1) / bm + E;
-    if ((e = moe::launch_gemm_swiglu(dtype, Xp, W1, W3, H, offsets, mt0, E, d_ff, d, maxmt, s)))
-      goto fail;
-    MOE_MARK(4);
-    if ((e = moe::launch_gemm_down(dtype, H, W2, Yp, offsets, mt1, E, d, d_ff, maxmt, s)))
-      goto fail;
-    MOE_MARK(5);
-  }
+  if ((e = moe::launch_gemm_swiglu(dtype, plan.dl1, Xp, W1, W3, H, offsets, mt0, E, d_ff, d,
+                                   (P + plan.bm1 - 1) / plan.bm1 + E, s)))
+    goto fail;
+  MOE_MARK(4);
+  if ((e = moe::launch_gemm_down(dtype, plan.dl2, H, W2, Yp, offsets, mt1, E, d, d_ff,
+                                 (P + plan.bm2 - 1) / plan.bm2 + E, s)))
+    goto fail;
+  MOE_MARK(5);
   if (shared) {
-    const int maxmt = (T + bm - 1) / bm;
-    if ((e = moe::launch_gemm_swiglu(dtype, x, Ws1, Ws3, Hs, shseg, shseg + 2, 1, d_ff_shared, d,
-                                     maxmt, s)))
+    if ((e = moe::launch_gemm_swiglu(dtype, plan.dl1, x, Ws1, Ws3, Hs, shseg, shseg + 2, 1,
+                                     d_ff_shared, d, (T + plan.bm1 - 1) / plan.bm1, s)))
       goto fail;
-    if ((e = moe::launch_gemm_down(dtype, Hs, Ws2, Ys, shseg, shseg + 4, 1, d, d_ff_shared,
-                                   maxmt, s)))
+    if ((e = moe::launch_gemm_down(dtype, plan.dl2, Hs, Ws2, Ys, shseg, shseg + 4, 1, d,
+                                   d_ff_shared, (T + plan.bm2 - 1) / plan.bm2, s)))
       goto fail;
   }
   MOE_MARK(6);

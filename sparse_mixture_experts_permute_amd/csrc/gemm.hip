@@ -24,9 +24,8 @@
 //   fp32: v_mfma_f32_32x32x2_f32, eight per 16-wide K step; lane group g feeds
 //         K indices g*8 + i to the i-th MFMA (A and B use the same order).
 //
-// Tile map.  blockIdx.x is the N tile; blockIdx.y is a global m-tile index g.
-// mtile_off[e] is the prefix of ceil(count_e / BM), so g belongs to the expert
-// e with mtile_off[e] <= g < mtile_off[e+1]; indices past mtile_off[E] exit.
+// Tile map.  mtile_off[e] is the prefix of ceil(count_e / BM) over experts;
+// map_tile turns a 1-D workgroup id into (expert, m-tile, n-tile).
 #include "common.h"
 #include "kernels.h"
 
@@ -59,6 +58,35 @@ template <> struct MfmaTraits<float> {
 };
 
 constexpr int GM_THREADS = 256;
+constexpr int NUM_XCD = 8;  // MI355X: 8 accelerator complex dies, each with its own L2
+
+// Workgroup -> (expert, global m-tile, n-tile).  Workgroups are dispatched to
+// the XCDs round-robin (id % 8), so each XCD gets a contiguous chunk of the
+// logical tile order; the logical order is expert-major, then n-tile, with the
+// expert's m-tiles fastest, so the workgroups that share a weight tile run at
+// the same time on the same XCD and its L2 serves the re-reads.  The chunking
+// uses the real tile count (known on the device once the permutation ran);
+// the grid is launched for an upper bound plus NUM_XCD and surplus
+// workgroups exit.
+struct Tile {
+  int e, g, n;
+};
+__device__ __forceinline__ bool map_tile(int hw, const int32_t *mtile_off, int G, int ntn,
+                                         Tile &t) {
+  const int R = ntn * mtile_off[G];
+  const int R8 = (R + NUM_XCD - 1) / NUM_XCD;
+  const int local = hw / NUM_XCD;
+  if (local >= R8) return false;
+  const int L = (hw % NUM_XCD) * R8 + local;
+  if (L >= R) return false;
+  const int e = upper_segment(mtile_off, G, L / ntn);
+  const int rem = L - ntn * mtile_off[e];
+  const int me = mtile_off[e + 1] - mtile_off[e];
+  t.e = e;
+  t.n = rem / me;
+  t.g = mtile_off[e] + rem % me;
+  return true;
+}
 
 template <typename T, int BM, int BNB, int WM, int WN, bool SWIGLU>
 __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_kernel(
@@ -79,14 +107,14 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_kernel(
 
   __shared__ uint4 lds[2][(BM + BNB) * LDW];
 
-  const int g = blockIdx.y;
-  const int total = mtile_off[G];
-  if (g >= total) return;
-  const int e = upper_segment(mtile_off, G, g);
-  const int row0 = seg_off[e] + (g - mtile_off[e]) * BM;
+  constexpr int COLS = SWIGLU ? BNB / 2 : BNB;  // output columns per tile
+  Tile tile;
+  if (!map_tile(blockIdx.x, mtile_off, G, (N + COLS - 1) / COLS, tile)) return;
+  const int e = tile.e;
+  const int row0 = seg_off[e] + (tile.g - mtile_off[e]) * BM;
   const int rows = min(BM, seg_off[e + 1] - row0);
   const int NOUT = N;  // output columns
-  const int n0 = blockIdx.x * (SWIGLU ? BNB / 2 : BNB);  // first output column
+  const int n0 = tile.n * COLS;  // first output column
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = lane_id();
@@ -239,17 +267,16 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
 
   __shared__ uint4 st0[STAGE_U4];
   __shared__ uint4 st1[STAGE_U4];
-
-  const int g = blockIdx.y;
-  const int total = mtile_off[G];
-  if (g >= total) return;
-  const int e = upper_segment(mtile_off, G, g);
-  const int row0 = seg_off[e] + (g - mtile_off[e]) * BM;
+  constexpr int COLS = SWIGLU ? BNB / 2 : BNB;
+  Tile tile;
+  if (!map_tile(blockIdx.x, mtile_off, G, (N + COLS - 1) / COLS, tile)) return;
+  const int e = tile.e;
+  const int row0 = seg_off[e] + (tile.g - mtile_off[e]) * BM;
   const int rows = min(BM, seg_off[e + 1] - row0);
-  const int n0 = blockIdx.x * (SWIGLU ? BNB / 2 : BNB);
+  const int n0 = tile.n * COLS;
 
   const int tid = threadIdx.x;
-  const int wave = tid / kWave, lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = lane_id();
   const int wm = wave / WN, wn = wave % WN;
 
   // Per-instruction global byte offsets (relative to uniform bases).  Wave w
@@ -311,43 +338,96 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
   int cidx[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) cidx[ks] = (ks * 2 + (lane >> 5)) ^ xf;
-  auto compute = [&](const uint4 *stage) {
+  // fragments of one 16-wide K step
+  auto rd = [&](const uint4 *stage, int ks, uint4 (&af)[TM], uint4 (&bf)[TN]) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      uint4 af[TM], bfr[TN];
+    for (int a = 0; a < TM; ++a) af[a] = stage[((wm * TM + a) * 32 + frow) * 8 + cidx[ks]];
 #pragma unroll
-      for (int a = 0; a < TM; ++a) af[a] = stage[((wm * TM + a) * 32 + frow) * 8 + cidx[ks]];
+    for (int b = 0; b < TN; ++b) bf[b] = stage[(BM + (wn * TN + b) * 32 + frow) * 8 + cidx[ks]];
+  };
+  auto mm = [&](const uint4 (&af)[TM], const uint4 (&bf)[TN]) {
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
 #pragma unroll
       for (int b = 0; b < TN; ++b)
-        bfr[b] = stage[(BM + (wn * TN + b) * 32 + frow) * 8 + cidx[ks]];
-#pragma unroll
-      for (int a = 0; a < TM; ++a)
-#pragma unroll
-        for (int b = 0; b < TN; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8_v, af[a]), __builtin_bit_cast(bf16x8_v, bfr[b]),
-              acc[a][b], 0, 0, 0);
-    }
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8_v, af[a]), __builtin_bit_cast(bf16x8_v, bf[b]), acc[a][b],
+            0, 0, 0);
   };
 
-  // Two-stage pipeline; the loop body has no early exit so the accumulators
-  // stay in place, and an odd final slice is handled after the loop.
+  // Software pipeline: the fragments of K step s+1 are read while the MFMAs
+  // of step s run, and the first step of the next slice is read right after
+  // the slice barrier, underneath the MFMAs of the last step of the current
+  // one.  The loop body has no early exit, so the accumulators stay in place.
   const int nk = K / 64;
+  uint4 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+  // Scheduling fences keep the program order below: the compiler would
+  // otherwise sink the LDS-DMA issue to the end of the slice (exposing the
+  // memory latency) and fold the fragment prefetch back into its consumers.
+#define SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
+#define SG(m, n) __builtin_amdgcn_sched_group_barrier(m, n, 0)
+#define P_RD_MM() do { SG(8,1); SG(0x100,1); SG(8,1); SG(0x100,1); SG(8,1); SG(0x100,1); SG(8,1); SG(0x100,1); \
+  SG(8,1); SG(0x100,1); SG(8,1); SG(0x100,1); SG(8,1); SG(0x100,1); SG(8,1); SG(0x100,1); SG(8,8); } while (0)
+#define P_LD_RD_MM() do { SG(8,1); SG(0x20,2); SG(0x100,1); SG(8,1); SG(0x20,2); SG(0x100,1); \
+  SG(8,1); SG(0x20,2); SG(0x100,1); SG(8,1); SG(0x20,2); SG(0x100,1); SG(8,1); SG(0x20,2); SG(0x100,1); \
+  SG(8,1); SG(0x20,2); SG(0x100,1); SG(8,1); SG(0x20,2); SG(0x100,1); SG(8,1); SG(0x20,2); SG(0x100,1); SG(8,8); } while (0)
   issue(st0, 0);
   wait_vmem();
   __syncthreads();
+  rd(st0, 0, fa0, fb0);
   int kt = 0;
   for (; kt + 1 < nk; kt += 2) {
     issue(st1, kt + 1);
-    compute(st0);
+    rd(st0, 1, fa1, fb1);
+    mm(fa0, fb0);
+    P_LD_RD_MM();
+    SCHED_FENCE();
+    rd(st0, 2, fa0, fb0);
+    mm(fa1, fb1);
+    P_RD_MM();
+    SCHED_FENCE();
+    rd(st0, 3, fa1, fb1);
+    mm(fa0, fb0);
+    P_RD_MM();
+    SCHED_FENCE();
+    wait_vmem();
+    __syncthreads();  // slice kt+1 is in st1; every wave is done reading st0
+    rd(st1, 0, fa0, fb0);
+    mm(fa1, fb1);
+    P_RD_MM();
+    SCHED_FENCE();
+    issue(st0, min(kt + 2, nk - 1));  // past the end: a harmless reload of the last slice
+    rd(st1, 1, fa1, fb1);
+    mm(fa0, fb0);
+    P_LD_RD_MM();
+    SCHED_FENCE();
+    rd(st1, 2, fa0, fb0);
+    mm(fa1, fb1);
+    P_RD_MM();
+    SCHED_FENCE();
+    rd(st1, 3, fa1, fb1);
+    mm(fa0, fb0);
+    P_RD_MM();
+    SCHED_FENCE();
     wait_vmem();
     __syncthreads();
-    if (kt + 2 < nk) issue(st0, kt + 2);
-    compute(st1);
-    wait_vmem();
-    __syncthreads();
+    rd(st0, 0, fa0, fb0);
+    mm(fa1, fb1);
+    P_RD_MM();
+    SCHED_FENCE();
   }
-  if (kt < nk) compute(st0);
+  if (kt < nk) {  // odd number of slices: the last one is in st0
+    rd(st0, 1, fa1, fb1);
+    mm(fa0, fb0);
+    SCHED_FENCE();
+    rd(st0, 2, fa0, fb0);
+    mm(fa1, fb1);
+    SCHED_FENCE();
+    rd(st0, 3, fa1, fb1);
+    mm(fa0, fb0);
+    mm(fa1, fb1);
+  }
+#undef SCHED_FENCE
 
   // ---- epilogue ----
   const int ccol = lane & 31;
@@ -383,7 +463,7 @@ hipError_t launch_dl(const void *A, const void *B1, const void *B3, void *C,
                      const int32_t *seg_off, const int32_t *mtile_off, int G, int N, int K,
                      int max_mtiles, hipStream_t s) {
   const int cols = SWIGLU ? BNB / 2 : BNB;
-  dim3 grid((N + cols - 1) / cols, max_mtiles);
+  dim3 grid(((N + cols - 1) / cols) * max_mtiles + NUM_XCD);
   hipLaunchKernelGGL((grouped_gemm_dl_kernel<BM, BNB, SWIGLU>), grid, dim3(GM_THREADS), 0, s,
                      (const bf16_t *)A, (const bf16_t *)B1, (const bf16_t *)B3, C, seg_off,
                      mtile_off, G, N, K);
@@ -395,7 +475,7 @@ hipError_t launch_one(const void *A, const void *B1, const void *B3, void *C,
                       const int32_t *seg_off, const int32_t *mtile_off, int G, int N, int K,
                       int max_mtiles, hipStream_t s) {
   const int cols = SWIGLU ? BNB / 2 : BNB;
-  dim3 grid((N + cols - 1) / cols, max_mtiles);
+  dim3 grid(((N + cols - 1) / cols) * max_mtiles + NUM_XCD);
   hipLaunchKernelGGL((grouped_gemm_kernel<T, BM, BNB, WM, WN, SWIGLU>), grid, dim3(GM_THREADS),
                      0, s, (const T *)A, (const T *)B1, (const T *)B3, C, seg_off, mtile_off, G,
                      N, K);
@@ -404,25 +484,39 @@ hipError_t launch_one(const void *A, const void *B1, const void *B3, void *C,
 
 }  // namespace
 
-int gemm_bm(int dtype) { return dtype == 1 ? 256 : 128; }
+GemmPlan gemm_plan(int dtype, int d, int d_ff, int d_ff_shared) {
+  GemmPlan p;
+  const int q = 64;  // K granule of the direct-to-LDS kernel
+  p.dl1 = dtype == 1 && d % q == 0;
+  p.dl2 = dtype == 1 && d_ff % q == 0 && (d_ff_shared == 0 || d_ff_shared % q == 0);
+  p.bm1 = p.dl1 ? 256 : 128;
+  p.bm2 = p.dl2 ? 256 : 128;
+  return p;
+}
 
-hipError_t launch_gemm_swiglu(int dtype, const void *A, const void *W1, const void *W3, void *H,
-                              const int32_t *seg_off, const int32_t *mtile_off, int G, int N,
-                              int K, int max_mtiles, hipStream_t s) {
+hipError_t launch_gemm_swiglu(int dtype, bool dl, const void *A, const void *W1, const void *W3,
+                              void *H, const int32_t *seg_off, const int32_t *mtile_off, int G,
+                              int N, int K, int max_mtiles, hipStream_t s) {
   if (max_mtiles <= 0) return hipSuccess;
-  if (dtype == 1)
+  if (dl)
     return launch_dl<256, 256, true>(A, W1, W3, H, seg_off, mtile_off, G, N, K, max_mtiles, s);
+  if (dtype == 1)
+    return launch_one<bf16_t, 128, 128, 2, 2, true>(A, W1, W3, H, seg_off, mtile_off, G, N, K,
+                                                    max_mtiles, s);
   return launch_one<float, 128, 128, 2, 2, true>(A, W1, W3, H, seg_off, mtile_off, G, N, K,
                                                  max_mtiles, s);
 }
 
-hipError_t launch_gemm_down(int dtype, const void *A, const void *W2, float *Y,
+hipError_t launch_gemm_down(int dtype, bool dl, const void *A, const void *W2, float *Y,
                             const int32_t *seg_off, const int32_t *mtile_off, int G, int N, int K,
                             int max_mtiles, hipStream_t s) {
   if (max_mtiles <= 0) return hipSuccess;
-  if (dtype == 1)
+  if (dl)
     return launch_dl<256, 256, false>(A, W2, nullptr, Y, seg_off, mtile_off, G, N, K,
                                       max_mtiles, s);
+  if (dtype == 1)
+    return launch_one<bf16_t, 128, 128, 2, 2, false>(A, W2, nullptr, Y, seg_off, mtile_off, G,
+                                                     N, K, max_mtiles, s);
   return launch_one<float, 128, 128, 2, 2, false>(A, W2, nullptr, Y, seg_off, mtile_off, G, N,
                                                   K, max_mtiles, s);
 }

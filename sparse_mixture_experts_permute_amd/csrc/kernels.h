@@ -17,11 +17,16 @@ hipError_t launch_permute(const int32_t *idx, int T, int E, int k, int bm0, int 
 hipError_t launch_gather(const void *x, const int32_t *perm, int P, int k, int d, int esize,
                          void *xp, hipStream_t s);
 
-int gemm_bm(int dtype);
-hipError_t launch_gemm_swiglu(int dtype, const void *A, const void *W1, const void *W3, void *H,
-                              const int32_t *seg_off, const int32_t *mtile_off, int G, int N,
-                              int K, int max_mtiles, hipStream_t s);
-hipError_t launch_gemm_down(int dtype, const void *A, const void *W2, float *Y,
+// Which grouped-GEMM kernel serves each projection, and its m-tile height.
+struct GemmPlan {
+  bool dl1, dl2;  // pipelined direct-to-LDS kernel for the SwiGLU / down GEMM
+  int bm1, bm2;   // rows per m-tile of the SwiGLU / down GEMM
+};
+GemmPlan gemm_plan(int dtype, int d, int d_ff, int d_ff_shared);
+hipError_t launch_gemm_swiglu(int dtype, bool dl, const void *A, const void *W1, const void *W3,
+                              void *H, const int32_t *seg_off, const int32_t *mtile_off, int G,
+                              int N, int K, int max_mtiles, hipStream_t s);
+hipError_t launch_gemm_down(int dtype, bool dl, const void *A, const void *W2, float *Y,
                             const int32_t *seg_off, const int32_t *mtile_off, int G, int N, int K,
                             int max_mtiles, hipStream_t s);
 
