@@ -65,7 +65,17 @@ def algorithmic(cfg, counts):
                 layer_bytes=layer_bytes, experts_hit=hit)
 
 
-def run_workload(cfg, host, dev, steps, warmup, flush_mb=0):
+def run_workload(cfg, host, dev, steps, warmup, flush_mb=0, graph=False):
+    """Time `steps` layer forwards.
+
+    Pass 1 (the timed region): back-to-back forwards through moe_forward_timed,
+    which also records HIP events at the stage boundaries on the stream the
+    kernels run on; ms_per_step is the elapsed time of the whole region / steps.
+    With flush_mb, a buffer of that size is read before every step (to evict the
+    256 MB MALL, which would otherwise hold the hit experts' weights between
+    steps) and the step time is measured per step around the forward only.  With graph=True, one forward is also captured in a HIP graph
+    and replayed (reported separately).
+    """
     import numpy as np
     import torch
 
@@ -82,36 +92,61 @@ def run_workload(cfg, host, dev, steps, warmup, flush_mb=0):
     layer = moe.MoELayer(dev["Wg"], dev["W1"], dev["W3"], dev["W2"], cfg.k, bias, shared)
     y = torch.empty_like(x)
     layer.workspace(T)
-    flush = torch.empty(flush_mb << 20, dtype=torch.uint8, device="cuda") if flush_mb else None
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(moe.NSTAGE_EVENTS)]
-              for _ in range(steps)]
+    flush = (torch.ones(flush_mb << 18, dtype=torch.float32, device="cuda") if flush_mb
+             else None)
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    events = [[ev() for _ in range(moe.NSTAGE_EVENTS)] for _ in range(steps)]
     for row in events:
         for e in row:
             e.record()
     for _ in range(warmup):
         layer(x, y)
     torch.cuda.synchronize()
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    t_start, t_end = ev(), ev()
     w0 = time.perf_counter()
     t_start.record()
     for i in range(steps):
         if flush is not None:
-            flush.zero_()  # evict the 256 MB MALL between steps
+            flush.sum()  # read flush_mb MB: evicts the 256 MB MALL without dirty lines
         layer.timed(x, y, events[i])
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    total_ms = t_start.elapsed_time(t_end)
     stage = np.zeros(len(moe.STAGES))
     for row in events:
         for s in range(len(moe.STAGES)):
             stage[s] += row[s].elapsed_time(row[s + 1])
     stage /= steps
-    layer_ms = float(stage.sum())
-    counts = layer.intermediates(T)["counts"].cpu().numpy()
-    return dict(total_ms=total_ms, wall_s=wall, stage_ms=stage, layer_ms=layer_ms,
-                counts=counts, layer=layer)
+    if flush is None:
+        ms = t_start.elapsed_time(t_end) / steps
+    else:
+        ms = float(np.mean([row[0].elapsed_time(row[-1]) for row in events]))
+    out = dict(ms=ms, wall_s=wall, stage_ms=stage, counts=layer.intermediates(T)["counts"].cpu().numpy())
+    if graph:
+        # one forward captured in a HIP graph, replayed; per-replay time between events
+        g = torch.cuda.CUDAGraph()
+        s_cap = torch.cuda.Stream()
+        s_cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s_cap):
+            layer(x, y)  # warm the capture stream
+        torch.cuda.current_stream().wait_stream(s_cap)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            layer(x, y)
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(steps):
+            if flush is not None:
+                flush.sum()
+            a, b_ = ev(), ev()
+            a.record()
+            g.replay()
+            b_.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b_))
+        out["graph_ms"] = float(np.median(times))
+        del g
+    return out
 
 
 def roofline_for(cfg, res):
@@ -132,7 +167,7 @@ def roofline_for(cfg, res):
     rl.update(traffic=None, kernel="grouped_gemm_swiglu", kernel_ms=round(g1_ms, 4),
               algorithmic_flop=a["g1_flop"], algorithmic_bytes=a["g1_bytes"])
     # whole-layer fractions
-    lt = res["layer_ms"] * 1e-3
+    lt = res["ms"] * 1e-3
     layer = dict(mfma_frac=round(a["layer_flop"] / lt / (peak_f * 1e12), 4),
                  hbm_frac=round(a["layer_bytes"] / lt / (PEAK_HBM_GBS * 1e9), 4),
                  experts_hit=a["experts_hit"])
@@ -189,7 +224,7 @@ def main():
 
     res = run_workload(cfg, host, dev, args.steps, args.warmup)
     rl, layer_fr = roofline_for(cfg, res)
-    ms = res["total_ms"] / args.steps
+    ms = res["ms"]
     value = cfg.T / (ms * 1e-3)
     stage = {s: round(float(v), 4) for s, v in zip(moe.STAGES, res["stage_ms"])}
     log(f"{cfg.name}: {ms:.3f} ms/step, {value:.0f} tokens/s, stages {stage}")
@@ -200,18 +235,26 @@ def main():
         for name, steps, flush in [("mixtral_prefill_T2048", 10, 0),
                                    ("mixtral_prefill_T8192_skew", 5, 0),
                                    ("mixtral_decode_T1", 20, 512),
+                                   ("mixtral_decode_T8", 20, 512),
+                                   ("mixtral_decode_T32", 20, 512),
                                    ("mixtral_decode_T128", 20, 512)]:
             if name == cfg.name:
                 continue
             c2 = CONFIGS[name]
-            r2 = run_workload(c2, host, dev, steps, 2, flush_mb=flush)
+            r2 = run_workload(c2, host, dev, steps, 2, flush_mb=flush, graph=bool(flush))
             rl2, lf2 = roofline_for(c2, r2)
-            ms2 = r2["layer_ms"]
+            ms2 = r2["ms"]
             e = dict(workload=name, T=c2.T, ms_per_step=round(ms2, 4),
                      tokens_per_s=round(c2.T / (ms2 * 1e-3), 1),
                      stage_ms={s: round(float(v), 4) for s, v in zip(moe.STAGES,
                                                                       r2["stage_ms"])},
                      roofline=rl2, layer=lf2, mall_flushed=bool(flush))
+            if "graph_ms" in r2:
+                gms = r2["graph_ms"]
+                e["graph_replay"] = dict(
+                    ms_per_step=round(gms, 4), tokens_per_s=round(c2.T / (gms * 1e-3), 1),
+                    hbm_frac=round(algorithmic(c2, r2["counts"])["layer_bytes"] / (gms * 1e-3)
+                                   / (PEAK_HBM_GBS * 1e9), 4))
             if c2.skew:
                 e["hot_expert_share"] = round(float(r2["counts"][0] / r2["counts"].sum()), 4)
             log(f"{name}: {ms2:.4f} ms/step (sum of stages), {e['tokens_per_s']} tokens/s")
@@ -248,6 +291,8 @@ def main():
         "cpu_baseline": cpu,
         "extra": extra,
         "wall_s_timed": round(res["wall_s"], 3),
+        "timing": "HIP events on the stream the kernels run on; stage events recorded by "
+                  "moe_forward_timed inside the timed region",
     }
     print(json.dumps(out), flush=True)
 

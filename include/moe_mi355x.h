@@ -64,14 +64,21 @@ enum {
     MOE_EDEVICE = -5     /* current device is not a gfx950 GPU */
 };
 
+/* Bytes of scratch moe_route needs for (T, d, E, dtype); 0 on invalid arguments. */
+size_t moe_route_workspace_bytes(int T, int d, int E, int dtype);
+
 /* Router + top-k + gate (the first two steps above).
  *   x      [T][d]   dtype          Wg [E][d] dtype
  *   bias   [E] fp32 or NULL (a per-expert logit offset, e.g. to skew routing)
  *   idx    [T][k] int32  out: selected experts, descending logit, ties -> lower e
  *   gate   [T][k] fp32   out: softmax over the selected logits
- *   logits [T][E] fp32   out (may be NULL): the router scores idx/gate came from */
+ *   logits [T][E] fp32   out (may be NULL): the router scores idx/gate came from
+ *   workspace: device scratch of moe_route_workspace_bytes(T, d, E, dtype)
+ *     bytes, 256-byte aligned (partial sums over slices of the d dimension,
+ *     added in a fixed order, so the scores are deterministic). */
 int moe_route(const void *x, const void *Wg, const float *bias, int T, int d, int E, int k,
-              int dtype, int32_t *idx, float *gate, float *logits, void *stream);
+              int dtype, int32_t *idx, float *gate, float *logits, void *workspace,
+              size_t workspace_bytes, void *stream);
 
 /* Bytes of scratch moe_permute needs for (T, E, k). */
 size_t moe_permute_workspace_bytes(int T, int E, int k);

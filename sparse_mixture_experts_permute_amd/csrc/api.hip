@@ -13,8 +13,8 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 enum Field {
-  F_LOGITS, F_IDX, F_GATE, F_COUNTS, F_OFFSETS, F_PERM, F_INV, F_MT0, F_MT1, F_SHSEG, F_BLK,
-  F_XP, F_H, F_YP, F_HS, F_YS, F_COUNT
+  F_LOGITS, F_IDX, F_GATE, F_COUNTS, F_OFFSETS, F_PERM, F_INV, F_MT0, F_MT1, F_SHSEG, F_ACT,
+  F_RPART, F_BLK, F_XP, F_H, F_YP, F_HS, F_YS, F_COUNT
 };
 
 struct Layout {
@@ -35,8 +35,12 @@ bool dims_ok(int T, int d, int d_ff, int E, int k, int dffs) {
 
 size_t esize(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
 
+int down_splits(const moe::GemmPlan &plan, int T, int k, int E, int d, int d_ff);
+
 Layout layout(int T, int d, int d_ff, int E, int k, int dffs, int dtype) {
   Layout L;
+  const moe::GemmPlan plan = moe::gemm_plan(dtype, d, d_ff, dffs, ((long long)T * k + E - 1) / E);
+  const int ksplit = down_splits(plan, T, k, E, d, d_ff);
   const size_t P = (size_t)T * k, es = esize(dtype);
   const size_t nb = (size_t)moe::permute_nblocks((int)P);
   size_t sz[F_COUNT] = {};
@@ -50,10 +54,12 @@ Layout layout(int T, int d, int d_ff, int E, int k, int dffs, int dtype) {
   sz[F_MT0] = (size_t)(E + 1) * 4;
   sz[F_MT1] = (size_t)(E + 1) * 4;
   sz[F_SHSEG] = 8 * 4;
+  sz[F_ACT] = (size_t)(E + 1) * 4;
+  sz[F_RPART] = moe::router_partial_bytes(T, d, E, (int)es);
   sz[F_BLK] = nb * E * 4;
   sz[F_XP] = P * d * es;
   sz[F_H] = P * d_ff * es;
-  sz[F_YP] = P * d * 4;
+  sz[F_YP] = (size_t)ksplit * P * d * 4;
   sz[F_HS] = (size_t)T * dffs * es;
   sz[F_YS] = dffs ? (size_t)T * d * 4 : 0;
   size_t o = 0;
@@ -80,6 +86,43 @@ int device_ok() {
 
 int launched(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ELAUNCH; }
 
+// K splits of the tiled down projection: a batch with few m-tiles (decode, few
+// rows per expert) would leave most CUs idle, so K is split until about 512
+// workgroups run; the combine adds the partial planes in a fixed order.
+int down_splits(const moe::GemmPlan &plan, int T, int k, int E, int d, int d_ff) {
+  if (!plan.dl2) return 1;
+  const long long P = (long long)T * k;
+  const long long active = P < E ? P : E;  // experts that can hold rows
+  const long long mt_floor = (P + plan.bm2 - 1) / plan.bm2;
+  const long long mt = active > mt_floor ? active : mt_floor;
+  const long long wgs = mt * ((d + 255) / 256);
+  int S = 1;
+  while (wgs * S < 512 && S < 16 && d_ff % (64 * S * 2) == 0) S *= 2;
+  return S;
+}
+
+// Row blocks of 16 that one pass of the weight-streaming kernel covers.
+int skinny_mb(long long rows) { return rows <= 12 ? 1 : rows <= 24 ? 2 : 4; }
+
+// The weight-streaming kernels serve the routed experts when they average one
+// row each (single-token decode: they also fold the row gather into the first
+// GEMM) and the shared expert up to 64 tokens; the tiled kernels (64-row tiles
+// for small batches, split K for the down projection) serve everything else.
+struct SkinnyPlan {
+  bool routed, shared;
+  int mb, mb_shared;
+};
+SkinnyPlan skinny_plan(int dtype, int T, int k, int E, int d, int d_ff, int dffs) {
+  SkinnyPlan p{};
+  if (dtype != MOE_BF16) return p;
+  const long long avg = ((long long)T * k + E - 1) / E;
+  p.routed = avg <= 1 && moe::skinny_ok(d_ff, d) && moe::skinny_ok(d, d_ff);
+  p.mb = skinny_mb(avg);
+  p.shared = dffs > 0 && T <= 64 && moe::skinny_ok(dffs, d) && moe::skinny_ok(d, dffs);
+  p.mb_shared = skinny_mb(T);
+  return p;
+}
+
 template <typename P> P *at(void *ws, size_t off) {
   return reinterpret_cast<P *>(reinterpret_cast<char *>(ws) + off);
 }
@@ -100,22 +143,33 @@ const char *moe_strerror(int status) {
   }
 }
 
+size_t moe_route_workspace_bytes(int T, int d, int E, int dtype) {
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return 0;
+  if (T < 0 || E < 1 || E > 256 || d < 64 || d % 64) return 0;
+  return align_up(moe::router_partial_bytes(T, d, E, (int)esize(dtype))) + kAlign;
+}
+
 int moe_route(const void *x, const void *Wg, const float *bias, int T, int d, int E, int k,
-              int dtype, int32_t *idx, float *gate, float *logits, void *stream) {
+              int dtype, int32_t *idx, float *gate, float *logits, void *workspace,
+              size_t workspace_bytes, void *stream) {
   if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_EDTYPE;
   if (T < 0 || E < 1 || E > 256 || k < 1 || k > E || d < 64 || d % 64) return MOE_EINVAL;
+  if ((long long)T * E >= (1LL << 31)) return MOE_EINVAL;
   if (T == 0) return MOE_OK;
-  if (!x || !Wg || !idx || !gate) return MOE_EINVAL;
+  if (!x || !Wg || !idx || !gate || !workspace) return MOE_EINVAL;
+  if (workspace_bytes < moe_route_workspace_bytes(T, d, E, dtype) ||
+      ((uintptr_t)workspace % kAlign))
+    return MOE_EWORKSPACE;
   int st = device_ok();
   if (st != MOE_OK) return st;
   return launched(moe::launch_router(dtype, x, Wg, bias, T, d, E, k, idx, gate, logits,
-                                     (hipStream_t)stream));
+                                     (float *)workspace, (hipStream_t)stream));
 }
 
 size_t moe_permute_workspace_bytes(int T, int E, int k) {
   if (T < 0 || E < 1 || k < 1) return 0;
   const size_t nb = (size_t)moe::permute_nblocks(T * k);
-  return align_up(nb * E * 4) + 3 * align_up((size_t)(E + 1) * 4 + 32);
+  return align_up(nb * E * 4) + 4 * align_up((size_t)(E + 1) * 4 + 32);
 }
 
 int moe_permute(const int32_t *idx, int T, int E, int k, int32_t *counts, int32_t *offsets,
@@ -142,9 +196,10 @@ int moe_permute(const int32_t *idx, int T, int E, int k, int32_t *counts, int32_
   int32_t *mt0 = (int32_t *)(w + align_up(nb * E * 4));
   int32_t *mt1 = mt0 + align_up((size_t)(E + 1) * 4 + 32) / 4;
   int32_t *sh = mt1 + align_up((size_t)(E + 1) * 4 + 32) / 4;
+  int32_t *act = sh + align_up((size_t)(E + 1) * 4 + 32) / 4;
   // the m-tile prefixes are by-products here; any tile height will do
   return launched(moe::launch_permute(idx, T, E, k, 256, 256, blk, counts, offsets, perm, inv,
-                                      mt0, mt1, sh, (hipStream_t)stream));
+                                      mt0, mt1, sh, act, (hipStream_t)stream));
 }
 
 size_t moe_workspace_bytes(int T, int d, int d_ff, int E, int k, int d_ff_shared, int dtype) {
@@ -187,7 +242,11 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
   hipStream_t s = (hipStream_t)stream;
   void *ws = workspace;
   const int P = T * k;
-  const moe::GemmPlan plan = moe::gemm_plan(dtype, d, d_ff, d_ff_shared);
+  const moe::GemmPlan plan =
+      moe::gemm_plan(dtype, d, d_ff, d_ff_shared, ((long long)T * k + E - 1) / E);
+  const SkinnyPlan sk = skinny_plan(dtype, T, k, E, d, d_ff, d_ff_shared);
+  const int ksplit = sk.routed ? 1 : down_splits(plan, T, k, E, d, d_ff);
+  const size_t plane = (size_t)P * d;
   float *logits = at<float>(ws, L.off[F_LOGITS]);
   int32_t *idx = at<int32_t>(ws, L.off[F_IDX]);
   float *gate = at<float>(ws, L.off[F_GATE]);
@@ -198,6 +257,7 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
   int32_t *mt0 = at<int32_t>(ws, L.off[F_MT0]);
   int32_t *mt1 = at<int32_t>(ws, L.off[F_MT1]);
   int32_t *shseg = at<int32_t>(ws, L.off[F_SHSEG]);
+  int32_t *act = at<int32_t>(ws, L.off[F_ACT]);
   int32_t *blk = at<int32_t>(ws, L.off[F_BLK]);
   void *Xp = at<char>(ws, L.off[F_XP]);
   void *H = at<char>(ws, L.off[F_H]);
@@ -210,32 +270,56 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
 #define MOE_MARK(i) \
   if (events && hipEventRecord((hipEvent_t)events[i], s) != hipSuccess) goto fail;
   MOE_MARK(0);
-  if ((e = moe::launch_router(dtype, x, Wg, bias, T, d, E, k, idx, gate, logits, s))) goto fail;
+  if ((e = moe::launch_router(dtype, x, Wg, bias, T, d, E, k, idx, gate, logits,
+                              at<float>(ws, L.off[F_RPART]), s)))
+    goto fail;
   MOE_MARK(1);
   if ((e = moe::launch_permute(idx, T, E, k, plan.bm1, plan.bm2, blk, counts, offsets, perm, inv,
-                               mt0, mt1, shseg, s)))
+                               mt0, mt1, shseg, act, s)))
     goto fail;
   MOE_MARK(2);
-  if ((e = moe::launch_gather(x, perm, P, k, d, (int)esize(dtype), Xp, s))) goto fail;
-  MOE_MARK(3);
-  if ((e = moe::launch_gemm_swiglu(dtype, plan.dl1, Xp, W1, W3, H, offsets, mt0, E, d_ff, d,
-                                   (P + plan.bm1 - 1) / plan.bm1 + E, s)))
-    goto fail;
-  MOE_MARK(4);
-  if ((e = moe::launch_gemm_down(dtype, plan.dl2, H, W2, Yp, offsets, mt1, E, d, d_ff,
-                                 (P + plan.bm2 - 1) / plan.bm2 + E, s)))
-    goto fail;
-  MOE_MARK(5);
+  if (sk.routed) {
+    // few rows per expert: weight-streaming kernels; the gather rides in the first GEMM
+    MOE_MARK(3);
+    if ((e = moe::launch_skinny_swiglu(sk.mb, x, perm, k, W1, W3, H, offsets, act, act + E, E,
+                                       d_ff, d, s)))
+      goto fail;
+    MOE_MARK(4);
+    if ((e = moe::launch_skinny_down(sk.mb, H, W2, Yp, offsets, act, act + E, E, d, d_ff, s)))
+      goto fail;
+    MOE_MARK(5);
+  } else {
+    if ((e = moe::launch_gather(x, perm, P, k, d, (int)esize(dtype), Xp, s))) goto fail;
+    MOE_MARK(3);
+    if ((e = moe::launch_gemm_swiglu(dtype, plan.dl1, plan.bm1, Xp, W1, W3, H, offsets, mt0, E, d_ff, d,
+                                     (P + plan.bm1 - 1) / plan.bm1 + E, s)))
+      goto fail;
+    MOE_MARK(4);
+    if ((e = moe::launch_gemm_down(dtype, plan.dl2, plan.bm2, H, W2, Yp, offsets, mt1, E, d, d_ff,
+                                   (P + plan.bm2 - 1) / plan.bm2 + E, ksplit, plane, s)))
+      goto fail;
+    MOE_MARK(5);
+  }
   if (shared) {
-    if ((e = moe::launch_gemm_swiglu(dtype, plan.dl1, x, Ws1, Ws3, Hs, shseg, shseg + 2, 1,
-                                     d_ff_shared, d, (T + plan.bm1 - 1) / plan.bm1, s)))
-      goto fail;
-    if ((e = moe::launch_gemm_down(dtype, plan.dl2, Hs, Ws2, Ys, shseg, shseg + 4, 1, d,
-                                   d_ff_shared, (T + plan.bm2 - 1) / plan.bm2, s)))
-      goto fail;
+    if (sk.shared) {
+      if ((e = moe::launch_skinny_swiglu(sk.mb_shared, x, nullptr, 1, Ws1, Ws3, Hs, shseg,
+                                         shseg + 6, shseg + 7, 1, d_ff_shared, d, s)))
+        goto fail;
+      if ((e = moe::launch_skinny_down(sk.mb_shared, Hs, Ws2, Ys, shseg, shseg + 6, shseg + 7, 1,
+                                       d, d_ff_shared, s)))
+        goto fail;
+    } else {
+      if ((e = moe::launch_gemm_swiglu(dtype, plan.dl1, plan.bm1, x, Ws1, Ws3, Hs, shseg, shseg + 2, 1,
+                                       d_ff_shared, d, (T + plan.bm1 - 1) / plan.bm1, s)))
+        goto fail;
+      if ((e = moe::launch_gemm_down(dtype, plan.dl2, plan.bm2, Hs, Ws2, Ys, shseg, shseg + 4, 1, d,
+                                     d_ff_shared, (T + plan.bm2 - 1) / plan.bm2, 1, 0, s)))
+        goto fail;
+    }
   }
   MOE_MARK(6);
-  if ((e = moe::launch_combine(dtype, Yp, shared ? Ys : nullptr, inv, gate, T, k, d, y, s)))
+  if ((e = moe::launch_combine(dtype, Yp, ksplit, plane, shared ? Ys : nullptr, inv, gate, T, k,
+                               d, y, s)))
     goto fail;
   MOE_MARK(7);
 #undef MOE_MARK

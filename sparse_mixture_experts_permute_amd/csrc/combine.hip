@@ -1,6 +1,8 @@
 // Gate-weighted combine back to token order:
 //   y[t][:] = sum_{j<k} gate[t][j] * Yp[inv[t*k+j]][:]  (+ Ys[t][:] for the shared expert)
-// summed in fp32 with j ascending, written once per token with no atomics
+// summed in fp32 with j ascending, written once per token with no atomics.
+// When the down projection split K, Yp has nsplit planes whose rows are added
+// first, in plane order
 // ("Chapter 10 MoE", sections 10.4 and 10.5; "Mixtral and MoE architecture",
 // weighted accumulation in the MixtralMoE listing).
 #include "common.h"
@@ -12,7 +14,8 @@ namespace {
 
 // One block per token; each thread handles 4 consecutive columns per step.
 template <typename T>
-__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ Yp,
+__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ Yp, int nsplit,
+                                                      size_t plane,
                                                       const float *__restrict__ Ys,
                                                       const int32_t *__restrict__ inv,
                                                       const float *__restrict__ gate, int k,
@@ -23,7 +26,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j = 0; j < k; ++j) {
       const float g = gate[(size_t)t * k + j];
-      const float4 v = reinterpret_cast<const float4 *>(Yp)[(size_t)inv[(size_t)t * k + j] * d4 + c];
+      const size_t row = (size_t)inv[(size_t)t * k + j] * d4 + c;
+      float4 v = reinterpret_cast<const float4 *>(Yp)[row];
+      for (int sp = 1; sp < nsplit; ++sp) {
+        const float4 u = reinterpret_cast<const float4 *>(Yp + sp * plane)[row];
+        v.x += u.x;
+        v.y += u.y;
+        v.z += u.z;
+        v.w += u.w;
+      }
       acc.x = fmaf(g, v.x, acc.x);
       acc.y = fmaf(g, v.y, acc.y);
       acc.z = fmaf(g, v.z, acc.z);
@@ -46,15 +57,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
 
 }  // namespace
 
-hipError_t launch_combine(int dtype, const float *Yp, const float *Ys, const int32_t *inv,
-                          const float *gate, int T, int k, int d, void *y, hipStream_t s) {
+hipError_t launch_combine(int dtype, const float *Yp, int nsplit, size_t plane, const float *Ys,
+                          const int32_t *inv, const float *gate, int T, int k, int d, void *y,
+                          hipStream_t s) {
   if (T <= 0) return hipSuccess;
   if (dtype == 1)
-    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(T), dim3(256), 0, s, Yp, Ys, inv, gate, k, d,
-                       (bf16_t *)y);
+    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(T), dim3(256), 0, s, Yp, nsplit, plane, Ys,
+                       inv, gate, k, d, (bf16_t *)y);
   else
-    hipLaunchKernelGGL(combine_kernel<float>, dim3(T), dim3(256), 0, s, Yp, Ys, inv, gate, k, d,
-                       (float *)y);
+    hipLaunchKernelGGL(combine_kernel<float>, dim3(T), dim3(256), 0, s, Yp, nsplit, plane, Ys,
+                       inv, gate, k, d, (float *)y);
   return hipGetLastError();
 }
 

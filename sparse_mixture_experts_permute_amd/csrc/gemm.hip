@@ -253,11 +253,14 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_kernel(
 // the 64 LDS banks.  Two stages of (BM + BNB) x 128 bytes; the loads of slice
 // kt+1 run while slice kt feeds the MFMAs, with no staging registers.
 // ---------------------------------------------------------------------------
+// Split K (down projection only): blockIdx.y picks one of gridDim.y equal K
+// ranges and its fp32 partial goes to output plane blockIdx.y (plane elements
+// apart); the combine adds the planes in a fixed order.
 template <int BM, int BNB, bool SWIGLU>
 __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
     const bf16_t *__restrict__ A, const bf16_t *__restrict__ B1, const bf16_t *__restrict__ B3,
     void *__restrict__ C, const int32_t *__restrict__ seg_off,
-    const int32_t *__restrict__ mtile_off, int G, int N, int K) {
+    const int32_t *__restrict__ mtile_off, int G, int N, int K, size_t plane) {
   constexpr int WM = 2, WN = 2;
   constexpr int TM = BM / WM / 32, TN = BNB / WN / 32;
   constexpr int ROWS = BM + BNB;          // tile rows per stage (A then B)
@@ -283,8 +286,10 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
   // loads A blocks w*IA .. w*IA+IA-1 and B blocks w*IB .. w*IB+IB-1 (8 rows
   // each), so whether an instruction reads A, W1 or W3 is fixed per j.
   constexpr int IA = BM / 32, IB = BNB / 32;  // instructions per wave per stage
-  const char *abase = reinterpret_cast<const char *>(A) + (size_t)row0 * K * 2;
-  const size_t eoff = (size_t)e * N * K * 2;
+  const int kpart = K / gridDim.y;  // K range of this split (a multiple of 64)
+  const size_t kb = (size_t)blockIdx.y * kpart * 2;  // its byte offset inside a row
+  const char *abase = reinterpret_cast<const char *>(A) + (size_t)row0 * K * 2 + kb;
+  const size_t eoff = (size_t)e * N * K * 2 + kb;
   const char *b1base = reinterpret_cast<const char *>(B1) + eoff;
   const char *b3base = SWIGLU ? reinterpret_cast<const char *>(B3) + eoff : b1base;
   uint32_t aoff[IA], boff[IB];
@@ -359,7 +364,7 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
   // of step s run, and the first step of the next slice is read right after
   // the slice barrier, underneath the MFMAs of the last step of the current
   // one.  The loop body has no early exit, so the accumulators stay in place.
-  const int nk = K / 64;
+  const int nk = kpart / 64;
   uint4 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
   // Scheduling fences keep the program order below: the compiler would
   // otherwise sink the LDS-DMA issue to the end of the slice (exposing the
@@ -451,7 +456,8 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
 #pragma unroll
         for (int b = 0; b < TN; ++b) {
           const int col = n0 + (wn * TN + b) * 32 + ccol;
-          if (col < N) reinterpret_cast<float *>(C)[orow + col] = acc[a][b][i];
+          if (col < N)
+            reinterpret_cast<float *>(C)[blockIdx.y * plane + orow + col] = acc[a][b][i];
         }
       }
     }
@@ -461,12 +467,12 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
 template <int BM, int BNB, bool SWIGLU>
 hipError_t launch_dl(const void *A, const void *B1, const void *B3, void *C,
                      const int32_t *seg_off, const int32_t *mtile_off, int G, int N, int K,
-                     int max_mtiles, hipStream_t s) {
+                     int max_mtiles, int ksplit, size_t plane, hipStream_t s) {
   const int cols = SWIGLU ? BNB / 2 : BNB;
-  dim3 grid(((N + cols - 1) / cols) * max_mtiles + NUM_XCD);
+  dim3 grid(((N + cols - 1) / cols) * max_mtiles + NUM_XCD, ksplit);
   hipLaunchKernelGGL((grouped_gemm_dl_kernel<BM, BNB, SWIGLU>), grid, dim3(GM_THREADS), 0, s,
                      (const bf16_t *)A, (const bf16_t *)B1, (const bf16_t *)B3, C, seg_off,
-                     mtile_off, G, N, K);
+                     mtile_off, G, N, K, plane);
   return hipGetLastError();
 }
 
@@ -484,22 +490,29 @@ hipError_t launch_one(const void *A, const void *B1, const void *B3, void *C,
 
 }  // namespace
 
-GemmPlan gemm_plan(int dtype, int d, int d_ff, int d_ff_shared) {
+GemmPlan gemm_plan(int dtype, int d, int d_ff, int d_ff_shared, long long rows_per_expert) {
   GemmPlan p;
   const int q = 64;  // K granule of the direct-to-LDS kernel
   p.dl1 = dtype == 1 && d % q == 0;
   p.dl2 = dtype == 1 && d_ff % q == 0 && (d_ff_shared == 0 || d_ff_shared % q == 0);
-  p.bm1 = p.dl1 ? 256 : 128;
-  p.bm2 = p.dl2 ? 256 : 128;
+  // 64-row tiles when experts hold few rows (less padding, two workgroups per CU)
+  const int bm_dl = rows_per_expert <= 96 ? 64 : 256;
+  p.bm1 = p.dl1 ? bm_dl : 128;
+  p.bm2 = p.dl2 ? bm_dl : 128;
   return p;
 }
 
-hipError_t launch_gemm_swiglu(int dtype, bool dl, const void *A, const void *W1, const void *W3,
-                              void *H, const int32_t *seg_off, const int32_t *mtile_off, int G,
-                              int N, int K, int max_mtiles, hipStream_t s) {
+hipError_t launch_gemm_swiglu(int dtype, bool dl, int bm, const void *A, const void *W1,
+                              const void *W3, void *H, const int32_t *seg_off,
+                              const int32_t *mtile_off, int G, int N, int K, int max_mtiles,
+                              hipStream_t s) {
   if (max_mtiles <= 0) return hipSuccess;
+  if (dl && bm == 64)
+    return launch_dl<64, 256, true>(A, W1, W3, H, seg_off, mtile_off, G, N, K, max_mtiles, 1, 0,
+                                    s);
   if (dl)
-    return launch_dl<256, 256, true>(A, W1, W3, H, seg_off, mtile_off, G, N, K, max_mtiles, s);
+    return launch_dl<256, 256, true>(A, W1, W3, H, seg_off, mtile_off, G, N, K, max_mtiles, 1,
+                                     0, s);
   if (dtype == 1)
     return launch_one<bf16_t, 128, 128, 2, 2, true>(A, W1, W3, H, seg_off, mtile_off, G, N, K,
                                                     max_mtiles, s);
@@ -507,13 +520,16 @@ hipError_t launch_gemm_swiglu(int dtype, bool dl, const void *A, const void *W1,
                                                  max_mtiles, s);
 }
 
-hipError_t launch_gemm_down(int dtype, bool dl, const void *A, const void *W2, float *Y,
+hipError_t launch_gemm_down(int dtype, bool dl, int bm, const void *A, const void *W2, float *Y,
                             const int32_t *seg_off, const int32_t *mtile_off, int G, int N, int K,
-                            int max_mtiles, hipStream_t s) {
+                            int max_mtiles, int ksplit, size_t plane, hipStream_t s) {
   if (max_mtiles <= 0) return hipSuccess;
+  if (dl && bm == 64)
+    return launch_dl<64, 256, false>(A, W2, nullptr, Y, seg_off, mtile_off, G, N, K,
+                                     max_mtiles, ksplit, plane, s);
   if (dl)
     return launch_dl<256, 256, false>(A, W2, nullptr, Y, seg_off, mtile_off, G, N, K,
-                                      max_mtiles, s);
+                                      max_mtiles, ksplit, plane, s);
   if (dtype == 1)
     return launch_one<bf16_t, 128, 128, 2, 2, false>(A, W2, nullptr, Y, seg_off, mtile_off, G,
                                                      N, K, max_mtiles, s);

@@ -5,15 +5,16 @@
 
 namespace moe {
 
+size_t router_partial_bytes(int T, int d, int E, int esize);
 hipError_t launch_router(int dtype, const void *x, const void *Wg, const float *bias, int T,
                          int d, int E, int k, int32_t *idx, float *gate, float *logits,
-                         hipStream_t s);
+                         float *part, hipStream_t s);
 
 int permute_nblocks(int P);
 hipError_t launch_permute(const int32_t *idx, int T, int E, int k, int bm0, int bm1,
                           int32_t *blk, int32_t *counts, int32_t *offsets, int32_t *perm,
                           int32_t *inv, int32_t *mtiles0, int32_t *mtiles1,
-                          int32_t *shared_seg, hipStream_t s);
+                          int32_t *shared_seg, int32_t *active, hipStream_t s);
 hipError_t launch_gather(const void *x, const int32_t *perm, int P, int k, int d, int esize,
                          void *xp, hipStream_t s);
 
@@ -22,15 +23,30 @@ struct GemmPlan {
   bool dl1, dl2;  // pipelined direct-to-LDS kernel for the SwiGLU / down GEMM
   int bm1, bm2;   // rows per m-tile of the SwiGLU / down GEMM
 };
-GemmPlan gemm_plan(int dtype, int d, int d_ff, int d_ff_shared);
-hipError_t launch_gemm_swiglu(int dtype, bool dl, const void *A, const void *W1, const void *W3,
-                              void *H, const int32_t *seg_off, const int32_t *mtile_off, int G,
-                              int N, int K, int max_mtiles, hipStream_t s);
-hipError_t launch_gemm_down(int dtype, bool dl, const void *A, const void *W2, float *Y,
+GemmPlan gemm_plan(int dtype, int d, int d_ff, int d_ff_shared, long long rows_per_expert);
+hipError_t launch_gemm_swiglu(int dtype, bool dl, int bm, const void *A, const void *W1,
+                              const void *W3, void *H, const int32_t *seg_off,
+                              const int32_t *mtile_off, int G, int N, int K, int max_mtiles,
+                              hipStream_t s);
+// ksplit > 1 (direct-to-LDS kernel only): K is split in ksplit equal ranges
+// whose fp32 partials go to planes `plane` elements apart.
+hipError_t launch_gemm_down(int dtype, bool dl, int bm, const void *A, const void *W2, float *Y,
                             const int32_t *seg_off, const int32_t *mtile_off, int G, int N, int K,
-                            int max_mtiles, hipStream_t s);
+                            int max_mtiles, int ksplit, size_t plane, hipStream_t s);
 
-hipError_t launch_combine(int dtype, const float *Yp, const float *Ys, const int32_t *inv,
-                          const float *gate, int T, int k, int d, void *y, hipStream_t s);
+// Weight-streaming grouped GEMMs for few rows per expert (bf16 only).
+bool skinny_ok(int N, int K);
+hipError_t launch_skinny_swiglu(int mb, const void *x, const int32_t *perm, int kslots,
+                                const void *W1, const void *W3, void *H,
+                                const int32_t *seg_off, const int32_t *active,
+                                const int32_t *nactive, int G, int N, int K, hipStream_t s);
+hipError_t launch_skinny_down(int mb, const void *Hin, const void *W2, float *Y,
+                              const int32_t *seg_off, const int32_t *active,
+                              const int32_t *nactive, int G, int N, int K, hipStream_t s);
+
+// Yp holds nsplit planes of `plane` floats each (summed in order).
+hipError_t launch_combine(int dtype, const float *Yp, int nsplit, size_t plane, const float *Ys,
+                          const int32_t *inv, const float *gate, int T, int k, int d, void *y,
+                          hipStream_t s);
 
 }  // namespace moe

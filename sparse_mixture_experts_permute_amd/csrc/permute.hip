@@ -42,8 +42,9 @@ __global__ __launch_bounds__(PM_CHUNK) void permute_hist_kernel(const int32_t *_
 __global__ __launch_bounds__(256) void permute_scan_kernel(
     int32_t *__restrict__ blk, int nb, int E, int P, int T, int bm0, int bm1,
     int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int32_t *__restrict__ mtiles0,
-    int32_t *__restrict__ mtiles1, int32_t *__restrict__ shared_seg) {
-  __shared__ int s0[256], s1[256], s2[256];
+    int32_t *__restrict__ mtiles1, int32_t *__restrict__ shared_seg,
+    int32_t *__restrict__ active) {
+  __shared__ int s0[256], s1[256], s2[256], s3[256];
   const int e = threadIdx.x;
   int total = 0;
   if (e < E)
@@ -51,18 +52,24 @@ __global__ __launch_bounds__(256) void permute_scan_kernel(
   s0[e] = e < E ? total : 0;
   s1[e] = e < E ? (total + bm0 - 1) / bm0 : 0;
   s2[e] = e < E ? (total + bm1 - 1) / bm1 : 0;
+  s3[e] = (e < E && total > 0) ? 1 : 0;
   __syncthreads();
   // inclusive Hillis-Steele scans over the experts (256 entries)
   for (int off = 1; off < 256; off <<= 1) {
     int a0 = e >= off ? s0[e - off] : 0;
     int a1 = e >= off ? s1[e - off] : 0;
     int a2 = e >= off ? s2[e - off] : 0;
+    int a3 = e >= off ? s3[e - off] : 0;
     __syncthreads();
     s0[e] += a0;
     s1[e] += a1;
     s2[e] += a2;
+    s3[e] += a3;
     __syncthreads();
   }
+  // compact list of the experts that received pairs; active[E] = their number
+  if (e < E && total > 0) active[s3[e] - 1] = e;
+  if (e == 0) active[E] = s3[255];
   if (e < E) {
     const int excl = s0[e] - total;
     counts[e] = total;
@@ -87,6 +94,8 @@ __global__ __launch_bounds__(256) void permute_scan_kernel(
     shared_seg[3] = (T + bm0 - 1) / bm0;
     shared_seg[4] = 0;
     shared_seg[5] = (T + bm1 - 1) / bm1;
+    shared_seg[6] = 0;  // the shared expert as a one-entry active list: {0}, count 1
+    shared_seg[7] = 1;
   }
 }
 
@@ -120,6 +129,113 @@ __global__ __launch_bounds__(PM_CHUNK) void permute_scatter_kernel(
   }
 }
 
+// Small batches: histogram, scan and stable scatter in one workgroup (one
+// launch instead of three).  Pairs are processed in order in chunks of 1024;
+// within a chunk a pair's slot is cursor[e] + (pairs of e in earlier waves of
+// the chunk) + (rank among equal experts inside its wave); cursor[e] then
+// advances by the chunk's count.  Same result as the three-kernel path.
+constexpr int PS_THREADS = 1024;
+constexpr int PS_WAVES = PS_THREADS / kWave;
+
+__global__ __launch_bounds__(PS_THREADS) void permute_small_kernel(
+    const int32_t *__restrict__ idx, int P, int E, int T, int bm0, int bm1,
+    int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int32_t *__restrict__ perm,
+    int32_t *__restrict__ inv, int32_t *__restrict__ mtiles0, int32_t *__restrict__ mtiles1,
+    int32_t *__restrict__ shared_seg, int32_t *__restrict__ active) {
+  __shared__ int hist[256], cursor[256], s1[256], s2[256], s3[256];
+  __shared__ int wc[PS_WAVES][256];
+  const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
+  if (tid < 256) hist[tid] = 0;
+  __syncthreads();
+  for (int p = tid; p < P; p += PS_THREADS) {
+    const int e = idx[p];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&hist[e], 1);
+  }
+  __syncthreads();
+  if (tid < 256) {
+    const int c = tid < E ? hist[tid] : 0;
+    cursor[tid] = c;
+    s1[tid] = tid < E ? (c + bm0 - 1) / bm0 : 0;
+    s2[tid] = tid < E ? (c + bm1 - 1) / bm1 : 0;
+    s3[tid] = (tid < E && c > 0) ? 1 : 0;
+  }
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {  // inclusive scans over the experts
+    int a0 = 0, a1 = 0, a2 = 0, a3 = 0;
+    if (tid < 256 && tid >= off) {
+      a0 = cursor[tid - off];
+      a1 = s1[tid - off];
+      a2 = s2[tid - off];
+      a3 = s3[tid - off];
+    }
+    __syncthreads();
+    if (tid < 256) {
+      cursor[tid] += a0;
+      s1[tid] += a1;
+      s2[tid] += a2;
+      s3[tid] += a3;
+    }
+    __syncthreads();
+  }
+  if (tid < E) {
+    const int c = hist[tid];
+    const int excl = cursor[tid] - c;
+    counts[tid] = c;
+    offsets[tid] = excl;
+    mtiles0[tid] = s1[tid] - (c + bm0 - 1) / bm0;
+    mtiles1[tid] = s2[tid] - (c + bm1 - 1) / bm1;
+    if (c > 0) active[s3[tid] - 1] = tid;
+  }
+  if (tid == 0) {
+    offsets[E] = cursor[255];  // inclusive scan: the number of placed pairs
+    mtiles0[E] = s1[255];
+    mtiles1[E] = s2[255];
+    active[E] = s3[255];
+    shared_seg[0] = 0;
+    shared_seg[1] = T;
+    shared_seg[2] = 0;
+    shared_seg[3] = (T + bm0 - 1) / bm0;
+    shared_seg[4] = 0;
+    shared_seg[5] = (T + bm1 - 1) / bm1;
+    shared_seg[6] = 0;
+    shared_seg[7] = 1;
+  }
+  __syncthreads();
+  if (tid < 256) cursor[tid] -= (tid < E ? hist[tid] : 0);  // exclusive start of each expert
+  __syncthreads();
+  for (int c0 = 0; c0 < P; c0 += PS_THREADS) {
+    for (int i = tid; i < PS_WAVES * 256; i += PS_THREADS) (&wc[0][0])[i] = 0;
+    __syncthreads();
+    const int p = c0 + tid;
+    const int ev = p < P ? idx[p] : -1;
+    const bool valid = (unsigned)ev < (unsigned)E;
+    const int e = valid ? ev : 0;
+    uint64_t same = __ballot(valid);
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit) {
+      const uint64_t ones = __ballot(valid && ((e >> bit) & 1));
+      same &= ((e >> bit) & 1) ? ones : ~ones;
+    }
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+    const int rank = __popcll(same & below);
+    if (valid && rank == 0) wc[w][e] = __popcll(same);
+    __syncthreads();
+    if (valid) {
+      int pos = cursor[e] + rank;
+      for (int w2 = 0; w2 < w; ++w2) pos += wc[w2][e];
+      perm[pos] = p;
+      inv[p] = pos;
+    }
+    __syncthreads();
+    if (tid < E) {
+      int add = 0;
+      for (int w2 = 0; w2 < PS_WAVES; ++w2) add += wc[w2][tid];
+      cursor[tid] += add;
+    }
+    __syncthreads();
+  }
+}
+
 // Xp[s][:] = x[perm[s] / k][:]; one block copies 4 rows with 16-byte accesses.
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint4 *__restrict__ x,
                                                           const int32_t *__restrict__ perm,
@@ -140,12 +256,17 @@ int permute_nblocks(int P) { return (P + PM_CHUNK - 1) / PM_CHUNK; }
 hipError_t launch_permute(const int32_t *idx, int T, int E, int k, int bm0, int bm1,
                           int32_t *blk, int32_t *counts, int32_t *offsets, int32_t *perm,
                           int32_t *inv, int32_t *mtiles0, int32_t *mtiles1,
-                          int32_t *shared_seg, hipStream_t s) {
+                          int32_t *shared_seg, int32_t *active, hipStream_t s) {
   const int P = T * k;
+  if (P <= 8 * PS_THREADS) {
+    hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(PS_THREADS), 0, s, idx, P, E, T, bm0,
+                       bm1, counts, offsets, perm, inv, mtiles0, mtiles1, shared_seg, active);
+    return hipGetLastError();
+  }
   const int nb = permute_nblocks(P);
   hipLaunchKernelGGL(permute_hist_kernel, dim3(nb), dim3(PM_CHUNK), 0, s, idx, P, E, blk);
   hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(256), 0, s, blk, nb, E, P, T, bm0, bm1,
-                     counts, offsets, mtiles0, mtiles1, shared_seg);
+                     counts, offsets, mtiles0, mtiles1, shared_seg, active);
   hipLaunchKernelGGL(permute_scatter_kernel, dim3(nb), dim3(PM_CHUNK), 0, s, idx, P, E, blk,
                      perm, inv);
   return hipGetLastError();

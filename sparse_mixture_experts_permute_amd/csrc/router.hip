@@ -1,16 +1,28 @@
-// Router scores, top-k selection and softmax gate, fused in one kernel.
+// Router scores, top-k selection and softmax gate.
 //
-// logits[t][e] = sum_i x[t][i] * Wg[e][i] (+ bias[e])  -- fp32 accumulate on the
-// vector ALU (the router is a skinny contraction; matrix cores are kept for the
-// expert GEMMs).  Then, per token, k rounds of a wavefront arg-max (ties go to
-// the lower expert index) and gate_j = exp(l_j - l_0) / sum_j' exp(l_j' - l_0)
-// over the selected logits ("Chapter 10 MoE", section 10.3; "Mistral 8x7B SMoE
-// architecture deep dive", section 3.2).
+// logits[t][e] = sum_i x[t][i] * Wg[e][i] (+ bias[e]), then per token the k
+// largest scores (ties go to the lower expert index) and
+// gate_j = exp(l_j - l_0) / sum_j' exp(l_j' - l_0) over the selected scores
+// ("Chapter 10 MoE", section 10.3; "Mistral 8x7B SMoE architecture deep
+// dive", section 3.2).  The router is a skinny contraction and runs on the
+// vector ALU in fp32 (bf16 pairs through v_dot2_f32_bf16); the matrix cores
+// are kept for the expert GEMMs.
 //
-// Work split: a 256-thread block owns 32 tokens and every expert.  Thread
-// (tg = tid/32, eg = tid%32) accumulates tokens 4*tg..4*tg+3 against experts
-// eg, eg+32, ..., so each Wg element fetched into LDS feeds 32 tokens.  The
-// feature dimension is streamed through LDS in 128-byte row chunks.
+// Two kernels:
+//  scores : partial scores over S slices of the feature dimension, each slice
+//           written to its own plane of a [S][T][E] buffer; S is chosen so the
+//           grid fills the GPU.  Two shapes:
+//           - up to 32 experts: one wavefront per (token, slice); lanes split the
+//             slice with 16-byte loads, keep all E sums in registers and reduce
+//             them with a butterfly at the end (the router weights, at most
+//             32 x d, stay in L2);
+//           - more experts: a register-tiled VALU GEMM.  A 256-thread block owns
+//             64 tokens x 64 experts x one slice; each thread keeps 4 x 4 sums
+//             and streams its slice through LDS in 64-element chunks
+//             (double-buffered, one barrier per chunk).
+//  topk   : one wavefront per token sums the S partials in a fixed order (so
+//           the scores do not depend on scheduling), adds the bias, writes the
+//           scores, and runs k rounds of a wavefront arg-max and the gate.
 #include "common.h"
 #include "kernels.h"
 
@@ -18,25 +30,20 @@ namespace moe {
 
 namespace {
 
-constexpr int RT_TOK = 32;      // tokens per block
-constexpr int RT_THREADS = 256;
-constexpr int RT_EMAX = 256;
-constexpr int RT_EJ = RT_EMAX / 32;  // experts per thread at most
-constexpr int RT_ROWB = 128;         // bytes of a row chunk
-constexpr int RT_PADB = 16;          // LDS row padding (bytes)
+constexpr int RS_TOK = 64, RS_EXP = 64;  // block tile
+constexpr int RS_THREADS = 256;
+constexpr int RS_ROWB = 128;            // bytes of a row chunk (64 bf16 / 32 fp32)
+constexpr int RS_LDW = (RS_ROWB + 16) / 16;  // padded LDS row stride in uint4
 
 template <typename T> struct RouterTraits;
 template <> struct RouterTraits<float> {
-  static constexpr int DC = RT_ROWB / 4;  // elements per chunk
-  static constexpr int VEC = 4;           // elements per 16-byte load
+  static constexpr int VEC = 4;  // elements per 16 bytes
 };
 template <> struct RouterTraits<bf16_t> {
-  static constexpr int DC = RT_ROWB / 2;
   static constexpr int VEC = 8;
 };
 
 __device__ __forceinline__ float dot16b(const uint4 &a, const uint4 &b, float acc, float) {
-  // fp32 x 4
   acc = fmaf(__uint_as_float(a.x), __uint_as_float(b.x), acc);
   acc = fmaf(__uint_as_float(a.y), __uint_as_float(b.y), acc);
   acc = fmaf(__uint_as_float(a.z), __uint_as_float(b.z), acc);
@@ -45,7 +52,6 @@ __device__ __forceinline__ float dot16b(const uint4 &a, const uint4 &b, float ac
 }
 
 __device__ __forceinline__ float dot16b(const uint4 &a, const uint4 &b, float acc, bf16_t) {
-  // bf16 x 8 through the packed bf16 dot (fp32 accumulate)
   acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, a.x),
                                         __builtin_bit_cast(bf16x2_v, b.x), acc, false);
   acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, a.y),
@@ -57,156 +63,259 @@ __device__ __forceinline__ float dot16b(const uint4 &a, const uint4 &b, float ac
   return acc;
 }
 
+// grid: (token tiles, expert tiles, feature slices); slice s covers
+// features [s*dslice, (s+1)*dslice), dslice a multiple of the chunk.
 template <typename T>
-__global__ __launch_bounds__(RT_THREADS) void router_topk_kernel(
-    const T *__restrict__ x, const T *__restrict__ Wg, const float *__restrict__ bias, int T_,
-    int d, int E, int k, int32_t *__restrict__ idx, float *__restrict__ gate,
-    float *__restrict__ logits) {
-  constexpr int DC = RouterTraits<T>::DC;
+__global__ __launch_bounds__(RS_THREADS, 2) void router_scores_kernel(
+    const T *__restrict__ x, const T *__restrict__ Wg, int T_, int d, int E, int dslice,
+    float *__restrict__ part) {
   constexpr int VEC = RouterTraits<T>::VEC;
-  constexpr int CPR = RT_ROWB / 16;            // 16-byte chunks per row chunk
-  constexpr int LDR = (RT_ROWB + RT_PADB) / 16;  // LDS row stride in uint4
-  __shared__ uint4 xs[RT_TOK * LDR];
-  __shared__ uint4 ws[RT_EMAX * LDR];
-  __shared__ float ls[RT_TOK][RT_EMAX + 1];
-  __shared__ float selv[RT_THREADS / kWave][RT_EMAX];
-  __shared__ int seli[RT_THREADS / kWave][RT_EMAX];
+  constexpr int CPR = RS_ROWB / 16;  // uint4 per row chunk (8)
+  __shared__ uint4 xs[2][RS_TOK * RS_LDW];
+  __shared__ uint4 ws[2][RS_EXP * RS_LDW];
 
   const int tid = threadIdx.x;
-  const int t0 = blockIdx.x * RT_TOK;
-  const int tg = tid / 32, eg = tid % 32;
-  const int ej = (E + 31) / 32;
-
-  float acc[4][RT_EJ];
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int j = 0; j < RT_EJ; ++j) acc[a][j] = 0.f;
+  const int t0 = blockIdx.x * RS_TOK, e0 = blockIdx.y * RS_EXP;
+  const int s = blockIdx.z;
+  const int tg = tid / 16, eg = tid % 16;  // 16 x 16 threads, 4 x 4 outputs each
 
   const uint4 *xg = reinterpret_cast<const uint4 *>(x);
   const uint4 *wgg = reinterpret_cast<const uint4 *>(Wg);
-  const size_t rowq = (size_t)d / VEC;  // uint4 per row
+  const size_t rowq = (size_t)d / VEC;
+  const size_t q0 = (size_t)s * dslice / VEC;
+  const int nchunk = dslice * (int)sizeof(T) / RS_ROWB;
 
-  for (int c0 = 0; c0 < d; c0 += DC) {
-    const size_t cq = (size_t)c0 / VEC;
-    // stage x chunk: RT_TOK rows x CPR uint4 (one per thread)
-    for (int i = tid; i < RT_TOK * CPR; i += RT_THREADS) {
-      int r = i / CPR, q = i % CPR;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (t0 + r < T_) v = xg[(size_t)(t0 + r) * rowq + cq + q];
-      xs[r * LDR + q] = v;
+  // each thread stages 2 x-chunks and 2 Wg-chunks of 16 bytes per row chunk
+  uint4 rx[2], rw[2];
+  auto gload = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int idx = tid + i * RS_THREADS;  // 0..511: 64 rows x 8 uint4
+      const int r = idx / CPR, q = idx % CPR;
+      const size_t col = q0 + (size_t)c * CPR + q;
+      rx[i] = (t0 + r < T_) ? xg[(size_t)(t0 + r) * rowq + col] : make_uint4(0, 0, 0, 0);
+      rw[i] = (e0 + r < E) ? wgg[(size_t)(e0 + r) * rowq + col] : make_uint4(0, 0, 0, 0);
     }
-    for (int i = tid; i < E * CPR; i += RT_THREADS) {
-      int r = i / CPR, q = i % CPR;
-      ws[r * LDR + q] = wgg[(size_t)r * rowq + cq + q];
+  };
+  auto lstore = [&](int b) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int idx = tid + i * RS_THREADS;
+      const int r = idx / CPR, q = idx % CPR;
+      xs[b][r * RS_LDW + q] = rx[i];
+      ws[b][r * RS_LDW + q] = rw[i];
     }
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < CPR; ++q) {
-      uint4 xv[4];
-#pragma unroll
-      for (int a = 0; a < 4; ++a) xv[a] = xs[(tg * 4 + a) * LDR + q];
-#pragma unroll
-      for (int j = 0; j < RT_EJ; ++j) {
-        if (j < ej) {
-          int e = eg + 32 * j;
-          if (e < E) {
-            uint4 wv = ws[e * LDR + q];
-#pragma unroll
-            for (int a = 0; a < 4; ++a) acc[a][j] = dot16b(xv[a], wv, acc[a][j], T());
-          }
-        }
-      }
-    }
-    __syncthreads();
-  }
+  };
 
-  // scores to LDS (and to global when requested)
+  float acc[4][4];
 #pragma unroll
-  for (int j = 0; j < RT_EJ; ++j) {
-    int e = eg + 32 * j;
-    if (j < ej && e < E) {
-      float b = bias ? bias[e] : 0.f;
+  for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        int tl = tg * 4 + a;
-        float v = acc[a][j] + b;
-        ls[tl][e] = v;
-        if (logits && t0 + tl < T_) logits[(size_t)(t0 + tl) * E + e] = v;
-      }
-    }
-  }
+    for (int j = 0; j < 4; ++j) acc[a][j] = 0.f;
+
+  gload(0);
+  lstore(0);
   __syncthreads();
+  for (int c = 0; c < nchunk; ++c) {
+    const int b = c & 1;
+    if (c + 1 < nchunk) gload(c + 1);
+#pragma unroll 2
+    for (int q = 0; q < CPR; ++q) {
+      uint4 xv[4], wv[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) xv[a] = xs[b][(tg * 4 + a) * RS_LDW + q];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) wv[j] = ws[b][(eg + 16 * j) * RS_LDW + q];
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[a][j] = dot16b(xv[a], wv[j], acc[a][j], T());
+    }
+    if (c + 1 < nchunk) lstore(b ^ 1);
+    __syncthreads();
+  }
 
-  // top-k + gate: each wave takes 8 tokens
-  const int w = tid / kWave, lane = lane_id();
-  for (int tl = w * (RT_TOK / 4); tl < (w + 1) * (RT_TOK / 4); ++tl) {
-    const int t = t0 + tl;
-    if (t >= T_) break;
-    float v[4];
+  float *out = part + (size_t)s * T_ * E;
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const int t = t0 + tg * 4 + a;
+    if (t >= T_) continue;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      int e = lane + kWave * j;
-      v[j] = e < E ? ls[tl][e] : -INFINITY;
+      const int e = e0 + eg + 16 * j;
+      if (e < E) out[(size_t)t * E + e] = acc[a][j];
     }
-    unsigned taken = 0;
-    for (int r = 0; r < k; ++r) {
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
+  }
+}
+
+// Up to 32 experts: one wavefront per (token, slice of NS*64*VEC features).
+template <typename T, int EB>
+__global__ __launch_bounds__(256) void router_scores_narrow_kernel(
+    const T *__restrict__ x, const T *__restrict__ Wg, int T_, int d, int E, int ns,
+    float *__restrict__ part) {
+  constexpr int VEC = RouterTraits<T>::VEC;
+  const int w = threadIdx.x / kWave, lane = lane_id();
+  const int t = blockIdx.x * 4 + w;
+  const int s = blockIdx.y;
+  if (t >= T_) return;
+  const uint4 *xg = reinterpret_cast<const uint4 *>(x);
+  const uint4 *wgg = reinterpret_cast<const uint4 *>(Wg);
+  const size_t rowq = (size_t)d / VEC;
+  const size_t q0 = (size_t)s * ns * kWave + lane;
+  float acc[EB];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        int e = lane + kWave * j;
-        if (e < E && !(taken & (1u << j)) && (bi == 0x7fffffff || v[j] > bv)) {
-          bv = v[j];
-          bi = e;
-        }
-      }
+  for (int e = 0; e < EB; ++e) acc[e] = 0.f;
+  for (int i = 0; i < ns; ++i) {
+    const size_t q = q0 + (size_t)i * kWave;
+    const uint4 xv = xg[(size_t)t * rowq + q];
 #pragma unroll
-      for (int off = kWave / 2; off > 0; off >>= 1) {
-        float ov = __shfl_xor(bv, off);
-        int oi = __shfl_xor(bi, off);
-        if (oi != 0x7fffffff && (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi))) {
-          bv = ov;
-          bi = oi;
-        }
-      }
-      if ((bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
-      if (lane == 0) {
-        selv[w][r] = bv;
-        seli[w][r] = bi;
+    for (int e = 0; e < EB; ++e)
+      if (e < E) acc[e] = dot16b(xv, wgg[(size_t)e * rowq + q], acc[e], T());
+  }
+  float *out = part + ((size_t)s * T_ + t) * E;
+#pragma unroll
+  for (int e = 0; e < EB; ++e) {
+    if (e < E) {
+      float v = acc[e];
+#pragma unroll
+      for (int off = kWave / 2; off > 0; off >>= 1) v += __shfl_xor(v, off);
+      if (lane == 0) out[e] = v;
+    }
+  }
+}
+
+// One wavefront per token: scores, k rounds of arg-max, softmax over the selected.
+__global__ __launch_bounds__(256) void router_topk_kernel(
+    const float *__restrict__ part, int S, const float *__restrict__ bias, int T_, int E, int k,
+    int32_t *__restrict__ idx, float *__restrict__ gate, float *__restrict__ logits) {
+  __shared__ float selv[4][256];
+  __shared__ int seli[4][256];
+  const int w = threadIdx.x / kWave, lane = lane_id();
+  const int t = blockIdx.x * 4 + w;
+  if (t >= T_) return;
+  float v[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = lane + kWave * j;
+    float l = -INFINITY;
+    if (e < E) {
+      l = 0.f;
+      for (int s = 0; s < S; ++s) l += part[((size_t)s * T_ + t) * E + e];
+      if (bias) l += bias[e];
+      if (logits) logits[(size_t)t * E + e] = l;
+    }
+    v[j] = l;
+  }
+  unsigned taken = 0;
+  for (int r = 0; r < k; ++r) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = lane + kWave * j;
+      if (e < E && !(taken & (1u << j)) && (bi == 0x7fffffff || v[j] > bv)) {
+        bv = v[j];
+        bi = e;
       }
     }
-    // lane 0's selections become visible to the whole wave
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    const float m = selv[w][0];
-    float z = 0.f;
-    for (int r = lane; r < k; r += kWave) z += expf(selv[w][r] - m);
 #pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) z += __shfl_xor(z, off);
-    for (int r = lane; r < k; r += kWave) {
-      idx[(size_t)t * k + r] = seli[w][r];
-      gate[(size_t)t * k + r] = expf(selv[w][r] - m) / z;
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oi = __shfl_xor(bi, off);
+      if (oi != 0x7fffffff && (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi))) {
+        bv = ov;
+        bi = oi;
+      }
     }
-    __builtin_amdgcn_wave_barrier();
+    if ((bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
+    if (lane == 0) {
+      selv[w][r] = bv;
+      seli[w][r] = bi;
+    }
+  }
+  // lane 0's selections become visible to the whole wave
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  const float m = selv[w][0];
+  float z = 0.f;
+  for (int r = lane; r < k; r += kWave) z += expf(selv[w][r] - m);
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) z += __shfl_xor(z, off);
+  for (int r = lane; r < k; r += kWave) {
+    idx[(size_t)t * k + r] = seli[w][r];
+    gate[(size_t)t * k + r] = expf(selv[w][r] - m) / z;
+  }
+}
+
+// Feature slices for the score kernels (enough work items to fill the GPU).
+// Narrow kernel: a slice is ns steps of 64 lanes x 16 bytes.  Tiled kernel: a
+// slice is a whole number of 128-byte chunks.
+struct RouterSplit {
+  bool narrow;
+  int S, ns;
+};
+RouterSplit router_split(int T, int d, int E, int esize) {
+  RouterSplit r{};
+  const int vec = 16 / esize;
+  r.narrow = E <= 32 && d % (kWave * vec) == 0;
+  if (r.narrow) {
+    const int steps = d / (kWave * vec);   // 16-byte steps per lane over the whole row
+    const long long waves_per_slice = T;   // one wave per token and slice
+    int S = steps;                         // finest split: one step per lane
+    while (S > 1 && (steps % (S / 2) == 0) && waves_per_slice * (S / 2) >= 2048) S /= 2;
+    r.S = S;
+    r.ns = steps / S;
+    return r;
+  }
+  const int chunk = RS_ROWB / esize;
+  const int nchunks = d / chunk;
+  const long long tiles = (long long)((T + RS_TOK - 1) / RS_TOK) * ((E + RS_EXP - 1) / RS_EXP);
+  int S = 1;
+  while (tiles * S < 512 && S * 2 <= nchunks && nchunks % (S * 2) == 0) S *= 2;
+  r.S = S;
+  r.ns = 0;
+  return r;
+}
+
+template <typename T>
+void launch_scores(const RouterSplit &r, const void *x, const void *Wg, int T_, int d, int E,
+                   float *part, hipStream_t s) {
+  if (r.narrow) {
+    dim3 grid((T_ + 3) / 4, r.S);
+    if (E <= 8)
+      hipLaunchKernelGGL((router_scores_narrow_kernel<T, 8>), grid, dim3(256), 0, s,
+                         (const T *)x, (const T *)Wg, T_, d, E, r.ns, part);
+    else if (E <= 16)
+      hipLaunchKernelGGL((router_scores_narrow_kernel<T, 16>), grid, dim3(256), 0, s,
+                         (const T *)x, (const T *)Wg, T_, d, E, r.ns, part);
+    else
+      hipLaunchKernelGGL((router_scores_narrow_kernel<T, 32>), grid, dim3(256), 0, s,
+                         (const T *)x, (const T *)Wg, T_, d, E, r.ns, part);
+  } else {
+    dim3 grid((T_ + RS_TOK - 1) / RS_TOK, (E + RS_EXP - 1) / RS_EXP, r.S);
+    hipLaunchKernelGGL(router_scores_kernel<T>, grid, dim3(RS_THREADS), 0, s, (const T *)x,
+                       (const T *)Wg, T_, d, E, d / r.S, part);
   }
 }
 
 }  // namespace
 
+size_t router_partial_bytes(int T, int d, int E, int esize) {
+  return (size_t)router_split(T, d, E, esize).S * T * E * 4;
+}
+
 hipError_t launch_router(int dtype, const void *x, const void *Wg, const float *bias, int T,
                          int d, int E, int k, int32_t *idx, float *gate, float *logits,
-                         hipStream_t s) {
-  dim3 grid((T + RT_TOK - 1) / RT_TOK);
+                         float *part, hipStream_t s) {
+  const int es = dtype == 1 ? 2 : 4;
+  const RouterSplit r = router_split(T, d, E, es);
   if (dtype == 1)
-    hipLaunchKernelGGL(router_topk_kernel<bf16_t>, grid, dim3(RT_THREADS), 0, s,
-                       (const bf16_t *)x, (const bf16_t *)Wg, bias, T, d, E, k, idx, gate,
-                       logits);
+    launch_scores<bf16_t>(r, x, Wg, T, d, E, part, s);
   else
-    hipLaunchKernelGGL(router_topk_kernel<float>, grid, dim3(RT_THREADS), 0, s,
-                       (const float *)x, (const float *)Wg, bias, T, d, E, k, idx, gate,
-                       logits);
+    launch_scores<float>(r, x, Wg, T, d, E, part, s);
+  hipLaunchKernelGGL(router_topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, part, r.S, bias, T,
+                     E, k, idx, gate, logits);
   return hipGetLastError();
 }
 

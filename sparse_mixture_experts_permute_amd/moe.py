@@ -37,7 +37,9 @@ def lib():
                            "(run python -m sparse_mixture_experts_permute_amd.build)")
         L = ctypes.CDLL(LIB_PATH)
         vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
-        L.moe_route.argtypes = [vp, vp, vp, i, i, i, i, i, vp, vp, vp, vp]
+        L.moe_route_workspace_bytes.argtypes = [i, i, i, i]
+        L.moe_route_workspace_bytes.restype = sz
+        L.moe_route.argtypes = [vp, vp, vp, i, i, i, i, i, vp, vp, vp, vp, sz, vp]
         L.moe_route.restype = i
         L.moe_permute_workspace_bytes.argtypes = [i, i, i]
         L.moe_permute_workspace_bytes.restype = sz
@@ -108,8 +110,10 @@ def route(x: torch.Tensor, Wg: torch.Tensor, k: int, bias: torch.Tensor | None =
     idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
     gate = torch.empty((T, k), dtype=torch.float32, device=x.device)
     logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    nbytes = lib().moe_route_workspace_bytes(T, d, E, _dt(x))
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=x.device)
     _check(lib().moe_route(_p(x), _p(Wg), _p(bias), T, d, E, k, _dt(x), _p(idx), _p(gate),
-                           _p(logits), _stream()), "moe_route")
+                           _p(logits), _p(ws), nbytes, _stream()), "moe_route")
     return idx, gate, logits
 
 

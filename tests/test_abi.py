@@ -68,17 +68,26 @@ def test_workspace_sizes(L):
 def test_argument_errors_before_launch(L):
     vp = ctypes.c_void_p
     fake = vp(0x1000)
+    big = 1 << 30
     # bad dtype
-    assert L.moe_route(fake, fake, None, 4, 64, 8, 2, 9, fake, fake, None, None) == -2
+    assert L.moe_route(fake, fake, None, 4, 64, 8, 2, 9, fake, fake, None, fake, big, None) == -2
     # k > E, k < 1, E > 256, d not a multiple of 64
-    assert L.moe_route(fake, fake, None, 4, 64, 8, 9, 1, fake, fake, None, None) == -1
-    assert L.moe_route(fake, fake, None, 4, 64, 8, 0, 1, fake, fake, None, None) == -1
-    assert L.moe_route(fake, fake, None, 4, 64, 300, 2, 1, fake, fake, None, None) == -1
-    assert L.moe_route(fake, fake, None, 4, 65, 8, 2, 1, fake, fake, None, None) == -1
+    assert L.moe_route(fake, fake, None, 4, 64, 8, 9, 1, fake, fake, None, fake, big, None) == -1
+    assert L.moe_route(fake, fake, None, 4, 64, 8, 0, 1, fake, fake, None, fake, big, None) == -1
+    assert L.moe_route(fake, fake, None, 4, 64, 300, 2, 1, fake, fake, None, fake, big, None) == -1
+    assert L.moe_route(fake, fake, None, 4, 65, 8, 2, 1, fake, fake, None, fake, big, None) == -1
     # missing required pointers
-    assert L.moe_route(None, fake, None, 4, 64, 8, 2, 1, fake, fake, None, None) == -1
+    assert L.moe_route(None, fake, None, 4, 64, 8, 2, 1, fake, fake, None, fake, big, None) == -1
+    assert L.moe_route(fake, fake, None, 4, 64, 8, 2, 1, fake, fake, None, None, big, None) == -1
+    # workspace too small / misaligned
+    assert L.moe_route(fake, fake, None, 4, 64, 8, 2, 1, fake, fake, None, vp(0x100000), 8,
+                       None) == -3
+    assert L.moe_route(fake, fake, None, 4, 64, 8, 2, 1, fake, fake, None, vp(0x100008), big,
+                       None) == -3
+    assert L.moe_route_workspace_bytes(4, 64, 8, 1) >= 4 * 8 * 4
+    assert L.moe_route_workspace_bytes(4, 64, 8, 5) == 0
     # T = 0 is a no-op
-    assert L.moe_route(None, None, None, 0, 64, 8, 2, 1, None, None, None, None) == 0
+    assert L.moe_route(None, None, None, 0, 64, 8, 2, 1, None, None, None, None, 0, None) == 0
     # forward: shared-expert pointers inconsistent with d_ff_shared
     args = [fake, fake, None, fake, fake, fake, fake, None, None, 64, 4, 8, 2, 64, 64, 1,
             fake, 1 << 30, vp(0x2000), None]

@@ -224,6 +224,11 @@ EDGE = [
     ("E256_k8_shared", 33, 128, 256, 64, 8, "bf16", 192, None),
     ("shared_f32", 45, 128, 16, 64, 4, "f32", 128, None),
     ("N_tail", 70, 192, 5, 192, 2, "bf16", 0, None),
+    # weight-streaming path (few rows per expert)
+    ("skinny_T5", 5, 256, 4, 256, 2, "bf16", 0, None),
+    ("skinny_hot_expert_two_passes", 70, 256, 4, 512, 2, "bf16", 0, ("hot", 2, 100.0)),
+    ("skinny_shared", 40, 256, 8, 256, 2, "bf16", 256, None),
+    ("skinny_E256_k8", 64, 512, 256, 256, 8, "bf16", 0, None),
 ]
 
 
