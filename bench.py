@@ -149,6 +149,23 @@ def run_workload(cfg, host, dev, steps, warmup, flush_mb=0, graph=False):
     return out
 
 
+def measured_traffic(cfg):
+    """HBM traffic per dispatch of the SwiGLU GEMM from the committed rocprofv3
+    counter runs (profiles/traffic.json), or None when those counters were
+    taken on another workload or on a different GEMM source."""
+    import hashlib
+    try:
+        rec = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))
+        src = open(os.path.join(ROOT, "sparse_mixture_experts_permute_amd", "csrc", "gemm.hip"),
+                   "rb").read()
+    except (OSError, ValueError):
+        return None
+    sha = hashlib.sha256(src).hexdigest()[:16]
+    if rec.get("gemm_source_sha256_prefix") != sha or rec.get("workload") != cfg.name:
+        return None
+    return rec.get("traffic_bytes")
+
+
 def roofline_for(cfg, res):
     from sparse_mixture_experts_permute_amd import moe
     a = algorithmic(cfg, res["counts"])
@@ -164,7 +181,8 @@ def roofline_for(cfg, res):
         ach = a["g1_bytes"] / (g1_ms * 1e-3) / 1e9
         rl = dict(bound="hbm", achieved=round(ach, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                   frac=round(ach / PEAK_HBM_GBS, 4))
-    rl.update(traffic=None, kernel="grouped_gemm_swiglu", kernel_ms=round(g1_ms, 4),
+    rl.update(traffic=measured_traffic(cfg), kernel="grouped_gemm_swiglu",
+              kernel_ms=round(g1_ms, 4),
               algorithmic_flop=a["g1_flop"], algorithmic_bytes=a["g1_bytes"])
     # whole-layer fractions
     lt = res["ms"] * 1e-3
