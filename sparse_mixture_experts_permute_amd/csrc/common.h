@@ -47,9 +47,6 @@ __device__ __forceinline__ void global_to_lds16(const void *g, uint4 *lds) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
 }
 
-// Wait until this wavefront's outstanding vector-memory operations are done.
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x3f70); }
-
 __device__ __forceinline__ float silu(float a) { return a / (1.0f + __expf(-a)); }
 
 // First index i in [0, n) with a[i+1] > g, for non-decreasing a[0..n] with a[0] <= g.

@@ -14,9 +14,10 @@
 // blocks of W1 and W3 for the same output columns, so a wave holds the W1 and
 // W3 accumulators of an output element in the same lane and register and the
 // SiLU * mul epilogue needs no data movement.  K is streamed in BK slices
-// through double-buffered LDS (one barrier per slice; the next slice's global
-// loads are in flight while the current one feeds the MFMAs).  LDS rows are
-// padded by 16 bytes, which keeps the 16-byte fragment reads conflict-free.
+// through double-buffered LDS.  The register-staged kernel (fp32, and bf16
+// with K not a multiple of 64) pads LDS rows by 16 bytes; the bf16 kernel
+// with direct global->LDS loads swizzles 16-byte chunks instead.  Both keep
+// the 16-byte fragment reads free of bank conflicts.
 //
 // Operands: both A and B are K-contiguous ([rows][K] and [N][K]), the layout
 // in which every lane of a 32x32 MFMA reads 16 consecutive bytes of K.
@@ -250,8 +251,16 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_kernel(
 // with f(row) = (row >> 1) & 7, so LDS chunk c of row r holds global chunk
 // c ^ f(r).  A fragment read (16 lanes, 16 consecutive rows, one global chunk)
 // then touches 16 distinct 16-byte slots modulo 256 bytes: conflict-free on
-// the 64 LDS banks.  Two stages of (BM + BNB) x 128 bytes; the loads of slice
-// kt+1 run while slice kt feeds the MFMAs, with no staging registers.
+// the 64 LDS banks.  Two stages of (BM + BNB) x 128 bytes, no staging
+// registers.
+//
+// The loads are bound by how many requests a CU keeps in flight, not by the
+// bandwidth of L2 or HBM, so the schedule gives each slice's loads as much
+// time as the two stages allow: every wave reads ALL fragments of a slice into
+// registers at the slice's start; once every wave has done so (a barrier a
+// quarter of the way in), the stage is refilled with the slice two ahead, and
+// those loads are spread over the next 32 MFMAs.  A load thus has about 1.75
+// slices of MFMA work to land (one slice with the stage held until the end).
 // ---------------------------------------------------------------------------
 // Split K (down projection only): blockIdx.y picks one of gridDim.y equal K
 // ranges and its fp32 partial goes to output plane blockIdx.y (plane elements
@@ -360,79 +369,66 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
             0, 0, 0);
   };
 
-  // Software pipeline: the fragments of K step s+1 are read while the MFMAs
-  // of step s run, and the first step of the next slice is read right after
-  // the slice barrier, underneath the MFMAs of the last step of the current
-  // one.  The loop body has no early exit, so the accumulators stay in place.
+  // Pipeline: a slice's fragments are all read into registers at its start,
+  // so its LDS stage can be refilled (with the slice two ahead) once every
+  // wave has read it, a quarter of the way into the slice; the load of a
+  // slice then has about 1.75 slices of MFMA work to land instead of one.
   const int nk = kpart / 64;
-  uint4 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
-  // Scheduling fences keep the program order below: the compiler would
-  // otherwise sink the LDS-DMA issue to the end of the slice (exposing the
-  // memory latency) and fold the fragment prefetch back into its consumers.
+  constexpr int PER = IA + IB;  // LDS-DMA instructions per wave per slice
+  uint4 f0a[TM], f0b[TN], g0a[TM], g0b[TN], f1a[TM], f1b[TN], f2a[TM], f2b[TN], f3a[TM], f3b[TN];
 #define SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
 #define SG(m, n) __builtin_amdgcn_sched_group_barrier(m, n, 0)
-#define P_RD_MM() do { SG(8,1); SG(0x100,1); SG(8,1); SG(0x100,1); SG(8,1); SG(0x100,1); SG(8,1); SG(0x100,1); \
-  SG(8,1); SG(0x100,1); SG(8,1); SG(0x100,1); SG(8,1); SG(0x100,1); SG(8,1); SG(0x100,1); SG(8,8); } while (0)
-#define P_LD_RD_MM() do { SG(8,1); SG(0x20,2); SG(0x100,1); SG(8,1); SG(0x20,2); SG(0x100,1); \
-  SG(8,1); SG(0x20,2); SG(0x100,1); SG(8,1); SG(0x20,2); SG(0x100,1); SG(8,1); SG(0x20,2); SG(0x100,1); \
-  SG(8,1); SG(0x20,2); SG(0x100,1); SG(8,1); SG(0x20,2); SG(0x100,1); SG(8,1); SG(0x20,2); SG(0x100,1); SG(8,8); } while (0)
+#define RAW_BARRIER() do { __atomic_signal_fence(__ATOMIC_SEQ_CST); __builtin_amdgcn_s_barrier(); \
+  __atomic_signal_fence(__ATOMIC_SEQ_CST); } while (0)
+#define VM_WAIT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0xF70)
+#define LGKM_WAIT0() __builtin_amdgcn_s_waitcnt(0xC07F)
+  // 32 MFMAs with one LDS-DMA issue after every second one
+#define P_MM_LD() do { for (int q_ = 0; q_ < 16; ++q_) { SG(8,1); SG(0x20,1); SG(8,1); } } while (0)
+  // 16 MFMAs with two LDS reads after each of the first 12
+#define P_MM_RD() do { for (int q_ = 0; q_ < 12; ++q_) { SG(8,1); SG(0x100,2); } SG(8,4); } while (0)
+  // body of one slice: S holds it, its K step 0 fragments are in (ca, cb);
+  // S2 receives / holds the next slice, whose step 0 goes to (na, nb)
+#define SLICE_BODY(S, S2, s, ca, cb, na, nb)                                   \
+  do {                                                                         \
+    rd(S, 1, f1a, f1b);                                                        \
+    rd(S, 2, f2a, f2b);                                                        \
+    rd(S, 3, f3a, f3b);                                                        \
+    mm(ca, cb);                                                                \
+    P_MM_RD();                                                                 \
+    SCHED_FENCE();                                                             \
+    LGKM_WAIT0();                                                              \
+    RAW_BARRIER(); /* every wave has read S */                                 \
+    issue(S, min((s) + 2, nk - 1)); /* past the end: a harmless reload */      \
+    mm(f1a, f1b);                                                              \
+    mm(f2a, f2b);                                                              \
+    P_MM_LD();                                                                 \
+    SCHED_FENCE();                                                             \
+    VM_WAIT(PER);                                                              \
+    RAW_BARRIER(); /* slice s+1 is in S2 */                                    \
+    rd(S2, 0, na, nb); /* past the end: stale, unused */                       \
+    mm(f3a, f3b);                                                              \
+    SCHED_FENCE();                                                             \
+  } while (0)
   issue(st0, 0);
-  wait_vmem();
-  __syncthreads();
-  rd(st0, 0, fa0, fb0);
+  issue(st1, min(1, nk - 1));
+  VM_WAIT(PER);
+  RAW_BARRIER();
+  rd(st0, 0, f0a, f0b);
   int kt = 0;
   for (; kt + 1 < nk; kt += 2) {
-    issue(st1, kt + 1);
-    rd(st0, 1, fa1, fb1);
-    mm(fa0, fb0);
-    P_LD_RD_MM();
-    SCHED_FENCE();
-    rd(st0, 2, fa0, fb0);
-    mm(fa1, fb1);
-    P_RD_MM();
-    SCHED_FENCE();
-    rd(st0, 3, fa1, fb1);
-    mm(fa0, fb0);
-    P_RD_MM();
-    SCHED_FENCE();
-    wait_vmem();
-    __syncthreads();  // slice kt+1 is in st1; every wave is done reading st0
-    rd(st1, 0, fa0, fb0);
-    mm(fa1, fb1);
-    P_RD_MM();
-    SCHED_FENCE();
-    issue(st0, min(kt + 2, nk - 1));  // past the end: a harmless reload of the last slice
-    rd(st1, 1, fa1, fb1);
-    mm(fa0, fb0);
-    P_LD_RD_MM();
-    SCHED_FENCE();
-    rd(st1, 2, fa0, fb0);
-    mm(fa1, fb1);
-    P_RD_MM();
-    SCHED_FENCE();
-    rd(st1, 3, fa1, fb1);
-    mm(fa0, fb0);
-    P_RD_MM();
-    SCHED_FENCE();
-    wait_vmem();
-    __syncthreads();
-    rd(st0, 0, fa0, fb0);
-    mm(fa1, fb1);
-    P_RD_MM();
-    SCHED_FENCE();
+    SLICE_BODY(st0, st1, kt, f0a, f0b, g0a, g0b);
+    SLICE_BODY(st1, st0, kt + 1, g0a, g0b, f0a, f0b);
   }
-  if (kt < nk) {  // odd number of slices: the last one is in st0
-    rd(st0, 1, fa1, fb1);
-    mm(fa0, fb0);
-    SCHED_FENCE();
-    rd(st0, 2, fa0, fb0);
-    mm(fa1, fb1);
-    SCHED_FENCE();
-    rd(st0, 3, fa1, fb1);
-    mm(fa0, fb0);
-    mm(fa1, fb1);
-  }
+  if (kt < nk) SLICE_BODY(st0, st1, kt, f0a, f0b, g0a, g0b);
+  VM_WAIT(0);
+#undef SLICE_BODY
+#undef P_MM_LD
+#undef P_MM_RD
+#undef RAW_BARRIER
+#undef VM_WAIT
+#undef LGKM_WAIT0
 #undef SCHED_FENCE
+#undef SG
 
   // ---- epilogue ----
   const int ccol = lane & 31;
