@@ -97,7 +97,7 @@ int down_splits(const moe::GemmPlan &plan, int T, int k, int E, int d, int d_ff)
   const long long mt = active > mt_floor ? active : mt_floor;
   const long long wgs = mt * ((d + 255) / 256);
   int S = 1;
-  while (wgs * S < 512 && S < 16 && d_ff % (64 * S * 2) == 0) S *= 2;
+  while (wgs * S < 512 && S < 16 && d_ff % (128 * S * 2) == 0) S *= 2;  // K parts of 128
   return S;
 }
 

@@ -18,11 +18,9 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t h) {
   return __uint_as_float(((uint32_t)h) << 16);
 }
 
-// Round to nearest even; inputs are finite.
+// Round to nearest even (the hardware conversion, v_cvt_pk_bf16_f32).
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
+  return __builtin_bit_cast(bf16_t, (__bf16)f);
 }
 
 template <typename T> struct Elem;
@@ -41,13 +39,28 @@ template <> struct Elem<bf16_t> {
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
 
-// 16 bytes per lane from global memory straight into LDS.  `lds` must be the
-// same for every lane of the wavefront; lane l's bytes land at lds + 16*l.
-__device__ __forceinline__ void global_to_lds16(const void *g, uint4 *lds) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+// Raw buffer resource over [base, base + bytes): loads at byte offsets >= bytes
+// return zeros (the hardware range check).  The last word selects 32-bit data
+// format, which untyped buffer loads require.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           0x00020000);
 }
 
-__device__ __forceinline__ float silu(float a) { return a / (1.0f + __expf(-a)); }
+// 16 bytes per lane from a buffer (byte offset `voff` per lane) straight into
+// LDS.  `lds` must be the same for every lane of the wavefront; lane l's bytes
+// land at lds + 16*l.
+__device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                uint4 *lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16,
+                                           (int)voff, 0, 0, 0);
+}
+
+// SiLU(a) = a * sigmoid(a), with the hardware exp2 and reciprocal (a few fp32
+// ulp, far below the bf16 rounding of the activations or a 1e-4 fp32 tolerance).
+__device__ __forceinline__ float silu(float a) {
+  return a * __builtin_amdgcn_rcpf(1.0f + __expf(-a));
+}
 
 // First index i in [0, n) with a[i+1] > g, for non-decreasing a[0..n] with a[0] <= g.
 __device__ __forceinline__ int upper_segment(const int32_t *a, int n, int g) {

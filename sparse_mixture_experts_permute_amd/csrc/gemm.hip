@@ -243,7 +243,7 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// bf16 variant with direct global->LDS loads (global_load_lds_dwordx4).
+// bf16 variant with direct loads into LDS (buffer_load_dwordx4 ... lds).
 //
 // Each wavefront instruction moves 64 x 16 bytes into 1 KB of contiguous LDS:
 // 8 tile rows of 128 bytes (64 bf16 of K).  Rows are not padded; instead lane
@@ -252,19 +252,87 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_kernel(
 // c ^ f(r).  A fragment read (16 lanes, 16 consecutive rows, one global chunk)
 // then touches 16 distinct 16-byte slots modulo 256 bytes: conflict-free on
 // the 64 LDS banks.  Two stages of (BM + BNB) x 128 bytes, no staging
-// registers.
+// registers.  The buffer resources are bounded to the tile's rows of A and to
+// the expert's N weight rows, so ragged tiles need no clamping.
 //
 // The loads are bound by how many requests a CU keeps in flight, not by the
 // bandwidth of L2 or HBM, so the schedule gives each slice's loads as much
 // time as the two stages allow: every wave reads ALL fragments of a slice into
 // registers at the slice's start; once every wave has done so (a barrier a
 // quarter of the way in), the stage is refilled with the slice two ahead, and
-// those loads are spread over the next 32 MFMAs.  A load thus has about 1.75
-// slices of MFMA work to land (one slice with the stage held until the end).
-// ---------------------------------------------------------------------------
+// those loads are spread over the remaining 48 MFMAs.  A load thus has about
+// 1.75 slices of MFMA work to land (one slice with the stage held until the
+// end).
+//
+// The kernel is persistent (one workgroup per CU, two for 64-row tiles): the
+// next tile's first slice is loaded while the current tile's epilogue runs.
+//
 // Split K (down projection only): blockIdx.y picks one of gridDim.y equal K
 // ranges and its fp32 partial goes to output plane blockIdx.y (plane elements
 // apart); the combine adds the planes in a fixed order.
+// ---------------------------------------------------------------------------
+// Epilogue of one tile of the direct-to-LDS kernel.  SwiGLU: each wave writes
+// its bf16 outputs to `stage` in row-major order (16-byte chunks XOR-swizzled
+// by row so rows r and r+4, written by the two halves of the wave, fall in
+// different banks), then stores whole 16-byte row chunks.  Down projection:
+// fp32 outputs are stored straight from the accumulators (32 consecutive
+// columns of two rows per instruction).
+template <int BM, int BNB, bool SWIGLU, int TM, int TN, typename TA>
+__device__ __forceinline__ void dl_epilogue(const TA &ta, f32x16_v (&acc)[TM][TN], uint4 *stage,
+                                            void *__restrict__ C, int N, size_t plane, int wave,
+                                            int lane) {
+  constexpr int WN = 2;
+  const int wm = wave / WN, wn = wave % WN;
+  const int row0 = ta.row0, rows = ta.rows, n0 = ta.n0;
+  const int ccol = lane & 31;
+  const int crow4 = (lane >> 5) * 4;
+  if constexpr (SWIGLU) {
+    constexpr int WC = 32 * TN / 2;          // columns per wave
+    static_assert(WC / 8 == 8, "swizzle assumes 128-byte rows");
+    char *reg = reinterpret_cast<char *>(stage) + wave * (32 * TM * WC * 2);
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+      for (int q = 0; q < TN / 2; ++q)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = a * 32 + (i / 4) * 8 + crow4 + (i % 4);
+          const int c = q * 32 + ccol;
+          const float h = silu(acc[a][2 * q][i]) * acc[a][2 * q + 1][i];
+          *reinterpret_cast<bf16_t *>(reg + r * (WC * 2) + (((c >> 3) ^ (r & 7)) << 4) +
+                                      (c & 7) * 2) = f32_to_bf16(h);
+        }
+    const int col = n0 + wn * WC + (lane & 7) * 8;
+#pragma unroll
+    for (int t = 0; t < 32 * TM / 8; ++t) {
+      const int r = t * 8 + (lane >> 3);
+      const uint4 v = *reinterpret_cast<const uint4 *>(reg + r * (WC * 2) +
+                                                        (((lane & 7) ^ (r & 7)) << 4));
+      const int grow = wm * 32 * TM + r;
+      if (grow < rows && col < N)
+        *reinterpret_cast<uint4 *>(reinterpret_cast<bf16_t *>(C) + (size_t)(row0 + grow) * N +
+                                   col) = v;
+    }
+  } else {
+    (void)stage;
+    float *out = reinterpret_cast<float *>(C) + blockIdx.y * plane;
+#pragma unroll
+    for (int a = 0; a < TM; ++a) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = (wm * TM + a) * 32 + (i / 4) * 8 + crow4 + (i % 4);
+        if (r >= rows) continue;
+        const size_t orow = (size_t)(row0 + r) * N;
+#pragma unroll
+        for (int b = 0; b < TN; ++b) {
+          const int col = n0 + (wn * TN + b) * 32 + ccol;
+          if (col < N) out[orow + col] = acc[a][b][i];
+        }
+      }
+    }
+  }
+}
+
 template <int BM, int BNB, bool SWIGLU>
 __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
     const bf16_t *__restrict__ A, const bf16_t *__restrict__ B1, const bf16_t *__restrict__ B3,
@@ -280,78 +348,95 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
   __shared__ uint4 st0[STAGE_U4];
   __shared__ uint4 st1[STAGE_U4];
   constexpr int COLS = SWIGLU ? BNB / 2 : BNB;
-  Tile tile;
-  if (!map_tile(blockIdx.x, mtile_off, G, (N + COLS - 1) / COLS, tile)) return;
-  const int e = tile.e;
-  const int row0 = seg_off[e] + (tile.g - mtile_off[e]) * BM;
-  const int rows = min(BM, seg_off[e + 1] - row0);
-  const int n0 = tile.n * COLS;
+  const int ntn = (N + COLS - 1) / COLS;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = lane_id();
   const int wm = wave / WN, wn = wave % WN;
 
-  // Per-instruction global byte offsets (relative to uniform bases).  Wave w
-  // loads A blocks w*IA .. w*IA+IA-1 and B blocks w*IB .. w*IB+IB-1 (8 rows
-  // each), so whether an instruction reads A, W1 or W3 is fixed per j.
-  constexpr int IA = BM / 32, IB = BNB / 32;  // instructions per wave per stage
-  const int kpart = K / gridDim.y;  // K range of this split (a multiple of 64)
+  constexpr int IA = BM / 32, IB = BNB / 32;  // LDS-DMA instructions per wave per stage
+  constexpr int PER = IA + IB;
+  const int kpart = K / gridDim.y;  // K range of this split (a multiple of 128)
   const size_t kb = (size_t)blockIdx.y * kpart * 2;  // its byte offset inside a row
-  const char *abase = reinterpret_cast<const char *>(A) + (size_t)row0 * K * 2 + kb;
-  const size_t eoff = (size_t)e * N * K * 2 + kb;
-  const char *b1base = reinterpret_cast<const char *>(B1) + eoff;
-  const char *b3base = SWIGLU ? reinterpret_cast<const char *>(B3) + eoff : b1base;
-  uint32_t aoff[IA], boff[IB];
+  const int nk = kpart / 64;        // 64-wide K slices (even)
   const int lrow = lane >> 3, lchunk = lane & 7;
-#pragma unroll
-  for (int j = 0; j < IA; ++j) {
-    const int r = (wave * IA + j) * 8 + lrow;
-    const int gch = lchunk ^ ((r >> 1) & 7);
-    aoff[j] = (uint32_t)min(r, rows - 1) * K * 2 + gch * 16;
-  }
-#pragma unroll
-  for (int j = 0; j < IB; ++j) {
-    const int br = (wave * IB + j) * 8 + lrow;
-    const int gch = lchunk ^ ((br >> 1) & 7);
-    int col;
-    if (SWIGLU) {
-      // 32-row blocks alternate W1 / W3 for the same 32 output columns
-      const int rb = br / 32, wnb = rb / TN, jj = rb % TN;
-      col = n0 + wnb * (TN / 2) * 32 + (jj / 2) * 32 + (br % 32);
-    } else {
-      col = n0 + br;
-    }
-    boff[j] = (uint32_t)min(col, N - 1) * K * 2 + gch * 16;
-  }
+
+  // Addressing of one tile.  A tile reads its rows of A and its columns of
+  // W1 / W3 (or W2) through buffer resources bounded to the segment's rows and
+  // the N rows of the expert's weight, so rows past either end read as zeros
+  // (their results are not stored) and nothing is clamped.  Wave w loads A
+  // blocks w*IA .. w*IA+IA-1 and B blocks w*IB .. w*IB+IB-1 (8 rows of 128
+  // bytes each); lane l takes row l/8 of the block and the 16-byte chunk
+  // (l % 8) ^ ((row >> 1) & 7), which only depends on the block's parity.
+  const uint32_t rowb = (uint32_t)K * 2;  // bytes per row of A and B
+  const uint32_t lc0 = (uint32_t)lrow * rowb + (uint32_t)((lchunk ^ (lrow >> 1)) * 16);
+  const uint32_t lc1 = lc0 ^ 64u;          // chunk ^ 4 for odd blocks
+  struct TileAddr {
+    __amdgpu_buffer_rsrc_t ra, r1, r3;
+    uint32_t lc0, lc1;
+    int row0, rows, n0;
+  };
+  auto setup = [&](const Tile &t, TileAddr &ta) {
+    const int e = t.e;
+    ta.row0 = seg_off[e] + (t.g - mtile_off[e]) * BM;
+    ta.rows = min(BM, seg_off[e + 1] - ta.row0);
+    ta.n0 = t.n * COLS;
+    ta.ra = make_rsrc(reinterpret_cast<const char *>(A) + (size_t)ta.row0 * rowb + kb,
+                      (uint32_t)ta.rows * rowb - (uint32_t)kb);
+    const size_t eoff = (size_t)e * N * rowb + kb;
+    const uint32_t wbytes = (uint32_t)N * rowb - (uint32_t)kb;
+    ta.r1 = make_rsrc(reinterpret_cast<const char *>(B1) + eoff, wbytes);
+    ta.r3 = SWIGLU ? make_rsrc(reinterpret_cast<const char *>(B3) + eoff, wbytes) : ta.r1;
+    // per-tile copies of the lane offsets: keeps the compiler from hoisting
+    // every instruction's offset out of the tile loop (and spilling them)
+    ta.lc0 = lc0;
+    ta.lc1 = lc1;
+    asm volatile("" : "+v"(ta.lc0), "+v"(ta.lc1));
+  };
   // B block parity: block (wave*IB + j)/4 is odd (a W3 block) iff (j/4) is odd,
   // because IB is a multiple of 8
   static_assert(!SWIGLU || IB % 8 == 0, "W1/W3 choice must be fixed per instruction");
-  auto issue = [&](uint4 *stage, int kt) {
+  static_assert(IA % 2 == 0 && IB % 2 == 0, "chunk swizzle parity per instruction");
+  // LDS-DMA instructions j0 <= j < j1 of one slice (A blocks first, then B)
+  auto issue_part = [&](const TileAddr &ta, uint4 *stage, int kt, int j0, int j1) {
     const uint32_t ko = (uint32_t)kt * 128;
 #pragma unroll
     for (int j = 0; j < IA; ++j)
-      global_to_lds16(abase + aoff[j] + ko, stage + (wave * IA + j) * 64);
+      if (j >= j0 && j < j1) {
+        const uint32_t u = (uint32_t)((wave * IA + j) * 8) * rowb + ko;
+        buffer_to_lds16(ta.ra, ((j & 1) ? ta.lc1 : ta.lc0) + u, stage + (wave * IA + j) * 64);
+      }
 #pragma unroll
     for (int j = 0; j < IB; ++j) {
-      const char *bb = (SWIGLU && ((j / 4) & 1)) ? b3base : b1base;
-      global_to_lds16(bb + boff[j] + ko, stage + BM * 8 + (wave * IB + j) * 64);
+      if (IA + j >= j0 && IA + j < j1) {
+        const int br = (wave * IB + j) * 8;  // first B row of the block
+        int col;
+        if (SWIGLU) {
+          // 32-row blocks alternate W1 / W3 for the same 32 output columns
+          const int rb = br / 32, wnb = rb / TN, jj = rb % TN;
+          col = ta.n0 + wnb * (TN / 2) * 32 + (jj / 2) * 32 + (br % 32);
+        } else {
+          col = ta.n0 + br;
+        }
+        const uint32_t u = (uint32_t)col * rowb + ko;
+        buffer_to_lds16((SWIGLU && ((j / 4) & 1)) ? ta.r3 : ta.r1, ((j & 1) ? ta.lc1 : ta.lc0) + u,
+                        stage + BM * 8 + (wave * IB + j) * 64);
+      }
     }
   };
+  auto issue = [&](const TileAddr &ta, uint4 *stage, int kt) { issue_part(ta, stage, kt, 0, PER); };
 
   f32x16_v acc[TM][TN];
-#pragma unroll
-  for (int a = 0; a < TM; ++a)
-#pragma unroll
-    for (int b = 0; b < TN; ++b)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
-
   // fragment addressing: row part and the swizzled chunk of each 16-wide K step
-  const int frow = lane & 31;
-  const int xf = (frow >> 1) & 7;
-  int cidx[4];
+  // (recomputed per tile from a laundered lane id, see lane_t below)
+  int frow, cidx[4];
+  auto set_frag_addr = [&](int ln) {
+    frow = ln & 31;
+    const int xf = (frow >> 1) & 7;
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) cidx[ks] = (ks * 2 + (lane >> 5)) ^ xf;
+    for (int ks = 0; ks < 4; ++ks) cidx[ks] = (ks * 2 + (ln >> 5)) ^ xf;
+  };
+  set_frag_addr(lane);
   // fragments of one 16-wide K step
   auto rd = [&](const uint4 *stage, int ks, uint4 (&af)[TM], uint4 (&bf)[TN]) {
 #pragma unroll
@@ -368,13 +453,6 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
             __builtin_bit_cast(bf16x8_v, af[a]), __builtin_bit_cast(bf16x8_v, bf[b]), acc[a][b],
             0, 0, 0);
   };
-
-  // Pipeline: a slice's fragments are all read into registers at its start,
-  // so its LDS stage can be refilled (with the slice two ahead) once every
-  // wave has read it, a quarter of the way into the slice; the load of a
-  // slice then has about 1.75 slices of MFMA work to land instead of one.
-  const int nk = kpart / 64;
-  constexpr int PER = IA + IB;  // LDS-DMA instructions per wave per slice
   uint4 f0a[TM], f0b[TN], g0a[TM], g0b[TN], f1a[TM], f1b[TN], f2a[TM], f2b[TN], f3a[TM], f3b[TN];
 #define SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
 #define SG(m, n) __builtin_amdgcn_sched_group_barrier(m, n, 0)
@@ -382,82 +460,124 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
   __atomic_signal_fence(__ATOMIC_SEQ_CST); } while (0)
 #define VM_WAIT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0xF70)
 #define LGKM_WAIT0() __builtin_amdgcn_s_waitcnt(0xC07F)
-  // 32 MFMAs with one LDS-DMA issue after every second one
-#define P_MM_LD() do { for (int q_ = 0; q_ < 16; ++q_) { SG(8,1); SG(0x20,1); SG(8,1); } } while (0)
   // 16 MFMAs with two LDS reads after each of the first 12
 #define P_MM_RD() do { for (int q_ = 0; q_ < 12; ++q_) { SG(8,1); SG(0x100,2); } SG(8,4); } while (0)
-  // body of one slice: S holds it, its K step 0 fragments are in (ca, cb);
-  // S2 receives / holds the next slice, whose step 0 goes to (na, nb)
-#define SLICE_BODY(S, S2, s, ca, cb, na, nb)                                   \
+  // loads of the slice two ahead: J1 of them spread over the MFMAs of K steps
+  // 1 and 2, the rest over step 3 (after the wait for the next slice)
+  constexpr int J1 = PER * 5 / 8;
+  // the interleave patterns are written for the 256 x 256 tile
+  constexpr bool FULL = TM == 4 && TN == 4 && PER == 16;
+#define P_MM_LD() do { for (int q_ = 0; q_ < J1; ++q_) { SG(8,3); SG(0x20,1); } SG(8, 32 - 3 * J1); } while (0)
+#define P_MM_RD_LD() do { for (int q_ = 0; q_ < PER - J1; ++q_) { SG(8,2); SG(0x100,1); SG(0x20,1); } \
+  SG(0x100, TM + TN - (PER - J1)); SG(8, 16 - 2 * (PER - J1)); } while (0)
+// ISSUE: the slice two ahead exists and is loaded into S; NEXT: a next slice
+// exists (wait for it, read its first K step)
+#define SLICE_BODY(S, S2, s, ca, cb, na, nb, ISSUE, NEXT)                      \
   do {                                                                         \
     rd(S, 1, f1a, f1b);                                                        \
     rd(S, 2, f2a, f2b);                                                        \
     rd(S, 3, f3a, f3b);                                                        \
     mm(ca, cb);                                                                \
-    P_MM_RD();                                                                 \
+    if constexpr (FULL) P_MM_RD();                                             \
     SCHED_FENCE();                                                             \
     LGKM_WAIT0();                                                              \
     RAW_BARRIER(); /* every wave has read S */                                 \
-    issue(S, min((s) + 2, nk - 1)); /* past the end: a harmless reload */      \
+    if constexpr (ISSUE) issue_part(cur, S, (s) + 2, 0, J1);                        \
     mm(f1a, f1b);                                                              \
     mm(f2a, f2b);                                                              \
-    P_MM_LD();                                                                 \
+    if constexpr (FULL && ISSUE) P_MM_LD();                                    \
     SCHED_FENCE();                                                             \
-    VM_WAIT(PER);                                                              \
-    RAW_BARRIER(); /* slice s+1 is in S2 */                                    \
-    rd(S2, 0, na, nb); /* past the end: stale, unused */                       \
+    if constexpr (NEXT) {                                                      \
+      if constexpr (ISSUE) VM_WAIT(J1); else VM_WAIT(0);                       \
+      RAW_BARRIER(); /* slice s+1 is in S2 */                                  \
+      rd(S2, 0, na, nb);                                                       \
+    }                                                                          \
+    if constexpr (ISSUE) issue_part(cur, S, (s) + 2, J1, PER);                      \
     mm(f3a, f3b);                                                              \
+    if constexpr (FULL && ISSUE && NEXT) P_MM_RD_LD();                         \
     SCHED_FENCE();                                                             \
   } while (0)
-  issue(st0, 0);
-  issue(st1, min(1, nk - 1));
+
+  // Persistent: the workgroup walks the tile order in steps of the grid size
+  // (a multiple of the XCD count, so it stays on its XCD's chunk).  The next
+  // tile's first slices are loaded while the current tile's epilogue runs.
+  int hw = blockIdx.x;
+  Tile tile;
+  if (!map_tile(hw, mtile_off, G, ntn, tile)) return;
+  TileAddr cur;
+  setup(tile, cur);
+  issue(cur, st0, 0);
+  issue(cur, st1, 1);
   VM_WAIT(PER);
   RAW_BARRIER();
   rd(st0, 0, f0a, f0b);
-  int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
-    SLICE_BODY(st0, st1, kt, f0a, f0b, g0a, g0b);
-    SLICE_BODY(st1, st0, kt + 1, g0a, g0b, f0a, f0b);
+  for (;;) {
+    // a per-tile copy of the lane id the compiler cannot see through: lane
+    // dependent addresses are then recomputed per tile instead of being hoisted
+    // out of the tile loop and spilled
+    int lane_t = lane;
+    asm volatile("" : "+v"(lane_t));
+    set_frag_addr(lane_t);
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+      for (int b = 0; b < TN; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
+    // From here on the wait for slice s+1 lets the J1 loads of slice s+2 that
+    // were issued before it stay in flight (the remaining PER - J1 come after).
+    // nk is even (checked by the host); the last pair issues nothing.
+    int kt = 0;
+    for (; kt + 2 < nk; kt += 2) {
+      SLICE_BODY(st0, st1, kt, f0a, f0b, g0a, g0b, true, true);
+      SLICE_BODY(st1, st0, kt + 1, g0a, g0b, f0a, f0b, true, true);
+    }
+    SLICE_BODY(st0, st1, kt, f0a, f0b, g0a, g0b, false, true);
+    SLICE_BODY(st1, st0, kt + 1, g0a, g0b, f0a, f0b, false, false);
+    // Every wave is past the last barrier of the tile, so no wave reads either
+    // stage any more: the next tile's first slice goes to st0 now, its second
+    // to st1 once the epilogue (which stages SwiGLU outputs in st1) is done.
+    hw += gridDim.x;
+    Tile nt;
+    const bool more = map_tile(hw, mtile_off, G, ntn, nt);
+    TileAddr nxt;
+    if (more) {
+      setup(nt, nxt);
+      issue(nxt, st0, 0);
+    }
+    dl_epilogue<BM, BNB, SWIGLU>(cur, acc, st1, C, N, plane, wave, lane_t);
+    if (!more) break;
+    if constexpr (SWIGLU) RAW_BARRIER();  // every wave has read its staged outputs back
+    issue(nxt, st1, 1);
+    VM_WAIT(PER);  // slice 0 (and the epilogue's stores) done, slice 1 may be in flight
+    RAW_BARRIER();
+    rd(st0, 0, f0a, f0b);
+    cur = nxt;
   }
-  if (kt < nk) SLICE_BODY(st0, st1, kt, f0a, f0b, g0a, g0b);
-  VM_WAIT(0);
 #undef SLICE_BODY
 #undef P_MM_LD
+#undef P_MM_RD_LD
 #undef P_MM_RD
 #undef RAW_BARRIER
 #undef VM_WAIT
 #undef LGKM_WAIT0
 #undef SCHED_FENCE
 #undef SG
+}
 
-  // ---- epilogue ----
-  const int ccol = lane & 31;
-  const int crow4 = (lane >> 5) * 4;
-#pragma unroll
-  for (int a = 0; a < TM; ++a) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = (wm * TM + a) * 32 + (i / 4) * 8 + crow4 + (i % 4);
-      if (r >= rows) continue;
-      const size_t orow = (size_t)(row0 + r) * N;
-      if (SWIGLU) {
-#pragma unroll
-        for (int q = 0; q < TN / 2; ++q) {
-          const int col = n0 + wn * (TN / 2) * 32 + q * 32 + ccol;
-          if (col < N)
-            reinterpret_cast<bf16_t *>(C)[orow + col] =
-                f32_to_bf16(silu(acc[a][2 * q][i]) * acc[a][2 * q + 1][i]);
-        }
-      } else {
-#pragma unroll
-        for (int b = 0; b < TN; ++b) {
-          const int col = n0 + (wn * TN + b) * 32 + ccol;
-          if (col < N)
-            reinterpret_cast<float *>(C)[blockIdx.y * plane + orow + col] = acc[a][b][i];
-        }
-      }
-    }
+// Workgroups that stay resident at once: one per CU for 256-row tiles (128 KB
+// of LDS), two for 64-row tiles.
+int resident_wgs(int bm) {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev] = n;
   }
+  return cus[dev] * (bm == 64 ? 2 : 1);
 }
 
 template <int BM, int BNB, bool SWIGLU>
@@ -465,7 +585,12 @@ hipError_t launch_dl(const void *A, const void *B1, const void *B3, void *C,
                      const int32_t *seg_off, const int32_t *mtile_off, int G, int N, int K,
                      int max_mtiles, int ksplit, size_t plane, hipStream_t s) {
   const int cols = SWIGLU ? BNB / 2 : BNB;
-  dim3 grid(((N + cols - 1) / cols) * max_mtiles + NUM_XCD, ksplit);
+  // persistent grid: at most what stays resident, a multiple of the XCD count
+  const long long upper = (long long)((N + cols - 1) / cols) * max_mtiles + NUM_XCD;
+  long long gx = resident_wgs(BM) / ksplit;
+  if (gx > upper) gx = upper;
+  gx = (gx + NUM_XCD - 1) / NUM_XCD * NUM_XCD;
+  dim3 grid((unsigned)gx, ksplit);
   hipLaunchKernelGGL((grouped_gemm_dl_kernel<BM, BNB, SWIGLU>), grid, dim3(GM_THREADS), 0, s,
                      (const bf16_t *)A, (const bf16_t *)B1, (const bf16_t *)B3, C, seg_off,
                      mtile_off, G, N, K, plane);
@@ -488,7 +613,7 @@ hipError_t launch_one(const void *A, const void *B1, const void *B3, void *C,
 
 GemmPlan gemm_plan(int dtype, int d, int d_ff, int d_ff_shared, long long rows_per_expert) {
   GemmPlan p;
-  const int q = 64;  // K granule of the direct-to-LDS kernel
+  const int q = 128;  // K granule of the direct-to-LDS kernel (pairs of 64-wide slices)
   p.dl1 = dtype == 1 && d % q == 0;
   p.dl2 = dtype == 1 && d_ff % q == 0 && (d_ff_shared == 0 || d_ff_shared % q == 0);
   // 64-row tiles when experts hold few rows (less padding, two workgroups per CU)
