@@ -62,23 +62,26 @@ constexpr int GM_THREADS = 256;
 constexpr int NUM_XCD = 8;  // MI355X: 8 accelerator complex dies, each with its own L2
 
 // Workgroup -> (expert, global m-tile, n-tile).  Workgroups are dispatched to
-// the XCDs round-robin (id % 8), so each XCD gets a contiguous chunk of the
-// logical tile order; the logical order is expert-major, then n-tile, with the
-// expert's m-tiles fastest, so the workgroups that share a weight tile run at
-// the same time on the same XCD and its L2 serves the re-reads.  The chunking
-// uses the real tile count (known on the device once the permutation ran);
-// the grid is launched for an upper bound plus NUM_XCD and surplus
-// workgroups exit.
+// the XCDs round-robin (id % 8).  The logical tile order is expert-major, then
+// n-tile, with the expert's m-tiles fastest; it is cut into blocks of BS
+// consecutive tiles, dealt to the XCDs in turn (block b -> XCD b % 8).  Within
+// a block the workgroups sharing a weight tile or a row tile run at the same
+// time on one XCD (its L2 serves the re-reads), and neighbouring blocks, which
+// share the expert's rows, run at the same time on the other XCDs (the MALL
+// serves those).  BS is chosen so that every XCD gets the same number of tiles
+// (within one block) for the grid's CUs per XCD; surplus workgroups exit.
 struct Tile {
   int e, g, n;
 };
 __device__ __forceinline__ bool map_tile(int hw, const int32_t *mtile_off, int G, int ntn,
                                          Tile &t) {
   const int R = ntn * mtile_off[G];
+  const int cpx = max(1, (int)gridDim.x / NUM_XCD);  // resident workgroups per XCD
   const int R8 = (R + NUM_XCD - 1) / NUM_XCD;
-  const int local = hw / NUM_XCD;
-  if (local >= R8) return false;
-  const int L = (hw % NUM_XCD) * R8 + local;
+  const int rounds = max(1, (R8 + cpx - 1) / cpx);
+  const int BS = max(1, (R + NUM_XCD * rounds - 1) / (NUM_XCD * rounds));
+  const int xcd = hw % NUM_XCD, local = hw / NUM_XCD;
+  const int L = ((local / BS) * NUM_XCD + xcd) * BS + local % BS;
   if (L >= R) return false;
   const int e = upper_segment(mtile_off, G, L / ntn);
   const int rem = L - ntn * mtile_off[e];
