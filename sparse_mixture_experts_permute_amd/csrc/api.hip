@@ -108,8 +108,10 @@ int skinny_mb(long long rows) { return rows <= 12 ? 1 : rows <= 24 ? 2 : 4; }
 // row each (single-token decode: they also fold the row gather into the first
 // GEMM) and the shared expert up to 64 tokens; the tiled kernels (64-row tiles
 // for small batches, split K for the down projection) serve everything else.
+// Up to four tokens (at most four rows on any expert) the vector-ALU kernels
+// stream the weights; beyond that the matrix-core ones do.
 struct SkinnyPlan {
-  bool routed, shared;
+  bool routed, shared, gemv, gemv_shared;
   int mb, mb_shared;
 };
 SkinnyPlan skinny_plan(int dtype, int T, int k, int E, int d, int d_ff, int dffs) {
@@ -117,8 +119,10 @@ SkinnyPlan skinny_plan(int dtype, int T, int k, int E, int d, int d_ff, int dffs
   if (dtype != MOE_BF16) return p;
   const long long avg = ((long long)T * k + E - 1) / E;
   p.routed = avg <= 1 && moe::skinny_ok(d_ff, d) && moe::skinny_ok(d, d_ff);
+  p.gemv = p.routed && T <= 4 && moe::gemv_ok(d_ff, d) && moe::gemv_ok(d, d_ff);
   p.mb = skinny_mb(avg);
   p.shared = dffs > 0 && T <= 64 && moe::skinny_ok(dffs, d) && moe::skinny_ok(d, dffs);
+  p.gemv_shared = p.shared && T <= 4 && moe::gemv_ok(dffs, d) && moe::gemv_ok(d, dffs);
   p.mb_shared = skinny_mb(T);
   return p;
 }
@@ -281,11 +285,15 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
   if (sk.routed) {
     // few rows per expert: weight-streaming kernels; the gather rides in the first GEMM
     MOE_MARK(3);
-    if ((e = moe::launch_skinny_swiglu(sk.mb, x, perm, k, W1, W3, H, offsets, act, act + E, E,
-                                       d_ff, d, s)))
+    if ((e = sk.gemv ? moe::launch_gemv_swiglu(T, x, perm, k, W1, W3, H, offsets, act, act + E,
+                                               E, d_ff, d, s)
+                     : moe::launch_skinny_swiglu(sk.mb, x, perm, k, W1, W3, H, offsets, act,
+                                                 act + E, E, d_ff, d, s)))
       goto fail;
     MOE_MARK(4);
-    if ((e = moe::launch_skinny_down(sk.mb, H, W2, Yp, offsets, act, act + E, E, d, d_ff, s)))
+    if ((e = sk.gemv ? moe::launch_gemv_down(T, H, W2, Yp, offsets, act, act + E, E, d, d_ff, s)
+                     : moe::launch_skinny_down(sk.mb, H, W2, Yp, offsets, act, act + E, E, d,
+                                               d_ff, s)))
       goto fail;
     MOE_MARK(5);
   } else {
@@ -301,7 +309,14 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
     MOE_MARK(5);
   }
   if (shared) {
-    if (sk.shared) {
+    if (sk.gemv_shared) {
+      if ((e = moe::launch_gemv_swiglu(T, x, nullptr, 1, Ws1, Ws3, Hs, shseg, shseg + 6,
+                                       shseg + 7, 1, d_ff_shared, d, s)))
+        goto fail;
+      if ((e = moe::launch_gemv_down(T, Hs, Ws2, Ys, shseg, shseg + 6, shseg + 7, 1, d,
+                                     d_ff_shared, s)))
+        goto fail;
+    } else if (sk.shared) {
       if ((e = moe::launch_skinny_swiglu(sk.mb_shared, x, nullptr, 1, Ws1, Ws3, Hs, shseg,
                                          shseg + 6, shseg + 7, 1, d_ff_shared, d, s)))
         goto fail;

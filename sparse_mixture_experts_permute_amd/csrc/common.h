@@ -50,10 +50,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 // 16 bytes per lane from a buffer (byte offset `voff` per lane) straight into
 // LDS.  `lds` must be the same for every lane of the wavefront; lane l's bytes
 // land at lds + 16*l.
+// NT: non-temporal (streaming) cache policy, for data read once.
+template <bool NT = false>
 __device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t r, uint32_t voff,
                                                 uint4 *lds) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16,
-                                           (int)voff, 0, 0, 0);
+                                           (int)voff, 0, 0, NT ? 2 : 0);
 }
 
 // SiLU(a) = a * sigmoid(a), with the hardware exp2 and reciprocal (a few fp32

@@ -422,7 +422,10 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
           col = ta.n0 + br;
         }
         const uint32_t u = (uint32_t)col * rowb + ko;
-        buffer_to_lds16((SWIGLU && ((j / 4) & 1)) ? ta.r3 : ta.r1, ((j & 1) ? ta.lc1 : ta.lc0) + u,
+        // 64-row tiles serve small batches, where a weight tile is read by
+        // one m-tile: stream it past the caches
+        buffer_to_lds16<BM == 64>((SWIGLU && ((j / 4) & 1)) ? ta.r3 : ta.r1,
+                                  ((j & 1) ? ta.lc1 : ta.lc0) + u,
                         stage + BM * 8 + (wave * IB + j) * 64);
       }
     }

@@ -154,6 +154,211 @@ hipError_t launch_mb(int mb, const void *A, const int32_t *perm, int kslots, con
   return hipGetLastError();
 }
 
+
+// ---------------------------------------------------------------------------
+// Vector-ALU weight streaming for experts that hold one to four rows (a single
+// decoded token).  Each wavefront instruction reads 1 KB of ONE weight row --
+// eight whole 128-byte lines -- with a non-temporal load (the weights are read
+// once), and v_dot2_f32_bf16 multiplies it with the matching slice of the
+// expert's rows, which each lane keeps in registers for the whole workgroup.
+// The four wavefronts split K; a workgroup walks its columns CB at a time with
+// the next group's weights in flight while the current one is reduced (lanes
+// by shuffles, wavefronts through LDS in a fixed order).
+// ---------------------------------------------------------------------------
+constexpr int GV_WAVES = 4;
+constexpr int GV_THREADS = GV_WAVES * kWave;
+constexpr int GV_CHUNK = 512;  // K elements per wavefront instruction (1 KB of bf16)
+
+typedef unsigned int gv_u4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ldg16_stream(const bf16_t *p) {
+  const gv_u4 v = __builtin_nontemporal_load(reinterpret_cast<const gv_u4 *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+// Workgroup barrier that waits only for this wave's LDS traffic: the weight
+// loads of the next group stay in flight (a __syncthreads() would wait for
+// every outstanding load of the wave first).
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+__device__ __forceinline__ float dot8_bf16(const uint4 &a, const uint4 &b, float acc) {
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, a.x),
+                                        __builtin_bit_cast(bf16x2_v, b.x), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, a.y),
+                                        __builtin_bit_cast(bf16x2_v, b.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, a.z),
+                                        __builtin_bit_cast(bf16x2_v, b.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, a.w),
+                                        __builtin_bit_cast(bf16x2_v, b.w), acc, false);
+  return acc;
+}
+
+// Columns per group: the largest power of two that keeps about 16 weight
+// loads (16 KB) per wavefront in flight.
+constexpr int gv_cb(int loads_per_col) {
+  int cb = 1;
+  while (cb * 2 * loads_per_col <= 16) cb *= 2;
+  return cb;
+}
+
+// KC: 1 KB chunks per wavefront (K = GV_WAVES * KC * GV_CHUNK); R: rows per
+// pass; CB: columns per group.  The workgroup owns columns c0 .. c0+cpw-1 of
+// active expert blockIdx.x / (N / cpw).
+template <bool SWIGLU, int R, int KC>
+__global__ __launch_bounds__(GV_THREADS) void gemv_kernel(
+    const bf16_t *__restrict__ A, const int32_t *__restrict__ perm, int kslots,
+    const bf16_t *__restrict__ B1, const bf16_t *__restrict__ B3, void *__restrict__ C,
+    const int32_t *__restrict__ seg_off, const int32_t *__restrict__ active,
+    const int32_t *__restrict__ nactive, int N, int K, int cpw) {
+  constexpr int NW = SWIGLU ? 2 : 1;
+  constexpr int CB = gv_cb(NW * KC);
+  __shared__ float red[2][GV_WAVES][CB][NW][R];
+
+  const int nblk = N / cpw;
+  const int a_idx = blockIdx.x / nblk;
+  if (a_idx >= nactive[0]) return;
+  const int e = active[a_idx];
+  const int c0 = (blockIdx.x % nblk) * cpw;
+  const int s0 = seg_off[e], cnt = seg_off[e + 1] - s0;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = lane_id();
+  const int kl = wave * KC * GV_CHUNK + lane * 8;  // first K element of the lane
+  const bf16_t *w1 = B1 + (size_t)e * N * K + kl;
+  const bf16_t *w3 = SWIGLU ? B3 + (size_t)e * N * K + kl : w1;
+  const int ngroups = cpw / CB;
+
+  for (int rg = 0; rg < cnt; rg += R) {
+    uint4 xa[R][KC];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int row = min(rg + r, cnt - 1);  // rows past the end: duplicates, not stored
+      const int src = perm ? perm[s0 + row] / kslots : s0 + row;
+      const bf16_t *ap = A + (size_t)src * K + kl;
+#pragma unroll
+      for (int i = 0; i < KC; ++i) xa[r][i] = *reinterpret_cast<const uint4 *>(ap + i * GV_CHUNK);
+    }
+    uint4 wa[CB][NW][KC], wb[CB][NW][KC];  // two groups of weights in flight
+    // Workgroups start at different groups of their columns: workgroups a
+    // fixed distance apart would otherwise all read the same offsets of their
+    // blocks at the same time and crowd a few HBM channels.
+    const int rot = blockIdx.x % ngroups;
+    auto col_of = [&](int g) { return c0 + ((g + rot) % ngroups) * CB; };
+    auto load = [&](uint4 (&dst)[CB][NW][KC], int g) {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const size_t ro = (size_t)(col_of(g) + cb) * K;
+#pragma unroll
+        for (int i = 0; i < KC; ++i) {
+          dst[cb][0][i] = ldg16_stream(w1 + ro + i * GV_CHUNK);
+          if (SWIGLU) dst[cb][NW - 1][i] = ldg16_stream(w3 + ro + i * GV_CHUNK);
+        }
+      }
+    };
+    // dot products of one group, reduced over the lanes, then over the waves
+    // (red[rb]: the two groups in flight use different halves)
+    auto compute = [&](const uint4 (&wv)[CB][NW][KC], int g, int rb) {
+      float acc[CB][NW][R];
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int m = 0; m < NW; ++m)
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            float t = 0.f;
+#pragma unroll
+            for (int i = 0; i < KC; ++i) t = dot8_bf16(xa[r][i], wv[cb][m][i], t);
+#pragma unroll
+            for (int off = kWave / 2; off > 0; off >>= 1) t += __shfl_xor(t, off);
+            acc[cb][m][r] = t;
+          }
+      if (lane == 0) {
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+          for (int m = 0; m < NW; ++m)
+#pragma unroll
+            for (int r = 0; r < R; ++r) red[rb][wave][cb][m][r] = acc[cb][m][r];
+      }
+      lds_barrier();
+      if (tid < CB * R) {
+        const int cb = tid / R, r = tid % R;
+        if (rg + r < cnt) {
+          float v[NW];
+#pragma unroll
+          for (int m = 0; m < NW; ++m) {
+            float t = 0.f;
+#pragma unroll
+            for (int w = 0; w < GV_WAVES; ++w) t += red[rb][w][cb][m][r];
+            v[m] = t;
+          }
+          const size_t out = (size_t)(s0 + rg + r) * N + col_of(g) + cb;
+          if (SWIGLU)
+            reinterpret_cast<bf16_t *>(C)[out] = f32_to_bf16(silu(v[0]) * v[NW - 1]);
+          else
+            reinterpret_cast<float *>(C)[out] = v[0];
+        }
+      }
+      // red[rb] is written again two groups later, after the next barrier
+    };
+    // ngroups is even (the host makes cpw a multiple of 2 CB): two groups in
+    // flight, no conditional loads inside the loop
+    load(wa, 0);
+    load(wb, 1);
+    int g = 0;
+    for (; g + 2 < ngroups; g += 2) {
+      compute(wa, g, 0);
+      load(wa, g + 2);
+      compute(wb, g + 1, 1);
+      load(wb, g + 3);
+    }
+    compute(wa, g, 0);
+    compute(wb, g + 1, 1);
+    lds_barrier();
+  }
+}
+
+template <bool SWIGLU, int R>
+hipError_t launch_gemv_r(const void *A, const int32_t *perm, int kslots, const void *B1,
+                         const void *B3, void *C, const int32_t *seg_off, const int32_t *active,
+                         const int32_t *nactive, int G, int N, int K, hipStream_t s) {
+  const int kc = K / (GV_WAVES * GV_CHUNK);
+  constexpr int NW = SWIGLU ? 2 : 1;
+  // columns per workgroup: a power of two from two groups up to 256, with
+  // about 128 workgroups per active expert (fewer, longer workgroups stream
+  // best)
+  int cpw = 256;
+  while (cpw > 1 && 2 * (N / cpw) < 256) cpw /= 2;
+  const bf16_t *a = (const bf16_t *)A, *b1 = (const bf16_t *)B1, *b3 = (const bf16_t *)B3;
+#define GV_CASE(KC_)                                                                          \
+  case KC_: {                                                                                 \
+    constexpr int CB = gv_cb(NW * KC_);                                                       \
+    const int cw = cpw < 2 * CB ? 2 * CB : cpw;                                               \
+    if (N % cw) return hipErrorInvalidValue;                                                  \
+    hipLaunchKernelGGL((gemv_kernel<SWIGLU, R, KC_>), dim3(G * (N / cw)), dim3(GV_THREADS),   \
+                       0, s, a, perm, kslots, b1, b3, C, seg_off, active, nactive, N, K, cw);  \
+    break;                                                                                    \
+  }
+  switch (kc) {
+    GV_CASE(1) GV_CASE(2) GV_CASE(3) GV_CASE(4) GV_CASE(5) GV_CASE(6) GV_CASE(7) GV_CASE(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef GV_CASE
+  return hipGetLastError();
+}
+
+template <bool SWIGLU>
+hipError_t launch_gemv(int rows, const void *A, const int32_t *perm, int kslots, const void *B1,
+                       const void *B3, void *C, const int32_t *seg_off, const int32_t *active,
+                       const int32_t *nactive, int G, int N, int K, hipStream_t s) {
+  if (rows <= 1)
+    return launch_gemv_r<SWIGLU, 1>(A, perm, kslots, B1, B3, C, seg_off, active, nactive, G, N, K, s);
+  if (rows <= 2)
+    return launch_gemv_r<SWIGLU, 2>(A, perm, kslots, B1, B3, C, seg_off, active, nactive, G, N, K, s);
+  return launch_gemv_r<SWIGLU, 4>(A, perm, kslots, B1, B3, C, seg_off, active, nactive, G, N, K, s);
+}
+
 }  // namespace
 
 bool skinny_ok(int N, int K) { return N % SK_NB == 0 && K % (SK_WAVES * SK_KC) == 0; }
@@ -170,6 +375,25 @@ hipError_t launch_skinny_down(int mb, const void *Hin, const void *W2, float *Y,
                               const int32_t *nactive, int G, int N, int K, hipStream_t s) {
   return launch_mb<false>(mb, Hin, nullptr, 1, W2, nullptr, Y, seg_off, active, nactive, G, N,
                           K, s);
+}
+
+bool gemv_ok(int N, int K) {
+  const int kc = K / (GV_WAVES * GV_CHUNK);
+  return K % (GV_WAVES * GV_CHUNK) == 0 && kc >= 1 && kc <= 8 && N % 64 == 0;
+}
+
+hipError_t launch_gemv_swiglu(int rows, const void *x, const int32_t *perm, int kslots,
+                              const void *W1, const void *W3, void *H, const int32_t *seg_off,
+                              const int32_t *active, const int32_t *nactive, int G, int N, int K,
+                              hipStream_t s) {
+  return launch_gemv<true>(rows, x, perm, kslots, W1, W3, H, seg_off, active, nactive, G, N, K, s);
+}
+
+hipError_t launch_gemv_down(int rows, const void *Hin, const void *W2, float *Y,
+                            const int32_t *seg_off, const int32_t *active,
+                            const int32_t *nactive, int G, int N, int K, hipStream_t s) {
+  return launch_gemv<false>(rows, Hin, nullptr, 1, W2, nullptr, Y, seg_off, active, nactive, G,
+                            N, K, s);
 }
 
 }  // namespace moe

@@ -36,6 +36,15 @@ hipError_t launch_gemm_down(int dtype, bool dl, int bm, const void *A, const voi
 
 // Weight-streaming grouped GEMMs for few rows per expert (bf16 only).
 bool skinny_ok(int N, int K);
+// vector-ALU weight streaming for experts holding at most `rows` (<= 4) rows
+bool gemv_ok(int N, int K);
+hipError_t launch_gemv_swiglu(int rows, const void *x, const int32_t *perm, int kslots,
+                              const void *W1, const void *W3, void *H, const int32_t *seg_off,
+                              const int32_t *active, const int32_t *nactive, int G, int N, int K,
+                              hipStream_t s);
+hipError_t launch_gemv_down(int rows, const void *Hin, const void *W2, float *Y,
+                            const int32_t *seg_off, const int32_t *active,
+                            const int32_t *nactive, int G, int N, int K, hipStream_t s);
 hipError_t launch_skinny_swiglu(int mb, const void *x, const int32_t *perm, int kslots,
                                 const void *W1, const void *W3, void *H,
                                 const int32_t *seg_off, const int32_t *active,

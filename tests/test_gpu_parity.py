@@ -229,6 +229,10 @@ EDGE = [
     ("skinny_hot_expert_two_passes", 70, 256, 4, 512, 2, "bf16", 0, ("hot", 2, 100.0)),
     ("skinny_shared", 40, 256, 8, 256, 2, "bf16", 256, None),
     ("skinny_E256_k8", 64, 512, 256, 256, 8, "bf16", 0, None),
+    # vector-ALU weight streaming (at most four tokens, K a multiple of 2048)
+    ("gemv_T1", 1, 2048, 8, 2048, 2, "bf16", 0, None),
+    ("gemv_T2_K6144_shared", 2, 2048, 4, 6144, 2, "bf16", 2048, None),
+    ("gemv_T4_hot_expert", 4, 2048, 8, 4096, 2, "bf16", 0, ("hot", 1, 100.0)),
 ]
 
 
