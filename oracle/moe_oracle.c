@@ -23,6 +23,9 @@
  *          and the numpy forward listing.
  *  [MIXA]  "Mixtral and MoE architecture" (astro-blog-cod.pages.dev), the
  *          MixtralMoE / FeedForward listing.
+ *  [OVW]   "Mixtral 8x7B model architecture" (bjdmk.com.cn news 6109040),
+ *          section 1.2 (the Router: softmax over all experts, then top-k).
+ *  [SMoE] section 2.4 also states the expert capacity limit used below.
  *
  * Layouts (row-major; every weight held as a Linear weight [out][in]):
  *   x   [T][d]         Wg  [E][d]        bias [E] (fp32, optional)
@@ -37,6 +40,11 @@
  *   orc_swiglu_row    pinned (E=1,k=1 dense FFN via numpy matmul)
  *   orc_forward       pinned (k=E softmax-weighted sum; invariants)
  *   orc_param_count   pinned (50,331,648 stated as 50.3M on [BENCH])
+ *   orc_gate_mode     pinned (torch softmax / sigmoid of the logits)
+ *   act GLU_SIGMOID   pinned (dense FFN via torch; the [BENCH] fused-weight
+ *                     formulation recomputed in numpy)
+ *   orc_keep          pinned (brute force on tiny inputs; no-drop case)
+ *   orc_capacity      pinned (the two worked numbers of [SMoE] 2.4)
  */
 #include <math.h>
 #ifdef _OPENMP
@@ -148,6 +156,65 @@ void orc_gate(const double *logits, const int32_t *idx, long T, int E, int k,
     }
 }
 
+/* Gate weights, all variants the pages print.  mode:
+ *  0  softmax over the k selected logits (orc_gate above) [SMoE 3.2; CH10 10.3]
+ *  1  softmax over all E logits, the selected entries taken as they are (no
+ *     renormalisation, the gates sum to at most one) [OVW 1.2 Router]
+ *  2  logistic sigmoid of each selected logit on its own [BENCH listing]. */
+void orc_gate_mode(const double *logits, const int32_t *idx, long T, int E,
+                   int k, int mode, double *gate)
+{
+    if (mode == 0) {
+        orc_gate(logits, idx, T, E, k, gate);
+        return;
+    }
+    for (long t = 0; t < T; ++t) {
+        const double *l = logits + (size_t)t * E;
+        const int32_t *ix = idx + (size_t)t * k;
+        if (mode == 1) {
+            double m = l[0];
+            for (int e = 1; e < E; ++e)
+                if (l[e] > m)
+                    m = l[e];
+            double zall = 0.0;
+            for (int e = 0; e < E; ++e)
+                zall += exp(l[e] - m);
+            for (int j = 0; j < k; ++j)
+                gate[(size_t)t * k + j] = exp(l[ix[j]] - m) / zall;
+        } else {
+            for (int j = 0; j < k; ++j)
+                gate[(size_t)t * k + j] = 1.0 / (1.0 + exp(-l[ix[j]]));
+        }
+    }
+}
+
+/* Expert capacity [SMoE 2.4]: an expert takes at most min(k*T, floor(cf*T))
+ * of a batch's T tokens (the page's two examples: batch 32, k=2 -> min(64,
+ * 1.2*32); batch 16 -> 1.2*16 = 19). */
+long orc_capacity(long T, int k, double cf)
+{
+    long c = (long)floor(cf * (double)T);
+    long m = (long)k * T;
+    return c < m ? c : m;
+}
+
+/* Which pairs an expert keeps under a capacity [SMoE 2.4 states the limit but
+ * not which pairs go; reading: an expert keeps its first `capacity` pairs in
+ * ascending pair id p = t*k + j, i.e. earlier tokens first].  keep[p] = 1 or
+ * 0.  A dropped pair contributes nothing and the token's other gates are not
+ * renormalised. */
+void orc_keep(const int32_t *idx, long T, int E, int k, long capacity,
+              int32_t *keep)
+{
+    long *seen = calloc((size_t)E, sizeof(long));
+    for (long p = 0; p < T * (long)k; ++p) {
+        int e = idx[p];
+        keep[p] = seen[e] < capacity ? 1 : 0;
+        seen[e] += 1;
+    }
+    free(seen);
+}
+
 /* Tokens per expert [CH10 10.4 grouping by expert; BENCH listing's per-expert
  * row lists]: counts[e] = number of (token, slot) pairs routed to e;
  * offsets is the exclusive prefix sum, offsets[E] = T*k. */
@@ -182,20 +249,24 @@ void orc_permute(const int32_t *idx, long T, int E, int k,
     free(cursor);
 }
 
-/* One SwiGLU expert on one token [SMoE 3.1; CH10 10.1; MIXA FeedForward]:
- * a = W1 x, c = W3 x (length dff), h = SiLU(a) * c with SiLU(a) = a/(1+e^-a),
+/* One gated expert on one token: a = W1 x, c = W3 x (length dff),
+ *   act 0 (SwiGLU) [SMoE 3.1; CH10 10.1; MIXA FeedForward]:
+ *         h = SiLU(a) * c with SiLU(a) = a/(1+e^-a);
+ *   act 1 (sigmoid GLU) [BENCH listing: the fused up projection's second half
+ *         gates the first through a logistic sigmoid; here W1 is that gated
+ *         half and W3 the other]: h = c / (1+e^-a);
  * out = W2 h (length d).  xr is the token row already widened to double;
  * w1/w3/w2 point at this expert's matrices, element offsets o1/o3/o2. */
 static void swiglu(const double *xr, int d, int dff, const void *W1, size_t o1,
                    const void *W3, size_t o3, const void *W2, size_t o2, int dt,
-                   double *h, double *wrow, double *out)
+                   int act, double *h, double *wrow, double *out)
 {
     for (int n = 0; n < dff; ++n) {
         row_to_double(W1, dt, o1 + (size_t)n * d, d, wrow);
         double a = dot(xr, wrow, d);
         row_to_double(W3, dt, o3 + (size_t)n * d, d, wrow);
         double c = dot(xr, wrow, d);
-        h[n] = a / (1.0 + exp(-a)) * c;
+        h[n] = act == 1 ? c / (1.0 + exp(-a)) : a / (1.0 + exp(-a)) * c;
     }
     for (int j = 0; j < d; ++j) {
         row_to_double(W2, dt, o2 + (size_t)j * dff, dff, wrow);
@@ -204,9 +275,10 @@ static void swiglu(const double *xr, int d, int dff, const void *W1, size_t o1,
 }
 
 /* Exposed single-row expert evaluation (used by per-token sampled checks):
- * out[d] = W2_e(SiLU(W1_e x_t) * W3_e x_t). */
+ * out[d] = W2_e(act(W1_e x_t, W3_e x_t)). */
 void orc_swiglu_row(const void *x, int dt, long t, int d, const void *W1,
-                    const void *W3, const void *W2, int e, int dff, double *out)
+                    const void *W3, const void *W2, int e, int dff, int act,
+                    double *out)
 {
     int wmax = d > dff ? d : dff;
     double *xr = malloc(sizeof(double) * d);
@@ -214,7 +286,7 @@ void orc_swiglu_row(const void *x, int dt, long t, int d, const void *W1,
     double *wrow = malloc(sizeof(double) * wmax);
     row_to_double(x, dt, (size_t)t * d, d, xr);
     size_t eo = (size_t)e * dff * d;
-    swiglu(xr, d, dff, W1, eo, W3, eo, W2, eo, dt, h, wrow, out);
+    swiglu(xr, d, dff, W1, eo, W3, eo, W2, eo, dt, act, h, wrow, out);
     free(xr);
     free(h);
     free(wrow);
@@ -223,20 +295,24 @@ void orc_swiglu_row(const void *x, int dt, long t, int d, const void *W1,
 /* Whole layer, computed through the permutation (the pages group pairs by
  * expert before running each expert):
  *   Yp[s] = FFN_e(x_t) with p = perm[s], t = p / k, e = idx[p];
- *   y[t]  = sum_{j<k} gate[t][j] * Yp[inv[t*k+j]]   (j ascending)
+ *   y[t]  = sum_{j<k, pair kept} gate[t][j] * Yp[inv[t*k+j]]   (j ascending)
  *           + shared FFN(x_t) with weight 1 when Ws1 != NULL [CH10 10.5].
+ * gate_mode (orc_gate_mode), act (swiglu) and capacity (orc_keep; a value
+ * >= T*k drops nothing) select the variants; only kept pairs are placed, so
+ * counts/offsets/perm cover the kept pairs and inv[p] = -1 for a dropped one.
  * Routing comes from `logits_in` when given (e.g. another implementation's
  * router scores), else from orc_logits.  Outputs that are non-NULL receive
  * the intermediates.  y is [T][d] in double.  Returns 0 or -1. */
-int orc_forward(const void *x, const void *Wg, const float *bias,
-                const void *W1, const void *W3, const void *W2,
-                const void *Ws1, const void *Ws3, const void *Ws2, int dffs,
-                long T, int E, int k, int d, int dff, int dt,
-                const double *logits_in, double *logits_out, int32_t *idx_out,
-                double *gate_out, int32_t *counts_out, int32_t *offsets_out,
-                int32_t *perm_out, int32_t *inv_out, double *y)
+int orc_forward_ex(const void *x, const void *Wg, const float *bias,
+                   const void *W1, const void *W3, const void *W2,
+                   const void *Ws1, const void *Ws3, const void *Ws2, int dffs,
+                   long T, int E, int k, int d, int dff, int dt, int gate_mode,
+                   int act, long capacity, const double *logits_in,
+                   double *logits_out, int32_t *idx_out, double *gate_out,
+                   int32_t *counts_out, int32_t *offsets_out,
+                   int32_t *perm_out, int32_t *inv_out, double *y)
 {
-    if (T < 0 || E < 1 || k < 1 || k > E || d < 1 || dff < 1)
+    if (T < 0 || E < 1 || k < 1 || k > E || d < 1 || dff < 1 || capacity < 0)
         return -1;
     long P = T * (long)k;
     double *logits = malloc(sizeof(double) * (size_t)(T > 0 ? T : 1) * E);
@@ -250,10 +326,35 @@ int orc_forward(const void *x, const void *Wg, const float *bias,
     int32_t *offsets = malloc(sizeof(int32_t) * (size_t)(E + 1));
     int32_t *perm = malloc(sizeof(int32_t) * (size_t)(P > 0 ? P : 1));
     int32_t *inv = malloc(sizeof(int32_t) * (size_t)(P > 0 ? P : 1));
+    int32_t *keep = malloc(sizeof(int32_t) * (size_t)(P > 0 ? P : 1));
     orc_topk(logits, T, E, k, idx);
-    orc_gate(logits, idx, T, E, k, gate);
-    orc_count(idx, T, E, k, counts, offsets);
-    orc_permute(idx, T, E, k, offsets, perm, inv);
+    orc_gate_mode(logits, idx, T, E, k, gate_mode, gate);
+    orc_keep(idx, T, E, k, capacity, keep);
+    /* counts and the stable grouping over the kept pairs only */
+    for (int e = 0; e < E; ++e)
+        counts[e] = 0;
+    for (long p = 0; p < P; ++p)
+        if (keep[p])
+            counts[idx[p]] += 1;
+    offsets[0] = 0;
+    for (int e = 0; e < E; ++e)
+        offsets[e + 1] = offsets[e] + counts[e];
+    {
+        int32_t *cursor = malloc(sizeof(int32_t) * (size_t)E);
+        for (int e = 0; e < E; ++e)
+            cursor[e] = offsets[e];
+        for (long p = 0; p < P; ++p) {
+            if (!keep[p]) {
+                inv[p] = -1;
+                continue;
+            }
+            int32_t sl = cursor[idx[p]]++;
+            perm[sl] = (int32_t)p;
+            inv[p] = sl;
+        }
+        free(cursor);
+    }
+    const long nkept = offsets[E];
 
     double *Yp = malloc(sizeof(double) * (size_t)(P > 0 ? P : 1) * d);
     int wmax = d > dff ? d : dff;
@@ -265,13 +366,13 @@ int orc_forward(const void *x, const void *Wg, const float *bias,
         double *h = malloc(sizeof(double) * (dff > dffs ? dff : dffs));
         double *wrow = malloc(sizeof(double) * wmax);
 #pragma omp for schedule(dynamic, 1)
-        for (long s = 0; s < P; ++s) {
+        for (long s = 0; s < nkept; ++s) {
             long p = perm[s];
             long t = p / k;
             int e = idx[p];
             size_t eo = (size_t)e * dff * d;
             row_to_double(x, dt, (size_t)t * d, d, xr);
-            swiglu(xr, d, dff, W1, eo, W3, eo, W2, eo, dt, h, wrow,
+            swiglu(xr, d, dff, W1, eo, W3, eo, W2, eo, dt, act, h, wrow,
                    Yp + (size_t)s * d);
         }
 #pragma omp for schedule(dynamic, 1)
@@ -280,15 +381,18 @@ int orc_forward(const void *x, const void *Wg, const float *bias,
             for (int c = 0; c < d; ++c)
                 yt[c] = 0.0;
             for (int j = 0; j < k; ++j) {
+                int32_t sl = inv[(size_t)t * k + j];
+                if (sl < 0)
+                    continue; /* dropped by the capacity limit */
                 double g = gate[(size_t)t * k + j];
-                const double *yp = Yp + (size_t)inv[(size_t)t * k + j] * d;
+                const double *yp = Yp + (size_t)sl * d;
                 for (int c = 0; c < d; ++c)
                     yt[c] += g * yp[c];
             }
             if (Ws1) {
                 double *ys = malloc(sizeof(double) * d);
                 row_to_double(x, dt, (size_t)t * d, d, xr);
-                swiglu(xr, d, dffs, Ws1, 0, Ws3, 0, Ws2, 0, dt, h, wrow, ys);
+                swiglu(xr, d, dffs, Ws1, 0, Ws3, 0, Ws2, 0, dt, act, h, wrow, ys);
                 for (int c = 0; c < d; ++c)
                     yt[c] += ys[c];
                 free(ys);
@@ -310,7 +414,7 @@ int orc_forward(const void *x, const void *Wg, const float *bias,
     if (offsets_out)
         memcpy(offsets_out, offsets, sizeof(int32_t) * (size_t)(E + 1));
     if (perm_out)
-        memcpy(perm_out, perm, sizeof(int32_t) * (size_t)P);
+        memcpy(perm_out, perm, sizeof(int32_t) * (size_t)nkept);
     if (inv_out)
         memcpy(inv_out, inv, sizeof(int32_t) * (size_t)P);
     free(logits);
@@ -320,19 +424,36 @@ int orc_forward(const void *x, const void *Wg, const float *bias,
     free(offsets);
     free(perm);
     free(inv);
+    free(keep);
     free(Yp);
     return 0;
 }
 
+/* The method as the spec pages define it: softmax over the selected
+ * logits, SwiGLU experts, no capacity limit. */
+int orc_forward(const void *x, const void *Wg, const float *bias,
+                const void *W1, const void *W3, const void *W2,
+                const void *Ws1, const void *Ws3, const void *Ws2, int dffs,
+                long T, int E, int k, int d, int dff, int dt,
+                const double *logits_in, double *logits_out, int32_t *idx_out,
+                double *gate_out, int32_t *counts_out, int32_t *offsets_out,
+                int32_t *perm_out, int32_t *inv_out, double *y)
+{
+    return orc_forward_ex(x, Wg, bias, W1, W3, W2, Ws1, Ws3, Ws2, dffs, T, E, k,
+                          d, dff, dt, 0, 0, T * (long)k, logits_in, logits_out,
+                          idx_out, gate_out, counts_out, offsets_out, perm_out,
+                          inv_out, y);
+}
+
 /* Output rows for a chosen list of tokens, given their routing (idx, gate
- * rows of those tokens): y[r] = sum_j gate[r][j] * FFN_{idx[r][j]}(x_{tok[r]})
- * (+ shared FFN).  Each token's output depends only on its own routing, so a
+ * rows of those tokens; a zero gate marks a dropped pair): y[r] = sum_j
+ * gate[r][j] * FFN_{idx[r][j]}(x_{tok[r]}) (+ shared FFN).  Each token's output depends only on its own routing, so a
  * sample of a large workload can be checked row by row. */
 void orc_forward_rows(const void *x, const void *W1, const void *W3,
                       const void *W2, const void *Ws1, const void *Ws3,
                       const void *Ws2, int dffs, int k, int d, int dff, int dt,
-                      long nrows, const int64_t *tok, const int32_t *idx,
-                      const double *gate, double *y)
+                      int act, long nrows, const int64_t *tok,
+                      const int32_t *idx, const double *gate, double *y)
 {
     int wmax = d > dff ? d : dff;
     if (dffs > wmax)
@@ -352,13 +473,15 @@ void orc_forward_rows(const void *x, const void *W1, const void *W3,
             for (int j = 0; j < k; ++j) {
                 int e = idx[(size_t)r * k + j];
                 size_t eo = (size_t)e * dff * d;
-                swiglu(xr, d, dff, W1, eo, W3, eo, W2, eo, dt, h, wrow, o);
                 double g = gate[(size_t)r * k + j];
+                if (g == 0.0)
+                    continue; /* a pair dropped by a capacity limit */
+                swiglu(xr, d, dff, W1, eo, W3, eo, W2, eo, dt, act, h, wrow, o);
                 for (int c = 0; c < d; ++c)
                     yr[c] += g * o[c];
             }
             if (Ws1) {
-                swiglu(xr, d, dffs, Ws1, 0, Ws3, 0, Ws2, 0, dt, h, wrow, o);
+                swiglu(xr, d, dffs, Ws1, 0, Ws3, 0, Ws2, 0, dt, act, h, wrow, o);
                 for (int c = 0; c < d; ++c)
                     yr[c] += o[c];
             }

@@ -21,6 +21,9 @@ _SRC = os.path.join(_HERE, "moe_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 F32, BF16 = 0, 1
+# gate variants (orc_gate_mode) and expert activations (swiglu in moe_oracle.c)
+GATE_SOFTMAX_TOPK, GATE_SOFTMAX_ALL, GATE_SIGMOID = 0, 1, 2
+ACT_SWIGLU, ACT_GLU_SIGMOID = 0, 1
 
 
 def build(force: bool = False) -> str:
@@ -51,15 +54,26 @@ def _bind(path: str):
     L.orc_permute.argtypes = [i32p, ctypes.c_long, ctypes.c_int, ctypes.c_int, i32p, i32p,
                               i32p]
     L.orc_swiglu_row.argtypes = [vp, ctypes.c_int, ctypes.c_long, ctypes.c_int, vp, vp, vp,
-                                 ctypes.c_int, ctypes.c_int, f64p]
+                                 ctypes.c_int, ctypes.c_int, ctypes.c_int, f64p]
+    L.orc_gate_mode.argtypes = [f64p, i32p, ctypes.c_long, ctypes.c_int, ctypes.c_int,
+                                ctypes.c_int, f64p]
+    L.orc_capacity.argtypes = [ctypes.c_long, ctypes.c_int, ctypes.c_double]
+    L.orc_capacity.restype = ctypes.c_long
+    L.orc_keep.argtypes = [i32p, ctypes.c_long, ctypes.c_int, ctypes.c_int, ctypes.c_long, i32p]
+    L.orc_forward_ex.argtypes = ([vp, vp, f32p, vp, vp, vp, vp, vp, vp, ctypes.c_int,
+                                  ctypes.c_long, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_long]
+                                 + [f64p, f64p, i32p, f64p, i32p, i32p, i32p, i32p, f64p])
+    L.orc_forward_ex.restype = ctypes.c_int
     L.orc_forward.argtypes = ([vp, vp, f32p, vp, vp, vp, vp, vp, vp, ctypes.c_int,
                                ctypes.c_long, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                ctypes.c_int, ctypes.c_int]
                               + [f64p, f64p, i32p, f64p, i32p, i32p, i32p, i32p, f64p])
     L.orc_forward.restype = ctypes.c_int
     L.orc_forward_rows.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int,
-                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_long,
-                                   vp, i32p, f64p, f64p]
+                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_long, vp, i32p, f64p, f64p]
     L.orc_param_count.argtypes = [ctypes.c_longlong] * 3
     L.orc_param_count.restype = ctypes.c_longlong
     L.orc_active_fraction.argtypes = [ctypes.c_int, ctypes.c_int]
@@ -134,11 +148,35 @@ def gate(lg, idx):
     return g
 
 
-def route(x, Wg, k, bias=None, logits_in=None):
+def gate_mode(lg, idx, mode):
+    """Gates of one of the variants (GATE_SOFTMAX_TOPK, GATE_SOFTMAX_ALL, GATE_SIGMOID)."""
+    lg, idx = _c(lg, np.float64), _c(idx, np.int32)
+    T, E = lg.shape
+    k = idx.shape[1]
+    g = np.empty((T, k), np.float64)
+    lib().orc_gate_mode(_ptr(lg), _ptr(idx), T, E, k, int(mode), _ptr(g))
+    return g
+
+
+def capacity(T, k, cf) -> int:
+    """Per-expert capacity min(k*T, floor(cf*T))."""
+    return int(lib().orc_capacity(T, k, float(cf)))
+
+
+def keep(idx, E, cap):
+    """1 for the pairs an expert keeps under capacity `cap` (first by pair id)."""
+    idx = _c(idx, np.int32)
+    T, k = idx.shape
+    out = np.empty(T * k, np.int32)
+    lib().orc_keep(_ptr(idx), T, E, k, int(cap), _ptr(out))
+    return out
+
+
+def route(x, Wg, k, bias=None, logits_in=None, gate_mode_=GATE_SOFTMAX_TOPK):
     """(logits, idx, gate) with the oracle's own fp64 logits or given ones."""
     lg = logits(x, Wg, bias) if logits_in is None else _c(logits_in, np.float64)
     idx = topk(lg, k)
-    return lg, idx, gate(lg, idx)
+    return lg, idx, gate_mode(lg, idx, gate_mode_)
 
 
 def count(idx, E):
@@ -160,20 +198,23 @@ def permute(idx, E):
     return counts, offsets, perm, inv
 
 
-def expert_row(x, t, W1, W3, W2, e):
-    """W2_e(SiLU(W1_e x_t) * W3_e x_t) for one token (fp64, length d)."""
+def expert_row(x, t, W1, W3, W2, e, act=ACT_SWIGLU):
+    """W2_e(act(W1_e x_t, W3_e x_t)) for one token (fp64, length d)."""
     x, W1, W3, W2 = _c(x), _c(W1), _c(W3), _c(W2)
     d = x.shape[1]
     dff = W1.shape[1]
     out = np.empty(d, np.float64)
     lib().orc_swiglu_row(_ptr(x), _dtype_code(x), t, d, _ptr(W1), _ptr(W3), _ptr(W2), e, dff,
-                         _ptr(out))
+                         int(act), _ptr(out))
     return out
 
 
-def forward(x, Wg, W1, W3, W2, k, bias=None, shared=None, logits_in=None):
+def forward(x, Wg, W1, W3, W2, k, bias=None, shared=None, logits_in=None,
+            gate_mode=GATE_SOFTMAX_TOPK, act=ACT_SWIGLU, capacity=None):
     """Whole layer through the permutation.  Returns a dict with y and every
-    intermediate (logits, idx, gate, counts, offsets, perm, inv)."""
+    intermediate (logits, idx, gate, counts, offsets, perm, inv).  With a
+    capacity, counts/offsets/perm cover the kept pairs (perm has offsets[E]
+    entries) and inv is -1 for a dropped pair."""
     x, Wg, W1, W3, W2 = _c(x), _c(Wg), _c(W1), _c(W3), _c(W2)
     bias = _c(bias, np.float32)
     T, d = x.shape
@@ -192,18 +233,29 @@ def forward(x, Wg, W1, W3, W2, k, bias=None, shared=None, logits_in=None):
                gate=np.empty((T, k)), counts=np.empty(E, np.int32),
                offsets=np.empty(E + 1, np.int32), perm=np.empty(P, np.int32),
                inv=np.empty(P, np.int32), y=np.empty((T, d)))
-    rc = lib().orc_forward(_ptr(x), _ptr(Wg), _ptr(bias), _ptr(W1), _ptr(W3), _ptr(W2),
-                           _ptr(Ws1), _ptr(Ws3), _ptr(Ws2), dffs, T, E, k, d, dff, dt,
-                           _ptr(lg_in), _ptr(out["logits"]), _ptr(out["idx"]),
-                           _ptr(out["gate"]), _ptr(out["counts"]), _ptr(out["offsets"]),
-                           _ptr(out["perm"]), _ptr(out["inv"]), _ptr(out["y"]))
+    cap = P if capacity is None else int(capacity)
+    if gate_mode == GATE_SOFTMAX_TOPK and act == ACT_SWIGLU and capacity is None:
+        rc = lib().orc_forward(_ptr(x), _ptr(Wg), _ptr(bias), _ptr(W1), _ptr(W3), _ptr(W2),
+                               _ptr(Ws1), _ptr(Ws3), _ptr(Ws2), dffs, T, E, k, d, dff, dt,
+                               _ptr(lg_in), _ptr(out["logits"]), _ptr(out["idx"]),
+                               _ptr(out["gate"]), _ptr(out["counts"]), _ptr(out["offsets"]),
+                               _ptr(out["perm"]), _ptr(out["inv"]), _ptr(out["y"]))
+    else:
+        rc = lib().orc_forward_ex(_ptr(x), _ptr(Wg), _ptr(bias), _ptr(W1), _ptr(W3), _ptr(W2),
+                                  _ptr(Ws1), _ptr(Ws3), _ptr(Ws2), dffs, T, E, k, d, dff, dt,
+                                  int(gate_mode), int(act), cap, _ptr(lg_in),
+                                  _ptr(out["logits"]), _ptr(out["idx"]), _ptr(out["gate"]),
+                                  _ptr(out["counts"]), _ptr(out["offsets"]), _ptr(out["perm"]),
+                                  _ptr(out["inv"]), _ptr(out["y"]))
     if rc != 0:
-        raise ValueError("invalid layer shape or k")
+        raise ValueError("invalid layer shape, k or capacity")
+    out["perm"] = out["perm"][: int(out["offsets"][E])]
     return out
 
 
-def forward_rows(x, W1, W3, W2, tokens, idx_rows, gate_rows, shared=None):
-    """y rows for the listed tokens given those tokens' routing rows."""
+def forward_rows(x, W1, W3, W2, tokens, idx_rows, gate_rows, shared=None, act=ACT_SWIGLU):
+    """y rows for the listed tokens given those tokens' routing rows (a zero
+    gate marks a dropped pair)."""
     x, W1, W3, W2 = _c(x), _c(W1), _c(W3), _c(W2)
     tokens = _c(np.asarray(tokens), np.int64)
     idx_rows, gate_rows = _c(idx_rows, np.int32), _c(gate_rows, np.float64)
@@ -218,7 +270,7 @@ def forward_rows(x, W1, W3, W2, tokens, idx_rows, gate_rows, shared=None):
     n = tokens.shape[0]
     y = np.empty((n, d), np.float64)
     lib().orc_forward_rows(_ptr(x), _ptr(W1), _ptr(W3), _ptr(W2), _ptr(Ws1), _ptr(Ws3),
-                           _ptr(Ws2), dffs, k, d, dff, _dtype_code(x), n, _ptr(tokens),
+                           _ptr(Ws2), dffs, k, d, dff, _dtype_code(x), int(act), n, _ptr(tokens),
                            _ptr(idx_rows), _ptr(gate_rows), _ptr(y))
     return y
 
