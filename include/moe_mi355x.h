@@ -134,6 +134,65 @@ int moe_forward_timed(const void *x, const void *Wg, const float *bias, const vo
                       int dtype, void *workspace, size_t workspace_bytes, void *y, void *stream,
                       void *const *events);
 
+/* ------------------------------------------------------------------------
+ * Variants the pages print beside the method (all optional; the calls above
+ * are these with the defaults).
+ *
+ *   gate_mode  MOE_GATE_SOFTMAX_TOPK  softmax over the k selected logits (the
+ *                                     method; default)
+ *              MOE_GATE_SOFTMAX_ALL   softmax over all E logits, the selected
+ *                                     entries used as they are (no
+ *                                     renormalisation): the Router of "Mixtral
+ *                                     8x7B model architecture", section 1.2
+ *              MOE_GATE_SIGMOID       logistic sigmoid of each selected logit:
+ *                                     the numpy function of "Trillion-parameter
+ *                                     MoE ... 7 expert configs measured"
+ *   activation MOE_ACT_SWIGLU         W2( SiLU(W1 x) * (W3 x) )  (default)
+ *              MOE_ACT_GLU_SIGMOID    W2( sigmoid(W1 x) * (W3 x) ): the same
+ *                                     numpy function's gated projection (its
+ *                                     fused [a | g] weight is [W3 | W1] here)
+ *   capacity   at most `capacity` pairs per expert ("Mistral 8x7B SMoE
+ *              architecture deep dive", section 2.4); an expert keeps its
+ *              first pairs in pair order t*k+j (the page does not say which
+ *              pairs go), a dropped pair contributes nothing and the token's
+ *              other gates are not renormalised.  capacity < 0: no limit.
+ * ------------------------------------------------------------------------ */
+enum { MOE_GATE_SOFTMAX_TOPK = 0, MOE_GATE_SOFTMAX_ALL = 1, MOE_GATE_SIGMOID = 2 };
+enum { MOE_ACT_SWIGLU = 0, MOE_ACT_GLU_SIGMOID = 1 };
+
+typedef struct {
+    int gate_mode;  /* MOE_GATE_* */
+    int activation; /* MOE_ACT_* */
+    int capacity;   /* pairs per expert; < 0: no limit */
+} moe_options;
+
+/* The page's capacity for a batch of T tokens: min(k*T, floor(cf*T))
+ * ("Mistral 8x7B SMoE ..." section 2.4: cf = 1.2 gives 38 for T=32, k=2).
+ * Host-only arithmetic; returns -1 for T < 0, k < 1 or cf < 0. */
+int moe_capacity(int T, int k, double capacity_factor);
+
+/* moe_route with a gate variant (gate_mode as above); MOE_EINVAL for an
+ * unknown mode. */
+int moe_route_ex(const void *x, const void *Wg, const float *bias, int T, int d, int E, int k,
+                 int dtype, int gate_mode, int32_t *idx, float *gate, float *logits,
+                 void *workspace, size_t workspace_bytes, void *stream);
+
+/* moe_permute under a per-expert capacity (< 0: no limit).  Only kept pairs
+ * are placed: counts[e] = pairs kept by expert e, offsets their exclusive
+ * prefix sum (offsets[E] = kept pairs), perm has offsets[E] valid entries,
+ * inv[p] = -1 for a dropped pair (and for an id outside [0, E)). */
+int moe_permute_ex(const int32_t *idx, int T, int E, int k, int capacity, int32_t *counts,
+                   int32_t *offsets, int32_t *perm, int32_t *inv, void *workspace,
+                   size_t workspace_bytes, void *stream);
+
+/* moe_forward with the variants in `opt` (NULL: the defaults).  Same
+ * workspace; its counts/offsets/perm/inv fields then follow moe_permute_ex. */
+int moe_forward_ex(const void *x, const void *Wg, const float *bias, const void *W1,
+                   const void *W3, const void *W2, const void *Ws1, const void *Ws3,
+                   const void *Ws2, int d_ff_shared, int T, int E, int k, int d, int d_ff,
+                   int dtype, const moe_options *opt, void *workspace, size_t workspace_bytes,
+                   void *y, void *stream);
+
 /* Static text for a status code. */
 const char *moe_strerror(int status);
 

@@ -3,6 +3,8 @@
 // GEMM -> combine, all enqueued on the caller's stream with no host sync.
 #include <string.h>
 
+#include <cmath>
+
 #include "../../include/moe_mi355x.h"
 #include "kernels.h"
 
@@ -153,10 +155,11 @@ size_t moe_route_workspace_bytes(int T, int d, int E, int dtype) {
   return align_up(moe::router_partial_bytes(T, d, E, (int)esize(dtype))) + kAlign;
 }
 
-int moe_route(const void *x, const void *Wg, const float *bias, int T, int d, int E, int k,
-              int dtype, int32_t *idx, float *gate, float *logits, void *workspace,
-              size_t workspace_bytes, void *stream) {
+int moe_route_ex(const void *x, const void *Wg, const float *bias, int T, int d, int E, int k,
+                 int dtype, int gate_mode, int32_t *idx, float *gate, float *logits,
+                 void *workspace, size_t workspace_bytes, void *stream) {
   if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_EDTYPE;
+  if (gate_mode < MOE_GATE_SOFTMAX_TOPK || gate_mode > MOE_GATE_SIGMOID) return MOE_EINVAL;
   if (T < 0 || E < 1 || E > 256 || k < 1 || k > E || d < 64 || d % 64) return MOE_EINVAL;
   if ((long long)T * E >= (1LL << 31)) return MOE_EINVAL;
   if (T == 0) return MOE_OK;
@@ -166,8 +169,23 @@ int moe_route(const void *x, const void *Wg, const float *bias, int T, int d, in
     return MOE_EWORKSPACE;
   int st = device_ok();
   if (st != MOE_OK) return st;
-  return launched(moe::launch_router(dtype, x, Wg, bias, T, d, E, k, idx, gate, logits,
-                                     (float *)workspace, (hipStream_t)stream));
+  return launched(moe::launch_router(dtype, x, Wg, bias, T, d, E, k, gate_mode, idx, gate,
+                                     logits, (float *)workspace, (hipStream_t)stream));
+}
+
+int moe_route(const void *x, const void *Wg, const float *bias, int T, int d, int E, int k,
+              int dtype, int32_t *idx, float *gate, float *logits, void *workspace,
+              size_t workspace_bytes, void *stream) {
+  return moe_route_ex(x, Wg, bias, T, d, E, k, dtype, MOE_GATE_SOFTMAX_TOPK, idx, gate, logits,
+                      workspace, workspace_bytes, stream);
+}
+
+int moe_capacity(int T, int k, double capacity_factor) {
+  if (T < 0 || k < 1 || !(capacity_factor >= 0.0)) return -1;
+  const double c = std::floor(capacity_factor * (double)T);
+  const long long m = (long long)k * T;
+  const long long cap = c < (double)m ? (long long)c : m;
+  return cap > INT32_MAX ? INT32_MAX : (int)cap;
 }
 
 size_t moe_permute_workspace_bytes(int T, int E, int k) {
@@ -176,9 +194,9 @@ size_t moe_permute_workspace_bytes(int T, int E, int k) {
   return align_up(nb * E * 4) + 4 * align_up((size_t)(E + 1) * 4 + 32);
 }
 
-int moe_permute(const int32_t *idx, int T, int E, int k, int32_t *counts, int32_t *offsets,
-                int32_t *perm, int32_t *inv, void *workspace, size_t workspace_bytes,
-                void *stream) {
+int moe_permute_ex(const int32_t *idx, int T, int E, int k, int capacity, int32_t *counts,
+                   int32_t *offsets, int32_t *perm, int32_t *inv, void *workspace,
+                   size_t workspace_bytes, void *stream) {
   if (T < 0 || E < 1 || E > 256 || k < 1 || k > E) return MOE_EINVAL;
   if ((long long)T * k >= (1LL << 31)) return MOE_EINVAL;
   if (T == 0) {
@@ -202,8 +220,15 @@ int moe_permute(const int32_t *idx, int T, int E, int k, int32_t *counts, int32_
   int32_t *sh = mt1 + align_up((size_t)(E + 1) * 4 + 32) / 4;
   int32_t *act = sh + align_up((size_t)(E + 1) * 4 + 32) / 4;
   // the m-tile prefixes are by-products here; any tile height will do
-  return launched(moe::launch_permute(idx, T, E, k, 256, 256, blk, counts, offsets, perm, inv,
-                                      mt0, mt1, sh, act, (hipStream_t)stream));
+  return launched(moe::launch_permute(idx, T, E, k, capacity, 256, 256, blk, counts, offsets,
+                                      perm, inv, mt0, mt1, sh, act, (hipStream_t)stream));
+}
+
+int moe_permute(const int32_t *idx, int T, int E, int k, int32_t *counts, int32_t *offsets,
+                int32_t *perm, int32_t *inv, void *workspace, size_t workspace_bytes,
+                void *stream) {
+  return moe_permute_ex(idx, T, E, k, -1, counts, offsets, perm, inv, workspace,
+                        workspace_bytes, stream);
 }
 
 size_t moe_workspace_bytes(int T, int d, int d_ff, int E, int k, int d_ff_shared, int dtype) {
@@ -229,9 +254,12 @@ namespace {
 int forward_impl(const void *x, const void *Wg, const float *bias, const void *W1,
                  const void *W3, const void *W2, const void *Ws1, const void *Ws3,
                  const void *Ws2, int d_ff_shared, int T, int E, int k, int d, int d_ff,
-                 int dtype, void *workspace, size_t workspace_bytes, void *y, void *stream,
-                 void *const *events) {
+                 int dtype, const moe_options *opt, void *workspace, size_t workspace_bytes,
+                 void *y, void *stream, void *const *events) {
   if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_EDTYPE;
+  const moe_options o = opt ? *opt : moe_options{MOE_GATE_SOFTMAX_TOPK, MOE_ACT_SWIGLU, -1};
+  if (o.gate_mode < MOE_GATE_SOFTMAX_TOPK || o.gate_mode > MOE_GATE_SIGMOID) return MOE_EINVAL;
+  if (o.activation != MOE_ACT_SWIGLU && o.activation != MOE_ACT_GLU_SIGMOID) return MOE_EINVAL;
   if (!dims_ok(T, d, d_ff, E, k, d_ff_shared)) return MOE_EINVAL;
   const bool shared = d_ff_shared > 0;
   if (shared != (Ws1 != nullptr) || shared != (Ws3 != nullptr) || shared != (Ws2 != nullptr))
@@ -274,21 +302,21 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
 #define MOE_MARK(i) \
   if (events && hipEventRecord((hipEvent_t)events[i], s) != hipSuccess) goto fail;
   MOE_MARK(0);
-  if ((e = moe::launch_router(dtype, x, Wg, bias, T, d, E, k, idx, gate, logits,
+  if ((e = moe::launch_router(dtype, x, Wg, bias, T, d, E, k, o.gate_mode, idx, gate, logits,
                               at<float>(ws, L.off[F_RPART]), s)))
     goto fail;
   MOE_MARK(1);
-  if ((e = moe::launch_permute(idx, T, E, k, plan.bm1, plan.bm2, blk, counts, offsets, perm, inv,
-                               mt0, mt1, shseg, act, s)))
+  if ((e = moe::launch_permute(idx, T, E, k, o.capacity, plan.bm1, plan.bm2, blk, counts,
+                               offsets, perm, inv, mt0, mt1, shseg, act, s)))
     goto fail;
   MOE_MARK(2);
   if (sk.routed) {
     // few rows per expert: weight-streaming kernels; the gather rides in the first GEMM
     MOE_MARK(3);
-    if ((e = sk.gemv ? moe::launch_gemv_swiglu(T, x, perm, k, W1, W3, H, offsets, act, act + E,
-                                               E, d_ff, d, s)
-                     : moe::launch_skinny_swiglu(sk.mb, x, perm, k, W1, W3, H, offsets, act,
-                                                 act + E, E, d_ff, d, s)))
+    if ((e = sk.gemv ? moe::launch_gemv_swiglu(T, o.activation, x, perm, k, W1, W3, H, offsets,
+                                               act, act + E, E, d_ff, d, s)
+                     : moe::launch_skinny_swiglu(sk.mb, o.activation, x, perm, k, W1, W3, H,
+                                                 offsets, act, act + E, E, d_ff, d, s)))
       goto fail;
     MOE_MARK(4);
     if ((e = sk.gemv ? moe::launch_gemv_down(T, H, W2, Yp, offsets, act, act + E, E, d, d_ff, s)
@@ -297,10 +325,12 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
       goto fail;
     MOE_MARK(5);
   } else {
-    if ((e = moe::launch_gather(x, perm, P, k, d, (int)esize(dtype), Xp, s))) goto fail;
+    if ((e = moe::launch_gather(x, perm, offsets + E, P, k, d, (int)esize(dtype), Xp, s)))
+      goto fail;
     MOE_MARK(3);
-    if ((e = moe::launch_gemm_swiglu(dtype, plan.dl1, plan.bm1, Xp, W1, W3, H, offsets, mt0, E, d_ff, d,
-                                     (P + plan.bm1 - 1) / plan.bm1 + E, s)))
+    if ((e = moe::launch_gemm_swiglu(dtype, plan.dl1, plan.bm1, o.activation, Xp, W1, W3, H,
+                                     offsets, mt0, E, d_ff, d, (P + plan.bm1 - 1) / plan.bm1 + E,
+                                     s)))
       goto fail;
     MOE_MARK(4);
     if ((e = moe::launch_gemm_down(dtype, plan.dl2, plan.bm2, H, W2, Yp, offsets, mt1, E, d, d_ff,
@@ -310,22 +340,23 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
   }
   if (shared) {
     if (sk.gemv_shared) {
-      if ((e = moe::launch_gemv_swiglu(T, x, nullptr, 1, Ws1, Ws3, Hs, shseg, shseg + 6,
-                                       shseg + 7, 1, d_ff_shared, d, s)))
+      if ((e = moe::launch_gemv_swiglu(T, o.activation, x, nullptr, 1, Ws1, Ws3, Hs, shseg,
+                                       shseg + 6, shseg + 7, 1, d_ff_shared, d, s)))
         goto fail;
       if ((e = moe::launch_gemv_down(T, Hs, Ws2, Ys, shseg, shseg + 6, shseg + 7, 1, d,
                                      d_ff_shared, s)))
         goto fail;
     } else if (sk.shared) {
-      if ((e = moe::launch_skinny_swiglu(sk.mb_shared, x, nullptr, 1, Ws1, Ws3, Hs, shseg,
-                                         shseg + 6, shseg + 7, 1, d_ff_shared, d, s)))
+      if ((e = moe::launch_skinny_swiglu(sk.mb_shared, o.activation, x, nullptr, 1, Ws1, Ws3,
+                                         Hs, shseg, shseg + 6, shseg + 7, 1, d_ff_shared, d, s)))
         goto fail;
       if ((e = moe::launch_skinny_down(sk.mb_shared, Hs, Ws2, Ys, shseg, shseg + 6, shseg + 7, 1,
                                        d, d_ff_shared, s)))
         goto fail;
     } else {
-      if ((e = moe::launch_gemm_swiglu(dtype, plan.dl1, plan.bm1, x, Ws1, Ws3, Hs, shseg, shseg + 2, 1,
-                                       d_ff_shared, d, (T + plan.bm1 - 1) / plan.bm1, s)))
+      if ((e = moe::launch_gemm_swiglu(dtype, plan.dl1, plan.bm1, o.activation, x, Ws1, Ws3, Hs,
+                                       shseg, shseg + 2, 1, d_ff_shared, d,
+                                       (T + plan.bm1 - 1) / plan.bm1, s)))
         goto fail;
       if ((e = moe::launch_gemm_down(dtype, plan.dl2, plan.bm2, Hs, Ws2, Ys, shseg, shseg + 4, 1, d,
                                      d_ff_shared, (T + plan.bm2 - 1) / plan.bm2, 1, 0, s)))
@@ -352,7 +383,16 @@ int moe_forward(const void *x, const void *Wg, const float *bias, const void *W1
                 const void *Ws2, int d_ff_shared, int T, int E, int k, int d, int d_ff,
                 int dtype, void *workspace, size_t workspace_bytes, void *y, void *stream) {
   return forward_impl(x, Wg, bias, W1, W3, W2, Ws1, Ws3, Ws2, d_ff_shared, T, E, k, d, d_ff,
-                      dtype, workspace, workspace_bytes, y, stream, nullptr);
+                      dtype, nullptr, workspace, workspace_bytes, y, stream, nullptr);
+}
+
+int moe_forward_ex(const void *x, const void *Wg, const float *bias, const void *W1,
+                   const void *W3, const void *W2, const void *Ws1, const void *Ws3,
+                   const void *Ws2, int d_ff_shared, int T, int E, int k, int d, int d_ff,
+                   int dtype, const moe_options *opt, void *workspace, size_t workspace_bytes,
+                   void *y, void *stream) {
+  return forward_impl(x, Wg, bias, W1, W3, W2, Ws1, Ws3, Ws2, d_ff_shared, T, E, k, d, d_ff,
+                      dtype, opt, workspace, workspace_bytes, y, stream, nullptr);
 }
 
 int moe_forward_timed(const void *x, const void *Wg, const float *bias, const void *W1,
@@ -364,7 +404,7 @@ int moe_forward_timed(const void *x, const void *Wg, const float *bias, const vo
   for (int i = 0; i < MOE_NSTAGE_EVENTS; ++i)
     if (!events[i]) return MOE_EINVAL;
   return forward_impl(x, Wg, bias, W1, W3, W2, Ws1, Ws3, Ws2, d_ff_shared, T, E, k, d, d_ff,
-                      dtype, workspace, workspace_bytes, y, stream, events);
+                      dtype, nullptr, workspace, workspace_bytes, y, stream, events);
 }
 
 }  // extern "C"

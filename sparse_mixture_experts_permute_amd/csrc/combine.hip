@@ -1,5 +1,6 @@
 // Gate-weighted combine back to token order:
 //   y[t][:] = sum_{j<k} gate[t][j] * Yp[inv[t*k+j]][:]  (+ Ys[t][:] for the shared expert)
+// A pair with inv < 0 was dropped by an expert's capacity limit and adds nothing.
 // summed in fp32 with j ascending, written once per token with no atomics.
 // When the down projection split K, Yp has nsplit planes whose rows are added
 // first, in plane order
@@ -25,8 +26,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
   for (int c = threadIdx.x; c < d4; c += 256) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j = 0; j < k; ++j) {
+      const int slot = inv[(size_t)t * k + j];
+      if (slot < 0) continue;
       const float g = gate[(size_t)t * k + j];
-      const size_t row = (size_t)inv[(size_t)t * k + j] * d4 + c;
+      const size_t row = (size_t)slot * d4 + c;
       float4 v = reinterpret_cast<const float4 *>(Yp)[row];
       for (int sp = 1; sp < nsplit; ++sp) {
         const float4 u = reinterpret_cast<const float4 *>(Yp + sp * plane)[row];

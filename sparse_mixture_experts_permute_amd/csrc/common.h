@@ -64,6 +64,12 @@ __device__ __forceinline__ float silu(float a) {
   return a * __builtin_amdgcn_rcpf(1.0f + __expf(-a));
 }
 
+// Hidden unit of a gated expert from its two projections g = W1 x, u = W3 x:
+// act 0 SiLU(g) * u (SwiGLU), act 1 sigmoid(g) * u (sigmoid-gated GLU).
+__device__ __forceinline__ float gated(float g, float u, int act) {
+  return act ? u * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) : silu(g) * u;
+}
+
 // First index i in [0, n) with a[i+1] > g, for non-decreasing a[0..n] with a[0] <= g.
 __device__ __forceinline__ int upper_segment(const int32_t *a, int n, int g) {
   int lo = 0, hi = n;  // invariant: a[lo] <= g, answer in [lo, hi)

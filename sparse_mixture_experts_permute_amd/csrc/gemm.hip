@@ -96,7 +96,7 @@ template <typename T, int BM, int BNB, int WM, int WN, bool SWIGLU>
 __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_kernel(
     const T *__restrict__ A, const T *__restrict__ B1, const T *__restrict__ B3,
     void *__restrict__ C, const int32_t *__restrict__ seg_off,
-    const int32_t *__restrict__ mtile_off, int G, int N, int K) {
+    const int32_t *__restrict__ mtile_off, int G, int N, int K, int act) {
   constexpr int BK = MfmaTraits<T>::BK;
   constexpr int ES = sizeof(T);
   constexpr int CPR = BK * ES / 16;            // 16-byte chunks per tile row (8)
@@ -230,7 +230,7 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_kernel(
         for (int q = 0; q < TN / 2; ++q) {
           const int col = n0 + wn * (TN / 2) * 32 + q * 32 + ccol;
           if (col < N) {
-            const float h = silu(acc[a][2 * q][i]) * acc[a][2 * q + 1][i];
+            const float h = gated(acc[a][2 * q][i], acc[a][2 * q + 1][i], act);
             MfmaTraits<T>::store(reinterpret_cast<T *>(C), orow + col, h);
           }
         }
@@ -282,8 +282,8 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_kernel(
 // columns of two rows per instruction).
 template <int BM, int BNB, bool SWIGLU, int TM, int TN, typename TA>
 __device__ __forceinline__ void dl_epilogue(const TA &ta, f32x16_v (&acc)[TM][TN], uint4 *stage,
-                                            void *__restrict__ C, int N, size_t plane, int wave,
-                                            int lane) {
+                                            void *__restrict__ C, int N, size_t plane, int act,
+                                            int wave, int lane) {
   constexpr int WN = 2;
   const int wm = wave / WN, wn = wave % WN;
   const int row0 = ta.row0, rows = ta.rows, n0 = ta.n0;
@@ -301,7 +301,7 @@ __device__ __forceinline__ void dl_epilogue(const TA &ta, f32x16_v (&acc)[TM][TN
         for (int i = 0; i < 16; ++i) {
           const int r = a * 32 + (i / 4) * 8 + crow4 + (i % 4);
           const int c = q * 32 + ccol;
-          const float h = silu(acc[a][2 * q][i]) * acc[a][2 * q + 1][i];
+          const float h = gated(acc[a][2 * q][i], acc[a][2 * q + 1][i], act);
           *reinterpret_cast<bf16_t *>(reg + r * (WC * 2) + (((c >> 3) ^ (r & 7)) << 4) +
                                       (c & 7) * 2) = f32_to_bf16(h);
         }
@@ -340,7 +340,7 @@ template <int BM, int BNB, bool SWIGLU>
 __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
     const bf16_t *__restrict__ A, const bf16_t *__restrict__ B1, const bf16_t *__restrict__ B3,
     void *__restrict__ C, const int32_t *__restrict__ seg_off,
-    const int32_t *__restrict__ mtile_off, int G, int N, int K, size_t plane) {
+    const int32_t *__restrict__ mtile_off, int G, int N, int K, size_t plane, int act) {
   constexpr int WM = 2, WN = 2;
   constexpr int TM = BM / WM / 32, TN = BNB / WN / 32;
   constexpr int ROWS = BM + BNB;          // tile rows per stage (A then B)
@@ -551,7 +551,7 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
       setup(nt, nxt);
       issue(nxt, st0, 0);
     }
-    dl_epilogue<BM, BNB, SWIGLU>(cur, acc, st1, C, N, plane, wave, lane_t);
+    dl_epilogue<BM, BNB, SWIGLU>(cur, acc, st1, C, N, plane, act, wave, lane_t);
     if (!more) break;
     if constexpr (SWIGLU) RAW_BARRIER();  // every wave has read its staged outputs back
     issue(nxt, st1, 1);
@@ -589,7 +589,7 @@ int resident_wgs(int bm) {
 template <int BM, int BNB, bool SWIGLU>
 hipError_t launch_dl(const void *A, const void *B1, const void *B3, void *C,
                      const int32_t *seg_off, const int32_t *mtile_off, int G, int N, int K,
-                     int max_mtiles, int ksplit, size_t plane, hipStream_t s) {
+                     int max_mtiles, int ksplit, size_t plane, int act, hipStream_t s) {
   const int cols = SWIGLU ? BNB / 2 : BNB;
   // persistent grid: at most what stays resident, a multiple of the XCD count
   const long long upper = (long long)((N + cols - 1) / cols) * max_mtiles + NUM_XCD;
@@ -599,19 +599,19 @@ hipError_t launch_dl(const void *A, const void *B1, const void *B3, void *C,
   dim3 grid((unsigned)gx, ksplit);
   hipLaunchKernelGGL((grouped_gemm_dl_kernel<BM, BNB, SWIGLU>), grid, dim3(GM_THREADS), 0, s,
                      (const bf16_t *)A, (const bf16_t *)B1, (const bf16_t *)B3, C, seg_off,
-                     mtile_off, G, N, K, plane);
+                     mtile_off, G, N, K, plane, act);
   return hipGetLastError();
 }
 
 template <typename T, int BM, int BNB, int WM, int WN, bool SWIGLU>
 hipError_t launch_one(const void *A, const void *B1, const void *B3, void *C,
                       const int32_t *seg_off, const int32_t *mtile_off, int G, int N, int K,
-                      int max_mtiles, hipStream_t s) {
+                      int max_mtiles, int act, hipStream_t s) {
   const int cols = SWIGLU ? BNB / 2 : BNB;
   dim3 grid(((N + cols - 1) / cols) * max_mtiles + NUM_XCD);
   hipLaunchKernelGGL((grouped_gemm_kernel<T, BM, BNB, WM, WN, SWIGLU>), grid, dim3(GM_THREADS),
                      0, s, (const T *)A, (const T *)B1, (const T *)B3, C, seg_off, mtile_off, G,
-                     N, K);
+                     N, K, act);
   return hipGetLastError();
 }
 
@@ -629,22 +629,22 @@ GemmPlan gemm_plan(int dtype, int d, int d_ff, int d_ff_shared, long long rows_p
   return p;
 }
 
-hipError_t launch_gemm_swiglu(int dtype, bool dl, int bm, const void *A, const void *W1,
-                              const void *W3, void *H, const int32_t *seg_off,
+hipError_t launch_gemm_swiglu(int dtype, bool dl, int bm, int act, const void *A,
+                              const void *W1, const void *W3, void *H, const int32_t *seg_off,
                               const int32_t *mtile_off, int G, int N, int K, int max_mtiles,
                               hipStream_t s) {
   if (max_mtiles <= 0) return hipSuccess;
   if (dl && bm == 64)
     return launch_dl<64, 256, true>(A, W1, W3, H, seg_off, mtile_off, G, N, K, max_mtiles, 1, 0,
-                                    s);
+                                    act, s);
   if (dl)
     return launch_dl<256, 256, true>(A, W1, W3, H, seg_off, mtile_off, G, N, K, max_mtiles, 1,
-                                     0, s);
+                                     0, act, s);
   if (dtype == 1)
     return launch_one<bf16_t, 128, 128, 2, 2, true>(A, W1, W3, H, seg_off, mtile_off, G, N, K,
-                                                    max_mtiles, s);
+                                                    max_mtiles, act, s);
   return launch_one<float, 128, 128, 2, 2, true>(A, W1, W3, H, seg_off, mtile_off, G, N, K,
-                                                 max_mtiles, s);
+                                                 max_mtiles, act, s);
 }
 
 hipError_t launch_gemm_down(int dtype, bool dl, int bm, const void *A, const void *W2, float *Y,
@@ -653,15 +653,15 @@ hipError_t launch_gemm_down(int dtype, bool dl, int bm, const void *A, const voi
   if (max_mtiles <= 0) return hipSuccess;
   if (dl && bm == 64)
     return launch_dl<64, 256, false>(A, W2, nullptr, Y, seg_off, mtile_off, G, N, K,
-                                     max_mtiles, ksplit, plane, s);
+                                     max_mtiles, ksplit, plane, 0, s);
   if (dl)
     return launch_dl<256, 256, false>(A, W2, nullptr, Y, seg_off, mtile_off, G, N, K,
-                                      max_mtiles, ksplit, plane, s);
+                                      max_mtiles, ksplit, plane, 0, s);
   if (dtype == 1)
     return launch_one<bf16_t, 128, 128, 2, 2, false>(A, W2, nullptr, Y, seg_off, mtile_off, G,
-                                                     N, K, max_mtiles, s);
+                                                     N, K, max_mtiles, 0, s);
   return launch_one<float, 128, 128, 2, 2, false>(A, W2, nullptr, Y, seg_off, mtile_off, G, N,
-                                                  K, max_mtiles, s);
+                                                  K, max_mtiles, 0, s);
 }
 
 }  // namespace moe

@@ -49,7 +49,7 @@ __global__ __launch_bounds__(SK_THREADS) void skinny_gemm_kernel(
     const bf16_t *__restrict__ A, const int32_t *__restrict__ perm, int kslots,
     const bf16_t *__restrict__ B1, const bf16_t *__restrict__ B3, void *__restrict__ C,
     const int32_t *__restrict__ seg_off, const int32_t *__restrict__ active,
-    const int32_t *__restrict__ nactive, int N, int K) {
+    const int32_t *__restrict__ nactive, int N, int K, int act) {
   constexpr int NW = SWIGLU ? 2 : 1;  // weight matrices per output
   __shared__ float red[SK_WAVES][NW * MB][4][kWave];
 
@@ -127,7 +127,7 @@ __global__ __launch_bounds__(SK_THREADS) void skinny_gemm_kernel(
         }
         const size_t out = (size_t)(s0 + r) * N + n0 + (l & 15);
         if (SWIGLU)
-          reinterpret_cast<bf16_t *>(C)[out] = f32_to_bf16(silu(s[0]) * s[NW - 1]);
+          reinterpret_cast<bf16_t *>(C)[out] = f32_to_bf16(gated(s[0], s[NW - 1], act));
         else
           reinterpret_cast<float *>(C)[out] = s[0];
       }
@@ -137,20 +137,21 @@ __global__ __launch_bounds__(SK_THREADS) void skinny_gemm_kernel(
 }
 
 template <bool SWIGLU>
-hipError_t launch_mb(int mb, const void *A, const int32_t *perm, int kslots, const void *B1,
-                     const void *B3, void *C, const int32_t *seg_off, const int32_t *active,
-                     const int32_t *nactive, int G, int N, int K, hipStream_t s) {
+hipError_t launch_mb(int mb, int act, const void *A, const int32_t *perm, int kslots,
+                     const void *B1, const void *B3, void *C, const int32_t *seg_off,
+                     const int32_t *active, const int32_t *nactive, int G, int N, int K,
+                     hipStream_t s) {
   dim3 grid(G * (N / SK_NB));
   const bf16_t *a = (const bf16_t *)A, *b1 = (const bf16_t *)B1, *b3 = (const bf16_t *)B3;
   if (mb <= 1)
     hipLaunchKernelGGL((skinny_gemm_kernel<SWIGLU, 1>), grid, dim3(SK_THREADS), 0, s, a, perm,
-                       kslots, b1, b3, C, seg_off, active, nactive, N, K);
+                       kslots, b1, b3, C, seg_off, active, nactive, N, K, act);
   else if (mb == 2)
     hipLaunchKernelGGL((skinny_gemm_kernel<SWIGLU, 2>), grid, dim3(SK_THREADS), 0, s, a, perm,
-                       kslots, b1, b3, C, seg_off, active, nactive, N, K);
+                       kslots, b1, b3, C, seg_off, active, nactive, N, K, act);
   else
     hipLaunchKernelGGL((skinny_gemm_kernel<SWIGLU, 4>), grid, dim3(SK_THREADS), 0, s, a, perm,
-                       kslots, b1, b3, C, seg_off, active, nactive, N, K);
+                       kslots, b1, b3, C, seg_off, active, nactive, N, K, act);
   return hipGetLastError();
 }
 
@@ -211,7 +212,7 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_kernel(
     const bf16_t *__restrict__ A, const int32_t *__restrict__ perm, int kslots,
     const bf16_t *__restrict__ B1, const bf16_t *__restrict__ B3, void *__restrict__ C,
     const int32_t *__restrict__ seg_off, const int32_t *__restrict__ active,
-    const int32_t *__restrict__ nactive, int N, int K, int cpw) {
+    const int32_t *__restrict__ nactive, int N, int K, int cpw, int act) {
   constexpr int NW = SWIGLU ? 2 : 1;
   constexpr int CB = gv_cb(NW * KC);
   __shared__ float red[2][GV_WAVES][CB][NW][R];
@@ -295,7 +296,7 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_kernel(
           }
           const size_t out = (size_t)(s0 + rg + r) * N + col_of(g) + cb;
           if (SWIGLU)
-            reinterpret_cast<bf16_t *>(C)[out] = f32_to_bf16(silu(v[0]) * v[NW - 1]);
+            reinterpret_cast<bf16_t *>(C)[out] = f32_to_bf16(gated(v[0], v[NW - 1], act));
           else
             reinterpret_cast<float *>(C)[out] = v[0];
         }
@@ -320,9 +321,10 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_kernel(
 }
 
 template <bool SWIGLU, int R>
-hipError_t launch_gemv_r(const void *A, const int32_t *perm, int kslots, const void *B1,
-                         const void *B3, void *C, const int32_t *seg_off, const int32_t *active,
-                         const int32_t *nactive, int G, int N, int K, hipStream_t s) {
+hipError_t launch_gemv_r(int act, const void *A, const int32_t *perm, int kslots,
+                         const void *B1, const void *B3, void *C, const int32_t *seg_off,
+                         const int32_t *active, const int32_t *nactive, int G, int N, int K,
+                         hipStream_t s) {
   const int kc = K / (GV_WAVES * GV_CHUNK);
   constexpr int NW = SWIGLU ? 2 : 1;
   // columns per workgroup: a power of two from two groups up to 256, with
@@ -337,7 +339,7 @@ hipError_t launch_gemv_r(const void *A, const int32_t *perm, int kslots, const v
     const int cw = cpw < 2 * CB ? 2 * CB : cpw;                                               \
     if (N % cw) return hipErrorInvalidValue;                                                  \
     hipLaunchKernelGGL((gemv_kernel<SWIGLU, R, KC_>), dim3(G * (N / cw)), dim3(GV_THREADS),   \
-                       0, s, a, perm, kslots, b1, b3, C, seg_off, active, nactive, N, K, cw);  \
+                       0, s, a, perm, kslots, b1, b3, C, seg_off, active, nactive, N, K, cw, act); \
     break;                                                                                    \
   }
   switch (kc) {
@@ -349,32 +351,37 @@ hipError_t launch_gemv_r(const void *A, const int32_t *perm, int kslots, const v
 }
 
 template <bool SWIGLU>
-hipError_t launch_gemv(int rows, const void *A, const int32_t *perm, int kslots, const void *B1,
-                       const void *B3, void *C, const int32_t *seg_off, const int32_t *active,
-                       const int32_t *nactive, int G, int N, int K, hipStream_t s) {
+hipError_t launch_gemv(int rows, int act, const void *A, const int32_t *perm, int kslots,
+                       const void *B1, const void *B3, void *C, const int32_t *seg_off,
+                       const int32_t *active, const int32_t *nactive, int G, int N, int K,
+                       hipStream_t s) {
   if (rows <= 1)
-    return launch_gemv_r<SWIGLU, 1>(A, perm, kslots, B1, B3, C, seg_off, active, nactive, G, N, K, s);
+    return launch_gemv_r<SWIGLU, 1>(act, A, perm, kslots, B1, B3, C, seg_off, active, nactive,
+                                    G, N, K, s);
   if (rows <= 2)
-    return launch_gemv_r<SWIGLU, 2>(A, perm, kslots, B1, B3, C, seg_off, active, nactive, G, N, K, s);
-  return launch_gemv_r<SWIGLU, 4>(A, perm, kslots, B1, B3, C, seg_off, active, nactive, G, N, K, s);
+    return launch_gemv_r<SWIGLU, 2>(act, A, perm, kslots, B1, B3, C, seg_off, active, nactive,
+                                    G, N, K, s);
+  return launch_gemv_r<SWIGLU, 4>(act, A, perm, kslots, B1, B3, C, seg_off, active, nactive, G,
+                                  N, K, s);
 }
 
 }  // namespace
 
 bool skinny_ok(int N, int K) { return N % SK_NB == 0 && K % (SK_WAVES * SK_KC) == 0; }
 
-hipError_t launch_skinny_swiglu(int mb, const void *x, const int32_t *perm, int kslots,
+hipError_t launch_skinny_swiglu(int mb, int act, const void *x, const int32_t *perm, int kslots,
                                 const void *W1, const void *W3, void *H,
                                 const int32_t *seg_off, const int32_t *active,
                                 const int32_t *nactive, int G, int N, int K, hipStream_t s) {
-  return launch_mb<true>(mb, x, perm, kslots, W1, W3, H, seg_off, active, nactive, G, N, K, s);
+  return launch_mb<true>(mb, act, x, perm, kslots, W1, W3, H, seg_off, active, nactive, G, N, K,
+                         s);
 }
 
 hipError_t launch_skinny_down(int mb, const void *Hin, const void *W2, float *Y,
                               const int32_t *seg_off, const int32_t *active,
                               const int32_t *nactive, int G, int N, int K, hipStream_t s) {
-  return launch_mb<false>(mb, Hin, nullptr, 1, W2, nullptr, Y, seg_off, active, nactive, G, N,
-                          K, s);
+  return launch_mb<false>(mb, 0, Hin, nullptr, 1, W2, nullptr, Y, seg_off, active, nactive, G,
+                          N, K, s);
 }
 
 bool gemv_ok(int N, int K) {
@@ -382,18 +389,19 @@ bool gemv_ok(int N, int K) {
   return K % (GV_WAVES * GV_CHUNK) == 0 && kc >= 1 && kc <= 8 && N % 64 == 0;
 }
 
-hipError_t launch_gemv_swiglu(int rows, const void *x, const int32_t *perm, int kslots,
+hipError_t launch_gemv_swiglu(int rows, int act, const void *x, const int32_t *perm, int kslots,
                               const void *W1, const void *W3, void *H, const int32_t *seg_off,
                               const int32_t *active, const int32_t *nactive, int G, int N, int K,
                               hipStream_t s) {
-  return launch_gemv<true>(rows, x, perm, kslots, W1, W3, H, seg_off, active, nactive, G, N, K, s);
+  return launch_gemv<true>(rows, act, x, perm, kslots, W1, W3, H, seg_off, active, nactive, G, N,
+                           K, s);
 }
 
 hipError_t launch_gemv_down(int rows, const void *Hin, const void *W2, float *Y,
                             const int32_t *seg_off, const int32_t *active,
                             const int32_t *nactive, int G, int N, int K, hipStream_t s) {
-  return launch_gemv<false>(rows, Hin, nullptr, 1, W2, nullptr, Y, seg_off, active, nactive, G,
-                            N, K, s);
+  return launch_gemv<false>(rows, 0, Hin, nullptr, 1, W2, nullptr, Y, seg_off, active, nactive,
+                            G, N, K, s);
 }
 
 }  // namespace moe

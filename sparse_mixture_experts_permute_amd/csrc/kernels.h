@@ -6,17 +6,22 @@
 namespace moe {
 
 size_t router_partial_bytes(int T, int d, int E, int esize);
+// gate_mode: 0 softmax over the selected logits, 1 softmax over all E (no
+// renormalisation), 2 sigmoid of each selected logit
 hipError_t launch_router(int dtype, const void *x, const void *Wg, const float *bias, int T,
-                         int d, int E, int k, int32_t *idx, float *gate, float *logits,
-                         float *part, hipStream_t s);
+                         int d, int E, int k, int gate_mode, int32_t *idx, float *gate,
+                         float *logits, float *part, hipStream_t s);
 
 int permute_nblocks(int P);
-hipError_t launch_permute(const int32_t *idx, int T, int E, int k, int bm0, int bm1,
-                          int32_t *blk, int32_t *counts, int32_t *offsets, int32_t *perm,
-                          int32_t *inv, int32_t *mtiles0, int32_t *mtiles1,
+// capacity: pairs an expert keeps (its first ones in pair order); >= T*k keeps
+// all.  Dropped pairs (and ids outside [0, E)) get inv = -1.
+hipError_t launch_permute(const int32_t *idx, int T, int E, int k, int capacity, int bm0,
+                          int bm1, int32_t *blk, int32_t *counts, int32_t *offsets,
+                          int32_t *perm, int32_t *inv, int32_t *mtiles0, int32_t *mtiles1,
                           int32_t *shared_seg, int32_t *active, hipStream_t s);
-hipError_t launch_gather(const void *x, const int32_t *perm, int P, int k, int d, int esize,
-                         void *xp, hipStream_t s);
+// xp[s] = x[perm[s] / k] for s < *placed (<= P, read on the device)
+hipError_t launch_gather(const void *x, const int32_t *perm, const int32_t *placed, int P, int k,
+                         int d, int esize, void *xp, hipStream_t s);
 
 // Which grouped-GEMM kernel serves each projection, and its m-tile height.
 struct GemmPlan {
@@ -24,8 +29,9 @@ struct GemmPlan {
   int bm1, bm2;   // rows per m-tile of the SwiGLU / down GEMM
 };
 GemmPlan gemm_plan(int dtype, int d, int d_ff, int d_ff_shared, long long rows_per_expert);
-hipError_t launch_gemm_swiglu(int dtype, bool dl, int bm, const void *A, const void *W1,
-                              const void *W3, void *H, const int32_t *seg_off,
+// act: 0 SiLU(W1 a) * (W3 a), 1 sigmoid(W1 a) * (W3 a)
+hipError_t launch_gemm_swiglu(int dtype, bool dl, int bm, int act, const void *A,
+                              const void *W1, const void *W3, void *H, const int32_t *seg_off,
                               const int32_t *mtile_off, int G, int N, int K, int max_mtiles,
                               hipStream_t s);
 // ksplit > 1 (direct-to-LDS kernel only): K is split in ksplit equal ranges
@@ -38,14 +44,14 @@ hipError_t launch_gemm_down(int dtype, bool dl, int bm, const void *A, const voi
 bool skinny_ok(int N, int K);
 // vector-ALU weight streaming for experts holding at most `rows` (<= 4) rows
 bool gemv_ok(int N, int K);
-hipError_t launch_gemv_swiglu(int rows, const void *x, const int32_t *perm, int kslots,
+hipError_t launch_gemv_swiglu(int rows, int act, const void *x, const int32_t *perm, int kslots,
                               const void *W1, const void *W3, void *H, const int32_t *seg_off,
                               const int32_t *active, const int32_t *nactive, int G, int N, int K,
                               hipStream_t s);
 hipError_t launch_gemv_down(int rows, const void *Hin, const void *W2, float *Y,
                             const int32_t *seg_off, const int32_t *active,
                             const int32_t *nactive, int G, int N, int K, hipStream_t s);
-hipError_t launch_skinny_swiglu(int mb, const void *x, const int32_t *perm, int kslots,
+hipError_t launch_skinny_swiglu(int mb, int act, const void *x, const int32_t *perm, int kslots,
                                 const void *W1, const void *W3, void *H,
                                 const int32_t *seg_off, const int32_t *active,
                                 const int32_t *nactive, int G, int N, int K, hipStream_t s);
@@ -53,7 +59,8 @@ hipError_t launch_skinny_down(int mb, const void *Hin, const void *W2, float *Y,
                               const int32_t *seg_off, const int32_t *active,
                               const int32_t *nactive, int G, int N, int K, hipStream_t s);
 
-// Yp holds nsplit planes of `plane` floats each (summed in order).
+// Yp holds nsplit planes of `plane` floats each (summed in order); a pair
+// with inv < 0 (dropped by a capacity limit) contributes nothing.
 hipError_t launch_combine(int dtype, const float *Yp, int nsplit, size_t plane, const float *Ys,
                           const int32_t *inv, const float *gate, int T, int k, int d, void *y,
                           hipStream_t s);

@@ -9,10 +9,16 @@
 // which atomics land.
 //
 //   hist    : block b counts the experts of pairs [256b, 256b+256) -> blk[b][e]
-//   scan    : one block turns blk[][] into per-block bases, counts, offsets and
-//             the m-tile prefix used by the grouped GEMM tile maps
-//   scatter : block b re-reads its pairs; a pair's slot is
-//             base[b][e] + (pairs of e in earlier waves of b) + (rank in wave)
+//   scan    : one block turns blk[][] into per-block rank bases, counts,
+//             offsets and the m-tile prefix used by the grouped GEMM tile maps
+//   scatter : block b re-reads its pairs; a pair's rank among its expert's
+//             pairs is base[b][e] + (pairs of e in earlier waves of b) + (rank
+//             in wave), and its slot is offsets[e] + rank
+//
+// Under a capacity limit ("Mistral 8x7B SMoE architecture deep dive", section
+// 2.4) an expert keeps the pairs of rank < capacity (its first ones in pair
+// order); counts, offsets and the tile prefixes cover the kept pairs, and a
+// dropped pair gets inv = -1.
 #include "common.h"
 #include "kernels.h"
 
@@ -40,15 +46,16 @@ __global__ __launch_bounds__(PM_CHUNK) void permute_hist_kernel(const int32_t *_
 
 // One block of 256 threads; thread e owns expert e.
 __global__ __launch_bounds__(256) void permute_scan_kernel(
-    int32_t *__restrict__ blk, int nb, int E, int P, int T, int bm0, int bm1,
+    int32_t *__restrict__ blk, int nb, int E, int P, int T, int capacity, int bm0, int bm1,
     int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int32_t *__restrict__ mtiles0,
     int32_t *__restrict__ mtiles1, int32_t *__restrict__ shared_seg,
     int32_t *__restrict__ active) {
   __shared__ int s0[256], s1[256], s2[256], s3[256];
   const int e = threadIdx.x;
-  int total = 0;
+  int raw = 0;
   if (e < E)
-    for (int b = 0; b < nb; ++b) total += blk[(size_t)b * E + e];
+    for (int b = 0; b < nb; ++b) raw += blk[(size_t)b * E + e];
+  const int total = min(raw, capacity);  // pairs the expert keeps
   s0[e] = e < E ? total : 0;
   s1[e] = e < E ? (total + bm0 - 1) / bm0 : 0;
   s2[e] = e < E ? (total + bm1 - 1) / bm1 : 0;
@@ -76,7 +83,7 @@ __global__ __launch_bounds__(256) void permute_scan_kernel(
     offsets[e] = excl;
     mtiles0[e] = s1[e] - (total + bm0 - 1) / bm0;
     mtiles1[e] = s2[e] - (total + bm1 - 1) / bm1;
-    int run = excl;
+    int run = 0;  // rank of the block's first pair among the expert's pairs
     for (int b = 0; b < nb; ++b) {
       int c = blk[(size_t)b * E + e];
       blk[(size_t)b * E + e] = run;
@@ -84,7 +91,7 @@ __global__ __launch_bounds__(256) void permute_scan_kernel(
     }
   }
   if (e == 0) {
-    offsets[E] = s0[255];  // == P when every id is in range
+    offsets[E] = s0[255];  // kept pairs (== P when nothing is dropped)
     mtiles0[E] = s1[255];
     mtiles1[E] = s2[255];
     // the shared expert is one segment of all T tokens
@@ -100,8 +107,8 @@ __global__ __launch_bounds__(256) void permute_scan_kernel(
 }
 
 __global__ __launch_bounds__(PM_CHUNK) void permute_scatter_kernel(
-    const int32_t *__restrict__ idx, int P, int E, const int32_t *__restrict__ base,
-    int32_t *__restrict__ perm, int32_t *__restrict__ inv) {
+    const int32_t *__restrict__ idx, int P, int E, int capacity, const int32_t *__restrict__ base,
+    const int32_t *__restrict__ offsets, int32_t *__restrict__ perm, int32_t *__restrict__ inv) {
   __shared__ int wc[PM_CHUNK / kWave][256];
   const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
   for (int i = tid; i < (PM_CHUNK / kWave) * 256; i += PM_CHUNK) (&wc[0][0])[i] = 0;
@@ -122,10 +129,17 @@ __global__ __launch_bounds__(PM_CHUNK) void permute_scatter_kernel(
   if (valid && rank == 0) wc[w][e] = __popcll(same);
   __syncthreads();
   if (valid) {
-    int pos = base[(size_t)blockIdx.x * E + e] + rank;
-    for (int w2 = 0; w2 < w; ++w2) pos += wc[w2][e];
-    perm[pos] = p;
-    inv[p] = pos;
+    int r = base[(size_t)blockIdx.x * E + e] + rank;
+    for (int w2 = 0; w2 < w; ++w2) r += wc[w2][e];
+    if (r < capacity) {
+      const int pos = offsets[e] + r;
+      perm[pos] = p;
+      inv[p] = pos;
+    } else {
+      inv[p] = -1;
+    }
+  } else if (p < P) {
+    inv[p] = -1;
   }
 }
 
@@ -138,11 +152,13 @@ constexpr int PS_THREADS = 1024;
 constexpr int PS_WAVES = PS_THREADS / kWave;
 
 __global__ __launch_bounds__(PS_THREADS) void permute_small_kernel(
-    const int32_t *__restrict__ idx, int P, int E, int T, int bm0, int bm1,
+    const int32_t *__restrict__ idx, int P, int E, int T, int capacity, int bm0, int bm1,
     int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int32_t *__restrict__ perm,
     int32_t *__restrict__ inv, int32_t *__restrict__ mtiles0, int32_t *__restrict__ mtiles1,
     int32_t *__restrict__ shared_seg, int32_t *__restrict__ active) {
-  __shared__ int hist[256], cursor[256], s1[256], s2[256], s3[256];
+  // hist: pairs per expert; koff: kept-pair offsets (scanned in place);
+  // rk: rank of the next pair of each expert
+  __shared__ int hist[256], koff[256], rk[256], s1[256], s2[256], s3[256];
   __shared__ int wc[PS_WAVES][256];
   const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
   if (tid < 256) hist[tid] = 0;
@@ -153,8 +169,9 @@ __global__ __launch_bounds__(PS_THREADS) void permute_small_kernel(
   }
   __syncthreads();
   if (tid < 256) {
-    const int c = tid < E ? hist[tid] : 0;
-    cursor[tid] = c;
+    const int c = tid < E ? min(hist[tid], capacity) : 0;  // kept pairs
+    koff[tid] = c;
+    rk[tid] = 0;
     s1[tid] = tid < E ? (c + bm0 - 1) / bm0 : 0;
     s2[tid] = tid < E ? (c + bm1 - 1) / bm1 : 0;
     s3[tid] = (tid < E && c > 0) ? 1 : 0;
@@ -163,14 +180,14 @@ __global__ __launch_bounds__(PS_THREADS) void permute_small_kernel(
   for (int off = 1; off < 256; off <<= 1) {  // inclusive scans over the experts
     int a0 = 0, a1 = 0, a2 = 0, a3 = 0;
     if (tid < 256 && tid >= off) {
-      a0 = cursor[tid - off];
+      a0 = koff[tid - off];
       a1 = s1[tid - off];
       a2 = s2[tid - off];
       a3 = s3[tid - off];
     }
     __syncthreads();
     if (tid < 256) {
-      cursor[tid] += a0;
+      koff[tid] += a0;
       s1[tid] += a1;
       s2[tid] += a2;
       s3[tid] += a3;
@@ -178,16 +195,15 @@ __global__ __launch_bounds__(PS_THREADS) void permute_small_kernel(
     __syncthreads();
   }
   if (tid < E) {
-    const int c = hist[tid];
-    const int excl = cursor[tid] - c;
+    const int c = min(hist[tid], capacity);
     counts[tid] = c;
-    offsets[tid] = excl;
+    offsets[tid] = koff[tid] - c;
     mtiles0[tid] = s1[tid] - (c + bm0 - 1) / bm0;
     mtiles1[tid] = s2[tid] - (c + bm1 - 1) / bm1;
     if (c > 0) active[s3[tid] - 1] = tid;
   }
   if (tid == 0) {
-    offsets[E] = cursor[255];  // inclusive scan: the number of placed pairs
+    offsets[E] = koff[255];  // inclusive scan: the number of kept pairs
     mtiles0[E] = s1[255];
     mtiles1[E] = s2[255];
     active[E] = s3[255];
@@ -201,7 +217,7 @@ __global__ __launch_bounds__(PS_THREADS) void permute_small_kernel(
     shared_seg[7] = 1;
   }
   __syncthreads();
-  if (tid < 256) cursor[tid] -= (tid < E ? hist[tid] : 0);  // exclusive start of each expert
+  if (tid < 256) koff[tid] -= (tid < E ? min(hist[tid], capacity) : 0);  // exclusive
   __syncthreads();
   for (int c0 = 0; c0 < P; c0 += PS_THREADS) {
     for (int i = tid; i < PS_WAVES * 256; i += PS_THREADS) (&wc[0][0])[i] = 0;
@@ -221,27 +237,38 @@ __global__ __launch_bounds__(PS_THREADS) void permute_small_kernel(
     if (valid && rank == 0) wc[w][e] = __popcll(same);
     __syncthreads();
     if (valid) {
-      int pos = cursor[e] + rank;
-      for (int w2 = 0; w2 < w; ++w2) pos += wc[w2][e];
-      perm[pos] = p;
-      inv[p] = pos;
+      int r = rk[e] + rank;
+      for (int w2 = 0; w2 < w; ++w2) r += wc[w2][e];
+      if (r < capacity) {
+        const int pos = koff[e] + r;
+        perm[pos] = p;
+        inv[p] = pos;
+      } else {
+        inv[p] = -1;
+      }
+    } else if (p < P) {
+      inv[p] = -1;
     }
     __syncthreads();
     if (tid < E) {
       int add = 0;
       for (int w2 = 0; w2 < PS_WAVES; ++w2) add += wc[w2][tid];
-      cursor[tid] += add;
+      rk[tid] += add;
     }
     __syncthreads();
   }
 }
 
 // Xp[s][:] = x[perm[s] / k][:]; one block copies 4 rows with 16-byte accesses.
+// Rows of the placed pairs only: *placed (offsets[E]) is below P when a
+// capacity limit dropped pairs.
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint4 *__restrict__ x,
                                                           const int32_t *__restrict__ perm,
-                                                          int P, int k, int rowq,
+                                                          const int32_t *__restrict__ placed,
+                                                          int k, int rowq,
                                                           uint4 *__restrict__ xp) {
   const int r0 = blockIdx.x * 4;
+  const int P = *placed;
   for (int r = r0; r < r0 + 4 && r < P; ++r) {
     const size_t src = (size_t)(perm[r] / k) * rowq;
     const size_t dst = (size_t)r * rowq;
@@ -253,30 +280,32 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint4 *__restric
 
 int permute_nblocks(int P) { return (P + PM_CHUNK - 1) / PM_CHUNK; }
 
-hipError_t launch_permute(const int32_t *idx, int T, int E, int k, int bm0, int bm1,
-                          int32_t *blk, int32_t *counts, int32_t *offsets, int32_t *perm,
-                          int32_t *inv, int32_t *mtiles0, int32_t *mtiles1,
+hipError_t launch_permute(const int32_t *idx, int T, int E, int k, int capacity, int bm0,
+                          int bm1, int32_t *blk, int32_t *counts, int32_t *offsets,
+                          int32_t *perm, int32_t *inv, int32_t *mtiles0, int32_t *mtiles1,
                           int32_t *shared_seg, int32_t *active, hipStream_t s) {
   const int P = T * k;
+  const int cap = capacity < 0 || capacity > P ? P : capacity;
   if (P <= 8 * PS_THREADS) {
-    hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(PS_THREADS), 0, s, idx, P, E, T, bm0,
-                       bm1, counts, offsets, perm, inv, mtiles0, mtiles1, shared_seg, active);
+    hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(PS_THREADS), 0, s, idx, P, E, T, cap,
+                       bm0, bm1, counts, offsets, perm, inv, mtiles0, mtiles1, shared_seg,
+                       active);
     return hipGetLastError();
   }
   const int nb = permute_nblocks(P);
   hipLaunchKernelGGL(permute_hist_kernel, dim3(nb), dim3(PM_CHUNK), 0, s, idx, P, E, blk);
-  hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(256), 0, s, blk, nb, E, P, T, bm0, bm1,
-                     counts, offsets, mtiles0, mtiles1, shared_seg, active);
-  hipLaunchKernelGGL(permute_scatter_kernel, dim3(nb), dim3(PM_CHUNK), 0, s, idx, P, E, blk,
-                     perm, inv);
+  hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(256), 0, s, blk, nb, E, P, T, cap, bm0,
+                     bm1, counts, offsets, mtiles0, mtiles1, shared_seg, active);
+  hipLaunchKernelGGL(permute_scatter_kernel, dim3(nb), dim3(PM_CHUNK), 0, s, idx, P, E, cap, blk,
+                     offsets, perm, inv);
   return hipGetLastError();
 }
 
-hipError_t launch_gather(const void *x, const int32_t *perm, int P, int k, int d, int esize,
-                         void *xp, hipStream_t s) {
+hipError_t launch_gather(const void *x, const int32_t *perm, const int32_t *placed, int P, int k,
+                         int d, int esize, void *xp, hipStream_t s) {
   const int rowq = d * esize / 16;
   hipLaunchKernelGGL(gather_rows_kernel, dim3((P + 3) / 4), dim3(256), 0, s,
-                     (const uint4 *)x, perm, P, k, rowq, (uint4 *)xp);
+                     (const uint4 *)x, perm, placed, k, rowq, (uint4 *)xp);
   return hipGetLastError();
 }
 

@@ -187,7 +187,8 @@ __global__ __launch_bounds__(256) void router_scores_narrow_kernel(
 // One wavefront per token: scores, k rounds of arg-max, softmax over the selected.
 __global__ __launch_bounds__(256) void router_topk_kernel(
     const float *__restrict__ part, int S, const float *__restrict__ bias, int T_, int E, int k,
-    int32_t *__restrict__ idx, float *__restrict__ gate, float *__restrict__ logits) {
+    int gate_mode, int32_t *__restrict__ idx, float *__restrict__ gate,
+    float *__restrict__ logits) {
   __shared__ float selv[4][256];
   __shared__ int seli[4][256];
   const int w = threadIdx.x / kWave, lane = lane_id();
@@ -237,14 +238,24 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  const float m = selv[w][0];
+  const float m = selv[w][0];  // the largest logit of the token
   float z = 0.f;
-  for (int r = lane; r < k; r += kWave) z += expf(selv[w][r] - m);
+  if (gate_mode == 0) {
+    // softmax over the k selected logits
+    for (int r = lane; r < k; r += kWave) z += expf(selv[w][r] - m);
+  } else if (gate_mode == 1) {
+    // softmax over all E logits (v[] holds -inf past E)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) z += expf(v[j] - m);
+  }
 #pragma unroll
   for (int off = kWave / 2; off > 0; off >>= 1) z += __shfl_xor(z, off);
   for (int r = lane; r < k; r += kWave) {
     idx[(size_t)t * k + r] = seli[w][r];
-    gate[(size_t)t * k + r] = expf(selv[w][r] - m) / z;
+    const float l = selv[w][r];
+    // gate_mode 2: logistic sigmoid of the selected logit on its own
+    gate[(size_t)t * k + r] =
+        gate_mode == 2 ? 1.0f / (1.0f + expf(-l)) : expf(l - m) / z;
   }
 }
 
@@ -306,8 +317,8 @@ size_t router_partial_bytes(int T, int d, int E, int esize) {
 }
 
 hipError_t launch_router(int dtype, const void *x, const void *Wg, const float *bias, int T,
-                         int d, int E, int k, int32_t *idx, float *gate, float *logits,
-                         float *part, hipStream_t s) {
+                         int d, int E, int k, int gate_mode, int32_t *idx, float *gate,
+                         float *logits, float *part, hipStream_t s) {
   const int es = dtype == 1 ? 2 : 4;
   const RouterSplit r = router_split(T, d, E, es);
   if (dtype == 1)
@@ -315,7 +326,7 @@ hipError_t launch_router(int dtype, const void *x, const void *Wg, const float *
   else
     launch_scores<float>(r, x, Wg, T, d, E, part, s);
   hipLaunchKernelGGL(router_topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, part, r.S, bias, T,
-                     E, k, idx, gate, logits);
+                     E, k, gate_mode, idx, gate, logits);
   return hipGetLastError();
 }
 

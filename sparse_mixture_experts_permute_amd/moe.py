@@ -17,11 +17,18 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
 
 MOE_F32, MOE_BF16 = 0, 1
+GATE_SOFTMAX_TOPK, GATE_SOFTMAX_ALL, GATE_SIGMOID = 0, 1, 2
+ACT_SWIGLU, ACT_GLU_SIGMOID = 0, 1
 NSTAGE_EVENTS = 8
 STAGES = ("router", "permute", "gather", "gemm_swiglu", "gemm_down", "shared_expert", "combine")
 WS_FIELDS = ("logits", "idx", "gate", "counts", "offsets", "perm", "inv")
 
 _lib = None
+
+
+class _Options(ctypes.Structure):
+    _fields_ = [("gate_mode", ctypes.c_int), ("activation", ctypes.c_int),
+                ("capacity", ctypes.c_int)]
 
 
 class MoEError(RuntimeError):
@@ -56,6 +63,15 @@ def lib():
         L.moe_forward_timed.restype = i
         L.moe_strerror.argtypes = [i]
         L.moe_strerror.restype = ctypes.c_char_p
+        L.moe_capacity.argtypes = [i, i, ctypes.c_double]
+        L.moe_capacity.restype = i
+        L.moe_route_ex.argtypes = [vp, vp, vp, i, i, i, i, i, i, vp, vp, vp, vp, sz, vp]
+        L.moe_route_ex.restype = i
+        L.moe_permute_ex.argtypes = [vp, i, i, i, i, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_permute_ex.restype = i
+        L.moe_forward_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i,
+                                     ctypes.POINTER(_Options), vp, sz, vp, vp]
+        L.moe_forward_ex.restype = i
         _lib = L
     return _lib
 
@@ -103,7 +119,16 @@ def tensor_to_numpy(t: torch.Tensor) -> np.ndarray:
     return t.numpy()
 
 
-def route(x: torch.Tensor, Wg: torch.Tensor, k: int, bias: torch.Tensor | None = None):
+def capacity(T: int, k: int, capacity_factor: float = 1.2) -> int:
+    """Per-expert capacity min(k*T, floor(cf*T)) for a batch of T tokens."""
+    c = lib().moe_capacity(T, k, float(capacity_factor))
+    if c < 0:
+        raise MoEError("invalid capacity arguments")
+    return c
+
+
+def route(x: torch.Tensor, Wg: torch.Tensor, k: int, bias: torch.Tensor | None = None,
+          gate_mode: int = GATE_SOFTMAX_TOPK):
     """(idx [T][k] int32, gate [T][k] fp32, logits [T][E] fp32)."""
     T, d = x.shape
     E = Wg.shape[0]
@@ -112,13 +137,16 @@ def route(x: torch.Tensor, Wg: torch.Tensor, k: int, bias: torch.Tensor | None =
     logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
     nbytes = lib().moe_route_workspace_bytes(T, d, E, _dt(x))
     ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=x.device)
-    _check(lib().moe_route(_p(x), _p(Wg), _p(bias), T, d, E, k, _dt(x), _p(idx), _p(gate),
-                           _p(logits), _p(ws), nbytes, _stream()), "moe_route")
+    _check(lib().moe_route_ex(_p(x), _p(Wg), _p(bias), T, d, E, k, _dt(x), int(gate_mode),
+                              _p(idx), _p(gate), _p(logits), _p(ws), nbytes, _stream()),
+           "moe_route_ex")
     return idx, gate, logits
 
 
-def permute(idx: torch.Tensor, E: int):
-    """(counts [E], offsets [E+1], perm [T*k], inv [T*k]), all int32."""
+def permute(idx: torch.Tensor, E: int, capacity: int = -1):
+    """(counts [E], offsets [E+1], perm [T*k], inv [T*k]), all int32.  Under a
+    capacity only kept pairs are placed (perm has offsets[E] valid entries)
+    and inv is -1 for a dropped pair."""
     T, k = idx.shape
     dev = idx.device
     counts = torch.empty(E, dtype=torch.int32, device=dev)
@@ -127,8 +155,8 @@ def permute(idx: torch.Tensor, E: int):
     inv = torch.empty(T * k, dtype=torch.int32, device=dev)
     nbytes = lib().moe_permute_workspace_bytes(T, E, k)
     ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
-    _check(lib().moe_permute(_p(idx), T, E, k, _p(counts), _p(offsets), _p(perm), _p(inv),
-                             _p(ws), nbytes, _stream()), "moe_permute")
+    _check(lib().moe_permute_ex(_p(idx), T, E, k, int(capacity), _p(counts), _p(offsets),
+                                _p(perm), _p(inv), _p(ws), nbytes, _stream()), "moe_permute_ex")
     return counts, offsets, perm, inv
 
 
@@ -150,11 +178,17 @@ class MoELayer:
     """One layer's weights plus a reusable workspace.
 
     W1, W3 [E][d_ff][d]; W2 [E][d][d_ff]; Wg [E][d]; optional bias [E] fp32;
-    optional shared (Ws1 [dffs][d], Ws3 [dffs][d], Ws2 [d][dffs]).
+    optional shared (Ws1 [dffs][d], Ws3 [dffs][d], Ws2 [d][dffs]).  The
+    variants (gate_mode, activation, capacity) follow moe_options in the C
+    header; the defaults are the method itself.
     """
 
-    def __init__(self, Wg, W1, W3, W2, k, bias=None, shared=None):
+    def __init__(self, Wg, W1, W3, W2, k, bias=None, shared=None,
+                 gate_mode=GATE_SOFTMAX_TOPK, activation=ACT_SWIGLU, capacity=-1):
         self.Wg, self.W1, self.W3, self.W2, self.k, self.bias = Wg, W1, W3, W2, k, bias
+        self.options = _Options(int(gate_mode), int(activation), int(capacity))
+        self._default = (gate_mode == GATE_SOFTMAX_TOPK and activation == ACT_SWIGLU
+                         and capacity < 0)
         self.E, self.d_ff, self.d = W1.shape
         self.shared = shared
         self.d_ff_shared = shared[0].shape[0] if shared is not None else 0
@@ -176,15 +210,25 @@ class MoELayer:
             y = torch.empty_like(x2)
         ws, n = self.workspace(T)
         Ws1, Ws3, Ws2 = self.shared if self.shared is not None else (None, None, None)
-        _check(lib().moe_forward(_p(x2), _p(self.Wg), _p(self.bias), _p(self.W1), _p(self.W3),
-                                 _p(self.W2), _p(Ws1), _p(Ws3), _p(Ws2), self.d_ff_shared, T,
-                                 self.E, self.k, self.d, self.d_ff, self.dtype, _p(ws), n, _p(y),
-                                 _stream()), "moe_forward")
+        if self._default:
+            _check(lib().moe_forward(_p(x2), _p(self.Wg), _p(self.bias), _p(self.W1),
+                                     _p(self.W3), _p(self.W2), _p(Ws1), _p(Ws3), _p(Ws2),
+                                     self.d_ff_shared, T, self.E, self.k, self.d, self.d_ff,
+                                     self.dtype, _p(ws), n, _p(y), _stream()), "moe_forward")
+        else:
+            _check(lib().moe_forward_ex(_p(x2), _p(self.Wg), _p(self.bias), _p(self.W1),
+                                        _p(self.W3), _p(self.W2), _p(Ws1), _p(Ws3), _p(Ws2),
+                                        self.d_ff_shared, T, self.E, self.k, self.d, self.d_ff,
+                                        self.dtype, ctypes.byref(self.options), _p(ws), n, _p(y),
+                                        _stream()), "moe_forward_ex")
         return y.reshape(shape)
 
     def timed(self, x: torch.Tensor, y: torch.Tensor, events) -> torch.Tensor:
         """Same as a call, recording `events` (NSTAGE_EVENTS torch.cuda.Event,
-        already created by a record) at the stage boundaries on the stream."""
+        already created by a record) at the stage boundaries on the stream
+        (the method's defaults only)."""
+        if not self._default:
+            raise MoEError("stage timing covers the default variant only")
         T = x.shape[0]
         ws, n = self.workspace(T)
         Ws1, Ws3, Ws2 = self.shared if self.shared is not None else (None, None, None)
@@ -216,6 +260,7 @@ class MoELayer:
                     perm=view("perm", P, torch.int32), inv=view("inv", P, torch.int32))
 
 
-def forward(x, Wg, W1, W3, W2, k, bias=None, shared=None):
-    """y = MoE(x) for x [..., d] (allocates its workspace)."""
-    return MoELayer(Wg, W1, W3, W2, k, bias, shared)(x)
+def forward(x, Wg, W1, W3, W2, k, bias=None, shared=None, **variants):
+    """y = MoE(x) for x [..., d] (allocates its workspace); `variants` are
+    MoELayer's gate_mode / activation / capacity."""
+    return MoELayer(Wg, W1, W3, W2, k, bias, shared, **variants)(x)

@@ -106,3 +106,32 @@ def test_argument_errors_before_launch(L):
     assert L.moe_forward(*args) == -1
     # permute: too-small workspace
     assert L.moe_permute(fake, 4, 8, 2, fake, fake, fake, fake, vp(0x100000), 8, None) == -3
+
+
+def test_variant_entry_points_check_arguments(L):
+    from sparse_mixture_experts_permute_amd import moe
+    vp = ctypes.c_void_p
+    fake = vp(0x1000)
+    big = 1 << 30
+    # capacity of "Mistral 8x7B SMoE architecture deep dive", section 2.4:
+    # min(k*T, floor(1.2*T)) -> 38 for a batch of 32 (k=2), 19 for 16
+    assert moe.capacity(32, 2, 1.2) == 38
+    assert moe.capacity(16, 2, 1.2) == 19
+    assert moe.capacity(10, 1, 5.0) == 10   # never above k*T
+    assert moe.capacity(0, 2, 1.2) == 0
+    assert L.moe_capacity(-1, 2, 1.2) == -1
+    assert L.moe_capacity(4, 0, 1.2) == -1
+    assert L.moe_capacity(4, 2, -0.5) == -1
+    # unknown gate mode
+    for mode in (-1, 3):
+        assert L.moe_route_ex(fake, fake, None, 4, 64, 8, 2, 1, mode, fake, fake, None, fake, big,
+                              None) == -1
+    # unknown gate mode / activation in the forward options
+    for gm, act in ((3, 0), (0, 2), (-1, 0)):
+        opt = moe._Options(gm, act, -1)
+        args = [fake, fake, None, fake, fake, fake, None, None, None, 0, 4, 8, 2, 64, 64, 1,
+                ctypes.byref(opt), vp(0x100000), 1 << 40, vp(0x2000), None]
+        assert L.moe_forward_ex(*args) == -1
+    # permute_ex: too-small workspace is still caught
+    assert L.moe_permute_ex(fake, 4, 8, 2, 3, fake, fake, fake, fake, vp(0x100000), 8,
+                            None) == -3

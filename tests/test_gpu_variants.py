@@ -1,0 +1,130 @@
+"""Parity of the variants beside the method (gate modes, the sigmoid-gated
+expert, the expert capacity limit) with the CPU oracle, on an MI355X.
+
+Same bars as the method's own parity tests: routing indices, counts, offsets,
+the permutation and the dropped pairs bit-exact against the oracle run on the
+GPU's router scores; gates within 1e-6; y within 1e-4 (fp32) or 1e-2 (bf16)
+relative L2.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from sparse_mixture_experts_permute_amd import moe
+from sparse_mixture_experts_permute_amd.inputs import LayerConfig, bf16_bits_to_f32, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 1e-2}
+
+
+def say(msg):
+    print(f"\n[gpu-variants] {msg}", flush=True)
+
+
+def f64(a):
+    return (bf16_bits_to_f32(a) if a.dtype == np.uint16 else a).astype(np.float64)
+
+
+def rel_l2(got, ref):
+    return float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+
+
+def inputs(T, d, E, dff, k, dtype, dffs=0, seed=7, skew=0.0):
+    cfg = LayerConfig("variant", T, d, E, dff, k, dtype, d_ff_shared=dffs, skew=skew, seed=seed)
+    h = make_inputs(cfg)
+    dev = {n: moe.tensor_from_numpy(a) for n, a in h.items() if a is not None}
+    dev["bias"] = torch.from_numpy(h["bias"]).cuda() if h["bias"] is not None else None
+    return cfg, h, dev
+
+
+# (label, T, d, E, d_ff, k, dtype, d_ff_shared, skew, gate_mode, activation, capacity)
+CASES = [
+    ("softmax_all_bf16", 300, 256, 8, 512, 2, "bf16", 0, 0.0, 1, 0, None),
+    ("sigmoid_gate_glu_f32", 200, 128, 6, 256, 2, "f32", 0, 0.0, 2, 1, None),
+    ("numpy_function_E32_bf16", 512, 512, 32, 1024, 2, "bf16", 0, 0.0, 2, 1, None),
+    ("glu_shared_bf16", 96, 256, 8, 256, 2, "bf16", 256, 0.0, 0, 1, None),
+    ("capacity_20_bf16", 300, 256, 8, 512, 2, "bf16", 0, 1.5, 0, 0, 20),
+    ("capacity_1_f32", 64, 128, 4, 128, 3, "f32", 0, 0.0, 0, 0, 1),
+    ("capacity_0_shared_bf16", 40, 256, 8, 256, 2, "bf16", 256, 0.0, 0, 0, 0),
+    ("capacity_multiblock_bf16", 5000, 128, 16, 128, 2, "bf16", 0, 2.0, 0, 0, 300),
+    ("capacity_decode_T3_bf16", 3, 2048, 8, 2048, 2, "bf16", 0, 0.0, 1, 1, 1),
+    ("capacity_page_cf_bf16", 512, 256, 8, 256, 2, "bf16", 0, 3.0, 0, 0, "page"),
+    ("capacity_cf_0.3_bf16", 512, 256, 8, 256, 2, "bf16", 0, 3.0, 2, 0, 0.3),
+]
+
+
+@pytest.mark.parametrize("c", CASES, ids=[c[0] for c in CASES])
+def test_variant_forward(c):
+    label, T, d, E, dff, k, dtype, dffs, skew, gm, act, cap = c
+    cfg, h, dev = inputs(T, d, E, dff, k, dtype, dffs, skew=skew)
+    if cap == "page":
+        cap = moe.capacity(T, k, 1.2)        # min(k*T, floor(1.2*T))
+    elif isinstance(cap, float):
+        cap = moe.capacity(T, k, cap)
+    capacity = -1 if cap is None else cap
+    say(f"{label}: T={T} d={d} E={E} d_ff={dff} k={k} {dtype} shared={dffs} gate={gm} "
+        f"act={act} capacity={capacity}")
+    sh = (dev["Ws1"], dev["Ws3"], dev["Ws2"]) if dffs else None
+    L = moe.MoELayer(dev["Wg"], dev["W1"], dev["W3"], dev["W2"], k, dev["bias"], sh,
+                     gate_mode=gm, activation=act, capacity=capacity)
+    y = L(dev["x"])
+    torch.cuda.synchronize()
+    it = {n: v.cpu().numpy() for n, v in L.intermediates(T).items()}
+    lg = it["logits"].astype(np.float64)
+    ref = O.forward(h["x"], h["Wg"], h["W1"], h["W3"], h["W2"], k, bias=h["bias"],
+                    shared=(h["Ws1"], h["Ws3"], h["Ws2"]) if dffs else None, logits_in=lg,
+                    gate_mode=gm, act=act, capacity=cap)
+    np.testing.assert_array_equal(it["idx"], ref["idx"])
+    assert np.max(np.abs(it["gate"] - ref["gate"])) <= 1e-6
+    np.testing.assert_array_equal(it["counts"], ref["counts"])
+    np.testing.assert_array_equal(it["offsets"], ref["offsets"])
+    kept = int(ref["offsets"][E])
+    np.testing.assert_array_equal(it["perm"][:kept], ref["perm"])
+    np.testing.assert_array_equal(it["inv"], ref["inv"])
+    got = f64(moe.tensor_to_numpy(y))
+    dropped = int(np.sum(ref["inv"] < 0))
+    if not np.any(ref["y"]):
+        say(f"{label}: every pair dropped, y must be zero")
+        assert not np.any(got)
+        return
+    err = rel_l2(got, ref["y"])
+    say(f"{label}: dropped {dropped} of {T * k} pairs, rel-L2 {err:.3e} (bar {TOL[dtype]})")
+    assert err <= TOL[dtype]
+
+
+@pytest.mark.parametrize("gm", [0, 1, 2])
+def test_route_gate_modes(gm):
+    cfg, h, dev = inputs(777, 512, 64, 64, 4, "bf16", seed=11)
+    idx, gate, logits = moe.route(dev["x"], dev["Wg"], 4, None, gate_mode=gm)
+    torch.cuda.synchronize()
+    lg = logits.double().cpu().numpy()
+    idx_ref = O.topk(lg, 4)
+    np.testing.assert_array_equal(idx.cpu().numpy(), idx_ref)
+    gref = O.gate_mode(lg, idx_ref, gm)
+    err = float(np.max(np.abs(gate.cpu().numpy() - gref)))
+    say(f"moe_route_ex gate_mode {gm}: max |gate - oracle| {err:.2e}")
+    assert err <= 1e-6
+
+
+@pytest.mark.parametrize("T,E,k,cap", [(1000, 8, 2, 100), (9000, 12, 3, 1500), (50, 4, 1, 0),
+                                       (4097, 256, 8, 7)])
+def test_permute_capacity(T, E, k, cap):
+    rng = np.random.default_rng(T + E)
+    # skewed expert choices, k distinct experts per token
+    w = np.exp(-np.arange(E) / 3.0)
+    idx = np.stack([rng.choice(E, size=k, replace=False, p=w / w.sum()) for _ in range(T)])
+    idx = idx.astype(np.int32)
+    counts, offsets, perm, inv = moe.permute(torch.from_numpy(idx).cuda(), E, capacity=cap)
+    torch.cuda.synchronize()
+    keep = O.keep(idx, E, cap).astype(bool)
+    kc = np.bincount(idx.reshape(-1)[keep], minlength=E)
+    np.testing.assert_array_equal(counts.cpu().numpy(), kc)
+    np.testing.assert_array_equal(offsets.cpu().numpy(), np.concatenate([[0], np.cumsum(kc)]))
+    order = np.flatnonzero(keep)[np.argsort(idx.reshape(-1)[keep], kind="stable")]
+    np.testing.assert_array_equal(perm.cpu().numpy()[:len(order)], order)
+    inv_ref = np.full(T * k, -1, np.int32)
+    inv_ref[order] = np.arange(len(order), dtype=np.int32)
+    np.testing.assert_array_equal(inv.cpu().numpy(), inv_ref)
+    say(f"moe_permute_ex T={T} E={E} k={k} capacity={cap}: kept {len(order)} of {T * k}")
