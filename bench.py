@@ -149,6 +149,38 @@ def run_workload(cfg, host, dev, steps, warmup, flush_mb=0, graph=False):
     return out
 
 
+def run_variant(cfg, dev, steps, warmup, **variants):
+    """Whole-layer time of moe_forward_ex with the given variants (HIP events
+    around `steps` back-to-back forwards) and the pairs the experts kept."""
+    import numpy as np
+    import torch
+
+    from sparse_mixture_experts_permute_amd import moe
+    T = cfg.T
+    x = dev["x"][:T].contiguous()
+    bias = None
+    if cfg.skew:
+        b = np.zeros(cfg.E, np.float32)
+        b[0] = cfg.skew
+        bias = torch.from_numpy(b).cuda()
+    layer = moe.MoELayer(dev["Wg"], dev["W1"], dev["W3"], dev["W2"], cfg.k, bias, None,
+                         **variants)
+    y = torch.empty_like(x)
+    for _ in range(warmup):
+        layer(x, y)
+    torch.cuda.synchronize()
+    a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        layer(x, y)
+    b_.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b_) / steps
+    it = layer.intermediates(T)
+    counts = it["counts"].cpu().numpy()
+    return dict(ms=ms, counts=counts, kept=int(counts.sum()))
+
+
 def measured_traffic(cfg):
     """HBM traffic per dispatch of the SwiGLU GEMM from the committed rocprofv3
     counter runs (profiles/traffic.json), or None when those counters were
@@ -278,6 +310,26 @@ def main():
             log(f"{name}: {ms2:.4f} ms/step (sum of stages), {e['tokens_per_s']} tokens/s")
             extra.append(e)
 
+    # the variants beside the method, at the headline shape (whole-layer time)
+    variants = []
+    if not args.no_extra and cfg.d == 4096 and cfg.E == 8 and cfg.T == 8192:
+        skew = CONFIGS["mixtral_prefill_T8192_skew"]
+        cap = moe.capacity(skew.T, skew.k, 1.2 * skew.k / skew.E)  # 1.2 x the mean load
+        for label, c2, kw in [
+                ("capacity_1.2x_mean_load_skew", skew, dict(capacity=cap)),
+                ("gate_softmax_all", cfg, dict(gate_mode=moe.GATE_SOFTMAX_ALL)),
+                ("sigmoid_gate_sigmoid_glu", cfg,
+                 dict(gate_mode=moe.GATE_SIGMOID, activation=moe.ACT_GLU_SIGMOID))]:
+            r3 = run_variant(c2, dev, 5, 2, **kw)
+            flop = 6.0 * c2.d * c2.d_ff * r3["kept"]
+            v = dict(variant=label, workload=c2.name, options=kw, ms_per_step=round(r3["ms"], 4),
+                     tokens_per_s=round(c2.T / (r3["ms"] * 1e-3), 1),
+                     pairs_kept=r3["kept"], pairs=c2.T * c2.k,
+                     layer_mfma_frac=round(flop / (r3["ms"] * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
+                                           4))
+            log(f"variant {label}: {r3['ms']:.3f} ms/step, kept {r3['kept']} of {c2.T * c2.k}")
+            variants.append(v)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
@@ -308,6 +360,7 @@ def main():
                           "mean": float(counts.mean())},
         "cpu_baseline": cpu,
         "extra": extra,
+        "variants": variants,
         "wall_s_timed": round(res["wall_s"], 3),
         "timing": "HIP events on the stream the kernels run on; stage events recorded by "
                   "moe_forward_timed inside the timed region",
