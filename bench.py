@@ -310,6 +310,32 @@ def main():
             log(f"{name}: {ms2:.4f} ms/step (sum of stages), {e['tokens_per_s']} tokens/s")
             extra.append(e)
 
+    # the fine-grained layer with a shared expert (256 experts, top-8)
+    if not args.no_extra and cfg.d == 4096 and cfg.E == 8:
+        del dev
+        torch.cuda.empty_cache()
+        fcfg = CONFIGS["fine_shared_T8192"]
+        log("generating inputs for the 256-expert layer")
+        fhost = make_inputs(fcfg)
+        fdev = {n: moe.tensor_from_numpy(a) for n, a in fhost.items() if a is not None}
+        del fhost
+        for name in ("fine_shared_T512", "fine_shared_T8192"):
+            c2 = CONFIGS[name]
+            r2 = run_workload(c2, None, fdev, 5, 2)
+            rl2, lf2 = roofline_for(c2, r2)
+            ms2 = r2["ms"]
+            e = dict(workload=name, T=c2.T, ms_per_step=round(ms2, 4),
+                     tokens_per_s=round(c2.T / (ms2 * 1e-3), 1),
+                     stage_ms={s_: round(float(v), 4) for s_, v in zip(moe.STAGES,
+                                                                        r2["stage_ms"])},
+                     roofline=rl2, layer=lf2, mall_flushed=False)
+            log(f"{name}: {ms2:.4f} ms/step, {e['tokens_per_s']} tokens/s, "
+                f"layer mfma {lf2['mfma_frac']} hbm {lf2['hbm_frac']}")
+            extra.append(e)
+        del fdev
+        torch.cuda.empty_cache()
+        dev = {n: moe.tensor_from_numpy(a) for n, a in host.items() if a is not None}
+
     # the variants beside the method, at the headline shape (whole-layer time)
     variants = []
     if not args.no_extra and cfg.d == 4096 and cfg.E == 8 and cfg.T == 8192:
