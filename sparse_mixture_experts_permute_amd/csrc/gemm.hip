@@ -268,70 +268,71 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_kernel(
 // end).
 //
 // The kernel is persistent (one workgroup per CU, two for 64-row tiles): the
-// next tile's first slice is loaded while the current tile's epilogue runs.
+// next tile's first two slices are loaded while the current tile's epilogue runs.
 //
 // Split K (down projection only): blockIdx.y picks one of gridDim.y equal K
 // ranges and its fp32 partial goes to output plane blockIdx.y (plane elements
 // apart); the combine adds the planes in a fixed order.
 // ---------------------------------------------------------------------------
-// Epilogue of one tile of the direct-to-LDS kernel.  SwiGLU: each wave writes
-// its bf16 outputs to `stage` in row-major order (16-byte chunks XOR-swizzled
-// by row so rows r and r+4, written by the two halves of the wave, fall in
-// different banks), then stores whole 16-byte row chunks.  Down projection:
-// fp32 outputs are stored straight from the accumulators (32 consecutive
-// columns of two rows per instruction).
+// Two floats to two bf16 (round to nearest even) in one 32-bit word, low first.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2_v;
+  const f32x2_v f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_v));
+}
+
+// Epilogue of one tile of the direct-to-LDS kernel.  The MFMAs take the
+// weight fragment as their first operand, so each accumulator block holds the
+// transposed product: lane l has token row l % 32 of the block and, in each of
+// the four groups of 8 output columns, the 4 consecutive columns starting at
+// 4 * (l / 32).  SwiGLU gates those 4 columns and stores them as 8 bytes of
+// bf16; the down projection stores them as 16 bytes of fp32.  No LDS staging,
+// so both stages are free for the next tile's loads during the epilogue.
 template <int BM, int BNB, bool SWIGLU, int TM, int TN, typename TA>
-__device__ __forceinline__ void dl_epilogue(const TA &ta, f32x16_v (&acc)[TM][TN], uint4 *stage,
+__device__ __forceinline__ void dl_epilogue(const TA &ta, f32x16_v (&acc)[TM][TN],
                                             void *__restrict__ C, int N, size_t plane, int act,
                                             int wave, int lane) {
   constexpr int WN = 2;
   const int wm = wave / WN, wn = wave % WN;
   const int row0 = ta.row0, rows = ta.rows, n0 = ta.n0;
-  const int ccol = lane & 31;
-  const int crow4 = (lane >> 5) * 4;
+  const int tr = lane & 31;          // token row inside a 32-row block
+  const int cq = (lane >> 5) * 4;    // first of the lane's 4 columns in each 8-column group
   if constexpr (SWIGLU) {
-    constexpr int WC = 32 * TN / 2;          // columns per wave
-    static_assert(WC / 8 == 8, "swizzle assumes 128-byte rows");
-    char *reg = reinterpret_cast<char *>(stage) + wave * (32 * TM * WC * 2);
+    constexpr int WC = 32 * TN / 2;  // output columns per wave
 #pragma unroll
-    for (int a = 0; a < TM; ++a)
+    for (int a = 0; a < TM; ++a) {
+      const int grow = (wm * TM + a) * 32 + tr;
+      bf16_t *dst = reinterpret_cast<bf16_t *>(C) + (size_t)(row0 + grow) * N + n0 + wn * WC;
 #pragma unroll
       for (int q = 0; q < TN / 2; ++q)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = a * 32 + (i / 4) * 8 + crow4 + (i % 4);
-          const int c = q * 32 + ccol;
-          const float h = gated(acc[a][2 * q][i], acc[a][2 * q + 1][i], act);
-          *reinterpret_cast<bf16_t *>(reg + r * (WC * 2) + (((c >> 3) ^ (r & 7)) << 4) +
-                                      (c & 7) * 2) = f32_to_bf16(h);
-        }
-    const int col = n0 + wn * WC + (lane & 7) * 8;
+        for (int g = 0; g < 4; ++g) {
+          float h[4];
 #pragma unroll
-    for (int t = 0; t < 32 * TM / 8; ++t) {
-      const int r = t * 8 + (lane >> 3);
-      const uint4 v = *reinterpret_cast<const uint4 *>(reg + r * (WC * 2) +
-                                                        (((lane & 7) ^ (r & 7)) << 4));
-      const int grow = wm * 32 * TM + r;
-      if (grow < rows && col < N)
-        *reinterpret_cast<uint4 *>(reinterpret_cast<bf16_t *>(C) + (size_t)(row0 + grow) * N +
-                                   col) = v;
+          for (int u = 0; u < 4; ++u)
+            h[u] = gated(acc[a][2 * q][g * 4 + u], acc[a][2 * q + 1][g * 4 + u], act);
+          uint2 v;
+          v.x = pack_bf16x2(h[0], h[1]);
+          v.y = pack_bf16x2(h[2], h[3]);
+          const int c = q * 32 + g * 8 + cq;
+          if (grow < rows && n0 + wn * WC + c < N) *reinterpret_cast<uint2 *>(dst + c) = v;
+        }
     }
   } else {
-    (void)stage;
     float *out = reinterpret_cast<float *>(C) + blockIdx.y * plane;
 #pragma unroll
     for (int a = 0; a < TM; ++a) {
+      const int r = (wm * TM + a) * 32 + tr;
+      float *dst = out + (size_t)(row0 + r) * N + n0;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = (wm * TM + a) * 32 + (i / 4) * 8 + crow4 + (i % 4);
-        if (r >= rows) continue;
-        const size_t orow = (size_t)(row0 + r) * N;
+      for (int b = 0; b < TN; ++b)
 #pragma unroll
-        for (int b = 0; b < TN; ++b) {
-          const int col = n0 + (wn * TN + b) * 32 + ccol;
-          if (col < N) out[orow + col] = acc[a][b][i];
+        for (int g = 0; g < 4; ++g) {
+          const int c = (wn * TN + b) * 32 + g * 8 + cq;
+          const float4 v = make_float4(acc[a][b][g * 4], acc[a][b][g * 4 + 1],
+                                       acc[a][b][g * 4 + 2], acc[a][b][g * 4 + 3]);
+          if (r < rows && n0 + c < N) *reinterpret_cast<float4 *>(dst + c) = v;
         }
-      }
     }
   }
 }
@@ -456,7 +457,7 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
 #pragma unroll
       for (int b = 0; b < TN; ++b)
         acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8_v, af[a]), __builtin_bit_cast(bf16x8_v, bf[b]), acc[a][b],
+            __builtin_bit_cast(bf16x8_v, bf[b]), __builtin_bit_cast(bf16x8_v, af[a]), acc[a][b],
             0, 0, 0);
   };
   uint4 f0a[TM], f0b[TN], g0a[TM], g0b[TN], f1a[TM], f1b[TN], f2a[TM], f2b[TN], f3a[TM], f3b[TN];
@@ -541,8 +542,8 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
     SLICE_BODY(st0, st1, kt, f0a, f0b, g0a, g0b, false, true);
     SLICE_BODY(st1, st0, kt + 1, g0a, g0b, f0a, f0b, false, false);
     // Every wave is past the last barrier of the tile, so no wave reads either
-    // stage any more: the next tile's first slice goes to st0 now, its second
-    // to st1 once the epilogue (which stages SwiGLU outputs in st1) is done.
+    // stage any more: the next tile's first two slices are loaded while the
+    // epilogue runs.
     hw += gridDim.x;
     Tile nt;
     const bool more = map_tile(hw, mtile_off, G, ntn, nt);
@@ -550,12 +551,11 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
     if (more) {
       setup(nt, nxt);
       issue(nxt, st0, 0);
+      issue(nxt, st1, 1);
     }
-    dl_epilogue<BM, BNB, SWIGLU>(cur, acc, st1, C, N, plane, act, wave, lane_t);
+    dl_epilogue<BM, BNB, SWIGLU>(cur, acc, C, N, plane, act, wave, lane_t);
     if (!more) break;
-    if constexpr (SWIGLU) RAW_BARRIER();  // every wave has read its staged outputs back
-    issue(nxt, st1, 1);
-    VM_WAIT(PER);  // slice 0 (and the epilogue's stores) done, slice 1 may be in flight
+    VM_WAIT(0);  // both slices (and the epilogue's stores) done
     RAW_BARRIER();
     rd(st0, 0, f0a, f0b);
     cur = nxt;
