@@ -16,7 +16,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 enum Field {
   F_LOGITS, F_IDX, F_GATE, F_COUNTS, F_OFFSETS, F_PERM, F_INV, F_MT0, F_MT1, F_SHSEG, F_ACT,
-  F_RPART, F_BLK, F_XP, F_H, F_YP, F_HS, F_YS, F_COUNT
+  F_FIXC, F_FIXP, F_RPART, F_BLK, F_XP, F_H, F_YP, F_HS, F_YS, F_COUNT
 };
 
 struct Layout {
@@ -37,11 +37,26 @@ bool dims_ok(int T, int d, int d_ff, int E, int k, int dffs) {
 
 size_t esize(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
 
+// Most output tiles a down projection that may split its last round can have
+// (0: none can); sizes the scratch of that split.
+long long dl_tiles(const moe::GemmPlan &plan, int T, int k, int E, int d, int d_ff, int dffs) {
+  if (!plan.dl2 || plan.bm2 != 256) return 0;
+  const long long P = (long long)T * k;
+  long long t = 0;
+  if (d_ff >= moe::SPLIT_MIN_K) t = (long long)((d + 255) / 256) * ((P + 255) / 256 + E);
+  if (dffs >= moe::SPLIT_MIN_K) {
+    const long long ts = (long long)((d + 255) / 256) * ((T + 255) / 256);
+    t = ts > t ? ts : t;
+  }
+  return t;
+}
+
 int down_splits(const moe::GemmPlan &plan, int T, int k, int E, int d, int d_ff);
 
 Layout layout(int T, int d, int d_ff, int E, int k, int dffs, int dtype) {
   Layout L;
   const moe::GemmPlan plan = moe::gemm_plan(dtype, d, d_ff, dffs, ((long long)T * k + E - 1) / E);
+  const long long tiles = dl_tiles(plan, T, k, E, d, d_ff, dffs);
   const int ksplit = down_splits(plan, T, k, E, d, d_ff);
   const size_t P = (size_t)T * k, es = esize(dtype);
   const size_t nb = (size_t)moe::permute_nblocks((int)P);
@@ -57,6 +72,8 @@ Layout layout(int T, int d, int d_ff, int E, int k, int dffs, int dtype) {
   sz[F_MT1] = (size_t)(E + 1) * 4;
   sz[F_SHSEG] = 8 * 4;
   sz[F_ACT] = (size_t)(E + 1) * 4;
+  sz[F_FIXC] = tiles ? (size_t)moe::FIX_SLOTS * 4 : 0;
+  sz[F_FIXP] = moe::fix_part_bytes(tiles);
   sz[F_RPART] = moe::router_partial_bytes(T, d, E, (int)es);
   sz[F_BLK] = nb * E * 4;
   sz[F_XP] = P * d * es;
@@ -88,9 +105,13 @@ int device_ok() {
 
 int launched(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ELAUNCH; }
 
-// K splits of the tiled down projection: a batch with few m-tiles (decode, few
-// rows per expert) would leave most CUs idle, so K is split until about 512
-// workgroups run; the combine adds the partial planes in a fixed order.
+// K planes of the tiled down projection: a batch with fewer tiles than one
+// round of the persistent kernel (256 workgroups of 256-row tiles, 512 of
+// 64-row tiles on 256 CUs) would leave most CUs idle, so every tile's K is
+// split until a round is full, and the combine adds the partial planes in a
+// fixed order (cheaper there than the kernel's own last-round split, whose
+// last part reads the other parts back).  From one round on, that last-round
+// split serves instead.
 int down_splits(const moe::GemmPlan &plan, int T, int k, int E, int d, int d_ff) {
   if (!plan.dl2) return 1;
   const long long P = (long long)T * k;
@@ -98,8 +119,9 @@ int down_splits(const moe::GemmPlan &plan, int T, int k, int E, int d, int d_ff)
   const long long mt_floor = (P + plan.bm2 - 1) / plan.bm2;
   const long long mt = active > mt_floor ? active : mt_floor;
   const long long wgs = mt * ((d + 255) / 256);
+  const long long round = plan.bm2 == 64 ? 512 : 256;
   int S = 1;
-  while (wgs * S < 512 && S < 16 && d_ff % (128 * S * 2) == 0) S *= 2;  // K parts of 128
+  while (wgs * S < round && S < 16 && d_ff % (128 * S * 2) == 0) S *= 2;  // K parts of 128
   return S;
 }
 
@@ -221,7 +243,8 @@ int moe_permute_ex(const int32_t *idx, int T, int E, int k, int capacity, int32_
   int32_t *act = sh + align_up((size_t)(E + 1) * 4 + 32) / 4;
   // the m-tile prefixes are by-products here; any tile height will do
   return launched(moe::launch_permute(idx, T, E, k, capacity, 256, 256, blk, counts, offsets,
-                                      perm, inv, mt0, mt1, sh, act, (hipStream_t)stream));
+                                      perm, inv, mt0, mt1, sh, act, nullptr, 0,
+                                      (hipStream_t)stream));
 }
 
 int moe_permute(const int32_t *idx, int T, int E, int k, int32_t *counts, int32_t *offsets,
@@ -296,6 +319,9 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
   float *Yp = at<float>(ws, L.off[F_YP]);
   void *Hs = at<char>(ws, L.off[F_HS]);
   float *Ys = at<float>(ws, L.off[F_YS]);
+  int32_t *fixc = L.off[F_FIXC + 1] > L.off[F_FIXC] ? at<int32_t>(ws, L.off[F_FIXC]) : nullptr;
+  const moe::FixScratch fx{fixc, fixc ? at<char>(ws, L.off[F_FIXP]) : nullptr,
+                           L.off[F_FIXP + 1] - L.off[F_FIXP]};
 
   hipError_t e;
   // stage boundary i: an optional timing event recorded on the stream
@@ -307,7 +333,8 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
     goto fail;
   MOE_MARK(1);
   if ((e = moe::launch_permute(idx, T, E, k, o.capacity, plan.bm1, plan.bm2, blk, counts,
-                               offsets, perm, inv, mt0, mt1, shseg, act, s)))
+                               offsets, perm, inv, mt0, mt1, shseg, act, fixc,
+                               fixc ? moe::FIX_SLOTS : 0, s)))
     goto fail;
   MOE_MARK(2);
   if (sk.routed) {
@@ -334,7 +361,7 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
       goto fail;
     MOE_MARK(4);
     if ((e = moe::launch_gemm_down(dtype, plan.dl2, plan.bm2, H, W2, Yp, offsets, mt1, E, d, d_ff,
-                                   (P + plan.bm2 - 1) / plan.bm2 + E, ksplit, plane, s)))
+                                   (P + plan.bm2 - 1) / plan.bm2 + E, ksplit, plane, fx, s)))
       goto fail;
     MOE_MARK(5);
   }
@@ -359,7 +386,7 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
                                        (T + plan.bm1 - 1) / plan.bm1, s)))
         goto fail;
       if ((e = moe::launch_gemm_down(dtype, plan.dl2, plan.bm2, Hs, Ws2, Ys, shseg, shseg + 4, 1, d,
-                                     d_ff_shared, (T + plan.bm2 - 1) / plan.bm2, 1, 0, s)))
+                                     d_ff_shared, (T + plan.bm2 - 1) / plan.bm2, 1, 0, fx, s)))
         goto fail;
     }
   }

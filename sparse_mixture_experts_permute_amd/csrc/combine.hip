@@ -1,9 +1,9 @@
 // Gate-weighted combine back to token order:
 //   y[t][:] = sum_{j<k} gate[t][j] * Yp[inv[t*k+j]][:]  (+ Ys[t][:] for the shared expert)
-// A pair with inv < 0 was dropped by an expert's capacity limit and adds nothing.
-// summed in fp32 with j ascending, written once per token with no atomics.
-// When the down projection split K, Yp has nsplit planes whose rows are added
-// first, in plane order
+// A pair with inv < 0 was dropped by an expert's capacity limit and adds
+// nothing.  Summed in fp32 with j ascending, written once per token with no
+// atomics.  When the down projection split K into planes, Yp has nsplit planes
+// whose rows are added first, in plane order
 // ("Chapter 10 MoE", sections 10.4 and 10.5; "Mixtral and MoE architecture",
 // weighted accumulation in the MixtralMoE listing).
 #include "common.h"

@@ -26,7 +26,9 @@
 //         K indices g*8 + i to the i-th MFMA (A and B use the same order).
 //
 // Tile map.  mtile_off[e] is the prefix of ceil(count_e / BM) over experts;
-// map_tile turns a 1-D workgroup id into (expert, m-tile, n-tile).
+// map_tile turns a 1-D workgroup id into (expert, m-tile, n-tile).  The
+// persistent kernel also splits the tiles of its last round along K
+// (plan_split).
 #include "common.h"
 #include "kernels.h"
 
@@ -73,23 +75,70 @@ constexpr int NUM_XCD = 8;  // MI355X: 8 accelerator complex dies, each with its
 struct Tile {
   int e, g, n;
 };
-__device__ __forceinline__ bool map_tile(int hw, const int32_t *mtile_off, int G, int ntn,
-                                         Tile &t) {
-  const int R = ntn * mtile_off[G];
+// Position in the logical order of the tile that workgroup slot hw takes, or
+// -1 (a surplus slot).  R tiles; the grid holds gridDim.x workgroups.
+__device__ __forceinline__ int tile_order(int hw, int R) {
   const int cpx = max(1, (int)gridDim.x / NUM_XCD);  // resident workgroups per XCD
   const int R8 = (R + NUM_XCD - 1) / NUM_XCD;
   const int rounds = max(1, (R8 + cpx - 1) / cpx);
   const int BS = max(1, (R + NUM_XCD * rounds - 1) / (NUM_XCD * rounds));
   const int xcd = hw % NUM_XCD, local = hw / NUM_XCD;
   const int L = ((local / BS) * NUM_XCD + xcd) * BS + local % BS;
-  if (L >= R) return false;
+  return L < R ? L : -1;
+}
+// Logical tile L -> (expert, global m-tile, n-tile): expert-major, then
+// n-tile, the expert's m-tiles fastest.
+__device__ __forceinline__ Tile decode_tile(int L, const int32_t *mtile_off, int G, int ntn) {
+  Tile t;
   const int e = upper_segment(mtile_off, G, L / ntn);
   const int rem = L - ntn * mtile_off[e];
   const int me = mtile_off[e + 1] - mtile_off[e];
   t.e = e;
   t.n = rem / me;
   t.g = mtile_off[e] + rem % me;
+  return t;
+}
+__device__ __forceinline__ bool map_tile(int hw, const int32_t *mtile_off, int G, int ntn,
+                                         Tile &t) {
+  const int L = tile_order(hw, ntn * mtile_off[G]);
+  if (L < 0) return false;
+  t = decode_tile(L, mtile_off, G, ntn);
   return true;
+}
+
+// Spreading the last, partial round of a persistent launch.  With W resident
+// workgroups, R tiles are q full rounds plus m = R mod W tail tiles, which
+// would leave W - m workgroups idle for a whole tile.  Instead each tail tile
+// is cut into S parts along K, so the tail becomes m*S shorter work units:
+// units 0 .. F-1 (F = R - m) are whole tiles, units F .. F + m*S - 1 are the
+// parts (part p of tail tile j is unit F + p*m + j).  Every part writes its fp32
+// partial sums to a scratch slot and counts itself in; the part that arrives
+// last adds all partials in part order (so the sum does not depend on timing)
+// and runs the tile's epilogue.  S is a power of two dividing the K slices
+// into pairs, at most 16 and with m*S <= part_cap, picked by an estimate of
+// the tail's time in K slices: ceil(m*S / W) rounds of nk/S slices of MFMA
+// work, 6 of fixed cost (the partial's store among them) and red10/10 per
+// partial the last part reads back; a split must save 15% of the tail.
+struct Split {
+  int F, m, S;
+};
+__device__ __forceinline__ Split plan_split(int R, int W, int nk, int red10, int part_cap) {
+  Split sp{R, 0, 1};
+  const int m = R % W;
+  if (m == 0 || m > FIX_SLOTS) return sp;
+  int best = nk * 85 / 10;  // the tail tiles run whole (a split must save 15%)
+  for (int s = 2; s <= 16 && (nk / 2) % s == 0 && m * s <= part_cap; s *= 2) {
+    const int cost = ((m * s + W - 1) / W) * (nk * 10 / s + 60 + red10 * s);
+    if (cost < best) {
+      best = cost;
+      sp.S = s;
+    }
+  }
+  if (sp.S > 1) {
+    sp.F = R - m;
+    sp.m = m;
+  }
+  return sp;
 }
 
 template <typename T, int BM, int BNB, int WM, int WN, bool SWIGLU>
@@ -268,11 +317,11 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_kernel(
 // end).
 //
 // The kernel is persistent (one workgroup per CU, two for 64-row tiles): the
-// next tile's first two slices are loaded while the current tile's epilogue runs.
-//
-// Split K (down projection only): blockIdx.y picks one of gridDim.y equal K
-// ranges and its fp32 partial goes to output plane blockIdx.y (plane elements
-// apart); the combine adds the planes in a fixed order.
+// next tile's first two slices are loaded while the current tile's epilogue
+// runs.  The tiles of the last round are split along K (plan_split), so that
+// every workgroup has work until the end.  A down projection with too few
+// tiles for the GPU instead splits every tile's K into planes (blockIdx.y)
+// that the combine adds.
 // ---------------------------------------------------------------------------
 // Two floats to two bf16 (round to nearest even) in one 32-bit word, low first.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -337,11 +386,14 @@ __device__ __forceinline__ void dl_epilogue(const TA &ta, f32x16_v (&acc)[TM][TN
   }
 }
 
-template <int BM, int BNB, bool SWIGLU>
+// SPLIT: the last round's tiles may be split along K (plan_split); compiled
+// only where that pays, since the split's code costs registers in every tile.
+template <int BM, int BNB, bool SWIGLU, bool SPLIT>
 __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
     const bf16_t *__restrict__ A, const bf16_t *__restrict__ B1, const bf16_t *__restrict__ B3,
     void *__restrict__ C, const int32_t *__restrict__ seg_off,
-    const int32_t *__restrict__ mtile_off, int G, int N, int K, size_t plane, int act) {
+    const int32_t *__restrict__ mtile_off, int G, int N, int K, size_t plane, int act,
+    int32_t *__restrict__ fix_cnt, f32x4_v *__restrict__ fix_part, int part_cap) {
   constexpr int WM = 2, WN = 2;
   constexpr int TM = BM / WM / 32, TN = BNB / WN / 32;
   constexpr int ROWS = BM + BNB;          // tile rows per stage (A then B)
@@ -351,6 +403,7 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
 
   __shared__ uint4 st0[STAGE_U4];
   __shared__ uint4 st1[STAGE_U4];
+  __shared__ int fix_arrived;
   constexpr int COLS = SWIGLU ? BNB / 2 : BNB;
   const int ntn = (N + COLS - 1) / COLS;
 
@@ -360,9 +413,17 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
 
   constexpr int IA = BM / 32, IB = BNB / 32;  // LDS-DMA instructions per wave per stage
   constexpr int PER = IA + IB;
-  const int kpart = K / gridDim.y;  // K range of this split (a multiple of 128)
-  const size_t kb = (size_t)blockIdx.y * kpart * 2;  // its byte offset inside a row
-  const int nk = kpart / 64;        // 64-wide K slices (even)
+  // K planes (down projection of small batches): blockIdx.y takes one of
+  // gridDim.y equal K ranges, its fp32 partial goes to output plane blockIdx.y
+  // (plane elements apart) and the combine adds the planes in order
+  const int kpl = K / gridDim.y;                          // a multiple of 128
+  const uint32_t kb_pl = (uint32_t)blockIdx.y * kpl * 2;  // its byte offset in a row
+  const int nk_all = kpl / 64;  // 64-wide K slices of a whole tile (even)
+  // work units: whole tiles, then the parts of the tail tiles (reading a
+  // partial back is bound by the latency of device-scope loads: about 10 slices)
+  const int R = ntn * mtile_off[G];
+  const Split sp = SPLIT && gridDim.y == 1 ? plan_split(R, gridDim.x, nk_all, 100, part_cap)
+                                           : Split{R, 0, 1};
   const int lrow = lane >> 3, lchunk = lane & 7;
 
   // Addressing of one tile.  A tile reads its rows of A and its columns of
@@ -379,16 +440,39 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
     __amdgpu_buffer_rsrc_t ra, r1, r3;
     uint32_t lc0, lc1;
     int row0, rows, n0;
+    int nk;    // K slices of this unit (even)
+    int part;  // part of a split tail tile, or -1 for a whole tile
+    int slot;  // the tail tile's index among the split ones
+  };
+  // work unit u -> tile and K range (false: no unit u)
+  auto map_unit = [&](int u, Tile &t, TileAddr &ta) -> bool {
+    if (u < sp.F || sp.S == 1) {
+      const int L = tile_order(u, sp.F);
+      if (L < 0) return false;
+      t = decode_tile(L, mtile_off, G, ntn);
+      ta.nk = nk_all;
+      ta.part = -1;
+      ta.slot = 0;
+      return true;
+    }
+    const int j = u - sp.F;
+    if (j >= sp.m * sp.S) return false;
+    ta.slot = j % sp.m;
+    ta.part = j / sp.m;
+    ta.nk = nk_all / sp.S;
+    t = decode_tile(sp.F + ta.slot, mtile_off, G, ntn);
+    return true;
   };
   auto setup = [&](const Tile &t, TileAddr &ta) {
     const int e = t.e;
+    const uint32_t kb = kb_pl + (ta.part < 0 ? 0u : (uint32_t)(ta.part * ta.nk) * 128u);
     ta.row0 = seg_off[e] + (t.g - mtile_off[e]) * BM;
     ta.rows = min(BM, seg_off[e + 1] - ta.row0);
     ta.n0 = t.n * COLS;
     ta.ra = make_rsrc(reinterpret_cast<const char *>(A) + (size_t)ta.row0 * rowb + kb,
-                      (uint32_t)ta.rows * rowb - (uint32_t)kb);
+                      (uint32_t)ta.rows * rowb - kb);
     const size_t eoff = (size_t)e * N * rowb + kb;
-    const uint32_t wbytes = (uint32_t)N * rowb - (uint32_t)kb;
+    const uint32_t wbytes = (uint32_t)N * rowb - kb;
     ta.r1 = make_rsrc(reinterpret_cast<const char *>(B1) + eoff, wbytes);
     ta.r3 = SWIGLU ? make_rsrc(reinterpret_cast<const char *>(B3) + eoff, wbytes) : ta.r1;
     // per-tile copies of the lane offsets: keeps the compiler from hoisting
@@ -505,13 +589,76 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
     SCHED_FENCE();                                                             \
   } while (0)
 
-  // Persistent: the workgroup walks the tile order in steps of the grid size
+  // The last part of a split tile to finish adds the partial sums of all its
+  // parts into acc (false: other parts are still missing, nothing to store).
+  // A tile's S partial slots hold its accumulators in lane order (float4
+  // number ((wave * TM * TN + a * TN + b) * 4 + g) * 64 + lane of each slot).
+  // The parts may run on different XCDs, whose L2 caches are not coherent
+  // with each other, so partials are stored and loaded with device scope
+  // (sc1): written through to memory, read from it.  A part's stores are
+  // complete before it counts itself in, so the part that counts S - 1 finds
+  // every partial in memory.
+  auto fixup = [&](const TileAddr &ta) -> bool {
+    constexpr uint32_t TILE_B = BM * BNB * 4;  // bytes of one partial
+    constexpr int SC1 = 16;                    // cache policy: device scope
+    typedef uint32_t u32x4_v __attribute__((ext_vector_type(4)));
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(fix_part + (size_t)ta.slot * sp.S * (TILE_B / 16), (uint32_t)sp.S * TILE_B);
+    const uint32_t lb = (uint32_t)(wave * TM * TN * 4 * 64 + lane) * 16;
+    // the per-instruction constant goes in the scalar offset
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+      for (int b = 0; b < TN; ++b)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4_v v = {acc[a][b][4 * g], acc[a][b][4 * g + 1], acc[a][b][4 * g + 2],
+                             acc[a][b][4 * g + 3]};
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_v, v), rs,
+                                                 (uint32_t)ta.part * TILE_B + lb,
+                                                 ((a * TN + b) * 4 + g) * 1024, SC1);
+        }
+    VM_WAIT(0);  // this wave's partial is in memory
+    RAW_BARRIER();
+    if (tid == 0)
+      fix_arrived = __hip_atomic_fetch_add(&fix_cnt[ta.slot], 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (fix_arrived != sp.S - 1) return false;
+    // acc = partial 0 + partial 1 + ... in part order (the own partial is read
+    // back too); TN * 4 loads in flight per wave
+    for (int q = 0; q < sp.S; ++q) {
+#pragma unroll
+      for (int a = 0; a < TM; ++a) {
+        f32x4_v v[TN][4];
+#pragma unroll
+        for (int b = 0; b < TN; ++b)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            v[b][g] = __builtin_bit_cast(
+                f32x4_v, __builtin_amdgcn_raw_buffer_load_b128(
+                             rs, (uint32_t)q * TILE_B + lb, ((a * TN + b) * 4 + g) * 1024, SC1));
+#pragma unroll
+        for (int b = 0; b < TN; ++b)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              acc[a][b][4 * g + i] = q == 0 ? v[b][g][i] : acc[a][b][4 * g + i] + v[b][g][i];
+      }
+    }
+    if (tid == 0)  // ready for the next launch
+      __hip_atomic_store(&fix_cnt[ta.slot], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return true;
+  };
+
+  // Persistent: the workgroup walks the work units in steps of the grid size
   // (a multiple of the XCD count, so it stays on its XCD's chunk).  The next
-  // tile's first slices are loaded while the current tile's epilogue runs.
+  // unit's first slices are loaded while the current unit's epilogue runs.
   int hw = blockIdx.x;
   Tile tile;
-  if (!map_tile(hw, mtile_off, G, ntn, tile)) return;
   TileAddr cur;
+  if (!map_unit(hw, tile, cur)) return;
   setup(tile, cur);
   issue(cur, st0, 0);
   issue(cur, st1, 1);
@@ -533,27 +680,30 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
         for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
     // From here on the wait for slice s+1 lets the J1 loads of slice s+2 that
     // were issued before it stay in flight (the remaining PER - J1 come after).
-    // nk is even (checked by the host); the last pair issues nothing.
+    // nk is even (K is a multiple of 128 and S divides K / 128); the last pair
+    // issues nothing.
     int kt = 0;
-    for (; kt + 2 < nk; kt += 2) {
+    for (; kt + 2 < cur.nk; kt += 2) {
       SLICE_BODY(st0, st1, kt, f0a, f0b, g0a, g0b, true, true);
       SLICE_BODY(st1, st0, kt + 1, g0a, g0b, f0a, f0b, true, true);
     }
     SLICE_BODY(st0, st1, kt, f0a, f0b, g0a, g0b, false, true);
     SLICE_BODY(st1, st0, kt + 1, g0a, g0b, f0a, f0b, false, false);
-    // Every wave is past the last barrier of the tile, so no wave reads either
-    // stage any more: the next tile's first two slices are loaded while the
+    // Every wave is past the last barrier of the unit, so no wave reads either
+    // stage any more: the next unit's first two slices are loaded while the
     // epilogue runs.
     hw += gridDim.x;
     Tile nt;
-    const bool more = map_tile(hw, mtile_off, G, ntn, nt);
     TileAddr nxt;
+    const bool more = map_unit(hw, nt, nxt);
     if (more) {
       setup(nt, nxt);
       issue(nxt, st0, 0);
       issue(nxt, st1, 1);
     }
-    dl_epilogue<BM, BNB, SWIGLU>(cur, acc, C, N, plane, act, wave, lane_t);
+    bool store = true;
+    if constexpr (SPLIT) store = cur.part < 0 || fixup(cur);
+    if (store) dl_epilogue<BM, BNB, SWIGLU>(cur, acc, C, N, plane, act, wave, lane_t);
     if (!more) break;
     VM_WAIT(0);  // both slices (and the epilogue's stores) done
     RAW_BARRIER();
@@ -586,20 +736,18 @@ int resident_wgs(int bm) {
   return cus[dev] * (bm == 64 ? 2 : 1);
 }
 
-template <int BM, int BNB, bool SWIGLU>
+template <int BM, int BNB, bool SWIGLU, bool SPLIT = false>
 hipError_t launch_dl(const void *A, const void *B1, const void *B3, void *C,
                      const int32_t *seg_off, const int32_t *mtile_off, int G, int N, int K,
-                     int max_mtiles, int ksplit, size_t plane, int act, hipStream_t s) {
-  const int cols = SWIGLU ? BNB / 2 : BNB;
-  // persistent grid: at most what stays resident, a multiple of the XCD count
-  const long long upper = (long long)((N + cols - 1) / cols) * max_mtiles + NUM_XCD;
-  long long gx = resident_wgs(BM) / ksplit;
-  if (gx > upper) gx = upper;
-  gx = (gx + NUM_XCD - 1) / NUM_XCD * NUM_XCD;
-  dim3 grid((unsigned)gx, ksplit);
-  hipLaunchKernelGGL((grouped_gemm_dl_kernel<BM, BNB, SWIGLU>), grid, dim3(GM_THREADS), 0, s,
-                     (const bf16_t *)A, (const bf16_t *)B1, (const bf16_t *)B3, C, seg_off,
-                     mtile_off, G, N, K, plane, act);
+                     int ksplit, size_t plane, int act, const FixScratch &fx, hipStream_t s) {
+  // persistent grid: what stays resident, a multiple of the XCD count
+  const int gx = (resident_wgs(BM) / ksplit + NUM_XCD - 1) / NUM_XCD * NUM_XCD;
+  const size_t cap = fx.part ? fx.part_bytes / ((size_t)BM * BNB * 4) : 0;
+  hipLaunchKernelGGL((grouped_gemm_dl_kernel<BM, BNB, SWIGLU, SPLIT>), dim3(gx, ksplit),
+                     dim3(GM_THREADS), 0, s, (const bf16_t *)A, (const bf16_t *)B1,
+                     (const bf16_t *)B3, C, seg_off, mtile_off, G, N, K, plane, act, fx.cnt,
+                     (f32x4_v *)fx.part,
+                     (int)(cap < (size_t)FIX_SLOTS * 16 ? cap : (size_t)FIX_SLOTS * 16));
   return hipGetLastError();
 }
 
@@ -616,6 +764,13 @@ hipError_t launch_one(const void *A, const void *B1, const void *B3, void *C,
 }
 
 }  // namespace
+
+size_t fix_part_bytes(long long tiles) {
+  // a split uses at most 16 parts of each tail tile, and the kernel's own
+  // estimate rules out more than two rounds of parts on 256 workgroups
+  const long long parts = tiles * 16 < 512 ? tiles * 16 : 512;
+  return (size_t)(parts > 0 ? parts : 0) * 256 * 256 * 4;
+}
 
 GemmPlan gemm_plan(int dtype, int d, int d_ff, int d_ff_shared, long long rows_per_expert) {
   GemmPlan p;
@@ -634,12 +789,13 @@ hipError_t launch_gemm_swiglu(int dtype, bool dl, int bm, int act, const void *A
                               const int32_t *mtile_off, int G, int N, int K, int max_mtiles,
                               hipStream_t s) {
   if (max_mtiles <= 0) return hipSuccess;
+  const FixScratch none{nullptr, nullptr, 0};
   if (dl && bm == 64)
-    return launch_dl<64, 256, true>(A, W1, W3, H, seg_off, mtile_off, G, N, K, max_mtiles, 1, 0,
-                                    act, s);
+    return launch_dl<64, 256, true>(A, W1, W3, H, seg_off, mtile_off, G, N, K, 1, 0, act, none,
+                                    s);
   if (dl)
-    return launch_dl<256, 256, true>(A, W1, W3, H, seg_off, mtile_off, G, N, K, max_mtiles, 1,
-                                     0, act, s);
+    return launch_dl<256, 256, true>(A, W1, W3, H, seg_off, mtile_off, G, N, K, 1, 0, act, none,
+                                     s);
   if (dtype == 1)
     return launch_one<bf16_t, 128, 128, 2, 2, true>(A, W1, W3, H, seg_off, mtile_off, G, N, K,
                                                     max_mtiles, act, s);
@@ -649,14 +805,20 @@ hipError_t launch_gemm_swiglu(int dtype, bool dl, int bm, int act, const void *A
 
 hipError_t launch_gemm_down(int dtype, bool dl, int bm, const void *A, const void *W2, float *Y,
                             const int32_t *seg_off, const int32_t *mtile_off, int G, int N, int K,
-                            int max_mtiles, int ksplit, size_t plane, hipStream_t s) {
+                            int max_mtiles, int ksplit, size_t plane, const FixScratch &fx,
+                            hipStream_t s) {
   if (max_mtiles <= 0) return hipSuccess;
   if (dl && bm == 64)
-    return launch_dl<64, 256, false>(A, W2, nullptr, Y, seg_off, mtile_off, G, N, K,
-                                     max_mtiles, ksplit, plane, 0, s);
+    return launch_dl<64, 256, false>(A, W2, nullptr, Y, seg_off, mtile_off, G, N, K, ksplit,
+                                     plane, 0, fx, s);
+  // the last-round split pays for long K only (the kernel's estimate never
+  // splits below SPLIT_MIN_K)
+  if (dl && ksplit == 1 && K >= SPLIT_MIN_K && fx.part)
+    return launch_dl<256, 256, false, true>(A, W2, nullptr, Y, seg_off, mtile_off, G, N, K, 1,
+                                            0, 0, fx, s);
   if (dl)
-    return launch_dl<256, 256, false>(A, W2, nullptr, Y, seg_off, mtile_off, G, N, K,
-                                      max_mtiles, ksplit, plane, 0, s);
+    return launch_dl<256, 256, false>(A, W2, nullptr, Y, seg_off, mtile_off, G, N, K, ksplit,
+                                      plane, 0, fx, s);
   if (dtype == 1)
     return launch_one<bf16_t, 128, 128, 2, 2, false>(A, W2, nullptr, Y, seg_off, mtile_off, G,
                                                      N, K, max_mtiles, 0, s);

@@ -15,10 +15,13 @@ hipError_t launch_router(int dtype, const void *x, const void *Wg, const float *
 int permute_nblocks(int P);
 // capacity: pairs an expert keeps (its first ones in pair order); >= T*k keeps
 // all.  Dropped pairs (and ids outside [0, E)) get inv = -1.
+// zero (may be NULL): nzero int32 set to 0 on the way (the GEMMs' arrival
+// counters, see FixScratch).
 hipError_t launch_permute(const int32_t *idx, int T, int E, int k, int capacity, int bm0,
                           int bm1, int32_t *blk, int32_t *counts, int32_t *offsets,
                           int32_t *perm, int32_t *inv, int32_t *mtiles0, int32_t *mtiles1,
-                          int32_t *shared_seg, int32_t *active, hipStream_t s);
+                          int32_t *shared_seg, int32_t *active, int32_t *zero, int nzero,
+                          hipStream_t s);
 // xp[s] = x[perm[s] / k] for s < *placed (<= P, read on the device)
 hipError_t launch_gather(const void *x, const int32_t *perm, const int32_t *placed, int P, int k,
                          int d, int esize, void *xp, hipStream_t s);
@@ -29,16 +32,33 @@ struct GemmPlan {
   int bm1, bm2;   // rows per m-tile of the SwiGLU / down GEMM
 };
 GemmPlan gemm_plan(int dtype, int d, int d_ff, int d_ff_shared, long long rows_per_expert);
+// Scratch of the direct-to-LDS down projection (256-row tiles, K of at least
+// SPLIT_MIN_K) for the tiles of its last round, which it splits along K:
+// FIX_SLOTS arrival counters (zero before the launch; the kernel leaves them
+// zero) and part_bytes of fp32 partial tiles (no split when part is NULL).
+// Launches on one stream may share it.
+constexpr int FIX_SLOTS = 1024;
+constexpr int SPLIT_MIN_K = 4864;
+struct FixScratch {
+  int32_t *cnt;
+  void *part;
+  size_t part_bytes;
+};
+// Partial-tile bytes that let every split the kernel would choose go ahead
+// for a GEMM of at most `tiles` output tiles.
+size_t fix_part_bytes(long long tiles);
 // act: 0 SiLU(W1 a) * (W3 a), 1 sigmoid(W1 a) * (W3 a)
 hipError_t launch_gemm_swiglu(int dtype, bool dl, int bm, int act, const void *A,
                               const void *W1, const void *W3, void *H, const int32_t *seg_off,
                               const int32_t *mtile_off, int G, int N, int K, int max_mtiles,
                               hipStream_t s);
-// ksplit > 1 (direct-to-LDS kernel only): K is split in ksplit equal ranges
-// whose fp32 partials go to planes `plane` elements apart.
+// ksplit > 1 (direct-to-LDS kernel only): every tile's K is split in ksplit
+// equal ranges whose fp32 partials go to planes `plane` elements apart (for
+// batches with few tiles; the last-round split then stays off).
 hipError_t launch_gemm_down(int dtype, bool dl, int bm, const void *A, const void *W2, float *Y,
                             const int32_t *seg_off, const int32_t *mtile_off, int G, int N, int K,
-                            int max_mtiles, int ksplit, size_t plane, hipStream_t s);
+                            int max_mtiles, int ksplit, size_t plane, const FixScratch &fx,
+                            hipStream_t s);
 
 // Weight-streaming grouped GEMMs for few rows per expert (bf16 only).
 bool skinny_ok(int N, int K);

@@ -49,9 +49,10 @@ __global__ __launch_bounds__(256) void permute_scan_kernel(
     int32_t *__restrict__ blk, int nb, int E, int P, int T, int capacity, int bm0, int bm1,
     int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int32_t *__restrict__ mtiles0,
     int32_t *__restrict__ mtiles1, int32_t *__restrict__ shared_seg,
-    int32_t *__restrict__ active) {
+    int32_t *__restrict__ active, int32_t *__restrict__ zero, int nzero) {
   __shared__ int s0[256], s1[256], s2[256], s3[256];
   const int e = threadIdx.x;
+  for (int i = e; i < nzero; i += 256) zero[i] = 0;
   int raw = 0;
   if (e < E)
     for (int b = 0; b < nb; ++b) raw += blk[(size_t)b * E + e];
@@ -155,12 +156,14 @@ __global__ __launch_bounds__(PS_THREADS) void permute_small_kernel(
     const int32_t *__restrict__ idx, int P, int E, int T, int capacity, int bm0, int bm1,
     int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int32_t *__restrict__ perm,
     int32_t *__restrict__ inv, int32_t *__restrict__ mtiles0, int32_t *__restrict__ mtiles1,
-    int32_t *__restrict__ shared_seg, int32_t *__restrict__ active) {
+    int32_t *__restrict__ shared_seg, int32_t *__restrict__ active, int32_t *__restrict__ zero,
+    int nzero) {
   // hist: pairs per expert; koff: kept-pair offsets (scanned in place);
   // rk: rank of the next pair of each expert
   __shared__ int hist[256], koff[256], rk[256], s1[256], s2[256], s3[256];
   __shared__ int wc[PS_WAVES][256];
   const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
+  for (int i = tid; i < nzero; i += PS_THREADS) zero[i] = 0;
   if (tid < 256) hist[tid] = 0;
   __syncthreads();
   for (int p = tid; p < P; p += PS_THREADS) {
@@ -283,19 +286,21 @@ int permute_nblocks(int P) { return (P + PM_CHUNK - 1) / PM_CHUNK; }
 hipError_t launch_permute(const int32_t *idx, int T, int E, int k, int capacity, int bm0,
                           int bm1, int32_t *blk, int32_t *counts, int32_t *offsets,
                           int32_t *perm, int32_t *inv, int32_t *mtiles0, int32_t *mtiles1,
-                          int32_t *shared_seg, int32_t *active, hipStream_t s) {
+                          int32_t *shared_seg, int32_t *active, int32_t *zero, int nzero,
+                          hipStream_t s) {
   const int P = T * k;
+  if (!zero) nzero = 0;
   const int cap = capacity < 0 || capacity > P ? P : capacity;
   if (P <= 8 * PS_THREADS) {
     hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(PS_THREADS), 0, s, idx, P, E, T, cap,
                        bm0, bm1, counts, offsets, perm, inv, mtiles0, mtiles1, shared_seg,
-                       active);
+                       active, zero, nzero);
     return hipGetLastError();
   }
   const int nb = permute_nblocks(P);
   hipLaunchKernelGGL(permute_hist_kernel, dim3(nb), dim3(PM_CHUNK), 0, s, idx, P, E, blk);
   hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(256), 0, s, blk, nb, E, P, T, cap, bm0,
-                     bm1, counts, offsets, mtiles0, mtiles1, shared_seg, active);
+                     bm1, counts, offsets, mtiles0, mtiles1, shared_seg, active, zero, nzero);
   hipLaunchKernelGGL(permute_scatter_kernel, dim3(nb), dim3(PM_CHUNK), 0, s, idx, P, E, cap, blk,
                      offsets, perm, inv);
   return hipGetLastError();

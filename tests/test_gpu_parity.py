@@ -185,9 +185,12 @@ def test_forward_sampled_full_size(name):
     rng = np.random.default_rng(7)
     rows = sample_rows(cfg.T, rng)
     # include tokens routed to the least-loaded non-empty expert (a ragged tile)
+    # and to the last non-empty one (its tiles end the tile order: the ones a
+    # last-round K split cuts into parts)
     nz = np.nonzero(counts)[0]
     emin = nz[np.argmin(counts[nz])]
-    rows = sorted(set(rows) | set(np.nonzero(np.any(idx_ref == emin, axis=1))[0][:4].tolist()))
+    for e in (emin, nz[-1]):
+        rows = sorted(set(rows) | set(np.nonzero(np.any(idx_ref == e, axis=1))[0][:4].tolist()))
     ref = O.forward_rows(h["x"], h["W1"], h["W3"], h["W2"], rows, idx_ref[rows], gate_ref[rows],
                          shared=shared_tuple(h))
     got = f64(moe.tensor_to_numpy(y[rows]))
@@ -203,6 +206,9 @@ def test_deterministic(name):
     h, d = case(cfg, T_max=8192)
     L = layer(d, cfg)
     y1 = L(d["x"]).clone()
+    # the second call starts from a workspace full of garbage (stale arrival
+    # counters and partial tiles of the down GEMM's last-round split)
+    L._ws.fill_(0x5A)
     y2 = L(d["x"]).clone()
     torch.cuda.synchronize()
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
@@ -229,6 +235,12 @@ EDGE = [
     ("skinny_hot_expert_two_passes", 70, 256, 4, 512, 2, "bf16", 0, ("hot", 2, 100.0)),
     ("skinny_shared", 40, 256, 8, 256, 2, "bf16", 256, None),
     ("skinny_E256_k8", 64, 512, 256, 256, 8, "bf16", 0, None),
+    # long K: d = 5120 with 64-row and 256-row tiles, a 14336-wide shared expert
+    ("K5120_bm64", 64, 5120, 4, 256, 2, "bf16", 0, None),
+    ("K5120_bm256", 256, 5120, 2, 256, 1, "bf16", 0, None),
+    ("shared_K14336", 96, 256, 4, 256, 2, "bf16", 14336, None),
+    # every tile of a small down projection split into 16 K planes
+    ("kplanes_down", 64, 256, 4, 14336, 2, "bf16", 0, None),
     # vector-ALU weight streaming (at most four tokens, K a multiple of 2048)
     ("gemv_T1", 1, 2048, 8, 2048, 2, "bf16", 0, None),
     ("gemv_T2_K6144_shared", 2, 2048, 4, 6144, 2, "bf16", 2048, None),
@@ -259,6 +271,13 @@ def test_edge_cases(case_):
     err = rel_l2(f64(moe.tensor_to_numpy(y)), ref["y"])
     say(f"edge {label}: rel-L2 {err:.3e}")
     assert err <= TOL[dt]
+    if label.startswith("kplanes"):
+        # a workspace full of garbage gives the same bits
+        y1 = y.clone()
+        L._ws.fill_(0x5A)
+        y2 = L(d_["x"])
+        torch.cuda.synchronize()
+        assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
 
 
 def test_zero_tokens():
