@@ -125,8 +125,9 @@ int moe_forward(const void *x, const void *Wg, const float *bias, const void *W1
  * hipEvent_t handles: [0] before the router, [1] after the router, [2] after
  * the permutation, [3] after the row gather, [4] after the SwiGLU GEMM, [5]
  * after the down GEMM, [6] after the shared expert (if any), [7] after the
- * combine.  Same results and errors as moe_forward; MOE_EINVAL if `events`
- * or any of its handles is NULL. */
+ * combine.  A decode step (T <= 4, T * k <= 64, E <= 64) runs top-k and the
+ * grouping in one launch: [1] and [2] then both follow it.  Same results and errors as
+ * moe_forward; MOE_EINVAL if `events` or any of its handles is NULL. */
 #define MOE_NSTAGE_EVENTS 8
 int moe_forward_timed(const void *x, const void *Wg, const float *bias, const void *W1,
                       const void *W3, const void *W2, const void *Ws1, const void *Ws3,

@@ -328,25 +328,39 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
 #define MOE_MARK(i) \
   if (events && hipEventRecord((hipEvent_t)events[i], s) != hipSuccess) goto fail;
   MOE_MARK(0);
-  if ((e = moe::launch_router(dtype, x, Wg, bias, T, d, E, k, o.gate_mode, idx, gate, logits,
-                              at<float>(ws, L.off[F_RPART]), s)))
-    goto fail;
-  MOE_MARK(1);
-  if ((e = moe::launch_permute(idx, T, E, k, o.capacity, plan.bm1, plan.bm2, blk, counts,
-                               offsets, perm, inv, mt0, mt1, shseg, act, fixc,
-                               fixc ? moe::FIX_SLOTS : 0, s)))
-    goto fail;
+  if (moe::route_permute_tiny_ok(T, E, k)) {
+    // a small batch: scores, then top-k, gate and grouping in one more launch
+    if ((e = moe::launch_route_permute_tiny(dtype, x, Wg, bias, T, d, E, k, o.gate_mode,
+                                            o.capacity, plan.bm1, plan.bm2, logits, idx, gate,
+                                            counts, offsets, perm, inv, mt0, mt1, shseg, act,
+                                            fixc, fixc ? moe::FIX_SLOTS : 0,
+                                            at<float>(ws, L.off[F_RPART]), s)))
+      goto fail;
+    MOE_MARK(1);
+  } else {
+    if ((e = moe::launch_router(dtype, x, Wg, bias, T, d, E, k, o.gate_mode, idx, gate, logits,
+                                at<float>(ws, L.off[F_RPART]), s)))
+      goto fail;
+    MOE_MARK(1);
+    if ((e = moe::launch_permute(idx, T, E, k, o.capacity, plan.bm1, plan.bm2, blk, counts,
+                                 offsets, perm, inv, mt0, mt1, shseg, act, fixc,
+                                 fixc ? moe::FIX_SLOTS : 0, s)))
+      goto fail;
+  }
   MOE_MARK(2);
   if (sk.routed) {
     // few rows per expert: weight-streaming kernels; the gather rides in the first GEMM
     MOE_MARK(3);
+    // a single token activates exactly k experts (fewer only under a capacity)
+    const int nact = T == 1 ? k : 0;
     if ((e = sk.gemv ? moe::launch_gemv_swiglu(T, o.activation, x, perm, k, W1, W3, H, offsets,
-                                               act, act + E, E, d_ff, d, s)
+                                               act, act + E, E, d_ff, d, nact, s)
                      : moe::launch_skinny_swiglu(sk.mb, o.activation, x, perm, k, W1, W3, H,
                                                  offsets, act, act + E, E, d_ff, d, s)))
       goto fail;
     MOE_MARK(4);
-    if ((e = sk.gemv ? moe::launch_gemv_down(T, H, W2, Yp, offsets, act, act + E, E, d, d_ff, s)
+    if ((e = sk.gemv ? moe::launch_gemv_down(T, H, W2, Yp, offsets, act, act + E, E, d, d_ff,
+                                             nact, s)
                      : moe::launch_skinny_down(sk.mb, H, W2, Yp, offsets, act, act + E, E, d,
                                                d_ff, s)))
       goto fail;
@@ -368,10 +382,10 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
   if (shared) {
     if (sk.gemv_shared) {
       if ((e = moe::launch_gemv_swiglu(T, o.activation, x, nullptr, 1, Ws1, Ws3, Hs, shseg,
-                                       shseg + 6, shseg + 7, 1, d_ff_shared, d, s)))
+                                       shseg + 6, shseg + 7, 1, d_ff_shared, d, 1, s)))
         goto fail;
       if ((e = moe::launch_gemv_down(T, Hs, Ws2, Ys, shseg, shseg + 6, shseg + 7, 1, d,
-                                     d_ff_shared, s)))
+                                     d_ff_shared, 1, s)))
         goto fail;
     } else if (sk.shared) {
       if ((e = moe::launch_skinny_swiglu(sk.mb_shared, o.activation, x, nullptr, 1, Ws1, Ws3,

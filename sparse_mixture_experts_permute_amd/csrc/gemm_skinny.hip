@@ -324,7 +324,7 @@ template <bool SWIGLU, int R>
 hipError_t launch_gemv_r(int act, const void *A, const int32_t *perm, int kslots,
                          const void *B1, const void *B3, void *C, const int32_t *seg_off,
                          const int32_t *active, const int32_t *nactive, int G, int N, int K,
-                         hipStream_t s) {
+                         int nact, hipStream_t s) {
   const int kc = K / (GV_WAVES * GV_CHUNK);
   constexpr int NW = SWIGLU ? 2 : 1;
   // columns per workgroup: a power of two from two groups up to 256, with
@@ -336,7 +336,15 @@ hipError_t launch_gemv_r(int act, const void *A, const int32_t *perm, int kslots
 #define GV_CASE(KC_)                                                                          \
   case KC_: {                                                                                 \
     constexpr int CB = gv_cb(NW * KC_);                                                       \
-    const int cw = cpw < 2 * CB ? 2 * CB : cpw;                                               \
+    int cw = cpw < 2 * CB ? 2 * CB : cpw;                                                     \
+    if (nact > 0) {                                                                           \
+      /* known active experts: as close to one workgroup per CU as N allows */                \
+      for (int m = 1; 2 * CB * m <= N; ++m)                                                   \
+        if (N % (2 * CB * m) == 0 && (long long)nact * (N / (2 * CB * m)) <= 256) {           \
+          cw = 2 * CB * m;                                                                    \
+          break;                                                                              \
+        }                                                                                     \
+    }                                                                                         \
     if (N % cw) return hipErrorInvalidValue;                                                  \
     hipLaunchKernelGGL((gemv_kernel<SWIGLU, R, KC_>), dim3(G * (N / cw)), dim3(GV_THREADS),   \
                        0, s, a, perm, kslots, b1, b3, C, seg_off, active, nactive, N, K, cw, act); \
@@ -354,15 +362,15 @@ template <bool SWIGLU>
 hipError_t launch_gemv(int rows, int act, const void *A, const int32_t *perm, int kslots,
                        const void *B1, const void *B3, void *C, const int32_t *seg_off,
                        const int32_t *active, const int32_t *nactive, int G, int N, int K,
-                       hipStream_t s) {
+                       int nact, hipStream_t s) {
   if (rows <= 1)
     return launch_gemv_r<SWIGLU, 1>(act, A, perm, kslots, B1, B3, C, seg_off, active, nactive,
-                                    G, N, K, s);
+                                    G, N, K, nact, s);
   if (rows <= 2)
     return launch_gemv_r<SWIGLU, 2>(act, A, perm, kslots, B1, B3, C, seg_off, active, nactive,
-                                    G, N, K, s);
+                                    G, N, K, nact, s);
   return launch_gemv_r<SWIGLU, 4>(act, A, perm, kslots, B1, B3, C, seg_off, active, nactive, G,
-                                  N, K, s);
+                                  N, K, nact, s);
 }
 
 }  // namespace
@@ -392,16 +400,17 @@ bool gemv_ok(int N, int K) {
 hipError_t launch_gemv_swiglu(int rows, int act, const void *x, const int32_t *perm, int kslots,
                               const void *W1, const void *W3, void *H, const int32_t *seg_off,
                               const int32_t *active, const int32_t *nactive, int G, int N, int K,
-                              hipStream_t s) {
+                              int nact, hipStream_t s) {
   return launch_gemv<true>(rows, act, x, perm, kslots, W1, W3, H, seg_off, active, nactive, G, N,
-                           K, s);
+                           K, nact, s);
 }
 
 hipError_t launch_gemv_down(int rows, const void *Hin, const void *W2, float *Y,
                             const int32_t *seg_off, const int32_t *active,
-                            const int32_t *nactive, int G, int N, int K, hipStream_t s) {
+                            const int32_t *nactive, int G, int N, int K, int nact,
+                            hipStream_t s) {
   return launch_gemv<false>(rows, 0, Hin, nullptr, 1, W2, nullptr, Y, seg_off, active, nactive,
-                            G, N, K, s);
+                            G, N, K, nact, s);
 }
 
 }  // namespace moe

@@ -12,6 +12,19 @@ hipError_t launch_router(int dtype, const void *x, const void *Wg, const float *
                          int d, int E, int k, int gate_mode, int32_t *idx, float *gate,
                          float *logits, float *part, hipStream_t s);
 
+// Decode steps (T <= 4, T * k <= 64 pairs, E <= 64): the router's scores, then top-k,
+// gate and the grouping by expert in one more launch; outputs as
+// launch_router + launch_permute (capacity as there; zero: nzero int32
+// cleared on the way, may be NULL; part: the router's partial-score scratch).
+bool route_permute_tiny_ok(int T, int E, int k);
+hipError_t launch_route_permute_tiny(int dtype, const void *x, const void *Wg, const float *bias,
+                                     int T, int d, int E, int k, int gate_mode, int capacity,
+                                     int bm0, int bm1, float *logits, int32_t *idx, float *gate,
+                                     int32_t *counts, int32_t *offsets, int32_t *perm,
+                                     int32_t *inv, int32_t *mtiles0, int32_t *mtiles1,
+                                     int32_t *shared_seg, int32_t *active, int32_t *zero,
+                                     int nzero, float *part, hipStream_t s);
+
 int permute_nblocks(int P);
 // capacity: pairs an expert keeps (its first ones in pair order); >= T*k keeps
 // all.  Dropped pairs (and ids outside [0, E)) get inv = -1.
@@ -64,13 +77,16 @@ hipError_t launch_gemm_down(int dtype, bool dl, int bm, const void *A, const voi
 bool skinny_ok(int N, int K);
 // vector-ALU weight streaming for experts holding at most `rows` (<= 4) rows
 bool gemv_ok(int N, int K);
+// nact: the number of active experts when the host knows it (a single token
+// has exactly k), else 0; it sets how many workgroups share the columns
 hipError_t launch_gemv_swiglu(int rows, int act, const void *x, const int32_t *perm, int kslots,
                               const void *W1, const void *W3, void *H, const int32_t *seg_off,
                               const int32_t *active, const int32_t *nactive, int G, int N, int K,
-                              hipStream_t s);
+                              int nact, hipStream_t s);
 hipError_t launch_gemv_down(int rows, const void *Hin, const void *W2, float *Y,
                             const int32_t *seg_off, const int32_t *active,
-                            const int32_t *nactive, int G, int N, int K, hipStream_t s);
+                            const int32_t *nactive, int G, int N, int K, int nact,
+                            hipStream_t s);
 hipError_t launch_skinny_swiglu(int mb, int act, const void *x, const int32_t *perm, int kslots,
                                 const void *W1, const void *W3, void *H,
                                 const int32_t *seg_off, const int32_t *active,

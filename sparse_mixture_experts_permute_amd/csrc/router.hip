@@ -184,29 +184,15 @@ __global__ __launch_bounds__(256) void router_scores_narrow_kernel(
   }
 }
 
-// One wavefront per token: scores, k rounds of arg-max, softmax over the selected.
-__global__ __launch_bounds__(256) void router_topk_kernel(
-    const float *__restrict__ part, int S, const float *__restrict__ bias, int T_, int E, int k,
-    int gate_mode, int32_t *__restrict__ idx, float *__restrict__ gate,
-    float *__restrict__ logits) {
-  __shared__ float selv[4][256];
-  __shared__ int seli[4][256];
-  const int w = threadIdx.x / kWave, lane = lane_id();
-  const int t = blockIdx.x * 4 + w;
-  if (t >= T_) return;
-  float v[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int e = lane + kWave * j;
-    float l = -INFINITY;
-    if (e < E) {
-      l = 0.f;
-      for (int s = 0; s < S; ++s) l += part[((size_t)s * T_ + t) * E + e];
-      if (bias) l += bias[e];
-      if (logits) logits[(size_t)t * E + e] = l;
-    }
-    v[j] = l;
-  }
+// One wavefront, one token: k rounds of a wavefront arg-max over the scores
+// v[j] of experts lane + 64 j (-inf past E; ties go to the lower index), then
+// the gate of each pick (gate_mode: 0 softmax over the selected, 1 softmax
+// over all E, 2 sigmoid of each).  selv / seli: this wave's LDS rows for the
+// picks.  Writes idx / gate [k] of the token.
+__device__ __forceinline__ void wave_topk_gate(const float (&v)[4], int E, int k, int gate_mode,
+                                               float *selv, int *seli, int32_t *__restrict__ idx,
+                                               float *__restrict__ gate) {
+  const int lane = lane_id();
   unsigned taken = 0;
   for (int r = 0; r < k; ++r) {
     float bv = -INFINITY;
@@ -230,32 +216,161 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
     }
     if ((bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
     if (lane == 0) {
-      selv[w][r] = bv;
-      seli[w][r] = bi;
+      selv[r] = bv;
+      seli[r] = bi;
     }
   }
   // lane 0's selections become visible to the whole wave
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  const float m = selv[w][0];  // the largest logit of the token
+  const float m = selv[0];  // the largest score of the token
   float z = 0.f;
   if (gate_mode == 0) {
-    // softmax over the k selected logits
-    for (int r = lane; r < k; r += kWave) z += expf(selv[w][r] - m);
+    // softmax over the k selected scores
+    for (int r = lane; r < k; r += kWave) z += expf(selv[r] - m);
   } else if (gate_mode == 1) {
-    // softmax over all E logits (v[] holds -inf past E)
+    // softmax over all E scores (v[] holds -inf past E)
 #pragma unroll
     for (int j = 0; j < 4; ++j) z += expf(v[j] - m);
   }
 #pragma unroll
   for (int off = kWave / 2; off > 0; off >>= 1) z += __shfl_xor(z, off);
   for (int r = lane; r < k; r += kWave) {
-    idx[(size_t)t * k + r] = seli[w][r];
-    const float l = selv[w][r];
-    // gate_mode 2: logistic sigmoid of the selected logit on its own
-    gate[(size_t)t * k + r] =
-        gate_mode == 2 ? 1.0f / (1.0f + expf(-l)) : expf(l - m) / z;
+    idx[r] = seli[r];
+    const float l = selv[r];
+    // gate_mode 2: logistic sigmoid of the selected score on its own
+    gate[r] = gate_mode == 2 ? 1.0f / (1.0f + expf(-l)) : expf(l - m) / z;
+  }
+}
+
+// One wavefront per token: scores (partials summed in slice order), top-k, gate.
+__global__ __launch_bounds__(256) void router_topk_kernel(
+    const float *__restrict__ part, int S, const float *__restrict__ bias, int T_, int E, int k,
+    int gate_mode, int32_t *__restrict__ idx, float *__restrict__ gate,
+    float *__restrict__ logits) {
+  __shared__ float selv[4][256];
+  __shared__ int seli[4][256];
+  const int w = threadIdx.x / kWave, lane = lane_id();
+  const int t = blockIdx.x * 4 + w;
+  if (t >= T_) return;
+  float v[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = lane + kWave * j;
+    float l = -INFINITY;
+    if (e < E) {
+      l = 0.f;
+      for (int s = 0; s < S; ++s) l += part[((size_t)s * T_ + t) * E + e];
+      if (bias) l += bias[e];
+      if (logits) logits[(size_t)t * E + e] = l;
+    }
+    v[j] = l;
+  }
+  wave_topk_gate(v, E, k, gate_mode, selv[w], seli[w], idx + (size_t)t * k, gate + (size_t)t * k);
+}
+
+// Top-k, gate and the grouping of the pairs by expert for a decode step
+// (T <= 4 tokens, T * k <= 64 pairs, E <= 64) in one workgroup: the launch that follows the
+// score kernel (one less than top-k and permutation kernels apart).  Scores
+// are summed over the slices exactly as router_topk_kernel does; the grouping
+// is the stable counting sort of the pair ids under the capacity (the pairs an
+// expert keeps, in pair order), by one wavefront with a lane per pair.
+// Outputs as router_topk_kernel plus the permutation kernels.
+__global__ __launch_bounds__(256) void topk_permute_tiny_kernel(
+    const float *__restrict__ part, int S, const float *__restrict__ bias, int T_, int E, int k,
+    int gate_mode, int capacity, int bm0, int bm1, float *__restrict__ logits,
+    int32_t *__restrict__ idx, float *__restrict__ gate, int32_t *__restrict__ counts,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ perm, int32_t *__restrict__ inv,
+    int32_t *__restrict__ mtiles0, int32_t *__restrict__ mtiles1,
+    int32_t *__restrict__ shared_seg, int32_t *__restrict__ active, int32_t *__restrict__ zero,
+    int nzero) {
+  __shared__ float selv[4][64];
+  __shared__ int seli[4][64];
+  __shared__ int sidx[64];
+  const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
+  for (int i = tid; i < nzero; i += 256) zero[i] = 0;
+  for (int t = w; t < T_; t += 4) {
+    float v[4];
+    v[0] = -INFINITY;
+    if (lane < E) {
+      float l = 0.f;
+      for (int s = 0; s < S; ++s) l += part[((size_t)s * T_ + t) * E + lane];
+      if (bias) l += bias[lane];
+      logits[(size_t)t * E + lane] = l;
+      v[0] = l;
+    }
+    v[1] = v[2] = v[3] = -INFINITY;
+    wave_topk_gate(v, E, k, gate_mode, selv[w], seli[w], idx + (size_t)t * k,
+                   gate + (size_t)t * k);
+    if (lane < k) sidx[t * k + lane] = seli[w][lane];
+  }
+  __syncthreads();
+  if (w != 0) return;
+  // grouping by expert, one lane per pair p = t * k + j (P <= 64)
+  const int P = T_ * k;
+  const bool valid = lane < P;
+  const int e = valid ? sidx[lane] : 0;
+  // lanes holding the same expert: intersect ballots over the bits of e (< 64)
+  uint64_t same = __ballot(valid);
+#pragma unroll
+  for (int bit = 0; bit < 6; ++bit) {
+    const uint64_t ones = __ballot(valid && ((e >> bit) & 1));
+    same &= ((e >> bit) & 1) ? ones : ~ones;
+  }
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  const int rank = __popcll(same & below);  // earlier pairs of the same expert
+  // lane x < E: pairs of expert x, kept pairs, m-tiles, and exclusive prefixes
+  int hist = 0;
+  for (int x = 0; x < E; ++x) {
+    const int n = __popcll(__ballot(valid && e == x));
+    if (lane == x) hist = n;
+  }
+  const int c = lane < E ? min(hist, capacity) : 0;
+  const int c0 = (c + bm0 - 1) / bm0, c1 = (c + bm1 - 1) / bm1, ca = c > 0 ? 1 : 0;
+  int s_c = c, s_0 = c0, s_1 = c1, s_a = ca;  // inclusive scans over the lanes
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int u_c = __shfl_up(s_c, off), u_0 = __shfl_up(s_0, off);
+    const int u_1 = __shfl_up(s_1, off), u_a = __shfl_up(s_a, off);
+    if (lane >= off) {
+      s_c += u_c;
+      s_0 += u_0;
+      s_1 += u_1;
+      s_a += u_a;
+    }
+  }
+  if (lane < E) {
+    counts[lane] = c;
+    offsets[lane] = s_c - c;
+    mtiles0[lane] = s_0 - c0;
+    mtiles1[lane] = s_1 - c1;
+    if (c > 0) active[s_a - 1] = lane;
+  }
+  if (lane == E - 1) {
+    offsets[E] = s_c;
+    mtiles0[E] = s_0;
+    mtiles1[E] = s_1;
+    active[E] = s_a;
+  }
+  const int first = __shfl(s_c - c, e);  // the expert's first slot
+  if (valid) {
+    if (rank < capacity) {
+      perm[first + rank] = lane;
+      inv[lane] = first + rank;
+    } else {
+      inv[lane] = -1;
+    }
+  }
+  if (lane == 0) {
+    shared_seg[0] = 0;
+    shared_seg[1] = T_;
+    shared_seg[2] = 0;
+    shared_seg[3] = (T_ + bm0 - 1) / bm0;
+    shared_seg[4] = 0;
+    shared_seg[5] = (T_ + bm1 - 1) / bm1;
+    shared_seg[6] = 0;
+    shared_seg[7] = 1;
   }
 }
 
@@ -311,6 +426,33 @@ void launch_scores(const RouterSplit &r, const void *x, const void *Wg, int T_, 
 }
 
 }  // namespace
+
+bool route_permute_tiny_ok(int T, int E, int k) {
+  // one token per wavefront: beyond that the tokens' top-k would run in turn
+  return T >= 1 && T <= 4 && E <= 64 && T * k <= 64;
+}
+
+hipError_t launch_route_permute_tiny(int dtype, const void *x, const void *Wg, const float *bias,
+                                     int T, int d, int E, int k, int gate_mode, int capacity,
+                                     int bm0, int bm1, float *logits, int32_t *idx, float *gate,
+                                     int32_t *counts, int32_t *offsets, int32_t *perm,
+                                     int32_t *inv, int32_t *mtiles0, int32_t *mtiles1,
+                                     int32_t *shared_seg, int32_t *active, int32_t *zero,
+                                     int nzero, float *part, hipStream_t s) {
+  const int P = T * k;
+  const int cap = capacity < 0 || capacity > P ? P : capacity;
+  if (!zero) nzero = 0;
+  const int es = dtype == 1 ? 2 : 4;
+  const RouterSplit r = router_split(T, d, E, es);
+  if (dtype == 1)
+    launch_scores<bf16_t>(r, x, Wg, T, d, E, part, s);
+  else
+    launch_scores<float>(r, x, Wg, T, d, E, part, s);
+  hipLaunchKernelGGL(topk_permute_tiny_kernel, dim3(1), dim3(256), 0, s, part, r.S, bias, T, E,
+                     k, gate_mode, cap, bm0, bm1, logits, idx, gate, counts, offsets, perm, inv,
+                     mtiles0, mtiles1, shared_seg, active, zero, nzero);
+  return hipGetLastError();
+}
 
 size_t router_partial_bytes(int T, int d, int E, int esize) {
   return (size_t)router_split(T, d, E, esize).S * T * E * 4;

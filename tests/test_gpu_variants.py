@@ -52,6 +52,10 @@ CASES = [
     ("capacity_decode_T3_bf16", 3, 2048, 8, 2048, 2, "bf16", 0, 0.0, 1, 1, 1),
     ("capacity_page_cf_bf16", 512, 256, 8, 256, 2, "bf16", 0, 3.0, 0, 0, "page"),
     ("capacity_cf_0.3_bf16", 512, 256, 8, 256, 2, "bf16", 0, 3.0, 2, 0, 0.3),
+    # decode steps (T <= 4, E <= 64): top-k and grouping in one launch
+    ("tiny_sigmoid_skew_f32", 3, 128, 8, 256, 2, "f32", 0, 1.5, 2, 0, None),
+    ("tiny_E64_k16_cap3_bf16", 4, 256, 64, 256, 16, "bf16", 0, 0.0, 0, 0, 3),
+    ("tiny_E20_k3_shared_f32", 4, 192, 20, 128, 3, "f32", 64, 0.0, 1, 1, None),
 ]
 
 
