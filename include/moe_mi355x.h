@@ -126,7 +126,9 @@ int moe_forward(const void *x, const void *Wg, const float *bias, const void *W1
  * the permutation, [3] after the row gather, [4] after the SwiGLU GEMM, [5]
  * after the down GEMM, [6] after the shared expert (if any), [7] after the
  * combine.  A decode step (T <= 4, T * k <= 64, E <= 64) runs top-k and the
- * grouping in one launch: [1] and [2] then both follow it.  Same results and errors as
+ * grouping in one launch: [1] and [2] then both follow it; when its down
+ * projection streams the weights and there is no shared expert, the combine
+ * rides in that kernel: [5], [6] and [7] then all follow it.  Same results and errors as
  * moe_forward; MOE_EINVAL if `events` or any of its handles is NULL. */
 #define MOE_NSTAGE_EVENTS 8
 int moe_forward_timed(const void *x, const void *Wg, const float *bias, const void *W1,

@@ -72,7 +72,7 @@ Layout layout(int T, int d, int d_ff, int E, int k, int dffs, int dtype) {
   sz[F_MT1] = (size_t)(E + 1) * 4;
   sz[F_SHSEG] = 8 * 4;
   sz[F_ACT] = (size_t)(E + 1) * 4;
-  sz[F_FIXC] = tiles ? (size_t)moe::FIX_SLOTS * 4 : 0;
+  sz[F_FIXC] = (size_t)moe::FIX_SLOTS * 4;  // arrival counters (cleared by each forward)
   sz[F_FIXP] = moe::fix_part_bytes(tiles);
   sz[F_RPART] = moe::router_partial_bytes(T, d, E, (int)es);
   sz[F_BLK] = nb * E * 4;
@@ -319,9 +319,12 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
   float *Yp = at<float>(ws, L.off[F_YP]);
   void *Hs = at<char>(ws, L.off[F_HS]);
   float *Ys = at<float>(ws, L.off[F_YS]);
-  int32_t *fixc = L.off[F_FIXC + 1] > L.off[F_FIXC] ? at<int32_t>(ws, L.off[F_FIXC]) : nullptr;
-  const moe::FixScratch fx{fixc, fixc ? at<char>(ws, L.off[F_FIXP]) : nullptr,
-                           L.off[F_FIXP + 1] - L.off[F_FIXP]};
+  int32_t *fixc = at<int32_t>(ws, L.off[F_FIXC]);
+  const size_t fixp_bytes = L.off[F_FIXP + 1] - L.off[F_FIXP];
+  const moe::FixScratch fx{fixc, fixp_bytes ? at<char>(ws, L.off[F_FIXP]) : nullptr, fixp_bytes};
+  // single-token-scale batches without a shared expert: the down projection's
+  // last workgroups also do the combine
+  const bool fused_combine = sk.gemv && !shared;
 
   hipError_t e;
   // stage boundary i: an optional timing event recorded on the stream
@@ -333,7 +336,7 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
     if ((e = moe::launch_route_permute_tiny(dtype, x, Wg, bias, T, d, E, k, o.gate_mode,
                                             o.capacity, plan.bm1, plan.bm2, logits, idx, gate,
                                             counts, offsets, perm, inv, mt0, mt1, shseg, act,
-                                            fixc, fixc ? moe::FIX_SLOTS : 0,
+                                            fixc, moe::FIX_SLOTS,
                                             at<float>(ws, L.off[F_RPART]), s)))
       goto fail;
     MOE_MARK(1);
@@ -343,8 +346,8 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
       goto fail;
     MOE_MARK(1);
     if ((e = moe::launch_permute(idx, T, E, k, o.capacity, plan.bm1, plan.bm2, blk, counts,
-                                 offsets, perm, inv, mt0, mt1, shseg, act, fixc,
-                                 fixc ? moe::FIX_SLOTS : 0, s)))
+                                 offsets, perm, inv, mt0, mt1, shseg, act, fixc, moe::FIX_SLOTS,
+                                 s)))
       goto fail;
   }
   MOE_MARK(2);
@@ -359,10 +362,13 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
                                                  offsets, act, act + E, E, d_ff, d, s)))
       goto fail;
     MOE_MARK(4);
-    if ((e = sk.gemv ? moe::launch_gemv_down(T, H, W2, Yp, offsets, act, act + E, E, d, d_ff,
-                                             nact, s)
-                     : moe::launch_skinny_down(sk.mb, H, W2, Yp, offsets, act, act + E, E, d,
-                                               d_ff, s)))
+    if ((e = fused_combine
+                 ? moe::launch_gemv_down_combine(T, H, W2, Yp, offsets, act, act + E, E, d, d_ff,
+                                                 nact, inv, gate, T, k, y, fixc, s)
+             : sk.gemv ? moe::launch_gemv_down(T, H, W2, Yp, offsets, act, act + E, E, d, d_ff,
+                                               nact, s)
+                       : moe::launch_skinny_down(sk.mb, H, W2, Yp, offsets, act, act + E, E, d,
+                                                 d_ff, s)))
       goto fail;
     MOE_MARK(5);
   } else {
@@ -405,7 +411,8 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
     }
   }
   MOE_MARK(6);
-  if ((e = moe::launch_combine(dtype, Yp, ksplit, plane, shared ? Ys : nullptr, inv, gate, T, k,
+  if (!fused_combine &&
+      (e = moe::launch_combine(dtype, Yp, ksplit, plane, shared ? Ys : nullptr, inv, gate, T, k,
                                d, y, s)))
     goto fail;
   MOE_MARK(7);

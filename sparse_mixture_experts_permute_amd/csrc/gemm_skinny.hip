@@ -207,18 +207,41 @@ constexpr int gv_cb(int loads_per_col) {
 // KC: 1 KB chunks per wavefront (K = GV_WAVES * KC * GV_CHUNK); R: rows per
 // pass; CB: columns per group.  The workgroup owns columns c0 .. c0+cpw-1 of
 // active expert blockIdx.x / (N / cpw).
-template <bool SWIGLU, int R, int KC>
+//
+// COMBINE (down projection): the gate-weighted combine rides along.  Outputs
+// go to Yp with device-scope stores; the workgroup then counts itself in on
+// its column block (cm.cnt, zero before the launch), and the last of the
+// block's active experts to finish forms y[t][c] = sum_j gate[t][j] *
+// Yp[inv[t*k+j]][c] for all T tokens and its columns, in the combine kernel's
+// order and arithmetic, and clears the counter.
+struct GemvCombine {
+  const int32_t *inv;
+  const float *gate;
+  int T, k;
+  bf16_t *y;
+  int32_t *cnt;
+};
+template <bool SWIGLU, int R, int KC, bool COMBINE = false>
 __global__ __launch_bounds__(GV_THREADS) void gemv_kernel(
     const bf16_t *__restrict__ A, const int32_t *__restrict__ perm, int kslots,
     const bf16_t *__restrict__ B1, const bf16_t *__restrict__ B3, void *__restrict__ C,
     const int32_t *__restrict__ seg_off, const int32_t *__restrict__ active,
-    const int32_t *__restrict__ nactive, int N, int K, int cpw, int act) {
+    const int32_t *__restrict__ nactive, int N, int K, int cpw, int act, GemvCombine cm) {
+  static_assert(!(SWIGLU && COMBINE), "the combine follows the down projection");
   constexpr int NW = SWIGLU ? 2 : 1;
   constexpr int CB = gv_cb(NW * KC);
   __shared__ float red[2][GV_WAVES][CB][NW][R];
+  __shared__ int arrived;
 
   const int nblk = N / cpw;
   const int a_idx = blockIdx.x / nblk;
+  if (COMBINE && nactive[0] == 0) {
+    // every pair dropped: y is zero
+    if (a_idx == 0)
+      for (int i = threadIdx.x; i < cm.T * cpw; i += GV_THREADS)
+        cm.y[(size_t)(i / cpw) * N + (blockIdx.x % nblk) * cpw + i % cpw] = 0;
+    return;
+  }
   if (a_idx >= nactive[0]) return;
   const int e = active[a_idx];
   const int c0 = (blockIdx.x % nblk) * cpw;
@@ -297,6 +320,9 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_kernel(
           const size_t out = (size_t)(s0 + rg + r) * N + col_of(g) + cb;
           if (SWIGLU)
             reinterpret_cast<bf16_t *>(C)[out] = f32_to_bf16(gated(v[0], v[NW - 1], act));
+          else if (COMBINE)
+            __hip_atomic_store(reinterpret_cast<float *>(C) + out, v[0], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
           else
             reinterpret_cast<float *>(C)[out] = v[0];
         }
@@ -318,13 +344,38 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_kernel(
     compute(wb, g + 1, 1);
     lds_barrier();
   }
+  if constexpr (COMBINE) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's outputs are in memory
+    __syncthreads();
+    const int blk = blockIdx.x % nblk;
+    if (tid == 0)
+      arrived = __hip_atomic_fetch_add(&cm.cnt[blk], 1, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (arrived != nactive[0] - 1) return;
+    const float *Yp = reinterpret_cast<const float *>(C);
+    for (int i = tid; i < cm.T * cpw; i += GV_THREADS) {
+      const int t = i / cpw, c = c0 + i % cpw;
+      float acc = 0.f;
+      for (int j = 0; j < cm.k; ++j) {
+        const int slot = cm.inv[(size_t)t * cm.k + j];
+        if (slot < 0) continue;
+        const float v = __hip_atomic_load(Yp + (size_t)slot * N + c, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+        acc = fmaf(cm.gate[(size_t)t * cm.k + j], v, acc);
+      }
+      cm.y[(size_t)t * N + c] = f32_to_bf16(acc);
+    }
+    if (tid == 0)
+      __hip_atomic_store(&cm.cnt[blk], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
-template <bool SWIGLU, int R>
+template <bool SWIGLU, int R, bool COMBINE = false>
 hipError_t launch_gemv_r(int act, const void *A, const int32_t *perm, int kslots,
                          const void *B1, const void *B3, void *C, const int32_t *seg_off,
                          const int32_t *active, const int32_t *nactive, int G, int N, int K,
-                         int nact, hipStream_t s) {
+                         int nact, const GemvCombine &cm, hipStream_t s) {
   const int kc = K / (GV_WAVES * GV_CHUNK);
   constexpr int NW = SWIGLU ? 2 : 1;
   // columns per workgroup: a power of two from two groups up to 256, with
@@ -346,8 +397,10 @@ hipError_t launch_gemv_r(int act, const void *A, const int32_t *perm, int kslots
         }                                                                                     \
     }                                                                                         \
     if (N % cw) return hipErrorInvalidValue;                                                  \
-    hipLaunchKernelGGL((gemv_kernel<SWIGLU, R, KC_>), dim3(G * (N / cw)), dim3(GV_THREADS),   \
-                       0, s, a, perm, kslots, b1, b3, C, seg_off, active, nactive, N, K, cw, act); \
+    if (COMBINE && N / cw > FIX_SLOTS) return hipErrorInvalidValue;                           \
+    hipLaunchKernelGGL((gemv_kernel<SWIGLU, R, KC_, COMBINE>), dim3(G * (N / cw)),            \
+                       dim3(GV_THREADS), 0, s, a, perm, kslots, b1, b3, C, seg_off, active,    \
+                       nactive, N, K, cw, act, cm);                                            \
     break;                                                                                    \
   }
   switch (kc) {
@@ -358,19 +411,19 @@ hipError_t launch_gemv_r(int act, const void *A, const int32_t *perm, int kslots
   return hipGetLastError();
 }
 
-template <bool SWIGLU>
+template <bool SWIGLU, bool COMBINE = false>
 hipError_t launch_gemv(int rows, int act, const void *A, const int32_t *perm, int kslots,
                        const void *B1, const void *B3, void *C, const int32_t *seg_off,
                        const int32_t *active, const int32_t *nactive, int G, int N, int K,
-                       int nact, hipStream_t s) {
+                       int nact, const GemvCombine &cm, hipStream_t s) {
   if (rows <= 1)
-    return launch_gemv_r<SWIGLU, 1>(act, A, perm, kslots, B1, B3, C, seg_off, active, nactive,
-                                    G, N, K, nact, s);
+    return launch_gemv_r<SWIGLU, 1, COMBINE>(act, A, perm, kslots, B1, B3, C, seg_off, active,
+                                             nactive, G, N, K, nact, cm, s);
   if (rows <= 2)
-    return launch_gemv_r<SWIGLU, 2>(act, A, perm, kslots, B1, B3, C, seg_off, active, nactive,
-                                    G, N, K, nact, s);
-  return launch_gemv_r<SWIGLU, 4>(act, A, perm, kslots, B1, B3, C, seg_off, active, nactive, G,
-                                  N, K, nact, s);
+    return launch_gemv_r<SWIGLU, 2, COMBINE>(act, A, perm, kslots, B1, B3, C, seg_off, active,
+                                             nactive, G, N, K, nact, cm, s);
+  return launch_gemv_r<SWIGLU, 4, COMBINE>(act, A, perm, kslots, B1, B3, C, seg_off, active,
+                                           nactive, G, N, K, nact, cm, s);
 }
 
 }  // namespace
@@ -402,7 +455,7 @@ hipError_t launch_gemv_swiglu(int rows, int act, const void *x, const int32_t *p
                               const int32_t *active, const int32_t *nactive, int G, int N, int K,
                               int nact, hipStream_t s) {
   return launch_gemv<true>(rows, act, x, perm, kslots, W1, W3, H, seg_off, active, nactive, G, N,
-                           K, nact, s);
+                           K, nact, GemvCombine{}, s);
 }
 
 hipError_t launch_gemv_down(int rows, const void *Hin, const void *W2, float *Y,
@@ -410,7 +463,17 @@ hipError_t launch_gemv_down(int rows, const void *Hin, const void *W2, float *Y,
                             const int32_t *nactive, int G, int N, int K, int nact,
                             hipStream_t s) {
   return launch_gemv<false>(rows, 0, Hin, nullptr, 1, W2, nullptr, Y, seg_off, active, nactive,
-                            G, N, K, nact, s);
+                            G, N, K, nact, GemvCombine{}, s);
+}
+
+hipError_t launch_gemv_down_combine(int rows, const void *Hin, const void *W2, float *Y,
+                                    const int32_t *seg_off, const int32_t *active,
+                                    const int32_t *nactive, int G, int N, int K, int nact,
+                                    const int32_t *inv, const float *gate, int T, int k, void *y,
+                                    int32_t *cnt, hipStream_t s) {
+  const GemvCombine cm{inv, gate, T, k, (bf16_t *)y, cnt};
+  return launch_gemv<false, true>(rows, 0, Hin, nullptr, 1, W2, nullptr, Y, seg_off, active,
+                                  nactive, G, N, K, nact, cm, s);
 }
 
 }  // namespace moe

@@ -87,6 +87,15 @@ hipError_t launch_gemv_down(int rows, const void *Hin, const void *W2, float *Y,
                             const int32_t *seg_off, const int32_t *active,
                             const int32_t *nactive, int G, int N, int K, int nact,
                             hipStream_t s);
+// launch_gemv_down that also writes y [T][N] (bf16) as launch_combine would
+// (no shared expert): the last workgroup of each column block combines the
+// T tokens' k outputs.  cnt: FIX_SLOTS counters, zero before the launch (the
+// kernel leaves them zero).
+hipError_t launch_gemv_down_combine(int rows, const void *Hin, const void *W2, float *Y,
+                                    const int32_t *seg_off, const int32_t *active,
+                                    const int32_t *nactive, int G, int N, int K, int nact,
+                                    const int32_t *inv, const float *gate, int T, int k, void *y,
+                                    int32_t *cnt, hipStream_t s);
 hipError_t launch_skinny_swiglu(int mb, int act, const void *x, const int32_t *perm, int kslots,
                                 const void *W1, const void *W3, void *H,
                                 const int32_t *seg_off, const int32_t *active,

@@ -56,6 +56,8 @@ CASES = [
     ("tiny_sigmoid_skew_f32", 3, 128, 8, 256, 2, "f32", 0, 1.5, 2, 0, None),
     ("tiny_E64_k16_cap3_bf16", 4, 256, 64, 256, 16, "bf16", 0, 0.0, 0, 0, 3),
     ("tiny_E20_k3_shared_f32", 4, 192, 20, 128, 3, "f32", 64, 0.0, 1, 1, None),
+    # weight-streaming down projection with the combine inside, every pair dropped
+    ("capacity_0_gemv_T2_bf16", 2, 2048, 8, 2048, 2, "bf16", 0, 0.0, 0, 0, 0),
 ]
 
 
