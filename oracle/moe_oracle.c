@@ -45,6 +45,8 @@
  *                     formulation recomputed in numpy)
  *   orc_keep          pinned (brute force on tiny inputs; no-drop case)
  *   orc_capacity      pinned (the two worked numbers of [SMoE] 2.4)
+ *   orc_entropy       pinned (closed forms; torch softmax + entr)
+ *   orc_route_entropy pinned (per-token torch.topk of the tempered softmax)
  */
 #include <math.h>
 #ifdef _OPENMP
@@ -188,6 +190,75 @@ void orc_gate_mode(const double *logits, const int32_t *idx, long T, int E,
     }
 }
 
+/* Entropy-aware routing [OVW 4.1, the entropy-controlled strategy]: the
+ * probabilities are a temperature-scaled softmax over all E scores,
+ * p_e = exp(l_e / tau) / sum_e' exp(l_e' / tau) (tau = 0.1 on the page); the
+ * token's entropy H = -sum_e p_e ln p_e decides its k: the larger k when
+ * H > threshold (0.8 on the page), else one less (the page's 3 and 2).
+ * orc_entropy: H per token, computed as ln Z - (1/Z) sum_e w_e u_e with
+ * u_e = (l_e - m) / tau, w_e = exp(u_e), m the largest score, Z = sum w_e,
+ * which is -sum p ln p rewritten so that p = 0 contributes 0. */
+#define ORC_ENTROPY_TAU 0.1
+#define ORC_ENTROPY_THRESHOLD 0.8
+void orc_entropy(const double *logits, long T, int E, double tau, double *H)
+{
+    for (long t = 0; t < T; ++t) {
+        const double *l = logits + (size_t)t * E;
+        double m = l[0];
+        for (int e = 1; e < E; ++e)
+            if (l[e] > m)
+                m = l[e];
+        double z = 0.0, s1 = 0.0;
+        for (int e = 0; e < E; ++e) {
+            double u = (l[e] - m) / tau;
+            double w = exp(u);
+            z += w;
+            s1 += w * u;
+        }
+        H[t] = log(z) - s1 / z;
+    }
+}
+
+/* The routing of [OVW 4.1]: idx [T][k] holds the token's top k_t experts by
+ * score (= by probability; descending, ties to the lower index), k_t = k when
+ * H > threshold else k - 1, and -1 in the slot past k_t; gate [T][k] the
+ * selected probabilities p_e as they are (no renormalisation; the page
+ * returns the top-k values of the probabilities), 0 in an empty slot.
+ * Reading: the page computes k per token but then takes the batch's largest
+ * k for every token; the per-token k is used (the page's +12% compute over
+ * top-2 fits only a per-token choice). */
+int orc_route_entropy(const double *logits, long T, int E, int k, double tau,
+                      double threshold, int32_t *idx, double *gate)
+{
+    if (k < 2 || k > E)
+        return -1;
+    double *H = malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+    orc_entropy(logits, T, E, tau, H);
+    orc_topk(logits, T, E, k, idx);
+    for (long t = 0; t < T; ++t) {
+        const double *l = logits + (size_t)t * E;
+        const int kt = H[t] > threshold ? k : k - 1;
+        double m = l[0];
+        for (int e = 1; e < E; ++e)
+            if (l[e] > m)
+                m = l[e];
+        double z = 0.0;
+        for (int e = 0; e < E; ++e)
+            z += exp((l[e] - m) / tau);
+        for (int j = 0; j < k; ++j) {
+            size_t q = (size_t)t * k + j;
+            if (j < kt) {
+                gate[q] = exp((l[idx[q]] - m) / tau) / z;
+            } else {
+                idx[q] = -1;
+                gate[q] = 0.0;
+            }
+        }
+    }
+    free(H);
+    return 0;
+}
+
 /* Expert capacity [SMoE 2.4]: an expert takes at most min(k*T, floor(cf*T))
  * of a batch's T tokens (the page's two examples: batch 32, k=2 -> min(64,
  * 1.2*32); batch 16 -> 1.2*16 = 19). */
@@ -209,6 +280,10 @@ void orc_keep(const int32_t *idx, long T, int E, int k, long capacity,
     long *seen = calloc((size_t)E, sizeof(long));
     for (long p = 0; p < T * (long)k; ++p) {
         int e = idx[p];
+        if (e < 0 || e >= E) { /* an empty slot (entropy-aware k) */
+            keep[p] = 0;
+            continue;
+        }
         keep[p] = seen[e] < capacity ? 1 : 0;
         seen[e] += 1;
     }
@@ -297,7 +372,8 @@ void orc_swiglu_row(const void *x, int dt, long t, int d, const void *W1,
  *   Yp[s] = FFN_e(x_t) with p = perm[s], t = p / k, e = idx[p];
  *   y[t]  = sum_{j<k, pair kept} gate[t][j] * Yp[inv[t*k+j]]   (j ascending)
  *           + shared FFN(x_t) with weight 1 when Ws1 != NULL [CH10 10.5].
- * gate_mode (orc_gate_mode), act (swiglu) and capacity (orc_keep; a value
+ * gate_mode (orc_gate_mode; 3: orc_route_entropy with the page's tau and
+ * threshold), act (swiglu) and capacity (orc_keep; a value
  * >= T*k drops nothing) select the variants; only kept pairs are placed, so
  * counts/offsets/perm cover the kept pairs and inv[p] = -1 for a dropped one.
  * Routing comes from `logits_in` when given (e.g. another implementation's
@@ -327,8 +403,17 @@ int orc_forward_ex(const void *x, const void *Wg, const float *bias,
     int32_t *perm = malloc(sizeof(int32_t) * (size_t)(P > 0 ? P : 1));
     int32_t *inv = malloc(sizeof(int32_t) * (size_t)(P > 0 ? P : 1));
     int32_t *keep = malloc(sizeof(int32_t) * (size_t)(P > 0 ? P : 1));
-    orc_topk(logits, T, E, k, idx);
-    orc_gate_mode(logits, idx, T, E, k, gate_mode, gate);
+    if (gate_mode == 3) {
+        if (orc_route_entropy(logits, T, E, k, ORC_ENTROPY_TAU, ORC_ENTROPY_THRESHOLD,
+                              idx, gate) != 0) {
+            free(logits); free(idx); free(gate); free(counts); free(offsets);
+            free(perm); free(inv); free(keep);
+            return -1;
+        }
+    } else {
+        orc_topk(logits, T, E, k, idx);
+        orc_gate_mode(logits, idx, T, E, k, gate_mode, gate);
+    }
     orc_keep(idx, T, E, k, capacity, keep);
     /* counts and the stable grouping over the kept pairs only */
     for (int e = 0; e < E; ++e)
@@ -383,7 +468,7 @@ int orc_forward_ex(const void *x, const void *Wg, const float *bias,
             for (int j = 0; j < k; ++j) {
                 int32_t sl = inv[(size_t)t * k + j];
                 if (sl < 0)
-                    continue; /* dropped by the capacity limit */
+                    continue; /* dropped by the capacity limit, or an empty slot */
                 double g = gate[(size_t)t * k + j];
                 const double *yp = Yp + (size_t)sl * d;
                 for (int c = 0; c < d; ++c)
@@ -472,10 +557,10 @@ void orc_forward_rows(const void *x, const void *W1, const void *W3,
                 yr[c] = 0.0;
             for (int j = 0; j < k; ++j) {
                 int e = idx[(size_t)r * k + j];
-                size_t eo = (size_t)e * dff * d;
                 double g = gate[(size_t)r * k + j];
-                if (g == 0.0)
-                    continue; /* a pair dropped by a capacity limit */
+                if (g == 0.0 || e < 0)
+                    continue; /* dropped by a capacity limit, or an empty slot */
+                size_t eo = (size_t)e * dff * d;
                 swiglu(xr, d, dff, W1, eo, W3, eo, W2, eo, dt, act, h, wrow, o);
                 for (int c = 0; c < d; ++c)
                     yr[c] += g * o[c];

@@ -22,7 +22,9 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 
 F32, BF16 = 0, 1
 # gate variants (orc_gate_mode) and expert activations (swiglu in moe_oracle.c)
-GATE_SOFTMAX_TOPK, GATE_SOFTMAX_ALL, GATE_SIGMOID = 0, 1, 2
+GATE_SOFTMAX_TOPK, GATE_SOFTMAX_ALL, GATE_SIGMOID, GATE_ENTROPY = 0, 1, 2, 3
+# the entropy-aware routing's temperature and entropy threshold as printed
+ENTROPY_TAU, ENTROPY_THRESHOLD = 0.1, 0.8
 ACT_SWIGLU, ACT_GLU_SIGMOID = 0, 1
 
 
@@ -60,6 +62,10 @@ def _bind(path: str):
     L.orc_capacity.argtypes = [ctypes.c_long, ctypes.c_int, ctypes.c_double]
     L.orc_capacity.restype = ctypes.c_long
     L.orc_keep.argtypes = [i32p, ctypes.c_long, ctypes.c_int, ctypes.c_int, ctypes.c_long, i32p]
+    L.orc_entropy.argtypes = [f64p, ctypes.c_long, ctypes.c_int, ctypes.c_double, f64p]
+    L.orc_route_entropy.argtypes = [f64p, ctypes.c_long, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_double, ctypes.c_double, i32p, f64p]
+    L.orc_route_entropy.restype = ctypes.c_int
     L.orc_forward_ex.argtypes = ([vp, vp, f32p, vp, vp, vp, vp, vp, vp, ctypes.c_int,
                                   ctypes.c_long, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -158,6 +164,28 @@ def gate_mode(lg, idx, mode):
     return g
 
 
+def entropy(lg, tau=ENTROPY_TAU):
+    """Entropy (natural log) of each token's softmax(logits / tau) over all experts."""
+    lg = _c(lg, np.float64)
+    T, E = lg.shape
+    H = np.empty(T, np.float64)
+    lib().orc_entropy(_ptr(lg), T, E, float(tau), _ptr(H))
+    return H
+
+
+def route_entropy(lg, k, tau=ENTROPY_TAU, threshold=ENTROPY_THRESHOLD):
+    """(idx, gate) of the entropy-aware routing: k experts where the entropy is
+    above the threshold, else k - 1 (the last slot then holds idx -1, gate 0)."""
+    lg = _c(lg, np.float64)
+    T, E = lg.shape
+    idx = np.empty((T, k), np.int32)
+    g = np.empty((T, k), np.float64)
+    if lib().orc_route_entropy(_ptr(lg), T, E, k, float(tau), float(threshold), _ptr(idx),
+                               _ptr(g)) != 0:
+        raise ValueError("entropy-aware routing needs 2 <= k <= E")
+    return idx, g
+
+
 def capacity(T, k, cf) -> int:
     """Per-expert capacity min(k*T, floor(cf*T))."""
     return int(lib().orc_capacity(T, k, float(cf)))
@@ -175,6 +203,8 @@ def keep(idx, E, cap):
 def route(x, Wg, k, bias=None, logits_in=None, gate_mode_=GATE_SOFTMAX_TOPK):
     """(logits, idx, gate) with the oracle's own fp64 logits or given ones."""
     lg = logits(x, Wg, bias) if logits_in is None else _c(logits_in, np.float64)
+    if gate_mode_ == GATE_ENTROPY:
+        return (lg,) + route_entropy(lg, k)
     idx = topk(lg, k)
     return lg, idx, gate_mode(lg, idx, gate_mode_)
 

@@ -314,11 +314,61 @@ def check_capacity():
         np.testing.assert_array_equal(out["y"], full["y"])  # cap = T*k drops nothing
 
 
+def check_entropy_routing():
+    # "Mixtral 8x7B model architecture" section 4.1 (entropy-controlled
+    # routing): closed forms of the entropy first
+    tau = O.ENTROPY_TAU
+    for E in (2, 8, 33):
+        H = O.entropy(np.full((3, E), 0.7), tau)
+        np.testing.assert_allclose(H, np.log(E), rtol=1e-14)
+    one_hot = np.zeros((1, 8))
+    one_hot[0, 5] = 50.0  # every other probability underflows to exactly 0
+    assert abs(O.entropy(one_hot, tau)[0]) < 1e-12
+    two = np.zeros((1, 6))
+    two[0, [1, 4]] = 40.0  # two equal winners far above the rest: ln 2
+    np.testing.assert_allclose(O.entropy(two, tau), np.log(2.0), rtol=1e-12)
+    # against torch: entropy of the tempered softmax, and per token the top-k_t
+    # of the probabilities with k_t = 3 above 0.8, else 2 (the page's numbers)
+    rng = np.random.default_rng(33)
+    for E, k, scale in ((8, 3, 0.15), (16, 3, 0.3), (5, 2, 0.1)):
+        lg = rng.standard_normal((300, E)) * scale
+        probs = torch.softmax(torch.from_numpy(lg) / tau, dim=-1)
+        H_ref = torch.special.entr(probs).sum(dim=-1).numpy()
+        np.testing.assert_allclose(O.entropy(lg, tau), H_ref, rtol=1e-12, atol=1e-13)
+        idx, gate = O.route_entropy(lg, k)
+        hi = H_ref > O.ENTROPY_THRESHOLD
+        assert hi.any() and (~hi).any(), "the sample should straddle the threshold"
+        for t in range(lg.shape[0]):
+            kt = k if hi[t] else k - 1
+            v, ix = torch.topk(probs[t], kt)
+            np.testing.assert_array_equal(idx[t, :kt], ix.numpy())
+            np.testing.assert_allclose(gate[t, :kt], v.numpy(), rtol=1e-12, atol=1e-15)
+            assert np.all(idx[t, kt:] == -1) and np.all(gate[t, kt:] == 0.0)
+    # the layer: an empty slot adds nothing and holds no slot of the grouping
+    inp = tiny(40, 24, 6, 16, 3, "f32", seed=44)
+    lg = rng.standard_normal((40, 6)) * 0.2
+    out = O.forward(inp["x"], inp["Wg"], inp["W1"], inp["W3"], inp["W2"], 3, logits_in=lg,
+                    gate_mode=O.GATE_ENTROPY)
+    idx, gate = O.route_entropy(lg, 3)
+    np.testing.assert_array_equal(out["idx"], idx)
+    valid = idx.reshape(-1) >= 0
+    assert np.all(out["inv"][~valid] == -1) and int(out["offsets"][-1]) == int(valid.sum())
+    np.testing.assert_array_equal(out["counts"], np.bincount(idx.reshape(-1)[valid], minlength=6))
+    ref = np.zeros((40, 24))
+    for t in range(40):
+        for j in range(3):
+            if idx[t, j] >= 0:
+                ref[t] += gate[t, j] * O.expert_row(inp["x"], t, inp["W1"], inp["W3"], inp["W2"],
+                                                    idx[t, j])
+    np.testing.assert_allclose(out["y"], ref, rtol=1e-12, atol=1e-14)
+
+
 CHECKS = [check_logits, check_topk_bruteforce, check_topk_duplicate_rows, check_gates,
           check_counts_and_permutation, check_dense_special_case,
           check_all_experts_special_case, check_shared_expert, check_invariants,
           check_given_logits_and_rows, check_page_numbers, check_gate_variants,
-          check_glu_sigmoid_dense, check_fused_weight_formulation, check_capacity]
+          check_glu_sigmoid_dense, check_fused_weight_formulation, check_capacity,
+          check_entropy_routing]
 
 
 @pytest.mark.parametrize("check", CHECKS, ids=[c.__name__ for c in CHECKS])
@@ -341,7 +391,16 @@ MUTANTS = [
     ("capacity_keeps_last", "keep[p] = seen[e] < capacity ? 1 : 0;",
      "keep[p] = 0;\n        { long tot = 0; for (long q = 0; q < T * (long)k; ++q) tot += idx[q] == e;\n          keep[p] = tot - seen[e] <= capacity ? 1 : 0; }"),
     ("capacity_rounds_up", "long c = (long)floor(cf * (double)T);", "long c = (long)ceil(cf * (double)T);"),
-    ("dropped_pairs_placed", "if (!keep[p]) {", "if (0) {"),
+    # (empty slots stay skipped: placing idx -1 would write outside the arrays)
+    ("dropped_pairs_placed", "if (!keep[p]) {", "if (idx[p] < 0) {"),
+    ("entropy_tau_multiplied", "double u = (l[e] - m) / tau;", "double u = (l[e] - m) * tau;"),
+    ("entropy_sign", "H[t] = log(z) - s1 / z;", "H[t] = log(z) + s1 / z;"),
+    ("entropy_k_swapped", "const int kt = H[t] > threshold ? k : k - 1;",
+     "const int kt = H[t] > threshold ? k - 1 : k;"),
+    ("entropy_gate_untempered", "gate[q] = exp((l[idx[q]] - m) / tau) / z;",
+     "gate[q] = exp(l[idx[q]] - m) / z;"),
+    ("entropy_empty_slot_kept", "idx[q] = -1;\n                gate[q] = 0.0;",
+     "gate[q] = 0.0;"),
     ("w3_for_w1", "row_to_double(W1, dt, o1 + (size_t)n * d, d, wrow);",
      "row_to_double(W3, dt, o3 + (size_t)n * d, d, wrow);"),
     ("w2_transposed", "row_to_double(W2, dt, o2 + (size_t)j * dff, dff, wrow);\n        out[j] = dot(h, wrow, dff);",
