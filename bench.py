@@ -361,7 +361,9 @@ def main():
                 ("capacity_1.2x_mean_load_skew", skew, dict(capacity=cap)),
                 ("gate_softmax_all", cfg, dict(gate_mode=moe.GATE_SOFTMAX_ALL)),
                 ("sigmoid_gate_sigmoid_glu", cfg,
-                 dict(gate_mode=moe.GATE_SIGMOID, activation=moe.ACT_GLU_SIGMOID))]:
+                 dict(gate_mode=moe.GATE_SIGMOID, activation=moe.ACT_GLU_SIGMOID)),
+                # entropy-aware k: 3 slots, a token takes 3 or 2 experts
+                ("entropy_k3_or_2", cfg.with_(k=3), dict(gate_mode=moe.GATE_ENTROPY))]:
             r3 = run_variant(c2, dev, 5, 2, **kw)
             flop = 6.0 * c2.d * c2.d_ff * r3["kept"]
             v = dict(variant=label, workload=c2.name, options=kw, ms_per_step=round(r3["ms"], 4),

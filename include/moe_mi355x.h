@@ -150,6 +150,17 @@ int moe_forward_timed(const void *x, const void *Wg, const float *bias, const vo
  *              MOE_GATE_SIGMOID       logistic sigmoid of each selected logit:
  *                                     the numpy function of "Trillion-parameter
  *                                     MoE ... 7 expert configs measured"
+ *              MOE_GATE_ENTROPY       entropy-aware k ("Mixtral 8x7B model
+ *                                     architecture", section 4.1): p =
+ *                                     softmax(logits / 0.1) over all E; a token
+ *                                     whose entropy -sum p ln p exceeds 0.8
+ *                                     takes k experts, otherwise k - 1 (the
+ *                                     page's 3 and 2; needs k >= 2); gates are
+ *                                     the selected p as they are.  The unused
+ *                                     slot holds idx -1 and gate 0 and is
+ *                                     placed nowhere (inv -1).  The page takes
+ *                                     the batch's largest k for every token;
+ *                                     here each token keeps its own.
  *   activation MOE_ACT_SWIGLU         W2( SiLU(W1 x) * (W3 x) )  (default)
  *              MOE_ACT_GLU_SIGMOID    W2( sigmoid(W1 x) * (W3 x) ): the same
  *                                     numpy function's gated projection (its
@@ -160,7 +171,12 @@ int moe_forward_timed(const void *x, const void *Wg, const float *bias, const vo
  *              pairs go), a dropped pair contributes nothing and the token's
  *              other gates are not renormalised.  capacity < 0: no limit.
  * ------------------------------------------------------------------------ */
-enum { MOE_GATE_SOFTMAX_TOPK = 0, MOE_GATE_SOFTMAX_ALL = 1, MOE_GATE_SIGMOID = 2 };
+enum {
+    MOE_GATE_SOFTMAX_TOPK = 0,
+    MOE_GATE_SOFTMAX_ALL = 1,
+    MOE_GATE_SIGMOID = 2,
+    MOE_GATE_ENTROPY = 3
+};
 enum { MOE_ACT_SWIGLU = 0, MOE_ACT_GLU_SIGMOID = 1 };
 
 typedef struct {
@@ -175,7 +191,7 @@ typedef struct {
 int moe_capacity(int T, int k, double capacity_factor);
 
 /* moe_route with a gate variant (gate_mode as above); MOE_EINVAL for an
- * unknown mode. */
+ * unknown mode, or MOE_GATE_ENTROPY with k < 2. */
 int moe_route_ex(const void *x, const void *Wg, const float *bias, int T, int d, int E, int k,
                  int dtype, int gate_mode, int32_t *idx, float *gate, float *logits,
                  void *workspace, size_t workspace_bytes, void *stream);

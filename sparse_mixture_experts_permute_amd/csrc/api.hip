@@ -181,7 +181,8 @@ int moe_route_ex(const void *x, const void *Wg, const float *bias, int T, int d,
                  int dtype, int gate_mode, int32_t *idx, float *gate, float *logits,
                  void *workspace, size_t workspace_bytes, void *stream) {
   if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_EDTYPE;
-  if (gate_mode < MOE_GATE_SOFTMAX_TOPK || gate_mode > MOE_GATE_SIGMOID) return MOE_EINVAL;
+  if (gate_mode < MOE_GATE_SOFTMAX_TOPK || gate_mode > MOE_GATE_ENTROPY) return MOE_EINVAL;
+  if (gate_mode == MOE_GATE_ENTROPY && k < 2) return MOE_EINVAL;
   if (T < 0 || E < 1 || E > 256 || k < 1 || k > E || d < 64 || d % 64) return MOE_EINVAL;
   if ((long long)T * E >= (1LL << 31)) return MOE_EINVAL;
   if (T == 0) return MOE_OK;
@@ -281,7 +282,8 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
                  void *y, void *stream, void *const *events) {
   if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_EDTYPE;
   const moe_options o = opt ? *opt : moe_options{MOE_GATE_SOFTMAX_TOPK, MOE_ACT_SWIGLU, -1};
-  if (o.gate_mode < MOE_GATE_SOFTMAX_TOPK || o.gate_mode > MOE_GATE_SIGMOID) return MOE_EINVAL;
+  if (o.gate_mode < MOE_GATE_SOFTMAX_TOPK || o.gate_mode > MOE_GATE_ENTROPY) return MOE_EINVAL;
+  if (o.gate_mode == MOE_GATE_ENTROPY && k < 2) return MOE_EINVAL;
   if (o.activation != MOE_ACT_SWIGLU && o.activation != MOE_ACT_GLU_SIGMOID) return MOE_EINVAL;
   if (!dims_ok(T, d, d_ff, E, k, d_ff_shared)) return MOE_EINVAL;
   const bool shared = d_ff_shared > 0;

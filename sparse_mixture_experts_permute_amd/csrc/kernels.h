@@ -7,7 +7,8 @@ namespace moe {
 
 size_t router_partial_bytes(int T, int d, int E, int esize);
 // gate_mode: 0 softmax over the selected logits, 1 softmax over all E (no
-// renormalisation), 2 sigmoid of each selected logit
+// renormalisation), 2 sigmoid of each selected logit, 3 entropy-aware k (an
+// unused slot gets idx -1, gate 0)
 hipError_t launch_router(int dtype, const void *x, const void *Wg, const float *bias, int T,
                          int d, int E, int k, int gate_mode, int32_t *idx, float *gate,
                          float *logits, float *part, hipStream_t s);

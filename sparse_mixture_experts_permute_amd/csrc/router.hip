@@ -187,8 +187,18 @@ __global__ __launch_bounds__(256) void router_scores_narrow_kernel(
 // One wavefront, one token: k rounds of a wavefront arg-max over the scores
 // v[j] of experts lane + 64 j (-inf past E; ties go to the lower index), then
 // the gate of each pick (gate_mode: 0 softmax over the selected, 1 softmax
-// over all E, 2 sigmoid of each).  selv / seli: this wave's LDS rows for the
-// picks.  Writes idx / gate [k] of the token.
+// over all E, 2 sigmoid of each, 3 entropy-aware: see below).  selv / seli:
+// this wave's LDS rows for the picks.  Writes idx / gate [k] of the token.
+//
+// Entropy-aware routing ("Mixtral 8x7B model architecture", section 4.1):
+// p = softmax(v / tau) over all E with tau = 0.1; the token keeps k experts
+// when the entropy -sum p ln p exceeds 0.8, else k - 1 (the page's 3 and 2;
+// per token, see the reading of that page), the gates are the selected p as
+// they are, and an empty slot gets idx -1 (placed nowhere) and gate 0.  The
+// entropy is evaluated as ln z - (sum w u) / z with u = (v - max) / tau,
+// w = exp(u), z = sum w, so a probability that underflows contributes 0.
+constexpr float ENTROPY_TAU = 0.1f;
+constexpr float ENTROPY_THRESHOLD = 0.8f;
 __device__ __forceinline__ void wave_topk_gate(const float (&v)[4], int E, int k, int gate_mode,
                                                float *selv, int *seli, int32_t *__restrict__ idx,
                                                float *__restrict__ gate) {
@@ -236,6 +246,29 @@ __device__ __forceinline__ void wave_topk_gate(const float (&v)[4], int E, int k
   }
 #pragma unroll
   for (int off = kWave / 2; off > 0; off >>= 1) z += __shfl_xor(z, off);
+  if (gate_mode == 3) {
+    float zt = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (lane + kWave * j < E) {
+        const float u = (v[j] - m) / ENTROPY_TAU;
+        const float w = expf(u);
+        zt += w;
+        s1 += w * u;
+      }
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+      zt += __shfl_xor(zt, off);
+      s1 += __shfl_xor(s1, off);
+    }
+    const float H = logf(zt) - s1 / zt;
+    const int kt = H > ENTROPY_THRESHOLD ? k : k - 1;
+    for (int r = lane; r < k; r += kWave) {
+      idx[r] = r < kt ? seli[r] : -1;
+      gate[r] = r < kt ? expf((selv[r] - m) / ENTROPY_TAU) / zt : 0.f;
+    }
+    return;
+  }
   for (int r = lane; r < k; r += kWave) {
     idx[r] = seli[r];
     const float l = selv[r];
@@ -303,14 +336,16 @@ __global__ __launch_bounds__(256) void topk_permute_tiny_kernel(
     v[1] = v[2] = v[3] = -INFINITY;
     wave_topk_gate(v, E, k, gate_mode, selv[w], seli[w], idx + (size_t)t * k,
                    gate + (size_t)t * k);
-    if (lane < k) sidx[t * k + lane] = seli[w][lane];
+    // lane r wrote idx[r] (k <= 64): its own store, read back in program order
+    if (lane < k) sidx[t * k + lane] = idx[(size_t)t * k + lane];
   }
   __syncthreads();
   if (w != 0) return;
   // grouping by expert, one lane per pair p = t * k + j (P <= 64)
   const int P = T_ * k;
-  const bool valid = lane < P;
-  const int e = valid ? sidx[lane] : 0;
+  const int ev = lane < P ? sidx[lane] : -1;
+  const bool valid = (unsigned)ev < (unsigned)E;  // an empty slot (idx -1) is placed nowhere
+  const int e = valid ? ev : 0;
   // lanes holding the same expert: intersect ballots over the bits of e (< 64)
   uint64_t same = __ballot(valid);
 #pragma unroll
@@ -361,6 +396,8 @@ __global__ __launch_bounds__(256) void topk_permute_tiny_kernel(
     } else {
       inv[lane] = -1;
     }
+  } else if (lane < P) {
+    inv[lane] = -1;
   }
   if (lane == 0) {
     shared_seg[0] = 0;

@@ -17,7 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
 
 MOE_F32, MOE_BF16 = 0, 1
-GATE_SOFTMAX_TOPK, GATE_SOFTMAX_ALL, GATE_SIGMOID = 0, 1, 2
+GATE_SOFTMAX_TOPK, GATE_SOFTMAX_ALL, GATE_SIGMOID, GATE_ENTROPY = 0, 1, 2, 3
 ACT_SWIGLU, ACT_GLU_SIGMOID = 0, 1
 NSTAGE_EVENTS = 8
 STAGES = ("router", "permute", "gather", "gemm_swiglu", "gemm_down", "shared_expert", "combine")

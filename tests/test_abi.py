@@ -122,14 +122,14 @@ def test_variant_entry_points_check_arguments(L):
     assert L.moe_capacity(-1, 2, 1.2) == -1
     assert L.moe_capacity(4, 0, 1.2) == -1
     assert L.moe_capacity(4, 2, -0.5) == -1
-    # unknown gate mode
-    for mode in (-1, 3):
-        assert L.moe_route_ex(fake, fake, None, 4, 64, 8, 2, 1, mode, fake, fake, None, fake, big,
+    # unknown gate mode; the entropy-aware mode needs k >= 2
+    for mode, k in ((-1, 2), (4, 2), (3, 1)):
+        assert L.moe_route_ex(fake, fake, None, 4, 64, 8, k, 1, mode, fake, fake, None, fake, big,
                               None) == -1
     # unknown gate mode / activation in the forward options
-    for gm, act in ((3, 0), (0, 2), (-1, 0)):
+    for gm, act, k in ((4, 0, 2), (0, 2, 2), (-1, 0, 2), (3, 0, 1)):
         opt = moe._Options(gm, act, -1)
-        args = [fake, fake, None, fake, fake, fake, None, None, None, 0, 4, 8, 2, 64, 64, 1,
+        args = [fake, fake, None, fake, fake, fake, None, None, None, 0, 4, 8, k, 64, 64, 1,
                 ctypes.byref(opt), vp(0x100000), 1 << 40, vp(0x2000), None]
         assert L.moe_forward_ex(*args) == -1
     # permute_ex: too-small workspace is still caught

@@ -58,6 +58,10 @@ CASES = [
     ("tiny_E20_k3_shared_f32", 4, 192, 20, 128, 3, "f32", 64, 0.0, 1, 1, None),
     # weight-streaming down projection with the combine inside, every pair dropped
     ("capacity_0_gemv_T2_bf16", 2, 2048, 8, 2048, 2, "bf16", 0, 0.0, 0, 0, 0),
+    # entropy-aware k ("Mixtral 8x7B model architecture" 4.1): 3 or 2 experts per token
+    ("entropy_k3_bf16", 300, 256, 8, 512, 3, "bf16", 0, 0.0, 3, 0, None),
+    ("entropy_k3_shared_cap_f32", 150, 128, 6, 128, 3, "f32", 64, 0.0, 3, 0, 40),
+    ("entropy_decode_T4_bf16", 4, 2048, 8, 2048, 3, "bf16", 0, 0.0, 3, 0, None),
 ]
 
 
@@ -79,6 +83,13 @@ def test_variant_forward(c):
     torch.cuda.synchronize()
     it = {n: v.cpu().numpy() for n, v in L.intermediates(T).items()}
     lg = it["logits"].astype(np.float64)
+    if gm == O.GATE_ENTROPY:
+        # the per-token k is a decision on the entropy (fp32 on the GPU, fp64
+        # here, from the same scores): these inputs keep every token clear of
+        # the threshold, so both sides decide alike
+        H = O.entropy(lg)
+        assert np.min(np.abs(H - O.ENTROPY_THRESHOLD)) > 1e-4
+        say(f"{label}: {int(np.sum(H > O.ENTROPY_THRESHOLD))} of {T} tokens take k={k}")
     ref = O.forward(h["x"], h["Wg"], h["W1"], h["W3"], h["W2"], k, bias=h["bias"],
                     shared=(h["Ws1"], h["Ws3"], h["Ws2"]) if dffs else None, logits_in=lg,
                     gate_mode=gm, act=act, capacity=cap)
@@ -98,6 +109,35 @@ def test_variant_forward(c):
     err = rel_l2(got, ref["y"])
     say(f"{label}: dropped {dropped} of {T * k} pairs, rel-L2 {err:.3e} (bar {TOL[dtype]})")
     assert err <= TOL[dtype]
+
+
+def test_route_entropy():
+    # entropy-aware k through moe_route_ex against the oracle on the GPU's
+    # scores.  A token whose fp64 entropy lies within 1e-4 of the threshold may
+    # take either k (the GPU decides in fp32); its experts and gates must then
+    # match the oracle's routing with that k.
+    cfg, h, dev = inputs(777, 512, 16, 64, 3, "bf16", seed=12)
+    idx, gate, logits = moe.route(dev["x"], dev["Wg"], 3, None, gate_mode=moe.GATE_ENTROPY)
+    torch.cuda.synchronize()
+    lg = logits.double().cpu().numpy()
+    gi, gg = idx.cpu().numpy(), gate.cpu().numpy()
+    H = O.entropy(lg)
+    ri, rg = O.route_entropy(lg, 3)
+    hi_i, hi_g = O.route_entropy(lg, 3, threshold=-1.0)    # k experts for every token
+    lo_i, lo_g = O.route_entropy(lg, 3, threshold=1e30)    # k - 1 for every token
+    near = np.abs(H - O.ENTROPY_THRESHOLD) < 1e-4
+    for t in range(lg.shape[0]):
+        if near[t]:
+            ok_i = hi_i[t] if gi[t, 2] >= 0 else lo_i[t]
+            ok_g = hi_g[t] if gi[t, 2] >= 0 else lo_g[t]
+        else:
+            ok_i, ok_g = ri[t], rg[t]
+        np.testing.assert_array_equal(gi[t], ok_i)
+        assert np.max(np.abs(gg[t] - ok_g)) <= 1e-6
+    n3 = int(np.sum(gi[:, 2] >= 0))
+    say(f"moe_route_ex entropy: {n3} of {lg.shape[0]} tokens take 3 experts, {int(near.sum())} "
+        f"near the threshold")
+    assert 0 < n3 < lg.shape[0]
 
 
 @pytest.mark.parametrize("gm", [0, 1, 2])
