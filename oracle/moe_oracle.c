@@ -47,6 +47,9 @@
  *   orc_capacity      pinned (the two worked numbers of [SMoE] 2.4)
  *   orc_entropy       pinned (closed forms; torch softmax + entr)
  *   orc_route_entropy pinned (per-token torch.topk of the tempered softmax)
+ *   orc_fp8_decode    pinned (all 256 codes against torch.float8_e4m3fn)
+ *   orc_fp8_encode    pinned (torch's float8_e4m3fn cast; brute-force nearest)
+ *   orc_quantize_fp8  pinned (per-expert amax by numpy; round trip bounds)
  */
 #include <math.h>
 #ifdef _OPENMP
@@ -59,11 +62,14 @@
 
 #define ORC_F32 0
 #define ORC_BF16 1
+#define ORC_F64 2 /* fp64 arrays, e.g. dequantized weights */
 
 /* Widen one stored element to double.  bf16 is the upper half of an IEEE
  * binary32, so the widening is exact. */
 static double elem(const void *p, int dt, size_t i)
 {
+    if (dt == ORC_F64)
+        return ((const double *)p)[i];
     if (dt == ORC_BF16) {
         uint32_t u = ((uint32_t)((const uint16_t *)p)[i]) << 16;
         float f;
@@ -257,6 +263,82 @@ int orc_route_entropy(const double *logits, long T, int E, int k, double tau,
     }
     free(H);
     return 0;
+}
+
+/* FP8 weights for the experts [SMoE 5.3: quantise only the expert weights,
+ * keep the router in high precision, and give every expert its own scale so
+ * that no error crosses experts].  Format: OCP FP8 E4M3 ("E4M3FN"): sign,
+ * 4 exponent bits with bias 7, 3 mantissa bits; exponent field 0 holds the
+ * subnormals m * 2^-9; no infinities; S.1111.111 is NaN; the largest finite
+ * value is 1.75 * 2^8 = 448. */
+double orc_fp8_decode(uint8_t c)
+{
+    int sign = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    double v;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9);
+    else
+        v = ldexp(1.0 + m / 8.0, e - 7);
+    return sign ? -v : v;
+}
+
+/* Nearest E4M3 value, ties to the even mantissa; magnitudes above 448 give
+ * 448 (the format has no infinity).  Scales are chosen so that no weight
+ * goes above 448 by more than a rounding of the scale. */
+uint8_t orc_fp8_encode(double v)
+{
+    uint8_t sign = signbit(v) ? 0x80 : 0; /* -0 keeps its sign */
+    double a = fabs(v);
+    if (a >= 448.0)
+        return sign | 0x7E; /* e = 15, m = 6: 448 */
+    if (a < ldexp(1.0, -6)) {
+        /* subnormal range: integer multiples of 2^-9 (8 * 2^-9 is the
+         * smallest normal, encoded as e = 1, m = 0 by the same bits) */
+        double m = rint(ldexp(a, 9)); /* rint: round half to even */
+        return sign | (uint8_t)m;
+    }
+    int ex;
+    frexp(a, &ex);       /* a = f * 2^ex, 0.5 <= f < 1 */
+    int e = ex - 1;      /* a = (1 + x) * 2^e with 0 <= x < 1 */
+    double m = rint((ldexp(a, -e) - 1.0) * 8.0);
+    if (m == 8.0) {      /* rounded up to the next power of two */
+        m = 0.0;
+        e += 1;
+    }
+    if (e + 7 > 15 || (e + 7 == 15 && m > 6.0))
+        return sign | 0x7E;
+    return sign | (uint8_t)(((e + 7) << 3) | (int)m);
+}
+
+/* Weight-only FP8 experts: W holds E experts of n elements each (one matrix
+ * per expert, any row layout).  scale[e] = amax_e / 448 rounded to fp32 (1 for
+ * an all-zero expert), amax_e the largest |w| of the expert; q = E4M3 of
+ * w / scale[e], the quotient taken in fp64.  The dequantized weight is
+ * scale[e] * decode(q). */
+void orc_quantize_fp8(const void *W, int dt, long E, long n, uint8_t *q, float *scale)
+{
+    for (long e = 0; e < E; ++e) {
+        double amax = 0.0;
+        for (long i = 0; i < n; ++i) {
+            double a = fabs(elem(W, dt, (size_t)e * n + i));
+            if (a > amax)
+                amax = a;
+        }
+        float s = amax > 0.0 ? (float)(amax / 448.0) : 1.0f;
+        scale[e] = s;
+        for (long i = 0; i < n; ++i)
+            q[(size_t)e * n + i] = orc_fp8_encode(elem(W, dt, (size_t)e * n + i) / (double)s);
+    }
+}
+
+/* out[e][i] = scale[e] * decode(q[e][i]) (fp64, exact). */
+void orc_dequant_fp8(const uint8_t *q, long E, long n, const float *scale, double *out)
+{
+    for (long e = 0; e < E; ++e)
+        for (long i = 0; i < n; ++i)
+            out[(size_t)e * n + i] = (double)scale[e] * orc_fp8_decode(q[(size_t)e * n + i]);
 }
 
 /* Expert capacity [SMoE 2.4]: an expert takes at most min(k*T, floor(cf*T))

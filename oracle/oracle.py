@@ -20,7 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "moe_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-F32, BF16 = 0, 1
+F32, BF16, F64 = 0, 1, 2
 # gate variants (orc_gate_mode) and expert activations (swiglu in moe_oracle.c)
 GATE_SOFTMAX_TOPK, GATE_SOFTMAX_ALL, GATE_SIGMOID, GATE_ENTROPY = 0, 1, 2, 3
 # the entropy-aware routing's temperature and entropy threshold as printed
@@ -63,6 +63,12 @@ def _bind(path: str):
     L.orc_capacity.restype = ctypes.c_long
     L.orc_keep.argtypes = [i32p, ctypes.c_long, ctypes.c_int, ctypes.c_int, ctypes.c_long, i32p]
     L.orc_entropy.argtypes = [f64p, ctypes.c_long, ctypes.c_int, ctypes.c_double, f64p]
+    L.orc_fp8_decode.argtypes = [ctypes.c_uint8]
+    L.orc_fp8_decode.restype = ctypes.c_double
+    L.orc_fp8_encode.argtypes = [ctypes.c_double]
+    L.orc_fp8_encode.restype = ctypes.c_uint8
+    L.orc_quantize_fp8.argtypes = [vp, ctypes.c_int, ctypes.c_long, ctypes.c_long, vp, f32p]
+    L.orc_dequant_fp8.argtypes = [vp, ctypes.c_long, ctypes.c_long, f32p, f64p]
     L.orc_route_entropy.argtypes = [f64p, ctypes.c_long, ctypes.c_int, ctypes.c_int,
                                     ctypes.c_double, ctypes.c_double, i32p, f64p]
     L.orc_route_entropy.restype = ctypes.c_int
@@ -115,7 +121,9 @@ def _dtype_code(a) -> int:
         return BF16
     if a.dtype == np.float32:
         return F32
-    raise TypeError(f"oracle inputs are float32 or bf16 bits (uint16), got {a.dtype}")
+    if a.dtype == np.float64:
+        return F64
+    raise TypeError(f"oracle inputs are float32, float64 or bf16 bits (uint16), got {a.dtype}")
 
 
 def _c(a, dtype=None):
@@ -184,6 +192,39 @@ def route_entropy(lg, k, tau=ENTROPY_TAU, threshold=ENTROPY_THRESHOLD):
                                _ptr(g)) != 0:
         raise ValueError("entropy-aware routing needs 2 <= k <= E")
     return idx, g
+
+
+def fp8_decode(codes):
+    """E4M3 (OCP, 'FN') value of each uint8 code (fp64)."""
+    return np.array([lib().orc_fp8_decode(int(c)) for c in np.asarray(codes).reshape(-1)],
+                    np.float64).reshape(np.shape(codes))
+
+
+def fp8_encode(values):
+    """Nearest E4M3 code of each value (ties to even; above 448 gives 448)."""
+    return np.array([lib().orc_fp8_encode(float(v)) for v in np.asarray(values).reshape(-1)],
+                    np.uint8).reshape(np.shape(values))
+
+
+def quantize_fp8(W):
+    """Per-expert FP8 quantisation of W [E, ...] (bf16 bits or float32):
+    (codes uint8 of W's shape, scale float32 [E])."""
+    W = _c(W)
+    E = W.shape[0]
+    n = W.size // E
+    q = np.empty(W.shape, np.uint8)
+    scale = np.empty(E, np.float32)
+    lib().orc_quantize_fp8(_ptr(W), _dtype_code(W), E, n, _ptr(q), _ptr(scale))
+    return q, scale
+
+
+def dequant_fp8(q, scale):
+    """scale[e] * decode(q[e]) in fp64, q [E, ...]."""
+    q, scale = _c(q, np.uint8), _c(scale, np.float32)
+    E = q.shape[0]
+    out = np.empty(q.shape, np.float64)
+    lib().orc_dequant_fp8(_ptr(q), E, q.size // E, _ptr(scale), _ptr(out))
+    return out
 
 
 def capacity(T, k, cf) -> int:

@@ -363,12 +363,75 @@ def check_entropy_routing():
     np.testing.assert_allclose(out["y"], ref, rtol=1e-12, atol=1e-14)
 
 
+def check_fp8():
+    # "Mistral 8x7B SMoE architecture deep dive" section 5.3: expert weights
+    # quantised with one scale per expert, router kept in high precision.
+    # E4M3 (OCP 'FN'): every code against torch's own float8_e4m3fn
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    dec = O.fp8_decode(codes)
+    assert np.all((dec == ref) | (np.isnan(dec) & np.isnan(ref)))
+    finite = codes[np.isfinite(ref)]
+    # encoding: torch's cast of fp32 values in range (magnitudes, subnormals,
+    # exact midpoints between neighbouring codes), and brute-force nearest
+    rng = np.random.default_rng(5)
+    vals = np.concatenate([rng.standard_normal(2000) * 40.0,
+                           rng.standard_normal(500) * 2.0 ** -7,
+                           (ref[finite][:-1] + ref[finite][1:]) / 2.0,
+                           ref[finite], [447.9, -447.9, 0.0]]).astype(np.float32)
+    vals = vals[np.abs(vals) <= 448.0]
+    enc = O.fp8_encode(vals)
+    tref = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(enc, tref)
+    fv = ref[finite]
+    for v in vals[:400]:
+        dist = np.abs(fv - float(v))
+        best = finite[dist == dist.min()]
+        if len(best) > 1:  # a tie: the even mantissa wins
+            best = best[(best & 1) == 0]
+        got = int(O.fp8_encode([v])[0])
+        assert got == int(best[0]) or (float(v) == 0.0 and ref[got] == 0.0)
+    assert int(O.fp8_encode([1000.0])[0]) == 0x7E and int(O.fp8_encode([-1e6])[0]) == 0xFE
+    # per-expert quantisation: the scale maps each expert's largest |w| to 448,
+    # every weight comes back within half a step of E4M3, and experts do not
+    # see each other's scale
+    W = (rng.standard_normal((3, 40, 24)) * np.array([0.02, 1.0, 30.0])[:, None, None])
+    W = W.astype(np.float32)
+    q, sc = O.quantize_fp8(W)
+    amax = np.abs(W).reshape(3, -1).max(axis=1).astype(np.float64)
+    np.testing.assert_array_equal(sc, (amax / 448.0).astype(np.float32))
+    deq = O.dequant_fp8(q, sc)
+    np.testing.assert_array_equal(deq, sc.astype(np.float64)[:, None, None] * O.fp8_decode(q))
+    r = W.astype(np.float64) / sc.astype(np.float64)[:, None, None]
+    step = np.where(np.abs(r) >= 2.0 ** -6, 2.0 ** (np.floor(np.log2(np.maximum(np.abs(r), 1e-300))) - 3),
+                    2.0 ** -9)
+    assert np.all(np.abs(O.fp8_decode(q) - r) <= step / 2 + 1e-12)
+    for e in range(3):
+        assert np.max(np.abs(O.fp8_decode(q[e]))) == 448.0
+    W2 = W.copy()
+    W2[0] *= 7.0
+    q2, sc2 = O.quantize_fp8(W2)
+    np.testing.assert_array_equal(q2[1:], q[1:])
+    np.testing.assert_array_equal(sc2[1:], sc[1:])
+    zq, zs = O.quantize_fp8(np.zeros((1, 8), np.float32))
+    assert zs[0] == 1.0 and not zq.any()
+    # the layer on fp64 (dequantised) weights: E=1, k=1 is torch's dense FFN
+    inp = tiny(17, 32, 1, 48, 1, "bf16", seed=15)
+    d1, d3, d2 = (O.dequant_fp8(*O.quantize_fp8(inp[n])) for n in ("W1", "W3", "W2"))
+    x64 = f64(inp["x"])
+    out = O.forward(x64, f64(inp["Wg"]), d1, d3, d2, 1)
+    X = torch.from_numpy(x64)
+    ref_y = F.linear(F.silu(F.linear(X, torch.from_numpy(d1[0]))) *
+                     F.linear(X, torch.from_numpy(d3[0])), torch.from_numpy(d2[0])).numpy()
+    np.testing.assert_allclose(out["y"], ref_y, rtol=1e-11, atol=1e-13)
+
+
 CHECKS = [check_logits, check_topk_bruteforce, check_topk_duplicate_rows, check_gates,
           check_counts_and_permutation, check_dense_special_case,
           check_all_experts_special_case, check_shared_expert, check_invariants,
           check_given_logits_and_rows, check_page_numbers, check_gate_variants,
           check_glu_sigmoid_dense, check_fused_weight_formulation, check_capacity,
-          check_entropy_routing]
+          check_entropy_routing, check_fp8]
 
 
 @pytest.mark.parametrize("check", CHECKS, ids=[c.__name__ for c in CHECKS])
@@ -393,6 +456,14 @@ MUTANTS = [
     ("capacity_rounds_up", "long c = (long)floor(cf * (double)T);", "long c = (long)ceil(cf * (double)T);"),
     # (empty slots stay skipped: placing idx -1 would write outside the arrays)
     ("dropped_pairs_placed", "if (!keep[p]) {", "if (idx[p] < 0) {"),
+    ("fp8_bias_8", "v = ldexp(1.0 + m / 8.0, e - 7);", "v = ldexp(1.0 + m / 8.0, e - 8);"),
+    ("fp8_subnormal_step", "v = ldexp((double)m, -9);", "v = ldexp((double)m, -10);"),
+    ("fp8_ties_away", "double m = rint((ldexp(a, -e) - 1.0) * 8.0);",
+     "double m = round((ldexp(a, -e) - 1.0) * 8.0);"),
+    ("fp8_saturate_480", "return sign | 0x7E; /* e = 15, m = 6: 448 */",
+     "return sign | 0x7F; /* e = 15, m = 6: 448 */"),
+    ("fp8_scale_per_tensor", "float s = amax > 0.0 ? (float)(amax / 448.0) : 1.0f;",
+     "float s = amax > 0.0 ? (float)(amax / 240.0) : 1.0f;"),
     ("entropy_tau_multiplied", "double u = (l[e] - m) / tau;", "double u = (l[e] - m) * tau;"),
     ("entropy_sign", "H[t] = log(z) - s1 / z;", "H[t] = log(z) + s1 / z;"),
     ("entropy_k_swapped", "const int kt = H[t] > threshold ? k : k - 1;",
