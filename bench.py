@@ -165,6 +165,37 @@ def run_workload(cfg, host, dev, steps, warmup, flush_mb=0, graph=False):
     return out
 
 
+def run_fp8(cfg, dev, steps, warmup, flush_mb):
+    """Decode step with FP8 experts (moe_forward_fp8; weights quantised once,
+    outside the timed region): mean per-step time around the forward with the
+    MALL flushed before each step, and the expert counts."""
+    import numpy as np
+    import torch
+
+    from sparse_mixture_experts_permute_amd import moe
+    T = cfg.T
+    x = dev["x"][:T].contiguous()
+    layer = moe.MoELayerFP8(dev["Wg"], dev["W1"], dev["W3"], dev["W2"], cfg.k)
+    y = torch.empty_like(x)
+    flush = torch.ones(flush_mb << 18, dtype=torch.float32, device="cuda")
+    for _ in range(warmup):
+        layer(x, y)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b_ in ev:
+        flush.sum()
+        a.record()
+        layer(x, y)
+        b_.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b_) for a, b_ in ev]))
+    counts = layer.intermediates(T)["counts"].cpu().numpy()
+    del layer
+    torch.cuda.empty_cache()
+    return dict(ms=ms, counts=counts)
+
+
 def run_variant(cfg, dev, steps, warmup, **variants):
     """Whole-layer time of moe_forward_ex with the given variants (HIP events
     around `steps` back-to-back forwards) and the pairs the experts kept."""
@@ -323,8 +354,22 @@ def main():
                                    / (PEAK_HBM_GBS * 1e9), 4))
             if c2.skew:
                 e["hot_expert_share"] = round(float(r2["counts"][0] / r2["counts"].sum()), 4)
-            log(f"{name}: {ms2:.4f} ms/step (sum of stages), {e['tokens_per_s']} tokens/s")
+            log(f"{name}: {ms2:.4f} ms/step, {e['tokens_per_s']} tokens/s")
             extra.append(e)
+        # weight-only FP8 experts for the single-token decode step
+        c2 = CONFIGS["mixtral_decode_T1"]
+        r8 = run_fp8(c2, dev, 20, 3, 512)
+        hit = int(np.count_nonzero(r8["counts"]))
+        b8 = (hit * 3.0 * c2.d * c2.d_ff + 2.0 * c2.T * c2.d * 2 + c2.E * c2.d * 2
+              + 3 * c2.E * 4)
+        e = dict(workload="mixtral_decode_T1", weights="fp8_e4m3_per_expert_scale",
+                 T=c2.T, ms_per_step=round(r8["ms"], 4),
+                 tokens_per_s=round(c2.T / (r8["ms"] * 1e-3), 1),
+                 layer=dict(hbm_frac=round(b8 / (r8["ms"] * 1e-3) / (PEAK_HBM_GBS * 1e9), 4),
+                            algorithmic_bytes=b8, experts_hit=hit),
+                 mall_flushed=True)
+        log(f"mixtral_decode_T1 fp8 experts: {r8['ms']:.4f} ms/step")
+        extra.append(e)
 
     # the fine-grained layer with a shared expert (256 experts, top-8)
     if not args.no_extra and cfg.d == 4096 and cfg.E == 8:

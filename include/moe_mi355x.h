@@ -212,6 +212,40 @@ int moe_forward_ex(const void *x, const void *Wg, const float *bias, const void 
                    int dtype, const moe_options *opt, void *workspace, size_t workspace_bytes,
                    void *y, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Weight-only FP8 experts for decode ("Mistral 8x7B SMoE architecture deep
+ * dive", section 5.3: quantise only the expert weights, keep the router in
+ * high precision, one scale per expert).  Format OCP FP8 E4M3 ("E4M3FN":
+ * largest finite 448, no infinities).  Symmetric; an FP8 float needs no
+ * zero-point.
+ * ------------------------------------------------------------------------ */
+
+/* Quantise E expert matrices of n elements each (W [E][n], dtype MOE_BF16 or
+ * MOE_F32, any layout inside an expert): scale[e] = amax_e / 448 rounded to
+ * fp32 (1 for an all-zero expert), amax_e the largest |w| of expert e, and
+ * q[e][i] = the E4M3 code nearest to W[e][i] / scale[e] (quotient in fp64,
+ * ties to the even mantissa, magnitudes above 448 give 448).  q [E][n] uint8
+ * and scale [E] fp32 are device outputs; scale doubles as scratch during the
+ * call.  Deterministic.  Used on W1 [E][d_ff][d], W3 and W2 [E][d][d_ff]. */
+int moe_quantize_fp8(const void *W, int E, long long n, int dtype, uint8_t *q, float *scale,
+                     void *stream);
+
+/* The layer with FP8 experts: y = sum_j gate_j * W2'( act(W1' x, W3' x) ) with
+ * W' = scale[e] * decode(q) (the router, activations and outputs stay bf16, as
+ * does all arithmetic outside the weights: fp32 accumulation).
+ *   x [T][d] bf16, Wg [E][d] bf16, bias as moe_forward; W1q, W3q [E][d_ff][d],
+ *   W2q [E][d][d_ff] uint8 with scales s1, s3, s2 [E] fp32 (moe_quantize_fp8);
+ *   opt: gate / activation / capacity variants as moe_forward_ex (NULL:
+ *   defaults); no shared expert.
+ *   workspace: moe_workspace_bytes(T, d, d_ff, E, k, 0, MOE_BF16) bytes.
+ * A decode path: T <= 4, and d and d_ff multiples of 2048 up to 16384
+ * (the weight-streaming kernels); MOE_EINVAL otherwise. */
+int moe_forward_fp8(const void *x, const void *Wg, const float *bias, const uint8_t *W1q,
+                    const uint8_t *W3q, const uint8_t *W2q, const float *s1, const float *s3,
+                    const float *s2, int T, int E, int k, int d, int d_ff,
+                    const moe_options *opt, void *workspace, size_t workspace_bytes, void *y,
+                    void *stream);
+
 /* Static text for a status code. */
 const char *moe_strerror(int status);
 

@@ -275,11 +275,17 @@ int moe_workspace_offsets(int T, int d, int d_ff, int E, int k, int d_ff_shared,
 
 namespace {
 
+// FP8 expert weights (moe_forward_fp8): codes and per-expert scales
+struct Fp8Experts {
+  const uint8_t *W1q, *W3q, *W2q;
+  const float *s1, *s3, *s2;
+};
+
 int forward_impl(const void *x, const void *Wg, const float *bias, const void *W1,
                  const void *W3, const void *W2, const void *Ws1, const void *Ws3,
                  const void *Ws2, int d_ff_shared, int T, int E, int k, int d, int d_ff,
                  int dtype, const moe_options *opt, void *workspace, size_t workspace_bytes,
-                 void *y, void *stream, void *const *events) {
+                 void *y, void *stream, void *const *events, const Fp8Experts *f8 = nullptr) {
   if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_EDTYPE;
   const moe_options o = opt ? *opt : moe_options{MOE_GATE_SOFTMAX_TOPK, MOE_ACT_SWIGLU, -1};
   if (o.gate_mode < MOE_GATE_SOFTMAX_TOPK || o.gate_mode > MOE_GATE_ENTROPY) return MOE_EINVAL;
@@ -301,7 +307,8 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
   const int P = T * k;
   const moe::GemmPlan plan =
       moe::gemm_plan(dtype, d, d_ff, d_ff_shared, ((long long)T * k + E - 1) / E);
-  const SkinnyPlan sk = skinny_plan(dtype, T, k, E, d, d_ff, d_ff_shared);
+  SkinnyPlan sk = skinny_plan(dtype, T, k, E, d, d_ff, d_ff_shared);
+  if (f8) sk.routed = sk.gemv = true;  // FP8 experts: weight streaming, checked by the caller
   const int ksplit = sk.routed ? 1 : down_splits(plan, T, k, E, d, d_ff);
   const size_t plane = (size_t)P * d;
   float *logits = at<float>(ws, L.off[F_LOGITS]);
@@ -358,13 +365,19 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
     MOE_MARK(3);
     // a single token activates exactly k experts (fewer only under a capacity)
     const int nact = T == 1 ? k : 0;
-    if ((e = sk.gemv ? moe::launch_gemv_swiglu(T, o.activation, x, perm, k, W1, W3, H, offsets,
+    if ((e = f8 ? moe::launch_gemv_swiglu_fp8(T, o.activation, x, perm, k, f8->W1q, f8->W3q,
+                                              f8->s1, f8->s3, H, offsets, act, act + E, E, d_ff,
+                                              d, nact, s)
+             : sk.gemv ? moe::launch_gemv_swiglu(T, o.activation, x, perm, k, W1, W3, H, offsets,
                                                act, act + E, E, d_ff, d, nact, s)
                      : moe::launch_skinny_swiglu(sk.mb, o.activation, x, perm, k, W1, W3, H,
                                                  offsets, act, act + E, E, d_ff, d, s)))
       goto fail;
     MOE_MARK(4);
-    if ((e = fused_combine
+    if ((e = f8 ? moe::launch_gemv_down_combine_fp8(T, H, f8->W2q, f8->s2, Yp, offsets, act,
+                                                    act + E, E, d, d_ff, nact, inv, gate, T, k,
+                                                    y, fixc, s)
+             : fused_combine
                  ? moe::launch_gemv_down_combine(T, H, W2, Yp, offsets, act, act + E, E, d, d_ff,
                                                  nact, inv, gate, T, k, y, fixc, s)
              : sk.gemv ? moe::launch_gemv_down(T, H, W2, Yp, offsets, act, act + E, E, d, d_ff,
@@ -455,6 +468,30 @@ int moe_forward_timed(const void *x, const void *Wg, const float *bias, const vo
     if (!events[i]) return MOE_EINVAL;
   return forward_impl(x, Wg, bias, W1, W3, W2, Ws1, Ws3, Ws2, d_ff_shared, T, E, k, d, d_ff,
                       dtype, nullptr, workspace, workspace_bytes, y, stream, events);
+}
+
+int moe_quantize_fp8(const void *W, int E, long long n, int dtype, uint8_t *q, float *scale,
+                     void *stream) {
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_EDTYPE;
+  if (E < 0 || n < 0) return MOE_EINVAL;
+  if (E == 0 || n == 0) return MOE_OK;
+  if (!W || !q || !scale) return MOE_EINVAL;
+  int st = device_ok();
+  if (st != MOE_OK) return st;
+  return launched(moe::launch_quantize_fp8(dtype, W, E, (size_t)n, q, scale, (hipStream_t)stream));
+}
+
+int moe_forward_fp8(const void *x, const void *Wg, const float *bias, const uint8_t *W1q,
+                    const uint8_t *W3q, const uint8_t *W2q, const float *s1, const float *s3,
+                    const float *s2, int T, int E, int k, int d, int d_ff,
+                    const moe_options *opt, void *workspace, size_t workspace_bytes, void *y,
+                    void *stream) {
+  if (T < 0 || T > 4) return MOE_EINVAL;
+  if (!moe::gemv_ok(d_ff, d) || !moe::gemv_ok(d, d_ff)) return MOE_EINVAL;
+  if (T > 0 && (!s1 || !s3 || !s2)) return MOE_EINVAL;
+  const Fp8Experts f8{W1q, W3q, W2q, s1, s3, s2};
+  return forward_impl(x, Wg, bias, W1q, W3q, W2q, nullptr, nullptr, nullptr, 0, T, E, k, d, d_ff,
+                      MOE_BF16, opt, workspace, workspace_bytes, y, stream, nullptr, &f8);
 }
 
 }  // extern "C"

@@ -1,0 +1,127 @@
+// Weight-only FP8 experts: quantisation of expert weights to OCP FP8 E4M3
+// ("E4M3FN": sign, 4 exponent bits with bias 7, 3 mantissa bits; exponent
+// field 0 holds the subnormals m * 2^-9; no infinities; S.1111.111 is NaN;
+// largest finite 448) with one scale per expert ("Mistral 8x7B SMoE
+// architecture deep dive", section 5.3: quantise only the expert weights,
+// keep the router in high precision, give each expert its own scale).
+//
+// scale[e] = amax_e / 448 rounded to fp32 (1 for an all-zero expert), amax_e
+// the largest |w| of expert e; q = the nearest E4M3 value of w / scale[e]
+// (quotient in fp64, ties to the even mantissa, magnitudes above 448 give
+// 448).  The dequantised weight is scale[e] * decode(q).  Four launches: clear
+// the per-expert maxima, reduce them (atomic max of non-negative float bits,
+// which is order independent), turn them into scales, encode.
+#include <cmath>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int Q_THREADS = 256;
+
+template <typename T>
+__device__ __forceinline__ float load_w(const T *p, size_t i);
+template <>
+__device__ __forceinline__ float load_w<float>(const float *p, size_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float load_w<bf16_t>(const bf16_t *p, size_t i) {
+  return bf16_to_f32(p[i]);
+}
+
+// Nearest E4M3 code of v (fp64 throughout: the steps are exact but the
+// rounding of the mantissa, which rint does half to even).
+__device__ __forceinline__ uint8_t fp8_e4m3_encode(double v) {
+  const uint8_t sign = signbit(v) ? 0x80 : 0;
+  const double a = fabs(v);
+  if (a >= 448.0) return sign | 0x7E;
+  if (a < 0.015625) {  // below 2^-6: multiples of 2^-9 (8 of them is the smallest normal)
+    return sign | (uint8_t)rint(a * 512.0);
+  }
+  int ex;
+  frexp(a, &ex);
+  int e = ex - 1;  // a = (1 + x) * 2^e
+  double m = rint((ldexp(a, -e) - 1.0) * 8.0);
+  if (m == 8.0) {
+    m = 0.0;
+    e += 1;
+  }
+  if (e + 7 > 15 || (e + 7 == 15 && m > 6.0)) return sign | 0x7E;
+  return sign | (uint8_t)(((e + 7) << 3) | (int)m);
+}
+
+__global__ void fp8_clear_kernel(float *__restrict__ amax, int E) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e < E) amax[e] = 0.f;
+}
+
+// grid (blocks per expert, E): block-local maximum, then one atomic per block
+template <typename T>
+__global__ __launch_bounds__(Q_THREADS) void fp8_amax_kernel(const T *__restrict__ W, size_t n,
+                                                             float *__restrict__ amax) {
+  __shared__ float red[Q_THREADS / kWave];
+  const int e = blockIdx.y;
+  const T *w = W + (size_t)e * n;
+  float m = 0.f;
+  for (size_t i = (size_t)blockIdx.x * Q_THREADS + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * Q_THREADS)
+    m = fmaxf(m, fabsf(load_w(w, i)));
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if (lane_id() == 0) red[threadIdx.x / kWave] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int i = 1; i < Q_THREADS / kWave; ++i) m = fmaxf(m, red[i]);
+    // non-negative floats order as their bit patterns
+    atomicMax(reinterpret_cast<unsigned int *>(amax) + e, __float_as_uint(m));
+  }
+}
+
+__global__ void fp8_scale_kernel(float *__restrict__ scale, int E) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e < E) {
+    const float a = scale[e];
+    scale[e] = a > 0.f ? (float)((double)a / 448.0) : 1.0f;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(Q_THREADS) void fp8_encode_kernel(const T *__restrict__ W, size_t n,
+                                                               const float *__restrict__ scale,
+                                                               uint8_t *__restrict__ q) {
+  const int e = blockIdx.y;
+  const double s = (double)scale[e];
+  const T *w = W + (size_t)e * n;
+  uint8_t *qe = q + (size_t)e * n;
+  for (size_t i = (size_t)blockIdx.x * Q_THREADS + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * Q_THREADS)
+    qe[i] = fp8_e4m3_encode((double)load_w(w, i) / s);
+}
+
+template <typename T>
+hipError_t quantize_t(const void *W, int E, size_t n, uint8_t *q, float *scale, hipStream_t s) {
+  const int eb = (E + Q_THREADS - 1) / Q_THREADS;
+  // about 2048 blocks in all, at least one per expert
+  const size_t per = (size_t)(2048 + E - 1) / E;
+  const unsigned bx = (unsigned)std::max<size_t>(1, std::min(per, (n + Q_THREADS - 1) / Q_THREADS));
+  hipLaunchKernelGGL(fp8_clear_kernel, dim3(eb), dim3(Q_THREADS), 0, s, scale, E);
+  hipLaunchKernelGGL((fp8_amax_kernel<T>), dim3(bx, E), dim3(Q_THREADS), 0, s, (const T *)W, n,
+                     scale);
+  hipLaunchKernelGGL(fp8_scale_kernel, dim3(eb), dim3(Q_THREADS), 0, s, scale, E);
+  hipLaunchKernelGGL((fp8_encode_kernel<T>), dim3(bx, E), dim3(Q_THREADS), 0, s, (const T *)W, n,
+                     scale, q);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize_fp8(int dtype, const void *W, int E, size_t n, uint8_t *q,
+                               float *scale, hipStream_t s) {
+  if (E <= 0 || n == 0) return hipSuccess;
+  return dtype == 1 ? quantize_t<bf16_t>(W, E, n, q, scale, s)
+                    : quantize_t<float>(W, E, n, q, scale, s);
+}
+
+}  // namespace moe

@@ -19,6 +19,7 @@
 // and B[k = (l/16)*8 .. +8][n = l%16]; the result holds C[m = (l/16)*4 + i][n =
 // l%16] in element i.  Weights are [N][K] (K-contiguous), so B = W^T is read
 // as 16 consecutive bytes of one weight row per lane.
+#include <type_traits>
 #include "common.h"
 #include "kernels.h"
 
@@ -196,8 +197,38 @@ __device__ __forceinline__ float dot8_bf16(const uint4 &a, const uint4 &b, float
   return acc;
 }
 
+// FP8 (E4M3) weights: 8 bytes (8 weights) per lane per instruction; the
+// conversion to fp32 is exact, so the products are those of the dequantized
+// weights up to the per-expert scale, applied to the reduced sums.
+typedef unsigned int gv_u2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 ldg8_stream(const uint8_t *p) {
+  const gv_u2 v = __builtin_nontemporal_load(reinterpret_cast<const gv_u2 *>(p));
+  return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ uint4 gv_load(const bf16_t *p) { return ldg16_stream(p); }
+__device__ __forceinline__ uint2 gv_load(const uint8_t *p) { return ldg8_stream(p); }
+__device__ __forceinline__ float gv_dot(const uint4 &a, const uint4 &b, float acc) {
+  return dot8_bf16(a, b, acc);
+}
+__device__ __forceinline__ float gv_dot(const uint4 &a, const uint2 &b, float acc) {
+  // fp32 products: the pairwise E4M3 -> fp32 conversion and fp32 FMAs keep up
+  // with the byte stream better than E4M3 -> bf16 conversions feeding dot2
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  const uint32_t av[4] = {a.x, a.y, a.z, a.w};
+  const uint32_t bw[2] = {b.x, b.y};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f2 w = (i & 1) ? __builtin_amdgcn_cvt_pk_f32_fp8(bw[i >> 1], true)
+                         : __builtin_amdgcn_cvt_pk_f32_fp8(bw[i >> 1], false);
+    acc = fmaf(__uint_as_float(av[i] << 16), w.x, acc);          // even element
+    acc = fmaf(__uint_as_float(av[i] & 0xFFFF0000u), w.y, acc);  // odd element
+  }
+  return acc;
+}
+
 // Columns per group: the largest power of two that keeps about 16 weight
-// loads (16 KB) per wavefront in flight.
+// loads (16 KB of bf16, 8 KB of FP8) per wavefront in flight (more columns
+// per group were slower for FP8: the per-group reductions grow with them).
 constexpr int gv_cb(int loads_per_col) {
   int cb = 1;
   while (cb * 2 * loads_per_col <= 16) cb *= 2;
@@ -221,13 +252,19 @@ struct GemvCombine {
   bf16_t *y;
   int32_t *cnt;
 };
-template <bool SWIGLU, int R, int KC, bool COMBINE = false>
+//
+// W8: FP8 weights (uint8 E4M3 codes) with per-expert scales sc1 (W1 or W2) and
+// sc3 (W3).
+template <bool SWIGLU, int R, int KC, bool COMBINE = false, bool W8 = false>
 __global__ __launch_bounds__(GV_THREADS) void gemv_kernel(
     const bf16_t *__restrict__ A, const int32_t *__restrict__ perm, int kslots,
-    const bf16_t *__restrict__ B1, const bf16_t *__restrict__ B3, void *__restrict__ C,
+    const void *__restrict__ B1v, const void *__restrict__ B3v, void *__restrict__ C,
     const int32_t *__restrict__ seg_off, const int32_t *__restrict__ active,
-    const int32_t *__restrict__ nactive, int N, int K, int cpw, int act, GemvCombine cm) {
+    const int32_t *__restrict__ nactive, int N, int K, int cpw, int act, GemvCombine cm,
+    const float *__restrict__ sc1, const float *__restrict__ sc3) {
   static_assert(!(SWIGLU && COMBINE), "the combine follows the down projection");
+  using WT = typename std::conditional<W8, uint8_t, bf16_t>::type;  // weight element
+  using WV = typename std::conditional<W8, uint2, uint4>::type;     // 8 weights
   constexpr int NW = SWIGLU ? 2 : 1;
   constexpr int CB = gv_cb(NW * KC);
   __shared__ float red[2][GV_WAVES][CB][NW][R];
@@ -249,8 +286,8 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_kernel(
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = lane_id();
   const int kl = wave * KC * GV_CHUNK + lane * 8;  // first K element of the lane
-  const bf16_t *w1 = B1 + (size_t)e * N * K + kl;
-  const bf16_t *w3 = SWIGLU ? B3 + (size_t)e * N * K + kl : w1;
+  const WT *w1 = reinterpret_cast<const WT *>(B1v) + (size_t)e * N * K + kl;
+  const WT *w3 = SWIGLU ? reinterpret_cast<const WT *>(B3v) + (size_t)e * N * K + kl : w1;
   const int ngroups = cpw / CB;
 
   for (int rg = 0; rg < cnt; rg += R) {
@@ -263,26 +300,26 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_kernel(
 #pragma unroll
       for (int i = 0; i < KC; ++i) xa[r][i] = *reinterpret_cast<const uint4 *>(ap + i * GV_CHUNK);
     }
-    uint4 wa[CB][NW][KC], wb[CB][NW][KC];  // two groups of weights in flight
+    WV wa[CB][NW][KC], wb[CB][NW][KC];  // two groups of weights in flight
     // Workgroups start at different groups of their columns: workgroups a
     // fixed distance apart would otherwise all read the same offsets of their
     // blocks at the same time and crowd a few HBM channels.
     const int rot = blockIdx.x % ngroups;
     auto col_of = [&](int g) { return c0 + ((g + rot) % ngroups) * CB; };
-    auto load = [&](uint4 (&dst)[CB][NW][KC], int g) {
+    auto load = [&](WV (&dst)[CB][NW][KC], int g) {
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
         const size_t ro = (size_t)(col_of(g) + cb) * K;
 #pragma unroll
         for (int i = 0; i < KC; ++i) {
-          dst[cb][0][i] = ldg16_stream(w1 + ro + i * GV_CHUNK);
-          if (SWIGLU) dst[cb][NW - 1][i] = ldg16_stream(w3 + ro + i * GV_CHUNK);
+          dst[cb][0][i] = gv_load(w1 + ro + i * GV_CHUNK);
+          if (SWIGLU) dst[cb][NW - 1][i] = gv_load(w3 + ro + i * GV_CHUNK);
         }
       }
     };
     // dot products of one group, reduced over the lanes, then over the waves
     // (red[rb]: the two groups in flight use different halves)
-    auto compute = [&](const uint4 (&wv)[CB][NW][KC], int g, int rb) {
+    auto compute = [&](const WV (&wv)[CB][NW][KC], int g, int rb) {
       float acc[CB][NW][R];
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb)
@@ -292,7 +329,7 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_kernel(
           for (int r = 0; r < R; ++r) {
             float t = 0.f;
 #pragma unroll
-            for (int i = 0; i < KC; ++i) t = dot8_bf16(xa[r][i], wv[cb][m][i], t);
+            for (int i = 0; i < KC; ++i) t = gv_dot(xa[r][i], wv[cb][m][i], t);
 #pragma unroll
             for (int off = kWave / 2; off > 0; off >>= 1) t += __shfl_xor(t, off);
             acc[cb][m][r] = t;
@@ -316,6 +353,10 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_kernel(
 #pragma unroll
             for (int w = 0; w < GV_WAVES; ++w) t += red[rb][w][cb][m][r];
             v[m] = t;
+          }
+          if (W8) {  // the experts' scales
+            v[0] *= sc1[e];
+            if (SWIGLU) v[NW - 1] *= sc3[e];
           }
           const size_t out = (size_t)(s0 + rg + r) * N + col_of(g) + cb;
           if (SWIGLU)
@@ -371,11 +412,12 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_kernel(
   }
 }
 
-template <bool SWIGLU, int R, bool COMBINE = false>
+template <bool SWIGLU, int R, bool COMBINE = false, bool W8 = false>
 hipError_t launch_gemv_r(int act, const void *A, const int32_t *perm, int kslots,
                          const void *B1, const void *B3, void *C, const int32_t *seg_off,
                          const int32_t *active, const int32_t *nactive, int G, int N, int K,
-                         int nact, const GemvCombine &cm, hipStream_t s) {
+                         int nact, const GemvCombine &cm, const float *sc1, const float *sc3,
+                         hipStream_t s) {
   const int kc = K / (GV_WAVES * GV_CHUNK);
   constexpr int NW = SWIGLU ? 2 : 1;
   // columns per workgroup: a power of two from two groups up to 256, with
@@ -383,10 +425,10 @@ hipError_t launch_gemv_r(int act, const void *A, const int32_t *perm, int kslots
   // best)
   int cpw = 256;
   while (cpw > 1 && 2 * (N / cpw) < 256) cpw /= 2;
-  const bf16_t *a = (const bf16_t *)A, *b1 = (const bf16_t *)B1, *b3 = (const bf16_t *)B3;
+  const bf16_t *a = (const bf16_t *)A;
 #define GV_CASE(KC_)                                                                          \
   case KC_: {                                                                                 \
-    constexpr int CB = gv_cb(NW * KC_);                                                       \
+    constexpr int CB = gv_cb(NW * KC_);                                                 \
     int cw = cpw < 2 * CB ? 2 * CB : cpw;                                                     \
     if (nact > 0) {                                                                           \
       /* known active experts: as close to one workgroup per CU as N allows */                \
@@ -398,9 +440,9 @@ hipError_t launch_gemv_r(int act, const void *A, const int32_t *perm, int kslots
     }                                                                                         \
     if (N % cw) return hipErrorInvalidValue;                                                  \
     if (COMBINE && N / cw > FIX_SLOTS) return hipErrorInvalidValue;                           \
-    hipLaunchKernelGGL((gemv_kernel<SWIGLU, R, KC_, COMBINE>), dim3(G * (N / cw)),            \
-                       dim3(GV_THREADS), 0, s, a, perm, kslots, b1, b3, C, seg_off, active,    \
-                       nactive, N, K, cw, act, cm);                                            \
+    hipLaunchKernelGGL((gemv_kernel<SWIGLU, R, KC_, COMBINE, W8>), dim3(G * (N / cw)),        \
+                       dim3(GV_THREADS), 0, s, a, perm, kslots, B1, B3, C, seg_off, active,    \
+                       nactive, N, K, cw, act, cm, sc1, sc3);                                  \
     break;                                                                                    \
   }
   switch (kc) {
@@ -411,19 +453,20 @@ hipError_t launch_gemv_r(int act, const void *A, const int32_t *perm, int kslots
   return hipGetLastError();
 }
 
-template <bool SWIGLU, bool COMBINE = false>
+template <bool SWIGLU, bool COMBINE = false, bool W8 = false>
 hipError_t launch_gemv(int rows, int act, const void *A, const int32_t *perm, int kslots,
                        const void *B1, const void *B3, void *C, const int32_t *seg_off,
                        const int32_t *active, const int32_t *nactive, int G, int N, int K,
-                       int nact, const GemvCombine &cm, hipStream_t s) {
+                       int nact, const GemvCombine &cm, hipStream_t s,
+                       const float *sc1 = nullptr, const float *sc3 = nullptr) {
   if (rows <= 1)
-    return launch_gemv_r<SWIGLU, 1, COMBINE>(act, A, perm, kslots, B1, B3, C, seg_off, active,
-                                             nactive, G, N, K, nact, cm, s);
+    return launch_gemv_r<SWIGLU, 1, COMBINE, W8>(act, A, perm, kslots, B1, B3, C, seg_off,
+                                                 active, nactive, G, N, K, nact, cm, sc1, sc3, s);
   if (rows <= 2)
-    return launch_gemv_r<SWIGLU, 2, COMBINE>(act, A, perm, kslots, B1, B3, C, seg_off, active,
-                                             nactive, G, N, K, nact, cm, s);
-  return launch_gemv_r<SWIGLU, 4, COMBINE>(act, A, perm, kslots, B1, B3, C, seg_off, active,
-                                           nactive, G, N, K, nact, cm, s);
+    return launch_gemv_r<SWIGLU, 2, COMBINE, W8>(act, A, perm, kslots, B1, B3, C, seg_off,
+                                                 active, nactive, G, N, K, nact, cm, sc1, sc3, s);
+  return launch_gemv_r<SWIGLU, 4, COMBINE, W8>(act, A, perm, kslots, B1, B3, C, seg_off, active,
+                                               nactive, G, N, K, nact, cm, sc1, sc3, s);
 }
 
 }  // namespace
@@ -474,6 +517,27 @@ hipError_t launch_gemv_down_combine(int rows, const void *Hin, const void *W2, f
   const GemvCombine cm{inv, gate, T, k, (bf16_t *)y, cnt};
   return launch_gemv<false, true>(rows, 0, Hin, nullptr, 1, W2, nullptr, Y, seg_off, active,
                                   nactive, G, N, K, nact, cm, s);
+}
+
+hipError_t launch_gemv_swiglu_fp8(int rows, int act, const void *x, const int32_t *perm,
+                                  int kslots, const uint8_t *W1q, const uint8_t *W3q,
+                                  const float *s1, const float *s3, void *H,
+                                  const int32_t *seg_off, const int32_t *active,
+                                  const int32_t *nactive, int G, int N, int K, int nact,
+                                  hipStream_t s) {
+  return launch_gemv<true, false, true>(rows, act, x, perm, kslots, W1q, W3q, H, seg_off, active,
+                                        nactive, G, N, K, nact, GemvCombine{}, s, s1, s3);
+}
+
+hipError_t launch_gemv_down_combine_fp8(int rows, const void *Hin, const uint8_t *W2q,
+                                        const float *s2, float *Y, const int32_t *seg_off,
+                                        const int32_t *active, const int32_t *nactive, int G,
+                                        int N, int K, int nact, const int32_t *inv,
+                                        const float *gate, int T, int k, void *y, int32_t *cnt,
+                                        hipStream_t s) {
+  const GemvCombine cm{inv, gate, T, k, (bf16_t *)y, cnt};
+  return launch_gemv<false, true, true>(rows, 0, Hin, nullptr, 1, W2q, nullptr, Y, seg_off,
+                                        active, nactive, G, N, K, nact, cm, s, s2, nullptr);
 }
 
 }  // namespace moe

@@ -13,6 +13,25 @@ hipError_t launch_router(int dtype, const void *x, const void *Wg, const float *
                          int d, int E, int k, int gate_mode, int32_t *idx, float *gate,
                          float *logits, float *part, hipStream_t s);
 
+// Weight-only FP8 experts: per-expert E4M3 quantisation of E matrices of n
+// elements (dtype 1 bf16, 0 fp32); scale [E] out.
+hipError_t launch_quantize_fp8(int dtype, const void *W, int E, size_t n, uint8_t *q,
+                               float *scale, hipStream_t s);
+// The weight-streaming kernels on FP8 experts (scales s1/s3/s2 [E]); the down
+// projection also does the combine (launch_gemv_down_combine).
+hipError_t launch_gemv_swiglu_fp8(int rows, int act, const void *x, const int32_t *perm,
+                                  int kslots, const uint8_t *W1q, const uint8_t *W3q,
+                                  const float *s1, const float *s3, void *H,
+                                  const int32_t *seg_off, const int32_t *active,
+                                  const int32_t *nactive, int G, int N, int K, int nact,
+                                  hipStream_t s);
+hipError_t launch_gemv_down_combine_fp8(int rows, const void *Hin, const uint8_t *W2q,
+                                        const float *s2, float *Y, const int32_t *seg_off,
+                                        const int32_t *active, const int32_t *nactive, int G,
+                                        int N, int K, int nact, const int32_t *inv,
+                                        const float *gate, int T, int k, void *y, int32_t *cnt,
+                                        hipStream_t s);
+
 // Decode steps (T <= 4, T * k <= 64 pairs, E <= 64): the router's scores, then top-k,
 // gate and the grouping by expert in one more launch; outputs as
 // launch_router + launch_permute (capacity as there; zero: nzero int32

@@ -72,6 +72,11 @@ def lib():
         L.moe_forward_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i,
                                      ctypes.POINTER(_Options), vp, sz, vp, vp]
         L.moe_forward_ex.restype = i
+        L.moe_quantize_fp8.argtypes = [vp, i, ctypes.c_longlong, i, vp, vp, vp]
+        L.moe_quantize_fp8.restype = i
+        L.moe_forward_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i,
+                                      ctypes.POINTER(_Options), vp, sz, vp, vp]
+        L.moe_forward_fp8.restype = i
         _lib = L
     return _lib
 
@@ -264,3 +269,55 @@ def forward(x, Wg, W1, W3, W2, k, bias=None, shared=None, **variants):
     """y = MoE(x) for x [..., d] (allocates its workspace); `variants` are
     MoELayer's gate_mode / activation / capacity."""
     return MoELayer(Wg, W1, W3, W2, k, bias, shared, **variants)(x)
+
+
+def quantize_fp8(W: torch.Tensor):
+    """Per-expert FP8 (E4M3) quantisation of expert weights W [E, ...] (bf16 or
+    fp32) on the GPU: (codes uint8 of W's shape, scale fp32 [E])."""
+    E = W.shape[0]
+    q = torch.empty(W.shape, dtype=torch.uint8, device=W.device)
+    scale = torch.empty(E, dtype=torch.float32, device=W.device)
+    _check(lib().moe_quantize_fp8(_p(W), E, W.numel() // max(E, 1), _dt(W), _p(q), _p(scale),
+                                  _stream()), "moe_quantize_fp8")
+    return q, scale
+
+
+class MoELayerFP8:
+    """A layer whose experts hold FP8 weights (decode: at most four tokens per
+    call).  Built from bf16 weights, quantised once on the GPU; the router
+    stays bf16."""
+
+    def __init__(self, Wg, W1, W3, W2, k, bias=None, gate_mode=GATE_SOFTMAX_TOPK,
+                 activation=ACT_SWIGLU, capacity=-1):
+        self.Wg, self.k, self.bias = Wg, k, bias
+        self.E, self.d_ff, self.d = W1.shape
+        self.W1q, self.s1 = quantize_fp8(W1)
+        self.W3q, self.s3 = quantize_fp8(W3)
+        self.W2q, self.s2 = quantize_fp8(W2)
+        self.options = _Options(int(gate_mode), int(activation), int(capacity))
+        self._ws = None
+
+    def workspace(self, T):
+        n = workspace_bytes(T, self.d, self.d_ff, self.E, self.k, 0, MOE_BF16)
+        if self._ws is None or self._ws.numel() < n:
+            self._ws = torch.empty(n, dtype=torch.uint8, device=self.W1q.device)
+        return self._ws, n
+
+    def __call__(self, x: torch.Tensor, y: torch.Tensor | None = None) -> torch.Tensor:
+        T = x.shape[0]
+        if y is None:
+            y = torch.empty_like(x)
+        ws, n = self.workspace(T)
+        _check(lib().moe_forward_fp8(_p(x), _p(self.Wg), _p(self.bias), _p(self.W1q),
+                                     _p(self.W3q), _p(self.W2q), _p(self.s1), _p(self.s3),
+                                     _p(self.s2), T, self.E, self.k, self.d, self.d_ff,
+                                     ctypes.byref(self.options), _p(ws), n, _p(y), _stream()),
+               "moe_forward_fp8")
+        return y
+
+    def intermediates(self, T) -> dict:
+        """Routing intermediates of the last call (as MoELayer.intermediates)."""
+        proxy = MoELayer.__new__(MoELayer)
+        proxy.d, proxy.d_ff, proxy.E, proxy.k = self.d, self.d_ff, self.E, self.k
+        proxy.d_ff_shared, proxy.dtype, proxy._ws = 0, MOE_BF16, self._ws
+        return MoELayer.intermediates(proxy, T)

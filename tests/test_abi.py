@@ -132,6 +132,13 @@ def test_variant_entry_points_check_arguments(L):
         args = [fake, fake, None, fake, fake, fake, None, None, None, 0, 4, 8, k, 64, 64, 1,
                 ctypes.byref(opt), vp(0x100000), 1 << 40, vp(0x2000), None]
         assert L.moe_forward_ex(*args) == -1
+    # FP8 experts: quantiser dtype / sizes; the forward is a decode path
+    assert L.moe_quantize_fp8(fake, 4, 16, 7, fake, fake, None) == -2
+    assert L.moe_quantize_fp8(fake, -1, 16, 1, fake, fake, None) == -1
+    assert L.moe_quantize_fp8(None, 0, 16, 1, None, None, None) == 0
+    for T, d, dff in ((5, 2048, 2048), (2, 1024, 2048), (2, 2048, 3072)):
+        assert L.moe_forward_fp8(fake, fake, None, fake, fake, fake, fake, fake, fake, T, 8, 2,
+                                 d, dff, None, vp(0x100000), 1 << 40, vp(0x2000), None) == -1
     # permute_ex: too-small workspace is still caught
     assert L.moe_permute_ex(fake, 4, 8, 2, 3, fake, fake, fake, fake, vp(0x100000), 8,
                             None) == -3
