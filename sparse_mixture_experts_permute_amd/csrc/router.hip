@@ -277,6 +277,21 @@ __device__ __forceinline__ void wave_topk_gate(const float (&v)[4], int E, int k
   }
 }
 
+// Sum of a score's S slice partials (stride apart), in slice order; the loads
+// go out eight at a time so that their latencies overlap.
+__device__ __forceinline__ float sum_partials(const float *__restrict__ p, size_t stride, int S) {
+  float l = 0.f;
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = s0 + i < S ? p[(size_t)(s0 + i) * stride] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (s0 + i < S) l += v[i];
+  }
+  return l;
+}
+
 // One wavefront per token: scores (partials summed in slice order), top-k, gate.
 __global__ __launch_bounds__(256) void router_topk_kernel(
     const float *__restrict__ part, int S, const float *__restrict__ bias, int T_, int E, int k,
@@ -293,8 +308,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
     const int e = lane + kWave * j;
     float l = -INFINITY;
     if (e < E) {
-      l = 0.f;
-      for (int s = 0; s < S; ++s) l += part[((size_t)s * T_ + t) * E + e];
+      l = sum_partials(part + (size_t)t * E + e, (size_t)T_ * E, S);
       if (bias) l += bias[e];
       if (logits) logits[(size_t)t * E + e] = l;
     }
@@ -327,8 +341,7 @@ __global__ __launch_bounds__(256) void topk_permute_tiny_kernel(
     float v[4];
     v[0] = -INFINITY;
     if (lane < E) {
-      float l = 0.f;
-      for (int s = 0; s < S; ++s) l += part[((size_t)s * T_ + t) * E + lane];
+      float l = sum_partials(part + (size_t)t * E + lane, (size_t)T_ * E, S);
       if (bias) l += bias[lane];
       logits[(size_t)t * E + lane] = l;
       v[0] = l;
