@@ -3,6 +3,7 @@
 // GEMM -> combine, all enqueued on the caller's stream with no host sync.
 #include <string.h>
 
+#include <algorithm>
 #include <cmath>
 
 #include "../../include/moe_mi355x.h"
@@ -334,13 +335,24 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
   // single-token-scale batches without a shared expert: the down projection's
   // last workgroups also do the combine
   const bool fused_combine = sk.gemv && !shared;
+  // a single token with a small router: the SwiGLU weight-streaming kernel
+  // routes it itself (no score or top-k launches)
+  const bool route_fused = sk.gemv && moe::route_fused_ok(T, d, E, k);
+  const moe::DecodeRoute rt{Wg, bias, E, k, o.gate_mode,
+                            o.capacity < 0 || o.capacity > P ? P : o.capacity,
+                            plan.bm1, plan.bm2, logits, idx, gate, counts, offsets, perm, inv,
+                            mt0, mt1, shseg, act, fixc, moe::FIX_SLOTS};
+  // experts a weight-streaming grid covers: at most P are active
+  const int G = std::min(E, P);
 
   hipError_t e;
   // stage boundary i: an optional timing event recorded on the stream
 #define MOE_MARK(i) \
   if (events && hipEventRecord((hipEvent_t)events[i], s) != hipSuccess) goto fail;
   MOE_MARK(0);
-  if (moe::route_permute_tiny_ok(T, E, k)) {
+  if (route_fused) {
+    MOE_MARK(1);
+  } else if (moe::route_permute_tiny_ok(T, E, k)) {
     // a small batch: scores, then top-k, gate and grouping in one more launch
     if ((e = moe::launch_route_permute_tiny(dtype, x, Wg, bias, T, d, E, k, o.gate_mode,
                                             o.capacity, plan.bm1, plan.bm2, logits, idx, gate,
@@ -365,22 +377,26 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
     MOE_MARK(3);
     // a single token activates exactly k experts (fewer only under a capacity)
     const int nact = T == 1 ? k : 0;
-    if ((e = f8 ? moe::launch_gemv_swiglu_fp8(T, o.activation, x, perm, k, f8->W1q, f8->W3q,
-                                              f8->s1, f8->s3, H, offsets, act, act + E, E, d_ff,
-                                              d, nact, s)
+    if ((e = route_fused
+                 ? moe::launch_gemv_swiglu_routed(o.activation, x, rt, f8 ? f8->W1q : W1,
+                                                  f8 ? f8->W3q : W3, f8 ? f8->s1 : nullptr,
+                                                  f8 ? f8->s3 : nullptr, H, d_ff, d, s)
+             : f8 ? moe::launch_gemv_swiglu_fp8(T, o.activation, x, perm, k, f8->W1q, f8->W3q,
+                                                f8->s1, f8->s3, H, offsets, act, act + E, G,
+                                                d_ff, d, nact, s)
              : sk.gemv ? moe::launch_gemv_swiglu(T, o.activation, x, perm, k, W1, W3, H, offsets,
-                                               act, act + E, E, d_ff, d, nact, s)
+                                               act, act + E, G, d_ff, d, nact, s)
                      : moe::launch_skinny_swiglu(sk.mb, o.activation, x, perm, k, W1, W3, H,
                                                  offsets, act, act + E, E, d_ff, d, s)))
       goto fail;
     MOE_MARK(4);
     if ((e = f8 ? moe::launch_gemv_down_combine_fp8(T, H, f8->W2q, f8->s2, Yp, offsets, act,
-                                                    act + E, E, d, d_ff, nact, inv, gate, T, k,
+                                                    act + E, G, d, d_ff, nact, inv, gate, T, k,
                                                     y, fixc, s)
              : fused_combine
-                 ? moe::launch_gemv_down_combine(T, H, W2, Yp, offsets, act, act + E, E, d, d_ff,
+                 ? moe::launch_gemv_down_combine(T, H, W2, Yp, offsets, act, act + E, G, d, d_ff,
                                                  nact, inv, gate, T, k, y, fixc, s)
-             : sk.gemv ? moe::launch_gemv_down(T, H, W2, Yp, offsets, act, act + E, E, d, d_ff,
+             : sk.gemv ? moe::launch_gemv_down(T, H, W2, Yp, offsets, act, act + E, G, d, d_ff,
                                                nact, s)
                        : moe::launch_skinny_down(sk.mb, H, W2, Yp, offsets, act, act + E, E, d,
                                                  d_ff, s)))

@@ -22,6 +22,7 @@
 #include <type_traits>
 #include "common.h"
 #include "kernels.h"
+#include "route_block.h"
 
 namespace moe {
 
@@ -252,17 +253,102 @@ struct GemvCombine {
   bf16_t *y;
   int32_t *cnt;
 };
+// ROUTE (SwiGLU, one token): the workgroup routes the token itself before it
+// streams weights.  The router scores come from a fixed split of the features
+// (thread i: the 16-byte chunks i, i + 256, ...; lanes then waves summed in a
+// fixed order), so every workgroup computes the same scores, top-k, gates and
+// grouping; workgroup 0 also writes them out for the launches that follow.
+struct RouteLds {
+  float red[GV_WAVES][64];
+  float logit[64], selv[64], gate[64];
+  int32_t seli[64], idx[64], counts[64], perm[64], inv[64];
+  int32_t offsets[65], mt0[65], mt1[65], active[65], shseg[8];
+};
+__device__ __forceinline__ void route_token(const bf16_t *__restrict__ x, int d,
+                                            const DecodeRoute &rt, RouteLds &rs) {
+  const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
+  const int E = rt.E;
+  const uint4 *xq = reinterpret_cast<const uint4 *>(x);
+  const uint4 *wq = reinterpret_cast<const uint4 *>(rt.Wg);
+  const int rowq = d / 8;               // 16-byte chunks per row
+  const int nj = d / (GV_THREADS * 8);  // chunks per thread (d is a multiple of 2048)
+  for (int e0 = 0; e0 < E; e0 += 8) {
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    for (int j = 0; j < nj; ++j) {
+      const int q = tid + GV_THREADS * j;
+      const uint4 xv = xq[q];
+      uint4 wv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        wv[i] = e0 + i < E ? wq[(size_t)(e0 + i) * rowq + q] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = dot8_bf16(xv, wv[i], acc[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float v = acc[i];
+#pragma unroll
+      for (int off = kWave / 2; off > 0; off >>= 1) v += __shfl_xor(v, off);
+      if (lane == 0 && e0 + i < E) rs.red[wave][e0 + i] = v;
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    float v[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    if (lane < E) {
+      float l = rs.red[0][lane];
+#pragma unroll
+      for (int w = 1; w < GV_WAVES; ++w) l += rs.red[w][lane];
+      if (rt.bias) l += rt.bias[lane];
+      rs.logit[lane] = l;
+      v[0] = l;
+    }
+    wave_topk_gate(v, E, rt.k, rt.gate_mode, rs.selv, rs.seli, rs.idx, rs.gate);
+    // lane j wrote idx[j] and reads it back as pair j's expert
+    wave_group_pairs(rs.idx, 1, E, rt.k, rt.capacity, rt.bm0, rt.bm1,
+                     RouteOut{rs.counts, rs.offsets, rs.perm, rs.inv, rs.mt0, rs.mt1, rs.shseg,
+                              rs.active});
+  }
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    const int k = rt.k, kept = rs.offsets[E], na = rs.active[E];
+    for (int i = tid; i < rt.nzero; i += GV_THREADS) rt.zero[i] = 0;
+    if (tid < E) {
+      rt.logits[tid] = rs.logit[tid];
+      rt.counts[tid] = rs.counts[tid];
+    }
+    if (tid <= E) {
+      rt.offsets[tid] = rs.offsets[tid];
+      rt.mtiles0[tid] = rs.mt0[tid];
+      rt.mtiles1[tid] = rs.mt1[tid];
+    }
+    if (tid < k) {
+      rt.idx[tid] = rs.idx[tid];
+      rt.gate[tid] = rs.gate[tid];
+      rt.inv[tid] = rs.inv[tid];
+    }
+    if (tid < kept) rt.perm[tid] = rs.perm[tid];
+    if (tid < na) rt.active[tid] = rs.active[tid];
+    if (tid == 0) rt.active[E] = na;
+    if (tid < 8) rt.shared_seg[tid] = rs.shseg[tid];
+  }
+}
+
 //
 // W8: FP8 weights (uint8 E4M3 codes) with per-expert scales sc1 (W1 or W2) and
 // sc3 (W3).
-template <bool SWIGLU, int R, int KC, bool COMBINE = false, bool W8 = false>
+template <bool SWIGLU, int R, int KC, bool COMBINE = false, bool W8 = false,
+          bool ROUTE = false>
 __global__ __launch_bounds__(GV_THREADS) void gemv_kernel(
     const bf16_t *__restrict__ A, const int32_t *__restrict__ perm, int kslots,
     const void *__restrict__ B1v, const void *__restrict__ B3v, void *__restrict__ C,
     const int32_t *__restrict__ seg_off, const int32_t *__restrict__ active,
     const int32_t *__restrict__ nactive, int N, int K, int cpw, int act, GemvCombine cm,
-    const float *__restrict__ sc1, const float *__restrict__ sc3) {
+    const float *__restrict__ sc1, const float *__restrict__ sc3, DecodeRoute rt) {
   static_assert(!(SWIGLU && COMBINE), "the combine follows the down projection");
+  static_assert(SWIGLU || !ROUTE, "a token is routed before its SwiGLU projection");
   using WT = typename std::conditional<W8, uint8_t, bf16_t>::type;  // weight element
   using WV = typename std::conditional<W8, uint2, uint4>::type;     // 8 weights
   constexpr int NW = SWIGLU ? 2 : 1;
@@ -270,6 +356,14 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_kernel(
   __shared__ float red[2][GV_WAVES][CB][NW][R];
   __shared__ int arrived;
 
+  __shared__ typename std::conditional<ROUTE, RouteLds, char>::type rsh;
+  if constexpr (ROUTE) {
+    route_token(A, K, rt, rsh);
+    seg_off = rsh.offsets;
+    active = rsh.active;
+    nactive = rsh.active + rt.E;
+    perm = rsh.perm;
+  }
   const int nblk = N / cpw;
   const int a_idx = blockIdx.x / nblk;
   if (COMBINE && nactive[0] == 0) {
@@ -412,12 +506,12 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_kernel(
   }
 }
 
-template <bool SWIGLU, int R, bool COMBINE = false, bool W8 = false>
+template <bool SWIGLU, int R, bool COMBINE = false, bool W8 = false, bool ROUTE = false>
 hipError_t launch_gemv_r(int act, const void *A, const int32_t *perm, int kslots,
                          const void *B1, const void *B3, void *C, const int32_t *seg_off,
                          const int32_t *active, const int32_t *nactive, int G, int N, int K,
                          int nact, const GemvCombine &cm, const float *sc1, const float *sc3,
-                         hipStream_t s) {
+                         hipStream_t s, const DecodeRoute &rt = DecodeRoute{}) {
   const int kc = K / (GV_WAVES * GV_CHUNK);
   constexpr int NW = SWIGLU ? 2 : 1;
   // columns per workgroup: a power of two from two groups up to 256, with
@@ -440,9 +534,9 @@ hipError_t launch_gemv_r(int act, const void *A, const int32_t *perm, int kslots
     }                                                                                         \
     if (N % cw) return hipErrorInvalidValue;                                                  \
     if (COMBINE && N / cw > FIX_SLOTS) return hipErrorInvalidValue;                           \
-    hipLaunchKernelGGL((gemv_kernel<SWIGLU, R, KC_, COMBINE, W8>), dim3(G * (N / cw)),        \
+    hipLaunchKernelGGL((gemv_kernel<SWIGLU, R, KC_, COMBINE, W8, ROUTE>), dim3(G * (N / cw)), \
                        dim3(GV_THREADS), 0, s, a, perm, kslots, B1, B3, C, seg_off, active,    \
-                       nactive, N, K, cw, act, cm, sc1, sc3);                                  \
+                       nactive, N, K, cw, act, cm, sc1, sc3, rt);                              \
     break;                                                                                    \
   }
   switch (kc) {
@@ -538,6 +632,24 @@ hipError_t launch_gemv_down_combine_fp8(int rows, const void *Hin, const uint8_t
   const GemvCombine cm{inv, gate, T, k, (bf16_t *)y, cnt};
   return launch_gemv<false, true, true>(rows, 0, Hin, nullptr, 1, W2q, nullptr, Y, seg_off,
                                         active, nactive, G, N, K, nact, cm, s, s2, nullptr);
+}
+
+bool route_fused_ok(int T, int d, int E, int k) {
+  return T == 1 && E >= 1 && E <= 64 && k <= E && (long long)E * d <= 65536 &&
+         d % (GV_THREADS * 8) == 0;
+}
+
+hipError_t launch_gemv_swiglu_routed(int act, const void *x, const DecodeRoute &r, const void *W1,
+                                     const void *W3, const float *s1, const float *s3, void *H,
+                                     int N, int K, hipStream_t s) {
+  // one token: at most k experts are active, and the grid covers exactly k
+  if (s1)
+    return launch_gemv_r<true, 1, false, true, true>(act, x, nullptr, r.k, W1, W3, H, nullptr,
+                                                     nullptr, nullptr, r.k, N, K, r.k,
+                                                     GemvCombine{}, s1, s3, s, r);
+  return launch_gemv_r<true, 1, false, false, true>(act, x, nullptr, r.k, W1, W3, H, nullptr,
+                                                    nullptr, nullptr, r.k, N, K, r.k,
+                                                    GemvCombine{}, nullptr, nullptr, s, r);
 }
 
 }  // namespace moe

@@ -45,6 +45,30 @@ hipError_t launch_route_permute_tiny(int dtype, const void *x, const void *Wg, c
                                      int32_t *shared_seg, int32_t *active, int32_t *zero,
                                      int nzero, float *part, hipStream_t s);
 
+// A single token whose router fits every workgroup (E * d <= 65536, E <= 64):
+// the SwiGLU weight-streaming kernel routes it itself.  Each of its
+// workgroups computes the token's scores, top-k, gate and grouping (the same
+// instructions on the same data, so all reach the same routing) and takes its
+// expert from them; workgroup 0 writes the routing outputs as
+// launch_route_permute_tiny does (capacity clamped to [0, k] by the caller)
+// and clears `zero`.
+struct DecodeRoute {
+  const void *Wg;
+  const float *bias;
+  int E, k, gate_mode, capacity, bm0, bm1;
+  float *logits;
+  int32_t *idx;
+  float *gate;
+  int32_t *counts, *offsets, *perm, *inv, *mtiles0, *mtiles1, *shared_seg, *active;
+  int32_t *zero;
+  int nzero;
+};
+bool route_fused_ok(int T, int d, int E, int k);
+// s1 / s3 NULL: bf16 W1 / W3; else FP8 codes with these per-expert scales
+hipError_t launch_gemv_swiglu_routed(int act, const void *x, const DecodeRoute &r, const void *W1,
+                                     const void *W3, const float *s1, const float *s3, void *H,
+                                     int N, int K, hipStream_t s);
+
 int permute_nblocks(int P);
 // capacity: pairs an expert keeps (its first ones in pair order); >= T*k keeps
 // all.  Dropped pairs (and ids outside [0, E)) get inv = -1.

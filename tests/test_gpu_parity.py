@@ -199,7 +199,8 @@ def test_forward_sampled_full_size(name):
     assert err <= TOL[cfg.dtype]
 
 
-@pytest.mark.parametrize("name", ["mixtral_prefill_T2048", "fine_shared_T512"])
+@pytest.mark.parametrize("name", ["mixtral_prefill_T2048", "fine_shared_T512",
+                                  "mixtral_decode_T1"])
 def test_deterministic(name):
     cfg = CONFIGS[name]
     say(f"determinism {name}")
@@ -245,6 +246,9 @@ EDGE = [
     ("gemv_T1", 1, 2048, 8, 2048, 2, "bf16", 0, None),
     ("gemv_T2_K6144_shared", 2, 2048, 4, 6144, 2, "bf16", 2048, None),
     ("gemv_T4_hot_expert", 4, 2048, 8, 4096, 2, "bf16", 0, ("hot", 1, 100.0)),
+    # one token routed inside the SwiGLU weight-streaming kernel (E * d <= 65536)
+    ("routed_T1_E32_k4_hot", 1, 2048, 32, 2048, 4, "bf16", 0, ("hot", 31, 100.0)),
+    ("routed_T1_E16_shared_limit", 1, 4096, 16, 2048, 2, "bf16", 4096, None),
 ]
 
 
@@ -271,7 +275,7 @@ def test_edge_cases(case_):
     err = rel_l2(f64(moe.tensor_to_numpy(y)), ref["y"])
     say(f"edge {label}: rel-L2 {err:.3e}")
     assert err <= TOL[dt]
-    if label.startswith("kplanes"):
+    if label.startswith(("kplanes", "gemv_T1", "routed")):
         # a workspace full of garbage gives the same bits
         y1 = y.clone()
         L._ws.fill_(0x5A)

@@ -39,7 +39,8 @@ def inputs(T, d, E, dff, k, dtype, dffs=0, seed=7, skew=0.0):
     return cfg, h, dev
 
 
-# (label, T, d, E, d_ff, k, dtype, d_ff_shared, skew, gate_mode, activation, capacity)
+# (label, T, d, E, d_ff, k, dtype, d_ff_shared, skew, gate_mode, activation, capacity[,
+#  seed])
 CASES = [
     ("softmax_all_bf16", 300, 256, 8, 512, 2, "bf16", 0, 0.0, 1, 0, None),
     ("sigmoid_gate_glu_f32", 200, 128, 6, 256, 2, "f32", 0, 0.0, 2, 1, None),
@@ -62,13 +63,21 @@ CASES = [
     ("entropy_k3_bf16", 300, 256, 8, 512, 3, "bf16", 0, 0.0, 3, 0, None),
     ("entropy_k3_shared_cap_f32", 150, 128, 6, 128, 3, "f32", 64, 0.0, 3, 0, 40),
     ("entropy_decode_T4_bf16", 4, 2048, 8, 2048, 3, "bf16", 0, 0.0, 3, 0, None),
+    # one token, routed by the SwiGLU weight-streaming kernel itself (E * d <= 65536)
+    ("routed_T1_skew_softmax_all_glu_bf16", 1, 2048, 8, 2048, 2, "bf16", 0, 1.5, 1, 1, None),
+    ("routed_T1_E32_k4_cap1_bf16", 1, 2048, 32, 2048, 4, "bf16", 0, 0.0, 0, 0, 1),
+    ("routed_T1_sigmoid_shared_bf16", 1, 2048, 16, 2048, 2, "bf16", 2048, 0.0, 2, 0, None),
+    ("routed_T1_cap0_bf16", 1, 4096, 8, 2048, 2, "bf16", 0, 0.0, 0, 0, 0),
+    ("routed_T1_entropy_k2_bf16", 1, 4096, 8, 2048, 3, "bf16", 0, 0.0, 3, 0, None),
+    ("routed_T1_entropy_k3_bf16", 1, 4096, 8, 2048, 3, "bf16", 0, 0.0, 3, 0, None, 41),
 ]
 
 
 @pytest.mark.parametrize("c", CASES, ids=[c[0] for c in CASES])
 def test_variant_forward(c):
-    label, T, d, E, dff, k, dtype, dffs, skew, gm, act, cap = c
-    cfg, h, dev = inputs(T, d, E, dff, k, dtype, dffs, skew=skew)
+    label, T, d, E, dff, k, dtype, dffs, skew, gm, act, cap = c[:12]
+    seed = c[12] if len(c) > 12 else 7
+    cfg, h, dev = inputs(T, d, E, dff, k, dtype, dffs, skew=skew, seed=seed)
     if cap == "page":
         cap = moe.capacity(T, k, 1.2)        # min(k*T, floor(1.2*T))
     elif isinstance(cap, float):
