@@ -342,6 +342,9 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
                             o.capacity < 0 || o.capacity > P ? P : o.capacity,
                             plan.bm1, plan.bm2, logits, idx, gate, counts, offsets, perm, inv,
                             mt0, mt1, shseg, act, fixc, moe::FIX_SLOTS};
+  // one token without a shared expert: a workgroup per column block covers
+  // all its experts and forms y itself
+  const bool token_down = fused_combine && T == 1 && moe::gemv_token_ok(d, d_ff, k);
   // experts a weight-streaming grid covers: at most P are active
   const int G = std::min(E, P);
 
@@ -390,7 +393,10 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
                                                  offsets, act, act + E, E, d_ff, d, s)))
       goto fail;
     MOE_MARK(4);
-    if ((e = f8 ? moe::launch_gemv_down_combine_fp8(T, H, f8->W2q, f8->s2, Yp, offsets, act,
+    if ((e = token_down
+                 ? moe::launch_gemv_down_token(H, f8 ? f8->W2q : W2, f8 ? f8->s2 : nullptr, offsets,
+                                               act, act + E, d, d_ff, inv, gate, k, y, s)
+             : f8 ? moe::launch_gemv_down_combine_fp8(T, H, f8->W2q, f8->s2, Yp, offsets, act,
                                                     act + E, G, d, d_ff, nact, inv, gate, T, k,
                                                     y, fixc, s)
              : fused_combine

@@ -272,19 +272,26 @@ __device__ __forceinline__ void route_token(const bf16_t *__restrict__ x, int d,
   const uint4 *wq = reinterpret_cast<const uint4 *>(rt.Wg);
   const int rowq = d / 8;               // 16-byte chunks per row
   const int nj = d / (GV_THREADS * 8);  // chunks per thread (d is a multiple of 2048)
+  constexpr int JU = 4;  // chunks whose loads go out together (one round trip up to d = 8192)
   for (int e0 = 0; e0 < E; e0 += 8) {
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    for (int j = 0; j < nj; ++j) {
-      const int q = tid + GV_THREADS * j;
-      const uint4 xv = xq[q];
-      uint4 wv[8];
+    for (int j0 = 0; j0 < nj; j0 += JU) {
+      uint4 xv[JU], wv[JU][8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        wv[i] = e0 + i < E ? wq[(size_t)(e0 + i) * rowq + q] : make_uint4(0, 0, 0, 0);
+      for (int u = 0; u < JU; ++u) {
+        const int q = tid + GV_THREADS * (j0 + u);
+        const bool in = j0 + u < nj;
+        xv[u] = in ? xq[q] : make_uint4(0, 0, 0, 0);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = dot8_bf16(xv, wv[i], acc[i]);
+        for (int i = 0; i < 8; ++i)
+          wv[u][i] = in && e0 + i < E ? wq[(size_t)(e0 + i) * rowq + q] : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < JU; ++u)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = dot8_bf16(xv[u], wv[u][i], acc[i]);
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -506,6 +513,129 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_kernel(
   }
 }
 
+// One token's down projection with the combine inside: a workgroup owns a
+// block of cw <= GT_COLS output columns for EVERY active expert, so the
+// token's k outputs of a column meet in its LDS and y is formed there (no
+// partial outputs leave the workgroup, no arrival counting).  The workgroup
+// walks (active expert, column group) units with two groups of weights in
+// flight across expert boundaries; the next expert's row of H is loaded with
+// the first weights of that expert.  Per column the arithmetic is that of
+// gemv_kernel (lanes by the butterfly, then waves in order, then the FP8
+// scale) followed by the combine kernel's (fmaf over j ascending, dropped
+// pairs skipped).
+constexpr int GT_COLS = 64, GT_SLOTS = 64;
+template <int KC, bool W8>
+__global__ __launch_bounds__(GV_THREADS) void gemv_down_token_kernel(
+    const bf16_t *__restrict__ H, const void *__restrict__ W2v,
+    const int32_t *__restrict__ seg_off, const int32_t *__restrict__ active,
+    const int32_t *__restrict__ nactive, int N, int K, int cw, const int32_t *__restrict__ inv,
+    const float *__restrict__ gate, int k, bf16_t *__restrict__ y, const float *__restrict__ sc) {
+  using WT = typename std::conditional<W8, uint8_t, bf16_t>::type;
+  using WV = typename std::conditional<W8, uint2, uint4>::type;
+  constexpr int CB = gv_cb(KC);
+  __shared__ float red[2][GV_WAVES][CB];
+  __shared__ float ys[GT_SLOTS][GT_COLS];  // [slot of H][column of the block]
+  __shared__ int ex[GT_SLOTS], slot[GT_SLOTS];
+  __shared__ float scl[GT_SLOTS];
+
+  const int tid = threadIdx.x;
+  const int c0 = blockIdx.x * cw;
+  const int na = nactive[0];
+  if (na == 0) {  // every pair dropped: y is zero
+    for (int i = tid; i < cw; i += GV_THREADS) y[c0 + i] = 0;
+    return;
+  }
+  if (tid < na) {
+    const int e = active[tid];
+    ex[tid] = e;
+    slot[tid] = seg_off[e];
+    scl[tid] = W8 ? sc[e] : 1.f;
+  }
+  __syncthreads();
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = lane_id();
+  const int kl = wave * KC * GV_CHUNK + lane * 8;
+  const WT *w0 = reinterpret_cast<const WT *>(W2v) + kl;
+  const int ngroups = cw / CB;  // even
+  const int units = na * ngroups;
+  const int rot = blockIdx.x % ngroups;  // see gemv_kernel
+  auto col_of = [&](int g) { return ((g + rot) % ngroups) * CB; };  // inside the block
+  auto load = [&](WV (&dst)[CB][KC], int u) {
+    const int a = u / ngroups;
+    const WT *w = w0 + (size_t)ex[a] * N * K;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const size_t ro = (size_t)(c0 + col_of(u % ngroups) + cb) * K;
+#pragma unroll
+      for (int i = 0; i < KC; ++i) dst[cb][i] = gv_load(w + ro + i * GV_CHUNK);
+    }
+  };
+  uint4 xa[KC], xn[KC];
+  auto load_x = [&](uint4 (&dst)[KC], int a) {
+    const bf16_t *ap = H + (size_t)slot[a] * K + kl;
+#pragma unroll
+    for (int i = 0; i < KC; ++i) dst[i] = *reinterpret_cast<const uint4 *>(ap + i * GV_CHUNK);
+  };
+  auto compute = [&](const WV (&wv)[CB][KC], int u, int rb) {
+    float acc[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      float t = 0.f;
+#pragma unroll
+      for (int i = 0; i < KC; ++i) t = gv_dot(xa[i], wv[cb][i], t);
+#pragma unroll
+      for (int off = kWave / 2; off > 0; off >>= 1) t += __shfl_xor(t, off);
+      acc[cb] = t;
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) red[rb][wave][cb] = acc[cb];
+    }
+    lds_barrier();
+    if (tid < CB) {
+      const int a = u / ngroups;
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < GV_WAVES; ++w) v += red[rb][w][tid];
+      if (W8) v *= scl[a];
+      ys[slot[a]][col_of(u % ngroups) + tid] = v;
+    }
+    // red[rb] is written again two units later, after the next barrier
+  };
+  WV wa[CB][KC], wb[CB][KC];
+  load_x(xa, 0);
+  load(wa, 0);
+  load(wb, 1);
+  int u = 0;
+  for (; u + 2 < units; u += 2) {
+    // units come in pairs of one expert (ngroups is even)
+    if (u > 0 && u % ngroups == 0) {
+#pragma unroll
+      for (int i = 0; i < KC; ++i) xa[i] = xn[i];
+    }
+    compute(wa, u, 0);
+    if ((u + 2) % ngroups == 0) load_x(xn, (u + 2) / ngroups);
+    load(wa, u + 2);
+    compute(wb, u + 1, 1);
+    load(wb, u + 3);
+  }
+  if (u > 0 && u % ngroups == 0) {
+#pragma unroll
+    for (int i = 0; i < KC; ++i) xa[i] = xn[i];
+  }
+  compute(wa, u, 0);
+  compute(wb, u + 1, 1);
+  __syncthreads();
+  for (int c = tid; c < cw; c += GV_THREADS) {
+    float acc = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const int s = inv[j];
+      if (s < 0) continue;
+      acc = fmaf(gate[j], ys[s][c], acc);
+    }
+    y[c0 + c] = f32_to_bf16(acc);
+  }
+}
+
 template <bool SWIGLU, int R, bool COMBINE = false, bool W8 = false, bool ROUTE = false>
 hipError_t launch_gemv_r(int act, const void *A, const int32_t *perm, int kslots,
                          const void *B1, const void *B3, void *C, const int32_t *seg_off,
@@ -650,6 +780,39 @@ hipError_t launch_gemv_swiglu_routed(int act, const void *x, const DecodeRoute &
   return launch_gemv_r<true, 1, false, false, true>(act, x, nullptr, r.k, W1, W3, H, nullptr,
                                                     nullptr, nullptr, r.k, N, K, r.k,
                                                     GemvCombine{}, nullptr, nullptr, s, r);
+}
+
+bool gemv_token_ok(int N, int K, int k) { return gemv_ok(N, K) && k <= GT_SLOTS; }
+
+hipError_t launch_gemv_down_token(const void *H, const void *W2, const float *s2,
+                                  const int32_t *seg_off, const int32_t *active,
+                                  const int32_t *nactive, int N, int K, const int32_t *inv,
+                                  const float *gate, int k, void *y, hipStream_t s) {
+  if (!gemv_token_ok(N, K, k)) return hipErrorInvalidValue;
+  const int kc = K / (GV_WAVES * GV_CHUNK);
+#define GT_CASE(KC_)                                                                        \
+  case KC_: {                                                                               \
+    constexpr int CB = gv_cb(KC_);                                                          \
+    /* the narrowest block (two groups) up to GT_COLS that keeps to one workgroup per CU */ \
+    int cw = 2 * CB;                                                                        \
+    while (N / cw > 256 && 2 * cw <= GT_COLS && N % (2 * cw) == 0) cw *= 2;                 \
+    if (N % cw) return hipErrorInvalidValue;                                                \
+    if (s2)                                                                                 \
+      hipLaunchKernelGGL((gemv_down_token_kernel<KC_, true>), dim3(N / cw), dim3(GV_THREADS), \
+                         0, s, (const bf16_t *)H, W2, seg_off, active, nactive, N, K, cw, inv, \
+                         gate, k, (bf16_t *)y, s2);                                         \
+    else                                                                                    \
+      hipLaunchKernelGGL((gemv_down_token_kernel<KC_, false>), dim3(N / cw), dim3(GV_THREADS), \
+                         0, s, (const bf16_t *)H, W2, seg_off, active, nactive, N, K, cw, inv, \
+                         gate, k, (bf16_t *)y, nullptr);                                    \
+    break;                                                                                  \
+  }
+  switch (kc) {
+    GT_CASE(1) GT_CASE(2) GT_CASE(3) GT_CASE(4) GT_CASE(5) GT_CASE(6) GT_CASE(7) GT_CASE(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef GT_CASE
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -140,6 +140,15 @@ hipError_t launch_gemv_down_combine(int rows, const void *Hin, const void *W2, f
                                     const int32_t *nactive, int G, int N, int K, int nact,
                                     const int32_t *inv, const float *gate, int T, int k, void *y,
                                     int32_t *cnt, hipStream_t s);
+// One token's down projection and combine (no shared expert, k <= 64): one
+// workgroup per block of output columns covers every active expert, forms y
+// [N] (bf16) in LDS as launch_combine would, and writes no partial outputs.
+// s2 NULL: bf16 W2; else FP8 codes with these per-expert scales.
+bool gemv_token_ok(int N, int K, int k);
+hipError_t launch_gemv_down_token(const void *H, const void *W2, const float *s2,
+                                  const int32_t *seg_off, const int32_t *active,
+                                  const int32_t *nactive, int N, int K, const int32_t *inv,
+                                  const float *gate, int k, void *y, hipStream_t s);
 hipError_t launch_skinny_swiglu(int mb, int act, const void *x, const int32_t *perm, int kslots,
                                 const void *W1, const void *W3, void *H,
                                 const int32_t *seg_off, const int32_t *active,
