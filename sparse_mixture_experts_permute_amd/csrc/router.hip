@@ -12,10 +12,12 @@
 //  scores : partial scores over S slices of the feature dimension, each slice
 //           written to its own plane of a [S][T][E] buffer; S is chosen so the
 //           grid fills the GPU.  Two shapes:
-//           - up to 32 experts: one wavefront per (token, slice); lanes split the
-//             slice with 16-byte loads, keep all E sums in registers and reduce
-//             them with a butterfly at the end (the router weights, at most
-//             32 x d, stay in L2);
+//           - up to 32 experts: four tokens per wavefront, 16 lanes each, which
+//             split the slice with 16-byte loads, keep all E sums in registers
+//             and reduce them over the 16 lanes at the end (the router weights,
+//             at most 32 x d, stay in L2 and each load of them serves four
+//             tokens).  With one slice (large batches) and k <= 16 this kernel
+//             also runs the top-k and the gate, and there is no second kernel;
 //           - more experts: a register-tiled VALU GEMM.  A 256-thread block owns
 //             64 tokens x 64 experts x one slice; each thread keeps 4 x 4 sums
 //             and streams its slice through LDS in 64-element chunks
@@ -149,40 +151,210 @@ __global__ __launch_bounds__(RS_THREADS, 2) void router_scores_kernel(
   }
 }
 
-// Up to 32 experts: one wavefront per (token, slice of NS*64*VEC features).
-template <typename T, int EB>
-__global__ __launch_bounds__(256) void router_scores_narrow_kernel(
+// Top-k and gate of one token from its E (<= EB) scores held by every lane of
+// a group (the same rule and arithmetic as wave_topk_gate: picks by strict >
+// in expert order, so ties go to the lower index; the sums run in expert or
+// pick order instead of the butterfly's).  Lane j < k of the group writes pick
+// j.  Returns nothing; idx / gate point at the token's k slots.
+template <int EB>
+__device__ __forceinline__ void group_topk_gate(const float (&v)[EB], int E, int k, int gate_mode,
+                                                int li, int32_t *__restrict__ idx,
+                                                float *__restrict__ gate) {
+  unsigned taken = 0;
+  float m = 0.f, zsel = 0.f, myv = 0.f;
+  int myi = 0;
+  for (int r = 0; r < k; ++r) {
+    float bv = -INFINITY;
+    int bi = -1;
+#pragma unroll
+    for (int e = 0; e < EB; ++e)
+      if (e < E && !(taken & (1u << e)) && (bi < 0 || v[e] > bv)) {
+        bv = v[e];
+        bi = e;
+      }
+    taken |= 1u << bi;
+    if (r == 0) m = bv;
+    zsel += expf(bv - m);
+    if (r == li) {
+      myv = bv;
+      myi = bi;
+    }
+  }
+  if (li >= k) return;
+  if (gate_mode == 3) {
+    float zt = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int e = 0; e < EB; ++e)
+      if (e < E) {
+        const float u = (v[e] - m) / ENTROPY_TAU;
+        const float w = expf(u);
+        zt += w;
+        s1 += w * u;
+      }
+    const float H = logf(zt) - s1 / zt;
+    const int kt = H > ENTROPY_THRESHOLD ? k : k - 1;
+    idx[li] = li < kt ? myi : -1;
+    gate[li] = li < kt ? expf((myv - m) / ENTROPY_TAU) / zt : 0.f;
+    return;
+  }
+  idx[li] = myi;
+  if (gate_mode == 2) {
+    gate[li] = 1.0f / (1.0f + expf(-myv));
+  } else if (gate_mode == 1) {
+    float z = 0.f;
+#pragma unroll
+    for (int e = 0; e < EB; ++e)
+      if (e < E) z += expf(v[e] - m);
+    gate[li] = expf(myv - m) / z;
+  } else {
+    gate[li] = expf(myv - m) / zsel;
+  }
+}
+
+// Up to 32 experts: a wavefront takes 4 tokens, 16 lanes each.  Per step the
+// 16 lanes of a token read 256 contiguous bytes of its row and the same 256
+// bytes of every router row; the four tokens' lanes read the same router
+// addresses, which one load serves, so the router weights are read once per
+// four tokens.  U steps go out together.  Slice s covers steps s*ns ..
+// s*ns+ns-1 of 16 x 16 bytes; the sums are reduced over the 16 lanes.
+// TOPK (one slice, k <= 16): the group then adds the bias, writes the scores
+// and runs top-k and the gate itself (no partials); else slice s's sums go to
+// part [S][T][E].
+template <typename T, int EB, bool TOPK>
+__global__ __launch_bounds__(256) void router_narrow_kernel(
     const T *__restrict__ x, const T *__restrict__ Wg, int T_, int d, int E, int ns,
-    float *__restrict__ part) {
+    float *__restrict__ part, const float *__restrict__ bias, int k, int gate_mode,
+    int32_t *__restrict__ idx, float *__restrict__ gate, float *__restrict__ logits) {
   constexpr int VEC = RouterTraits<T>::VEC;
+  constexpr int U = EB <= 16 ? 2 : 1;
   const int w = threadIdx.x / kWave, lane = lane_id();
-  const int t = blockIdx.x * 4 + w;
+  const int li = lane & 15;
+  const int t = (blockIdx.x * 4 + w) * 4 + (lane >> 4);
   const int s = blockIdx.y;
-  if (t >= T_) return;
+  const bool tv = t < T_;
   const uint4 *xg = reinterpret_cast<const uint4 *>(x);
   const uint4 *wgg = reinterpret_cast<const uint4 *>(Wg);
   const size_t rowq = (size_t)d / VEC;
-  const size_t q0 = (size_t)s * ns * kWave + lane;
+  const size_t q0 = (size_t)s * ns * 16 + li;
   float acc[EB];
 #pragma unroll
   for (int e = 0; e < EB; ++e) acc[e] = 0.f;
-  for (int i = 0; i < ns; ++i) {
-    const size_t q = q0 + (size_t)i * kWave;
-    const uint4 xv = xg[(size_t)t * rowq + q];
+  for (int i = 0; i < ns; i += U) {
+    uint4 xv[U], wv[U][EB];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool in = i + u < ns;
+      const size_t q = q0 + (size_t)(i + u) * 16;
+      xv[u] = in && tv ? xg[(size_t)t * rowq + q] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < EB; ++e)
+        wv[u][e] = in && e < E ? wgg[(size_t)e * rowq + q] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int e = 0; e < EB; ++e) acc[e] = dot16b(xv[u], wv[u][e], acc[e], T());
+  }
+#pragma unroll
+  for (int e = 0; e < EB; ++e)
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) acc[e] += __shfl_xor(acc[e], off);
+  if (!tv) return;
+  if constexpr (TOPK) {
+#pragma unroll
+    for (int e = 0; e < EB; ++e) {
+      if (bias && e < E) acc[e] += bias[e];
+      if (logits && e < E && (e & 15) == li) logits[(size_t)t * E + e] = acc[e];
+    }
+    group_topk_gate(acc, E, k, gate_mode, li, idx + (size_t)t * k, gate + (size_t)t * k);
+  } else {
+    float *out = part + ((size_t)s * T_ + t) * E;
 #pragma unroll
     for (int e = 0; e < EB; ++e)
-      if (e < E) acc[e] = dot16b(xv, wgg[(size_t)e * rowq + q], acc[e], T());
+      if (e < E && (e & 15) == li) out[e] = acc[e];
   }
-  float *out = part + ((size_t)s * T_ + t) * E;
+}
+
+// Large batches with a small router (E <= 16, E * d * size <= 64 KB, k <= 16):
+// the workgroup copies the router weights into LDS once and streams 16 tokens'
+// rows, four per wavefront with 16 lanes each (per step 256 contiguous bytes
+// of a row), RX steps in flight and the next RX issued before the current ones
+// are used; the router chunks come from LDS (the four tokens' lanes read the
+// same addresses).  The sums are reduced over the 16 lanes, then the group
+// adds the bias, writes the scores and runs top-k and the gate.  (More steps
+// in flight, or more experts per step, and the compiler's hoisting of the LDS
+// reads runs out of registers.)
+template <int EB> constexpr int router_rx() { return EB <= 8 ? 4 : 2; }
+template <typename T, int EB>
+__global__ __launch_bounds__(256, 2) void router_lds_kernel(
+    const T *__restrict__ x, const T *__restrict__ Wg, int T_, int d, int E,
+    const float *__restrict__ bias, int k, int gate_mode, int32_t *__restrict__ idx,
+    float *__restrict__ gate, float *__restrict__ logits) {
+  constexpr int VEC = RouterTraits<T>::VEC;
+  constexpr int RX = router_rx<EB>();
+  extern __shared__ uint4 wl[];  // [E][d / VEC]
+  const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
+  const int li = lane & 15;
+  const int t = (blockIdx.x * 4 + w) * 4 + (lane >> 4);
+  const bool tv = t < T_;
+  const int rowq = d / VEC;
+  const int steps = rowq / 16;  // a multiple of 2 RX
+  // a token past the end reads row 0 and writes nothing
+  const uint4 *xg = reinterpret_cast<const uint4 *>(x) + (size_t)(tv ? t : 0) * rowq + li;
+  // start the row's first steps before the router copy
+  uint4 xa[RX], xb[RX];
 #pragma unroll
-  for (int e = 0; e < EB; ++e) {
-    if (e < E) {
-      float v = acc[e];
+  for (int u = 0; u < RX; ++u) xa[u] = xg[16 * u];
+  {
+    const uint4 *wgg = reinterpret_cast<const uint4 *>(Wg);
+    const int nq = E * rowq;  // a multiple of 256 * 8
+    for (int i0 = 0; i0 < nq; i0 += 256 * 8) {
+      uint4 c[8];
 #pragma unroll
-      for (int off = kWave / 2; off > 0; off >>= 1) v += __shfl_xor(v, off);
-      if (lane == 0) out[e] = v;
+      for (int j = 0; j < 8; ++j) c[j] = wgg[i0 + j * 256 + tid];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) wl[i0 + j * 256 + tid] = c[j];
     }
   }
+  __syncthreads();
+  float acc[EB];
+#pragma unroll
+  for (int e = 0; e < EB; ++e) acc[e] = 0.f;
+  // sums past E read router row E - 1 (no branch between the LDS reads) and
+  // are never used
+  auto use = [&](const uint4 (&xv)[RX], int j0) {
+#pragma unroll
+    for (int u = 0; u < RX; ++u) {
+      const int q = li + 16 * (j0 + u);
+#pragma unroll
+      for (int e = 0; e < EB; ++e) acc[e] = dot16b(xv[u], wl[min(e, E - 1) * rowq + q], acc[e], T());
+      // one step at a time: hoisting every step's LDS reads would take more
+      // registers than the loads in flight leave
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    }
+  };
+  // steps is a multiple of 2 RX: xb holds steps j0 + RX .., xa the next 2 RX
+  for (int j0 = 0; j0 < steps; j0 += 2 * RX) {
+#pragma unroll
+    for (int u = 0; u < RX; ++u) xb[u] = xg[16 * (j0 + RX + u)];
+    use(xa, j0);
+    if (j0 + 2 * RX < steps) {
+#pragma unroll
+      for (int u = 0; u < RX; ++u) xa[u] = xg[16 * (j0 + 2 * RX + u)];
+    }
+    use(xb, j0 + RX);
+  }
+#pragma unroll
+  for (int e = 0; e < EB; ++e)
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) acc[e] += __shfl_xor(acc[e], off);
+  if (!tv) return;
+#pragma unroll
+  for (int e = 0; e < EB; ++e) {
+    if (bias && e < E) acc[e] += bias[e];
+    if (logits && e < E && (e & 15) == li) logits[(size_t)t * E + e] = acc[e];
+  }
+  group_topk_gate(acc, E, k, gate_mode, li, idx + (size_t)t * k, gate + (size_t)t * k);
 }
 
 // Sum of a score's S slice partials (stride apart), in slice order; the loads
@@ -267,8 +439,8 @@ __global__ __launch_bounds__(256) void topk_permute_tiny_kernel(
 }
 
 // Feature slices for the score kernels (enough work items to fill the GPU).
-// Narrow kernel: a slice is ns steps of 64 lanes x 16 bytes.  Tiled kernel: a
-// slice is a whole number of 128-byte chunks.
+// Narrow kernel: a slice is ns steps of 16 lanes x 16 bytes per token.  Tiled
+// kernel: a slice is a whole number of 128-byte chunks.
 struct RouterSplit {
   bool narrow;
   int S, ns;
@@ -276,11 +448,11 @@ struct RouterSplit {
 RouterSplit router_split(int T, int d, int E, int esize) {
   RouterSplit r{};
   const int vec = 16 / esize;
-  r.narrow = E <= 32 && d % (kWave * vec) == 0;
+  r.narrow = E <= 32 && d % (16 * vec) == 0;
   if (r.narrow) {
-    const int steps = d / (kWave * vec);   // 16-byte steps per lane over the whole row
-    const long long waves_per_slice = T;   // one wave per token and slice
-    int S = steps;                         // finest split: one step per lane
+    const int steps = d / (16 * vec);               // 16-byte steps per lane over the whole row
+    const long long waves_per_slice = (T + 3) / 4;  // four tokens per wave
+    int S = steps;                                  // finest split: one step per lane
     while (S > 1 && (steps % (S / 2) == 0) && waves_per_slice * (S / 2) >= 2048) S /= 2;
     r.S = S;
     r.ns = steps / S;
@@ -296,20 +468,29 @@ RouterSplit router_split(int T, int d, int E, int esize) {
   return r;
 }
 
+template <typename T, bool TOPK>
+void launch_narrow(const RouterSplit &r, const void *x, const void *Wg, int T_, int d, int E,
+                   float *part, const float *bias, int k, int gate_mode, int32_t *idx,
+                   float *gate, float *logits, hipStream_t s) {
+  dim3 grid((T_ + 15) / 16, r.S);
+#define RN_LAUNCH(EB)                                                                          \
+  hipLaunchKernelGGL((router_narrow_kernel<T, EB, TOPK>), grid, dim3(256), 0, s, (const T *)x, \
+                     (const T *)Wg, T_, d, E, r.ns, part, bias, k, gate_mode, idx, gate, logits)
+  if (E <= 8)
+    RN_LAUNCH(8);
+  else if (E <= 16)
+    RN_LAUNCH(16);
+  else
+    RN_LAUNCH(32);
+#undef RN_LAUNCH
+}
+
 template <typename T>
 void launch_scores(const RouterSplit &r, const void *x, const void *Wg, int T_, int d, int E,
                    float *part, hipStream_t s) {
   if (r.narrow) {
-    dim3 grid((T_ + 3) / 4, r.S);
-    if (E <= 8)
-      hipLaunchKernelGGL((router_scores_narrow_kernel<T, 8>), grid, dim3(256), 0, s,
-                         (const T *)x, (const T *)Wg, T_, d, E, r.ns, part);
-    else if (E <= 16)
-      hipLaunchKernelGGL((router_scores_narrow_kernel<T, 16>), grid, dim3(256), 0, s,
-                         (const T *)x, (const T *)Wg, T_, d, E, r.ns, part);
-    else
-      hipLaunchKernelGGL((router_scores_narrow_kernel<T, 32>), grid, dim3(256), 0, s,
-                         (const T *)x, (const T *)Wg, T_, d, E, r.ns, part);
+    launch_narrow<T, false>(r, x, Wg, T_, d, E, part, nullptr, 0, 0, nullptr, nullptr, nullptr,
+                            s);
   } else {
     dim3 grid((T_ + RS_TOK - 1) / RS_TOK, (E + RS_EXP - 1) / RS_EXP, r.S);
     hipLaunchKernelGGL(router_scores_kernel<T>, grid, dim3(RS_THREADS), 0, s, (const T *)x,
@@ -355,6 +536,32 @@ hipError_t launch_router(int dtype, const void *x, const void *Wg, const float *
                          float *logits, float *part, hipStream_t s) {
   const int es = dtype == 1 ? 2 : 4;
   const RouterSplit r = router_split(T, d, E, es);
+  const size_t wl_bytes = (size_t)E * d * es;
+  const int rx = E <= 8 ? router_rx<8>() : router_rx<16>();
+  if (E <= 16 && k <= 16 && wl_bytes <= 65536 && T >= 4096 &&
+      d % (16 * (16 / es) * 2 * rx) == 0 && (wl_bytes / 16) % (256 * 8) == 0) {
+    // many tokens, a router that fits LDS: one kernel, router weights in LDS
+#define RL_LAUNCH(TT, EB)                                                                     \
+  hipLaunchKernelGGL((router_lds_kernel<TT, EB>), dim3((T + 15) / 16), dim3(256), wl_bytes, s, \
+                     (const TT *)x, (const TT *)Wg, T, d, E, bias, k, gate_mode, idx, gate, logits)
+    if (dtype == 1) {
+      if (E <= 8) RL_LAUNCH(bf16_t, 8); else RL_LAUNCH(bf16_t, 16);
+    } else {
+      if (E <= 8) RL_LAUNCH(float, 8); else RL_LAUNCH(float, 16);
+    }
+#undef RL_LAUNCH
+    return hipGetLastError();
+  }
+  if (r.narrow && r.S == 1 && k <= 16) {
+    // whole rows per wave: top-k and gate in the score kernel
+    if (dtype == 1)
+      launch_narrow<bf16_t, true>(r, x, Wg, T, d, E, nullptr, bias, k, gate_mode, idx, gate,
+                                  logits, s);
+    else
+      launch_narrow<float, true>(r, x, Wg, T, d, E, nullptr, bias, k, gate_mode, idx, gate,
+                                 logits, s);
+    return hipGetLastError();
+  }
   if (dtype == 1)
     launch_scores<bf16_t>(r, x, Wg, T, d, E, part, s);
   else

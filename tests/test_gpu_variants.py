@@ -149,6 +149,61 @@ def test_route_entropy():
     assert 0 < n3 < lg.shape[0]
 
 
+def check_route(lg, gi, gg, k, gm):
+    """GPU top-k and gates against the oracle on the GPU's scores; with the
+    entropy rule a token within 1e-4 of the threshold may take either k."""
+    if gm != O.GATE_ENTROPY:
+        idx_ref = O.topk(lg, k)
+        np.testing.assert_array_equal(gi, idx_ref)
+        return float(np.max(np.abs(gg - O.gate_mode(lg, idx_ref, gm))))
+    H = O.entropy(lg)
+    ri, rg = O.route_entropy(lg, k)
+    hi_i, hi_g = O.route_entropy(lg, k, threshold=-1.0)
+    lo_i, lo_g = O.route_entropy(lg, k, threshold=1e30)
+    near = np.abs(H - O.ENTROPY_THRESHOLD) < 1e-4
+    ri, rg = ri.copy(), rg.copy()
+    full = gi[:, k - 1] >= 0
+    ri[near & full], rg[near & full] = hi_i[near & full], hi_g[near & full]
+    ri[near & ~full], rg[near & ~full] = lo_i[near & ~full], lo_g[near & ~full]
+    np.testing.assert_array_equal(gi, ri)
+    return float(np.max(np.abs(gg - rg)))
+
+
+# many tokens with a small router: the score kernel also runs top-k and the
+# gate (router weights in LDS up to E * d * size = 64 KB and E <= 16, else the
+# register-tiled score kernel with one feature slice)
+ROUTE_FUSED = [
+    # (label, T, d, E, k, dtype, gate_mode, skew)
+    ("lds_E8_k2_skew_bf16", 4100, 4096, 8, 2, "bf16", 0, 1.5),
+    ("lds_E8_k8_softmax_all_bf16", 4096, 2048, 8, 8, "bf16", 1, 0.0),
+    ("lds_E16_k4_sigmoid_f32", 4096, 1024, 16, 4, "f32", 2, 0.0),
+    ("lds_E16_k3_entropy_bf16", 4111, 2048, 16, 3, "bf16", 3, 0.0),
+    ("narrow_E32_k16_bf16", 8192, 512, 32, 16, "bf16", 0, 0.0),
+    ("narrow_E24_k3_entropy_f32", 8200, 256, 24, 3, "f32", 3, 0.0),
+    ("narrow_E12_k2_sigmoid_skew_bf16", 9000, 384, 12, 2, "bf16", 2, 2.0),
+]
+
+
+@pytest.mark.parametrize("c", ROUTE_FUSED, ids=[c[0] for c in ROUTE_FUSED])
+def test_route_fused_topk(c):
+    label, T, d, E, k, dtype, gm, skew = c
+    cfg = LayerConfig("route", T, d, E, 64, k, dtype, skew=skew, seed=21)
+    h = make_inputs(cfg, with_weights=False)
+    x = moe.tensor_from_numpy(h["x"])
+    Wg = moe.tensor_from_numpy(h["Wg"])
+    bias = torch.from_numpy(h["bias"]).cuda() if h["bias"] is not None else None
+    idx, gate, logits = moe.route(x, Wg, k, bias, gate_mode=gm)
+    torch.cuda.synchronize()
+    lg = logits.double().cpu().numpy()
+    # the scores themselves: fp32 sums of the bf16-rounded inputs
+    ref_lg = O.logits(h["x"], h["Wg"], h["bias"])
+    lerr = float(np.max(np.abs(lg - ref_lg)) / np.max(np.abs(ref_lg)))
+    err = check_route(lg, idx.cpu().numpy(), gate.cpu().numpy(), k, gm)
+    say(f"moe_route_ex {label}: max |gate - oracle| {err:.2e}, scores rel {lerr:.1e}")
+    assert err <= 1e-6
+    assert lerr <= 1e-5
+
+
 @pytest.mark.parametrize("gm", [0, 1, 2])
 def test_route_gate_modes(gm):
     cfg, h, dev = inputs(777, 512, 64, 64, 4, "bf16", seed=11)
