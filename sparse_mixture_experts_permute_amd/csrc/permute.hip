@@ -9,8 +9,9 @@
 // which atomics land.
 //
 //   hist    : block b counts the experts of pairs [256b, 256b+256) -> blk[b][e]
-//   scan    : one block turns blk[][] into per-block rank bases, counts,
-//             offsets and the m-tile prefix used by the grouped GEMM tile maps
+//   scan    : one block turns blk[][] into per-block rank bases (1024 threads
+//             over (block range, expert)), counts, offsets and the m-tile
+//             prefix used by the grouped GEMM tile maps
 //   scatter : block b re-reads its pairs; a pair's rank among its expert's
 //             pairs is base[b][e] + (pairs of e in earlier waves of b) + (rank
 //             in wave), and its slot is offsets[e] + rank
@@ -44,52 +45,96 @@ __global__ __launch_bounds__(PM_CHUNK) void permute_hist_kernel(const int32_t *_
   if (tid < E) blk[(size_t)blockIdx.x * E + tid] = h[tid];
 }
 
-// One block of 256 threads; thread e owns expert e.
-__global__ __launch_bounds__(256) void permute_scan_kernel(
+// One block of 1024 threads.  The per-block counts blk[b][e] are summed and
+// turned into rank bases by thread (q, e): expert e (of EP, E rounded up to a
+// power of two) and part q of the blocks (Q = 1024 / EP contiguous parts),
+// with eight loads in flight; the parts' sums give each part its starting rank
+// and each expert its total.  Then threads e < 256 scan over the experts.
+constexpr int SC_THREADS = 1024;
+__global__ __launch_bounds__(SC_THREADS) void permute_scan_kernel(
     int32_t *__restrict__ blk, int nb, int E, int P, int T, int capacity, int bm0, int bm1,
     int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int32_t *__restrict__ mtiles0,
     int32_t *__restrict__ mtiles1, int32_t *__restrict__ shared_seg,
     int32_t *__restrict__ active, int32_t *__restrict__ zero, int nzero) {
-  __shared__ int s0[256], s1[256], s2[256], s3[256];
-  const int e = threadIdx.x;
-  for (int i = e; i < nzero; i += 256) zero[i] = 0;
-  int raw = 0;
-  if (e < E)
-    for (int b = 0; b < nb; ++b) raw += blk[(size_t)b * E + e];
-  const int total = min(raw, capacity);  // pairs the expert keeps
-  s0[e] = e < E ? total : 0;
-  s1[e] = e < E ? (total + bm0 - 1) / bm0 : 0;
-  s2[e] = e < E ? (total + bm1 - 1) / bm1 : 0;
-  s3[e] = (e < E && total > 0) ? 1 : 0;
+  __shared__ int s0[256], s1[256], s2[256], s3[256], tot[256];
+  __shared__ int psum[SC_THREADS];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < nzero; i += SC_THREADS) zero[i] = 0;
+  int EP = 1;
+  while (EP < E) EP <<= 1;
+  const int Q = SC_THREADS / EP, pe = tid % EP, q = tid / EP;
+  const int R = (nb + Q - 1) / Q;
+  const int b0 = q * R, b1 = min(nb, b0 + R);
+  int sum = 0;
+  if (pe < E) {
+    for (int b = b0; b < b1; b += 8) {
+      int v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = b + i < b1 ? blk[(size_t)(b + i) * E + pe] : 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sum += v[i];
+    }
+  }
+  psum[tid] = sum;
+  __syncthreads();
+  if (pe < E) {
+    // rank of the part's first pair among the expert's pairs, then the
+    // parts' blocks get their running bases
+    int run = 0;
+    for (int q2 = 0; q2 < q; ++q2) run += psum[q2 * EP + pe];
+    if (q == 0) {
+      int t = 0;
+      for (int q2 = 0; q2 < Q; ++q2) t += psum[q2 * EP + pe];
+      tot[pe] = t;
+    }
+    for (int b = b0; b < b1; b += 8) {
+      int v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = b + i < b1 ? blk[(size_t)(b + i) * E + pe] : 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (b + i < b1) {
+          blk[(size_t)(b + i) * E + pe] = run;
+          run += v[i];
+        }
+    }
+  }
+  __syncthreads();
+  const int e = tid;
+  const int total = e < E ? min(tot[e], capacity) : 0;  // pairs the expert keeps
+  if (e < 256) {
+    s0[e] = total;
+    s1[e] = e < E ? (total + bm0 - 1) / bm0 : 0;
+    s2[e] = e < E ? (total + bm1 - 1) / bm1 : 0;
+    s3[e] = (e < E && total > 0) ? 1 : 0;
+  }
   __syncthreads();
   // inclusive Hillis-Steele scans over the experts (256 entries)
   for (int off = 1; off < 256; off <<= 1) {
-    int a0 = e >= off ? s0[e - off] : 0;
-    int a1 = e >= off ? s1[e - off] : 0;
-    int a2 = e >= off ? s2[e - off] : 0;
-    int a3 = e >= off ? s3[e - off] : 0;
+    int a0 = 0, a1 = 0, a2 = 0, a3 = 0;
+    if (e < 256 && e >= off) {
+      a0 = s0[e - off];
+      a1 = s1[e - off];
+      a2 = s2[e - off];
+      a3 = s3[e - off];
+    }
     __syncthreads();
-    s0[e] += a0;
-    s1[e] += a1;
-    s2[e] += a2;
-    s3[e] += a3;
+    if (e < 256) {
+      s0[e] += a0;
+      s1[e] += a1;
+      s2[e] += a2;
+      s3[e] += a3;
+    }
     __syncthreads();
   }
   // compact list of the experts that received pairs; active[E] = their number
   if (e < E && total > 0) active[s3[e] - 1] = e;
   if (e == 0) active[E] = s3[255];
   if (e < E) {
-    const int excl = s0[e] - total;
     counts[e] = total;
-    offsets[e] = excl;
+    offsets[e] = s0[e] - total;
     mtiles0[e] = s1[e] - (total + bm0 - 1) / bm0;
     mtiles1[e] = s2[e] - (total + bm1 - 1) / bm1;
-    int run = 0;  // rank of the block's first pair among the expert's pairs
-    for (int b = 0; b < nb; ++b) {
-      int c = blk[(size_t)b * E + e];
-      blk[(size_t)b * E + e] = run;
-      run += c;
-    }
   }
   if (e == 0) {
     offsets[E] = s0[255];  // kept pairs (== P when nothing is dropped)
@@ -299,8 +344,9 @@ hipError_t launch_permute(const int32_t *idx, int T, int E, int k, int capacity,
   }
   const int nb = permute_nblocks(P);
   hipLaunchKernelGGL(permute_hist_kernel, dim3(nb), dim3(PM_CHUNK), 0, s, idx, P, E, blk);
-  hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(256), 0, s, blk, nb, E, P, T, cap, bm0,
-                     bm1, counts, offsets, mtiles0, mtiles1, shared_seg, active, zero, nzero);
+  hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(SC_THREADS), 0, s, blk, nb, E, P, T, cap,
+                     bm0, bm1, counts, offsets, mtiles0, mtiles1, shared_seg, active, zero,
+                     nzero);
   hipLaunchKernelGGL(permute_scatter_kernel, dim3(nb), dim3(PM_CHUNK), 0, s, idx, P, E, cap, blk,
                      offsets, perm, inv);
   return hipGetLastError();
