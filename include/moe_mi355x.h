@@ -126,10 +126,13 @@ int moe_forward(const void *x, const void *Wg, const float *bias, const void *W1
  * the permutation, [3] after the row gather, [4] after the SwiGLU GEMM, [5]
  * after the down GEMM, [6] after the shared expert (if any), [7] after the
  * combine.  A decode step (T <= 4, T * k <= 64, E <= 64) runs top-k and the
- * grouping in one launch: [1] and [2] then both follow it; when its down
+ * grouping in one launch: [1] and [2] then both follow it.  A single token
+ * whose router has at most 65536 elements is routed inside the SwiGLU
+ * projection: [0] to [3] then all precede that kernel.  When the down
  * projection streams the weights and there is no shared expert, the combine
- * rides in that kernel: [5], [6] and [7] then all follow it.  Same results and errors as
- * moe_forward; MOE_EINVAL if `events` or any of its handles is NULL. */
+ * rides in that kernel: [5], [6] and [7] then all follow it.  Same results
+ * and errors as moe_forward; MOE_EINVAL if `events` or any of its handles is
+ * NULL. */
 #define MOE_NSTAGE_EVENTS 8
 int moe_forward_timed(const void *x, const void *Wg, const float *bias, const void *W1,
                       const void *W3, const void *W2, const void *Ws1, const void *Ws3,
