@@ -27,6 +27,9 @@
 //
 // Tile map.  mtile_off[e] is the prefix of ceil(count_e / BM) over experts;
 // map_tile turns a 1-D workgroup id into (expert, m-tile, n-tile).  The
+// direct-to-LDS kernel takes expert e's rows as seg_off[e] .. seg_end[e] - 1,
+// so one segment can be served by two launches (256-row tiles for its bulk,
+// 64-row tiles for a short remainder).  The
 // persistent kernel also splits the tiles of its last round along K
 // (plan_split).
 #include "common.h"
@@ -392,8 +395,9 @@ template <int BM, int BNB, bool SWIGLU, bool SPLIT>
 __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
     const bf16_t *__restrict__ A, const bf16_t *__restrict__ B1, const bf16_t *__restrict__ B3,
     void *__restrict__ C, const int32_t *__restrict__ seg_off,
-    const int32_t *__restrict__ mtile_off, int G, int N, int K, size_t plane, int act,
-    int32_t *__restrict__ fix_cnt, f32x4_v *__restrict__ fix_part, int part_cap) {
+    const int32_t *__restrict__ seg_end, const int32_t *__restrict__ mtile_off, int G, int N,
+    int K, size_t plane, int act, int32_t *__restrict__ fix_cnt, f32x4_v *__restrict__ fix_part,
+    int part_cap) {
   constexpr int WM = 2, WN = 2;
   constexpr int TM = BM / WM / 32, TN = BNB / WN / 32;
   constexpr int ROWS = BM + BNB;          // tile rows per stage (A then B)
@@ -467,7 +471,7 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
     const int e = t.e;
     const uint32_t kb = kb_pl + (ta.part < 0 ? 0u : (uint32_t)(ta.part * ta.nk) * 128u);
     ta.row0 = seg_off[e] + (t.g - mtile_off[e]) * BM;
-    ta.rows = min(BM, seg_off[e + 1] - ta.row0);
+    ta.rows = min(BM, seg_end[e] - ta.row0);
     ta.n0 = t.n * COLS;
     ta.ra = make_rsrc(reinterpret_cast<const char *>(A) + (size_t)ta.row0 * rowb + kb,
                       (uint32_t)ta.rows * rowb - kb);
@@ -738,14 +742,16 @@ int resident_wgs(int bm) {
 
 template <int BM, int BNB, bool SWIGLU, bool SPLIT = false>
 hipError_t launch_dl(const void *A, const void *B1, const void *B3, void *C,
-                     const int32_t *seg_off, const int32_t *mtile_off, int G, int N, int K,
-                     int ksplit, size_t plane, int act, const FixScratch &fx, hipStream_t s) {
+                     const int32_t *seg_off, const int32_t *seg_end, const int32_t *mtile_off,
+                     int G, int N, int K, int ksplit, size_t plane, int act, const FixScratch &fx,
+                     hipStream_t s) {
   // persistent grid: what stays resident, a multiple of the XCD count
   const int gx = (resident_wgs(BM) / ksplit + NUM_XCD - 1) / NUM_XCD * NUM_XCD;
   const size_t cap = fx.part ? fx.part_bytes / ((size_t)BM * BNB * 4) : 0;
   hipLaunchKernelGGL((grouped_gemm_dl_kernel<BM, BNB, SWIGLU, SPLIT>), dim3(gx, ksplit),
                      dim3(GM_THREADS), 0, s, (const bf16_t *)A, (const bf16_t *)B1,
-                     (const bf16_t *)B3, C, seg_off, mtile_off, G, N, K, plane, act, fx.cnt,
+                     (const bf16_t *)B3, C, seg_off, seg_end ? seg_end : seg_off + 1, mtile_off, G,
+                     N, K, plane, act, fx.cnt,
                      (f32x4_v *)fx.part,
                      (int)(cap < (size_t)FIX_SLOTS * 16 ? cap : (size_t)FIX_SLOTS * 16));
   return hipGetLastError();
@@ -787,15 +793,16 @@ GemmPlan gemm_plan(int dtype, int d, int d_ff, int d_ff_shared, long long rows_p
 hipError_t launch_gemm_swiglu(int dtype, bool dl, int bm, int act, const void *A,
                               const void *W1, const void *W3, void *H, const int32_t *seg_off,
                               const int32_t *mtile_off, int G, int N, int K, int max_mtiles,
-                              hipStream_t s) {
+                              hipStream_t s, const int32_t *seg_end) {
   if (max_mtiles <= 0) return hipSuccess;
   const FixScratch none{nullptr, nullptr, 0};
   if (dl && bm == 64)
-    return launch_dl<64, 256, true>(A, W1, W3, H, seg_off, mtile_off, G, N, K, 1, 0, act, none,
-                                    s);
+    return launch_dl<64, 256, true>(A, W1, W3, H, seg_off, seg_end, mtile_off, G, N, K, 1, 0,
+                                    act, none, s);
   if (dl)
-    return launch_dl<256, 256, true>(A, W1, W3, H, seg_off, mtile_off, G, N, K, 1, 0, act, none,
-                                     s);
+    return launch_dl<256, 256, true>(A, W1, W3, H, seg_off, seg_end, mtile_off, G, N, K, 1, 0,
+                                     act, none, s);
+  if (seg_end) return hipErrorInvalidValue;  // the tiled kernels take whole segments
   if (dtype == 1)
     return launch_one<bf16_t, 128, 128, 2, 2, true>(A, W1, W3, H, seg_off, mtile_off, G, N, K,
                                                     max_mtiles, act, s);
@@ -806,19 +813,20 @@ hipError_t launch_gemm_swiglu(int dtype, bool dl, int bm, int act, const void *A
 hipError_t launch_gemm_down(int dtype, bool dl, int bm, const void *A, const void *W2, float *Y,
                             const int32_t *seg_off, const int32_t *mtile_off, int G, int N, int K,
                             int max_mtiles, int ksplit, size_t plane, const FixScratch &fx,
-                            hipStream_t s) {
+                            hipStream_t s, const int32_t *seg_end) {
   if (max_mtiles <= 0) return hipSuccess;
   if (dl && bm == 64)
-    return launch_dl<64, 256, false>(A, W2, nullptr, Y, seg_off, mtile_off, G, N, K, ksplit,
-                                     plane, 0, fx, s);
+    return launch_dl<64, 256, false>(A, W2, nullptr, Y, seg_off, seg_end, mtile_off, G, N, K,
+                                     ksplit, plane, 0, fx, s);
   // the last-round split pays for long K only (the kernel's estimate never
   // splits below SPLIT_MIN_K)
   if (dl && ksplit == 1 && K >= SPLIT_MIN_K && fx.part)
-    return launch_dl<256, 256, false, true>(A, W2, nullptr, Y, seg_off, mtile_off, G, N, K, 1,
-                                            0, 0, fx, s);
+    return launch_dl<256, 256, false, true>(A, W2, nullptr, Y, seg_off, seg_end, mtile_off, G,
+                                            N, K, 1, 0, 0, fx, s);
   if (dl)
-    return launch_dl<256, 256, false>(A, W2, nullptr, Y, seg_off, mtile_off, G, N, K, ksplit,
-                                      plane, 0, fx, s);
+    return launch_dl<256, 256, false>(A, W2, nullptr, Y, seg_off, seg_end, mtile_off, G, N, K,
+                                      ksplit, plane, 0, fx, s);
+  if (seg_end) return hipErrorInvalidValue;  // the tiled kernels take whole segments
   if (dtype == 1)
     return launch_one<bf16_t, 128, 128, 2, 2, false>(A, W2, nullptr, Y, seg_off, mtile_off, G,
                                                      N, K, max_mtiles, 0, s);

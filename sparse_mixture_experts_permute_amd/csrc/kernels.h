@@ -74,11 +74,16 @@ int permute_nblocks(int P);
 // all.  Dropped pairs (and ids outside [0, E)) get inv = -1.
 // zero (may be NULL): nzero int32 set to 0 on the way (the GEMMs' arrival
 // counters, see FixScratch).
+// mid (may be NULL): split tiling for large batches.  mtiles0 is then the
+// prefix of each expert's 256-row tiles and mtiles1 of its 64-row remainder
+// tiles (at most SPLIT_REM_TILES; bm0 and bm1 are not used), and mid[e] the
+// row where the remainder starts (offsets[e + 1] when there is none).
+constexpr int SPLIT_REM_TILES = 2;
 hipError_t launch_permute(const int32_t *idx, int T, int E, int k, int capacity, int bm0,
                           int bm1, int32_t *blk, int32_t *counts, int32_t *offsets,
                           int32_t *perm, int32_t *inv, int32_t *mtiles0, int32_t *mtiles1,
                           int32_t *shared_seg, int32_t *active, int32_t *zero, int nzero,
-                          hipStream_t s);
+                          hipStream_t s, int32_t *mid = nullptr);
 // xp[s] = x[perm[s] / k] for s < *placed (<= P, read on the device)
 hipError_t launch_gather(const void *x, const int32_t *perm, const int32_t *placed, int P, int k,
                          int d, int esize, void *xp, hipStream_t s);
@@ -105,17 +110,19 @@ struct FixScratch {
 // for a GEMM of at most `tiles` output tiles.
 size_t fix_part_bytes(long long tiles);
 // act: 0 SiLU(W1 a) * (W3 a), 1 sigmoid(W1 a) * (W3 a)
+// seg_end (direct-to-LDS kernel only; NULL: seg_off + 1): expert e's rows
+// are seg_off[e] .. seg_end[e] - 1, with mtile_off the prefix of its tiles.
 hipError_t launch_gemm_swiglu(int dtype, bool dl, int bm, int act, const void *A,
                               const void *W1, const void *W3, void *H, const int32_t *seg_off,
                               const int32_t *mtile_off, int G, int N, int K, int max_mtiles,
-                              hipStream_t s);
+                              hipStream_t s, const int32_t *seg_end = nullptr);
 // ksplit > 1 (direct-to-LDS kernel only): every tile's K is split in ksplit
 // equal ranges whose fp32 partials go to planes `plane` elements apart (for
 // batches with few tiles; the last-round split then stays off).
 hipError_t launch_gemm_down(int dtype, bool dl, int bm, const void *A, const void *W2, float *Y,
                             const int32_t *seg_off, const int32_t *mtile_off, int G, int N, int K,
                             int max_mtiles, int ksplit, size_t plane, const FixScratch &fx,
-                            hipStream_t s);
+                            hipStream_t s, const int32_t *seg_end = nullptr);
 
 // Weight-streaming grouped GEMMs for few rows per expert (bf16 only).
 bool skinny_ok(int N, int K);

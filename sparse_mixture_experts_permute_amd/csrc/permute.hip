@@ -29,6 +29,24 @@ namespace {
 
 constexpr int PM_CHUNK = 256;  // pairs per block == threads per block
 
+// Split tiling of an expert's c kept rows (large batches): 256-row tiles for
+// the bulk and, when c runs at most 128 rows past a multiple of 256, 64-row
+// tiles for that remainder, served by a second GEMM launch (a 256-row tile
+// for a few rows would cost a whole tile).  main / rem: tiles of each kind;
+// main_rows: rows the 256-row tiles cover.
+__device__ __forceinline__ void tile_split(int c, int &main, int &rem, int &main_rows) {
+  const int r = c & 255;
+  if (c < 256 || r == 0 || r > 128) {
+    main = (c + 255) >> 8;
+    rem = 0;
+    main_rows = c;
+  } else {
+    main = c >> 8;
+    rem = (r + 63) >> 6;
+    main_rows = c - r;
+  }
+}
+
 __global__ __launch_bounds__(PM_CHUNK) void permute_hist_kernel(const int32_t *__restrict__ idx,
                                                                 int P, int E,
                                                                 int32_t *__restrict__ blk) {
@@ -55,7 +73,8 @@ __global__ __launch_bounds__(SC_THREADS) void permute_scan_kernel(
     int32_t *__restrict__ blk, int nb, int E, int P, int T, int capacity, int bm0, int bm1,
     int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int32_t *__restrict__ mtiles0,
     int32_t *__restrict__ mtiles1, int32_t *__restrict__ shared_seg,
-    int32_t *__restrict__ active, int32_t *__restrict__ zero, int nzero) {
+    int32_t *__restrict__ active, int32_t *__restrict__ zero, int nzero,
+    int32_t *__restrict__ mid) {
   __shared__ int s0[256], s1[256], s2[256], s3[256], tot[256];
   __shared__ int psum[SC_THREADS];
   const int tid = threadIdx.x;
@@ -102,10 +121,14 @@ __global__ __launch_bounds__(SC_THREADS) void permute_scan_kernel(
   __syncthreads();
   const int e = tid;
   const int total = e < E ? min(tot[e], capacity) : 0;  // pairs the expert keeps
+  // m-tiles: of bm0 / bm1 rows, or (mid != NULL) the split tiling's 256-row
+  // and 64-row tiles
+  int t0 = (total + bm0 - 1) / bm0, t1 = (total + bm1 - 1) / bm1, mrows = total;
+  if (mid) tile_split(total, t0, t1, mrows);
   if (e < 256) {
     s0[e] = total;
-    s1[e] = e < E ? (total + bm0 - 1) / bm0 : 0;
-    s2[e] = e < E ? (total + bm1 - 1) / bm1 : 0;
+    s1[e] = e < E ? t0 : 0;
+    s2[e] = e < E ? t1 : 0;
     s3[e] = (e < E && total > 0) ? 1 : 0;
   }
   __syncthreads();
@@ -133,8 +156,9 @@ __global__ __launch_bounds__(SC_THREADS) void permute_scan_kernel(
   if (e < E) {
     counts[e] = total;
     offsets[e] = s0[e] - total;
-    mtiles0[e] = s1[e] - (total + bm0 - 1) / bm0;
-    mtiles1[e] = s2[e] - (total + bm1 - 1) / bm1;
+    mtiles0[e] = s1[e] - t0;
+    mtiles1[e] = s2[e] - t1;
+    if (mid) mid[e] = s0[e] - total + mrows;
   }
   if (e == 0) {
     offsets[E] = s0[255];  // kept pairs (== P when nothing is dropped)
@@ -202,7 +226,7 @@ __global__ __launch_bounds__(PS_THREADS) void permute_small_kernel(
     int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int32_t *__restrict__ perm,
     int32_t *__restrict__ inv, int32_t *__restrict__ mtiles0, int32_t *__restrict__ mtiles1,
     int32_t *__restrict__ shared_seg, int32_t *__restrict__ active, int32_t *__restrict__ zero,
-    int nzero) {
+    int nzero, int32_t *__restrict__ mid) {
   // hist: pairs per expert; koff: kept-pair offsets (scanned in place);
   // rk: rank of the next pair of each expert
   __shared__ int hist[256], koff[256], rk[256], s1[256], s2[256], s3[256];
@@ -218,10 +242,12 @@ __global__ __launch_bounds__(PS_THREADS) void permute_small_kernel(
   __syncthreads();
   if (tid < 256) {
     const int c = tid < E ? min(hist[tid], capacity) : 0;  // kept pairs
+    int t0 = (c + bm0 - 1) / bm0, t1 = (c + bm1 - 1) / bm1, mrows = c;
+    if (mid) tile_split(c, t0, t1, mrows);
     koff[tid] = c;
     rk[tid] = 0;
-    s1[tid] = tid < E ? (c + bm0 - 1) / bm0 : 0;
-    s2[tid] = tid < E ? (c + bm1 - 1) / bm1 : 0;
+    s1[tid] = tid < E ? t0 : 0;
+    s2[tid] = tid < E ? t1 : 0;
     s3[tid] = (tid < E && c > 0) ? 1 : 0;
   }
   __syncthreads();
@@ -244,10 +270,13 @@ __global__ __launch_bounds__(PS_THREADS) void permute_small_kernel(
   }
   if (tid < E) {
     const int c = min(hist[tid], capacity);
+    int t0 = (c + bm0 - 1) / bm0, t1 = (c + bm1 - 1) / bm1, mrows = c;
+    if (mid) tile_split(c, t0, t1, mrows);
     counts[tid] = c;
     offsets[tid] = koff[tid] - c;
-    mtiles0[tid] = s1[tid] - (c + bm0 - 1) / bm0;
-    mtiles1[tid] = s2[tid] - (c + bm1 - 1) / bm1;
+    mtiles0[tid] = s1[tid] - t0;
+    mtiles1[tid] = s2[tid] - t1;
+    if (mid) mid[tid] = koff[tid] - c + mrows;
     if (c > 0) active[s3[tid] - 1] = tid;
   }
   if (tid == 0) {
@@ -332,21 +361,21 @@ hipError_t launch_permute(const int32_t *idx, int T, int E, int k, int capacity,
                           int bm1, int32_t *blk, int32_t *counts, int32_t *offsets,
                           int32_t *perm, int32_t *inv, int32_t *mtiles0, int32_t *mtiles1,
                           int32_t *shared_seg, int32_t *active, int32_t *zero, int nzero,
-                          hipStream_t s) {
+                          hipStream_t s, int32_t *mid) {
   const int P = T * k;
   if (!zero) nzero = 0;
   const int cap = capacity < 0 || capacity > P ? P : capacity;
   if (P <= 8 * PS_THREADS) {
     hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(PS_THREADS), 0, s, idx, P, E, T, cap,
                        bm0, bm1, counts, offsets, perm, inv, mtiles0, mtiles1, shared_seg,
-                       active, zero, nzero);
+                       active, zero, nzero, mid);
     return hipGetLastError();
   }
   const int nb = permute_nblocks(P);
   hipLaunchKernelGGL(permute_hist_kernel, dim3(nb), dim3(PM_CHUNK), 0, s, idx, P, E, blk);
   hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(SC_THREADS), 0, s, blk, nb, E, P, T, cap,
                      bm0, bm1, counts, offsets, mtiles0, mtiles1, shared_seg, active, zero,
-                     nzero);
+                     nzero, mid);
   hipLaunchKernelGGL(permute_scatter_kernel, dim3(nb), dim3(PM_CHUNK), 0, s, idx, P, E, cap, blk,
                      offsets, perm, inv);
   return hipGetLastError();

@@ -246,6 +246,14 @@ EDGE = [
     ("gemv_T1", 1, 2048, 8, 2048, 2, "bf16", 0, None),
     ("gemv_T2_K6144_shared", 2, 2048, 4, 6144, 2, "bf16", 2048, None),
     ("gemv_T4_hot_expert", 4, 2048, 8, 4096, 2, "bf16", 0, ("hot", 1, 100.0)),
+    # 256-row tiles with under 512 rows per expert: 64-row tiles for short remainders
+    # (one or two remainder tiles, remainders over 128 rows kept whole, experts below
+    # 256 rows and at exactly 256, K planes)
+    ("split_remainders_E4_k1", 1300, 256, 4, 256, 1, "bf16", 0, None),
+    ("split_ceil_E4_k1", 1800, 256, 4, 256, 1, "bf16", 0, None),
+    ("split_below_256_E12", 3000, 256, 12, 256, 1, "bf16", 0, None),
+    ("split_kplanes", 1100, 256, 4, 2048, 1, "bf16", 0, None),
+    ("split_shared", 1500, 256, 4, 256, 1, "bf16", 256, None),
     # one token routed inside the SwiGLU weight-streaming kernel (E * d <= 65536)
     ("routed_T1_E32_k4_hot", 1, 2048, 32, 2048, 4, "bf16", 0, ("hot", 31, 100.0)),
     ("routed_T1_E16_shared_limit", 1, 4096, 16, 2048, 2, "bf16", 4096, None),
@@ -275,7 +283,7 @@ def test_edge_cases(case_):
     err = rel_l2(f64(moe.tensor_to_numpy(y)), ref["y"])
     say(f"edge {label}: rel-L2 {err:.3e}")
     assert err <= TOL[dt]
-    if label.startswith(("kplanes", "gemv_T1", "routed")):
+    if label.startswith(("kplanes", "gemv_T1", "routed", "split")):
         # a workspace full of garbage gives the same bits
         y1 = y.clone()
         L._ws.fill_(0x5A)
