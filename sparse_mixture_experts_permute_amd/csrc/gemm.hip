@@ -391,13 +391,16 @@ __device__ __forceinline__ void dl_epilogue(const TA &ta, f32x16_v (&acc)[TM][TN
 
 // SPLIT: the last round's tiles may be split along K (plan_split); compiled
 // only where that pays, since the split's code costs registers in every tile.
-template <int BM, int BNB, bool SWIGLU, bool SPLIT>
+// GATHER: A is the token matrix x (a_bytes bytes) and tile row s reads x row
+// gperm[s] / gk, so the grouped rows are never written out; each lane keeps
+// the byte offsets of its rows for the tile (one per A instruction).
+template <int BM, int BNB, bool SWIGLU, bool SPLIT, bool GATHER = false>
 __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
     const bf16_t *__restrict__ A, const bf16_t *__restrict__ B1, const bf16_t *__restrict__ B3,
     void *__restrict__ C, const int32_t *__restrict__ seg_off,
     const int32_t *__restrict__ seg_end, const int32_t *__restrict__ mtile_off, int G, int N,
     int K, size_t plane, int act, int32_t *__restrict__ fix_cnt, f32x4_v *__restrict__ fix_part,
-    int part_cap) {
+    int part_cap, const int32_t *__restrict__ gperm, int gk, uint32_t a_bytes) {
   constexpr int WM = 2, WN = 2;
   constexpr int TM = BM / WM / 32, TN = BNB / WN / 32;
   constexpr int ROWS = BM + BNB;          // tile rows per stage (A then B)
@@ -443,6 +446,7 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
   struct TileAddr {
     __amdgpu_buffer_rsrc_t ra, r1, r3;
     uint32_t lc0, lc1;
+    uint32_t ga[GATHER ? IA : 1];  // GATHER: byte offset in x of each A instruction's row
     int row0, rows, n0;
     int nk;    // K slices of this unit (even)
     int part;  // part of a split tail tile, or -1 for a whole tile
@@ -473,8 +477,21 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
     ta.row0 = seg_off[e] + (t.g - mtile_off[e]) * BM;
     ta.rows = min(BM, seg_end[e] - ta.row0);
     ta.n0 = t.n * COLS;
-    ta.ra = make_rsrc(reinterpret_cast<const char *>(A) + (size_t)ta.row0 * rowb + kb,
-                      (uint32_t)ta.rows * rowb - kb);
+    if constexpr (GATHER) {
+      // the whole of x; a row past the tile's end reads at a_bytes, past the
+      // buffer's range, which loads zeros
+      ta.ra = make_rsrc(reinterpret_cast<const char *>(A) + kb, a_bytes - kb);
+      const uint32_t cx0 = (uint32_t)((lchunk ^ (lrow >> 1)) * 16);
+#pragma unroll
+      for (int j = 0; j < IA; ++j) {
+        const int r = (wave * IA + j) * 8 + lrow;
+        const uint32_t cx = (j & 1) ? (cx0 ^ 64u) : cx0;
+        ta.ga[j] = (r < ta.rows ? (uint32_t)(gperm[ta.row0 + r] / gk) * rowb : a_bytes) + cx;
+      }
+    } else {
+      ta.ra = make_rsrc(reinterpret_cast<const char *>(A) + (size_t)ta.row0 * rowb + kb,
+                        (uint32_t)ta.rows * rowb - kb);
+    }
     const size_t eoff = (size_t)e * N * rowb + kb;
     const uint32_t wbytes = (uint32_t)N * rowb - kb;
     ta.r1 = make_rsrc(reinterpret_cast<const char *>(B1) + eoff, wbytes);
@@ -495,8 +512,12 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
 #pragma unroll
     for (int j = 0; j < IA; ++j)
       if (j >= j0 && j < j1) {
-        const uint32_t u = (uint32_t)((wave * IA + j) * 8) * rowb + ko;
-        buffer_to_lds16(ta.ra, ((j & 1) ? ta.lc1 : ta.lc0) + u, stage + (wave * IA + j) * 64);
+        if constexpr (GATHER) {
+          buffer_to_lds16(ta.ra, ta.ga[j] + ko, stage + (wave * IA + j) * 64);
+        } else {
+          const uint32_t u = (uint32_t)((wave * IA + j) * 8) * rowb + ko;
+          buffer_to_lds16(ta.ra, ((j & 1) ? ta.lc1 : ta.lc0) + u, stage + (wave * IA + j) * 64);
+        }
       }
 #pragma unroll
     for (int j = 0; j < IB; ++j) {
@@ -740,20 +761,21 @@ int resident_wgs(int bm) {
   return cus[dev] * (bm == 64 ? 2 : 1);
 }
 
-template <int BM, int BNB, bool SWIGLU, bool SPLIT = false>
+template <int BM, int BNB, bool SWIGLU, bool SPLIT = false, bool GATHER = false>
 hipError_t launch_dl(const void *A, const void *B1, const void *B3, void *C,
                      const int32_t *seg_off, const int32_t *seg_end, const int32_t *mtile_off,
                      int G, int N, int K, int ksplit, size_t plane, int act, const FixScratch &fx,
-                     hipStream_t s) {
+                     hipStream_t s, const int32_t *gperm = nullptr, int gk = 1,
+                     uint32_t a_bytes = 0) {
   // persistent grid: what stays resident, a multiple of the XCD count
   const int gx = (resident_wgs(BM) / ksplit + NUM_XCD - 1) / NUM_XCD * NUM_XCD;
   const size_t cap = fx.part ? fx.part_bytes / ((size_t)BM * BNB * 4) : 0;
-  hipLaunchKernelGGL((grouped_gemm_dl_kernel<BM, BNB, SWIGLU, SPLIT>), dim3(gx, ksplit),
+  hipLaunchKernelGGL((grouped_gemm_dl_kernel<BM, BNB, SWIGLU, SPLIT, GATHER>), dim3(gx, ksplit),
                      dim3(GM_THREADS), 0, s, (const bf16_t *)A, (const bf16_t *)B1,
                      (const bf16_t *)B3, C, seg_off, seg_end ? seg_end : seg_off + 1, mtile_off, G,
-                     N, K, plane, act, fx.cnt,
-                     (f32x4_v *)fx.part,
-                     (int)(cap < (size_t)FIX_SLOTS * 16 ? cap : (size_t)FIX_SLOTS * 16));
+                     N, K, plane, act, fx.cnt, (f32x4_v *)fx.part,
+                     (int)(cap < (size_t)FIX_SLOTS * 16 ? cap : (size_t)FIX_SLOTS * 16), gperm,
+                     gk, a_bytes);
   return hipGetLastError();
 }
 
@@ -790,12 +812,23 @@ GemmPlan gemm_plan(int dtype, int d, int d_ff, int d_ff_shared, long long rows_p
   return p;
 }
 
+bool gemm_gather_ok(int dtype, bool dl, int bm, long long a_bytes) {
+  return dtype == 1 && dl && bm == 64 && a_bytes + (1LL << 20) < (1LL << 31);
+}
+
 hipError_t launch_gemm_swiglu(int dtype, bool dl, int bm, int act, const void *A,
                               const void *W1, const void *W3, void *H, const int32_t *seg_off,
                               const int32_t *mtile_off, int G, int N, int K, int max_mtiles,
-                              hipStream_t s, const int32_t *seg_end) {
+                              hipStream_t s, const int32_t *seg_end, const int32_t *gperm, int gk,
+                              long long a_bytes) {
   if (max_mtiles <= 0) return hipSuccess;
   const FixScratch none{nullptr, nullptr, 0};
+  if (gperm) {
+    if (!gemm_gather_ok(dtype, dl, bm, a_bytes)) return hipErrorInvalidValue;
+    return launch_dl<64, 256, true, false, true>(A, W1, W3, H, seg_off, seg_end, mtile_off, G, N,
+                                                 K, 1, 0, act, none, s, gperm, gk,
+                                                 (uint32_t)a_bytes);
+  }
   if (dl && bm == 64)
     return launch_dl<64, 256, true>(A, W1, W3, H, seg_off, seg_end, mtile_off, G, N, K, 1, 0,
                                     act, none, s);

@@ -112,10 +112,14 @@ size_t fix_part_bytes(long long tiles);
 // act: 0 SiLU(W1 a) * (W3 a), 1 sigmoid(W1 a) * (W3 a)
 // seg_end (direct-to-LDS kernel only; NULL: seg_off + 1): expert e's rows
 // are seg_off[e] .. seg_end[e] - 1, with mtile_off the prefix of its tiles.
+// gperm (gemm_gather_ok only): A is x itself (a_bytes bytes) and grouped row s
+// is read from x row gperm[s] / gk inside the GEMM (no gathered copy).
+bool gemm_gather_ok(int dtype, bool dl, int bm, long long a_bytes);
 hipError_t launch_gemm_swiglu(int dtype, bool dl, int bm, int act, const void *A,
                               const void *W1, const void *W3, void *H, const int32_t *seg_off,
                               const int32_t *mtile_off, int G, int N, int K, int max_mtiles,
-                              hipStream_t s, const int32_t *seg_end = nullptr);
+                              hipStream_t s, const int32_t *seg_end = nullptr,
+                              const int32_t *gperm = nullptr, int gk = 1, long long a_bytes = 0);
 // ksplit > 1 (direct-to-LDS kernel only): every tile's K is split in ksplit
 // equal ranges whose fp32 partials go to planes `plane` elements apart (for
 // batches with few tiles; the last-round split then stays off).
