@@ -358,9 +358,10 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
   // T=8192 gain 5%).
   const bool split = !sk.routed && plan.dl1 && plan.dl2 && plan.bm1 == 256 && plan.bm2 == 256 &&
                      (long long)P < 512LL * E;
-  // 64-row tiles read their rows straight from x (no gathered copy)
-  const bool gather_fused =
-      !sk.routed && plan.dl1 && moe::gemm_gather_ok(dtype, plan.dl1, plan.bm1, (long long)T * d * 2);
+  // 64-row tiles (and the split tiling's 256-row tiles) read their rows
+  // straight from x (no gathered copy)
+  const bool gather_fused = !sk.routed && plan.dl1 && (plan.bm1 == 64 || split) &&
+                            moe::gemm_gather_ok(dtype, plan.dl1, plan.bm1, (long long)T * d * 2);
 
   hipError_t e;
   // stage boundary i: an optional timing event recorded on the stream
@@ -427,7 +428,15 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
         (e = moe::launch_gather(x, perm, offsets + E, P, k, d, (int)esize(dtype), Xp, s)))
       goto fail;
     MOE_MARK(3);
-    if (gather_fused) {
+    if (gather_fused && split) {
+      if ((e = moe::launch_gemm_swiglu(dtype, true, 256, o.activation, x, W1, W3, H, offsets, mt0,
+                                       E, d_ff, d, P / 256 + E, s, mid, perm, k,
+                                       (long long)T * d * 2)) ||
+          (e = moe::launch_gemm_swiglu(dtype, true, 64, o.activation, x, W1, W3, H, mid, mt1, E,
+                                       d_ff, d, moe::SPLIT_REM_TILES * E, s, offsets + 1, perm, k,
+                                       (long long)T * d * 2)))
+        goto fail;
+    } else if (gather_fused) {
       if ((e = moe::launch_gemm_swiglu(dtype, true, 64, o.activation, x, W1, W3, H, offsets, mt0,
                                        E, d_ff, d, (P + 63) / 64 + E, s, nullptr, perm, k,
                                        (long long)T * d * 2)))

@@ -813,7 +813,7 @@ GemmPlan gemm_plan(int dtype, int d, int d_ff, int d_ff_shared, long long rows_p
 }
 
 bool gemm_gather_ok(int dtype, bool dl, int bm, long long a_bytes) {
-  return dtype == 1 && dl && bm == 64 && a_bytes + (1LL << 20) < (1LL << 31);
+  return dtype == 1 && dl && (bm == 64 || bm == 256) && a_bytes + (1LL << 20) < (1LL << 31);
 }
 
 hipError_t launch_gemm_swiglu(int dtype, bool dl, int bm, int act, const void *A,
@@ -825,9 +825,13 @@ hipError_t launch_gemm_swiglu(int dtype, bool dl, int bm, int act, const void *A
   const FixScratch none{nullptr, nullptr, 0};
   if (gperm) {
     if (!gemm_gather_ok(dtype, dl, bm, a_bytes)) return hipErrorInvalidValue;
-    return launch_dl<64, 256, true, false, true>(A, W1, W3, H, seg_off, seg_end, mtile_off, G, N,
-                                                 K, 1, 0, act, none, s, gperm, gk,
-                                                 (uint32_t)a_bytes);
+    if (bm == 64)
+      return launch_dl<64, 256, true, false, true>(A, W1, W3, H, seg_off, seg_end, mtile_off, G,
+                                                   N, K, 1, 0, act, none, s, gperm, gk,
+                                                   (uint32_t)a_bytes);
+    return launch_dl<256, 256, true, false, true>(A, W1, W3, H, seg_off, seg_end, mtile_off, G, N,
+                                                  K, 1, 0, act, none, s, gperm, gk,
+                                                  (uint32_t)a_bytes);
   }
   if (dl && bm == 64)
     return launch_dl<64, 256, true>(A, W1, W3, H, seg_off, seg_end, mtile_off, G, N, K, 1, 0,
