@@ -358,6 +358,9 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
   // T=8192 gain 5%).
   const bool split = !sk.routed && plan.dl1 && plan.dl2 && plan.bm1 == 256 && plan.bm2 == 256 &&
                      (long long)P < 512LL * E;
+  // the tiled down projection of the bf16 layer leaves its outputs in bf16
+  // (one plane), which halves what it writes and the combine reads
+  const bool yp_bf16 = dtype == MOE_BF16 && !sk.routed && ksplit == 1 && plan.dl2;
   // 64-row tiles (and the split tiling's 256-row tiles) read their rows
   // straight from x (no gathered copy)
   const bool gather_fused = !sk.routed && plan.dl1 && (plan.bm1 == 64 || split) &&
@@ -455,13 +458,14 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
     MOE_MARK(4);
     if (split) {
       if ((e = moe::launch_gemm_down(dtype, true, 256, H, W2, Yp, offsets, mt0, E, d, d_ff,
-                                     P / 256 + E, ksplit, plane, fx, s, mid)) ||
+                                     P / 256 + E, ksplit, plane, fx, s, mid, yp_bf16)) ||
           (e = moe::launch_gemm_down(dtype, true, 64, H, W2, Yp, mid, mt1, E, d, d_ff,
-                                     moe::SPLIT_REM_TILES * E, ksplit, plane, fx, s, offsets + 1)))
+                                     moe::SPLIT_REM_TILES * E, ksplit, plane, fx, s, offsets + 1,
+                                     yp_bf16)))
         goto fail;
     } else if ((e = moe::launch_gemm_down(dtype, plan.dl2, plan.bm2, H, W2, Yp, offsets, mt1, E, d,
                                           d_ff, (P + plan.bm2 - 1) / plan.bm2 + E, ksplit, plane,
-                                          fx, s))) {
+                                          fx, s, nullptr, yp_bf16))) {
       goto fail;
     }
     MOE_MARK(5);
@@ -494,7 +498,7 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
   MOE_MARK(6);
   if (!fused_combine &&
       (e = moe::launch_combine(dtype, Yp, ksplit, plane, shared ? Ys : nullptr, inv, gate, T, k,
-                               d, y, s)))
+                               d, y, s, yp_bf16)))
     goto fail;
   MOE_MARK(7);
 #undef MOE_MARK

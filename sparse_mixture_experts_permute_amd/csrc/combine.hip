@@ -3,7 +3,8 @@
 // A pair with inv < 0 was dropped by an expert's capacity limit and adds
 // nothing.  Summed in fp32 with j ascending, written once per token with no
 // atomics.  When the down projection split K into planes, Yp has nsplit planes
-// whose rows are added first, in plane order
+// whose rows are added first, in plane order; the bf16 layer's tiled down
+// projection otherwise leaves Yp in bf16
 // ("Chapter 10 MoE", sections 10.4 and 10.5; "Mixtral and MoE architecture",
 // weighted accumulation in the MixtralMoE listing).
 #include "common.h"
@@ -13,9 +14,20 @@ namespace moe {
 
 namespace {
 
+// Four consecutive elements of a Yp row (fp32 or bf16) as fp32.
+__device__ __forceinline__ float4 load4(const float *p, size_t i4) {
+  return reinterpret_cast<const float4 *>(p)[i4];
+}
+__device__ __forceinline__ float4 load4(const bf16_t *p, size_t i4) {
+  const uint2 u = reinterpret_cast<const uint2 *>(p)[i4];
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                     __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
+}
+
 // One block per token; each thread handles 4 consecutive columns per step.
-template <typename T>
-__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ Yp, int nsplit,
+// YT: Yp's element type (bf16 Yp has one plane).
+template <typename T, typename YT>
+__global__ __launch_bounds__(256) void combine_kernel(const YT *__restrict__ Yp, int nsplit,
                                                       size_t plane,
                                                       const float *__restrict__ Ys,
                                                       const int32_t *__restrict__ inv,
@@ -30,9 +42,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
       if (slot < 0) continue;
       const float g = gate[(size_t)t * k + j];
       const size_t row = (size_t)slot * d4 + c;
-      float4 v = reinterpret_cast<const float4 *>(Yp)[row];
+      float4 v = load4(Yp, row);
       for (int sp = 1; sp < nsplit; ++sp) {
-        const float4 u = reinterpret_cast<const float4 *>(Yp + sp * plane)[row];
+        const float4 u = load4(Yp + sp * plane, row);
         v.x += u.x;
         v.y += u.y;
         v.z += u.z;
@@ -60,16 +72,20 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
 
 }  // namespace
 
-hipError_t launch_combine(int dtype, const float *Yp, int nsplit, size_t plane, const float *Ys,
+hipError_t launch_combine(int dtype, const void *Yp, int nsplit, size_t plane, const float *Ys,
                           const int32_t *inv, const float *gate, int T, int k, int d, void *y,
-                          hipStream_t s) {
+                          hipStream_t s, bool yp_bf16) {
   if (T <= 0) return hipSuccess;
-  if (dtype == 1)
-    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(T), dim3(256), 0, s, Yp, nsplit, plane, Ys,
-                       inv, gate, k, d, (bf16_t *)y);
+  if (yp_bf16 && nsplit != 1) return hipErrorInvalidValue;
+  if (yp_bf16)
+    hipLaunchKernelGGL((combine_kernel<bf16_t, bf16_t>), dim3(T), dim3(256), 0, s,
+                       (const bf16_t *)Yp, 1, plane, Ys, inv, gate, k, d, (bf16_t *)y);
+  else if (dtype == 1)
+    hipLaunchKernelGGL((combine_kernel<bf16_t, float>), dim3(T), dim3(256), 0, s,
+                       (const float *)Yp, nsplit, plane, Ys, inv, gate, k, d, (bf16_t *)y);
   else
-    hipLaunchKernelGGL(combine_kernel<float>, dim3(T), dim3(256), 0, s, Yp, nsplit, plane, Ys,
-                       inv, gate, k, d, (float *)y);
+    hipLaunchKernelGGL((combine_kernel<float, float>), dim3(T), dim3(256), 0, s,
+                       (const float *)Yp, nsplit, plane, Ys, inv, gate, k, d, (float *)y);
   return hipGetLastError();
 }
 

@@ -337,9 +337,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // weight fragment as their first operand, so each accumulator block holds the
 // transposed product: lane l has token row l % 32 of the block and, in each of
 // the four groups of 8 output columns, the 4 consecutive columns starting at
-// 4 * (l / 32).  SwiGLU gates those 4 columns and stores them as 8 bytes of
-// bf16; the down projection stores them as 16 bytes of fp32.  No LDS staging,
-// so both stages are free for the next tile's loads during the epilogue.
+// 4 * (l / 32).  SwiGLU gates those 4 columns (act: the gate's activation)
+// and stores them as 8 bytes of bf16; the down projection stores them as 16
+// bytes of fp32 into plane blockIdx.y, or (act = 1, one plane) as 8 bytes of
+// bf16.  No LDS staging, so both stages are free for the next tile's loads
+// during the epilogue.
 template <int BM, int BNB, bool SWIGLU, int TM, int TN, typename TA>
 __device__ __forceinline__ void dl_epilogue(const TA &ta, f32x16_v (&acc)[TM][TN],
                                             void *__restrict__ C, int N, size_t plane, int act,
@@ -368,6 +370,23 @@ __device__ __forceinline__ void dl_epilogue(const TA &ta, f32x16_v (&acc)[TM][TN
           v.y = pack_bf16x2(h[2], h[3]);
           const int c = q * 32 + g * 8 + cq;
           if (grow < rows && n0 + wn * WC + c < N) *reinterpret_cast<uint2 *>(dst + c) = v;
+        }
+    }
+  } else if (act) {
+    bf16_t *out = reinterpret_cast<bf16_t *>(C);
+#pragma unroll
+    for (int a = 0; a < TM; ++a) {
+      const int r = (wm * TM + a) * 32 + tr;
+      bf16_t *dst = out + (size_t)(row0 + r) * N + n0;
+#pragma unroll
+      for (int b = 0; b < TN; ++b)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int c = (wn * TN + b) * 32 + g * 8 + cq;
+          uint2 v;
+          v.x = pack_bf16x2(acc[a][b][g * 4], acc[a][b][g * 4 + 1]);
+          v.y = pack_bf16x2(acc[a][b][g * 4 + 2], acc[a][b][g * 4 + 3]);
+          if (r < rows && n0 + c < N) *reinterpret_cast<uint2 *>(dst + c) = v;
         }
     }
   } else {
@@ -847,22 +866,24 @@ hipError_t launch_gemm_swiglu(int dtype, bool dl, int bm, int act, const void *A
                                                  max_mtiles, act, s);
 }
 
-hipError_t launch_gemm_down(int dtype, bool dl, int bm, const void *A, const void *W2, float *Y,
+hipError_t launch_gemm_down(int dtype, bool dl, int bm, const void *A, const void *W2, void *Y,
                             const int32_t *seg_off, const int32_t *mtile_off, int G, int N, int K,
                             int max_mtiles, int ksplit, size_t plane, const FixScratch &fx,
-                            hipStream_t s, const int32_t *seg_end) {
+                            hipStream_t s, const int32_t *seg_end, bool ybf16) {
   if (max_mtiles <= 0) return hipSuccess;
+  if (ybf16 && (!dl || ksplit != 1)) return hipErrorInvalidValue;
+  const int yb = ybf16 ? 1 : 0;
   if (dl && bm == 64)
     return launch_dl<64, 256, false>(A, W2, nullptr, Y, seg_off, seg_end, mtile_off, G, N, K,
-                                     ksplit, plane, 0, fx, s);
+                                     ksplit, plane, yb, fx, s);
   // the last-round split pays for long K only (the kernel's estimate never
   // splits below SPLIT_MIN_K)
   if (dl && ksplit == 1 && K >= SPLIT_MIN_K && fx.part)
     return launch_dl<256, 256, false, true>(A, W2, nullptr, Y, seg_off, seg_end, mtile_off, G,
-                                            N, K, 1, 0, 0, fx, s);
+                                            N, K, 1, 0, yb, fx, s);
   if (dl)
     return launch_dl<256, 256, false>(A, W2, nullptr, Y, seg_off, seg_end, mtile_off, G, N, K,
-                                      ksplit, plane, 0, fx, s);
+                                      ksplit, plane, yb, fx, s);
   if (seg_end) return hipErrorInvalidValue;  // the tiled kernels take whole segments
   if (dtype == 1)
     return launch_one<bf16_t, 128, 128, 2, 2, false>(A, W2, nullptr, Y, seg_off, mtile_off, G,

@@ -123,10 +123,11 @@ hipError_t launch_gemm_swiglu(int dtype, bool dl, int bm, int act, const void *A
 // ksplit > 1 (direct-to-LDS kernel only): every tile's K is split in ksplit
 // equal ranges whose fp32 partials go to planes `plane` elements apart (for
 // batches with few tiles; the last-round split then stays off).
-hipError_t launch_gemm_down(int dtype, bool dl, int bm, const void *A, const void *W2, float *Y,
+// ybf16 (direct-to-LDS kernel, one plane): Y is stored as bf16, else fp32.
+hipError_t launch_gemm_down(int dtype, bool dl, int bm, const void *A, const void *W2, void *Y,
                             const int32_t *seg_off, const int32_t *mtile_off, int G, int N, int K,
                             int max_mtiles, int ksplit, size_t plane, const FixScratch &fx,
-                            hipStream_t s, const int32_t *seg_end = nullptr);
+                            hipStream_t s, const int32_t *seg_end = nullptr, bool ybf16 = false);
 
 // Weight-streaming grouped GEMMs for few rows per expert (bf16 only).
 bool skinny_ok(int N, int K);
@@ -168,10 +169,11 @@ hipError_t launch_skinny_down(int mb, const void *Hin, const void *W2, float *Y,
                               const int32_t *seg_off, const int32_t *active,
                               const int32_t *nactive, int G, int N, int K, hipStream_t s);
 
-// Yp holds nsplit planes of `plane` floats each (summed in order); a pair
-// with inv < 0 (dropped by a capacity limit) contributes nothing.
-hipError_t launch_combine(int dtype, const float *Yp, int nsplit, size_t plane, const float *Ys,
+// Yp holds nsplit planes of `plane` floats each (summed in order), or with
+// yp_bf16 one plane of bf16; a pair with inv < 0 (dropped by a capacity
+// limit) contributes nothing.
+hipError_t launch_combine(int dtype, const void *Yp, int nsplit, size_t plane, const float *Ys,
                           const int32_t *inv, const float *gate, int T, int k, int d, void *y,
-                          hipStream_t s);
+                          hipStream_t s, bool yp_bf16 = false);
 
 }  // namespace moe
