@@ -596,7 +596,8 @@ int orc_forward_ex(const void *x, const void *Wg, const float *bias,
     return 0;
 }
 
-/* The method as the spec pages define it: softmax over the selected
+/* The method itself ("Chapter 10 MoE", section 10.3; "Mistral 8x7B SMoE
+ * architecture deep dive", sections 3.1 and 3.2): softmax over the selected
  * logits, SwiGLU experts, no capacity limit. */
 int orc_forward(const void *x, const void *Wg, const float *bias,
                 const void *W1, const void *W3, const void *W2,
