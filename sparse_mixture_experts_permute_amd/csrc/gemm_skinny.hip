@@ -636,6 +636,78 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_down_token_kernel(
   }
 }
 
+// One token's SwiGLU projection (K = KF * 512) after the routing prologue,
+// every wavefront on its own run of the workgroup's columns: the 64 lanes
+// split K in pieces of 8 weights of KF chunks per row and reduce by the
+// butterfly, with two columns' W1 and W3 rows in flight.  No wavefront waits
+// for another (gemv_kernel's cross-wave reduction puts a barrier between a
+// group's data and the next group's loads).  W8: FP8 codes with the
+// per-expert scales applied to the reduced sums.
+template <int KF, bool W8>
+__global__ __launch_bounds__(GV_THREADS) void gemv_swiglu_wave_kernel(
+    const bf16_t *__restrict__ x, const void *__restrict__ W1v, const void *__restrict__ W3v,
+    bf16_t *__restrict__ H, int N, int K, int cpw, int act, DecodeRoute rt,
+    const float *__restrict__ sc1, const float *__restrict__ sc3) {
+  using WT = typename std::conditional<W8, uint8_t, bf16_t>::type;
+  using WV = typename std::conditional<W8, uint2, uint4>::type;
+  __shared__ RouteLds rsh;
+  route_token(x, K, rt, rsh);
+  const int nblk = N / cpw;
+  const int a_idx = blockIdx.x / nblk;
+  if (a_idx >= rsh.active[rt.E]) return;
+  const int e = rsh.active[a_idx];
+  const int s0 = rsh.offsets[e];
+  const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
+  const int ncw = cpw / GV_WAVES;
+  const int c0 = (blockIdx.x % nblk) * cpw + wave * ncw;
+  uint4 xa[KF];
+  const bf16_t *xp = x + (size_t)(rsh.perm[s0] / rt.k) * K + lane * 8;
+#pragma unroll
+  for (int i = 0; i < KF; ++i) xa[i] = *reinterpret_cast<const uint4 *>(xp + i * GV_CHUNK);
+  const WT *w1 = reinterpret_cast<const WT *>(W1v) + (size_t)e * N * K + lane * 8;
+  const WT *w3 = reinterpret_cast<const WT *>(W3v) + (size_t)e * N * K + lane * 8;
+  const int rot = (blockIdx.x + wave) % ncw;  // spread the workgroups over HBM channels
+  auto col = [&](int j) { return c0 + (j + rot) % ncw; };
+  auto load = [&](WV (&dst)[2][KF], int j) {
+    const size_t ro = (size_t)col(j) * K;
+#pragma unroll
+    for (int i = 0; i < KF; ++i) {
+      dst[0][i] = gv_load(w1 + ro + i * GV_CHUNK);
+      dst[1][i] = gv_load(w3 + ro + i * GV_CHUNK);
+    }
+  };
+  auto compute = [&](const WV (&w)[2][KF], int j) {
+    float g = 0.f, u = 0.f;
+#pragma unroll
+    for (int i = 0; i < KF; ++i) {
+      g = gv_dot(xa[i], w[0][i], g);
+      u = gv_dot(xa[i], w[1][i], u);
+    }
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+      g += __shfl_xor(g, off);
+      u += __shfl_xor(u, off);
+    }
+    if (W8) {
+      g *= sc1[e];
+      u *= sc3[e];
+    }
+    if (lane == 0) H[(size_t)s0 * N + col(j)] = f32_to_bf16(gated(g, u, act));
+  };
+  WV wa[2][KF], wb[2][KF];
+  load(wa, 0);
+  load(wb, 1);
+  int j = 0;
+  for (; j + 2 < ncw; j += 2) {  // ncw is even
+    compute(wa, j);
+    load(wa, j + 2);
+    compute(wb, j + 1);
+    load(wb, j + 3);
+  }
+  compute(wa, j);
+  compute(wb, j + 1);
+}
+
 template <bool SWIGLU, int R, bool COMBINE = false, bool W8 = false, bool ROUTE = false>
 hipError_t launch_gemv_r(int act, const void *A, const int32_t *perm, int kslots,
                          const void *B1, const void *B3, void *C, const int32_t *seg_off,
@@ -772,6 +844,29 @@ bool route_fused_ok(int T, int d, int E, int k) {
 hipError_t launch_gemv_swiglu_routed(int act, const void *x, const DecodeRoute &r, const void *W1,
                                      const void *W3, const float *s1, const float *s3, void *H,
                                      int N, int K, hipStream_t s) {
+  const int kf = K / GV_CHUNK;
+  if (kf == 4 || kf == 8) {
+    // column blocks of a multiple of 8 (an even number per wavefront), as
+    // many as make one workgroup per CU over the k active experts
+    int cpw = N;
+    for (int m = 2 * GV_WAVES; m <= N; m += 2 * GV_WAVES)
+      if (N % m == 0 && (long long)r.k * (N / m) <= 256) {
+        cpw = m;
+        break;
+      }
+    if (N % cpw || (cpw / GV_WAVES) % 2) return hipErrorInvalidValue;
+    const dim3 grid(r.k * (N / cpw));
+#define GW_LAUNCH(KF_, W8_)                                                                   \
+  hipLaunchKernelGGL((gemv_swiglu_wave_kernel<KF_, W8_>), grid, dim3(GV_THREADS), 0, s,        \
+                     (const bf16_t *)x, W1, W3, (bf16_t *)H, N, K, cpw, act, r, s1, s3)
+    if (kf == 8) {
+      if (s1) GW_LAUNCH(8, true); else GW_LAUNCH(8, false);
+    } else {
+      if (s1) GW_LAUNCH(4, true); else GW_LAUNCH(4, false);
+    }
+#undef GW_LAUNCH
+    return hipGetLastError();
+  }
   // one token: at most k experts are active, and the grid covers exactly k
   if (s1)
     return launch_gemv_r<true, 1, false, true, true>(act, x, nullptr, r.k, W1, W3, H, nullptr,
