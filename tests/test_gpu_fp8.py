@@ -65,7 +65,8 @@ def fp8_case(T, d, E, dff, k, seed=3, skew=0.0):
 
 @pytest.mark.parametrize("T,E,k,dff,gm,cap", [(1, 8, 2, 2048, 0, None), (2, 8, 2, 4096, 0, None),
                                              (3, 8, 2, 2048, 1, None), (4, 4, 2, 2048, 0, None),
-                                             (4, 8, 3, 2048, 3, None), (3, 8, 2, 2048, 0, 1)])
+                                             (4, 8, 3, 2048, 3, None), (3, 8, 2, 2048, 0, 1),
+                                             (1, 8, 3, 4096, 3, None), (1, 16, 4, 2048, 2, None)])
 def test_forward_fp8(T, E, k, dff, gm, cap):
     d = 2048
     cfg, h, dev = fp8_case(T, d, E, dff, k, seed=T * 10 + E, skew=1.5 if cap else 0.0)

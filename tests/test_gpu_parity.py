@@ -257,6 +257,9 @@ EDGE = [
     # one token routed inside the SwiGLU weight-streaming kernel (E * d <= 65536)
     ("routed_T1_E32_k4_hot", 1, 2048, 32, 2048, 4, "bf16", 0, ("hot", 31, 100.0)),
     ("routed_T1_E16_shared_limit", 1, 4096, 16, 2048, 2, "bf16", 4096, None),
+    # d = 6144: the routed kernel whose four waves split K (the per-wavefront one takes d of
+    # 2048 or 4096)
+    ("routed_T1_d6144", 1, 6144, 8, 2048, 2, "bf16", 0, None),
 ]
 
 
