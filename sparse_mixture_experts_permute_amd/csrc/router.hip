@@ -19,9 +19,10 @@
 //             tokens).  With one slice (large batches) and k <= 16 this kernel
 //             also runs the top-k and the gate, and there is no second kernel;
 //           - more experts: a register-tiled VALU GEMM.  A 256-thread block owns
-//             64 tokens x 64 experts x one slice; each thread keeps 4 x 4 sums
-//             and streams its slice through LDS in 64-element chunks
-//             (double-buffered, one barrier per chunk).
+//             128 tokens x 128 experts x one slice; each thread keeps 8 x 8 sums
+//             (8 LDS reads per 64 dot products) and streams its slice through
+//             LDS in 64-element chunks (double-buffered, one barrier per
+//             chunk).
 //  topk   : one wavefront per token sums the S partials in a fixed order (so
 //           the scores do not depend on scheduling), adds the bias, writes the
 //           scores, and runs k rounds of a wavefront arg-max and the gate.
@@ -33,7 +34,9 @@ namespace moe {
 
 namespace {
 
-constexpr int RS_TOK = 64, RS_EXP = 64;  // block tile
+constexpr int RS_TOK = 128, RS_EXP = 128;  // block tile
+constexpr int RS_JT = RS_TOK / 16;  // tokens per thread
+constexpr int RS_JE = RS_EXP / 16;  // experts per thread
 constexpr int RS_THREADS = 256;
 constexpr int RS_ROWB = 128;            // bytes of a row chunk (64 bf16 / 32 fp32)
 constexpr int RS_LDW = (RS_ROWB + 16) / 16;  // padded LDS row stride in uint4
@@ -80,7 +83,7 @@ __global__ __launch_bounds__(RS_THREADS, 2) void router_scores_kernel(
   const int tid = threadIdx.x;
   const int t0 = blockIdx.x * RS_TOK, e0 = blockIdx.y * RS_EXP;
   const int s = blockIdx.z;
-  const int tg = tid / 16, eg = tid % 16;  // 16 x 16 threads, 4 x 4 outputs each
+  const int tg = tid / 16, eg = tid % 16;  // 16 x 16 threads, RS_JT x RS_JE outputs each
 
   const uint4 *xg = reinterpret_cast<const uint4 *>(x);
   const uint4 *wgg = reinterpret_cast<const uint4 *>(Wg);
@@ -88,33 +91,42 @@ __global__ __launch_bounds__(RS_THREADS, 2) void router_scores_kernel(
   const size_t q0 = (size_t)s * dslice / VEC;
   const int nchunk = dslice * (int)sizeof(T) / RS_ROWB;
 
-  // each thread stages 2 x-chunks and 2 Wg-chunks of 16 bytes per row chunk
-  uint4 rx[2], rw[2];
+  constexpr int NX = RS_TOK * CPR / RS_THREADS, NW = RS_EXP * CPR / RS_THREADS;
+  uint4 rx[NX], rw[NW];
   auto gload = [&](int c) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int idx = tid + i * RS_THREADS;  // 0..511: 64 rows x 8 uint4
+    for (int i = 0; i < NX; ++i) {
+      const int idx = tid + i * RS_THREADS;
       const int r = idx / CPR, q = idx % CPR;
       const size_t col = q0 + (size_t)c * CPR + q;
       rx[i] = (t0 + r < T_) ? xg[(size_t)(t0 + r) * rowq + col] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      const int idx = tid + i * RS_THREADS;
+      const int r = idx / CPR, q = idx % CPR;
+      const size_t col = q0 + (size_t)c * CPR + q;
       rw[i] = (e0 + r < E) ? wgg[(size_t)(e0 + r) * rowq + col] : make_uint4(0, 0, 0, 0);
     }
   };
   auto lstore = [&](int b) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < NX; ++i) {
       const int idx = tid + i * RS_THREADS;
-      const int r = idx / CPR, q = idx % CPR;
-      xs[b][r * RS_LDW + q] = rx[i];
-      ws[b][r * RS_LDW + q] = rw[i];
+      xs[b][(idx / CPR) * RS_LDW + idx % CPR] = rx[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      const int idx = tid + i * RS_THREADS;
+      ws[b][(idx / CPR) * RS_LDW + idx % CPR] = rw[i];
     }
   };
 
-  float acc[4][4];
+  float acc[RS_JT][RS_JE];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < RS_JT; ++a)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[a][j] = 0.f;
+    for (int j = 0; j < RS_JE; ++j) acc[a][j] = 0.f;
 
   gload(0);
   lstore(0);
@@ -124,15 +136,15 @@ __global__ __launch_bounds__(RS_THREADS, 2) void router_scores_kernel(
     if (c + 1 < nchunk) gload(c + 1);
 #pragma unroll 2
     for (int q = 0; q < CPR; ++q) {
-      uint4 xv[4], wv[4];
+      uint4 xv[RS_JT], wv[RS_JE];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) xv[a] = xs[b][(tg * 4 + a) * RS_LDW + q];
+      for (int a = 0; a < RS_JT; ++a) xv[a] = xs[b][(tg * RS_JT + a) * RS_LDW + q];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) wv[j] = ws[b][(eg + 16 * j) * RS_LDW + q];
+      for (int j = 0; j < RS_JE; ++j) wv[j] = ws[b][(eg + 16 * j) * RS_LDW + q];
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int a = 0; a < RS_JT; ++a)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[a][j] = dot16b(xv[a], wv[j], acc[a][j], T());
+        for (int j = 0; j < RS_JE; ++j) acc[a][j] = dot16b(xv[a], wv[j], acc[a][j], T());
     }
     if (c + 1 < nchunk) lstore(b ^ 1);
     __syncthreads();
@@ -140,11 +152,11 @@ __global__ __launch_bounds__(RS_THREADS, 2) void router_scores_kernel(
 
   float *out = part + (size_t)s * T_ * E;
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int t = t0 + tg * 4 + a;
+  for (int a = 0; a < RS_JT; ++a) {
+    const int t = t0 + tg * RS_JT + a;
     if (t >= T_) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < RS_JE; ++j) {
       const int e = e0 + eg + 16 * j;
       if (e < E) out[(size_t)t * E + e] = acc[a][j];
     }
