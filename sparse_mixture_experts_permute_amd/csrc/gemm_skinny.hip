@@ -159,14 +159,21 @@ hipError_t launch_mb(int mb, int act, const void *A, const int32_t *perm, int ks
 
 
 // ---------------------------------------------------------------------------
-// Vector-ALU weight streaming for experts that hold one to four rows (a single
-// decoded token).  Each wavefront instruction reads 1 KB of ONE weight row --
-// eight whole 128-byte lines -- with a non-temporal load (the weights are read
-// once), and v_dot2_f32_bf16 multiplies it with the matching slice of the
-// expert's rows, which each lane keeps in registers for the whole workgroup.
-// The four wavefronts split K; a workgroup walks its columns CB at a time with
-// the next group's weights in flight while the current one is reduced (lanes
-// by shuffles, wavefronts through LDS in a fixed order).
+// Vector-ALU weight streaming for experts that hold one to four rows (decode
+// steps).  Each wavefront instruction reads 1 KB of ONE weight row -- eight
+// whole 128-byte lines -- with a non-temporal load (the weights are read once),
+// and v_dot2_f32_bf16 multiplies it with the matching slice of the expert's
+// rows, which each lane keeps in registers for the whole workgroup.
+//  gemv_kernel             : up to four rows; the four wavefronts split K and a
+//                            workgroup walks its columns CB at a time with the
+//                            next group's weights in flight while the current
+//                            one is reduced (lanes by shuffles, wavefronts
+//                            through LDS in a fixed order)
+//  gemv_swiglu_wave_kernel : one token's SwiGLU projection after routing it,
+//                            every wavefront on its own columns over all of K
+//  gemv_down_token_kernel  : one token's down projection, a workgroup covering
+//                            a column block of every active expert, with the
+//                            combine formed in LDS
 // ---------------------------------------------------------------------------
 constexpr int GV_WAVES = 4;
 constexpr int GV_THREADS = GV_WAVES * kWave;
