@@ -300,8 +300,8 @@ def cpu_baseline(cfg, host, n_tokens):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer's "
-              "single-GPU path is what this build measures", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the layer is "
+              "measured on a single GPU", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
