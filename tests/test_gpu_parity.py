@@ -260,6 +260,9 @@ EDGE = [
     # d = 6144: the routed kernel whose four waves split K (the per-wavefront one takes d of
     # 2048 or 4096)
     ("routed_T1_d6144", 1, 6144, 8, 2048, 2, "bf16", 0, None),
+    # one token on a dense layer (E = k = 1) and on every expert (k = E)
+    ("routed_T1_dense_E1", 1, 2048, 1, 2048, 1, "bf16", 0, None),
+    ("routed_T1_k_equals_E", 1, 2048, 8, 4096, 8, "bf16", 0, None),
 ]
 
 
