@@ -53,6 +53,11 @@ CASES = [
     ("capacity_decode_T3_bf16", 3, 2048, 8, 2048, 2, "bf16", 0, 0.0, 1, 1, 1),
     ("capacity_page_cf_bf16", 512, 256, 8, 256, 2, "bf16", 0, 3.0, 0, 0, "page"),
     ("capacity_cf_0.3_bf16", 512, 256, 8, 256, 2, "bf16", 0, 3.0, 2, 0, 0.3),
+    # combine over more than eight pairs per token (rows loaded eight at a time):
+    # k = 16 with dropped pairs, and k = 12 (a partly filled second group) with
+    # a shared expert
+    ("combine_k16_cap_bf16", 64, 256, 64, 256, 16, "bf16", 0, 0.0, 0, 0, 10),
+    ("combine_k12_shared_f32", 40, 128, 32, 128, 12, "f32", 64, 0.0, 0, 0, None),
     # decode steps (T <= 4, E <= 64): top-k and grouping in one launch
     ("tiny_sigmoid_skew_f32", 3, 128, 8, 256, 2, "f32", 0, 1.5, 2, 0, None),
     ("tiny_E64_k16_cap3_bf16", 4, 256, 64, 256, 16, "bf16", 0, 0.0, 0, 0, 3),
