@@ -28,6 +28,9 @@
  *  - Every pointer argument is a DEVICE pointer owned by the caller; the
  *    library never allocates, frees or retains memory, and never synchronises
  *    the host with the device.
+ *  - Alignment: x, the weights (and FP8 codes) and y 16 bytes; bias, scales,
+ *    logits, gates and int32 arrays 4 bytes (any PyTorch allocation or row
+ *    slice qualifies).  A misaligned pointer is MOE_EINVAL.
  *  - `stream` is a hipStream_t (NULL = the default stream).  All work is
  *    enqueued on it asynchronously; results are valid once the stream has
  *    reached that point.
@@ -57,7 +60,7 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
 enum {
     MOE_OK = 0,
-    MOE_EINVAL = -1,     /* bad shape, k, E, or a required NULL pointer */
+    MOE_EINVAL = -1,     /* bad shape, k, E, a required NULL pointer, misalignment */
     MOE_EDTYPE = -2,     /* dtype not MOE_F32 / MOE_BF16 */
     MOE_EWORKSPACE = -3, /* workspace too small or misaligned (needs 256 B) */
     MOE_ELAUNCH = -4,    /* the HIP runtime refused a kernel launch */

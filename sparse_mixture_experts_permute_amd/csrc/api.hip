@@ -38,6 +38,11 @@ bool dims_ok(int T, int d, int d_ff, int E, int k, int dffs) {
 
 size_t esize(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
 
+// The kernels move tensors 16 bytes at a time (x, weights, y) and fp32 / int32
+// arrays 4 bytes at a time; a null pointer passes (checked separately).
+bool al16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+bool al4(const void *p) { return ((uintptr_t)p & 3) == 0; }
+
 // Most output tiles a down projection that may split its last round can have
 // (0: none can); sizes the scratch of that split.
 long long dl_tiles(const moe::GemmPlan &plan, int T, int k, int E, int d, int d_ff, int dffs) {
@@ -164,7 +169,8 @@ extern "C" {
 const char *moe_strerror(int status) {
   switch (status) {
     case MOE_OK: return "ok";
-    case MOE_EINVAL: return "invalid argument (shape, k, E or a required NULL pointer)";
+    case MOE_EINVAL:
+      return "invalid argument (shape, k, E, a required NULL pointer or a misaligned tensor)";
     case MOE_EDTYPE: return "unsupported dtype (MOE_F32 or MOE_BF16)";
     case MOE_EWORKSPACE: return "workspace too small or not 256-byte aligned";
     case MOE_ELAUNCH: return "kernel launch failed";
@@ -189,6 +195,8 @@ int moe_route_ex(const void *x, const void *Wg, const float *bias, int T, int d,
   if ((long long)T * E >= (1LL << 31)) return MOE_EINVAL;
   if (T == 0) return MOE_OK;
   if (!x || !Wg || !idx || !gate || !workspace) return MOE_EINVAL;
+  if (!al16(x) || !al16(Wg) || !al4(bias) || !al4(idx) || !al4(gate) || !al4(logits))
+    return MOE_EINVAL;
   if (workspace_bytes < moe_route_workspace_bytes(T, d, E, dtype) ||
       ((uintptr_t)workspace % kAlign))
     return MOE_EWORKSPACE;
@@ -232,6 +240,7 @@ int moe_permute_ex(const int32_t *idx, int T, int E, int k, int capacity, int32_
     return launched(hipMemsetAsync(offsets, 0, (size_t)(E + 1) * 4, s));
   }
   if (!idx || !counts || !offsets || !perm || !inv || !workspace) return MOE_EINVAL;
+  if (!al4(idx) || !al4(counts) || !al4(offsets) || !al4(perm) || !al4(inv)) return MOE_EINVAL;
   if (workspace_bytes < moe_permute_workspace_bytes(T, E, k) ||
       ((uintptr_t)workspace % kAlign))
     return MOE_EWORKSPACE;
@@ -299,6 +308,10 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
     return MOE_EINVAL;
   if (T == 0) return MOE_OK;
   if (!x || !Wg || !W1 || !W3 || !W2 || !y || !workspace || x == y) return MOE_EINVAL;
+  if (!al16(x) || !al16(Wg) || !al16(W1) || !al16(W3) || !al16(W2) || !al16(Ws1) ||
+      !al16(Ws3) || !al16(Ws2) || !al16(y) || !al4(bias))
+    return MOE_EINVAL;
+  if (f8 && (!al4(f8->s1) || !al4(f8->s3) || !al4(f8->s2))) return MOE_EINVAL;
   const Layout L = layout(T, d, d_ff, E, k, d_ff_shared, dtype);
   if (workspace_bytes < L.total || ((uintptr_t)workspace % kAlign)) return MOE_EWORKSPACE;
   int st = device_ok();

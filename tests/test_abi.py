@@ -106,6 +106,21 @@ def test_argument_errors_before_launch(L):
     assert L.moe_forward(*args) == -1
     # permute: too-small workspace
     assert L.moe_permute(fake, 4, 8, 2, fake, fake, fake, fake, vp(0x100000), 8, None) == -3
+    # misaligned tensors (16 bytes for x, weights and y; 4 for fp32 / int32 arrays)
+    for i in (0, 1, 3, 4, 5, 18):
+        args = [fake, fake, None, fake, fake, fake, None, None, None, 0, 4, 8, 2, 64, 64, 1,
+                vp(0x100000), 1 << 40, vp(0x2000), None]
+        args[i] = vp(args[i].value + 8)
+        assert L.moe_forward(*args) == -1, i
+    args = [fake, fake, vp(0x3002), fake, fake, fake, None, None, None, 0, 4, 8, 2, 64, 64, 1,
+            vp(0x100000), 1 << 40, vp(0x2000), None]
+    assert L.moe_forward(*args) == -1  # bias
+    assert L.moe_route(vp(0x1008), fake, None, 4, 64, 8, 2, 1, fake, fake, None, fake, big,
+                       None) == -1
+    assert L.moe_route(fake, fake, None, 4, 64, 8, 2, 1, vp(0x1002), fake, None, fake, big,
+                       None) == -1
+    assert L.moe_permute(vp(0x1002), 4, 8, 2, fake, fake, fake, fake, vp(0x100000), 1 << 30,
+                         None) == -1
 
 
 def test_variant_entry_points_check_arguments(L):
