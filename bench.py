@@ -36,7 +36,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="mixtral_prefill_T8192")
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -124,8 +124,16 @@ def run_workload(cfg, host, dev, steps, warmup, flush_mb=0, graph=False):
     wall = time.perf_counter() - w0
     if flush is None:
         ms = t_start.elapsed_time(t_end) / steps
-    else:
-        ms = float(np.mean([a.elapsed_time(b_) for a, b_ in step_ev]))
+        # the same steps again, each between events of its own (median and
+        # fastest step; ms_per_step above keeps the events out of its region)
+        for a, b_ in step_ev:
+            a.record()
+            layer(x, y)
+            b_.record()
+        torch.cuda.synchronize()
+    per_step = [a.elapsed_time(b_) for a, b_ in step_ev]
+    if flush is not None:
+        ms = float(np.mean(per_step))
     # pass 2: stage breakdown
     for i in range(steps):
         if flush is not None:
@@ -137,7 +145,9 @@ def run_workload(cfg, host, dev, steps, warmup, flush_mb=0, graph=False):
         for s in range(len(moe.STAGES)):
             stage[s] += row[s].elapsed_time(row[s + 1])
     stage /= steps
-    out = dict(ms=ms, wall_s=wall, stage_ms=stage, counts=layer.intermediates(T)["counts"].cpu().numpy())
+    out = dict(ms=ms, wall_s=wall, stage_ms=stage, counts=layer.intermediates(T)["counts"].cpu().numpy(),
+               step_ms={"median": round(float(np.median(per_step)), 4),
+                        "min": round(float(np.min(per_step)), 4)})
     if graph:
         # one forward captured in a HIP graph, replayed; per-replay time between events
         g = torch.cuda.CUDAGraph()
@@ -345,7 +355,7 @@ def main():
                      tokens_per_s=round(c2.T / (ms2 * 1e-3), 1),
                      stage_ms={s: round(float(v), 4) for s, v in zip(moe.STAGES,
                                                                       r2["stage_ms"])},
-                     roofline=rl2, layer=lf2, mall_flushed=bool(flush))
+                     step_ms=r2["step_ms"], roofline=rl2, layer=lf2, mall_flushed=bool(flush))
             if "graph_ms" in r2:
                 gms = r2["graph_ms"]
                 e["graph_replay"] = dict(
@@ -389,7 +399,7 @@ def main():
                      tokens_per_s=round(c2.T / (ms2 * 1e-3), 1),
                      stage_ms={s_: round(float(v), 4) for s_, v in zip(moe.STAGES,
                                                                         r2["stage_ms"])},
-                     roofline=rl2, layer=lf2, mall_flushed=False)
+                     step_ms=r2["step_ms"], roofline=rl2, layer=lf2, mall_flushed=False)
             log(f"{name}: {ms2:.4f} ms/step, {e['tokens_per_s']} tokens/s, "
                 f"layer mfma {lf2['mfma_frac']} hbm {lf2['hbm_frac']}")
             extra.append(e)
@@ -444,6 +454,7 @@ def main():
                    "global_batch": cfg.T, "parallelism": "single GPU"},
         "roofline": rl,
         "layer_roofline": layer_fr,
+        "step_ms": res["step_ms"],
         "stage_ms": stage,
         "expert_counts": {"min": int(counts.min()), "max": int(counts.max()),
                           "mean": float(counts.mean())},
@@ -452,7 +463,8 @@ def main():
         "variants": variants,
         "wall_s_timed": round(res["wall_s"], 3),
         "timing": "HIP events on the stream the kernels run on: ms_per_step over back-to-back "
-                  "moe_forward calls; stage and kernel times from a second pass through "
+                  "moe_forward calls; step_ms (median, fastest) from the same steps again, "
+                  "each between events of its own; stage and kernel times from a pass through "
                   "moe_forward_timed (events at every stage boundary)",
     }
     print(json.dumps(out), flush=True)
