@@ -65,7 +65,7 @@ def algorithmic(cfg, counts):
                 layer_bytes=layer_bytes, experts_hit=hit)
 
 
-def run_workload(cfg, host, dev, steps, warmup, flush_mb=0, graph=False):
+def run_workload(cfg, host, dev, steps, warmup, flush_mb=0, graph=False, min_warm_s=0.0):
     """Time `steps` layer forwards.
 
     Pass 1 (the timed region for ms_per_step): back-to-back moe_forward calls
@@ -79,7 +79,9 @@ def run_workload(cfg, host, dev, steps, warmup, flush_mb=0, graph=False):
     run on; each kernel's duration comes from there.  The extra event records
     cost a few microseconds each, which is why they stay out of pass 1.
     With graph=True, one forward is also captured in a HIP graph and replayed
-    (reported separately).
+    (reported separately).  min_warm_s: warm-up continues past `warmup` steps
+    until that much time has passed (the clocks settle after the host-side
+    set-up of a workload).
     """
     import numpy as np
     import torch
@@ -104,8 +106,14 @@ def run_workload(cfg, host, dev, steps, warmup, flush_mb=0, graph=False):
     for row in events:
         for e in row:
             e.record()
-    for _ in range(warmup):
+    n_warm, w_start = 0, time.perf_counter()
+    while n_warm < warmup or time.perf_counter() - w_start < min_warm_s:
+        if flush is not None:
+            flush.sum()
         layer(x, y)
+        n_warm += 1
+        if n_warm % 8 == 0:
+            torch.cuda.synchronize()  # keep the host clock in step with the device
     torch.cuda.synchronize()
     # pass 1: step time
     t_start, t_end = ev(), ev()
@@ -348,7 +356,7 @@ def main():
             if name == cfg.name:
                 continue
             c2 = CONFIGS[name]
-            r2 = run_workload(c2, host, dev, steps, 2, flush_mb=flush, graph=bool(flush))
+            r2 = run_workload(c2, host, dev, steps, 2, flush_mb=flush, graph=bool(flush), min_warm_s=0.25)
             rl2, lf2 = roofline_for(c2, r2)
             ms2 = r2["ms"]
             e = dict(workload=name, T=c2.T, ms_per_step=round(ms2, 4),
@@ -392,7 +400,7 @@ def main():
         del fhost
         for name in ("fine_shared_T512", "fine_shared_T8192"):
             c2 = CONFIGS[name]
-            r2 = run_workload(c2, None, fdev, 5, 2)
+            r2 = run_workload(c2, None, fdev, 5, 2, min_warm_s=0.25)
             rl2, lf2 = roofline_for(c2, r2)
             ms2 = r2["ms"]
             e = dict(workload=name, T=c2.T, ms_per_step=round(ms2, 4),
