@@ -8,7 +8,7 @@
 // scale[e] = amax_e / 448 rounded to fp32 (1 for an all-zero expert), amax_e
 // the largest |w| of expert e; q = the nearest E4M3 value of w / scale[e]
 // (quotient in fp64, ties to the even mantissa, magnitudes above 448 give
-// 448).  The dequantised weight is scale[e] * decode(q).  Four launches: clear
+// 448; rounded by integer arithmetic on the quotient's bits).  The dequantised weight is scale[e] * decode(q).  Four launches: clear
 // the per-expert maxima, reduce them (atomic max of non-negative float bits,
 // which is order independent), turn them into scales, encode.
 #include <cmath>
@@ -31,25 +31,29 @@ __device__ __forceinline__ float load_w<bf16_t>(const bf16_t *p, size_t i) {
   return bf16_to_f32(p[i]);
 }
 
-// Nearest E4M3 code of v (fp64 throughout: the steps are exact but the
-// rounding of the mantissa, which rint does half to even).
+// Nearest E4M3 code of v by integer rounding of its fp64 bit pattern.  The
+// significand S (53 bits with the hidden one) times 2^(e - 52) is |v|; the
+// code's quantum is 2^(e - 3) for e >= -6 and 2^-9 below (the subnormal
+// step), so |v| / quantum = S / 2^sh with sh = 49 (normal range) or
+// 43 - e.  The quotient r is rounded half to even from the shifted-out bits;
+// then code = 8 * (e + 6) + r in the normal range (r = 16 carries into the
+// next exponent by itself) and code = r below it (r = 8 is the smallest
+// normal, 0x08).  Codes above 0x7E (448) saturate to 0x7E.
 __device__ __forceinline__ uint8_t fp8_e4m3_encode(double v) {
-  const uint8_t sign = signbit(v) ? 0x80 : 0;
-  const double a = fabs(v);
-  if (a >= 448.0) return sign | 0x7E;
-  if (a < 0.015625) {  // below 2^-6: multiples of 2^-9 (8 of them is the smallest normal)
-    return sign | (uint8_t)rint(a * 512.0);
-  }
-  int ex;
-  frexp(a, &ex);
-  int e = ex - 1;  // a = (1 + x) * 2^e
-  double m = rint((ldexp(a, -e) - 1.0) * 8.0);
-  if (m == 8.0) {
-    m = 0.0;
-    e += 1;
-  }
-  if (e + 7 > 15 || (e + 7 == 15 && m > 6.0)) return sign | 0x7E;
-  return sign | (uint8_t)(((e + 7) << 3) | (int)m);
+  const uint64_t bits = (uint64_t)__double_as_longlong(v);
+  const uint8_t sign = (uint8_t)((bits >> 56) & 0x80);
+  const int bexp = (int)((bits >> 52) & 0x7FF);
+  if (bexp == 0) return sign;  // zero or an fp64 subnormal (far below 2^-10)
+  const int e = bexp - 1023;
+  if (e > 8) return sign | 0x7E;
+  const uint64_t S = (bits & ((1ull << 52) - 1)) | (1ull << 52);
+  const int sh = e >= -6 ? 49 : 43 - e;
+  if (sh > 53) return sign;  // below 2^-10: rounds to zero (2^-10 itself ties to 0)
+  uint64_t r = S >> sh;
+  const uint64_t rem = S & ((1ull << sh) - 1), half = 1ull << (sh - 1);
+  if (rem > half || (rem == half && (r & 1))) ++r;
+  const uint64_t code = (e >= -6 ? (uint64_t)(8 * (e + 6)) : 0ull) + r;
+  return sign | (uint8_t)(code > 0x7E ? 0x7E : code);
 }
 
 __global__ void fp8_clear_kernel(float *__restrict__ amax, int E) {

@@ -102,6 +102,38 @@ def _p(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _same(t, ref, shape, name):
+    """t must have `shape`, ref's dtype and ref's device (MoEError otherwise)."""
+    if tuple(t.shape) != tuple(shape):
+        raise MoEError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != ref.dtype:
+        raise MoEError(f"{name}: dtype {t.dtype}, expected {ref.dtype}")
+    if t.device != ref.device:
+        raise MoEError(f"{name}: on {t.device}, expected {ref.device}")
+
+
+def _check_bias(bias, E, ref):
+    if bias is None:
+        return
+    if tuple(bias.shape) != (E,) or bias.dtype != torch.float32:
+        raise MoEError(f"bias: expected fp32 [{E}], got {bias.dtype} {tuple(bias.shape)}")
+    if bias.device != ref.device:
+        raise MoEError(f"bias: on {bias.device}, expected {ref.device}")
+
+
+def _check_tokens(x, y, d, ref):
+    """x [..., d] (and y of x's shape) with ref's dtype and device."""
+    if x.dim() < 1 or x.shape[-1] != d:
+        raise MoEError(f"x: last dimension {tuple(x.shape)[-1:]} , expected {d}")
+    _same(x, ref, x.shape, "x")
+    if x.device.type != "cuda":
+        raise MoEError(f"x: on {x.device}; the layer runs on a HIP device")
+    if y is not None:
+        _same(y, ref, x.shape, "y")
+        if y.data_ptr() == x.data_ptr():
+            raise MoEError("y may not alias x")
+
+
 def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
@@ -135,8 +167,14 @@ def capacity(T: int, k: int, capacity_factor: float = 1.2) -> int:
 def route(x: torch.Tensor, Wg: torch.Tensor, k: int, bias: torch.Tensor | None = None,
           gate_mode: int = GATE_SOFTMAX_TOPK):
     """(idx [T][k] int32, gate [T][k] fp32, logits [T][E] fp32)."""
+    if x.dim() != 2 or Wg.dim() != 2:
+        raise MoEError("route: x [T][d] and Wg [E][d]")
     T, d = x.shape
     E = Wg.shape[0]
+    _same(Wg, x, (E, d), "Wg")
+    _check_bias(bias, E, x)
+    if x.device.type != "cuda":
+        raise MoEError(f"x: on {x.device}; the router runs on a HIP device")
     idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
     gate = torch.empty((T, k), dtype=torch.float32, device=x.device)
     logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
@@ -194,10 +232,26 @@ class MoELayer:
         self.options = _Options(int(gate_mode), int(activation), int(capacity))
         self._default = (gate_mode == GATE_SOFTMAX_TOPK and activation == ACT_SWIGLU
                          and capacity < 0)
+        if W1.dim() != 3:
+            raise MoEError("W1: expected [E][d_ff][d]")
         self.E, self.d_ff, self.d = W1.shape
-        self.shared = shared
-        self.d_ff_shared = shared[0].shape[0] if shared is not None else 0
         self.dtype = _dt(W1)
+        E, d, d_ff = self.E, self.d, self.d_ff
+        _same(W3, W1, (E, d_ff, d), "W3")
+        _same(W2, W1, (E, d, d_ff), "W2")
+        _same(Wg, W1, (E, d), "Wg")
+        _check_bias(bias, E, W1)
+        self.shared = shared
+        self.d_ff_shared = 0
+        if shared is not None:
+            Ws1, Ws3, Ws2 = shared
+            if Ws1.dim() != 2:
+                raise MoEError("Ws1: expected [d_ff_shared][d]")
+            dffs = Ws1.shape[0]
+            _same(Ws1, W1, (dffs, d), "Ws1")
+            _same(Ws3, W1, (dffs, d), "Ws3")
+            _same(Ws2, W1, (d, dffs), "Ws2")
+            self.d_ff_shared = dffs
         self._ws = None
         self._ws_T = -1
 
@@ -208,6 +262,7 @@ class MoELayer:
         return self._ws, n
 
     def __call__(self, x: torch.Tensor, y: torch.Tensor | None = None) -> torch.Tensor:
+        _check_tokens(x, y, self.d, self.W1)
         shape = x.shape
         x2 = x.reshape(-1, self.d)  # batch dims flattened into tokens
         T = x2.shape[0]
@@ -234,6 +289,7 @@ class MoELayer:
         (the method's defaults only)."""
         if not self._default:
             raise MoEError("stage timing covers the default variant only")
+        _check_tokens(x, y, self.d, self.W1)
         T = x.shape[0]
         ws, n = self.workspace(T)
         Ws1, Ws3, Ws2 = self.shared if self.shared is not None else (None, None, None)
@@ -290,7 +346,14 @@ class MoELayerFP8:
     def __init__(self, Wg, W1, W3, W2, k, bias=None, gate_mode=GATE_SOFTMAX_TOPK,
                  activation=ACT_SWIGLU, capacity=-1):
         self.Wg, self.k, self.bias = Wg, k, bias
+        if W1.dim() != 3 or W1.dtype != torch.bfloat16:
+            raise MoEError("W1: expected bf16 [E][d_ff][d]")
         self.E, self.d_ff, self.d = W1.shape
+        E, d, d_ff = self.E, self.d, self.d_ff
+        _same(W3, W1, (E, d_ff, d), "W3")
+        _same(W2, W1, (E, d, d_ff), "W2")
+        _same(Wg, W1, (E, d), "Wg")
+        _check_bias(bias, E, W1)
         self.W1q, self.s1 = quantize_fp8(W1)
         self.W3q, self.s3 = quantize_fp8(W3)
         self.W2q, self.s2 = quantize_fp8(W2)
@@ -304,6 +367,9 @@ class MoELayerFP8:
         return self._ws, n
 
     def __call__(self, x: torch.Tensor, y: torch.Tensor | None = None) -> torch.Tensor:
+        if x.dim() != 2:
+            raise MoEError("x: expected [T][d]")
+        _check_tokens(x, y, self.d, self.Wg)
         T = x.shape[0]
         if y is None:
             y = torch.empty_like(x)

@@ -157,3 +157,61 @@ def test_variant_entry_points_check_arguments(L):
     # permute_ex: too-small workspace is still caught
     assert L.moe_permute_ex(fake, 4, 8, 2, 3, fake, fake, fake, fake, vp(0x100000), 8,
                             None) == -3
+
+
+def _layer_tensors(dtype=None, E=4, d=64, d_ff=128):
+    import torch
+    dtype = dtype or torch.bfloat16
+    return dict(Wg=torch.zeros(E, d, dtype=dtype), W1=torch.zeros(E, d_ff, d, dtype=dtype),
+                W3=torch.zeros(E, d_ff, d, dtype=dtype), W2=torch.zeros(E, d, d_ff, dtype=dtype))
+
+
+def test_binding_rejects_mismatched_layers():
+    """The binding checks shapes, dtypes and devices before calling the
+    library, whose one dtype covers every tensor of a call."""
+    import torch
+
+    from sparse_mixture_experts_permute_amd import moe
+    t = _layer_tensors()
+    moe.MoELayer(t["Wg"], t["W1"], t["W3"], t["W2"], 2)  # consistent: accepted
+    bad = [
+        dict(W3=torch.zeros(4, 128, 64, dtype=torch.float32)),  # dtype differs
+        dict(W3=torch.zeros(4, 64, 128, dtype=torch.bfloat16)),  # W3 not like W1
+        dict(W2=torch.zeros(4, 128, 64, dtype=torch.bfloat16)),  # W2 transposed
+        dict(Wg=torch.zeros(3, 64, dtype=torch.bfloat16)),  # fewer router rows than E
+        dict(Wg=torch.zeros(4, 64, dtype=torch.float32)),  # router dtype
+    ]
+    for change in bad:
+        u = dict(t, **change)
+        with pytest.raises(moe.MoEError):
+            moe.MoELayer(u["Wg"], u["W1"], u["W3"], u["W2"], 2)
+    with pytest.raises(moe.MoEError):  # bias must be fp32 [E]
+        moe.MoELayer(t["Wg"], t["W1"], t["W3"], t["W2"], 2, bias=torch.zeros(4, dtype=torch.bfloat16))
+    with pytest.raises(moe.MoEError):
+        moe.MoELayer(t["Wg"], t["W1"], t["W3"], t["W2"], 2, bias=torch.zeros(5))
+    sh = (torch.zeros(32, 64, dtype=torch.bfloat16), torch.zeros(32, 64, dtype=torch.bfloat16),
+          torch.zeros(64, 32, dtype=torch.bfloat16))
+    moe.MoELayer(t["Wg"], t["W1"], t["W3"], t["W2"], 2, shared=sh)
+    with pytest.raises(moe.MoEError):  # Ws2 must be [d][d_ff_shared]
+        moe.MoELayer(t["Wg"], t["W1"], t["W3"], t["W2"], 2, shared=(sh[0], sh[1], sh[0]))
+
+
+def test_binding_rejects_mismatched_tokens():
+    import torch
+
+    from sparse_mixture_experts_permute_amd import moe
+    t = _layer_tensors()
+    layer = moe.MoELayer(t["Wg"], t["W1"], t["W3"], t["W2"], 2)
+    for x, y in [(torch.zeros(8, 64, dtype=torch.float32), None),  # x dtype differs
+                 (torch.zeros(8, 32, dtype=torch.bfloat16), None),  # x width is not d
+                 (torch.zeros(8, 64, dtype=torch.bfloat16),
+                  torch.zeros(8, 64, dtype=torch.float32)),  # y dtype differs
+                 (torch.zeros(8, 64, dtype=torch.bfloat16),
+                  torch.zeros(4, 64, dtype=torch.bfloat16)),  # y too short
+                 (torch.zeros(8, 64, dtype=torch.bfloat16), None)]:  # host tensors
+        with pytest.raises(moe.MoEError):
+            layer(x, y)
+    with pytest.raises(moe.MoEError):  # router dtype differs from x
+        moe.route(torch.zeros(8, 64, dtype=torch.bfloat16), torch.zeros(4, 64), 2)
+    with pytest.raises(moe.MoEError):
+        moe.route(torch.zeros(8, 64), torch.zeros(4, 32), 2)
