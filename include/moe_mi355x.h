@@ -64,7 +64,8 @@ enum {
     MOE_EDTYPE = -2,     /* dtype not MOE_F32 / MOE_BF16 */
     MOE_EWORKSPACE = -3, /* workspace too small or misaligned (needs 256 B) */
     MOE_ELAUNCH = -4,    /* the HIP runtime refused a kernel launch */
-    MOE_EDEVICE = -5     /* current device is not a gfx950 GPU */
+    MOE_EDEVICE = -5,    /* current device is not a gfx950 GPU */
+    MOE_ESCRATCH = -6    /* moe_forward_noalloc: the shape needs more than its static scratch */
 };
 
 /* Bytes of scratch moe_route needs for (T, d, E, dtype); 0 on invalid arguments. */
@@ -251,6 +252,28 @@ int moe_forward_fp8(const void *x, const void *Wg, const float *bias, const uint
                     const float *s2, int T, int E, int k, int d, int d_ff,
                     const moe_options *opt, void *workspace, size_t workspace_bytes, void *y,
                     void *stream);
+
+/* ------------------------------------------------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the layer
+ * with its scratch in a static device array of MOE_NOALLOC_SCRATCH_BYTES
+ * per GPU, which the library holds from its first use on a device until the
+ * process ends.  Same arguments and results as moe_forward, without the
+ * workspace; allocates and frees nothing.
+ *   Returns MOE_ESCRATCH when the shape needs more scratch than the array
+ *   holds, i.e. when moe_workspace_bytes for the same arguments exceeds
+ *   MOE_NOALLOC_SCRATCH_BYTES (128 MiB: the Mixtral-shaped layer up to about
+ *   1000 tokens, its decode steps, every 512-wide layer of 512 tokens).
+ *   Every call on one GPU uses that GPU's one array: calls that overlap on a
+ *   GPU (on different streams, or from different threads) race, and the
+ *   intermediates of moe_workspace_offsets are not exposed.  Each call clears
+ *   what its kernels need cleared; nothing depends on a previous call.
+ * ------------------------------------------------------------------------ */
+#define MOE_NOALLOC_SCRATCH_BYTES (128u << 20)
+int moe_forward_noalloc(const void *x, const void *Wg, const float *bias, const void *W1,
+                        const void *W3, const void *W2, const void *Ws1, const void *Ws3,
+                        const void *Ws2, int d_ff_shared, int T, int E, int k, int d, int d_ff,
+                        int dtype, void *y, void *stream);
 
 /* Static text for a status code. */
 const char *moe_strerror(int status);

@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "../../include/moe_mi355x.h"
 #include "kernels.h"
@@ -175,6 +176,8 @@ const char *moe_strerror(int status) {
     case MOE_EWORKSPACE: return "workspace too small or not 256-byte aligned";
     case MOE_ELAUNCH: return "kernel launch failed";
     case MOE_EDEVICE: return "current device is not a gfx950 GPU";
+    case MOE_ESCRATCH:
+      return "the layer needs more scratch than moe_forward_noalloc's static array holds";
     default: return "unknown status";
   }
 }
@@ -575,6 +578,53 @@ int moe_forward_fp8(const void *x, const void *Wg, const float *bias, const uint
   const Fp8Experts f8{W1q, W3q, W2q, s1, s3, s2};
   return forward_impl(x, Wg, bias, W1q, W3q, W2q, nullptr, nullptr, nullptr, 0, T, E, k, d, d_ff,
                       MOE_BF16, opt, workspace, workspace_bytes, y, stream, nullptr, &f8);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of moe_forward_noalloc: one array per GPU, allocated with the code
+// object when the library is loaded on that device and held until the process
+// ends.  Host code uses the per-device address from hipGetSymbolAddress, never
+// the array's name (a host-side stand-in, not a device address).
+constexpr size_t kNoAllocBytes = (size_t)MOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
+// scratch's address on the current device (NULL if it cannot be had)
+void *noalloc_scratch() {
+  static std::mutex mu;
+  static void *addr[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> g(mu);
+  if (!addr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    addr[dev] = p;
+  }
+  return addr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_forward_noalloc(const void *x, const void *Wg, const float *bias, const void *W1,
+                        const void *W3, const void *W2, const void *Ws1, const void *Ws3,
+                        const void *Ws2, int d_ff_shared, int T, int E, int k, int d, int d_ff,
+                        int dtype, void *y, void *stream) {
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_EDTYPE;
+  if (!dims_ok(T, d, d_ff, E, k, d_ff_shared)) return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  const size_t need = layout(T, d, d_ff, E, k, d_ff_shared, dtype).total;
+  if (need > kNoAllocBytes) return MOE_ESCRATCH;
+  int st = device_ok();
+  if (st != MOE_OK) return st;
+  void *ws = noalloc_scratch();
+  if (!ws) return MOE_ELAUNCH;
+  return forward_impl(x, Wg, bias, W1, W3, W2, Ws1, Ws3, Ws2, d_ff_shared, T, E, k, d, d_ff,
+                      dtype, nullptr, ws, kNoAllocBytes, y, stream, nullptr);
 }
 
 }  // extern "C"

@@ -77,6 +77,9 @@ def lib():
         L.moe_forward_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i,
                                       ctypes.POINTER(_Options), vp, sz, vp, vp]
         L.moe_forward_fp8.restype = i
+        L.moe_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i,
+                                          i, vp, vp]
+        L.moe_forward_noalloc.restype = i
         _lib = L
     return _lib
 

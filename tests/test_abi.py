@@ -215,3 +215,15 @@ def test_binding_rejects_mismatched_tokens():
         moe.route(torch.zeros(8, 64, dtype=torch.bfloat16), torch.zeros(4, 64), 2)
     with pytest.raises(moe.MoEError):
         moe.route(torch.zeros(8, 64), torch.zeros(4, 32), 2)
+
+
+def test_noalloc_rejects_before_launch(L):
+    """moe_forward_noalloc checks its arguments, and that the shape fits its
+    static scratch, before it touches a device."""
+    fake = ctypes.c_void_p(0x1000)
+    args = [fake, fake, None, fake, fake, fake, None, None, None, 0]
+    # 1.1 GB of scratch for the Mixtral-shaped layer at 8192 tokens: too large
+    assert L.moe_forward_noalloc(*args, 8192, 8, 2, 4096, 14336, 1, fake, None) == -6
+    assert L.moe_forward_noalloc(*args, 8, 8, 9, 4096, 14336, 1, fake, None) == -1  # k > E
+    assert L.moe_forward_noalloc(*args, 8, 8, 2, 4096, 14336, 5, fake, None) == -2  # dtype
+    assert b"static" in L.moe_strerror(-6)
