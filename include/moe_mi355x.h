@@ -22,9 +22,19 @@
  * flat pair ids p = t*k + j by expert.
  *
  * Conventions for every call
- *  - All tensors are row-major and dense.  Every weight is held as a Linear
- *    weight [out][in]:  Wg [E][d], W1 and W3 [E][d_ff][d], W2 [E][d][d_ff],
- *    shared Ws1 and Ws3 [d_ff_shared][d], Ws2 [d][d_ff_shared].
+ *  - All tensors are row-major and dense.  The router is Wg [E][d] (scores
+ *    x Wg^T).  Expert weights come in one of two layouts (moe_options
+ *    weight_layout):
+ *      MOE_LAYOUT_OUT_IN (default): Linear weights [out][in]: W1 and W3
+ *        [E][d_ff][d], W2 [E][d][d_ff], shared Ws1 and Ws3 [d_ff_shared][d],
+ *        Ws2 [d][d_ff_shared] ("Chapter 10 MoE" and the "Mixtral and MoE
+ *        architecture" listing hold nn.Linear weights);
+ *      MOE_LAYOUT_IN_OUT: [in][out], the layer multiplies x W: W1 and W3
+ *        [E][d][d_ff], W2 [E][d_ff][d], shared Ws1 and Ws3 [d][d_ff_shared],
+ *        Ws2 [d_ff_shared][d] (the numpy forward of "Trillion-parameter MoE
+ *        ... 7 expert configs measured" multiplies x @ W1[e] and h @ W2[e]).
+ *    Both give the same results up to the order of fp32 additions (the tiled
+ *    kernels: the same bits).
  *  - Every pointer argument is a DEVICE pointer owned by the caller; the
  *    library never allocates, frees or retains memory, and never synchronises
  *    the host with the device.
@@ -136,13 +146,15 @@ int moe_forward(const void *x, const void *Wg, const float *bias, const void *W1
  * projection streams the weights and there is no shared expert, the combine
  * rides in that kernel: [5], [6] and [7] then all follow it.  Same results
  * and errors as moe_forward; MOE_EINVAL if `events` or any of its handles is
- * NULL. */
+ * NULL.  `opt`: the variants and weight layout of moe_forward_ex (NULL: the
+ * defaults). */
 #define MOE_NSTAGE_EVENTS 8
+struct moe_options_s; /* moe_options, defined below */
 int moe_forward_timed(const void *x, const void *Wg, const float *bias, const void *W1,
                       const void *W3, const void *W2, const void *Ws1, const void *Ws3,
                       const void *Ws2, int d_ff_shared, int T, int E, int k, int d, int d_ff,
-                      int dtype, void *workspace, size_t workspace_bytes, void *y, void *stream,
-                      void *const *events);
+                      int dtype, const struct moe_options_s *opt, void *workspace,
+                      size_t workspace_bytes, void *y, void *stream, void *const *events);
 
 /* ------------------------------------------------------------------------
  * Variants the pages print beside the method (all optional; the calls above
@@ -172,6 +184,8 @@ int moe_forward_timed(const void *x, const void *Wg, const float *bias, const vo
  *              MOE_ACT_GLU_SIGMOID    W2( sigmoid(W1 x) * (W3 x) ): the same
  *                                     numpy function's gated projection (its
  *                                     fused [a | g] weight is [W3 | W1] here)
+ *   weight_layout  MOE_LAYOUT_OUT_IN or MOE_LAYOUT_IN_OUT (see the
+ *              conventions above); MOE_EINVAL otherwise
  *   capacity   at most `capacity` pairs per expert ("Mistral 8x7B SMoE
  *              architecture deep dive", section 2.4); an expert keeps its
  *              first pairs in pair order t*k+j (the page does not say which
@@ -186,10 +200,13 @@ enum {
 };
 enum { MOE_ACT_SWIGLU = 0, MOE_ACT_GLU_SIGMOID = 1 };
 
-typedef struct {
-    int gate_mode;  /* MOE_GATE_* */
-    int activation; /* MOE_ACT_* */
-    int capacity;   /* pairs per expert; < 0: no limit */
+enum { MOE_LAYOUT_OUT_IN = 0, MOE_LAYOUT_IN_OUT = 1 };
+
+typedef struct moe_options_s {
+    int gate_mode;     /* MOE_GATE_* */
+    int activation;    /* MOE_ACT_* */
+    int capacity;      /* pairs per expert; < 0: no limit */
+    int weight_layout; /* MOE_LAYOUT_*: expert weights [out][in] (default) or [in][out] */
 } moe_options;
 
 /* The page's capacity for a batch of T tokens: min(k*T, floor(cf*T))
@@ -210,6 +227,15 @@ int moe_route_ex(const void *x, const void *Wg, const float *bias, int T, int d,
 int moe_permute_ex(const int32_t *idx, int T, int E, int k, int capacity, int32_t *counts,
                    int32_t *offsets, int32_t *perm, int32_t *inv, void *workspace,
                    size_t workspace_bytes, void *stream);
+
+/* moe_forward with expert weights in the [in][out] layout (MOE_LAYOUT_IN_OUT):
+ * W1, W3 [E][d][d_ff], W2 [E][d_ff][d]; shared Ws1, Ws3 [d][d_ff_shared], Ws2
+ * [d_ff_shared][d] ("Trillion-parameter MoE ... 7 expert configs measured",
+ * the numpy forward: x @ W1[e], h @ W2[e]).  Everything else as moe_forward. */
+int moe_forward_inout(const void *x, const void *Wg, const float *bias, const void *W1,
+                      const void *W3, const void *W2, const void *Ws1, const void *Ws3,
+                      const void *Ws2, int d_ff_shared, int T, int E, int k, int d, int d_ff,
+                      int dtype, void *workspace, size_t workspace_bytes, void *y, void *stream);
 
 /* moe_forward with the variants in `opt` (NULL: the defaults).  Same
  * workspace; its counts/offsets/perm/inv fields then follow moe_permute_ex. */

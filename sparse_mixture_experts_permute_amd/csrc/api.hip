@@ -301,7 +301,14 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
                  int dtype, const moe_options *opt, void *workspace, size_t workspace_bytes,
                  void *y, void *stream, void *const *events, const Fp8Experts *f8 = nullptr) {
   if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_EDTYPE;
-  const moe_options o = opt ? *opt : moe_options{MOE_GATE_SOFTMAX_TOPK, MOE_ACT_SWIGLU, -1};
+  const moe_options o =
+      opt ? *opt : moe_options{MOE_GATE_SOFTMAX_TOPK, MOE_ACT_SWIGLU, -1, MOE_LAYOUT_OUT_IN};
+  if (o.weight_layout != MOE_LAYOUT_OUT_IN && o.weight_layout != MOE_LAYOUT_IN_OUT)
+    return MOE_EINVAL;
+  // [in][out] weights: the tiled kernels read them through transposing LDS
+  // reads, few-token steps through the [K][N] weight-streaming kernel
+  const bool tb = o.weight_layout == MOE_LAYOUT_IN_OUT;
+  if (f8 && tb) return MOE_EINVAL;
   if (o.gate_mode < MOE_GATE_SOFTMAX_TOPK || o.gate_mode > MOE_GATE_ENTROPY) return MOE_EINVAL;
   if (o.gate_mode == MOE_GATE_ENTROPY && k < 2) return MOE_EINVAL;
   if (o.activation != MOE_ACT_SWIGLU && o.activation != MOE_ACT_GLU_SIGMOID) return MOE_EINVAL;
@@ -327,6 +334,14 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
       moe::gemm_plan(dtype, d, d_ff, d_ff_shared, ((long long)T * k + E - 1) / E);
   SkinnyPlan sk = skinny_plan(dtype, T, k, E, d, d_ff, d_ff_shared);
   if (f8) sk.routed = sk.gemv = true;  // FP8 experts: weight streaming, checked by the caller
+  if (tb) {
+    // [K][N] weights: vector-ALU streaming up to four tokens, tiles beyond
+    sk.gemv = sk.gemv && moe::gemv_t_ok(d_ff, d) && moe::gemv_t_ok(d, d_ff);
+    sk.routed = sk.gemv;
+    sk.gemv_shared = sk.gemv_shared && moe::gemv_t_ok(d_ff_shared, d) &&
+                     moe::gemv_t_ok(d, d_ff_shared);
+    sk.shared = sk.gemv_shared;
+  }
   const int ksplit = sk.routed ? 1 : down_splits(plan, T, k, E, d, d_ff);
   const size_t plane = (size_t)P * d;
   float *logits = at<float>(ws, L.off[F_LOGITS]);
@@ -352,10 +367,10 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
   const moe::FixScratch fx{fixc, fixp_bytes ? at<char>(ws, L.off[F_FIXP]) : nullptr, fixp_bytes};
   // single-token-scale batches without a shared expert: the down projection's
   // last workgroups also do the combine
-  const bool fused_combine = sk.gemv && !shared;
+  const bool fused_combine = sk.gemv && !shared && !tb;
   // a single token with a small router: the SwiGLU weight-streaming kernel
   // routes it itself (no score or top-k launches)
-  const bool route_fused = sk.gemv && moe::route_fused_ok(T, d, E, k);
+  const bool route_fused = sk.gemv && !tb && moe::route_fused_ok(T, d, E, k);
   const moe::DecodeRoute rt{Wg, bias, E, k, o.gate_mode,
                             o.capacity < 0 || o.capacity > P ? P : o.capacity,
                             plan.bm1, plan.bm2, logits, idx, gate, counts, offsets, perm, inv,
@@ -421,6 +436,8 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
              : f8 ? moe::launch_gemv_swiglu_fp8(T, o.activation, x, perm, k, f8->W1q, f8->W3q,
                                                 f8->s1, f8->s3, H, offsets, act, act + E, G,
                                                 d_ff, d, nact, s)
+             : tb ? moe::launch_gemv_t_swiglu(T, o.activation, x, perm, k, W1, W3, H, offsets,
+                                              act, act + E, G, d_ff, d, s)
              : sk.gemv ? moe::launch_gemv_swiglu(T, o.activation, x, perm, k, W1, W3, H, offsets,
                                                act, act + E, G, d_ff, d, nact, s)
                      : moe::launch_skinny_swiglu(sk.mb, o.activation, x, perm, k, W1, W3, H,
@@ -436,6 +453,7 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
              : fused_combine
                  ? moe::launch_gemv_down_combine(T, H, W2, Yp, offsets, act, act + E, G, d, d_ff,
                                                  nact, inv, gate, T, k, y, fixc, s)
+             : tb ? moe::launch_gemv_t_down(T, H, W2, Yp, offsets, act, act + E, G, d, d_ff, s)
              : sk.gemv ? moe::launch_gemv_down(T, H, W2, Yp, offsets, act, act + E, G, d, d_ff,
                                                nact, s)
                        : moe::launch_skinny_down(sk.mb, H, W2, Yp, offsets, act, act + E, E, d,
@@ -450,44 +468,53 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
     if (gather_fused && split) {
       if ((e = moe::launch_gemm_swiglu(dtype, true, 256, o.activation, x, W1, W3, H, offsets, mt0,
                                        E, d_ff, d, P / 256 + E, s, mid, perm, k,
-                                       (long long)T * d * 2)) ||
+                                       (long long)T * d * 2, tb)) ||
           (e = moe::launch_gemm_swiglu(dtype, true, 64, o.activation, x, W1, W3, H, mid, mt1, E,
                                        d_ff, d, moe::SPLIT_REM_TILES * E, s, offsets + 1, perm, k,
-                                       (long long)T * d * 2)))
+                                       (long long)T * d * 2, tb)))
         goto fail;
     } else if (gather_fused) {
       if ((e = moe::launch_gemm_swiglu(dtype, true, 64, o.activation, x, W1, W3, H, offsets, mt0,
                                        E, d_ff, d, (P + 63) / 64 + E, s, nullptr, perm, k,
-                                       (long long)T * d * 2)))
+                                       (long long)T * d * 2, tb)))
         goto fail;
     } else if (split) {
       if ((e = moe::launch_gemm_swiglu(dtype, true, 256, o.activation, Xp, W1, W3, H, offsets, mt0,
-                                       E, d_ff, d, P / 256 + E, s, mid)) ||
+                                       E, d_ff, d, P / 256 + E, s, mid, nullptr, 1, 0, tb)) ||
           (e = moe::launch_gemm_swiglu(dtype, true, 64, o.activation, Xp, W1, W3, H, mid, mt1, E,
-                                       d_ff, d, moe::SPLIT_REM_TILES * E, s, offsets + 1)))
+                                       d_ff, d, moe::SPLIT_REM_TILES * E, s, offsets + 1, nullptr,
+                                       1, 0, tb)))
         goto fail;
     } else if ((e = moe::launch_gemm_swiglu(dtype, plan.dl1, plan.bm1, o.activation, Xp, W1, W3,
                                             H, offsets, mt0, E, d_ff, d,
-                                            (P + plan.bm1 - 1) / plan.bm1 + E, s))) {
+                                            (P + plan.bm1 - 1) / plan.bm1 + E, s, nullptr, nullptr,
+                                            1, 0, tb))) {
       goto fail;
     }
     MOE_MARK(4);
     if (split) {
       if ((e = moe::launch_gemm_down(dtype, true, 256, H, W2, Yp, offsets, mt0, E, d, d_ff,
-                                     P / 256 + E, ksplit, plane, fx, s, mid, yp_bf16)) ||
+                                     P / 256 + E, ksplit, plane, fx, s, mid, yp_bf16, tb)) ||
           (e = moe::launch_gemm_down(dtype, true, 64, H, W2, Yp, mid, mt1, E, d, d_ff,
                                      moe::SPLIT_REM_TILES * E, ksplit, plane, fx, s, offsets + 1,
-                                     yp_bf16)))
+                                     yp_bf16, tb)))
         goto fail;
     } else if ((e = moe::launch_gemm_down(dtype, plan.dl2, plan.bm2, H, W2, Yp, offsets, mt1, E, d,
                                           d_ff, (P + plan.bm2 - 1) / plan.bm2 + E, ksplit, plane,
-                                          fx, s, nullptr, yp_bf16))) {
+                                          fx, s, nullptr, yp_bf16, tb))) {
       goto fail;
     }
     MOE_MARK(5);
   }
   if (shared) {
-    if (sk.gemv_shared) {
+    if (sk.gemv_shared && tb) {
+      if ((e = moe::launch_gemv_t_swiglu(T, o.activation, x, nullptr, 1, Ws1, Ws3, Hs, shseg,
+                                         shseg + 6, shseg + 7, 1, d_ff_shared, d, s)))
+        goto fail;
+      if ((e = moe::launch_gemv_t_down(T, Hs, Ws2, Ys, shseg, shseg + 6, shseg + 7, 1, d,
+                                       d_ff_shared, s)))
+        goto fail;
+    } else if (sk.gemv_shared) {
       if ((e = moe::launch_gemv_swiglu(T, o.activation, x, nullptr, 1, Ws1, Ws3, Hs, shseg,
                                        shseg + 6, shseg + 7, 1, d_ff_shared, d, 1, s)))
         goto fail;
@@ -504,10 +531,12 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
     } else {
       if ((e = moe::launch_gemm_swiglu(dtype, plan.dl1, plan.bm1, o.activation, x, Ws1, Ws3, Hs,
                                        shseg, shseg + 2, 1, d_ff_shared, d,
-                                       (T + plan.bm1 - 1) / plan.bm1, s)))
+                                       (T + plan.bm1 - 1) / plan.bm1, s, nullptr, nullptr, 1, 0,
+                                       tb)))
         goto fail;
       if ((e = moe::launch_gemm_down(dtype, plan.dl2, plan.bm2, Hs, Ws2, Ys, shseg, shseg + 4, 1, d,
-                                     d_ff_shared, (T + plan.bm2 - 1) / plan.bm2, 1, 0, fx, s)))
+                                     d_ff_shared, (T + plan.bm2 - 1) / plan.bm2, 1, 0, fx, s,
+                                     nullptr, false, tb)))
         goto fail;
     }
   }
@@ -544,16 +573,25 @@ int moe_forward_ex(const void *x, const void *Wg, const float *bias, const void 
                       dtype, opt, workspace, workspace_bytes, y, stream, nullptr);
 }
 
+int moe_forward_inout(const void *x, const void *Wg, const float *bias, const void *W1,
+                      const void *W3, const void *W2, const void *Ws1, const void *Ws3,
+                      const void *Ws2, int d_ff_shared, int T, int E, int k, int d, int d_ff,
+                      int dtype, void *workspace, size_t workspace_bytes, void *y, void *stream) {
+  const moe_options o{MOE_GATE_SOFTMAX_TOPK, MOE_ACT_SWIGLU, -1, MOE_LAYOUT_IN_OUT};
+  return forward_impl(x, Wg, bias, W1, W3, W2, Ws1, Ws3, Ws2, d_ff_shared, T, E, k, d, d_ff,
+                      dtype, &o, workspace, workspace_bytes, y, stream, nullptr);
+}
+
 int moe_forward_timed(const void *x, const void *Wg, const float *bias, const void *W1,
                       const void *W3, const void *W2, const void *Ws1, const void *Ws3,
                       const void *Ws2, int d_ff_shared, int T, int E, int k, int d, int d_ff,
-                      int dtype, void *workspace, size_t workspace_bytes, void *y, void *stream,
-                      void *const *events) {
+                      int dtype, const moe_options *opt, void *workspace,
+                      size_t workspace_bytes, void *y, void *stream, void *const *events) {
   if (!events) return MOE_EINVAL;
   for (int i = 0; i < MOE_NSTAGE_EVENTS; ++i)
     if (!events[i]) return MOE_EINVAL;
   return forward_impl(x, Wg, bias, W1, W3, W2, Ws1, Ws3, Ws2, d_ff_shared, T, E, k, d, d_ff,
-                      dtype, nullptr, workspace, workspace_bytes, y, stream, events);
+                      dtype, opt, workspace, workspace_bytes, y, stream, events);
 }
 
 int moe_quantize_fp8(const void *W, int E, long long n, int dtype, uint8_t *q, float *scale,

@@ -9,6 +9,7 @@ typedef uint16_t bf16_t;  // bf16 held as its bit pattern
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_v;
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_v;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_v;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_v;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_v;
 

@@ -144,7 +144,7 @@ __device__ __forceinline__ Split plan_split(int R, int W, int nk, int red10, int
   return sp;
 }
 
-template <typename T, int BM, int BNB, int WM, int WN, bool SWIGLU>
+template <typename T, int BM, int BNB, int WM, int WN, bool SWIGLU, bool TB = false>
 __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_kernel(
     const T *__restrict__ A, const T *__restrict__ B1, const T *__restrict__ B3,
     void *__restrict__ C, const int32_t *__restrict__ seg_off,
@@ -190,9 +190,30 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_kernel(
     dstA[i] = r * LDW + q;
   }
   const size_t bexp = (size_t)e * N * rowq;  // expert offset in uint4
+  // TB ([K][N] weights): chunk c holds VE consecutive columns of k-row c / (BNB
+  // / VE); it is stored transposed into the [column][K] LDS tile
+  constexpr int VE = 16 / ES;  // elements per 16-byte chunk
+  const size_t bstep = TB ? (size_t)BK * N / VE : (size_t)CPR;  // uint4 per K slice
 #pragma unroll
   for (int i = 0; i < B_CH; ++i) {
     int c = tid + i * GM_THREADS;
+    if constexpr (TB) {
+      const int kk = c / (BNB / VE), r = (c % (BNB / VE)) * VE;
+      const T *base;
+      int col;
+      if (SWIGLU) {
+        int rb = r / 32, wnb = rb / TN, j = rb % TN;
+        col = n0 + wnb * (TN / 2) * 32 + (j / 2) * 32 + (r % 32);
+        base = (j & 1) ? B3 : B1;
+      } else {
+        col = n0 + r;
+        base = B1;
+      }
+      col = min(col, N - VE);
+      srcB[i] = reinterpret_cast<const uint4 *>(base + ((size_t)e * K + kk) * N + col);
+      dstB[i] = (BM + r) * LDW * VE + kk;  // in elements
+      continue;
+    }
     int r = c / CPR, q = c % CPR;
     const T *base;
     int col;
@@ -224,13 +245,23 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_kernel(
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) ra[i] = srcA[i][ko];
 #pragma unroll
-    for (int i = 0; i < B_CH; ++i) rb[i] = srcB[i][ko];
+    for (int i = 0; i < B_CH; ++i) rb[i] = srcB[i][(size_t)kt * bstep];
   };
   auto lstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) lds[buf][dstA[i]] = ra[i];
 #pragma unroll
-    for (int i = 0; i < B_CH; ++i) lds[buf][dstB[i]] = rb[i];
+    for (int i = 0; i < B_CH; ++i) {
+      if constexpr (TB) {
+        T v[VE];
+        __builtin_memcpy(v, &rb[i], 16);
+        T *l = reinterpret_cast<T *>(lds[buf]);
+#pragma unroll
+        for (int u = 0; u < VE; ++u) l[dstB[i] + u * LDW * VE] = v[u];
+      } else {
+        lds[buf][dstB[i]] = rb[i];
+      }
+    }
   };
 
   gload(0);
@@ -413,7 +444,7 @@ __device__ __forceinline__ void dl_epilogue(const TA &ta, f32x16_v (&acc)[TM][TN
 // GATHER: A is the token matrix x (a_bytes bytes) and tile row s reads x row
 // gperm[s] / gk, so the grouped rows are never written out; each lane keeps
 // the byte offsets of its rows for the tile (one per A instruction).
-template <int BM, int BNB, bool SWIGLU, bool SPLIT, bool GATHER = false>
+template <int BM, int BNB, bool SWIGLU, bool SPLIT, bool GATHER = false, bool TB = false>
 __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
     const bf16_t *__restrict__ A, const bf16_t *__restrict__ B1, const bf16_t *__restrict__ B3,
     void *__restrict__ C, const int32_t *__restrict__ seg_off,
@@ -426,6 +457,7 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
   constexpr int STAGE_U4 = ROWS * 8;      // uint4 per stage
   static_assert(!SWIGLU || (TN % 2 == 0), "SwiGLU pairs W1/W3 blocks inside a wave");
   static_assert(BM % 32 == 0 && BNB % 32 == 0, "rows per stage must split over 4 waves");
+  static_assert(!TB || BNB == 256, "the [K][N] weight tile is two 128-column halves");
 
   __shared__ uint4 st0[STAGE_U4];
   __shared__ uint4 st1[STAGE_U4];
@@ -462,9 +494,16 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
   const uint32_t rowb = (uint32_t)K * 2;  // bytes per row of A and B
   const uint32_t lc0 = (uint32_t)lrow * rowb + (uint32_t)((lchunk ^ (lrow >> 1)) * 16);
   const uint32_t lc1 = lc0 ^ 64u;          // chunk ^ 4 for odd blocks
+  // TB ([K][N] weights): an instruction moves 4 k-rows of 128 columns (256 B
+  // each) of one matrix; lane l takes k-row l / 16 and LDS chunk l % 16, which
+  // holds global chunk (l % 16) ^ (4 * (row & 3)) of its row (row & 3 = l / 16)
+  const uint32_t tbl = TB ? (uint32_t)(lane >> 4) * (uint32_t)N * 2u +
+                                (uint32_t)(((lane & 15) ^ ((lane >> 4) << 2)) * 16)
+                          : 0u;
   struct TileAddr {
     __amdgpu_buffer_rsrc_t ra, r1, r3;
     uint32_t lc0, lc1;
+    uint32_t tbl;  // TB: the lane's byte offset inside a [K][N] weight instruction
     uint32_t ga[GATHER ? IA : 1];  // GATHER: byte offset in x of each A instruction's row
     int row0, rows, n0;
     int nk;    // K slices of this unit (even)
@@ -511,15 +550,19 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
       ta.ra = make_rsrc(reinterpret_cast<const char *>(A) + (size_t)ta.row0 * rowb + kb,
                         (uint32_t)ta.rows * rowb - kb);
     }
-    const size_t eoff = (size_t)e * N * rowb + kb;
-    const uint32_t wbytes = (uint32_t)N * rowb - kb;
+    // [N][K] weights: the unit's K range starts kb bytes into every row;
+    // [K][N] weights (TB): it starts kb / 2 rows of N elements into the matrix
+    const uint32_t wkb = TB ? (kb / 2) * (uint32_t)N * 2u : kb;
+    const size_t eoff = (size_t)e * N * rowb + wkb;
+    const uint32_t wbytes = (uint32_t)N * rowb - wkb;
     ta.r1 = make_rsrc(reinterpret_cast<const char *>(B1) + eoff, wbytes);
     ta.r3 = SWIGLU ? make_rsrc(reinterpret_cast<const char *>(B3) + eoff, wbytes) : ta.r1;
     // per-tile copies of the lane offsets: keeps the compiler from hoisting
     // every instruction's offset out of the tile loop (and spilling them)
     ta.lc0 = lc0;
     ta.lc1 = lc1;
-    asm volatile("" : "+v"(ta.lc0), "+v"(ta.lc1));
+    ta.tbl = tbl;
+    asm volatile("" : "+v"(ta.lc0), "+v"(ta.lc1), "+v"(ta.tbl));
   };
   // B block parity: block (wave*IB + j)/4 is odd (a W3 block) iff (j/4) is odd,
   // because IB is a multiple of 8
@@ -538,6 +581,23 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
           buffer_to_lds16(ta.ra, ((j & 1) ? ta.lc1 : ta.lc0) + u, stage + (wave * IA + j) * 64);
         }
       }
+    if constexpr (TB) {
+      // B stage: [half][k-row 0..63][128 columns]; half = matrix (W1, W3) for
+      // SwiGLU, else columns n0 + 128 * half.  Instruction q = wave * IB + j
+      // fills k-rows 4 * (q % 16) .. + 3 of half q / 16.
+      const uint32_t kob = (uint32_t)kt * 128u * (uint32_t)N;  // 64 k-rows per slice
+#pragma unroll
+      for (int j = 0; j < IB; ++j) {
+        if (IA + j >= j0 && IA + j < j1) {
+          const int q = wave * IB + j, h = q / 16, kq = q % 16;
+          const uint32_t colb = (uint32_t)(SWIGLU ? ta.n0 : ta.n0 + 128 * h) * 2u;
+          buffer_to_lds16<BM == 64>((SWIGLU && h) ? ta.r3 : ta.r1,
+                                    ta.tbl + kob + (uint32_t)kq * 8u * (uint32_t)N + colb,
+                                    stage + BM * 8 + q * 64);
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < IB; ++j) {
       if (IA + j >= j0 && IA + j < j1) {
@@ -565,19 +625,54 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
   // fragment addressing: row part and the swizzled chunk of each 16-wide K step
   // (recomputed per tile from a laundered lane id, see lane_t below)
   int frow, cidx[4];
+  // TB: byte offset inside the B stage of the lane's transposed read for
+  // 32-column block beta of a half (its K step 0, first 4 k-rows).  Lane l of
+  // group g = l / 16 (i = l % 16) addresses k-row 8 * (g / 2) + i / 4 and
+  // columns 32 * beta + 16 * (g % 2) + 4 * (i % 4) .. + 3; ds_read_tr16_b64
+  // then hands lane i of the group column 32 * beta + 16 * (g % 2) + i of
+  // those four k-rows, which is what a 32x32x16 MFMA lane needs (column l % 32,
+  // K values 8 * (l / 32) + 0..3; the next read gives + 4..7).
+  int tbo[4];
   auto set_frag_addr = [&](int ln) {
     frow = ln & 31;
     const int xf = (frow >> 1) & 7;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) cidx[ks] = (ks * 2 + (ln >> 5)) ^ xf;
+    if constexpr (TB) {
+      const int g = (ln >> 4) & 3, i = ln & 15, r = i >> 2;
+#pragma unroll
+      for (int be = 0; be < 4; ++be)
+        tbo[be] = BM * 128 + (8 * (g >> 1) + r) * 256 +
+                  ((4 * (be ^ r)) + 2 * (g & 1) + ((i & 3) >> 1)) * 16 + 8 * (i & 1);
+    }
   };
   set_frag_addr(lane);
   // fragments of one 16-wide K step
   auto rd = [&](const uint4 *stage, int ks, uint4 (&af)[TM], uint4 (&bf)[TN]) {
 #pragma unroll
     for (int a = 0; a < TM; ++a) af[a] = stage[((wm * TM + a) * 32 + frow) * 8 + cidx[ks]];
+    if constexpr (TB) {
+      typedef __attribute__((address_space(3))) bf16x4_v lds_bf16x4;
+      const __attribute__((address_space(3))) char *sb =
+          (const __attribute__((address_space(3))) char *)stage;
 #pragma unroll
-    for (int b = 0; b < TN; ++b) bf[b] = stage[(BM + (wn * TN + b) * 32 + frow) * 8 + cidx[ks]];
+      for (int b = 0; b < TN; ++b) {
+        // SwiGLU: block b of wave wn is matrix b & 1, columns wn * 64 + (b / 2) * 32
+        // of the half; down: half wn, columns b * 32
+        const int m = SWIGLU ? (b & 1) : wn;
+        const int be = SWIGLU ? 2 * wn + (b >> 1) : b;
+        const int off = tbo[be] + m * 16384 + ks * 16 * 256;
+        const bf16x4_v lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(sb + off));
+        const bf16x4_v hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(sb + off + 4 * 256));
+        const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+        bf[b] = make_uint4(l2.x, l2.y, h2.x, h2.y);
+      }
+    } else {
+#pragma unroll
+      for (int b = 0; b < TN; ++b)
+        bf[b] = stage[(BM + (wn * TN + b) * 32 + frow) * 8 + cidx[ks]];
+    }
   };
   auto mm = [&](const uint4 (&af)[TM], const uint4 (&bf)[TN]) {
 #pragma unroll
@@ -595,8 +690,10 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
   __atomic_signal_fence(__ATOMIC_SEQ_CST); } while (0)
 #define VM_WAIT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0xF70)
 #define LGKM_WAIT0() __builtin_amdgcn_s_waitcnt(0xC07F)
-  // 16 MFMAs with two LDS reads after each of the first 12
-#define P_MM_RD() do { for (int q_ = 0; q_ < 12; ++q_) { SG(8,1); SG(0x100,2); } SG(8,4); } while (0)
+  // LDS read instructions per 16-wide K step (a transposed B fragment takes two)
+  constexpr int RDS = TM + (TB ? 2 : 1) * TN;
+  // 16 MFMAs with RDS / 4 LDS reads after each of the first 12
+#define P_MM_RD() do { for (int q_ = 0; q_ < 12; ++q_) { SG(8,1); SG(0x100,RDS / 4); } SG(8,4); } while (0)
   // loads of the slice two ahead: J1 of them spread over the MFMAs of K steps
   // 1 and 2, the rest over step 3 (after the wait for the next slice)
   constexpr int J1 = PER * 5 / 8;
@@ -604,7 +701,7 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
   constexpr bool FULL = TM == 4 && TN == 4 && PER == 16;
 #define P_MM_LD() do { for (int q_ = 0; q_ < J1; ++q_) { SG(8,3); SG(0x20,1); } SG(8, 32 - 3 * J1); } while (0)
 #define P_MM_RD_LD() do { for (int q_ = 0; q_ < PER - J1; ++q_) { SG(8,2); SG(0x100,1); SG(0x20,1); } \
-  SG(0x100, TM + TN - (PER - J1)); SG(8, 16 - 2 * (PER - J1)); } while (0)
+  SG(0x100, RDS - (PER - J1)); SG(8, 16 - 2 * (PER - J1)); } while (0)
 // ISSUE: the slice two ahead exists and is loaded into S; NEXT: a next slice
 // exists (wait for it, read its first K step)
 #define SLICE_BODY(S, S2, s, ca, cb, na, nb, ISSUE, NEXT)                      \
@@ -780,7 +877,7 @@ int resident_wgs(int bm) {
   return cus[dev] * (bm == 64 ? 2 : 1);
 }
 
-template <int BM, int BNB, bool SWIGLU, bool SPLIT = false, bool GATHER = false>
+template <int BM, int BNB, bool SWIGLU, bool SPLIT = false, bool GATHER = false, bool TB = false>
 hipError_t launch_dl(const void *A, const void *B1, const void *B3, void *C,
                      const int32_t *seg_off, const int32_t *seg_end, const int32_t *mtile_off,
                      int G, int N, int K, int ksplit, size_t plane, int act, const FixScratch &fx,
@@ -789,7 +886,7 @@ hipError_t launch_dl(const void *A, const void *B1, const void *B3, void *C,
   // persistent grid: what stays resident, a multiple of the XCD count
   const int gx = (resident_wgs(BM) / ksplit + NUM_XCD - 1) / NUM_XCD * NUM_XCD;
   const size_t cap = fx.part ? fx.part_bytes / ((size_t)BM * BNB * 4) : 0;
-  hipLaunchKernelGGL((grouped_gemm_dl_kernel<BM, BNB, SWIGLU, SPLIT, GATHER>), dim3(gx, ksplit),
+  hipLaunchKernelGGL((grouped_gemm_dl_kernel<BM, BNB, SWIGLU, SPLIT, GATHER, TB>), dim3(gx, ksplit),
                      dim3(GM_THREADS), 0, s, (const bf16_t *)A, (const bf16_t *)B1,
                      (const bf16_t *)B3, C, seg_off, seg_end ? seg_end : seg_off + 1, mtile_off, G,
                      N, K, plane, act, fx.cnt, (f32x4_v *)fx.part,
@@ -798,13 +895,13 @@ hipError_t launch_dl(const void *A, const void *B1, const void *B3, void *C,
   return hipGetLastError();
 }
 
-template <typename T, int BM, int BNB, int WM, int WN, bool SWIGLU>
+template <typename T, int BM, int BNB, int WM, int WN, bool SWIGLU, bool TB>
 hipError_t launch_one(const void *A, const void *B1, const void *B3, void *C,
                       const int32_t *seg_off, const int32_t *mtile_off, int G, int N, int K,
                       int max_mtiles, int act, hipStream_t s) {
   const int cols = SWIGLU ? BNB / 2 : BNB;
   dim3 grid(((N + cols - 1) / cols) * max_mtiles + NUM_XCD);
-  hipLaunchKernelGGL((grouped_gemm_kernel<T, BM, BNB, WM, WN, SWIGLU>), grid, dim3(GM_THREADS),
+  hipLaunchKernelGGL((grouped_gemm_kernel<T, BM, BNB, WM, WN, SWIGLU, TB>), grid, dim3(GM_THREADS),
                      0, s, (const T *)A, (const T *)B1, (const T *)B3, C, seg_off, mtile_off, G,
                      N, K, act);
   return hipGetLastError();
@@ -835,61 +932,90 @@ bool gemm_gather_ok(int dtype, bool dl, int bm, long long a_bytes) {
   return dtype == 1 && dl && (bm == 64 || bm == 256) && a_bytes + (1LL << 20) < (1LL << 31);
 }
 
-hipError_t launch_gemm_swiglu(int dtype, bool dl, int bm, int act, const void *A,
-                              const void *W1, const void *W3, void *H, const int32_t *seg_off,
-                              const int32_t *mtile_off, int G, int N, int K, int max_mtiles,
-                              hipStream_t s, const int32_t *seg_end, const int32_t *gperm, int gk,
-                              long long a_bytes) {
-  if (max_mtiles <= 0) return hipSuccess;
+namespace {
+
+template <bool TB>
+hipError_t gemm_swiglu_t(int dtype, bool dl, int bm, int act, const void *A, const void *W1,
+                         const void *W3, void *H, const int32_t *seg_off,
+                         const int32_t *mtile_off, int G, int N, int K, int max_mtiles,
+                         hipStream_t s, const int32_t *seg_end, const int32_t *gperm, int gk,
+                         long long a_bytes) {
   const FixScratch none{nullptr, nullptr, 0};
   if (gperm) {
     if (!gemm_gather_ok(dtype, dl, bm, a_bytes)) return hipErrorInvalidValue;
     if (bm == 64)
-      return launch_dl<64, 256, true, false, true>(A, W1, W3, H, seg_off, seg_end, mtile_off, G,
-                                                   N, K, 1, 0, act, none, s, gperm, gk,
-                                                   (uint32_t)a_bytes);
-    return launch_dl<256, 256, true, false, true>(A, W1, W3, H, seg_off, seg_end, mtile_off, G, N,
-                                                  K, 1, 0, act, none, s, gperm, gk,
-                                                  (uint32_t)a_bytes);
+      return launch_dl<64, 256, true, false, true, TB>(A, W1, W3, H, seg_off, seg_end, mtile_off,
+                                                       G, N, K, 1, 0, act, none, s, gperm, gk,
+                                                       (uint32_t)a_bytes);
+    return launch_dl<256, 256, true, false, true, TB>(A, W1, W3, H, seg_off, seg_end, mtile_off,
+                                                      G, N, K, 1, 0, act, none, s, gperm, gk,
+                                                      (uint32_t)a_bytes);
   }
   if (dl && bm == 64)
-    return launch_dl<64, 256, true>(A, W1, W3, H, seg_off, seg_end, mtile_off, G, N, K, 1, 0,
-                                    act, none, s);
+    return launch_dl<64, 256, true, false, false, TB>(A, W1, W3, H, seg_off, seg_end, mtile_off,
+                                                      G, N, K, 1, 0, act, none, s);
   if (dl)
-    return launch_dl<256, 256, true>(A, W1, W3, H, seg_off, seg_end, mtile_off, G, N, K, 1, 0,
-                                     act, none, s);
+    return launch_dl<256, 256, true, false, false, TB>(A, W1, W3, H, seg_off, seg_end, mtile_off,
+                                                       G, N, K, 1, 0, act, none, s);
   if (seg_end) return hipErrorInvalidValue;  // the tiled kernels take whole segments
   if (dtype == 1)
-    return launch_one<bf16_t, 128, 128, 2, 2, true>(A, W1, W3, H, seg_off, mtile_off, G, N, K,
-                                                    max_mtiles, act, s);
-  return launch_one<float, 128, 128, 2, 2, true>(A, W1, W3, H, seg_off, mtile_off, G, N, K,
-                                                 max_mtiles, act, s);
+    return launch_one<bf16_t, 128, 128, 2, 2, true, TB>(A, W1, W3, H, seg_off, mtile_off, G, N,
+                                                        K, max_mtiles, act, s);
+  return launch_one<float, 128, 128, 2, 2, true, TB>(A, W1, W3, H, seg_off, mtile_off, G, N, K,
+                                                     max_mtiles, act, s);
+}
+
+template <bool TB>
+hipError_t gemm_down_t(int dtype, bool dl, int bm, const void *A, const void *W2, void *Y,
+                       const int32_t *seg_off, const int32_t *mtile_off, int G, int N, int K,
+                       int max_mtiles, int ksplit, size_t plane, const FixScratch &fx,
+                       hipStream_t s, const int32_t *seg_end, bool ybf16) {
+  const int yb = ybf16 ? 1 : 0;
+  if (dl && bm == 64)
+    return launch_dl<64, 256, false, false, false, TB>(A, W2, nullptr, Y, seg_off, seg_end,
+                                                       mtile_off, G, N, K, ksplit, plane, yb,
+                                                       fx, s);
+  // the last-round split pays for long K only (the kernel's estimate never
+  // splits below SPLIT_MIN_K)
+  if (dl && ksplit == 1 && K >= SPLIT_MIN_K && fx.part)
+    return launch_dl<256, 256, false, true, false, TB>(A, W2, nullptr, Y, seg_off, seg_end,
+                                                       mtile_off, G, N, K, 1, 0, yb, fx, s);
+  if (dl)
+    return launch_dl<256, 256, false, false, false, TB>(A, W2, nullptr, Y, seg_off, seg_end,
+                                                        mtile_off, G, N, K, ksplit, plane, yb,
+                                                        fx, s);
+  if (seg_end) return hipErrorInvalidValue;  // the tiled kernels take whole segments
+  if (dtype == 1)
+    return launch_one<bf16_t, 128, 128, 2, 2, false, TB>(A, W2, nullptr, Y, seg_off, mtile_off,
+                                                         G, N, K, max_mtiles, 0, s);
+  return launch_one<float, 128, 128, 2, 2, false, TB>(A, W2, nullptr, Y, seg_off, mtile_off, G,
+                                                      N, K, max_mtiles, 0, s);
+}
+
+}  // namespace
+
+hipError_t launch_gemm_swiglu(int dtype, bool dl, int bm, int act, const void *A,
+                              const void *W1, const void *W3, void *H, const int32_t *seg_off,
+                              const int32_t *mtile_off, int G, int N, int K, int max_mtiles,
+                              hipStream_t s, const int32_t *seg_end, const int32_t *gperm, int gk,
+                              long long a_bytes, bool tb) {
+  if (max_mtiles <= 0) return hipSuccess;
+  return tb ? gemm_swiglu_t<true>(dtype, dl, bm, act, A, W1, W3, H, seg_off, mtile_off, G, N, K,
+                                  max_mtiles, s, seg_end, gperm, gk, a_bytes)
+            : gemm_swiglu_t<false>(dtype, dl, bm, act, A, W1, W3, H, seg_off, mtile_off, G, N, K,
+                                   max_mtiles, s, seg_end, gperm, gk, a_bytes);
 }
 
 hipError_t launch_gemm_down(int dtype, bool dl, int bm, const void *A, const void *W2, void *Y,
                             const int32_t *seg_off, const int32_t *mtile_off, int G, int N, int K,
                             int max_mtiles, int ksplit, size_t plane, const FixScratch &fx,
-                            hipStream_t s, const int32_t *seg_end, bool ybf16) {
+                            hipStream_t s, const int32_t *seg_end, bool ybf16, bool tb) {
   if (max_mtiles <= 0) return hipSuccess;
   if (ybf16 && (!dl || ksplit != 1)) return hipErrorInvalidValue;
-  const int yb = ybf16 ? 1 : 0;
-  if (dl && bm == 64)
-    return launch_dl<64, 256, false>(A, W2, nullptr, Y, seg_off, seg_end, mtile_off, G, N, K,
-                                     ksplit, plane, yb, fx, s);
-  // the last-round split pays for long K only (the kernel's estimate never
-  // splits below SPLIT_MIN_K)
-  if (dl && ksplit == 1 && K >= SPLIT_MIN_K && fx.part)
-    return launch_dl<256, 256, false, true>(A, W2, nullptr, Y, seg_off, seg_end, mtile_off, G,
-                                            N, K, 1, 0, yb, fx, s);
-  if (dl)
-    return launch_dl<256, 256, false>(A, W2, nullptr, Y, seg_off, seg_end, mtile_off, G, N, K,
-                                      ksplit, plane, yb, fx, s);
-  if (seg_end) return hipErrorInvalidValue;  // the tiled kernels take whole segments
-  if (dtype == 1)
-    return launch_one<bf16_t, 128, 128, 2, 2, false>(A, W2, nullptr, Y, seg_off, mtile_off, G,
-                                                     N, K, max_mtiles, 0, s);
-  return launch_one<float, 128, 128, 2, 2, false>(A, W2, nullptr, Y, seg_off, mtile_off, G, N,
-                                                  K, max_mtiles, 0, s);
+  return tb ? gemm_down_t<true>(dtype, dl, bm, A, W2, Y, seg_off, mtile_off, G, N, K, max_mtiles,
+                                ksplit, plane, fx, s, seg_end, ybf16)
+            : gemm_down_t<false>(dtype, dl, bm, A, W2, Y, seg_off, mtile_off, G, N, K,
+                                 max_mtiles, ksplit, plane, fx, s, seg_end, ybf16);
 }
 
 }  // namespace moe

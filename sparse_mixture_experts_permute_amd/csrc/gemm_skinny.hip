@@ -715,6 +715,180 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_swiglu_wave_kernel(
   compute(wb, j + 1);
 }
 
+// ---------------------------------------------------------------------------
+// Weight streaming for [K][N] expert weights (in x out: the layer computes
+// rows of A W), up to R rows per pass.  A workgroup owns one (active expert,
+// block of CW output columns) pair and reads that weight slice once; its four
+// wavefronts split K.  Lane l covers columns c0 + 8 * (l % LPR) .. + 7 (LPR =
+// CW / 8 lanes per k-row) of its own contiguous run of M = K / (4 * 64 / LPR)
+// k-rows, so a wavefront instruction reads 64 / LPR whole k-row segments of
+// CW * 2 bytes, and one 16-byte load of each row's activations serves eight
+// k-rows.  The products are summed in fp32 per column; lanes that share
+// columns are then reduced by the butterfly and the wavefronts through LDS,
+// both in a fixed order.
+// ---------------------------------------------------------------------------
+template <bool SWIGLU, int R, int CW>
+__global__ __launch_bounds__(GV_THREADS) void gemv_t_kernel(
+    const bf16_t *__restrict__ A, const int32_t *__restrict__ perm, int kslots,
+    const bf16_t *__restrict__ B1, const bf16_t *__restrict__ B3, void *__restrict__ C,
+    const int32_t *__restrict__ seg_off, const int32_t *__restrict__ active,
+    const int32_t *__restrict__ nactive, int N, int K, int act) {
+  constexpr int NW = SWIGLU ? 2 : 1;
+  constexpr int LPR = CW / 8;     // lanes per k-row
+  constexpr int KG = kWave / LPR; // k-rows per wavefront instruction
+  __shared__ float red[GV_WAVES][NW][R][CW];
+  const int nblk = N / CW;
+  const int a_idx = blockIdx.x / nblk;
+  if (a_idx >= nactive[0]) return;
+  const int e = active[a_idx];
+  const int c0 = (blockIdx.x % nblk) * CW;
+  const int s0 = seg_off[e], cnt = seg_off[e + 1] - s0;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = lane_id();
+  const int M = K / (GV_WAVES * KG);  // k-rows per lane, a multiple of 8 (host check)
+  const int kb = wave * (K / GV_WAVES) + (lane / LPR) * M;
+  const int cl = c0 + (lane % LPR) * 8;
+  const bf16_t *w1 = B1 + ((size_t)e * K + kb) * N + cl;
+  const bf16_t *w3 = SWIGLU ? B3 + ((size_t)e * K + kb) * N + cl : w1;
+  const int ng = M / 8;  // groups of 8 k-rows
+
+  for (int rg = 0; rg < cnt; rg += R) {
+    const bf16_t *ap[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int row = min(rg + r, cnt - 1);  // rows past the end: duplicates, not stored
+      const int src = perm ? perm[s0 + row] / kslots : s0 + row;
+      ap[r] = A + (size_t)src * K + kb;
+    }
+    float acc[NW][R][8];
+#pragma unroll
+    for (int m = 0; m < NW; ++m)
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[m][r][j] = 0.f;
+    uint4 wa[NW][8], wb[NW][8], xa[R], xb[R];
+    auto load = [&](uint4 (&w)[NW][8], uint4 (&xv)[R], int g) {
+      const size_t ro = (size_t)g * 8 * N;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        w[0][i] = ldg16_stream(w1 + ro + (size_t)i * N);
+        if (SWIGLU) w[NW - 1][i] = ldg16_stream(w3 + ro + (size_t)i * N);
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) xv[r] = *reinterpret_cast<const uint4 *>(ap[r] + g * 8);
+    };
+    auto compute = [&](const uint4 (&w)[NW][8], const uint4 (&xv)[R]) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+#pragma unroll
+        for (int m = 0; m < NW; ++m) {
+          const uint32_t wq[4] = {w[m][i].x, w[m][i].y, w[m][i].z, w[m][i].w};
+          float wf[8];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            wf[2 * q] = __uint_as_float(wq[q] << 16);
+            wf[2 * q + 1] = __uint_as_float(wq[q] & 0xFFFF0000u);
+          }
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            const uint32_t xw = (&xv[r].x)[i >> 1];
+            const float xs = __uint_as_float((i & 1) ? (xw & 0xFFFF0000u) : (xw << 16));
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[m][r][j] = fmaf(xs, wf[j], acc[m][r][j]);
+          }
+        }
+      }
+    };
+    // ng is even (M is a multiple of 16 when K allows, else handled by the tail)
+    load(wa, xa, 0);
+    if (ng > 1) load(wb, xb, 1);
+    int g = 0;
+    for (; g + 2 < ng; g += 2) {
+      compute(wa, xa);
+      load(wa, xa, g + 2);
+      compute(wb, xb);
+      if (g + 3 < ng) load(wb, xb, g + 3);
+    }
+    compute(wa, xa);
+    if (g + 1 < ng) compute(wb, xb);
+    // lanes of one column set (same lane % LPR) hold partial sums over
+    // different k-rows: butterfly over the k-row groups, then waves in order
+#pragma unroll
+    for (int m = 0; m < NW; ++m)
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          float v = acc[m][r][j];
+#pragma unroll
+          for (int off = LPR; off < kWave; off <<= 1) v += __shfl_xor(v, off);
+          acc[m][r][j] = v;
+        }
+    if (lane < LPR) {
+#pragma unroll
+      for (int m = 0; m < NW; ++m)
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) red[wave][m][r][lane * 8 + j] = acc[m][r][j];
+    }
+    __syncthreads();
+    for (int o = tid; o < R * CW; o += GV_THREADS) {
+      const int r = o / CW, c = o % CW;
+      if (rg + r < cnt) {
+        float v[NW];
+#pragma unroll
+        for (int m = 0; m < NW; ++m) {
+          float t = 0.f;
+#pragma unroll
+          for (int w = 0; w < GV_WAVES; ++w) t += red[w][m][r][c];
+          v[m] = t;
+        }
+        const size_t out = (size_t)(s0 + rg + r) * N + c0 + c;
+        if (SWIGLU)
+          reinterpret_cast<bf16_t *>(C)[out] = f32_to_bf16(gated(v[0], v[NW - 1], act));
+        else
+          reinterpret_cast<float *>(C)[out] = v[0];
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <bool SWIGLU, int R>
+hipError_t launch_gemv_t_r(int act, const void *A, const int32_t *perm, int kslots,
+                           const void *B1, const void *B3, void *C, const int32_t *seg_off,
+                           const int32_t *active, const int32_t *nactive, int G, int N, int K,
+                           hipStream_t s) {
+  const bf16_t *a = (const bf16_t *)A, *b1 = (const bf16_t *)B1, *b3 = (const bf16_t *)B3;
+  // 64-column blocks when they give every CU a workgroup, else 32
+  if ((long long)G * (N / 64) >= 256 && K % (GV_WAVES * 8 * 8) == 0 && N % 64 == 0) {
+    hipLaunchKernelGGL((gemv_t_kernel<SWIGLU, R, 64>), dim3(G * (N / 64)), dim3(GV_THREADS), 0,
+                       s, a, perm, kslots, b1, b3, C, seg_off, active, nactive, N, K, act);
+  } else {
+    if (K % (GV_WAVES * 16 * 8) || N % 32) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemv_t_kernel<SWIGLU, R, 32>), dim3(G * (N / 32)), dim3(GV_THREADS), 0,
+                       s, a, perm, kslots, b1, b3, C, seg_off, active, nactive, N, K, act);
+  }
+  return hipGetLastError();
+}
+
+template <bool SWIGLU>
+hipError_t launch_gemv_t(int rows, int act, const void *A, const int32_t *perm, int kslots,
+                         const void *B1, const void *B3, void *C, const int32_t *seg_off,
+                         const int32_t *active, const int32_t *nactive, int G, int N, int K,
+                         hipStream_t s) {
+  if (rows <= 1)
+    return launch_gemv_t_r<SWIGLU, 1>(act, A, perm, kslots, B1, B3, C, seg_off, active, nactive,
+                                      G, N, K, s);
+  if (rows <= 2)
+    return launch_gemv_t_r<SWIGLU, 2>(act, A, perm, kslots, B1, B3, C, seg_off, active, nactive,
+                                      G, N, K, s);
+  return launch_gemv_t_r<SWIGLU, 4>(act, A, perm, kslots, B1, B3, C, seg_off, active, nactive, G,
+                                    N, K, s);
+}
+
 template <bool SWIGLU, int R, bool COMBINE = false, bool W8 = false, bool ROUTE = false>
 hipError_t launch_gemv_r(int act, const void *A, const int32_t *perm, int kslots,
                          const void *B1, const void *B3, void *C, const int32_t *seg_off,
@@ -841,6 +1015,23 @@ hipError_t launch_gemv_down_combine_fp8(int rows, const void *Hin, const uint8_t
   const GemvCombine cm{inv, gate, T, k, (bf16_t *)y, cnt};
   return launch_gemv<false, true, true>(rows, 0, Hin, nullptr, 1, W2q, nullptr, Y, seg_off,
                                         active, nactive, G, N, K, nact, cm, s, s2, nullptr);
+}
+
+bool gemv_t_ok(int N, int K) { return N % 32 == 0 && K % (GV_WAVES * 16 * 8) == 0; }
+
+hipError_t launch_gemv_t_swiglu(int rows, int act, const void *x, const int32_t *perm,
+                                int kslots, const void *W1, const void *W3, void *H,
+                                const int32_t *seg_off, const int32_t *active,
+                                const int32_t *nactive, int G, int N, int K, hipStream_t s) {
+  return launch_gemv_t<true>(rows, act, x, perm, kslots, W1, W3, H, seg_off, active, nactive, G,
+                             N, K, s);
+}
+
+hipError_t launch_gemv_t_down(int rows, const void *Hin, const void *W2, float *Y,
+                              const int32_t *seg_off, const int32_t *active,
+                              const int32_t *nactive, int G, int N, int K, hipStream_t s) {
+  return launch_gemv_t<false>(rows, 0, Hin, nullptr, 1, W2, nullptr, Y, seg_off, active, nactive,
+                              G, N, K, s);
 }
 
 bool route_fused_ok(int T, int d, int E, int k) {

@@ -110,6 +110,7 @@ struct FixScratch {
 // for a GEMM of at most `tiles` output tiles.
 size_t fix_part_bytes(long long tiles);
 // act: 0 SiLU(W1 a) * (W3 a), 1 sigmoid(W1 a) * (W3 a)
+// tb: the weights are [K][N] per expert (in x out, A W) instead of [N][K]
 // seg_end (direct-to-LDS kernel only; NULL: seg_off + 1): expert e's rows
 // are seg_off[e] .. seg_end[e] - 1, with mtile_off the prefix of its tiles.
 // gperm (gemm_gather_ok only): A is x itself (a_bytes bytes) and grouped row s
@@ -119,7 +120,8 @@ hipError_t launch_gemm_swiglu(int dtype, bool dl, int bm, int act, const void *A
                               const void *W1, const void *W3, void *H, const int32_t *seg_off,
                               const int32_t *mtile_off, int G, int N, int K, int max_mtiles,
                               hipStream_t s, const int32_t *seg_end = nullptr,
-                              const int32_t *gperm = nullptr, int gk = 1, long long a_bytes = 0);
+                              const int32_t *gperm = nullptr, int gk = 1, long long a_bytes = 0,
+                              bool tb = false);
 // ksplit > 1 (direct-to-LDS kernel only): every tile's K is split in ksplit
 // equal ranges whose fp32 partials go to planes `plane` elements apart (for
 // batches with few tiles; the last-round split then stays off).
@@ -127,7 +129,8 @@ hipError_t launch_gemm_swiglu(int dtype, bool dl, int bm, int act, const void *A
 hipError_t launch_gemm_down(int dtype, bool dl, int bm, const void *A, const void *W2, void *Y,
                             const int32_t *seg_off, const int32_t *mtile_off, int G, int N, int K,
                             int max_mtiles, int ksplit, size_t plane, const FixScratch &fx,
-                            hipStream_t s, const int32_t *seg_end = nullptr, bool ybf16 = false);
+                            hipStream_t s, const int32_t *seg_end = nullptr, bool ybf16 = false,
+                            bool tb = false);
 
 // Weight-streaming grouped GEMMs for few rows per expert (bf16 only).
 bool skinny_ok(int N, int K);
@@ -161,6 +164,16 @@ hipError_t launch_gemv_down_token(const void *H, const void *W2, const float *s2
                                   const int32_t *seg_off, const int32_t *active,
                                   const int32_t *nactive, int N, int K, const int32_t *inv,
                                   const float *gate, int k, void *y, hipStream_t s);
+// [K][N] (in x out) weights, up to four rows per expert per pass (more rows
+// loop): vector-ALU weight streaming, H bf16 / Y fp32 as the gemv kernels
+bool gemv_t_ok(int N, int K);
+hipError_t launch_gemv_t_swiglu(int rows, int act, const void *x, const int32_t *perm,
+                                int kslots, const void *W1, const void *W3, void *H,
+                                const int32_t *seg_off, const int32_t *active,
+                                const int32_t *nactive, int G, int N, int K, hipStream_t s);
+hipError_t launch_gemv_t_down(int rows, const void *Hin, const void *W2, float *Y,
+                              const int32_t *seg_off, const int32_t *active,
+                              const int32_t *nactive, int G, int N, int K, hipStream_t s);
 hipError_t launch_skinny_swiglu(int mb, int act, const void *x, const int32_t *perm, int kslots,
                                 const void *W1, const void *W3, void *H,
                                 const int32_t *seg_off, const int32_t *active,

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
 MOE_F32, MOE_BF16 = 0, 1
 GATE_SOFTMAX_TOPK, GATE_SOFTMAX_ALL, GATE_SIGMOID, GATE_ENTROPY = 0, 1, 2, 3
 ACT_SWIGLU, ACT_GLU_SIGMOID = 0, 1
+LAYOUT_OUT_IN, LAYOUT_IN_OUT = 0, 1
 NSTAGE_EVENTS = 8
 STAGES = ("router", "permute", "gather", "gemm_swiglu", "gemm_down", "shared_expert", "combine")
 WS_FIELDS = ("logits", "idx", "gate", "counts", "offsets", "perm", "inv")
@@ -28,7 +29,7 @@ _lib = None
 
 class _Options(ctypes.Structure):
     _fields_ = [("gate_mode", ctypes.c_int), ("activation", ctypes.c_int),
-                ("capacity", ctypes.c_int)]
+                ("capacity", ctypes.c_int), ("weight_layout", ctypes.c_int)]
 
 
 class MoEError(RuntimeError):
@@ -59,7 +60,8 @@ def lib():
         L.moe_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp,
                                   sz, vp, vp]
         L.moe_forward.restype = i
-        L.moe_forward_timed.argtypes = L.moe_forward.argtypes + [vp]
+        L.moe_forward_timed.argtypes = (L.moe_forward.argtypes[:16] + [ctypes.POINTER(_Options)]
+                                        + L.moe_forward.argtypes[16:] + [vp])
         L.moe_forward_timed.restype = i
         L.moe_strerror.argtypes = [i]
         L.moe_strerror.restype = ctypes.c_char_p
@@ -80,6 +82,8 @@ def lib():
         L.moe_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i,
                                           i, vp, vp]
         L.moe_forward_noalloc.restype = i
+        L.moe_forward_inout.argtypes = L.moe_forward.argtypes
+        L.moe_forward_inout.restype = i
         _lib = L
     return _lib
 
@@ -223,25 +227,37 @@ def workspace_offsets(T, d, d_ff, E, k, d_ff_shared=0, dtype=MOE_BF16) -> dict:
 class MoELayer:
     """One layer's weights plus a reusable workspace.
 
-    W1, W3 [E][d_ff][d]; W2 [E][d][d_ff]; Wg [E][d]; optional bias [E] fp32;
-    optional shared (Ws1 [dffs][d], Ws3 [dffs][d], Ws2 [d][dffs]).  The
-    variants (gate_mode, activation, capacity) follow moe_options in the C
-    header; the defaults are the method itself.
+    Expert weights in the layout `weight_layout` names: LAYOUT_OUT_IN (Linear
+    weights) W1, W3 [E][d_ff][d], W2 [E][d][d_ff], shared (Ws1 [dffs][d], Ws3
+    [dffs][d], Ws2 [d][dffs]); LAYOUT_IN_OUT (x @ W) W1, W3 [E][d][d_ff], W2
+    [E][d_ff][d], shared (Ws1 [d][dffs], Ws3 [d][dffs], Ws2 [dffs][d]).
+    Wg [E][d]; optional bias [E] fp32.  The variants (gate_mode, activation,
+    capacity) follow moe_options in the C header; the defaults are the method
+    itself.
     """
 
     def __init__(self, Wg, W1, W3, W2, k, bias=None, shared=None,
-                 gate_mode=GATE_SOFTMAX_TOPK, activation=ACT_SWIGLU, capacity=-1):
+                 gate_mode=GATE_SOFTMAX_TOPK, activation=ACT_SWIGLU, capacity=-1,
+                 weight_layout=LAYOUT_OUT_IN):
         self.Wg, self.W1, self.W3, self.W2, self.k, self.bias = Wg, W1, W3, W2, k, bias
-        self.options = _Options(int(gate_mode), int(activation), int(capacity))
+        if weight_layout not in (LAYOUT_OUT_IN, LAYOUT_IN_OUT):
+            raise MoEError(f"unknown weight layout {weight_layout}")
+        self.inout = weight_layout == LAYOUT_IN_OUT
+        self.options = _Options(int(gate_mode), int(activation), int(capacity),
+                                int(weight_layout))
         self._default = (gate_mode == GATE_SOFTMAX_TOPK and activation == ACT_SWIGLU
                          and capacity < 0)
         if W1.dim() != 3:
-            raise MoEError("W1: expected [E][d_ff][d]")
-        self.E, self.d_ff, self.d = W1.shape
+            raise MoEError("W1: expected a 3-d expert tensor")
+        if self.inout:
+            self.E, self.d, self.d_ff = W1.shape
+        else:
+            self.E, self.d_ff, self.d = W1.shape
         self.dtype = _dt(W1)
         E, d, d_ff = self.E, self.d, self.d_ff
-        _same(W3, W1, (E, d_ff, d), "W3")
-        _same(W2, W1, (E, d, d_ff), "W2")
+        io = (lambda a, b: (b, a)) if self.inout else (lambda a, b: (a, b))  # [out][in]
+        _same(W3, W1, (E,) + io(d_ff, d), "W3")
+        _same(W2, W1, (E,) + io(d, d_ff), "W2")
         _same(Wg, W1, (E, d), "Wg")
         _check_bias(bias, E, W1)
         self.shared = shared
@@ -249,11 +265,11 @@ class MoELayer:
         if shared is not None:
             Ws1, Ws3, Ws2 = shared
             if Ws1.dim() != 2:
-                raise MoEError("Ws1: expected [d_ff_shared][d]")
-            dffs = Ws1.shape[0]
-            _same(Ws1, W1, (dffs, d), "Ws1")
-            _same(Ws3, W1, (dffs, d), "Ws3")
-            _same(Ws2, W1, (d, dffs), "Ws2")
+                raise MoEError("Ws1: expected a 2-d matrix")
+            dffs = Ws1.shape[1] if self.inout else Ws1.shape[0]
+            _same(Ws1, W1, io(dffs, d), "Ws1")
+            _same(Ws3, W1, io(dffs, d), "Ws3")
+            _same(Ws2, W1, io(d, dffs), "Ws2")
             self.d_ff_shared = dffs
         self._ws = None
         self._ws_T = -1
@@ -273,7 +289,13 @@ class MoELayer:
             y = torch.empty_like(x2)
         ws, n = self.workspace(T)
         Ws1, Ws3, Ws2 = self.shared if self.shared is not None else (None, None, None)
-        if self._default:
+        if self._default and self.inout:
+            _check(lib().moe_forward_inout(_p(x2), _p(self.Wg), _p(self.bias), _p(self.W1),
+                                           _p(self.W3), _p(self.W2), _p(Ws1), _p(Ws3), _p(Ws2),
+                                           self.d_ff_shared, T, self.E, self.k, self.d,
+                                           self.d_ff, self.dtype, _p(ws), n, _p(y), _stream()),
+                   "moe_forward_inout")
+        elif self._default:
             _check(lib().moe_forward(_p(x2), _p(self.Wg), _p(self.bias), _p(self.W1),
                                      _p(self.W3), _p(self.W2), _p(Ws1), _p(Ws3), _p(Ws2),
                                      self.d_ff_shared, T, self.E, self.k, self.d, self.d_ff,
@@ -288,10 +310,7 @@ class MoELayer:
 
     def timed(self, x: torch.Tensor, y: torch.Tensor, events) -> torch.Tensor:
         """Same as a call, recording `events` (NSTAGE_EVENTS torch.cuda.Event,
-        already created by a record) at the stage boundaries on the stream
-        (the method's defaults only)."""
-        if not self._default:
-            raise MoEError("stage timing covers the default variant only")
+        already created by a record) at the stage boundaries on the stream."""
         _check_tokens(x, y, self.d, self.W1)
         T = x.shape[0]
         ws, n = self.workspace(T)
@@ -301,7 +320,8 @@ class MoELayer:
         _check(lib().moe_forward_timed(_p(x), _p(self.Wg), _p(self.bias), _p(self.W1),
                                        _p(self.W3), _p(self.W2), _p(Ws1), _p(Ws3), _p(Ws2),
                                        self.d_ff_shared, T, self.E, self.k, self.d, self.d_ff,
-                                       self.dtype, _p(ws), n, _p(y), _stream(), handles),
+                                       self.dtype, ctypes.byref(self.options), _p(ws), n, _p(y),
+                                       _stream(), handles),
                "moe_forward_timed")
         return y
 
@@ -360,7 +380,7 @@ class MoELayerFP8:
         self.W1q, self.s1 = quantize_fp8(W1)
         self.W3q, self.s3 = quantize_fp8(W3)
         self.W2q, self.s2 = quantize_fp8(W2)
-        self.options = _Options(int(gate_mode), int(activation), int(capacity))
+        self.options = _Options(int(gate_mode), int(activation), int(capacity), LAYOUT_OUT_IN)
         self._ws = None
 
     def workspace(self, T):
