@@ -27,6 +27,16 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
+# Context, not targets: the numpy timings of the 7-config granularity table on
+# "Trillion-parameter MoE activates only 4.9%: 7 expert configs measured"
+# (results table; 2-core i5-1340P under WSL, T=512, d=512, float32; median and
+# fastest of 20 runs, ms).  The page times its own function: sigmoid route
+# weights and a sigmoid-gated expert.
+PAGE_NUMPY_MS = {(1, 32768, 1): (1195.30, 1014.21), (8, 4096, 1): (117.49, 109.76),
+                 (8, 4096, 2): (235.78, 208.57), (32, 1024, 1): (65.45, 61.45),
+                 (32, 1024, 2): (150.10, 111.87), (64, 512, 4): (160.41, 128.77),
+                 (128, 256, 8): (219.62, 203.44)}
+
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
@@ -38,6 +48,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="mixtral_prefill_T8192")
+    ap.add_argument("--layout", choices=("outin", "inout"), default="outin",
+                    help="expert weights as Linear weights [out][in] or as [in][out] (x @ W)")
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=0,
@@ -65,7 +77,17 @@ def algorithmic(cfg, counts):
                 layer_bytes=layer_bytes, experts_hit=hit)
 
 
-def run_workload(cfg, host, dev, steps, warmup, flush_mb=0, graph=False, min_warm_s=0.0):
+def transposed(dev):
+    """The expert weights of `dev` in the [in][out] layout (copies)."""
+    out = dict(dev)
+    for n in ("W1", "W3", "W2", "Ws1", "Ws3", "Ws2"):
+        if out.get(n) is not None:
+            out[n] = out[n].transpose(-1, -2).contiguous()
+    return out
+
+
+def run_workload(cfg, host, dev, steps, warmup, flush_mb=0, graph=False, min_warm_s=0.0,
+                 inout=False, **variants):
     """Time `steps` layer forwards.
 
     Pass 1 (the timed region for ms_per_step): back-to-back moe_forward calls
@@ -96,7 +118,9 @@ def run_workload(cfg, host, dev, steps, warmup, flush_mb=0, graph=False, min_war
         b[0] = cfg.skew
         bias = torch.from_numpy(b).cuda()
     shared = (dev["Ws1"], dev["Ws3"], dev["Ws2"]) if cfg.d_ff_shared else None
-    layer = moe.MoELayer(dev["Wg"], dev["W1"], dev["W3"], dev["W2"], cfg.k, bias, shared)
+    layer = moe.MoELayer(dev["Wg"], dev["W1"], dev["W3"], dev["W2"], cfg.k, bias, shared,
+                         weight_layout=moe.LAYOUT_IN_OUT if inout else moe.LAYOUT_OUT_IN,
+                         **variants)
     y = torch.empty_like(x)
     layer.workspace(T)
     flush = (torch.ones(flush_mb << 18, dtype=torch.float32, device="cuda") if flush_mb
@@ -183,7 +207,7 @@ def run_workload(cfg, host, dev, steps, warmup, flush_mb=0, graph=False, min_war
     return out
 
 
-def run_fp8(cfg, dev, steps, warmup, flush_mb):
+def run_fp8(cfg, dev, steps, warmup, flush_mb, layer=None):
     """Decode step with FP8 experts (moe_forward_fp8; weights quantised once,
     outside the timed region): mean per-step time around the forward with the
     MALL flushed before each step, and the expert counts."""
@@ -193,7 +217,8 @@ def run_fp8(cfg, dev, steps, warmup, flush_mb):
     from sparse_mixture_experts_permute_amd import moe
     T = cfg.T
     x = dev["x"][:T].contiguous()
-    layer = moe.MoELayerFP8(dev["Wg"], dev["W1"], dev["W3"], dev["W2"], cfg.k)
+    if layer is None:
+        layer = moe.MoELayerFP8(dev["Wg"], dev["W1"], dev["W3"], dev["W2"], cfg.k)
     y = torch.empty_like(x)
     flush = torch.ones(flush_mb << 18, dtype=torch.float32, device="cuda")
     for _ in range(warmup):
@@ -209,8 +234,6 @@ def run_fp8(cfg, dev, steps, warmup, flush_mb):
     torch.cuda.synchronize()
     ms = float(np.mean([a.elapsed_time(b_) for a, b_ in ev]))
     counts = layer.intermediates(T)["counts"].cpu().numpy()
-    del layer
-    torch.cuda.empty_cache()
     return dict(ms=ms, counts=counts)
 
 
@@ -310,9 +333,81 @@ def cpu_baseline(cfg, host, n_tokens):
     O.forward(x, host["Wg"], host["W1"], host["W3"], host["W2"], cfg.k, bias=bias, shared=shared)
     el = time.perf_counter() - t0
     return dict(value=round(n_tokens / el, 3), unit="tokens/s", cores=O.num_threads(),
-                kind="oracle",
+                kind="oracle", affinity_cores=len(os.sched_getaffinity(0)),
+                cpu_model=cpu_model(),
                 sample=f"first {n_tokens} of {cfg.T} tokens of {cfg.name}, whole layer "
                        f"(fp64 router, top-k, permutation, experts, combine) in {el:.1f} s")
+
+
+def cpu_model():
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_small(cfg):
+    """The oracle on the 512-token fp32 layer (E=8, top-2, d_ff=4096): its
+    first 64 tokens on one core, then all 512 on every core of the affinity
+    mask (tokens/s each)."""
+    from oracle import oracle as O
+    from sparse_mixture_experts_permute_amd.inputs import make_inputs
+    h = make_inputs(cfg)
+    out = {}
+    n_all = len(os.sched_getaffinity(0))
+    for label, n_tok, threads in (("one_core", 64, 1), ("all_cores", cfg.T, n_all)):
+        O.set_threads(threads)
+        t0 = time.perf_counter()
+        O.forward(h["x"][:n_tok], h["Wg"], h["W1"], h["W3"], h["W2"], cfg.k)
+        el = time.perf_counter() - t0
+        out[label] = dict(value=round(n_tok / el, 2), unit="tokens/s", cores=O.num_threads(),
+                          sample=f"first {n_tok} of {cfg.T} tokens, {el:.2f} s")
+    O.set_threads(n_all)
+    return out
+
+
+def small_runs(CONFIGS):
+    """The small layers, each step preceded by a 512 MB read (MALL flush)."""
+    import numpy as np
+    import torch
+
+    from sparse_mixture_experts_permute_amd import moe
+    from sparse_mixture_experts_permute_amd.inputs import make_inputs
+    out = []
+    names = ["small_fp32"] + [n for n in CONFIGS if n.startswith("granularity_")]
+    for name in names:
+        c2 = CONFIGS[name]
+        h = make_inputs(c2)
+        d2 = {n: moe.tensor_from_numpy(a) for n, a in h.items() if a is not None}
+        runs = [("method", {})]
+        if c2.dtype == "f32" and name != "small_fp32":
+            # the timed function of the granularity page, at its own shape
+            runs.append(("page_function_sigmoid_gates_sigmoid_glu",
+                         dict(gate_mode=moe.GATE_SIGMOID, activation=moe.ACT_GLU_SIGMOID)))
+        for label, kw in runs:
+            r2 = run_workload(c2, None, d2, 10, 3, flush_mb=512, min_warm_s=0.1, **kw)
+            a = algorithmic(c2, r2["counts"])
+            lt = r2["ms"] * 1e-3
+            peak = PEAK_BF16_TFLOPS if c2.dtype == "bf16" else PEAK_F32_TFLOPS
+            e = dict(workload=name, function=label, dtype=c2.dtype, T=c2.T, E=c2.E,
+                     d_ff=c2.d_ff, k=c2.k, ms_per_step=round(r2["ms"], 4),
+                     step_ms=r2["step_ms"], tokens_per_s=round(c2.T / lt, 1),
+                     mfma_frac=round(a["layer_flop"] / lt / (peak * 1e12), 4),
+                     mfma_peak_tflops=peak,
+                     hbm_frac=round(a["layer_bytes"] / lt / (PEAK_HBM_GBS * 1e9), 4),
+                     mall_flushed=True)
+            page = PAGE_NUMPY_MS.get((c2.E, c2.d_ff, c2.k))
+            if page and label != "method":
+                e["page_numpy_2core_ms"] = {"median": page[0], "fastest": page[1]}
+            log(f"{name} {label}: {r2['ms']:.4f} ms/step, mfma {e['mfma_frac']}, "
+                f"hbm {e['hbm_frac']}")
+            out.append(e)
+        del d2
+        torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -336,8 +431,13 @@ def main():
     dev = {n: moe.tensor_from_numpy(a) for n, a in host.items() if a is not None}
     torch.cuda.synchronize()
     log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
+    inout = args.layout == "inout"
+    head_dev = transposed(dev) if inout else dev
 
-    res = run_workload(cfg, host, dev, args.steps, args.warmup)
+    res = run_workload(cfg, host, head_dev, args.steps, args.warmup, inout=inout)
+    if inout:
+        del head_dev
+        torch.cuda.empty_cache()
     rl, layer_fr = roofline_for(cfg, res)
     ms = res["ms"]
     value = cfg.T / (ms * 1e-3)
@@ -374,20 +474,45 @@ def main():
                 e["hot_expert_share"] = round(float(r2["counts"][0] / r2["counts"].sum()), 4)
             log(f"{name}: {ms2:.4f} ms/step, {e['tokens_per_s']} tokens/s")
             extra.append(e)
-        # weight-only FP8 experts for the single-token decode step
-        c2 = CONFIGS["mixtral_decode_T1"]
-        r8 = run_fp8(c2, dev, 20, 3, 512)
-        hit = int(np.count_nonzero(r8["counts"]))
-        b8 = (hit * 3.0 * c2.d * c2.d_ff + 2.0 * c2.T * c2.d * 2 + c2.E * c2.d * 2
-              + 3 * c2.E * 4)
-        e = dict(workload="mixtral_decode_T1", weights="fp8_e4m3_per_expert_scale",
-                 T=c2.T, ms_per_step=round(r8["ms"], 4),
-                 tokens_per_s=round(c2.T / (r8["ms"] * 1e-3), 1),
-                 layer=dict(hbm_frac=round(b8 / (r8["ms"] * 1e-3) / (PEAK_HBM_GBS * 1e9), 4),
-                            algorithmic_bytes=b8, experts_hit=hit),
-                 mall_flushed=True)
-        log(f"mixtral_decode_T1 fp8 experts: {r8['ms']:.4f} ms/step")
-        extra.append(e)
+        # the headline shape and two decode steps with the other weight layout
+        other = not inout
+        odev = transposed(dev) if other else dev
+        for name, steps, flush in [(cfg.name, 10, 0), ("mixtral_decode_T1", 20, 512),
+                                   ("mixtral_decode_T128", 20, 512)]:
+            c2 = CONFIGS[name]
+            r2 = run_workload(c2, host, odev, steps, 2, flush_mb=flush, min_warm_s=0.25,
+                              inout=other)
+            rl2, lf2 = roofline_for(c2, r2)
+            e = dict(workload=name, weight_layout="in_out" if other else "out_in", T=c2.T,
+                     ms_per_step=round(r2["ms"], 4),
+                     tokens_per_s=round(c2.T / (r2["ms"] * 1e-3), 1), step_ms=r2["step_ms"],
+                     stage_ms={s_: round(float(v), 4) for s_, v in zip(moe.STAGES,
+                                                                        r2["stage_ms"])},
+                     roofline=rl2, layer=lf2, mall_flushed=bool(flush))
+            log(f"{name} ({e['weight_layout']} weights): {r2['ms']:.4f} ms/step")
+            extra.append(e)
+        if other:
+            del odev
+            torch.cuda.empty_cache()
+        # weight-only FP8 experts for decode steps (weights quantised once)
+        l8 = moe.MoELayerFP8(dev["Wg"], dev["W1"], dev["W3"], dev["W2"], cfg.k)
+        for name in ("mixtral_decode_T1", "mixtral_decode_T8", "mixtral_decode_T32",
+                     "mixtral_decode_T128"):
+            c2 = CONFIGS[name]
+            r8 = run_fp8(c2, dev, 20, 3, 512, layer=l8)
+            hit = int(np.count_nonzero(r8["counts"]))
+            b8 = (hit * 3.0 * c2.d * c2.d_ff + 2.0 * c2.T * c2.d * 2 + c2.E * c2.d * 2
+                  + 3 * c2.E * 4)
+            e = dict(workload=name, weights="fp8_e4m3_per_expert_scale",
+                     T=c2.T, ms_per_step=round(r8["ms"], 4),
+                     tokens_per_s=round(c2.T / (r8["ms"] * 1e-3), 1),
+                     layer=dict(hbm_frac=round(b8 / (r8["ms"] * 1e-3) / (PEAK_HBM_GBS * 1e9), 4),
+                                algorithmic_bytes=b8, experts_hit=hit),
+                     mall_flushed=True)
+            log(f"{name} fp8 experts: {r8['ms']:.4f} ms/step, hbm {e['layer']['hbm_frac']}")
+            extra.append(e)
+        del l8
+        torch.cuda.empty_cache()
 
     # the fine-grained layer with a shared expert (256 experts, top-8)
     if not args.no_extra and cfg.d == 4096 and cfg.E == 8:
@@ -437,10 +562,23 @@ def main():
             log(f"variant {label}: {r3['ms']:.3f} ms/step, kept {r3['kept']} of {c2.T * c2.k}")
             variants.append(v)
 
+    # the 512-wide layers the pages time: the small fp32 layer and the 7-config
+    # granularity sweep in fp32 and bf16 (weights fit the 256 MB MALL, so a
+    # 512 MB read evicts them before every step), and the pages' own function
+    # (sigmoid route weights, sigmoid-gated experts) at the sweep's shapes
+    small = []
+    if not args.no_extra:
+        del dev
+        torch.cuda.empty_cache()
+        small = small_runs(CONFIGS)
+        dev = None
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         cpu = cpu_baseline(cfg, host, args.cpu_tokens)
+        if not args.no_extra:
+            cpu["granularity_E8_k2_f32"] = cpu_small(CONFIGS["granularity_E8_k2_f32"])
         log(f"cpu baseline: {cpu}")
 
     out = {
@@ -467,8 +605,10 @@ def main():
         "expert_counts": {"min": int(counts.min()), "max": int(counts.max()),
                           "mean": float(counts.mean())},
         "cpu_baseline": cpu,
+        "weight_layout": "in_out" if inout else "out_in",
         "extra": extra,
         "variants": variants,
+        "small_layers": small,
         "wall_s_timed": round(res["wall_s"], 3),
         "timing": "HIP events on the stream the kernels run on: ms_per_step over back-to-back "
                   "moe_forward calls; step_ms (median, fastest) from the same steps again, "

@@ -271,8 +271,10 @@ int moe_quantize_fp8(const void *W, int E, long long n, int dtype, uint8_t *q, f
  *   opt: gate / activation / capacity variants as moe_forward_ex (NULL:
  *   defaults); no shared expert.
  *   workspace: moe_workspace_bytes(T, d, d_ff, E, k, 0, MOE_BF16) bytes.
- * A decode path: T <= 4, and d and d_ff multiples of 2048 up to 16384
- * (the weight-streaming kernels); MOE_EINVAL otherwise. */
+ * Decode-sized batches: up to four tokens with d and d_ff multiples of 2048
+ * up to 16384 (vector-ALU weight streaming), or batches averaging at most 96
+ * rows per expert with d and d_ff multiples of 128 (64-row matrix-core tiles
+ * that widen the codes to bf16 in LDS reads); MOE_EINVAL otherwise. */
 int moe_forward_fp8(const void *x, const void *Wg, const float *bias, const uint8_t *W1q,
                     const uint8_t *W3q, const uint8_t *W2q, const float *s1, const float *s3,
                     const float *s2, int T, int E, int k, int d, int d_ff,

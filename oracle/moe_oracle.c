@@ -685,3 +685,14 @@ int orc_num_threads(void)
     return 1;
 #endif
 }
+
+/* Threads for the oracle's later OpenMP regions (n >= 1; for timing it on a
+ * given number of host cores). */
+void orc_set_threads(int n)
+{
+#ifdef _OPENMP
+    omp_set_num_threads(n > 0 ? n : 1);
+#else
+    (void)n;
+#endif
+}

@@ -91,6 +91,8 @@ def _bind(path: str):
     L.orc_active_fraction.argtypes = [ctypes.c_int, ctypes.c_int]
     L.orc_active_fraction.restype = ctypes.c_double
     L.orc_num_threads.restype = ctypes.c_int
+    L.orc_set_threads.argtypes = [ctypes.c_int]
+    L.orc_set_threads.restype = None
     return L
 
 
@@ -357,3 +359,8 @@ def active_fraction(E, k) -> float:
 def num_threads() -> int:
     """Threads the oracle's OpenMP regions use."""
     return int(lib().orc_num_threads())
+
+
+def set_threads(n: int) -> None:
+    """Threads for the oracle's later OpenMP regions."""
+    lib().orc_set_threads(int(n))

@@ -333,7 +333,10 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
   const moe::GemmPlan plan =
       moe::gemm_plan(dtype, d, d_ff, d_ff_shared, ((long long)T * k + E - 1) / E);
   SkinnyPlan sk = skinny_plan(dtype, T, k, E, d, d_ff, d_ff_shared);
-  if (f8) sk.routed = sk.gemv = true;  // FP8 experts: weight streaming, checked by the caller
+  // FP8 experts: vector-ALU weight streaming up to four tokens, 64-row tiles
+  // beyond (the caller checked that one of them applies)
+  const bool f8_tiled = f8 && !(T <= 4 && moe::gemv_ok(d_ff, d) && moe::gemv_ok(d, d_ff));
+  if (f8) sk.routed = sk.gemv = !f8_tiled;
   if (tb) {
     // [K][N] weights: vector-ALU streaming up to four tokens, tiles beyond
     sk.gemv = sk.gemv && moe::gemv_t_ok(d_ff, d) && moe::gemv_t_ok(d, d_ff);
@@ -465,7 +468,13 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
         (e = moe::launch_gather(x, perm, offsets + E, P, k, d, (int)esize(dtype), Xp, s)))
       goto fail;
     MOE_MARK(3);
-    if (gather_fused && split) {
+    if (f8) {
+      if ((e = moe::launch_gemm_swiglu_fp8(o.activation, gather_fused ? x : Xp, f8->W1q, f8->W3q,
+                                           f8->s1, f8->s3, H, offsets, mt0, E, d_ff, d,
+                                           (P + 63) / 64 + E, s, gather_fused ? perm : nullptr, k,
+                                           gather_fused ? (long long)T * d * 2 : 0)))
+        goto fail;
+    } else if (gather_fused && split) {
       if ((e = moe::launch_gemm_swiglu(dtype, true, 256, o.activation, x, W1, W3, H, offsets, mt0,
                                        E, d_ff, d, P / 256 + E, s, mid, perm, k,
                                        (long long)T * d * 2, tb)) ||
@@ -492,7 +501,11 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
       goto fail;
     }
     MOE_MARK(4);
-    if (split) {
+    if (f8) {
+      if ((e = moe::launch_gemm_down_fp8(H, f8->W2q, f8->s2, Yp, offsets, mt1, E, d, d_ff,
+                                         (P + 63) / 64 + E, ksplit, plane, s, yp_bf16)))
+        goto fail;
+    } else if (split) {
       if ((e = moe::launch_gemm_down(dtype, true, 256, H, W2, Yp, offsets, mt0, E, d, d_ff,
                                      P / 256 + E, ksplit, plane, fx, s, mid, yp_bf16, tb)) ||
           (e = moe::launch_gemm_down(dtype, true, 64, H, W2, Yp, mid, mt1, E, d, d_ff,
@@ -610,8 +623,15 @@ int moe_forward_fp8(const void *x, const void *Wg, const float *bias, const uint
                     const float *s2, int T, int E, int k, int d, int d_ff,
                     const moe_options *opt, void *workspace, size_t workspace_bytes, void *y,
                     void *stream) {
-  if (T < 0 || T > 4) return MOE_EINVAL;
-  if (!moe::gemv_ok(d_ff, d) || !moe::gemv_ok(d, d_ff)) return MOE_EINVAL;
+  if (T < 0 || E < 1 || k < 1 || k > E) return MOE_EINVAL;
+  // up to four tokens: the weight-streaming kernels (d and d_ff multiples of
+  // 2048 up to 16384); beyond: 64-row tiles (at most 96 rows per expert on
+  // average, d and d_ff multiples of 128)
+  const bool streamed = T <= 4 && moe::gemv_ok(d_ff, d) && moe::gemv_ok(d, d_ff);
+  const long long rpe = ((long long)T * k + E - 1) / E;
+  const moe::GemmPlan plan = moe::gemm_plan(MOE_BF16, d, d_ff, 0, rpe);
+  const bool tiled = plan.dl1 && plan.dl2 && plan.bm1 == 64 && plan.bm2 == 64;
+  if (!streamed && !tiled) return MOE_EINVAL;
   if (T > 0 && (!s1 || !s3 || !s2)) return MOE_EINVAL;
   const Fp8Experts f8{W1q, W3q, W2q, s1, s3, s2};
   return forward_impl(x, Wg, bias, W1q, W3q, W2q, nullptr, nullptr, nullptr, 0, T, E, k, d, d_ff,

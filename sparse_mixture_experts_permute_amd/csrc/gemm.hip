@@ -444,20 +444,28 @@ __device__ __forceinline__ void dl_epilogue(const TA &ta, f32x16_v (&acc)[TM][TN
 // GATHER: A is the token matrix x (a_bytes bytes) and tile row s reads x row
 // gperm[s] / gk, so the grouped rows are never written out; each lane keeps
 // the byte offsets of its rows for the tile (one per A instruction).
-template <int BM, int BNB, bool SWIGLU, bool SPLIT, bool GATHER = false, bool TB = false>
+// W8: the weights are FP8 (E4M3) codes [N][K] with one scale per expert (sc1
+// for W1 or W2, sc3 for W3).  They reach LDS as codes (64 bytes of K per row
+// and slice; 16-byte chunk c of row r sits in slot c ^ ((r >> 2) & 3)); a
+// fragment read converts its 8 codes to bf16 exactly, and the epilogue
+// multiplies the sums by the expert's scales.  64-row tiles only.
+template <int BM, int BNB, bool SWIGLU, bool SPLIT, bool GATHER = false, bool TB = false,
+          bool W8 = false>
 __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
     const bf16_t *__restrict__ A, const bf16_t *__restrict__ B1, const bf16_t *__restrict__ B3,
     void *__restrict__ C, const int32_t *__restrict__ seg_off,
     const int32_t *__restrict__ seg_end, const int32_t *__restrict__ mtile_off, int G, int N,
     int K, size_t plane, int act, int32_t *__restrict__ fix_cnt, f32x4_v *__restrict__ fix_part,
-    int part_cap, const int32_t *__restrict__ gperm, int gk, uint32_t a_bytes) {
+    int part_cap, const int32_t *__restrict__ gperm, int gk, uint32_t a_bytes,
+    const float *__restrict__ sc1, const float *__restrict__ sc3) {
   constexpr int WM = 2, WN = 2;
   constexpr int TM = BM / WM / 32, TN = BNB / WN / 32;
-  constexpr int ROWS = BM + BNB;          // tile rows per stage (A then B)
-  constexpr int STAGE_U4 = ROWS * 8;      // uint4 per stage
+  // A rows of 128 bytes, then B rows of 128 bytes (64 for FP8 codes)
+  constexpr int STAGE_U4 = BM * 8 + BNB * (W8 ? 4 : 8);  // uint4 per stage
   static_assert(!SWIGLU || (TN % 2 == 0), "SwiGLU pairs W1/W3 blocks inside a wave");
   static_assert(BM % 32 == 0 && BNB % 32 == 0, "rows per stage must split over 4 waves");
   static_assert(!TB || BNB == 256, "the [K][N] weight tile is two 128-column halves");
+  static_assert(!W8 || (BM == 64 && !TB && !SPLIT), "FP8 weights: 64-row tiles of [N][K] codes");
 
   __shared__ uint4 st0[STAGE_U4];
   __shared__ uint4 st1[STAGE_U4];
@@ -469,7 +477,8 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = lane_id();
   const int wm = wave / WN, wn = wave % WN;
 
-  constexpr int IA = BM / 32, IB = BNB / 32;  // LDS-DMA instructions per wave per stage
+  // LDS-DMA instructions per wave per stage (an FP8 instruction moves 16 B rows)
+  constexpr int IA = BM / 32, IB = BNB / (W8 ? 64 : 32);
   constexpr int PER = IA + IB;
   // K planes (down projection of small batches): blockIdx.y takes one of
   // gridDim.y equal K ranges, its fp32 partial goes to output plane blockIdx.y
@@ -500,10 +509,17 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
   const uint32_t tbl = TB ? (uint32_t)(lane >> 4) * (uint32_t)N * 2u +
                                 (uint32_t)(((lane & 15) ^ ((lane >> 4) << 2)) * 16)
                           : 0u;
+  // W8: an instruction moves 16 rows of 64 code bytes; lane l takes row l / 4
+  // and LDS slot l % 4, which holds chunk (l % 4) ^ (l / 16) of its row (the
+  // row's (r >> 2) & 3 is l / 16 for every instruction)
+  const uint32_t w8l =
+      W8 ? (uint32_t)(lane >> 2) * (uint32_t)K + (uint32_t)(((lane & 3) ^ (lane >> 4)) * 16) : 0u;
   struct TileAddr {
     __amdgpu_buffer_rsrc_t ra, r1, r3;
     uint32_t lc0, lc1;
     uint32_t tbl;  // TB: the lane's byte offset inside a [K][N] weight instruction
+    uint32_t w8l;  // W8: the lane's byte offset inside an FP8 weight instruction
+    int e;         // the unit's expert
     uint32_t ga[GATHER ? IA : 1];  // GATHER: byte offset in x of each A instruction's row
     int row0, rows, n0;
     int nk;    // K slices of this unit (even)
@@ -552,9 +568,12 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
     }
     // [N][K] weights: the unit's K range starts kb bytes into every row;
     // [K][N] weights (TB): it starts kb / 2 rows of N elements into the matrix
-    const uint32_t wkb = TB ? (kb / 2) * (uint32_t)N * 2u : kb;
-    const size_t eoff = (size_t)e * N * rowb + wkb;
-    const uint32_t wbytes = (uint32_t)N * rowb - wkb;
+    // FP8 codes (W8): one byte per element, so kb / 2 bytes into every row
+    const uint32_t wkb = TB ? (kb / 2) * (uint32_t)N * 2u : W8 ? kb / 2 : kb;
+    const uint32_t wrow = W8 ? (uint32_t)K : rowb;  // bytes per weight row
+    const size_t eoff = (size_t)e * N * wrow + wkb;
+    const uint32_t wbytes = (uint32_t)N * wrow - wkb;
+    ta.e = e;
     ta.r1 = make_rsrc(reinterpret_cast<const char *>(B1) + eoff, wbytes);
     ta.r3 = SWIGLU ? make_rsrc(reinterpret_cast<const char *>(B3) + eoff, wbytes) : ta.r1;
     // per-tile copies of the lane offsets: keeps the compiler from hoisting
@@ -562,11 +581,12 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
     ta.lc0 = lc0;
     ta.lc1 = lc1;
     ta.tbl = tbl;
-    asm volatile("" : "+v"(ta.lc0), "+v"(ta.lc1), "+v"(ta.tbl));
+    ta.w8l = w8l;
+    asm volatile("" : "+v"(ta.lc0), "+v"(ta.lc1), "+v"(ta.tbl), "+v"(ta.w8l));
   };
   // B block parity: block (wave*IB + j)/4 is odd (a W3 block) iff (j/4) is odd,
   // because IB is a multiple of 8
-  static_assert(!SWIGLU || IB % 8 == 0, "W1/W3 choice must be fixed per instruction");
+  static_assert(W8 || !SWIGLU || IB % 8 == 0, "W1/W3 choice must be fixed per instruction");
   static_assert(IA % 2 == 0 && IB % 2 == 0, "chunk swizzle parity per instruction");
   // LDS-DMA instructions j0 <= j < j1 of one slice (A blocks first, then B)
   auto issue_part = [&](const TileAddr &ta, uint4 *stage, int kt, int j0, int j1) {
@@ -581,6 +601,29 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
           buffer_to_lds16(ta.ra, ((j & 1) ? ta.lc1 : ta.lc0) + u, stage + (wave * IA + j) * 64);
         }
       }
+    if constexpr (W8) {
+      // instruction q = wave * IB + j fills B rows 16 q .. 16 q + 15 (code bytes
+      // 64 kt .. 64 kt + 63 of their weight rows), all in one 32-row block
+      const uint32_t ko8 = (uint32_t)kt * 64u;
+#pragma unroll
+      for (int j = 0; j < IB; ++j) {
+        if (IA + j >= j0 && IA + j < j1) {
+          const int q = wave * IB + j, br = 16 * q;
+          int col;
+          bool w3 = false;
+          if (SWIGLU) {
+            const int rb = br / 32, wnb = rb / TN, jj = rb % TN;
+            col = ta.n0 + wnb * (TN / 2) * 32 + (jj / 2) * 32 + (br % 32);
+            w3 = jj & 1;
+          } else {
+            col = ta.n0 + br;
+          }
+          buffer_to_lds16<true>(w3 ? ta.r3 : ta.r1, ta.w8l + (uint32_t)col * (uint32_t)K + ko8,
+                                stage + BM * 8 + q * 64);
+        }
+      }
+      return;
+    }
     if constexpr (TB) {
       // B stage: [half][k-row 0..63][128 columns]; half = matrix (W1, W3) for
       // SwiGLU, else columns n0 + 128 * half.  Instruction q = wave * IB + j
@@ -633,11 +676,18 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
   // those four k-rows, which is what a 32x32x16 MFMA lane needs (column l % 32,
   // K values 8 * (l / 32) + 0..3; the next read gives + 4..7).
   int tbo[4];
+  int w8o[4];  // W8: byte offset of the lane's 8 codes of K step ks in its row
   auto set_frag_addr = [&](int ln) {
     frow = ln & 31;
     const int xf = (frow >> 1) & 7;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) cidx[ks] = (ks * 2 + (ln >> 5)) ^ xf;
+    if constexpr (W8) {
+      const int f = ((ln & 31) >> 2) & 3;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        w8o[ks] = BM * 128 + (ln & 31) * 64 + 16 * (ks ^ f) + 8 * ((ln >> 5) & 1);
+    }
     if constexpr (TB) {
       const int g = (ln >> 4) & 3, i = ln & 15, r = i >> 2;
 #pragma unroll
@@ -651,7 +701,19 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
   auto rd = [&](const uint4 *stage, int ks, uint4 (&af)[TM], uint4 (&bf)[TN]) {
 #pragma unroll
     for (int a = 0; a < TM; ++a) af[a] = stage[((wm * TM + a) * 32 + frow) * 8 + cidx[ks]];
-    if constexpr (TB) {
+    if constexpr (W8) {
+      const char *sb = (const char *)stage;
+#pragma unroll
+      for (int b = 0; b < TN; ++b) {
+        const uint2 q = *reinterpret_cast<const uint2 *>(sb + w8o[ks] + (wn * TN + b) * 32 * 64);
+        // E4M3 -> bf16 is exact; gfx950 converts two codes at a time
+        bf[b] = make_uint4(
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.x, 1.f, false)),
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.x, 1.f, true)),
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.y, 1.f, false)),
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.y, 1.f, true)));
+      }
+    } else if constexpr (TB) {
       typedef __attribute__((address_space(3))) bf16x4_v lds_bf16x4;
       const __attribute__((address_space(3))) char *sb =
           (const __attribute__((address_space(3))) char *)stage;
@@ -844,6 +906,16 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
     }
     bool store = true;
     if constexpr (SPLIT) store = cur.part < 0 || fixup(cur);
+    if constexpr (W8) {
+      // the experts' scales: W1 (or W2) blocks and W3 blocks
+      const float s1v = sc1[cur.e], s3v = SWIGLU ? sc3[cur.e] : s1v;
+#pragma unroll
+      for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int b = 0; b < TN; ++b)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[a][b][i] *= (SWIGLU && (b & 1)) ? s3v : s1v;
+    }
     if (store) dl_epilogue<BM, BNB, SWIGLU>(cur, acc, C, N, plane, act, wave, lane_t);
     if (!more) break;
     VM_WAIT(0);  // both slices (and the epilogue's stores) done
@@ -877,21 +949,24 @@ int resident_wgs(int bm) {
   return cus[dev] * (bm == 64 ? 2 : 1);
 }
 
-template <int BM, int BNB, bool SWIGLU, bool SPLIT = false, bool GATHER = false, bool TB = false>
+template <int BM, int BNB, bool SWIGLU, bool SPLIT = false, bool GATHER = false, bool TB = false,
+          bool W8 = false>
 hipError_t launch_dl(const void *A, const void *B1, const void *B3, void *C,
                      const int32_t *seg_off, const int32_t *seg_end, const int32_t *mtile_off,
                      int G, int N, int K, int ksplit, size_t plane, int act, const FixScratch &fx,
                      hipStream_t s, const int32_t *gperm = nullptr, int gk = 1,
-                     uint32_t a_bytes = 0) {
+                     uint32_t a_bytes = 0, const float *sc1 = nullptr,
+                     const float *sc3 = nullptr) {
   // persistent grid: what stays resident, a multiple of the XCD count
   const int gx = (resident_wgs(BM) / ksplit + NUM_XCD - 1) / NUM_XCD * NUM_XCD;
   const size_t cap = fx.part ? fx.part_bytes / ((size_t)BM * BNB * 4) : 0;
-  hipLaunchKernelGGL((grouped_gemm_dl_kernel<BM, BNB, SWIGLU, SPLIT, GATHER, TB>), dim3(gx, ksplit),
+  hipLaunchKernelGGL((grouped_gemm_dl_kernel<BM, BNB, SWIGLU, SPLIT, GATHER, TB, W8>),
+                     dim3(gx, ksplit),
                      dim3(GM_THREADS), 0, s, (const bf16_t *)A, (const bf16_t *)B1,
                      (const bf16_t *)B3, C, seg_off, seg_end ? seg_end : seg_off + 1, mtile_off, G,
                      N, K, plane, act, fx.cnt, (f32x4_v *)fx.part,
                      (int)(cap < (size_t)FIX_SLOTS * 16 ? cap : (size_t)FIX_SLOTS * 16), gperm,
-                     gk, a_bytes);
+                     gk, a_bytes, sc1, sc3);
   return hipGetLastError();
 }
 
@@ -1004,6 +1079,39 @@ hipError_t launch_gemm_swiglu(int dtype, bool dl, int bm, int act, const void *A
                                   max_mtiles, s, seg_end, gperm, gk, a_bytes)
             : gemm_swiglu_t<false>(dtype, dl, bm, act, A, W1, W3, H, seg_off, mtile_off, G, N, K,
                                    max_mtiles, s, seg_end, gperm, gk, a_bytes);
+}
+
+hipError_t launch_gemm_swiglu_fp8(int act, const void *A, const uint8_t *W1q, const uint8_t *W3q,
+                                  const float *s1, const float *s3, void *H,
+                                  const int32_t *seg_off, const int32_t *mtile_off, int G, int N,
+                                  int K, int max_mtiles, hipStream_t s, const int32_t *gperm,
+                                  int gk, long long a_bytes) {
+  if (max_mtiles <= 0) return hipSuccess;
+  const FixScratch none{nullptr, nullptr, 0};
+  if (K % 128) return hipErrorInvalidValue;
+  if (gperm) {
+    if (!gemm_gather_ok(1, true, 64, a_bytes)) return hipErrorInvalidValue;
+    return launch_dl<64, 256, true, false, true, false, true>(A, W1q, W3q, H, seg_off, nullptr,
+                                                              mtile_off, G, N, K, 1, 0, act, none,
+                                                              s, gperm, gk, (uint32_t)a_bytes, s1,
+                                                              s3);
+  }
+  return launch_dl<64, 256, true, false, false, false, true>(A, W1q, W3q, H, seg_off, nullptr,
+                                                             mtile_off, G, N, K, 1, 0, act, none,
+                                                             s, nullptr, 1, 0, s1, s3);
+}
+
+hipError_t launch_gemm_down_fp8(const void *A, const uint8_t *W2q, const float *s2, void *Y,
+                                const int32_t *seg_off, const int32_t *mtile_off, int G, int N,
+                                int K, int max_mtiles, int ksplit, size_t plane, hipStream_t s,
+                                bool ybf16) {
+  if (max_mtiles <= 0) return hipSuccess;
+  if (K % (128 * ksplit) || (ybf16 && ksplit != 1)) return hipErrorInvalidValue;
+  const FixScratch none{nullptr, nullptr, 0};
+  return launch_dl<64, 256, false, false, false, false, true>(A, W2q, nullptr, Y, seg_off, nullptr,
+                                                              mtile_off, G, N, K, ksplit, plane,
+                                                              ybf16 ? 1 : 0, none, s, nullptr, 1,
+                                                              0, s2, nullptr);
 }
 
 hipError_t launch_gemm_down(int dtype, bool dl, int bm, const void *A, const void *W2, void *Y,

@@ -206,7 +206,7 @@ __device__ __forceinline__ float dot8_bf16(const uint4 &a, const uint4 &b, float
 }
 
 // FP8 (E4M3) weights: 8 bytes (8 weights) per lane per instruction; the
-// conversion to fp32 is exact, so the products are those of the dequantized
+// conversion to bf16 is exact, so the products are those of the dequantized
 // weights up to the per-expert scale, applied to the reduced sums.
 typedef unsigned int gv_u2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint2 ldg8_stream(const uint8_t *p) {
@@ -219,18 +219,17 @@ __device__ __forceinline__ float gv_dot(const uint4 &a, const uint4 &b, float ac
   return dot8_bf16(a, b, acc);
 }
 __device__ __forceinline__ float gv_dot(const uint4 &a, const uint2 &b, float acc) {
-  // fp32 products: the pairwise E4M3 -> fp32 conversion and fp32 FMAs keep up
-  // with the byte stream better than E4M3 -> bf16 conversions feeding dot2
-  typedef float f2 __attribute__((ext_vector_type(2)));
-  const uint32_t av[4] = {a.x, a.y, a.z, a.w};
-  const uint32_t bw[2] = {b.x, b.y};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const f2 w = (i & 1) ? __builtin_amdgcn_cvt_pk_f32_fp8(bw[i >> 1], true)
-                         : __builtin_amdgcn_cvt_pk_f32_fp8(bw[i >> 1], false);
-    acc = fmaf(__uint_as_float(av[i] << 16), w.x, acc);          // even element
-    acc = fmaf(__uint_as_float(av[i] & 0xFFFF0000u), w.y, acc);  // odd element
-  }
+  // E4M3 -> bf16 is exact (3 mantissa bits into 7), two codes per conversion
+  // (gfx950's scaled conversion with scale 1), then the same dot2 as the bf16
+  // weights: four conversions and four dot2 per 8 weights
+  const bf16x2_v w01 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b.x, 1.0f, false);
+  const bf16x2_v w23 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b.x, 1.0f, true);
+  const bf16x2_v w45 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b.y, 1.0f, false);
+  const bf16x2_v w67 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b.y, 1.0f, true);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, a.x), w01, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, a.y), w23, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, a.z), w45, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, a.w), w67, acc, false);
   return acc;
 }
 

@@ -132,6 +132,20 @@ hipError_t launch_gemm_down(int dtype, bool dl, int bm, const void *A, const voi
                             hipStream_t s, const int32_t *seg_end = nullptr, bool ybf16 = false,
                             bool tb = false);
 
+// The 64-row tiled GEMMs on FP8 (E4M3) expert weights [N][K] with per-expert
+// scales (s1 / s3 / s2 [E]); arguments otherwise as launch_gemm_swiglu /
+// launch_gemm_down (K a multiple of 128; the down projection's K planes each
+// a multiple of 128).
+hipError_t launch_gemm_swiglu_fp8(int act, const void *A, const uint8_t *W1q, const uint8_t *W3q,
+                                  const float *s1, const float *s3, void *H,
+                                  const int32_t *seg_off, const int32_t *mtile_off, int G, int N,
+                                  int K, int max_mtiles, hipStream_t s, const int32_t *gperm,
+                                  int gk, long long a_bytes);
+hipError_t launch_gemm_down_fp8(const void *A, const uint8_t *W2q, const float *s2, void *Y,
+                                const int32_t *seg_off, const int32_t *mtile_off, int G, int N,
+                                int K, int max_mtiles, int ksplit, size_t plane, hipStream_t s,
+                                bool ybf16);
+
 // Weight-streaming grouped GEMMs for few rows per expert (bf16 only).
 bool skinny_ok(int N, int K);
 // vector-ALU weight streaming for experts holding at most `rows` (<= 4) rows

@@ -123,3 +123,68 @@ def test_forward_fp8_mixtral_T1_sampled():
     err = rel_l2(f64(moe.tensor_to_numpy(y))[0], ref)
     say(f"mixtral decode T=1 fp8: experts {idx.tolist()}, rel-L2 {err:.3e}")
     assert err <= 1e-2
+
+
+# more than four tokens: 64-row matrix-core tiles that widen the codes to bf16
+@pytest.mark.parametrize("T,E,k,d,dff,gm,cap", [
+    (8, 8, 2, 2048, 2048, 0, None), (32, 8, 2, 1024, 1536, 0, None),
+    (128, 8, 2, 512, 1024, 1, None), (40, 16, 4, 256, 512, 3, None),
+    (64, 8, 2, 256, 14336, 0, None),  # every down-projection tile split into K planes
+    (100, 4, 1, 384, 640, 2, 20), (5, 8, 2, 256, 384, 0, None), (300, 32, 2, 128, 256, 0, None)])
+def test_forward_fp8_tiled(T, E, k, d, dff, gm, cap):
+    cfg, h, dev = fp8_case(T, d, E, dff, k, seed=T + E + d, skew=1.5 if cap else 0.0)
+    say(f"forward_fp8 tiled T={T} E={E} k={k} d={d} d_ff={dff} gate={gm} capacity={cap}")
+    L = moe.MoELayerFP8(dev["Wg"], dev["W1"], dev["W3"], dev["W2"], k, dev["bias"],
+                        gate_mode=gm, capacity=-1 if cap is None else cap)
+    y = L(dev["x"])
+    torch.cuda.synchronize()
+    it = {n: v.cpu().numpy() for n, v in L.intermediates(T).items()}
+    lg = it["logits"].astype(np.float64)
+    deq = {}
+    for n, qn, sn in (("W1", "W1q", "s1"), ("W3", "W3q", "s3"), ("W2", "W2q", "s2")):
+        q_ref, s_ref = O.quantize_fp8(h[n])
+        np.testing.assert_array_equal(getattr(L, sn).cpu().numpy(), s_ref)
+        np.testing.assert_array_equal(getattr(L, qn).cpu().numpy(), q_ref)
+        deq[n] = O.dequant_fp8(q_ref, s_ref)
+    ref = O.forward(f64(h["x"]), f64(h["Wg"]), deq["W1"], deq["W3"], deq["W2"], k,
+                    bias=h["bias"], logits_in=lg, gate_mode=gm, capacity=cap)
+    if gm == O.GATE_ENTROPY:
+        assert np.min(np.abs(O.entropy(lg) - O.ENTROPY_THRESHOLD)) > 1e-4
+    np.testing.assert_array_equal(it["idx"], ref["idx"])
+    np.testing.assert_array_equal(it["inv"], ref["inv"])
+    err = rel_l2(f64(moe.tensor_to_numpy(y)), ref["y"])
+    say(f"forward_fp8 tiled: rel-L2 {err:.3e} against the dequantised oracle (bar 1e-2)")
+    assert err <= 1e-2
+
+
+@pytest.mark.parametrize("name", ["mixtral_decode_T8", "mixtral_decode_T128"])
+def test_forward_fp8_mixtral_sampled(name):
+    """Mixtral-shaped decode batches with FP8 experts: sampled tokens against
+    the oracle on the dequantised weights of each expert they reach (one
+    expert's matrices at a time, so that the fp64 copies stay small)."""
+    cfg = CONFIGS[name]
+    h = make_inputs(cfg)
+    dev = {n: moe.tensor_from_numpy(a) for n, a in h.items() if a is not None}
+    L = moe.MoELayerFP8(dev["Wg"], dev["W1"], dev["W3"], dev["W2"], cfg.k)
+    y = L(dev["x"])
+    torch.cuda.synchronize()
+    it = {n: v.cpu().numpy() for n, v in L.intermediates(cfg.T).items()}
+    rows = sorted({0, cfg.T - 1} | set(np.random.default_rng(5).choice(cfg.T, 6, replace=False)))
+    idx, gate = it["idx"][rows], it["gate"][rows].astype(np.float64)
+    ref = np.zeros((len(rows), cfg.d))
+    x64 = f64(h["x"])
+    for e in sorted(set(idx.ravel().tolist())):
+        parts = {}
+        for n, qn, sn in (("W1", "W1q", "s1"), ("W3", "W3q", "s3"), ("W2", "W2q", "s2")):
+            q_ref, s_ref = O.quantize_fp8(h[n][e:e + 1])
+            np.testing.assert_array_equal(getattr(L, qn)[e].cpu().numpy(), q_ref[0])
+            assert getattr(L, sn)[e].item() == s_ref[0]
+            parts[n] = O.dequant_fp8(q_ref, s_ref)
+        for i, t in enumerate(rows):
+            for j in range(cfg.k):
+                if idx[i, j] == e:
+                    ref[i] += gate[i, j] * O.expert_row(x64, t, parts["W1"], parts["W3"],
+                                                        parts["W2"], 0)
+    err = rel_l2(f64(moe.tensor_to_numpy(y))[rows], ref)
+    say(f"{name} fp8: {len(rows)} sampled tokens, rel-L2 {err:.3e}")
+    assert err <= 1e-2
