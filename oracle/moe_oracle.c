@@ -47,6 +47,8 @@
  *   orc_capacity      pinned (the two worked numbers of [SMoE] 2.4)
  *   orc_entropy       pinned (closed forms; torch softmax + entr)
  *   orc_route_entropy pinned (per-token torch.topk of the tempered softmax)
+ *   orc_route_entropy_batch pinned (torch.topk of the tempered softmax with
+ *                     the batch's largest k; brute force on tiny batches)
  *   orc_fp8_decode    pinned (all 256 codes against torch.float8_e4m3fn)
  *   orc_fp8_encode    pinned (torch's float8_e4m3fn cast; brute-force nearest)
  *   orc_quantize_fp8  pinned (per-expert amax by numpy; round trip bounds)
@@ -265,6 +267,48 @@ int orc_route_entropy(const double *logits, long T, int E, int k, double tau,
     return 0;
 }
 
+/* The routing of [OVW 4.1] as its listing prints it: the per-token k_t as
+ * above (k when H > threshold, else k - 1), then one k for the whole batch,
+ * the largest k_t, so that every token keeps its top max_t k_t experts by
+ * probability (descending, ties to the lower index) with the probabilities as
+ * gates; the slot past that k (when it is k - 1) holds idx -1 and gate 0 for
+ * every token.  Returns the batch's k, or -1 for k < 2 or k > E. */
+int orc_route_entropy_batch(const double *logits, long T, int E, int k, double tau,
+                            double threshold, int32_t *idx, double *gate)
+{
+    if (k < 2 || k > E)
+        return -1;
+    double *H = malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+    orc_entropy(logits, T, E, tau, H);
+    int kb = k - 1;
+    for (long t = 0; t < T; ++t)
+        if (H[t] > threshold)
+            kb = k;
+    orc_topk(logits, T, E, k, idx);
+    for (long t = 0; t < T; ++t) {
+        const double *l = logits + (size_t)t * E;
+        double m = l[0];
+        for (int e = 1; e < E; ++e)
+            if (l[e] > m)
+                m = l[e];
+        double z = 0.0;
+        for (int e = 0; e < E; ++e)
+            z += exp((l[e] - m) / tau);
+        for (int j = 0; j < k; ++j) {
+            size_t q = (size_t)t * k + j;
+            if (j < kb) {
+                const double w = exp((l[idx[q]] - m) / tau);
+                gate[q] = w / z;
+            } else {
+                gate[q] = 0.0;
+                idx[q] = -1; /* the slot past the batch's k */
+            }
+        }
+    }
+    free(H);
+    return kb;
+}
+
 /* FP8 weights for the experts [SMoE 5.3: quantise only the expert weights,
  * keep the router in high precision, and give every expert its own scale so
  * that no error crosses experts].  Format: OCP FP8 E4M3 ("E4M3FN"): sign,
@@ -454,8 +498,8 @@ void orc_swiglu_row(const void *x, int dt, long t, int d, const void *W1,
  *   Yp[s] = FFN_e(x_t) with p = perm[s], t = p / k, e = idx[p];
  *   y[t]  = sum_{j<k, pair kept} gate[t][j] * Yp[inv[t*k+j]]   (j ascending)
  *           + shared FFN(x_t) with weight 1 when Ws1 != NULL [CH10 10.5].
- * gate_mode (orc_gate_mode; 3: orc_route_entropy with the page's tau and
- * threshold), act (swiglu) and capacity (orc_keep; a value
+ * gate_mode (orc_gate_mode; 3: orc_route_entropy, 4: orc_route_entropy_batch,
+ * both with the page's tau and threshold), act (swiglu) and capacity (orc_keep; a value
  * >= T*k drops nothing) select the variants; only kept pairs are placed, so
  * counts/offsets/perm cover the kept pairs and inv[p] = -1 for a dropped one.
  * Routing comes from `logits_in` when given (e.g. another implementation's
@@ -485,9 +529,14 @@ int orc_forward_ex(const void *x, const void *Wg, const float *bias,
     int32_t *perm = malloc(sizeof(int32_t) * (size_t)(P > 0 ? P : 1));
     int32_t *inv = malloc(sizeof(int32_t) * (size_t)(P > 0 ? P : 1));
     int32_t *keep = malloc(sizeof(int32_t) * (size_t)(P > 0 ? P : 1));
-    if (gate_mode == 3) {
-        if (orc_route_entropy(logits, T, E, k, ORC_ENTROPY_TAU, ORC_ENTROPY_THRESHOLD,
-                              idx, gate) != 0) {
+    if (gate_mode == 3 || gate_mode == 4) {
+        const int rc = gate_mode == 3
+                           ? orc_route_entropy(logits, T, E, k, ORC_ENTROPY_TAU,
+                                               ORC_ENTROPY_THRESHOLD, idx, gate)
+                           : (orc_route_entropy_batch(logits, T, E, k, ORC_ENTROPY_TAU,
+                                                      ORC_ENTROPY_THRESHOLD, idx, gate) < 0
+                                  ? -1 : 0);
+        if (rc != 0) {
             free(logits); free(idx); free(gate); free(counts); free(offsets);
             free(perm); free(inv); free(keep);
             return -1;

@@ -23,6 +23,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 F32, BF16, F64 = 0, 1, 2
 # gate variants (orc_gate_mode) and expert activations (swiglu in moe_oracle.c)
 GATE_SOFTMAX_TOPK, GATE_SOFTMAX_ALL, GATE_SIGMOID, GATE_ENTROPY = 0, 1, 2, 3
+GATE_ENTROPY_BATCH = 4  # the entropy-aware routing with the batch's largest k
 # the entropy-aware routing's temperature and entropy threshold as printed
 ENTROPY_TAU, ENTROPY_THRESHOLD = 0.1, 0.8
 ACT_SWIGLU, ACT_GLU_SIGMOID = 0, 1
@@ -72,6 +73,8 @@ def _bind(path: str):
     L.orc_route_entropy.argtypes = [f64p, ctypes.c_long, ctypes.c_int, ctypes.c_int,
                                     ctypes.c_double, ctypes.c_double, i32p, f64p]
     L.orc_route_entropy.restype = ctypes.c_int
+    L.orc_route_entropy_batch.argtypes = L.orc_route_entropy.argtypes
+    L.orc_route_entropy_batch.restype = ctypes.c_int
     L.orc_forward_ex.argtypes = ([vp, vp, f32p, vp, vp, vp, vp, vp, vp, ctypes.c_int,
                                   ctypes.c_long, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -196,6 +199,22 @@ def route_entropy(lg, k, tau=ENTROPY_TAU, threshold=ENTROPY_THRESHOLD):
     return idx, g
 
 
+def route_entropy_batch(lg, k, tau=ENTROPY_TAU, threshold=ENTROPY_THRESHOLD):
+    """(idx, gate, kb) of the entropy-aware routing with one k for the batch:
+    kb = the largest per-token k (k where the entropy is above the threshold,
+    else k - 1); every token keeps its top kb experts, and the slot past kb
+    holds idx -1, gate 0."""
+    lg = _c(lg, np.float64)
+    T, E = lg.shape
+    idx = np.empty((T, k), np.int32)
+    g = np.empty((T, k), np.float64)
+    kb = lib().orc_route_entropy_batch(_ptr(lg), T, E, k, float(tau), float(threshold),
+                                       _ptr(idx), _ptr(g))
+    if kb < 0:
+        raise ValueError("entropy-aware routing needs 2 <= k <= E")
+    return idx, g, kb
+
+
 def fp8_decode(codes):
     """E4M3 (OCP, 'FN') value of each uint8 code (fp64)."""
     return np.array([lib().orc_fp8_decode(int(c)) for c in np.asarray(codes).reshape(-1)],
@@ -248,6 +267,8 @@ def route(x, Wg, k, bias=None, logits_in=None, gate_mode_=GATE_SOFTMAX_TOPK):
     lg = logits(x, Wg, bias) if logits_in is None else _c(logits_in, np.float64)
     if gate_mode_ == GATE_ENTROPY:
         return (lg,) + route_entropy(lg, k)
+    if gate_mode_ == GATE_ENTROPY_BATCH:
+        return (lg,) + route_entropy_batch(lg, k)[:2]
     idx = topk(lg, k)
     return lg, idx, gate_mode(lg, idx, gate_mode_)
 

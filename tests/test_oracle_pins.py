@@ -363,6 +363,59 @@ def check_entropy_routing():
     np.testing.assert_allclose(out["y"], ref, rtol=1e-12, atol=1e-14)
 
 
+def check_entropy_batch_routing():
+    # "Mixtral 8x7B model architecture" section 4.1 as its listing prints it:
+    # a per-token k (3 above the entropy threshold, else 2), then torch.topk of
+    # the tempered softmax with the batch's largest k for every token
+    tau = O.ENTROPY_TAU
+    rng = np.random.default_rng(35)
+    for E, k, scale, T in ((8, 3, 0.15, 200), (16, 3, 0.3, 64), (5, 2, 0.1, 90)):
+        lg = rng.standard_normal((T, E)) * scale
+        probs = torch.softmax(torch.from_numpy(lg) / tau, dim=-1)
+        H = torch.special.entr(probs).sum(dim=-1).numpy()
+        for sub in (slice(0, T), np.nonzero(H <= O.ENTROPY_THRESHOLD)[0][:20]):
+            l2 = lg[sub]
+            Hs = H[sub]
+            kmax = int(np.max(np.where(Hs > O.ENTROPY_THRESHOLD, k, k - 1)))
+            idx, gate, kb = O.route_entropy_batch(l2, k)
+            assert kb == kmax
+            v, ix = torch.topk(probs[sub], kmax, dim=-1)
+            np.testing.assert_array_equal(idx[:, :kmax], ix.numpy())
+            np.testing.assert_allclose(gate[:, :kmax], v.numpy(), rtol=1e-12, atol=1e-15)
+            assert np.all(idx[:, kmax:] == -1) and np.all(gate[:, kmax:] == 0.0)
+            if kmax == k - 1:
+                # no token above the threshold: the same as the per-token rule
+                i1, g1 = O.route_entropy(l2, k)
+                np.testing.assert_array_equal(idx, i1)
+                np.testing.assert_array_equal(gate, g1)
+    # brute force on tiny batches: every token's kb best experts by probability,
+    # ties to the lower index (a full stable sort)
+    for T, E, k in ((1, 4, 2), (3, 6, 3), (7, 3, 2)):
+        lg = np.round(rng.standard_normal((T, E)) * 0.2, 1)  # ties happen
+        idx, gate, kb = O.route_entropy_batch(lg, k)
+        for t in range(T):
+            m = lg[t].max()
+            w = np.exp((lg[t] - m) / tau)
+            p = w / w.sum()
+            order = sorted(range(E), key=lambda e: (-lg[t, e], e))
+            assert list(idx[t, :kb]) == order[:kb]
+            np.testing.assert_allclose(gate[t, :kb], p[order[:kb]], rtol=1e-12)
+    # the layer with the batch rule: every token's slots as routed, empty ones add nothing
+    inp = tiny(30, 24, 6, 16, 3, "f32", seed=45)
+    lg = rng.standard_normal((30, 6)) * 0.05  # flat scores: high entropy somewhere
+    out = O.forward(inp["x"], inp["Wg"], inp["W1"], inp["W3"], inp["W2"], 3, logits_in=lg,
+                    gate_mode=O.GATE_ENTROPY_BATCH)
+    idx, gate, kb = O.route_entropy_batch(lg, 3)
+    np.testing.assert_array_equal(out["idx"], idx)
+    ref = np.zeros((30, 24))
+    for t in range(30):
+        for j in range(3):
+            if idx[t, j] >= 0:
+                ref[t] += gate[t, j] * O.expert_row(inp["x"], t, inp["W1"], inp["W3"], inp["W2"],
+                                                    idx[t, j])
+    np.testing.assert_allclose(out["y"], ref, rtol=1e-12, atol=1e-14)
+
+
 def check_fp8():
     # "Mistral 8x7B SMoE architecture deep dive" section 5.3: expert weights
     # quantised with one scale per expert, router kept in high precision.
@@ -431,7 +484,7 @@ CHECKS = [check_logits, check_topk_bruteforce, check_topk_duplicate_rows, check_
           check_all_experts_special_case, check_shared_expert, check_invariants,
           check_given_logits_and_rows, check_page_numbers, check_gate_variants,
           check_glu_sigmoid_dense, check_fused_weight_formulation, check_capacity,
-          check_entropy_routing, check_fp8]
+          check_entropy_routing, check_entropy_batch_routing, check_fp8]
 
 
 @pytest.mark.parametrize("check", CHECKS, ids=[c.__name__ for c in CHECKS])
@@ -472,6 +525,10 @@ MUTANTS = [
      "gate[q] = exp(l[idx[q]] - m) / z;"),
     ("entropy_empty_slot_kept", "idx[q] = -1;\n                gate[q] = 0.0;",
      "gate[q] = 0.0;"),
+    ("entropy_batch_min_k", "        if (H[t] > threshold)\n            kb = k;",
+     "        if (H[t] <= threshold)\n            kb = k - 1;"),
+    ("entropy_batch_per_token", "            if (j < kb) {",
+     "            if (j < (H[t] > threshold ? k : k - 1)) {"),
     ("w3_for_w1", "row_to_double(W1, dt, o1 + (size_t)n * d, d, wrow);",
      "row_to_double(W3, dt, o3 + (size_t)n * d, d, wrow);"),
     ("w2_transposed", "row_to_double(W2, dt, o2 + (size_t)j * dff, dff, wrow);\n        out[j] = dot(h, wrow, dff);",
