@@ -675,7 +675,7 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
   // then hands lane i of the group column 32 * beta + 16 * (g % 2) + i of
   // those four k-rows, which is what a 32x32x16 MFMA lane needs (column l % 32,
   // K values 8 * (l / 32) + 0..3; the next read gives + 4..7).
-  int tbo[4];
+  int tbo[TN];
   int w8o[4];  // W8: byte offset of the lane's 8 codes of K step ks in its row
   auto set_frag_addr = [&](int ln) {
     frow = ln & 31;
@@ -689,11 +689,17 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
         w8o[ks] = BM * 128 + (ln & 31) * 64 + 16 * (ks ^ f) + 8 * ((ln >> 5) & 1);
     }
     if constexpr (TB) {
+      // the wave's block b: SwiGLU matrix b & 1, beta 2 * wn + b / 2; down
+      // half wn, beta b (the wave-dependent parts folded in here, so that a
+      // read's offset is a constant beyond this per-lane value)
       const int g = (ln >> 4) & 3, i = ln & 15, r = i >> 2;
 #pragma unroll
-      for (int be = 0; be < 4; ++be)
-        tbo[be] = BM * 128 + (8 * (g >> 1) + r) * 256 +
-                  ((4 * (be ^ r)) + 2 * (g & 1) + ((i & 3) >> 1)) * 16 + 8 * (i & 1);
+      for (int b = 0; b < TN; ++b) {
+        const int m = SWIGLU ? (b & 1) : wn;
+        const int be = SWIGLU ? 2 * wn + (b >> 1) : b;
+        tbo[b] = BM * 128 + m * 16384 + (8 * (g >> 1) + r) * 256 +
+                 ((4 * (be ^ r)) + 2 * (g & 1) + ((i & 3) >> 1)) * 16 + 8 * (i & 1);
+      }
     }
   };
   set_frag_addr(lane);
@@ -720,10 +726,8 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
 #pragma unroll
       for (int b = 0; b < TN; ++b) {
         // SwiGLU: block b of wave wn is matrix b & 1, columns wn * 64 + (b / 2) * 32
-        // of the half; down: half wn, columns b * 32
-        const int m = SWIGLU ? (b & 1) : wn;
-        const int be = SWIGLU ? 2 * wn + (b >> 1) : b;
-        const int off = tbo[be] + m * 16384 + ks * 16 * 256;
+        // of the half; down: half wn, columns b * 32 (folded into tbo[b])
+        const int off = tbo[b] + ks * 16 * 256;
         const bf16x4_v lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(sb + off));
         const bf16x4_v hi =
             __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(sb + off + 4 * 256));
