@@ -179,7 +179,14 @@ int moe_forward_timed(const void *x, const void *Wg, const float *bias, const vo
  *                                     slot holds idx -1 and gate 0 and is
  *                                     placed nowhere (inv -1).  The page takes
  *                                     the batch's largest k for every token;
- *                                     here each token keeps its own.
+ *                                     in this mode each token keeps its own
+ *              MOE_GATE_ENTROPY_BATCH the same routing as the page's listing
+ *                                     prints it: one k for the whole call,
+ *                                     the largest per-token k (k if any
+ *                                     token's entropy exceeds 0.8, else
+ *                                     k - 1, in which case every token's
+ *                                     last slot is empty: idx -1, gate 0);
+ *                                     needs k >= 2.
  *   activation MOE_ACT_SWIGLU         W2( SiLU(W1 x) * (W3 x) )  (default)
  *              MOE_ACT_GLU_SIGMOID    W2( sigmoid(W1 x) * (W3 x) ): the same
  *                                     numpy function's gated projection (its
@@ -196,7 +203,8 @@ enum {
     MOE_GATE_SOFTMAX_TOPK = 0,
     MOE_GATE_SOFTMAX_ALL = 1,
     MOE_GATE_SIGMOID = 2,
-    MOE_GATE_ENTROPY = 3
+    MOE_GATE_ENTROPY = 3,
+    MOE_GATE_ENTROPY_BATCH = 4
 };
 enum { MOE_ACT_SWIGLU = 0, MOE_ACT_GLU_SIGMOID = 1 };
 
@@ -215,7 +223,7 @@ typedef struct moe_options_s {
 int moe_capacity(int T, int k, double capacity_factor);
 
 /* moe_route with a gate variant (gate_mode as above); MOE_EINVAL for an
- * unknown mode, or MOE_GATE_ENTROPY with k < 2. */
+ * unknown mode, or an entropy-aware mode with k < 2. */
 int moe_route_ex(const void *x, const void *Wg, const float *bias, int T, int d, int E, int k,
                  int dtype, int gate_mode, int32_t *idx, float *gate, float *logits,
                  void *workspace, size_t workspace_bytes, void *stream);

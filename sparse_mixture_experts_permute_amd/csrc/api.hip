@@ -192,8 +192,9 @@ int moe_route_ex(const void *x, const void *Wg, const float *bias, int T, int d,
                  int dtype, int gate_mode, int32_t *idx, float *gate, float *logits,
                  void *workspace, size_t workspace_bytes, void *stream) {
   if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_EDTYPE;
-  if (gate_mode < MOE_GATE_SOFTMAX_TOPK || gate_mode > MOE_GATE_ENTROPY) return MOE_EINVAL;
-  if (gate_mode == MOE_GATE_ENTROPY && k < 2) return MOE_EINVAL;
+  if (gate_mode < MOE_GATE_SOFTMAX_TOPK || gate_mode > MOE_GATE_ENTROPY_BATCH) return MOE_EINVAL;
+  if ((gate_mode == MOE_GATE_ENTROPY || gate_mode == MOE_GATE_ENTROPY_BATCH) && k < 2)
+    return MOE_EINVAL;
   if (T < 0 || E < 1 || E > 256 || k < 1 || k > E || d < 64 || d % 64) return MOE_EINVAL;
   if ((long long)T * E >= (1LL << 31)) return MOE_EINVAL;
   if (T == 0) return MOE_OK;
@@ -309,8 +310,12 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
   // reads, few-token steps through the [K][N] weight-streaming kernel
   const bool tb = o.weight_layout == MOE_LAYOUT_IN_OUT;
   if (f8 && tb) return MOE_EINVAL;
-  if (o.gate_mode < MOE_GATE_SOFTMAX_TOPK || o.gate_mode > MOE_GATE_ENTROPY) return MOE_EINVAL;
-  if (o.gate_mode == MOE_GATE_ENTROPY && k < 2) return MOE_EINVAL;
+  if (o.gate_mode < MOE_GATE_SOFTMAX_TOPK || o.gate_mode > MOE_GATE_ENTROPY_BATCH)
+    return MOE_EINVAL;
+  if ((o.gate_mode == MOE_GATE_ENTROPY || o.gate_mode == MOE_GATE_ENTROPY_BATCH) && k < 2)
+    return MOE_EINVAL;
+  // one token: the batch's largest k is the token's own
+  const int gmode = o.gate_mode == MOE_GATE_ENTROPY_BATCH && T == 1 ? MOE_GATE_ENTROPY : o.gate_mode;
   if (o.activation != MOE_ACT_SWIGLU && o.activation != MOE_ACT_GLU_SIGMOID) return MOE_EINVAL;
   if (!dims_ok(T, d, d_ff, E, k, d_ff_shared)) return MOE_EINVAL;
   const bool shared = d_ff_shared > 0;
@@ -374,7 +379,7 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
   // a single token with a small router: the SwiGLU weight-streaming kernel
   // routes it itself (no score or top-k launches)
   const bool route_fused = sk.gemv && !tb && moe::route_fused_ok(T, d, E, k);
-  const moe::DecodeRoute rt{Wg, bias, E, k, o.gate_mode,
+  const moe::DecodeRoute rt{Wg, bias, E, k, gmode,
                             o.capacity < 0 || o.capacity > P ? P : o.capacity,
                             plan.bm1, plan.bm2, logits, idx, gate, counts, offsets, perm, inv,
                             mt0, mt1, shseg, act, fixc, moe::FIX_SLOTS};
@@ -407,9 +412,9 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
   MOE_MARK(0);
   if (route_fused) {
     MOE_MARK(1);
-  } else if (moe::route_permute_tiny_ok(T, E, k)) {
+  } else if (moe::route_permute_tiny_ok(T, E, k) && gmode != MOE_GATE_ENTROPY_BATCH) {
     // a small batch: scores, then top-k, gate and grouping in one more launch
-    if ((e = moe::launch_route_permute_tiny(dtype, x, Wg, bias, T, d, E, k, o.gate_mode,
+    if ((e = moe::launch_route_permute_tiny(dtype, x, Wg, bias, T, d, E, k, gmode,
                                             o.capacity, plan.bm1, plan.bm2, logits, idx, gate,
                                             counts, offsets, perm, inv, mt0, mt1, shseg, act,
                                             fixc, moe::FIX_SLOTS,
@@ -417,7 +422,7 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
       goto fail;
     MOE_MARK(1);
   } else {
-    if ((e = moe::launch_router(dtype, x, Wg, bias, T, d, E, k, o.gate_mode, idx, gate, logits,
+    if ((e = moe::launch_router(dtype, x, Wg, bias, T, d, E, k, gmode, idx, gate, logits,
                                 at<float>(ws, L.off[F_RPART]), s)))
       goto fail;
     MOE_MARK(1);

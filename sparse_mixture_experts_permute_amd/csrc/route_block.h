@@ -18,6 +18,10 @@ namespace moe {
 // they are, and an empty slot gets idx -1 (placed nowhere) and gate 0.  The
 // entropy is evaluated as ln z - (sum w u) / z with u = (v - max) / tau,
 // w = exp(u), z = sum w, so a probability that underflows contributes 0.
+// gate_mode 4 (the page's listing: one k for the batch, the largest per-token
+// k): the same, except that a slot past the token's own k keeps its
+// probability and holds -(e + 2) for its expert e, so that a later pass
+// over the batch (entropy_batch_kernel) can keep or empty it.
 constexpr float ENTROPY_TAU = 0.1f;
 constexpr float ENTROPY_THRESHOLD = 0.8f;
 __device__ __forceinline__ void wave_topk_gate(const float (&v)[4], int E, int k, int gate_mode,
@@ -67,7 +71,7 @@ __device__ __forceinline__ void wave_topk_gate(const float (&v)[4], int E, int k
   }
 #pragma unroll
   for (int off = kWave / 2; off > 0; off >>= 1) z += __shfl_xor(z, off);
-  if (gate_mode == 3) {
+  if (gate_mode == 3 || gate_mode == 4) {
     float zt = 0.f, s1 = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -85,8 +89,14 @@ __device__ __forceinline__ void wave_topk_gate(const float (&v)[4], int E, int k
     const float H = logf(zt) - s1 / zt;
     const int kt = H > ENTROPY_THRESHOLD ? k : k - 1;
     for (int r = lane; r < k; r += kWave) {
-      idx[r] = r < kt ? seli[r] : -1;
-      gate[r] = r < kt ? expf((selv[r] - m) / ENTROPY_TAU) / zt : 0.f;
+      const float p = expf((selv[r] - m) / ENTROPY_TAU) / zt;
+      if (gate_mode == 4) {
+        idx[r] = r < kt ? seli[r] : -(seli[r] + 2);
+        gate[r] = p;
+      } else {
+        idx[r] = r < kt ? seli[r] : -1;
+        gate[r] = r < kt ? p : 0.f;
+      }
     }
     return;
   }

@@ -193,7 +193,7 @@ __device__ __forceinline__ void group_topk_gate(const float (&v)[EB], int E, int
     }
   }
   if (li >= k) return;
-  if (gate_mode == 3) {
+  if (gate_mode == 3 || gate_mode == 4) {
     float zt = 0.f, s1 = 0.f;
 #pragma unroll
     for (int e = 0; e < EB; ++e)
@@ -205,8 +205,14 @@ __device__ __forceinline__ void group_topk_gate(const float (&v)[EB], int E, int
       }
     const float H = logf(zt) - s1 / zt;
     const int kt = H > ENTROPY_THRESHOLD ? k : k - 1;
-    idx[li] = li < kt ? myi : -1;
-    gate[li] = li < kt ? expf((myv - m) / ENTROPY_TAU) / zt : 0.f;
+    const float p = expf((myv - m) / ENTROPY_TAU) / zt;
+    if (gate_mode == 4) {  // see wave_topk_gate
+      idx[li] = li < kt ? myi : -(myi + 2);
+      gate[li] = p;
+    } else {
+      idx[li] = li < kt ? myi : -1;
+      gate[li] = li < kt ? p : 0.f;
+    }
     return;
   }
   idx[li] = myi;
@@ -450,6 +456,31 @@ __global__ __launch_bounds__(256) void topk_permute_tiny_kernel(
                    RouteOut{counts, offsets, perm, inv, mtiles0, mtiles1, shared_seg, active});
 }
 
+// The entropy-aware routing with one k for the batch ("Mixtral 8x7B model
+// architecture", section 4.1, as its listing prints it: the batch's largest
+// per-token k).  The top-k kernels (gate_mode 4) leave each token's last slot
+// as its expert e when the token's own k is the full k, else as -(e + 2);
+// one workgroup then keeps every last slot if any token takes the full k
+// (its expert restored, its probability kept), else empties them all (idx
+// -1, gate 0).
+__global__ __launch_bounds__(1024) void entropy_batch_kernel(int32_t *__restrict__ idx,
+                                                             float *__restrict__ gate, int T_,
+                                                             int k) {
+  int any = 0;
+  for (int t = threadIdx.x; t < T_; t += 1024) any |= idx[(size_t)t * k + k - 1] >= 0;
+  any = __syncthreads_or(any);
+  for (int t = threadIdx.x; t < T_; t += 1024) {
+    const size_t q = (size_t)t * k + k - 1;
+    const int v = idx[q];
+    if (any) {
+      if (v < 0) idx[q] = -v - 2;
+    } else {
+      idx[q] = -1;
+      gate[q] = 0.f;
+    }
+  }
+}
+
 // Feature slices for the score kernels (enough work items to fill the GPU).
 // Narrow kernel: a slice is ns steps of 16 lanes x 16 bytes per token.  Tiled
 // kernel: a slice is a whole number of 128-byte chunks.
@@ -543,9 +574,26 @@ size_t router_partial_bytes(int T, int d, int E, int esize) {
   return (size_t)router_split(T, d, E, esize).S * T * E * 4;
 }
 
+namespace {
+hipError_t launch_router_scores_topk(int dtype, const void *x, const void *Wg, const float *bias,
+                                     int T, int d, int E, int k, int gate_mode, int32_t *idx,
+                                     float *gate, float *logits, float *part, hipStream_t s);
+}  // namespace
+
 hipError_t launch_router(int dtype, const void *x, const void *Wg, const float *bias, int T,
                          int d, int E, int k, int gate_mode, int32_t *idx, float *gate,
                          float *logits, float *part, hipStream_t s) {
+  hipError_t e = launch_router_scores_topk(dtype, x, Wg, bias, T, d, E, k, gate_mode, idx, gate,
+                                           logits, part, s);
+  if (e != hipSuccess || gate_mode != 4 || T == 0) return e;
+  hipLaunchKernelGGL(entropy_batch_kernel, dim3(1), dim3(1024), 0, s, idx, gate, T, k);
+  return hipGetLastError();
+}
+
+namespace {
+hipError_t launch_router_scores_topk(int dtype, const void *x, const void *Wg, const float *bias,
+                                     int T, int d, int E, int k, int gate_mode, int32_t *idx,
+                                     float *gate, float *logits, float *part, hipStream_t s) {
   const int es = dtype == 1 ? 2 : 4;
   const RouterSplit r = router_split(T, d, E, es);
   const size_t wl_bytes = (size_t)E * d * es;
@@ -583,4 +631,5 @@ hipError_t launch_router(int dtype, const void *x, const void *Wg, const float *
   return hipGetLastError();
 }
 
+}  // namespace
 }  // namespace moe

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
 
 MOE_F32, MOE_BF16 = 0, 1
 GATE_SOFTMAX_TOPK, GATE_SOFTMAX_ALL, GATE_SIGMOID, GATE_ENTROPY = 0, 1, 2, 3
+GATE_ENTROPY_BATCH = 4
 ACT_SWIGLU, ACT_GLU_SIGMOID = 0, 1
 LAYOUT_OUT_IN, LAYOUT_IN_OUT = 0, 1
 NSTAGE_EVENTS = 8

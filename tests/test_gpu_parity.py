@@ -183,20 +183,39 @@ def test_forward_sampled_full_size(name):
     if cfg.skew:
         say(f"{name}: hot-expert share {counts[0] / counts.sum():.3f}")
     rng = np.random.default_rng(7)
-    rows = sample_rows(cfg.T, rng)
-    # include tokens routed to the least-loaded non-empty expert (a ragged tile)
-    # and to the last non-empty one (its tiles end the tile order: the ones a
-    # last-round K split cuts into parts)
+    rows = set(sample_rows(cfg.T, rng))
+    # Whole tiles: every token of the last non-empty expert (its tiles end the
+    # tile order, so they are the ones a last-round K split cuts into parts,
+    # over every column block), every token in the last two 256-row tiles of
+    # the most-loaded expert (its ragged last tile) and a few tokens of the
+    # least-loaded one
+    perm = inter["perm"].numpy()
+    offsets = inter["offsets"].numpy()
     nz = np.nonzero(counts)[0]
-    emin = nz[np.argmin(counts[nz])]
-    for e in (emin, nz[-1]):
-        rows = sorted(set(rows) | set(np.nonzero(np.any(idx_ref == e, axis=1))[0][:4].tolist()))
+    elast, emax, emin = nz[-1], int(np.argmax(counts)), nz[np.argmin(counts[nz])]
+    tiles = {}  # (expert, 256-row tile of its slots) -> tokens
+    for e, first in ((elast, 0), (emax, max(0, (counts[emax] - 1) // 256 - 1) * 256)):
+        for s_ in range(offsets[e] + first, offsets[e + 1]):
+            t = int(perm[s_]) // cfg.k
+            tiles.setdefault((int(e), (s_ - offsets[e]) // 256), []).append(t)
+            rows.add(t)
+    rows |= set(np.nonzero(np.any(idx_ref == emin, axis=1))[0][:4].tolist())
+    rows = sorted(rows)
     ref = O.forward_rows(h["x"], h["W1"], h["W3"], h["W2"], rows, idx_ref[rows], gate_ref[rows],
                          shared=shared_tuple(h))
     got = f64(moe.tensor_to_numpy(y[rows]))
     err = rel_l2(got, ref)
-    say(f"{name}: sampled {len(rows)} rows rel-L2 {err:.3e}; own-score route flips {nflip}")
+    pos = {t: i for i, t in enumerate(rows)}
+    worst, worst_tile = 0.0, None
+    for key, toks in tiles.items():
+        sel = [pos[t] for t in toks]
+        e_t = rel_l2(got[sel], ref[sel])
+        if e_t > worst:
+            worst, worst_tile = e_t, key
+    say(f"{name}: {len(rows)} rows ({len(tiles)} whole m-tiles of experts {elast} and {emax}) "
+        f"rel-L2 {err:.3e}; worst m-tile {worst_tile} {worst:.3e}; own-score route flips {nflip}")
     assert err <= TOL[cfg.dtype]
+    assert worst <= TOL[cfg.dtype]
 
 
 @pytest.mark.parametrize("name", ["mixtral_prefill_T2048", "fine_shared_T512",

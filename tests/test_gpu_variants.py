@@ -75,6 +75,12 @@ CASES = [
     ("routed_T1_cap0_bf16", 1, 4096, 8, 2048, 2, "bf16", 0, 0.0, 0, 0, 0),
     ("routed_T1_entropy_k2_bf16", 1, 4096, 8, 2048, 3, "bf16", 0, 0.0, 3, 0, None),
     ("routed_T1_entropy_k3_bf16", 1, 4096, 8, 2048, 3, "bf16", 0, 0.0, 3, 0, None, 41),
+    # the same section's listing as printed: one k for the batch, its largest per-token k
+    ("entropy_batch_k3_bf16", 300, 256, 8, 512, 3, "bf16", 0, 0.0, 4, 0, None),
+    ("entropy_batch_low_f32", 200, 128, 8, 256, 3, "f32", 0, 4.0, 4, 0, None),
+    ("entropy_batch_cap_shared_bf16", 150, 256, 6, 256, 3, "bf16", 128, 0.0, 4, 1, 40),
+    ("entropy_batch_decode_T3_bf16", 3, 2048, 8, 2048, 3, "bf16", 0, 0.0, 4, 0, None),
+    ("routed_T1_entropy_batch_bf16", 1, 4096, 8, 2048, 3, "bf16", 0, 0.0, 4, 0, None, 41),
 ]
 
 
@@ -97,7 +103,7 @@ def test_variant_forward(c):
     torch.cuda.synchronize()
     it = {n: v.cpu().numpy() for n, v in L.intermediates(T).items()}
     lg = it["logits"].astype(np.float64)
-    if gm == O.GATE_ENTROPY:
+    if gm in (O.GATE_ENTROPY, O.GATE_ENTROPY_BATCH):
         # the per-token k is a decision on the entropy (fp32 on the GPU, fp64
         # here, from the same scores): these inputs keep every token clear of
         # the threshold, so both sides decide alike
@@ -243,3 +249,21 @@ def test_permute_capacity(T, E, k, cap):
     inv_ref[order] = np.arange(len(order), dtype=np.int32)
     np.testing.assert_array_equal(inv.cpu().numpy(), inv_ref)
     say(f"moe_permute_ex T={T} E={E} k={k} capacity={cap}: kept {len(order)} of {T * k}")
+
+
+@pytest.mark.parametrize("skew,expect_k", [(0.0, 3), (4.0, 2)])
+def test_route_entropy_batch_branches(skew, expect_k):
+    """One k for the batch: the full k when any token's entropy exceeds the
+    threshold, else every token's last slot empty (moe_route_ex)."""
+    cfg, h, dev = inputs(256, 256, 8, 256, 3, "bf16", skew=skew, seed=19)
+    say(f"entropy batch routing, skew {skew}")
+    idx, gate, logits = moe.route(dev["x"], dev["Wg"], 3, dev["bias"],
+                                  gate_mode=moe.GATE_ENTROPY_BATCH)
+    torch.cuda.synchronize()
+    lg = logits.double().cpu().numpy()
+    H = O.entropy(lg)
+    assert np.min(np.abs(H - O.ENTROPY_THRESHOLD)) > 1e-4
+    idx_ref, gate_ref, kb = O.route_entropy_batch(lg, 3)
+    assert kb == expect_k
+    np.testing.assert_array_equal(idx.cpu().numpy(), idx_ref)
+    assert np.max(np.abs(gate.cpu().numpy() - gate_ref)) <= 1e-6
