@@ -350,7 +350,13 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
                      moe::gemv_t_ok(d, d_ff_shared);
     sk.shared = sk.gemv_shared;
   }
-  const int ksplit = sk.routed ? 1 : down_splits(plan, T, k, E, d, d_ff);
+  // K planes of the down projection: the tiled kernel's choice; the [K][N]
+  // weight-streaming kernel takes up to 4 (within the workspace's planes)
+  const int ksplit =
+      sk.routed ? (tb ? moe::gemv_t_down_splits(std::min(E, T * k), d, d_ff,
+                                                std::min(4, down_splits(plan, T, k, E, d, d_ff)))
+                      : 1)
+                : down_splits(plan, T, k, E, d, d_ff);
   const size_t plane = (size_t)P * d;
   float *logits = at<float>(ws, L.off[F_LOGITS]);
   int32_t *idx = at<int32_t>(ws, L.off[F_IDX]);
@@ -461,7 +467,8 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
              : fused_combine
                  ? moe::launch_gemv_down_combine(T, H, W2, Yp, offsets, act, act + E, G, d, d_ff,
                                                  nact, inv, gate, T, k, y, fixc, s)
-             : tb ? moe::launch_gemv_t_down(T, H, W2, Yp, offsets, act, act + E, G, d, d_ff, s)
+             : tb ? moe::launch_gemv_t_down(T, H, W2, Yp, offsets, act, act + E, G, d, d_ff,
+                                            ksplit, plane, s)
              : sk.gemv ? moe::launch_gemv_down(T, H, W2, Yp, offsets, act, act + E, G, d, d_ff,
                                                nact, s)
                        : moe::launch_skinny_down(sk.mb, H, W2, Yp, offsets, act, act + E, E, d,
@@ -530,7 +537,7 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
                                          shseg + 6, shseg + 7, 1, d_ff_shared, d, s)))
         goto fail;
       if ((e = moe::launch_gemv_t_down(T, Hs, Ws2, Ys, shseg, shseg + 6, shseg + 7, 1, d,
-                                       d_ff_shared, s)))
+                                       d_ff_shared, 1, 0, s)))
         goto fail;
     } else if (sk.gemv_shared) {
       if ((e = moe::launch_gemv_swiglu(T, o.activation, x, nullptr, 1, Ws1, Ws3, Hs, shseg,

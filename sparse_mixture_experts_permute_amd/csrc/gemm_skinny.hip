@@ -719,10 +719,11 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_swiglu_wave_kernel(
 // rows of A W), up to R rows per pass.  A workgroup owns one (active expert,
 // block of CW output columns) pair and reads that weight slice once; its four
 // wavefronts split K.  Lane l covers columns c0 + 8 * (l % LPR) .. + 7 (LPR =
-// CW / 8 lanes per k-row) of its own contiguous run of M = K / (4 * 64 / LPR)
-// k-rows, so a wavefront instruction reads 64 / LPR whole k-row segments of
-// CW * 2 bytes, and one 16-byte load of each row's activations serves eight
-// k-rows.  The products are summed in fp32 per column; lanes that share
+// CW / 8 lanes per k-row); the KG = 64 / LPR lane groups of a wavefront take
+// the consecutive 8-row pieces of a block of 8 * KG k-rows, so one
+// instruction reads KG k-row segments of CW * 2 bytes that lie within 8 * KG
+// rows of each other, and one 16-byte load of each row's activations serves a
+// lane's eight k-rows.  The products are summed in fp32 per column; lanes that share
 // columns are then reduced by the butterfly and the wavefronts through LDS,
 // both in a fixed order.
 // ---------------------------------------------------------------------------
@@ -731,7 +732,7 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_t_kernel(
     const bf16_t *__restrict__ A, const int32_t *__restrict__ perm, int kslots,
     const bf16_t *__restrict__ B1, const bf16_t *__restrict__ B3, void *__restrict__ C,
     const int32_t *__restrict__ seg_off, const int32_t *__restrict__ active,
-    const int32_t *__restrict__ nactive, int N, int K, int act) {
+    const int32_t *__restrict__ nactive, int N, int K, int act, size_t plane) {
   constexpr int NW = SWIGLU ? 2 : 1;
   constexpr int LPR = CW / 8;     // lanes per k-row
   constexpr int KG = kWave / LPR; // k-rows per wavefront instruction
@@ -744,12 +745,16 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_t_kernel(
   const int s0 = seg_off[e], cnt = seg_off[e + 1] - s0;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = lane_id();
-  const int M = K / (GV_WAVES * KG);  // k-rows per lane, a multiple of 8 (host check)
-  const int kb = wave * (K / GV_WAVES) + (lane / LPR) * M;
+  // The down projection may split K over gridDim.y workgroups (part y writes
+  // its fp32 sums to plane y, the combine adds the planes in order).  The
+  // wave's K range holds ng blocks of 8 * KG k-rows (a whole number: host
+  // check); lane group j takes rows 8 j .. 8 j + 7 of each.
+  const int Kp = K / gridDim.y;
+  const int kb = blockIdx.y * Kp + wave * (Kp / GV_WAVES) + (lane / LPR) * 8;
   const int cl = c0 + (lane % LPR) * 8;
   const bf16_t *w1 = B1 + ((size_t)e * K + kb) * N + cl;
   const bf16_t *w3 = SWIGLU ? B3 + ((size_t)e * K + kb) * N + cl : w1;
-  const int ng = M / 8;  // groups of 8 k-rows
+  const int ng = Kp / (GV_WAVES * 8 * KG);
 
   for (int rg = 0; rg < cnt; rg += R) {
     const bf16_t *ap[R];
@@ -768,14 +773,14 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_t_kernel(
         for (int j = 0; j < 8; ++j) acc[m][r][j] = 0.f;
     uint4 wa[NW][8], wb[NW][8], xa[R], xb[R];
     auto load = [&](uint4 (&w)[NW][8], uint4 (&xv)[R], int g) {
-      const size_t ro = (size_t)g * 8 * N;
+      const size_t ro = (size_t)g * 8 * KG * N;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         w[0][i] = ldg16_stream(w1 + ro + (size_t)i * N);
         if (SWIGLU) w[NW - 1][i] = ldg16_stream(w3 + ro + (size_t)i * N);
       }
 #pragma unroll
-      for (int r = 0; r < R; ++r) xv[r] = *reinterpret_cast<const uint4 *>(ap[r] + g * 8);
+      for (int r = 0; r < R; ++r) xv[r] = *reinterpret_cast<const uint4 *>(ap[r] + g * 8 * KG);
     };
     auto compute = [&](const uint4 (&w)[NW][8], const uint4 (&xv)[R]) {
 #pragma unroll
@@ -799,7 +804,6 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_t_kernel(
         }
       }
     };
-    // ng is even (M is a multiple of 16 when K allows, else handled by the tail)
     load(wa, xa, 0);
     if (ng > 1) load(wb, xb, 1);
     int g = 0;
@@ -848,28 +852,50 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_t_kernel(
         if (SWIGLU)
           reinterpret_cast<bf16_t *>(C)[out] = f32_to_bf16(gated(v[0], v[NW - 1], act));
         else
-          reinterpret_cast<float *>(C)[out] = v[0];
+          reinterpret_cast<float *>(C)[blockIdx.y * plane + out] = v[0];
       }
     }
     __syncthreads();
   }
 }
 
+// Column block of the [K][N] weight-streaming kernel: the widest (up to
+// GVT_MAX_CW columns) that still gives GVT_MIN_WG workgroups with the K
+// parts.  Wider blocks read longer runs of each k-row (128 columns: 256
+// bytes), which the memory system serves better (one token's SwiGLU, 470 MB:
+// 32 columns 183 us, 64 95 us, 128 79 us).
+constexpr int GVT_MAX_CW = 128, GVT_MIN_WG = 128;
+inline int gvt_kg(int cw) { return kWave / (cw / 8); }
+inline bool gvt_fits(int cw, int N, int Kp) {
+  return N % cw == 0 && Kp % (GV_WAVES * 8 * gvt_kg(cw)) == 0;
+}
+inline int gvt_cw(int G, int N, int Kp, int ksplit) {
+  for (int cw = GVT_MAX_CW; cw >= 32; cw /= 2)
+    if (gvt_fits(cw, N, Kp) && ((long long)G * (N / cw) * ksplit >= GVT_MIN_WG || cw == 32))
+      return cw;
+  return 0;
+}
+
 template <bool SWIGLU, int R>
 hipError_t launch_gemv_t_r(int act, const void *A, const int32_t *perm, int kslots,
                            const void *B1, const void *B3, void *C, const int32_t *seg_off,
                            const int32_t *active, const int32_t *nactive, int G, int N, int K,
-                           hipStream_t s) {
+                           int ksplit, size_t plane, hipStream_t s) {
   const bf16_t *a = (const bf16_t *)A, *b1 = (const bf16_t *)B1, *b3 = (const bf16_t *)B3;
-  // 64-column blocks when they give every CU a workgroup, else 32
-  if ((long long)G * (N / 64) >= 256 && K % (GV_WAVES * 8 * 8) == 0 && N % 64 == 0) {
-    hipLaunchKernelGGL((gemv_t_kernel<SWIGLU, R, 64>), dim3(G * (N / 64)), dim3(GV_THREADS), 0,
-                       s, a, perm, kslots, b1, b3, C, seg_off, active, nactive, N, K, act);
-  } else {
-    if (K % (GV_WAVES * 16 * 8) || N % 32) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemv_t_kernel<SWIGLU, R, 32>), dim3(G * (N / 32)), dim3(GV_THREADS), 0,
-                       s, a, perm, kslots, b1, b3, C, seg_off, active, nactive, N, K, act);
+  if ((SWIGLU && ksplit != 1) || ksplit < 1 || K % ksplit) return hipErrorInvalidValue;
+  const int cw = gvt_cw(G, N, K / ksplit, ksplit);
+#define GVT_LAUNCH(CW_)                                                                       \
+  hipLaunchKernelGGL((gemv_t_kernel<SWIGLU, R, CW_>), dim3(G * (N / CW_), ksplit),           \
+                     dim3(GV_THREADS), 0, s, a, perm, kslots, b1, b3, C, seg_off, active,    \
+                     nactive, N, K, act, plane)
+  switch (cw) {
+    case 256: GVT_LAUNCH(256); break;
+    case 128: GVT_LAUNCH(128); break;
+    case 64: GVT_LAUNCH(64); break;
+    case 32: GVT_LAUNCH(32); break;
+    default: return hipErrorInvalidValue;
   }
+#undef GVT_LAUNCH
   return hipGetLastError();
 }
 
@@ -877,15 +903,15 @@ template <bool SWIGLU>
 hipError_t launch_gemv_t(int rows, int act, const void *A, const int32_t *perm, int kslots,
                          const void *B1, const void *B3, void *C, const int32_t *seg_off,
                          const int32_t *active, const int32_t *nactive, int G, int N, int K,
-                         hipStream_t s) {
+                         int ksplit, size_t plane, hipStream_t s) {
   if (rows <= 1)
     return launch_gemv_t_r<SWIGLU, 1>(act, A, perm, kslots, B1, B3, C, seg_off, active, nactive,
-                                      G, N, K, s);
+                                      G, N, K, ksplit, plane, s);
   if (rows <= 2)
     return launch_gemv_t_r<SWIGLU, 2>(act, A, perm, kslots, B1, B3, C, seg_off, active, nactive,
-                                      G, N, K, s);
+                                      G, N, K, ksplit, plane, s);
   return launch_gemv_t_r<SWIGLU, 4>(act, A, perm, kslots, B1, B3, C, seg_off, active, nactive, G,
-                                    N, K, s);
+                                    N, K, ksplit, plane, s);
 }
 
 template <bool SWIGLU, int R, bool COMBINE = false, bool W8 = false, bool ROUTE = false>
@@ -1016,21 +1042,31 @@ hipError_t launch_gemv_down_combine_fp8(int rows, const void *Hin, const uint8_t
                                         active, nactive, G, N, K, nact, cm, s, s2, nullptr);
 }
 
-bool gemv_t_ok(int N, int K) { return N % 32 == 0 && K % (GV_WAVES * 16 * 8) == 0; }
+bool gemv_t_ok(int N, int K) { return gvt_fits(32, N, K); }
 
 hipError_t launch_gemv_t_swiglu(int rows, int act, const void *x, const int32_t *perm,
                                 int kslots, const void *W1, const void *W3, void *H,
                                 const int32_t *seg_off, const int32_t *active,
                                 const int32_t *nactive, int G, int N, int K, hipStream_t s) {
   return launch_gemv_t<true>(rows, act, x, perm, kslots, W1, W3, H, seg_off, active, nactive, G,
-                             N, K, s);
+                             N, K, 1, 0, s);
+}
+
+int gemv_t_down_splits(int G, int N, int K, int max_split) {
+  // enough K parts for a workgroup per CU in the widest column blocks
+  int S = 1;
+  while (S * 2 <= max_split && (long long)G * (N / GVT_MAX_CW) * S < 256 && K % (S * 2) == 0 &&
+         gvt_cw(G, N, K / (S * 2), S * 2) != 0)
+    S *= 2;
+  return S;
 }
 
 hipError_t launch_gemv_t_down(int rows, const void *Hin, const void *W2, float *Y,
                               const int32_t *seg_off, const int32_t *active,
-                              const int32_t *nactive, int G, int N, int K, hipStream_t s) {
+                              const int32_t *nactive, int G, int N, int K, int ksplit,
+                              size_t plane, hipStream_t s) {
   return launch_gemv_t<false>(rows, 0, Hin, nullptr, 1, W2, nullptr, Y, seg_off, active, nactive,
-                              G, N, K, s);
+                              G, N, K, ksplit, plane, s);
 }
 
 bool route_fused_ok(int T, int d, int E, int k) {

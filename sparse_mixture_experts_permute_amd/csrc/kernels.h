@@ -185,9 +185,14 @@ hipError_t launch_gemv_t_swiglu(int rows, int act, const void *x, const int32_t 
                                 int kslots, const void *W1, const void *W3, void *H,
                                 const int32_t *seg_off, const int32_t *active,
                                 const int32_t *nactive, int G, int N, int K, hipStream_t s);
+// the down projection may split K into ksplit parts (fp32 planes `plane`
+// floats apart, added in order by the combine); gemv_t_down_splits: the parts
+// that give every CU a workgroup, at most max_split
+int gemv_t_down_splits(int G, int N, int K, int max_split);
 hipError_t launch_gemv_t_down(int rows, const void *Hin, const void *W2, float *Y,
                               const int32_t *seg_off, const int32_t *active,
-                              const int32_t *nactive, int G, int N, int K, hipStream_t s);
+                              const int32_t *nactive, int G, int N, int K, int ksplit,
+                              size_t plane, hipStream_t s);
 hipError_t launch_skinny_swiglu(int mb, int act, const void *x, const int32_t *perm, int kslots,
                                 const void *W1, const void *W3, void *H,
                                 const int32_t *seg_off, const int32_t *active,
