@@ -6,7 +6,7 @@ counters, and the summary of rocprofv3 outputs into the text kept in profiles/.
       kernel for FETCH_SIZE / WRITE_SIZE)
   python -m sparse_mixture_experts_permute_amd.profiling summarize --stats S.csv
       [--fetch F.csv --write W.csv --cal-fetch CF.csv --cal-write CW.csv]
-      [--kernel SUBSTR] [--bench bench.json] [--cmd "..."]
+      [--trace T.csv] [--kernel SUBSTR] [--bench bench.json] [--cmd "..."]
       prints a markdown summary (kernel table, per-dispatch traffic of the
       selected kernel scaled by the copy calibration)
 """
@@ -51,6 +51,15 @@ def _read_stats(path):
     return out
 
 
+def _durations(path, substr):
+    """Per-dispatch durations (us) of the kernels whose name holds substr."""
+    out = []
+    for r in csv.DictReader(open(path)):
+        if substr in r["Kernel_Name"]:
+            out.append((float(r["End_Timestamp"]) - float(r["Start_Timestamp"])) / 1e3)
+    return out
+
+
 def _per_dispatch(path, counter):
     """{kernel name: [value per dispatch]} for one counter (summed over agents)."""
     per = defaultdict(lambda: defaultdict(float))
@@ -86,6 +95,13 @@ def summarize(a) -> str:
         k = sel[0]
         lines.append(f"Selected kernel `{_short(k['name'])}`: {k['calls']} dispatches, "
                      f"average {k['avg_us']:.1f} us.")
+        if a.trace:
+            d = sorted(_durations(a.trace, a.kernel))
+            if d:
+                lines.append(f"Per-dispatch durations from the kernel trace: median "
+                             f"{statistics.median(d):.1f} us, fastest {d[0]:.1f} us, slowest "
+                             f"{d[-1]:.1f} us over {len(d)} dispatches (the warm-up dispatches, "
+                             f"before the clocks settle, are the slow ones).")
         lines.append("")
     if a.fetch and a.write and a.cal_fetch and a.cal_write and sel:
         cf, mf = _calibration(a.cal_fetch, "FETCH_SIZE", a.cal_mib)
@@ -126,6 +142,7 @@ def main(argv=None):
     c.add_argument("--mib", type=int, default=COPY_MIB_DEFAULT)
     s = sub.add_parser("summarize")
     s.add_argument("--stats", required=True)
+    s.add_argument("--trace", help="kernel_trace.csv of the same run (per-dispatch durations)")
     s.add_argument("--fetch")
     s.add_argument("--write")
     s.add_argument("--cal-fetch")
