@@ -395,12 +395,14 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
   // experts a weight-streaming grid covers: at most P are active
   const int G = std::min(E, P);
   // 256-row tiles with fewer than 512 rows per expert on average: an expert's
-  // rows past its last full tile, when few, go to 64-row tiles of a second
-  // launch (mt0: 256-row tiles, mt1: remainder tiles, mid: where each expert's
-  // remainder starts).  With more rows per expert the padding is a small part
-  // of the work and the second launch's long K loops on few small tiles cost
-  // more than it saves (measured on Mixtral T=2048 and 8192; 256 experts at
-  // T=8192 gain 5%).
+  // rows past its last full tile, when few (up to 128), go to light 64-row
+  // tiles of the same launch, placed after the expert's full tiles of the
+  // same weight columns (mt0: full-tile prefix, mt1: light-tile prefix, mid:
+  // where each expert's light rows start).  Measured on 256 experts at
+  // T=8192: 8.50 -> 8.30 ms against a second launch for those rows (which read
+  // the weights from HBM again); on Mixtral (about 2048 rows per expert) light
+  // tiles in place of partly filled 256-row tiles cost more (4.67 -> 4.94 ms),
+  // so that layer keeps one tile height.
   const bool split = !sk.routed && plan.dl1 && plan.dl2 && plan.bm1 == 256 && plan.bm2 == 256 &&
                      (long long)P < 512LL * E;
   // the tiled down projection of the bf16 layer leaves its outputs in bf16
@@ -488,11 +490,8 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
         goto fail;
     } else if (gather_fused && split) {
       if ((e = moe::launch_gemm_swiglu(dtype, true, 256, o.activation, x, W1, W3, H, offsets, mt0,
-                                       E, d_ff, d, P / 256 + E, s, mid, perm, k,
-                                       (long long)T * d * 2, tb)) ||
-          (e = moe::launch_gemm_swiglu(dtype, true, 64, o.activation, x, W1, W3, H, mid, mt1, E,
-                                       d_ff, d, moe::SPLIT_REM_TILES * E, s, offsets + 1, perm, k,
-                                       (long long)T * d * 2, tb)))
+                                       E, d_ff, d, P / 256 + 3 * E, s, offsets + 1, perm, k,
+                                       (long long)T * d * 2, tb, mid, mt1)))
         goto fail;
     } else if (gather_fused) {
       if ((e = moe::launch_gemm_swiglu(dtype, true, 64, o.activation, x, W1, W3, H, offsets, mt0,
@@ -501,10 +500,8 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
         goto fail;
     } else if (split) {
       if ((e = moe::launch_gemm_swiglu(dtype, true, 256, o.activation, Xp, W1, W3, H, offsets, mt0,
-                                       E, d_ff, d, P / 256 + E, s, mid, nullptr, 1, 0, tb)) ||
-          (e = moe::launch_gemm_swiglu(dtype, true, 64, o.activation, Xp, W1, W3, H, mid, mt1, E,
-                                       d_ff, d, moe::SPLIT_REM_TILES * E, s, offsets + 1, nullptr,
-                                       1, 0, tb)))
+                                       E, d_ff, d, P / 256 + 3 * E, s, offsets + 1, nullptr, 1, 0,
+                                       tb, mid, mt1)))
         goto fail;
     } else if ((e = moe::launch_gemm_swiglu(dtype, plan.dl1, plan.bm1, o.activation, Xp, W1, W3,
                                             H, offsets, mt0, E, d_ff, d,
@@ -519,10 +516,8 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
         goto fail;
     } else if (split) {
       if ((e = moe::launch_gemm_down(dtype, true, 256, H, W2, Yp, offsets, mt0, E, d, d_ff,
-                                     P / 256 + E, ksplit, plane, fx, s, mid, yp_bf16, tb)) ||
-          (e = moe::launch_gemm_down(dtype, true, 64, H, W2, Yp, mid, mt1, E, d, d_ff,
-                                     moe::SPLIT_REM_TILES * E, ksplit, plane, fx, s, offsets + 1,
-                                     yp_bf16, tb)))
+                                     P / 256 + 3 * E, ksplit, plane, fx, s, offsets + 1, yp_bf16,
+                                     tb, mid, mt1)))
         goto fail;
     } else if ((e = moe::launch_gemm_down(dtype, plan.dl2, plan.bm2, H, W2, Yp, offsets, mt1, E, d,
                                           d_ff, (P + plan.bm2 - 1) / plan.bm2 + E, ksplit, plane,

@@ -77,6 +77,7 @@ constexpr int NUM_XCD = 8;  // MI355X: 8 accelerator complex dies, each with its
 // (within one block) for the grid's CUs per XCD; surplus workgroups exit.
 struct Tile {
   int e, g, n;
+  int light;  // a 64-row light tile of a 256-row launch (below)
 };
 // Position in the logical order of the tile that workgroup slot hw takes, or
 // -1 (a surplus slot).  R tiles; the grid holds gridDim.x workgroups.
@@ -99,6 +100,33 @@ __device__ __forceinline__ Tile decode_tile(int L, const int32_t *mtile_off, int
   t.e = e;
   t.n = rem / me;
   t.g = mtile_off[e] + rem % me;
+  t.light = 0;
+  return t;
+}
+// Light tiles.  A 256-row launch may also serve the few rows of an expert
+// past its last full tile ("light" 64-row tiles, at most two per expert):
+// expert e then has mt0[e+1] - mt0[e] full tiles followed by lt[e+1] - lt[e]
+// light tiles in its m-tile order (mt0, lt: prefixes), so that a light tile
+// runs next to the full tiles of the same weight columns and reads them
+// through the same L2.  Combined prefix: mt0[e] + lt[e].
+__device__ __forceinline__ Tile decode_tile_light(int L, const int32_t *mt0, const int32_t *lt,
+                                                  int G, int ntn) {
+  const int gt = L / ntn;
+  int lo = 0, hi = G;  // largest e with mt0[e] + lt[e] <= gt
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (mt0[mid] + lt[mid] <= gt) lo = mid; else hi = mid;
+  }
+  Tile t;
+  const int c0 = mt0[lo] + lt[lo];
+  const int rem = L - ntn * c0;
+  const int me = mt0[lo + 1] + lt[lo + 1] - c0;
+  const int gl = rem % me;  // m-tile of the expert: its full tiles first
+  const int full = mt0[lo + 1] - mt0[lo];
+  t.e = lo;
+  t.n = rem / me;
+  t.light = gl >= full;
+  t.g = t.light ? gl - full : mt0[lo] + gl;  // light: its index among the expert's light tiles
   return t;
 }
 __device__ __forceinline__ bool map_tile(int hw, const int32_t *mtile_off, int G, int ntn,
@@ -449,15 +477,20 @@ __device__ __forceinline__ void dl_epilogue(const TA &ta, f32x16_v (&acc)[TM][TN
 // and slice; 16-byte chunk c of row r sits in slot c ^ ((r >> 2) & 3)); a
 // fragment read converts its 8 codes to bf16 exactly, and the epilogue
 // multiplies the sums by the expert's scales.  64-row tiles only.
+// LIGHT: the launch also serves light 64-row tiles (lmt: their per-expert
+// prefix, lmid[e]: the row where expert e's light rows start; full tiles end
+// there); a light tile's rows sit in wave row 0's first two 32-row blocks,
+// whose MFMAs alone run.
 template <int BM, int BNB, bool SWIGLU, bool SPLIT, bool GATHER = false, bool TB = false,
-          bool W8 = false>
+          bool W8 = false, bool LIGHT = false>
 __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
     const bf16_t *__restrict__ A, const bf16_t *__restrict__ B1, const bf16_t *__restrict__ B3,
     void *__restrict__ C, const int32_t *__restrict__ seg_off,
     const int32_t *__restrict__ seg_end, const int32_t *__restrict__ mtile_off, int G, int N,
     int K, size_t plane, int act, int32_t *__restrict__ fix_cnt, f32x4_v *__restrict__ fix_part,
     int part_cap, const int32_t *__restrict__ gperm, int gk, uint32_t a_bytes,
-    const float *__restrict__ sc1, const float *__restrict__ sc3) {
+    const float *__restrict__ sc1, const float *__restrict__ sc3,
+    const int32_t *__restrict__ lmid, const int32_t *__restrict__ lmt) {
   constexpr int WM = 2, WN = 2;
   constexpr int TM = BM / WM / 32, TN = BNB / WN / 32;
   // A rows of 128 bytes, then B rows of 128 bytes (64 for FP8 codes)
@@ -466,6 +499,7 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
   static_assert(BM % 32 == 0 && BNB % 32 == 0, "rows per stage must split over 4 waves");
   static_assert(!TB || BNB == 256, "the [K][N] weight tile is two 128-column halves");
   static_assert(!W8 || (BM == 64 && !TB && !SPLIT), "FP8 weights: 64-row tiles of [N][K] codes");
+  static_assert(!LIGHT || (BM == 256 && !SPLIT && !W8), "light tiles: 256-row launches");
 
   __shared__ uint4 st0[STAGE_U4];
   __shared__ uint4 st1[STAGE_U4];
@@ -488,7 +522,7 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
   const int nk_all = kpl / 64;  // 64-wide K slices of a whole tile (even)
   // work units: whole tiles, then the parts of the tail tiles (reading a
   // partial back is bound by the latency of device-scope loads: about 10 slices)
-  const int R = ntn * mtile_off[G];
+  const int R = ntn * (LIGHT ? mtile_off[G] + lmt[G] : mtile_off[G]);
   const Split sp = SPLIT && gridDim.y == 1 ? plan_split(R, gridDim.x, nk_all, 100, part_cap)
                                            : Split{R, 0, 1};
   const int lrow = lane >> 3, lchunk = lane & 7;
@@ -522,6 +556,7 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
     int e;         // the unit's expert
     uint32_t ga[GATHER ? IA : 1];  // GATHER: byte offset in x of each A instruction's row
     int row0, rows, n0;
+    int light; // a light 64-row tile (LIGHT)
     int nk;    // K slices of this unit (even)
     int part;  // part of a split tail tile, or -1 for a whole tile
     int slot;  // the tail tile's index among the split ones
@@ -531,7 +566,8 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
     if (u < sp.F || sp.S == 1) {
       const int L = tile_order(u, sp.F);
       if (L < 0) return false;
-      t = decode_tile(L, mtile_off, G, ntn);
+      if constexpr (LIGHT) t = decode_tile_light(L, mtile_off, lmt, G, ntn);
+      else t = decode_tile(L, mtile_off, G, ntn);
       ta.nk = nk_all;
       ta.part = -1;
       ta.slot = 0;
@@ -548,8 +584,14 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
   auto setup = [&](const Tile &t, TileAddr &ta) {
     const int e = t.e;
     const uint32_t kb = kb_pl + (ta.part < 0 ? 0u : (uint32_t)(ta.part * ta.nk) * 128u);
-    ta.row0 = seg_off[e] + (t.g - mtile_off[e]) * BM;
-    ta.rows = min(BM, seg_end[e] - ta.row0);
+    if (LIGHT && t.light) {
+      ta.row0 = lmid[e] + t.g * 64;
+      ta.rows = min(64, seg_end[e] - ta.row0);
+    } else {
+      ta.row0 = seg_off[e] + (t.g - mtile_off[e]) * BM;
+      ta.rows = min(BM, (LIGHT ? lmid[e] : seg_end[e]) - ta.row0);
+    }
+    ta.light = LIGHT ? t.light : 0;
     ta.n0 = t.n * COLS;
     if constexpr (GATHER) {
       // the whole of x; a row past the tile's end reads at a_bytes, past the
@@ -749,6 +791,18 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
             __builtin_bit_cast(bf16x8_v, bf[b]), __builtin_bit_cast(bf16x8_v, af[a]), acc[a][b],
             0, 0, 0);
   };
+  // a light tile: rows 0..63, the first two 32-row blocks of wave row 0
+  auto mml = [&](const uint4 (&af)[TM], const uint4 (&bf)[TN]) {
+    if (wm == 0) {
+#pragma unroll
+      for (int a = 0; a < 2 && a < TM; ++a)
+#pragma unroll
+        for (int b = 0; b < TN; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8_v, bf[b]), __builtin_bit_cast(bf16x8_v, af[a]),
+              acc[a][b], 0, 0, 0);
+    }
+  };
   uint4 f0a[TM], f0b[TN], g0a[TM], g0b[TN], f1a[TM], f1b[TN], f2a[TM], f2b[TN], f3a[TM], f3b[TN];
 #define SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
 #define SG(m, n) __builtin_amdgcn_sched_group_barrier(m, n, 0)
@@ -770,20 +824,20 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
   SG(0x100, RDS - (PER - J1)); SG(8, 16 - 2 * (PER - J1)); } while (0)
 // ISSUE: the slice two ahead exists and is loaded into S; NEXT: a next slice
 // exists (wait for it, read its first K step)
-#define SLICE_BODY(S, S2, s, ca, cb, na, nb, ISSUE, NEXT)                      \
+#define SLICE_BODY(S, S2, s, ca, cb, na, nb, ISSUE, NEXT, MMF, PAT)            \
   do {                                                                         \
     rd(S, 1, f1a, f1b);                                                        \
     rd(S, 2, f2a, f2b);                                                        \
     rd(S, 3, f3a, f3b);                                                        \
-    mm(ca, cb);                                                                \
-    if constexpr (FULL) P_MM_RD();                                             \
+    MMF(ca, cb);                                                               \
+    if constexpr (PAT) P_MM_RD();                                              \
     SCHED_FENCE();                                                             \
     LGKM_WAIT0();                                                              \
     RAW_BARRIER(); /* every wave has read S */                                 \
     if constexpr (ISSUE) issue_part(cur, S, (s) + 2, 0, J1);                        \
-    mm(f1a, f1b);                                                              \
-    mm(f2a, f2b);                                                              \
-    if constexpr (FULL && ISSUE) P_MM_LD();                                    \
+    MMF(f1a, f1b);                                                             \
+    MMF(f2a, f2b);                                                             \
+    if constexpr (PAT && ISSUE) P_MM_LD();                                     \
     SCHED_FENCE();                                                             \
     if constexpr (NEXT) {                                                      \
       if constexpr (ISSUE) VM_WAIT(J1); else VM_WAIT(0);                       \
@@ -791,8 +845,8 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
       rd(S2, 0, na, nb);                                                       \
     }                                                                          \
     if constexpr (ISSUE) issue_part(cur, S, (s) + 2, J1, PER);                      \
-    mm(f3a, f3b);                                                              \
-    if constexpr (FULL && ISSUE && NEXT) P_MM_RD_LD();                         \
+    MMF(f3a, f3b);                                                             \
+    if constexpr (PAT && ISSUE && NEXT) P_MM_RD_LD();                          \
     SCHED_FENCE();                                                             \
   } while (0)
 
@@ -890,12 +944,21 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
     // nk is even (K is a multiple of 128 and S divides K / 128); the last pair
     // issues nothing.
     int kt = 0;
-    for (; kt + 2 < cur.nk; kt += 2) {
-      SLICE_BODY(st0, st1, kt, f0a, f0b, g0a, g0b, true, true);
-      SLICE_BODY(st1, st0, kt + 1, g0a, g0b, f0a, f0b, true, true);
+    if (LIGHT && cur.light) {
+      for (; kt + 2 < cur.nk; kt += 2) {
+        SLICE_BODY(st0, st1, kt, f0a, f0b, g0a, g0b, true, true, mml, false);
+        SLICE_BODY(st1, st0, kt + 1, g0a, g0b, f0a, f0b, true, true, mml, false);
+      }
+      SLICE_BODY(st0, st1, kt, f0a, f0b, g0a, g0b, false, true, mml, false);
+      SLICE_BODY(st1, st0, kt + 1, g0a, g0b, f0a, f0b, false, false, mml, false);
+    } else {
+      for (; kt + 2 < cur.nk; kt += 2) {
+        SLICE_BODY(st0, st1, kt, f0a, f0b, g0a, g0b, true, true, mm, FULL);
+        SLICE_BODY(st1, st0, kt + 1, g0a, g0b, f0a, f0b, true, true, mm, FULL);
+      }
+      SLICE_BODY(st0, st1, kt, f0a, f0b, g0a, g0b, false, true, mm, FULL);
+      SLICE_BODY(st1, st0, kt + 1, g0a, g0b, f0a, f0b, false, false, mm, FULL);
     }
-    SLICE_BODY(st0, st1, kt, f0a, f0b, g0a, g0b, false, true);
-    SLICE_BODY(st1, st0, kt + 1, g0a, g0b, f0a, f0b, false, false);
     // Every wave is past the last barrier of the unit, so no wave reads either
     // stage any more: the next unit's first two slices are loaded while the
     // epilogue runs.
@@ -954,23 +1017,24 @@ int resident_wgs(int bm) {
 }
 
 template <int BM, int BNB, bool SWIGLU, bool SPLIT = false, bool GATHER = false, bool TB = false,
-          bool W8 = false>
+          bool W8 = false, bool LIGHT = false>
 hipError_t launch_dl(const void *A, const void *B1, const void *B3, void *C,
                      const int32_t *seg_off, const int32_t *seg_end, const int32_t *mtile_off,
                      int G, int N, int K, int ksplit, size_t plane, int act, const FixScratch &fx,
                      hipStream_t s, const int32_t *gperm = nullptr, int gk = 1,
                      uint32_t a_bytes = 0, const float *sc1 = nullptr,
-                     const float *sc3 = nullptr) {
+                     const float *sc3 = nullptr, const int32_t *lmid = nullptr,
+                     const int32_t *lmt = nullptr) {
   // persistent grid: what stays resident, a multiple of the XCD count
   const int gx = (resident_wgs(BM) / ksplit + NUM_XCD - 1) / NUM_XCD * NUM_XCD;
   const size_t cap = fx.part ? fx.part_bytes / ((size_t)BM * BNB * 4) : 0;
-  hipLaunchKernelGGL((grouped_gemm_dl_kernel<BM, BNB, SWIGLU, SPLIT, GATHER, TB, W8>),
+  hipLaunchKernelGGL((grouped_gemm_dl_kernel<BM, BNB, SWIGLU, SPLIT, GATHER, TB, W8, LIGHT>),
                      dim3(gx, ksplit),
                      dim3(GM_THREADS), 0, s, (const bf16_t *)A, (const bf16_t *)B1,
                      (const bf16_t *)B3, C, seg_off, seg_end ? seg_end : seg_off + 1, mtile_off, G,
                      N, K, plane, act, fx.cnt, (f32x4_v *)fx.part,
                      (int)(cap < (size_t)FIX_SLOTS * 16 ? cap : (size_t)FIX_SLOTS * 16), gperm,
-                     gk, a_bytes, sc1, sc3);
+                     gk, a_bytes, sc1, sc3, lmid, lmt);
   return hipGetLastError();
 }
 
@@ -1018,8 +1082,20 @@ hipError_t gemm_swiglu_t(int dtype, bool dl, int bm, int act, const void *A, con
                          const void *W3, void *H, const int32_t *seg_off,
                          const int32_t *mtile_off, int G, int N, int K, int max_mtiles,
                          hipStream_t s, const int32_t *seg_end, const int32_t *gperm, int gk,
-                         long long a_bytes) {
+                         long long a_bytes, const int32_t *lmid, const int32_t *lmt) {
   const FixScratch none{nullptr, nullptr, 0};
+  if (lmt) {  // 256-row tiles with light tiles for the rows past them
+    if (!dl || bm != 256 || !lmid || !seg_end) return hipErrorInvalidValue;
+    if (gperm) {
+      if (!gemm_gather_ok(dtype, dl, bm, a_bytes)) return hipErrorInvalidValue;
+      return launch_dl<256, 256, true, false, true, TB, false, true>(
+          A, W1, W3, H, seg_off, seg_end, mtile_off, G, N, K, 1, 0, act, none, s, gperm, gk,
+          (uint32_t)a_bytes, nullptr, nullptr, lmid, lmt);
+    }
+    return launch_dl<256, 256, true, false, false, TB, false, true>(
+        A, W1, W3, H, seg_off, seg_end, mtile_off, G, N, K, 1, 0, act, none, s, nullptr, 1, 0,
+        nullptr, nullptr, lmid, lmt);
+  }
   if (gperm) {
     if (!gemm_gather_ok(dtype, dl, bm, a_bytes)) return hipErrorInvalidValue;
     if (bm == 64)
@@ -1048,8 +1124,15 @@ template <bool TB>
 hipError_t gemm_down_t(int dtype, bool dl, int bm, const void *A, const void *W2, void *Y,
                        const int32_t *seg_off, const int32_t *mtile_off, int G, int N, int K,
                        int max_mtiles, int ksplit, size_t plane, const FixScratch &fx,
-                       hipStream_t s, const int32_t *seg_end, bool ybf16) {
+                       hipStream_t s, const int32_t *seg_end, bool ybf16, const int32_t *lmid,
+                       const int32_t *lmt) {
   const int yb = ybf16 ? 1 : 0;
+  if (lmt) {  // 256-row tiles with light tiles for the rows past them
+    if (!dl || bm != 256 || !lmid || !seg_end) return hipErrorInvalidValue;
+    return launch_dl<256, 256, false, false, false, TB, false, true>(
+        A, W2, nullptr, Y, seg_off, seg_end, mtile_off, G, N, K, ksplit, plane, yb, fx, s,
+        nullptr, 1, 0, nullptr, nullptr, lmid, lmt);
+  }
   if (dl && bm == 64)
     return launch_dl<64, 256, false, false, false, TB>(A, W2, nullptr, Y, seg_off, seg_end,
                                                        mtile_off, G, N, K, ksplit, plane, yb,
@@ -1077,12 +1160,13 @@ hipError_t launch_gemm_swiglu(int dtype, bool dl, int bm, int act, const void *A
                               const void *W1, const void *W3, void *H, const int32_t *seg_off,
                               const int32_t *mtile_off, int G, int N, int K, int max_mtiles,
                               hipStream_t s, const int32_t *seg_end, const int32_t *gperm, int gk,
-                              long long a_bytes, bool tb) {
+                              long long a_bytes, bool tb, const int32_t *lmid,
+                              const int32_t *lmt) {
   if (max_mtiles <= 0) return hipSuccess;
   return tb ? gemm_swiglu_t<true>(dtype, dl, bm, act, A, W1, W3, H, seg_off, mtile_off, G, N, K,
-                                  max_mtiles, s, seg_end, gperm, gk, a_bytes)
+                                  max_mtiles, s, seg_end, gperm, gk, a_bytes, lmid, lmt)
             : gemm_swiglu_t<false>(dtype, dl, bm, act, A, W1, W3, H, seg_off, mtile_off, G, N, K,
-                                   max_mtiles, s, seg_end, gperm, gk, a_bytes);
+                                   max_mtiles, s, seg_end, gperm, gk, a_bytes, lmid, lmt);
 }
 
 hipError_t launch_gemm_swiglu_fp8(int act, const void *A, const uint8_t *W1q, const uint8_t *W3q,
@@ -1121,13 +1205,14 @@ hipError_t launch_gemm_down_fp8(const void *A, const uint8_t *W2q, const float *
 hipError_t launch_gemm_down(int dtype, bool dl, int bm, const void *A, const void *W2, void *Y,
                             const int32_t *seg_off, const int32_t *mtile_off, int G, int N, int K,
                             int max_mtiles, int ksplit, size_t plane, const FixScratch &fx,
-                            hipStream_t s, const int32_t *seg_end, bool ybf16, bool tb) {
+                            hipStream_t s, const int32_t *seg_end, bool ybf16, bool tb,
+                            const int32_t *lmid, const int32_t *lmt) {
   if (max_mtiles <= 0) return hipSuccess;
   if (ybf16 && (!dl || ksplit != 1)) return hipErrorInvalidValue;
   return tb ? gemm_down_t<true>(dtype, dl, bm, A, W2, Y, seg_off, mtile_off, G, N, K, max_mtiles,
-                                ksplit, plane, fx, s, seg_end, ybf16)
+                                ksplit, plane, fx, s, seg_end, ybf16, lmid, lmt)
             : gemm_down_t<false>(dtype, dl, bm, A, W2, Y, seg_off, mtile_off, G, N, K,
-                                 max_mtiles, ksplit, plane, fx, s, seg_end, ybf16);
+                                 max_mtiles, ksplit, plane, fx, s, seg_end, ybf16, lmid, lmt);
 }
 
 }  // namespace moe

@@ -111,6 +111,10 @@ struct FixScratch {
 size_t fix_part_bytes(long long tiles);
 // act: 0 SiLU(W1 a) * (W3 a), 1 sigmoid(W1 a) * (W3 a)
 // tb: the weights are [K][N] per expert (in x out, A W) instead of [N][K]
+// lmid / lmt (256-row direct-to-LDS tiles only): the same launch also serves
+// each expert's rows from lmid[e] to seg_end[e] as light 64-row tiles (lmt:
+// their prefix over the experts) placed after its full tiles, which end at
+// lmid[e]
 // seg_end (direct-to-LDS kernel only; NULL: seg_off + 1): expert e's rows
 // are seg_off[e] .. seg_end[e] - 1, with mtile_off the prefix of its tiles.
 // gperm (gemm_gather_ok only): A is x itself (a_bytes bytes) and grouped row s
@@ -121,7 +125,8 @@ hipError_t launch_gemm_swiglu(int dtype, bool dl, int bm, int act, const void *A
                               const int32_t *mtile_off, int G, int N, int K, int max_mtiles,
                               hipStream_t s, const int32_t *seg_end = nullptr,
                               const int32_t *gperm = nullptr, int gk = 1, long long a_bytes = 0,
-                              bool tb = false);
+                              bool tb = false, const int32_t *lmid = nullptr,
+                              const int32_t *lmt = nullptr);
 // ksplit > 1 (direct-to-LDS kernel only): every tile's K is split in ksplit
 // equal ranges whose fp32 partials go to planes `plane` elements apart (for
 // batches with few tiles; the last-round split then stays off).
@@ -130,7 +135,8 @@ hipError_t launch_gemm_down(int dtype, bool dl, int bm, const void *A, const voi
                             const int32_t *seg_off, const int32_t *mtile_off, int G, int N, int K,
                             int max_mtiles, int ksplit, size_t plane, const FixScratch &fx,
                             hipStream_t s, const int32_t *seg_end = nullptr, bool ybf16 = false,
-                            bool tb = false);
+                            bool tb = false, const int32_t *lmid = nullptr,
+                            const int32_t *lmt = nullptr);
 
 // The 64-row tiled GEMMs on FP8 (E4M3) expert weights [N][K] with per-expert
 // scales (s1 / s3 / s2 [E]); arguments otherwise as launch_gemm_swiglu /
