@@ -544,7 +544,7 @@ def main():
     variants = []
     if not args.no_extra and cfg.d == 4096 and cfg.E == 8 and cfg.T == 8192:
         skew = CONFIGS["mixtral_prefill_T8192_skew"]
-        cap = moe.capacity(skew.T, skew.k, 1.2 * skew.k / skew.E)  # 1.2 x the mean load
+        cap = moe.capacity_mean(skew.T, skew.k, skew.E, 1.2)  # 1.2 x the mean load
         for label, c2, kw in [
                 ("capacity_1.2x_mean_load_skew", skew, dict(capacity=cap)),
                 ("gate_softmax_all", cfg, dict(gate_mode=moe.GATE_SOFTMAX_ALL)),

@@ -222,6 +222,12 @@ typedef struct moe_options_s {
  * Host-only arithmetic; returns -1 for T < 0, k < 1 or cf < 0. */
 int moe_capacity(int T, int k, double capacity_factor);
 
+/* The capacity as cf times an expert's mean load: ceil(cf * T * k / E) (the
+ * page's formula above compares cf with the batch alone, so for k >= 2 it
+ * never limits an expert: an expert holds at most T pairs).  Host-only;
+ * -1 for T < 0, k < 1, E < 1 or cf < 0; saturates at INT32_MAX. */
+int moe_capacity_mean(int T, int k, int E, double capacity_factor);
+
 /* moe_route with a gate variant (gate_mode as above); MOE_EINVAL for an
  * unknown mode, or an entropy-aware mode with k < 2. */
 int moe_route_ex(const void *x, const void *Wg, const float *bias, int T, int d, int E, int k,

@@ -225,6 +225,12 @@ int moe_capacity(int T, int k, double capacity_factor) {
   return cap > INT32_MAX ? INT32_MAX : (int)cap;
 }
 
+int moe_capacity_mean(int T, int k, int E, double capacity_factor) {
+  if (T < 0 || k < 1 || E < 1 || !(capacity_factor >= 0.0)) return -1;
+  const double c = std::ceil(capacity_factor * (double)T * (double)k / (double)E);
+  return c >= (double)INT32_MAX ? INT32_MAX : (int)c;
+}
+
 size_t moe_permute_workspace_bytes(int T, int E, int k) {
   if (T < 0 || E < 1 || k < 1) return 0;
   const size_t nb = (size_t)moe::permute_nblocks(T * k);

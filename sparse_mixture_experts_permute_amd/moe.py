@@ -68,6 +68,8 @@ def lib():
         L.moe_strerror.restype = ctypes.c_char_p
         L.moe_capacity.argtypes = [i, i, ctypes.c_double]
         L.moe_capacity.restype = i
+        L.moe_capacity_mean.argtypes = [i, i, i, ctypes.c_double]
+        L.moe_capacity_mean.restype = i
         L.moe_route_ex.argtypes = [vp, vp, vp, i, i, i, i, i, i, vp, vp, vp, vp, sz, vp]
         L.moe_route_ex.restype = i
         L.moe_permute_ex.argtypes = [vp, i, i, i, i, vp, vp, vp, vp, vp, sz, vp]
@@ -167,6 +169,14 @@ def tensor_to_numpy(t: torch.Tensor) -> np.ndarray:
 def capacity(T: int, k: int, capacity_factor: float = 1.2) -> int:
     """Per-expert capacity min(k*T, floor(cf*T)) for a batch of T tokens."""
     c = lib().moe_capacity(T, k, float(capacity_factor))
+    if c < 0:
+        raise MoEError("invalid capacity arguments")
+    return c
+
+
+def capacity_mean(T: int, k: int, E: int, capacity_factor: float = 1.2) -> int:
+    """Per-expert capacity ceil(cf * T * k / E): cf times an expert's mean load."""
+    c = lib().moe_capacity_mean(T, k, E, float(capacity_factor))
     if c < 0:
         raise MoEError("invalid capacity arguments")
     return c

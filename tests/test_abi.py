@@ -239,3 +239,15 @@ def test_noalloc_rejects_before_launch(L):
     assert L.moe_forward_noalloc(*args, 8, 8, 9, 4096, 14336, 1, fake, None) == -1  # k > E
     assert L.moe_forward_noalloc(*args, 8, 8, 2, 4096, 14336, 5, fake, None) == -2  # dtype
     assert b"static" in L.moe_strerror(-6)
+
+
+def test_capacity_mean(L):
+    """ceil(cf * T * k / E): 1.2 x the mean load of the Mixtral-shaped prefill
+    (8192 tokens, top-2, 8 experts: mean 2048) is 2457.6 -> 2458."""
+    assert L.moe_capacity_mean(8192, 2, 8, 1.2) == 2458
+    assert L.moe_capacity_mean(512, 8, 128, 1.0) == 32
+    assert L.moe_capacity_mean(512, 8, 128, 1.25) == 40
+    assert L.moe_capacity_mean(1, 1, 256, 1.0) == 1
+    assert L.moe_capacity_mean(0, 2, 8, 1.2) == 0
+    assert L.moe_capacity_mean(-1, 2, 8, 1.2) == -1
+    assert L.moe_capacity_mean(4, 2, 0, 1.2) == -1
