@@ -80,9 +80,9 @@ struct Tile {
   int light;  // a 64-row light tile of a 256-row launch (below)
 };
 // Position in the logical order of the tile that workgroup slot hw takes, or
-// -1 (a surplus slot).  R tiles; the grid holds gridDim.x workgroups.
-__device__ __forceinline__ int tile_order(int hw, int R) {
-  const int cpx = max(1, (int)gridDim.x / NUM_XCD);  // resident workgroups per XCD
+// -1 (a surplus slot).  R tiles; W workgroups walk them (a multiple of 8).
+__device__ __forceinline__ int tile_order(int hw, int R, int W) {
+  const int cpx = max(1, W / NUM_XCD);  // resident workgroups per XCD
   const int R8 = (R + NUM_XCD - 1) / NUM_XCD;
   const int rounds = max(1, (R8 + cpx - 1) / cpx);
   const int BS = max(1, (R + NUM_XCD * rounds - 1) / (NUM_XCD * rounds));
@@ -131,7 +131,7 @@ __device__ __forceinline__ Tile decode_tile_light(int L, const int32_t *mt0, con
 }
 __device__ __forceinline__ bool map_tile(int hw, const int32_t *mtile_off, int G, int ntn,
                                          Tile &t) {
-  const int L = tile_order(hw, ntn * mtile_off[G]);
+  const int L = tile_order(hw, ntn * mtile_off[G], gridDim.x);
   if (L < 0) return false;
   t = decode_tile(L, mtile_off, G, ntn);
   return true;
@@ -523,7 +523,19 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
   // work units: whole tiles, then the parts of the tail tiles (reading a
   // partial back is bound by the latency of device-scope loads: about 10 slices)
   const int R = ntn * (LIGHT ? mtile_off[G] + lmt[G] : mtile_off[G]);
-  const Split sp = SPLIT && gridDim.y == 1 ? plan_split(R, gridDim.x, nk_all, 100, part_cap)
+  // Workgroups in use.  64-row tiles serve weight-streaming batches, where a
+  // partly used last round costs bandwidth: as many workgroups as give every
+  // one the same number of tiles walk them, the rest exit (Mixtral-shaped
+  // decode, 784 tiles on 512 resident workgroups: SwiGLU GEMM 0.308 -> 0.286
+  // ms at 8 tokens).  Larger tiles keep the whole grid (the last-round split
+  // spreads their tail).
+  int Wg = gridDim.x;
+  if constexpr (BM == 64) {
+    const int rounds = max(1, (R + Wg - 1) / Wg);  // R may be 0 (every pair dropped)
+    Wg = min((int)gridDim.x, ((R + rounds - 1) / rounds + NUM_XCD - 1) / NUM_XCD * NUM_XCD);
+  }
+  if ((int)blockIdx.x >= Wg) return;
+  const Split sp = SPLIT && gridDim.y == 1 ? plan_split(R, Wg, nk_all, 100, part_cap)
                                            : Split{R, 0, 1};
   const int lrow = lane >> 3, lchunk = lane & 7;
 
@@ -564,7 +576,7 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
   // work unit u -> tile and K range (false: no unit u)
   auto map_unit = [&](int u, Tile &t, TileAddr &ta) -> bool {
     if (u < sp.F || sp.S == 1) {
-      const int L = tile_order(u, sp.F);
+      const int L = tile_order(u, sp.F, Wg);
       if (L < 0) return false;
       if constexpr (LIGHT) t = decode_tile_light(L, mtile_off, lmt, G, ntn);
       else t = decode_tile(L, mtile_off, G, ntn);
@@ -913,8 +925,8 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
     return true;
   };
 
-  // Persistent: the workgroup walks the work units in steps of the grid size
-  // (a multiple of the XCD count, so it stays on its XCD's chunk).  The next
+  // Persistent: the workgroup walks the work units in steps of Wg (a
+  // multiple of the XCD count, so it stays on its XCD's chunk).  The next
   // unit's first slices are loaded while the current unit's epilogue runs.
   int hw = blockIdx.x;
   Tile tile;
@@ -962,7 +974,7 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
     // Every wave is past the last barrier of the unit, so no wave reads either
     // stage any more: the next unit's first two slices are loaded while the
     // epilogue runs.
-    hw += gridDim.x;
+    hw += Wg;
     Tile nt;
     TileAddr nxt;
     const bool more = map_unit(hw, nt, nxt);
