@@ -121,7 +121,17 @@ int launched(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ELAUNCH; }
 // last part reads the other parts back).  From one round on, that last-round
 // split serves instead.
 int down_splits(const moe::GemmPlan &plan, int T, int k, int E, int d, int d_ff) {
-  if (!plan.dl2) return 1;
+  if (!plan.dl2) {
+    // the register-staged kernel (128 x 128 tiles, two workgroups per CU):
+    // K parts of a multiple of 64 until the grid covers every CU twice
+    const long long P = (long long)T * k;
+    const long long active = P < E ? P : E;
+    const long long mt_floor = (P + 127) / 128;
+    const long long wgs = (active > mt_floor ? active : mt_floor) * ((d + 127) / 128);
+    int S = 1;
+    while (wgs * S < 512 && S < 16 && d_ff % (64 * S * 2) == 0) S *= 2;
+    return S;
+  }
   const long long P = (long long)T * k;
   const long long active = P < E ? P : E;  // experts that can hold rows
   const long long mt_floor = (P + plan.bm2 - 1) / plan.bm2;

@@ -176,7 +176,7 @@ template <typename T, int BM, int BNB, int WM, int WN, bool SWIGLU, bool TB = fa
 __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_kernel(
     const T *__restrict__ A, const T *__restrict__ B1, const T *__restrict__ B3,
     void *__restrict__ C, const int32_t *__restrict__ seg_off,
-    const int32_t *__restrict__ mtile_off, int G, int N, int K, int act) {
+    const int32_t *__restrict__ mtile_off, int G, int N, int K, int act, size_t plane) {
   constexpr int BK = MfmaTraits<T>::BK;
   constexpr int ES = sizeof(T);
   constexpr int CPR = BK * ES / 16;            // 16-byte chunks per tile row (8)
@@ -199,6 +199,10 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_kernel(
   const int rows = min(BM, seg_off[e + 1] - row0);
   const int NOUT = N;  // output columns
   const int n0 = tile.n * COLS;  // first output column
+  // K planes (down projection): blockIdx.y takes one of gridDim.y equal K
+  // ranges and writes its fp32 sums to output plane blockIdx.y (plane
+  // elements apart); the combine adds the planes in order
+  const int Kp = K / gridDim.y, kbeg = blockIdx.y * Kp;
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = lane_id();
@@ -214,7 +218,8 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_kernel(
     int c = tid + i * GM_THREADS;
     int r = c / CPR, q = c % CPR;
     int rr = min(r, rows - 1);
-    srcA[i] = reinterpret_cast<const uint4 *>(A) + (size_t)(row0 + rr) * rowq + q;
+    srcA[i] = reinterpret_cast<const uint4 *>(A) + (size_t)(row0 + rr) * rowq + q +
+              (size_t)kbeg * ES / 16;
     dstA[i] = r * LDW + q;
   }
   const size_t bexp = (size_t)e * N * rowq;  // expert offset in uint4
@@ -238,7 +243,7 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_kernel(
         base = B1;
       }
       col = min(col, N - VE);
-      srcB[i] = reinterpret_cast<const uint4 *>(base + ((size_t)e * K + kk) * N + col);
+      srcB[i] = reinterpret_cast<const uint4 *>(base + ((size_t)e * K + kbeg + kk) * N + col);
       dstB[i] = (BM + r) * LDW * VE + kk;  // in elements
       continue;
     }
@@ -254,7 +259,8 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_kernel(
       base = B1;
     }
     col = min(col, N - 1);
-    srcB[i] = reinterpret_cast<const uint4 *>(base) + bexp + (size_t)col * rowq + q;
+    srcB[i] = reinterpret_cast<const uint4 *>(base) + bexp + (size_t)col * rowq + q +
+              (size_t)kbeg * ES / 16;
     dstB[i] = (BM + r) * LDW + q;
   }
 
@@ -267,7 +273,7 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_kernel(
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
 
   uint4 ra[A_CH], rb[B_CH];
-  const int nk = K / BK;
+  const int nk = Kp / BK;
   auto gload = [&](int kt) {
     const size_t ko = (size_t)kt * CPR;
 #pragma unroll
@@ -349,7 +355,8 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_kernel(
 #pragma unroll
         for (int b = 0; b < TN; ++b) {
           const int col = n0 + (wn * TN + b) * 32 + ccol;
-          if (col < N) reinterpret_cast<float *>(C)[orow + col] = acc[a][b][i];
+          if (col < N)
+            reinterpret_cast<float *>(C)[blockIdx.y * plane + orow + col] = acc[a][b][i];
         }
       }
     }
@@ -1053,12 +1060,15 @@ hipError_t launch_dl(const void *A, const void *B1, const void *B3, void *C,
 template <typename T, int BM, int BNB, int WM, int WN, bool SWIGLU, bool TB>
 hipError_t launch_one(const void *A, const void *B1, const void *B3, void *C,
                       const int32_t *seg_off, const int32_t *mtile_off, int G, int N, int K,
-                      int max_mtiles, int act, hipStream_t s) {
+                      int max_mtiles, int act, hipStream_t s, int ksplit = 1,
+                      size_t plane = 0) {
   const int cols = SWIGLU ? BNB / 2 : BNB;
-  dim3 grid(((N + cols - 1) / cols) * max_mtiles + NUM_XCD);
+  if (ksplit < 1 || (SWIGLU && ksplit != 1) || K % (ksplit * MfmaTraits<T>::BK))
+    return hipErrorInvalidValue;
+  dim3 grid(((N + cols - 1) / cols) * max_mtiles + NUM_XCD, ksplit);
   hipLaunchKernelGGL((grouped_gemm_kernel<T, BM, BNB, WM, WN, SWIGLU, TB>), grid, dim3(GM_THREADS),
                      0, s, (const T *)A, (const T *)B1, (const T *)B3, C, seg_off, mtile_off, G,
-                     N, K, act);
+                     N, K, act, plane);
   return hipGetLastError();
 }
 
@@ -1161,9 +1171,10 @@ hipError_t gemm_down_t(int dtype, bool dl, int bm, const void *A, const void *W2
   if (seg_end) return hipErrorInvalidValue;  // the tiled kernels take whole segments
   if (dtype == 1)
     return launch_one<bf16_t, 128, 128, 2, 2, false, TB>(A, W2, nullptr, Y, seg_off, mtile_off,
-                                                         G, N, K, max_mtiles, 0, s);
+                                                         G, N, K, max_mtiles, 0, s, ksplit,
+                                                         plane);
   return launch_one<float, 128, 128, 2, 2, false, TB>(A, W2, nullptr, Y, seg_off, mtile_off, G,
-                                                      N, K, max_mtiles, 0, s);
+                                                      N, K, max_mtiles, 0, s, ksplit, plane);
 }
 
 }  // namespace
