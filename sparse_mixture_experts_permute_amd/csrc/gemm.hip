@@ -54,11 +54,16 @@ template <> struct MfmaTraits<bf16_t> {
 template <> struct MfmaTraits<float> {
   static constexpr int BK = 32;
   static constexpr int FRAG_U4 = 2;
+  // the fragments stay in registers: each uint4 is reinterpreted as a value
+  // (a float pointer into the fragment arrays would put them in scratch)
   __device__ __forceinline__ static void mma(const uint4 *a, const uint4 *b, f32x16_v &c) {
-    const float *af = reinterpret_cast<const float *>(a);
-    const float *bf = reinterpret_cast<const float *>(b);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) c = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i], bf[i], c, 0, 0, 0);
+    for (int u = 0; u < FRAG_U4; ++u) {
+      const f32x4_v av = __builtin_bit_cast(f32x4_v, a[u]);
+      const f32x4_v bv = __builtin_bit_cast(f32x4_v, b[u]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) c = __builtin_amdgcn_mfma_f32_32x32x2f32(av[i], bv[i], c, 0, 0, 0);
+    }
   }
   __device__ __forceinline__ static void store(float *p, size_t i, float v) { p[i] = v; }
 };
@@ -272,18 +277,23 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_kernel(
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
 
-  uint4 ra[A_CH], rb[B_CH];
+  // staging registers of the next K slice, as plain vectors (uint4 arrays
+  // copied through here stayed in scratch memory, which serialised every
+  // slice's global loads ahead of its MFMAs)
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  u32x4_t ra[A_CH], rb[B_CH];
   const int nk = Kp / BK;
   auto gload = [&](int kt) {
     const size_t ko = (size_t)kt * CPR;
 #pragma unroll
-    for (int i = 0; i < A_CH; ++i) ra[i] = srcA[i][ko];
+    for (int i = 0; i < A_CH; ++i) ra[i] = *reinterpret_cast<const u32x4_t *>(srcA[i] + ko);
 #pragma unroll
-    for (int i = 0; i < B_CH; ++i) rb[i] = srcB[i][(size_t)kt * bstep];
+    for (int i = 0; i < B_CH; ++i)
+      rb[i] = *reinterpret_cast<const u32x4_t *>(srcB[i] + (size_t)kt * bstep);
   };
   auto lstore = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < A_CH; ++i) lds[buf][dstA[i]] = ra[i];
+    for (int i = 0; i < A_CH; ++i) *reinterpret_cast<u32x4_t *>(&lds[buf][dstA[i]]) = ra[i];
 #pragma unroll
     for (int i = 0; i < B_CH; ++i) {
       if constexpr (TB) {
@@ -293,7 +303,7 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_kernel(
 #pragma unroll
         for (int u = 0; u < VE; ++u) l[dstB[i] + u * LDW * VE] = v[u];
       } else {
-        lds[buf][dstB[i]] = rb[i];
+        *reinterpret_cast<u32x4_t *>(&lds[buf][dstB[i]]) = rb[i];
       }
     }
   };
