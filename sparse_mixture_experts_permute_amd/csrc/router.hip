@@ -293,6 +293,57 @@ __global__ __launch_bounds__(256) void router_narrow_kernel(
   }
 }
 
+// Small batches with up to 32 experts: one wavefront per token, in one
+// launch.  Lane l takes the 16-byte chunks l, l + 64, ... of the token's row
+// and of every router row (U steps in flight), the sums are reduced over the
+// 64 lanes, and the lanes then run top-k and the gate as in the kernel above
+// (lane j < k writes pick j).  Against the d-split kernel plus its top-k
+// launch, this saves a launch and the partial sums' round trip.
+template <typename T, int EB>
+__global__ __launch_bounds__(256) void router_wave_kernel(
+    const T *__restrict__ x, const T *__restrict__ Wg, int T_, int d, int E,
+    const float *__restrict__ bias, int k, int gate_mode, int32_t *__restrict__ idx,
+    float *__restrict__ gate, float *__restrict__ logits) {
+  constexpr int VEC = RouterTraits<T>::VEC;
+  constexpr int U = EB <= 8 ? 4 : EB <= 16 ? 2 : 1;
+  const int lane = lane_id();
+  const int t = blockIdx.x * 4 + (int)threadIdx.x / kWave;
+  if (t >= T_) return;  // the whole wavefront: no barrier follows
+  const int rowq = d / VEC;  // a multiple of 64
+  const int nq = rowq / 64;
+  const uint4 *xr = reinterpret_cast<const uint4 *>(x) + (size_t)t * rowq;
+  const uint4 *wgg = reinterpret_cast<const uint4 *>(Wg);
+  float acc[EB];
+#pragma unroll
+  for (int e = 0; e < EB; ++e) acc[e] = 0.f;
+  for (int i = 0; i < nq; i += U) {
+    uint4 xv[U], wv[U][EB];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool in = i + u < nq;
+      const int q = (i + u) * 64 + lane;
+      xv[u] = in ? xr[q] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < EB; ++e)
+        wv[u][e] = in && e < E ? wgg[(size_t)e * rowq + q] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int e = 0; e < EB; ++e) acc[e] = dot16b(xv[u], wv[u][e], acc[e], T());
+  }
+#pragma unroll
+  for (int e = 0; e < EB; ++e)
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) acc[e] += __shfl_xor(acc[e], off);
+#pragma unroll
+  for (int e = 0; e < EB; ++e) {
+    if (bias && e < E) acc[e] += bias[e];
+    if (logits && e < E && e == lane) logits[(size_t)t * E + e] = acc[e];
+  }
+  group_topk_gate(acc, E, k, gate_mode, lane, idx + (size_t)t * k, gate + (size_t)t * k);
+}
+
 // Large batches with a small router (E <= 16, E * d * size <= 64 KB, k <= 16):
 // the workgroup copies the router weights into LDS once and streams 16 tokens'
 // rows, four per wavefront with 16 lanes each (per step 256 contiguous bytes
@@ -591,6 +642,9 @@ hipError_t launch_router(int dtype, const void *x, const void *Wg, const float *
 }
 
 namespace {
+// Batches up to this many tokens route with one wavefront per token.
+constexpr int ROUTER_WAVE_MAX_T = 2048;
+
 hipError_t launch_router_scores_topk(int dtype, const void *x, const void *Wg, const float *bias,
                                      int T, int d, int E, int k, int gate_mode, int32_t *idx,
                                      float *gate, float *logits, float *part, hipStream_t s) {
@@ -610,6 +664,19 @@ hipError_t launch_router_scores_topk(int dtype, const void *x, const void *Wg, c
       if (E <= 8) RL_LAUNCH(float, 8); else RL_LAUNCH(float, 16);
     }
 #undef RL_LAUNCH
+    return hipGetLastError();
+  }
+  if (E <= 32 && k <= 16 && T <= ROUTER_WAVE_MAX_T && (d / (16 / es)) % 64 == 0) {
+    // small batches: one wavefront per token, top-k in the same launch
+#define RW_LAUNCH(TT, EB)                                                                       \
+  hipLaunchKernelGGL((router_wave_kernel<TT, EB>), dim3((T + 3) / 4), dim3(256), 0, s,          \
+                     (const TT *)x, (const TT *)Wg, T, d, E, bias, k, gate_mode, idx, gate, logits)
+    if (dtype == 1) {
+      if (E <= 8) RW_LAUNCH(bf16_t, 8); else if (E <= 16) RW_LAUNCH(bf16_t, 16); else RW_LAUNCH(bf16_t, 32);
+    } else {
+      if (E <= 8) RW_LAUNCH(float, 8); else if (E <= 16) RW_LAUNCH(float, 16); else RW_LAUNCH(float, 32);
+    }
+#undef RW_LAUNCH
     return hipGetLastError();
   }
   if (r.narrow && r.S == 1 && k <= 16) {
