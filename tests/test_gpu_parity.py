@@ -273,6 +273,12 @@ EDGE = [
     ("split_below_256_E12", 3000, 256, 12, 256, 1, "bf16", 0, None),
     ("split_kplanes", 1100, 256, 4, 2048, 1, "bf16", 0, None),
     ("split_shared", 1500, 256, 4, 256, 1, "bf16", 256, None),
+    # the one-launch router (a wavefront per token, up to 2048 tokens): its largest expert count and k,
+    # an expert count that leaves part of its 32-wide register block unused, and the first batch past
+    # it (feature-split scores plus a top-k launch)
+    ("router_wave_T2048_E32_k16", 2048, 512, 32, 256, 16, "bf16", 0, None),
+    ("router_wave_E17_f32", 300, 512, 17, 256, 3, "f32", 0, None),
+    ("router_split_T2049_E17_f32", 2049, 512, 17, 256, 3, "f32", 0, None),
     # one token routed inside the SwiGLU weight-streaming kernel (E * d <= 65536)
     ("routed_T1_E32_k4_hot", 1, 2048, 32, 2048, 4, "bf16", 0, ("hot", 31, 100.0)),
     ("routed_T1_E16_shared_limit", 1, 4096, 16, 2048, 2, "bf16", 4096, None),
