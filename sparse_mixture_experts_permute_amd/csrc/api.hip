@@ -400,7 +400,7 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
   const bool fused_combine = sk.gemv && !shared && !tb;
   // a single token with a small router: the SwiGLU weight-streaming kernel
   // routes it itself (no score or top-k launches)
-  const bool route_fused = sk.gemv && !tb && moe::route_fused_ok(T, d, E, k);
+  const bool route_fused = sk.gemv && moe::route_fused_ok(T, d, E, k);
   const moe::DecodeRoute rt{Wg, bias, E, k, gmode,
                             o.capacity < 0 || o.capacity > P ? P : o.capacity,
                             plan.bm1, plan.bm2, logits, idx, gate, counts, offsets, perm, inv,
@@ -461,7 +461,9 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
     MOE_MARK(3);
     // a single token activates exactly k experts (fewer only under a capacity)
     const int nact = T == 1 ? k : 0;
-    if ((e = route_fused
+    if ((e = route_fused && tb
+                 ? moe::launch_gemv_t_swiglu_routed(o.activation, x, rt, W1, W3, H, d_ff, d, s)
+             : route_fused
                  ? moe::launch_gemv_swiglu_routed(o.activation, x, rt, f8 ? f8->W1q : W1,
                                                   f8 ? f8->W3q : W3, f8 ? f8->s1 : nullptr,
                                                   f8 ? f8->s3 : nullptr, H, d_ff, d, s)

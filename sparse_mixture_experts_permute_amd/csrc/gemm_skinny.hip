@@ -727,16 +727,27 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_swiglu_wave_kernel(
 // columns are then reduced by the butterfly and the wavefronts through LDS,
 // both in a fixed order.
 // ---------------------------------------------------------------------------
-template <bool SWIGLU, int R, int CW>
+// ROUTE (SwiGLU, one token): the workgroup routes the token itself first, as
+// gemv_kernel's ROUTE variant does.
+template <bool SWIGLU, int R, int CW, bool ROUTE = false>
 __global__ __launch_bounds__(GV_THREADS) void gemv_t_kernel(
     const bf16_t *__restrict__ A, const int32_t *__restrict__ perm, int kslots,
     const bf16_t *__restrict__ B1, const bf16_t *__restrict__ B3, void *__restrict__ C,
     const int32_t *__restrict__ seg_off, const int32_t *__restrict__ active,
-    const int32_t *__restrict__ nactive, int N, int K, int act, size_t plane) {
+    const int32_t *__restrict__ nactive, int N, int K, int act, size_t plane, DecodeRoute rt) {
+  static_assert(SWIGLU || !ROUTE, "a token is routed before its SwiGLU projection");
   constexpr int NW = SWIGLU ? 2 : 1;
   constexpr int LPR = CW / 8;     // lanes per k-row
   constexpr int KG = kWave / LPR; // k-rows per wavefront instruction
   __shared__ float red[GV_WAVES][NW][R][CW];
+  __shared__ typename std::conditional<ROUTE, RouteLds, char>::type rsh;
+  if constexpr (ROUTE) {
+    route_token(A, K, rt, rsh);
+    seg_off = rsh.offsets;
+    active = rsh.active;
+    nactive = rsh.active + rt.E;
+    perm = rsh.perm;
+  }
   const int nblk = N / CW;
   const int a_idx = blockIdx.x / nblk;
   if (a_idx >= nactive[0]) return;
@@ -887,7 +898,7 @@ hipError_t launch_gemv_t_r(int act, const void *A, const int32_t *perm, int kslo
 #define GVT_LAUNCH(CW_)                                                                       \
   hipLaunchKernelGGL((gemv_t_kernel<SWIGLU, R, CW_>), dim3(G * (N / CW_), ksplit),           \
                      dim3(GV_THREADS), 0, s, a, perm, kslots, b1, b3, C, seg_off, active,    \
-                     nactive, N, K, act, plane)
+                     nactive, N, K, act, plane, DecodeRoute{})
   switch (cw) {
     case 256: GVT_LAUNCH(256); break;
     case 128: GVT_LAUNCH(128); break;
@@ -1050,6 +1061,29 @@ hipError_t launch_gemv_t_swiglu(int rows, int act, const void *x, const int32_t 
                                 const int32_t *nactive, int G, int N, int K, hipStream_t s) {
   return launch_gemv_t<true>(rows, act, x, perm, kslots, W1, W3, H, seg_off, active, nactive, G,
                              N, K, 1, 0, s);
+}
+
+hipError_t launch_gemv_t_swiglu_routed(int act, const void *x, const DecodeRoute &r,
+                                       const void *W1, const void *W3, void *H, int N, int K,
+                                       hipStream_t s) {
+  // a single token activates at most k experts: a grid for k of them (the
+  // workgroups of experts past the active count return)
+  const int G = r.k;
+  const int cw = gvt_cw(G, N, K, 1);
+  const bf16_t *a = (const bf16_t *)x, *b1 = (const bf16_t *)W1, *b3 = (const bf16_t *)W3;
+#define GVTR_LAUNCH(CW_)                                                                      \
+  hipLaunchKernelGGL((gemv_t_kernel<true, 1, CW_, true>), dim3(G * (N / CW_), 1),              \
+                     dim3(GV_THREADS), 0, s, a, nullptr, r.k, b1, b3, H, nullptr, nullptr,     \
+                     nullptr, N, K, act, (size_t)0, r)
+  switch (cw) {
+    case 256: GVTR_LAUNCH(256); break;
+    case 128: GVTR_LAUNCH(128); break;
+    case 64: GVTR_LAUNCH(64); break;
+    case 32: GVTR_LAUNCH(32); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef GVTR_LAUNCH
+  return hipGetLastError();
 }
 
 int gemv_t_down_splits(int G, int N, int K, int max_split) {

@@ -187,6 +187,10 @@ hipError_t launch_gemv_down_token(const void *H, const void *W2, const float *s2
 // [K][N] (in x out) weights, up to four rows per expert per pass (more rows
 // loop): vector-ALU weight streaming, H bf16 / Y fp32 as the gemv kernels
 bool gemv_t_ok(int N, int K);
+// one token routed inside the [K][N] SwiGLU kernel (route_fused_ok, gemv_t_ok)
+hipError_t launch_gemv_t_swiglu_routed(int act, const void *x, const DecodeRoute &r,
+                                       const void *W1, const void *W3, void *H, int N, int K,
+                                       hipStream_t s);
 hipError_t launch_gemv_t_swiglu(int rows, int act, const void *x, const int32_t *perm,
                                 int kslots, const void *W1, const void *W3, void *H,
                                 const int32_t *seg_off, const int32_t *active,

@@ -105,6 +105,10 @@ EDGE = [
     ("split_remainders_E4_k1", 1300, 256, 4, 256, 1, "bf16", 0),
     # few tokens: the [K][N] weight-streaming kernel (64- and 32-column blocks)
     ("stream_T1", 1, 2048, 8, 2048, 2, "bf16", 0),
+    # one token routed inside the [K][N] SwiGLU kernel: with a shared expert, and with k = 4
+    # of 32 experts and one expert's bias dominant
+    ("stream_T1_routed_shared", 1, 4096, 8, 2048, 2, "bf16", 2048),
+    ("stream_T1_routed_k4_hot", 1, 2048, 32, 1024, 4, "bf16", 0),
     ("stream_T2_shared", 2, 2048, 4, 6144, 2, "bf16", 2048),
     ("stream_T3_k4", 3, 1024, 8, 1536, 4, "bf16", 0),
     ("stream_T4_hot", 4, 2048, 8, 4096, 2, "bf16", 0),
@@ -126,7 +130,11 @@ def test_inout_edge_cases(case_):
     d = {n: moe.tensor_from_numpy(a) for n, a in h.items() if a is not None}
     d.setdefault("bias", None)
     a, b, ya, yb = run_both(d, cfg)
-    lg = b.intermediates(T)["logits"].double().cpu().numpy()
+    # the same routing in both layouts (the same router arithmetic, whichever kernel runs it)
+    ia, ib = a.intermediates(T), b.intermediates(T)
+    for n in ("idx", "gate", "counts", "offsets", "perm", "inv"):
+        assert torch.equal(ia[n], ib[n]), n
+    lg = ib["logits"].double().cpu().numpy()
     ref = O.forward(h["x"], h["Wg"], h["W1"], h["W3"], h["W2"], k, bias=h.get("bias"),
                     shared=shared_tuple(h), logits_in=lg)
     err = rel_l2(f64(moe.tensor_to_numpy(yb)), ref["y"])
