@@ -28,10 +28,9 @@
 // Tile map.  mtile_off[e] is the prefix of ceil(count_e / BM) over experts;
 // map_tile turns a 1-D workgroup id into (expert, m-tile, n-tile).  The
 // direct-to-LDS kernel takes expert e's rows as seg_off[e] .. seg_end[e] - 1,
-// so one segment can be served by two launches (256-row tiles for its bulk,
-// 64-row tiles for a short remainder).  The
-// persistent kernel also splits the tiles of its last round along K
-// (plan_split).
+// so a segment's bulk can go to 256-row tiles and a short remainder to light
+// 64-row tiles of the same launch (LIGHT).  The persistent kernel also splits
+// the tiles of its last round along K (plan_split).
 #include "common.h"
 #include "kernels.h"
 

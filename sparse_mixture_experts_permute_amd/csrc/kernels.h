@@ -74,10 +74,11 @@ int permute_nblocks(int P);
 // all.  Dropped pairs (and ids outside [0, E)) get inv = -1.
 // zero (may be NULL): nzero int32 set to 0 on the way (the GEMMs' arrival
 // counters, see FixScratch).
-// mid (may be NULL): split tiling for large batches.  mtiles0 is then the
-// prefix of each expert's 256-row tiles and mtiles1 of its 64-row remainder
-// tiles (at most SPLIT_REM_TILES; bm0 and bm1 are not used), and mid[e] the
-// row where the remainder starts (offsets[e + 1] when there is none).
+// mid (may be NULL): split tiling (experts under 512 rows on average).
+// mtiles0 is then the prefix of each expert's full 256-row tiles and mtiles1
+// of its light 64-row tiles for the rows past them (at most SPLIT_REM_TILES;
+// bm0 and bm1 are not used), and mid[e] the row where those rows start
+// (offsets[e + 1] when there are none).
 constexpr int SPLIT_REM_TILES = 2;
 hipError_t launch_permute(const int32_t *idx, int T, int E, int k, int capacity, int bm0,
                           int bm1, int32_t *blk, int32_t *counts, int32_t *offsets,
