@@ -141,10 +141,11 @@ int moe_forward(const void *x, const void *Wg, const float *bias, const void *W1
  * after the down GEMM, [6] after the shared expert (if any), [7] after the
  * combine.  A decode step (T <= 4, T * k <= 64, E <= 64) runs top-k and the
  * grouping in one launch: [1] and [2] then both follow it.  A single token
- * whose router has at most 65536 elements is routed inside the SwiGLU
- * projection: [0] to [3] then all precede that kernel.  When the down
- * projection streams the weights and there is no shared expert, the combine
- * rides in that kernel: [5], [6] and [7] then all follow it.  Same results
+ * whose router has at most 65536 elements (d a multiple of 2048) is routed
+ * inside the SwiGLU projection, in either weight layout: [0] to [3] then all
+ * precede that kernel.  When the down projection streams [out][in] weights
+ * and there is no shared expert, the combine rides in that kernel: [5], [6]
+ * and [7] then all follow it.  Same results
  * and errors as moe_forward; MOE_EINVAL if `events` or any of its handles is
  * NULL.  `opt`: the variants and weight layout of moe_forward_ex (NULL: the
  * defaults). */
