@@ -328,6 +328,51 @@ def test_edge_cases(case_):
         assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
 
 
+# Exact ties in the router scores: duplicated router rows (experts 3 and 5, 1
+# and 6) score bit-identically, and biases put them on top, so top-k must
+# break each tie to the lower index (3 before 5, then 1 before 6), on every
+# router path: one token routed inside the SwiGLU kernel, the tiny decode
+# path, the one-launch router, the feature-split router with its top-k launch,
+# the router with its weights in LDS, and the many-expert score kernel.
+TIES = [
+    # (label, T, d, E, k)
+    ("T1_fused", 1, 2048, 8, 3),
+    ("T3_tiny", 3, 512, 8, 3),
+    ("T64_wave", 64, 512, 8, 3),
+    ("T64_wave_k1", 64, 512, 8, 1),
+    ("T3000_split", 3000, 512, 16, 3),
+    ("T4096_lds", 4096, 2048, 16, 3),
+    ("T64_E64_scores", 64, 512, 64, 3),
+]
+
+
+@pytest.mark.parametrize("case_", TIES, ids=[c[0] for c in TIES])
+def test_router_exact_ties(case_):
+    label, T, dm, E, k = case_
+    say(f"router ties {label}: T={T} d={dm} E={E} k={k}")
+    cfg = LayerConfig(f"ties_{label}", T, dm, E, 256, k, "bf16", seed=7)
+    h = make_inputs(cfg)
+    h["Wg"] = h["Wg"].copy()
+    h["Wg"][5] = h["Wg"][3]
+    h["Wg"][6] = h["Wg"][1]
+    b = np.zeros(E, np.float32)
+    b[3] = b[5] = 40.0  # far above any score of these inputs
+    b[1] = b[6] = 20.0
+    h["bias"] = b
+    d_ = {n: moe.tensor_from_numpy(a) for n, a in h.items() if a is not None}
+    L = layer(d_, cfg)
+    L(d_["x"])
+    torch.cuda.synchronize()
+    it = {kk: v.cpu() for kk, v in L.intermediates(T).items()}
+    lg = it["logits"]
+    assert torch.equal(lg[:, 3], lg[:, 5]) and torch.equal(lg[:, 1], lg[:, 6])
+    idx = it["idx"].numpy()
+    want = [3, 5, 1][:k]
+    assert (idx == np.array(want, np.int32)).all(), idx[:4]
+    idx_ref, _, _ = check_routing(h, cfg, it["idx"], it["gate"], it["logits"])
+    check_permutation(idx_ref, E, it["counts"], it["offsets"], it["perm"], it["inv"])
+
+
 def test_zero_tokens():
     say("edge T=0")
     cfg = LayerConfig("empty", 4, 64, 4, 64, 2, "bf16")
