@@ -509,7 +509,8 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
     } else if (gather_fused && split) {
       if ((e = moe::launch_gemm_swiglu(dtype, true, 256, o.activation, x, W1, W3, H, offsets, mt0,
                                        E, d_ff, d, P / 256 + 3 * E, s, offsets + 1, perm, k,
-                                       (long long)T * d * 2, tb, mid, mt1)))
+                                       (long long)T * d * 2, tb, mid, mt1,
+                                       fixc + moe::FIX_SLOTS - moe::TILE_Q_SLOTS)))
         goto fail;
     } else if (gather_fused) {
       if ((e = moe::launch_gemm_swiglu(dtype, true, 64, o.activation, x, W1, W3, H, offsets, mt0,
@@ -519,7 +520,7 @@ int forward_impl(const void *x, const void *Wg, const float *bias, const void *W
     } else if (split) {
       if ((e = moe::launch_gemm_swiglu(dtype, true, 256, o.activation, Xp, W1, W3, H, offsets, mt0,
                                        E, d_ff, d, P / 256 + 3 * E, s, offsets + 1, nullptr, 1, 0,
-                                       tb, mid, mt1)))
+                                       tb, mid, mt1, fixc + moe::FIX_SLOTS - moe::TILE_Q_SLOTS)))
         goto fail;
     } else if ((e = moe::launch_gemm_swiglu(dtype, plan.dl1, plan.bm1, o.activation, Xp, W1, W3,
                                             H, offsets, mt0, E, d_ff, d,

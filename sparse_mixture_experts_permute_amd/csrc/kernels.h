@@ -101,6 +101,9 @@ GemmPlan gemm_plan(int dtype, int d, int d_ff, int d_ff_shared, long long rows_p
 // zero) and part_bytes of fp32 partial tiles (no split when part is NULL).
 // Launches on one stream may share it.
 constexpr int FIX_SLOTS = 1024;
+// The last TILE_Q_SLOTS of those counters are the per-XCD tile queues of the
+// 256-row launches with light tiles (zero before the launch, left zero).
+constexpr int TILE_Q_SLOTS = 16;
 constexpr int SPLIT_MIN_K = 4864;
 struct FixScratch {
   int32_t *cnt;
@@ -115,7 +118,9 @@ size_t fix_part_bytes(long long tiles);
 // lmid / lmt (256-row direct-to-LDS tiles only): the same launch also serves
 // each expert's rows from lmid[e] to seg_end[e] as light 64-row tiles (lmt:
 // their prefix over the experts) placed after its full tiles, which end at
-// lmid[e]
+// lmid[e]; tile_q (with lmt; NULL: fixed order): 2 * 8 counters, zero before
+// the launch and left zero, through which each XCD's workgroups take its tiles
+// (the down projection uses the last TILE_Q_SLOTS of fx.cnt)
 // seg_end (direct-to-LDS kernel only; NULL: seg_off + 1): expert e's rows
 // are seg_off[e] .. seg_end[e] - 1, with mtile_off the prefix of its tiles.
 // gperm (gemm_gather_ok only): A is x itself (a_bytes bytes) and grouped row s
@@ -127,7 +132,7 @@ hipError_t launch_gemm_swiglu(int dtype, bool dl, int bm, int act, const void *A
                               hipStream_t s, const int32_t *seg_end = nullptr,
                               const int32_t *gperm = nullptr, int gk = 1, long long a_bytes = 0,
                               bool tb = false, const int32_t *lmid = nullptr,
-                              const int32_t *lmt = nullptr);
+                              const int32_t *lmt = nullptr, int32_t *tile_q = nullptr);
 // ksplit > 1 (direct-to-LDS kernel only): every tile's K is split in ksplit
 // equal ranges whose fp32 partials go to planes `plane` elements apart (for
 // batches with few tiles; the last-round split then stays off).
