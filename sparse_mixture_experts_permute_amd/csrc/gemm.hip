@@ -497,8 +497,9 @@ __device__ __forceinline__ void dl_epilogue(const TA &ta, f32x16_v (&acc)[TM][TN
 // gperm[s] / gk, so the grouped rows are never written out; each lane keeps
 // the byte offsets of its rows for the tile (one per A instruction).
 // W8: the weights are FP8 (E4M3) codes [N][K] with one scale per expert (sc1
-// for W1 or W2, sc3 for W3).  They reach LDS as codes (64 bytes of K per row
-// and slice; 16-byte chunk c of row r sits in slot c ^ ((r >> 2) & 3)); a
+// for W1 or W2, sc3 for W3).  They reach LDS as codes, 128 bytes of K per row
+// and code stage (whole 128-byte lines; 16-byte chunk c of row r sits in slot
+// c ^ ((r >> 1) & 7)), so one code stage serves two 64-wide K slices; a
 // fragment read converts its 8 codes to bf16 exactly, and the epilogue
 // multiplies the sums by the expert's scales.  64-row tiles only.
 // LIGHT: the launch also serves light 64-row tiles (lmt: their per-expert
@@ -526,22 +527,23 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
   static_assert(!W8 || (BM == 64 && !TB && !SPLIT), "FP8 weights: 64-row tiles of [N][K] codes");
   static_assert(!LIGHT || (BM == 256 && !SPLIT && !W8), "light tiles: 256-row launches");
 
-  // FP8 tiles: a ring of two row stages and four code stages.  Slice s reads
-  // rows ra[s % 2] and codes rb[s % 4] and then refills them with the rows of
-  // slice s+2 and the codes of slice s+4, so a code load has three and a half
-  // slices to land instead of one and three quarters (FP8 decode, Mixtral
-  // shape: T=8 0.407 -> 0.359 ms, T=128 0.485 -> 0.422 ms).  Each stage is an
-  // array of its own and fixed per slice of a four-slice unrolled loop: with
-  // the stage picked at run time the compiler cannot tell which stage a read
-  // touches and waits for every load in flight before it.  80 KB per
-  // workgroup, two per CU.
+  // FP8 tiles: two row stages of one 64-wide K slice and two code stages of
+  // a slice pair (128 codes per weight row: a code load reads whole 128-byte
+  // lines, where a load of one slice's 64 codes per row reads half-lines and
+  // moves half the bytes per memory request).  Slice s reads rows ra[s % 2]
+  // and half s % 2 of code stage pc[(s / 2) % 2], then refills ra[s % 2] with
+  // the rows of slice s+2; an odd slice s also refills the code stage it has
+  // just finished with the codes of slices s+3 and s+4, which then have two
+  // and a half slices to land.  Each stage is an array of its own and fixed
+  // per slice of a four-slice unrolled loop: with the stage picked at run time
+  // the compiler cannot tell which stage a read touches and waits for every
+  // load in flight before it.  80 KB per workgroup, two per CU.
   constexpr bool RING4 = W8;
-  constexpr int A_U4 = BM * 8, B_U4 = BNB * 4;
+  constexpr int A_U4 = BM * 8, P_U4 = BNB * 8;
   __shared__ uint4 st0[RING4 ? 1 : STAGE_U4];
   __shared__ uint4 st1[RING4 ? 1 : STAGE_U4];
   __shared__ uint4 ra0[RING4 ? A_U4 : 1], ra1[RING4 ? A_U4 : 1];
-  __shared__ uint4 rb0[RING4 ? B_U4 : 1], rb1[RING4 ? B_U4 : 1], rb2[RING4 ? B_U4 : 1],
-      rb3[RING4 ? B_U4 : 1];
+  __shared__ uint4 pc0[RING4 ? P_U4 : 1], pc1[RING4 ? P_U4 : 1];
   __shared__ int fix_arrived;
   __shared__ int q_next;  // LIGHT with a queue: the next tile's index in the XCD's order
   constexpr int COLS = SWIGLU ? BNB / 2 : BNB;
@@ -551,8 +553,9 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = lane_id();
   const int wm = wave / WN, wn = wave % WN;
 
-  // LDS-DMA instructions per wave per stage (an FP8 instruction moves 16 B rows)
-  constexpr int IA = BM / 32, IB = BNB / (W8 ? 64 : 32);
+  // LDS-DMA instructions per wave per stage; IBP: code instructions per wave
+  // per FP8 code stage (8 rows of 128 codes each)
+  constexpr int IA = BM / 32, IB = BNB / 32, IBP = BNB / 32;
   constexpr int PER = IA + IB;
   // K planes (down projection of small batches): blockIdx.y takes one of
   // gridDim.y equal K ranges, its fp32 partial goes to output plane blockIdx.y
@@ -595,16 +598,20 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
   const uint32_t tbl = TB ? (uint32_t)(lane >> 4) * (uint32_t)N * 2u +
                                 (uint32_t)(((lane & 15) ^ ((lane >> 4) << 2)) * 16)
                           : 0u;
-  // W8: an instruction moves 16 rows of 64 code bytes; lane l takes row l / 4
-  // and LDS slot l % 4, which holds chunk (l % 4) ^ (l / 16) of its row (the
-  // row's (r >> 2) & 3 is l / 16 for every instruction)
-  const uint32_t w8l =
-      W8 ? (uint32_t)(lane >> 2) * (uint32_t)K + (uint32_t)(((lane & 3) ^ (lane >> 4)) * 16) : 0u;
+  // W8: instruction q moves code rows 8q .. 8q+7, 128 bytes of each; lane l
+  // takes row 8q + l / 8 and LDS slot l % 8, which holds chunk (l % 8) ^ x of
+  // its row, x = (row >> 1) & 7 = 4 (q & 1) + l / 16 (w8l0: q even, w8l1: odd)
+  const uint32_t w8l0 =
+      W8 ? (uint32_t)(lane >> 3) * (uint32_t)K + (uint32_t)(((lane & 7) ^ (lane >> 4)) * 16) : 0u;
+  const uint32_t w8l1 =
+      W8 ? (uint32_t)(lane >> 3) * (uint32_t)K +
+               (uint32_t)(((lane & 7) ^ (4 + (lane >> 4))) * 16)
+         : 0u;
   struct TileAddr {
     __amdgpu_buffer_rsrc_t ra, r1, r3;
     uint32_t lc0, lc1;
     uint32_t tbl;  // TB: the lane's byte offset inside a [K][N] weight instruction
-    uint32_t w8l;  // W8: the lane's byte offset inside an FP8 weight instruction
+    uint32_t w8l0, w8l1;  // W8: the lane's byte offset inside an even / odd code instruction
     int e;         // the unit's expert
     uint32_t ga[GATHER ? IA : 1];  // GATHER: byte offset in x of each A instruction's row
     int row0, rows, n0;
@@ -675,8 +682,9 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
     ta.lc0 = lc0;
     ta.lc1 = lc1;
     ta.tbl = tbl;
-    ta.w8l = w8l;
-    asm volatile("" : "+v"(ta.lc0), "+v"(ta.lc1), "+v"(ta.tbl), "+v"(ta.w8l));
+    ta.w8l0 = w8l0;
+    ta.w8l1 = w8l1;
+    asm volatile("" : "+v"(ta.lc0), "+v"(ta.lc1), "+v"(ta.tbl), "+v"(ta.w8l0), "+v"(ta.w8l1));
   };
   // B block parity: block (wave*IB + j)/4 is odd (a W3 block) iff (j/4) is odd,
   // because IB is a multiple of 8
@@ -734,15 +742,17 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
     }
   };
   auto issue = [&](const TileAddr &ta, uint4 *stage, int kt) { issue_part(ta, stage, kt, 0, PER); };
-  // ring: rows of slice kta into sa, codes of slice ktb into sb (instruction q
-  // = wave * IB + j fills code rows 16 q .. 16 q + 15, 64 bytes of each, all in
-  // one 32-row block); a slice past the unit's end is loaded from past the
-  // buffer's range (zeros, no memory read), which keeps every slice's load
-  // count and wait the same
-  auto issue4 = [&](const TileAddr &ta, uint4 *sa, int kta, uint4 *sb, int ktb, int j0, int j1) {
+  // ring: rows of slice kta into sa and, when kpb >= 0, the codes of slice
+  // pair kpb (K 128 kpb .. + 127) into sb; code instruction q = wave * IBP + j
+  // fills code rows 8q .. 8q+7, all in one 32-row block.  Instructions j0 <= j
+  // < j1 of the slice: the IA row instructions first, then the IBP code ones.
+  // A slice or pair past the unit's end is loaded from past the buffer's
+  // range (zeros, no memory read), which keeps every slice's load count and
+  // wait the same.
+  auto issue4 = [&](const TileAddr &ta, uint4 *sa, int kta, uint4 *sb, int kpb, int j0, int j1) {
     uint32_t koa = (uint32_t)kta * 128 + (kta < ta.nk ? 0u : 0x80000000u);
-    uint32_t ko8 = (uint32_t)ktb * 64 + (ktb < ta.nk ? 0u : 0x80000000u);
-    asm volatile("" : "+s"(koa), "+s"(ko8));
+    uint32_t kop = (uint32_t)kpb * 128 + (2 * kpb < ta.nk ? 0u : 0x80000000u);
+    asm volatile("" : "+s"(koa), "+s"(kop));
 #pragma unroll
     for (int j = 0; j < IA; ++j)
       if (j >= j0 && j < j1) {
@@ -753,10 +763,11 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
           buffer_to_lds16(ta.ra, ((j & 1) ? ta.lc1 : ta.lc0) + u, sa + (wave * IA + j) * 64);
         }
       }
+    if (kpb < 0) return;
 #pragma unroll
-    for (int j = 0; j < IB; ++j)
+    for (int j = 0; j < IBP; ++j)
       if (IA + j >= j0 && IA + j < j1) {
-        const int q = wave * IB + j, br = 16 * q;
+        const int q = wave * IBP + j, br = 8 * q;
         int col;
         bool w3 = false;
         if (SWIGLU) {
@@ -766,15 +777,15 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
         } else {
           col = ta.n0 + br;
         }
-        buffer_to_lds16<true>(w3 ? ta.r3 : ta.r1, ta.w8l + (uint32_t)col * (uint32_t)K + ko8,
+        buffer_to_lds16<true>(w3 ? ta.r3 : ta.r1,
+                              ((j & 1) ? ta.w8l1 : ta.w8l0) + (uint32_t)col * (uint32_t)K + kop,
                               sb + q * 64);
       }
   };
+  // a unit's first slices: rows of slices 0 and 1, codes of pairs 0 and 1
   auto prologue4 = [&](const TileAddr &ta) {
-    issue4(ta, ra0, 0, rb0, 0, 0, PER);
-    issue4(ta, ra1, 1, rb1, 1, 0, PER);
-    issue4(ta, ra0, 0, rb2, 2, IA, PER);
-    issue4(ta, ra0, 0, rb3, 3, IA, PER);
+    issue4(ta, ra0, 0, pc0, 0, 0, IA + IBP);
+    issue4(ta, ra1, 1, pc1, 1, 0, IA + IBP);
   };
 
   f32x16_v acc[TM][TN];
@@ -789,17 +800,17 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
   // those four k-rows, which is what a 32x32x16 MFMA lane needs (column l % 32,
   // K values 8 * (l / 32) + 0..3; the next read gives + 4..7).
   int tbo[TN];
-  int w8o[4];  // W8: byte offset in a code stage of the lane's 8 codes of K step ks
+  // W8: the lane's 8 codes of chunk x (= 4 h + K step ks) sit at byte
+  // w8b + 16 (x ^ w8f) of a code stage (two registers, not one per chunk)
+  int w8b = 0, w8f = 0;
   auto set_frag_addr = [&](int ln) {
     frow = ln & 31;
     const int xf = (frow >> 1) & 7;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) cidx[ks] = (ks * 2 + (ln >> 5)) ^ xf;
     if constexpr (W8) {
-      const int f = ((ln & 31) >> 2) & 3;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        w8o[ks] = (ln & 31) * 64 + 16 * (ks ^ f) + 8 * ((ln >> 5) & 1);
+      w8f = ((ln & 31) >> 1) & 7;
+      w8b = (ln & 31) * 128 + 8 * ((ln >> 5) & 1);
     }
     if constexpr (TB) {
       // the wave's block b: SwiGLU matrix b & 1, beta 2 * wn + b / 2; down
@@ -842,18 +853,21 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
     }
   };
   int rd_tag = 0;  // the slice being read (varies per slice)
-  auto rd4 = [&](const uint4 *sa, const uint4 *sb, int ks, uint4 (&af)[TM], uint4 (&bf)[TN]) {
+  // fragments of K step ks of a slice: rows from sa, codes from half h of sb
+  auto rd4 = [&](const uint4 *sa, const uint4 *sb, int h, int ks, uint4 (&af)[TM],
+                 uint4 (&bf)[TN]) {
     // lane offsets through an opaque copy tied to the slice: every read is a
     // register plus a constant offset, not a register per read held across
     // the loop
-    int oa = ((wm * TM * 32 + frow) * 8 + cidx[ks]) * 16, ob = w8o[ks] + wn * TN * 32 * 64;
-    asm("" : "+v"(oa), "+v"(ob) : "s"(rd_tag));
+    int oa = ((wm * TM * 32 + frow) * 8 + cidx[ks]) * 16, f = w8f;
+    asm("" : "+v"(oa), "+v"(f) : "s"(rd_tag));
+    const int ob = w8b + 16 * ((h * 4 + ks) ^ f) + wn * TN * 32 * 128;
     const char *pa = reinterpret_cast<const char *>(sa), *pb = reinterpret_cast<const char *>(sb);
 #pragma unroll
     for (int a = 0; a < TM; ++a) af[a] = *reinterpret_cast<const uint4 *>(pa + oa + a * 4096);
 #pragma unroll
     for (int b = 0; b < TN; ++b) {
-      const uint2 q = *reinterpret_cast<const uint2 *>(pb + ob + b * 32 * 64);
+      const uint2 q = *reinterpret_cast<const uint2 *>(pb + ob + b * 32 * 128);
       // E4M3 -> bf16 is exact; gfx950 converts two codes at a time
       bf[b] = make_uint4(
           __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.x, 1.f, false)),
@@ -897,6 +911,7 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
   // loads of the slice two ahead: J1 of them spread over the MFMAs of K steps
   // 1 and 2, the rest over step 3 (after the wait for the next slice)
   constexpr int J1 = PER * 5 / 8;
+  constexpr int J1O = (IA + IBP) / 2;  // FP8 ring: an odd slice's loads before its wait
   // the interleave patterns are written for the 256 x 256 tile
   constexpr bool FULL = TM == 4 && TN == 4 && PER == 16;
 #define P_MM_LD() do { for (int q_ = 0; q_ < J1; ++q_) { SG(8,3); SG(0x20,1); } SG(8, 32 - 3 * J1); } while (0)
@@ -930,35 +945,40 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
     SCHED_FENCE();                                                             \
   } while (0)
 
-// ring slice s (stages SA, SB; the next slice's in NA, NB).  Its wait leaves
-// in flight the codes of slice s+3 and the first J1 loads of this slice, all
-// issued after the rows of slice s+1 (whose codes are older still).
-#define R4_BODY(s, SA, SB, NA, NB, ca, cb, na, nb)                                          \
+// ring slice s (rows SA, codes half H of SB; the next slice's in NA, half NH
+// of NB).  Even s issues the rows of slice s+2 (IA loads, all before its
+// wait); odd s also the codes of pair (s+1)/2 + 1 into SB (IA + IBP loads,
+// J1O of them before its wait).  The wait for slice s+1 leaves in flight: at
+// even s the codes issued by slice s-1 after the rows of slice s+1, and this
+// slice's rows; at odd s this slice's first J1O loads (the codes slice s+1
+// reads were issued by slice s-2).
+#define R4_BODY(s, ODD, SA, SB, H, NA, NB, NH, ca, cb, na, nb)                             \
   do {                                                                                      \
     rd_tag = (s);                                                                           \
-    rd4(SA, SB, 1, f1a, f1b);                                                               \
-    rd4(SA, SB, 2, f2a, f2b);                                                               \
-    rd4(SA, SB, 3, f3a, f3b);                                                               \
+    rd4(SA, SB, H, 1, f1a, f1b);                                                            \
+    rd4(SA, SB, H, 2, f2a, f2b);                                                            \
+    rd4(SA, SB, H, 3, f3a, f3b);                                                            \
     mm(ca, cb);                                                                             \
     SCHED_FENCE();                                                                          \
     LGKM_WAIT0();                                                                           \
     RAW_BARRIER();                                                                          \
-    issue4(cur, SA, (s) + 2, SB, (s) + 4, 0, J1);                                           \
+    if constexpr (ODD) issue4(cur, SA, (s) + 2, SB, ((s) + 1) / 2 + 1, 0, J1O);             \
+    else issue4(cur, SA, (s) + 2, SB, -1, 0, IA);                                           \
     mm(f1a, f1b);                                                                           \
     mm(f2a, f2b);                                                                           \
     SCHED_FENCE();                                                                          \
-    VM_WAIT(IB + J1);                                                                       \
+    if constexpr (ODD) VM_WAIT(J1O); else VM_WAIT(IBP + IA);                                \
     RAW_BARRIER();                                                                          \
-    rd4(NA, NB, 0, na, nb);                                                                 \
-    issue4(cur, SA, (s) + 2, SB, (s) + 4, J1, PER);                                         \
+    rd4(NA, NB, NH, 0, na, nb);                                                             \
+    if constexpr (ODD) issue4(cur, SA, (s) + 2, SB, ((s) + 1) / 2 + 1, J1O, IA + IBP);      \
     mm(f3a, f3b);                                                                           \
     SCHED_FENCE();                                                                          \
   } while (0)
-#define R4_LAST(SA, SB, ca, cb)                                                             \
+#define R4_LAST(SA, SB, H, ca, cb)                                                          \
   do {                                                                                      \
-    rd4(SA, SB, 1, f1a, f1b);                                                               \
-    rd4(SA, SB, 2, f2a, f2b);                                                               \
-    rd4(SA, SB, 3, f3a, f3b);                                                               \
+    rd4(SA, SB, H, 1, f1a, f1b);                                                            \
+    rd4(SA, SB, H, 2, f2a, f2b);                                                            \
+    rd4(SA, SB, H, 3, f3a, f3b);                                                            \
     mm(ca, cb);                                                                             \
     SCHED_FENCE();                                                                          \
     LGKM_WAIT0();                                                                           \
@@ -971,19 +991,19 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
 #define R4_SLICES()                                                                         \
   do {                                                                                      \
     for (; kt + 4 < cur.nk; kt += 4) {                                                      \
-      R4_BODY(kt, ra0, rb0, ra1, rb1, f0a, f0b, g0a, g0b);                                  \
-      R4_BODY(kt + 1, ra1, rb1, ra0, rb2, g0a, g0b, f0a, f0b);                              \
-      R4_BODY(kt + 2, ra0, rb2, ra1, rb3, f0a, f0b, g0a, g0b);                              \
-      R4_BODY(kt + 3, ra1, rb3, ra0, rb0, g0a, g0b, f0a, f0b);                              \
+      R4_BODY(kt, false, ra0, pc0, 0, ra1, pc0, 1, f0a, f0b, g0a, g0b);                     \
+      R4_BODY(kt + 1, true, ra1, pc0, 1, ra0, pc1, 0, g0a, g0b, f0a, f0b);                  \
+      R4_BODY(kt + 2, false, ra0, pc1, 0, ra1, pc1, 1, f0a, f0b, g0a, g0b);                 \
+      R4_BODY(kt + 3, true, ra1, pc1, 1, ra0, pc0, 0, g0a, g0b, f0a, f0b);                  \
     }                                                                                       \
     /* 2 or 4 slices left, the first in stages 0 */                                         \
-    R4_BODY(kt, ra0, rb0, ra1, rb1, f0a, f0b, g0a, g0b);                                    \
+    R4_BODY(kt, false, ra0, pc0, 0, ra1, pc0, 1, f0a, f0b, g0a, g0b);                       \
     if (kt + 2 == cur.nk) {                                                                 \
-      R4_LAST(ra1, rb1, g0a, g0b);                                                          \
+      R4_LAST(ra1, pc0, 1, g0a, g0b);                                                       \
     } else {                                                                                \
-      R4_BODY(kt + 1, ra1, rb1, ra0, rb2, g0a, g0b, f0a, f0b);                              \
-      R4_BODY(kt + 2, ra0, rb2, ra1, rb3, f0a, f0b, g0a, g0b);                              \
-      R4_LAST(ra1, rb3, g0a, g0b);                                                          \
+      R4_BODY(kt + 1, true, ra1, pc0, 1, ra0, pc1, 0, g0a, g0b, f0a, f0b);                  \
+      R4_BODY(kt + 2, false, ra0, pc1, 0, ra1, pc1, 1, f0a, f0b, g0a, g0b);                 \
+      R4_LAST(ra1, pc1, 1, g0a, g0b);                                                       \
     }                                                                                       \
   } while (0)
 
@@ -1089,9 +1109,9 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
   setup(tile, cur);
   if constexpr (RING4) {
     prologue4(cur);
-    VM_WAIT(PER + 2 * IB);
+    VM_WAIT(IA + IBP);  // rows of slice 0 and codes of pair 0 are in
     RAW_BARRIER();
-    rd4(ra0, rb0, 0, f0a, f0b);
+    rd4(ra0, pc0, 0, 0, f0a, f0b);
   } else {
     issue(cur, st0, 0);
     issue(cur, st1, 1);
@@ -1174,7 +1194,7 @@ __global__ __launch_bounds__(GM_THREADS) void grouped_gemm_dl_kernel(
     VM_WAIT(0);  // both slices (and the epilogue's stores) done
     RAW_BARRIER();
     if constexpr (RING4)
-      rd4(ra0, rb0, 0, f0a, f0b);
+      rd4(ra0, pc0, 0, 0, f0a, f0b);
     else
       rd(st0, 0, f0a, f0b);
     cur = nxt;
