@@ -9,6 +9,10 @@ counters, and the summary of rocprofv3 outputs into the text kept in profiles/.
       [--trace T.csv] [--kernel SUBSTR] [--bench bench.json] [--cmd "..."]
       prints a markdown summary (kernel table, per-dispatch traffic of the
       selected kernel scaled by the copy calibration)
+  python -m sparse_mixture_experts_permute_amd.profiling fp8-decode --T 8 [--steps 20]
+      runs back-to-back decode steps of the Mixtral-shaped layer with FP8
+      experts (weights quantised once, before the steps) for a kernel trace
+      or counter pass, and prints the mean step time
 """
 from __future__ import annotations
 
@@ -31,6 +35,35 @@ def run_copy(mib: int) -> None:
         dst.copy_(src)
     torch.cuda.synchronize()
     print(f"copied {mib} MiB x 3", flush=True)
+
+
+def run_fp8_decode(T: int, steps: int) -> None:
+    import os
+
+    import torch
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    if root not in sys.path:  # run as a script path
+        sys.path.insert(0, root)
+
+    from sparse_mixture_experts_permute_amd import moe
+    from sparse_mixture_experts_permute_amd.inputs import CONFIGS, make_inputs
+    cfg = CONFIGS["mixtral_decode_T128"]
+    host = make_inputs(cfg, T=max(T, cfg.T))
+    dev = {n: moe.tensor_from_numpy(a) for n, a in host.items() if a is not None}
+    layer = moe.MoELayerFP8(dev["Wg"], dev["W1"], dev["W3"], dev["W2"], cfg.k)
+    x = dev["x"][:T].contiguous()
+    y = torch.empty_like(x)
+    for _ in range(3):
+        layer(x, y)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        layer(x, y)
+    b.record()
+    torch.cuda.synchronize()
+    print(f"fp8 decode T={T}: {a.elapsed_time(b) / steps * 1e3:.1f} us/step "
+          f"(back-to-back, {steps} steps)", flush=True)
 
 
 def _short(name: str) -> str:
@@ -140,6 +173,9 @@ def main(argv=None):
     sub = ap.add_subparsers(dest="cmd_name", required=True)
     c = sub.add_parser("copy")
     c.add_argument("--mib", type=int, default=COPY_MIB_DEFAULT)
+    f = sub.add_parser("fp8-decode")
+    f.add_argument("--T", type=int, default=8)
+    f.add_argument("--steps", type=int, default=20)
     s = sub.add_parser("summarize")
     s.add_argument("--stats", required=True)
     s.add_argument("--trace", help="kernel_trace.csv of the same run (per-dispatch durations)")
@@ -154,6 +190,8 @@ def main(argv=None):
     a = ap.parse_args(argv)
     if a.cmd_name == "copy":
         run_copy(a.mib)
+    elif a.cmd_name == "fp8-decode":
+        run_fp8_decode(a.T, a.steps)
     else:
         print(summarize(a))
 
