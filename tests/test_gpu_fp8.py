@@ -159,9 +159,10 @@ def test_forward_fp8_tiled(T, E, k, d, dff, gm, cap):
 
 @pytest.mark.parametrize("name", ["mixtral_decode_T8", "mixtral_decode_T128"])
 def test_forward_fp8_mixtral_sampled(name):
-    """Mixtral-shaped decode batches with FP8 experts: sampled tokens against
-    the oracle on the dequantised weights of each expert they reach (one
-    expert's matrices at a time, so that the fp64 copies stay small)."""
+    """Mixtral-shaped decode batches with FP8 experts: every token against the
+    oracle on the dequantised weights of each expert it reaches (one expert's
+    matrices at a time, so that the fp64 copies stay small), so every 64-row
+    tile and every column block of both GEMMs is compared."""
     cfg = CONFIGS[name]
     h = make_inputs(cfg)
     dev = {n: moe.tensor_from_numpy(a) for n, a in h.items() if a is not None}
@@ -169,9 +170,8 @@ def test_forward_fp8_mixtral_sampled(name):
     y = L(dev["x"])
     torch.cuda.synchronize()
     it = {n: v.cpu().numpy() for n, v in L.intermediates(cfg.T).items()}
-    rows = sorted({0, cfg.T - 1} | set(np.random.default_rng(5).choice(cfg.T, 6, replace=False)))
-    idx, gate = it["idx"][rows], it["gate"][rows].astype(np.float64)
-    ref = np.zeros((len(rows), cfg.d))
+    idx, gate = it["idx"], it["gate"].astype(np.float64)
+    ref = np.zeros((cfg.T, cfg.d))
     x64 = f64(h["x"])
     for e in sorted(set(idx.ravel().tolist())):
         parts = {}
@@ -180,11 +180,16 @@ def test_forward_fp8_mixtral_sampled(name):
             np.testing.assert_array_equal(getattr(L, qn)[e].cpu().numpy(), q_ref[0])
             assert getattr(L, sn)[e].item() == s_ref[0]
             parts[n] = O.dequant_fp8(q_ref, s_ref)
-        for i, t in enumerate(rows):
-            for j in range(cfg.k):
-                if idx[i, j] == e:
-                    ref[i] += gate[i, j] * O.expert_row(x64, t, parts["W1"], parts["W3"],
-                                                        parts["W2"], 0)
-    err = rel_l2(f64(moe.tensor_to_numpy(y))[rows], ref)
-    say(f"{name} fp8: {len(rows)} sampled tokens, rel-L2 {err:.3e}")
+        # the tokens that reach expert e, each with the gate of that pair
+        tok, slot = np.nonzero(idx == e)
+        ref[tok] += O.forward_rows(x64, parts["W1"], parts["W3"], parts["W2"], tok,
+                                   np.zeros((len(tok), 1), np.int32),
+                                   gate[tok, slot][:, None])
+    got = f64(moe.tensor_to_numpy(y))
+    err = rel_l2(got, ref)
+    worst = max(rel_l2(got[t], ref[t]) for t in range(cfg.T))
+    say(f"{name} fp8: all {cfg.T} tokens, rel-L2 {err:.3e}, worst token {worst:.3e}")
     assert err <= 1e-2
+    # each token on its own as well (three times the bar, as for the edge
+    # cases): one wrong 64-row tile hardly moves the whole output's error
+    assert worst <= 3e-2
