@@ -130,7 +130,8 @@ def test_forward_fp8_mixtral_T1_sampled():
     (8, 8, 2, 2048, 2048, 0, None), (32, 8, 2, 1024, 1536, 0, None),
     (128, 8, 2, 512, 1024, 1, None), (40, 16, 4, 256, 512, 3, None),
     (64, 8, 2, 256, 14336, 0, None),  # every down-projection tile split into K planes
-    (100, 4, 1, 384, 640, 2, 20), (5, 8, 2, 256, 384, 0, None), (300, 32, 2, 128, 256, 0, None)])
+    (100, 4, 1, 384, 640, 2, 20), (5, 8, 2, 256, 384, 0, None), (300, 32, 2, 128, 256, 0, None),
+    (384, 8, 2, 256, 512, 0, None)])  # 96 rows per expert: two or more 64-row tiles each
 def test_forward_fp8_tiled(T, E, k, d, dff, gm, cap):
     cfg, h, dev = fp8_case(T, d, E, dff, k, seed=T + E + d, skew=1.5 if cap else 0.0)
     say(f"forward_fp8 tiled T={T} E={E} k={k} d={d} d_ff={dff} gate={gm} capacity={cap}")
