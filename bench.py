@@ -286,6 +286,21 @@ def measured_traffic(cfg):
     return rec.get("traffic_bytes")
 
 
+def count_summary(counts):
+    """Rows per expert of one step: min / max / mean, every expert's count
+    when there are at most 64, else an 8-bin histogram of the counts."""
+    import numpy as np
+    c = np.asarray(counts)
+    out = {"min": int(c.min()), "max": int(c.max()), "mean": float(c.mean())}
+    if c.size <= 64:
+        out["per_expert"] = [int(v) for v in c]
+    else:
+        h, edges = np.histogram(c, bins=8)
+        out["histogram"] = {"bin_edges": [round(float(e), 1) for e in edges],
+                            "experts": [int(v) for v in h]}
+    return out
+
+
 def roofline_for(cfg, res):
     from sparse_mixture_experts_permute_amd import moe
     a = algorithmic(cfg, res["counts"])
@@ -463,7 +478,8 @@ def main():
                      tokens_per_s=round(c2.T / (ms2 * 1e-3), 1),
                      stage_ms={s: round(float(v), 4) for s, v in zip(moe.STAGES,
                                                                       r2["stage_ms"])},
-                     step_ms=r2["step_ms"], roofline=rl2, layer=lf2, mall_flushed=bool(flush))
+                     step_ms=r2["step_ms"], roofline=rl2, layer=lf2, mall_flushed=bool(flush),
+                     expert_counts=count_summary(r2["counts"]))
             if "graph_ms" in r2:
                 gms = r2["graph_ms"]
                 e["graph_replay"] = dict(
@@ -532,7 +548,8 @@ def main():
                      tokens_per_s=round(c2.T / (ms2 * 1e-3), 1),
                      stage_ms={s_: round(float(v), 4) for s_, v in zip(moe.STAGES,
                                                                         r2["stage_ms"])},
-                     step_ms=r2["step_ms"], roofline=rl2, layer=lf2, mall_flushed=False)
+                     step_ms=r2["step_ms"], roofline=rl2, layer=lf2, mall_flushed=False,
+                     expert_counts=count_summary(r2["counts"]))
             log(f"{name}: {ms2:.4f} ms/step, {e['tokens_per_s']} tokens/s, "
                 f"layer mfma {lf2['mfma_frac']} hbm {lf2['hbm_frac']}")
             extra.append(e)
@@ -602,8 +619,7 @@ def main():
         "layer_roofline": layer_fr,
         "step_ms": res["step_ms"],
         "stage_ms": stage,
-        "expert_counts": {"min": int(counts.min()), "max": int(counts.max()),
-                          "mean": float(counts.mean())},
+        "expert_counts": count_summary(counts),
         "cpu_baseline": cpu,
         "weight_layout": "in_out" if inout else "out_in",
         "extra": extra,
