@@ -55,5 +55,26 @@ def build(verbose: bool = True) -> str:
     return OUT
 
 
+# A plain C program that calls the library (tests/c_abi): host code only, so
+# gcc builds it against the HIP runtime and the in-tree library.
+C_CALLER_SRC = os.path.join(os.path.dirname(HERE), "tests", "c_abi", "moe_c_caller.c")
+C_CALLER = os.path.join(os.path.dirname(HERE), "tests", "c_abi", "moe_c_caller")
+
+
+def build_c_caller(verbose: bool = True) -> str:
+    rocm = os.path.dirname(os.path.dirname(HIPCC))  # the ROCm root (/opt/rocm)
+    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-D__HIP_PLATFORM_AMD__", f"-I{rocm}/include",
+           C_CALLER_SRC, "-o", C_CALLER, f"-L{HERE}", "-lmoe_mi355x", f"-L{rocm}/lib",
+           "-lamdhip64", "-Wl,-rpath,$ORIGIN/../../sparse_mixture_experts_permute_amd",
+           f"-Wl,-rpath,{rocm}/lib"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"gcc failed for {C_CALLER_SRC}:\n{r.stdout}{r.stderr}")
+    if verbose:
+        print(f"built {C_CALLER}")
+    return C_CALLER
+
+
 if __name__ == "__main__":
     build()
+    build_c_caller()

@@ -251,3 +251,15 @@ def test_capacity_mean(L):
     assert L.moe_capacity_mean(0, 2, 8, 1.2) == 0
     assert L.moe_capacity_mean(-1, 2, 8, 1.2) == -1
     assert L.moe_capacity_mean(4, 2, 0, 1.2) == -1
+
+
+def test_c_caller_built_and_linked():
+    """The plain C caller of the ABI (run on the GPU by test_gpu_c_abi.py) is
+    built and resolves the library and the HIP runtime: without arguments it
+    prints its usage before touching a device."""
+    import subprocess
+
+    from sparse_mixture_experts_permute_amd.build import C_CALLER
+    assert os.path.exists(C_CALLER), f"{C_CALLER} not built (the package build compiles it)"
+    r = subprocess.run([C_CALLER], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 2 and "usage" in r.stderr
