@@ -1155,9 +1155,10 @@ hipError_t launch_gemv_down_token(const void *H, const void *W2, const float *s2
 #define GT_CASE(KC_)                                                                        \
   case KC_: {                                                                               \
     constexpr int CB = gv_cb(KC_);                                                          \
-    /* the narrowest block (two groups) up to GT_COLS that keeps to one workgroup per CU */ \
+    /* the narrowest block (two groups) up to GT_COLS that keeps to two workgroups per CU */ \
+    /* (Mixtral shape, one token, FP8 weights: 0.7-1.5 us per step off one per CU) */     \
     int cw = 2 * CB;                                                                        \
-    while (N / cw > 256 && 2 * cw <= GT_COLS && N % (2 * cw) == 0) cw *= 2;                 \
+    while (N / cw > 512 && 2 * cw <= GT_COLS && N % (2 * cw) == 0) cw *= 2;                 \
     if (N % cw) return hipErrorInvalidValue;                                                \
     if (s2)                                                                                 \
       hipLaunchKernelGGL((gemv_down_token_kernel<KC_, true>), dim3(N / cw), dim3(GV_THREADS), \
